@@ -1,0 +1,226 @@
+"""CPU oracle for the NABLA hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never calls it and
+shares no code with it.  The arithmetic lives in ``nabla_oracle.c`` (fp32
+estimator with a fixed reduction order, fp64 attention); this module only
+marshals numpy arrays through ctypes.
+
+Pages followed: FastVideo API page "nabla" (nablaT_v2 source; the
+NablaAttentionImpl.forward source; the NablaAttentionMetadata fields) and the
+"NABLA: Neighborhood Adaptive Block-Level Attention" summary page (Technical
+Summary, Methodology).
+
+Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
+against closed forms, brute force, invariants or library routines
+(nothing here is "parity unpinned").
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "liborc_nabla.so")
+
+BLOCK = 64
+FIX_BITS = 48
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _b
+        _b.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.orc_set_threads.argtypes = [i32]
+    lib.orc_get_threads.restype = i32
+    lib.orc_fractal_index.argtypes = [i32, i32, i32, i32, i32]
+    lib.orc_fractal_index.restype = i64
+    lib.orc_fractal_permute.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, i32]
+    lib.orc_sta_mask.argtypes = [P, i32, i32, i32, i32, i32, i32]
+    lib.orc_pool.argtypes = [P, P, i32, i32, i32, i32]
+    lib.orc_scores.argtypes = [P, P, P, i32, i32, i32, i32]
+    lib.orc_nexp.argtypes = [ctypes.c_float]
+    lib.orc_nexp.restype = ctypes.c_float
+    lib.orc_nexp_vec.argtypes = [P, P, i64]
+    lib.orc_softmax_row.argtypes = [P, i32, P, P, P, P]
+    lib.orc_cut_fixed.argtypes = [f64]
+    lib.orc_cut_fixed.restype = i64
+    lib.orc_select_row.argtypes = [P, i32, f64, P, P]
+    lib.orc_block_mask.argtypes = [P, P, i32, i32, i32, i32, P, f64, P, P, P, P]
+    lib.orc_block_mask.restype = i32
+    lib.orc_attention.argtypes = [P, P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
+    lib.orc_attention.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def set_threads(n: int) -> int:
+    lib = _load()
+    lib.orc_set_threads(int(n))
+    return lib.orc_get_threads()
+
+
+def get_threads() -> int:
+    return _load().orc_get_threads()
+
+
+# ---------------------------------------------------------------- O1 permute
+def fractal_index(t, y, x, H, W) -> int:
+    return _load().orc_fractal_index(t, y, x, H, W)
+
+
+def fractal_permute(x, inverse=False):
+    """x natural [B,T,H,W,heads,D] -> fractal [B,S,heads,D] (or back).
+
+    Any fixed-size dtype (the permutation moves bytes).  For ``inverse`` pass
+    the fractal tensor with shape [B,T,H,W,heads,D] viewed as such.
+    """
+    x = np.ascontiguousarray(x)
+    B, T, H, W, heads, D = x.shape
+    y = np.empty_like(x)
+    _load().orc_fractal_permute(_ptr(x), _ptr(y), x.itemsize, B, T, H, W, heads, D, int(inverse))
+    return y
+
+
+# ---------------------------------------------------------------- O2 STA
+def sta_mask(Tt, Ht, Wt, wt, wh, ww):
+    nb = Tt * Ht * Wt
+    out = np.empty((nb, nb), dtype=np.uint8)
+    _load().orc_sta_mask(_ptr(out), Tt, Ht, Wt, wt, wh, ww)
+    return out
+
+
+# ---------------------------------------------------------------- O3-O5
+def pool(x):
+    """x [B,S,heads,D] (fp32 values) -> [B,heads,S/64,D] fp32."""
+    x = _f32(x)
+    B, S, heads, D = x.shape
+    out = np.empty((B, heads, S // BLOCK, D), dtype=np.float32)
+    _load().orc_pool(_ptr(x), _ptr(out), B, S, heads, D)
+    return out
+
+
+def scores(qa, ka):
+    qa, ka = _f32(qa), _f32(ka)
+    B, heads, nb, D = qa.shape
+    out = np.empty((B, heads, nb, nb), dtype=np.float32)
+    _load().orc_scores(_ptr(qa), _ptr(ka), _ptr(out), B, heads, nb, D)
+    return out
+
+
+def nexp(x):
+    x = _f32(x)
+    y = np.empty_like(x)
+    _load().orc_nexp_vec(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def softmax_row(s):
+    """Returns (e, p, P, Z): exp weights, fp32 probabilities, their 2^-48 fixed-point values, Z."""
+    s = _f32(s)
+    nb = s.shape[0]
+    e = np.empty(nb, np.float32)
+    p = np.empty(nb, np.float32)
+    P = np.empty(nb, np.int64)
+    Z = np.zeros(1, np.float64)
+    _load().orc_softmax_row(_ptr(s), nb, _ptr(e), _ptr(p), _ptr(P), _ptr(Z))
+    return e, p, P, float(Z[0])
+
+
+def cut_fixed(thr) -> int:
+    return _load().orc_cut_fixed(float(thr))
+
+
+def select_row(s, thr):
+    """Returns (kept uint8 [nb], diag int64 [3] = (i0, c_{i0-1}, c_{i0}))."""
+    s = _f32(s)
+    nb = s.shape[0]
+    kept = np.empty(nb, np.uint8)
+    diag = np.empty(3, np.int64)
+    _load().orc_select_row(_ptr(s), nb, float(thr), _ptr(kept), _ptr(diag))
+    return kept, diag
+
+
+# ---------------------------------------------------------------- O3-O9
+def block_mask(q, k, sta, thr, want_nabla=False):
+    """The estimator.  q, k [B,S,heads,D] fp32 values; sta [nb,nb] uint8 or None.
+
+    Returns dict with kv_nb [B,h,nb] int32, kv_inds [B,h,nb,nb] int32
+    (kept ascending, then dropped ascending), diag [B,h,nb,3] int64 and,
+    if asked, mnabla [B,h,nb,nb] uint8 (mask before the STA union).
+    """
+    q, k = _f32(q), _f32(k)
+    B, S, heads, D = q.shape
+    nb = S // BLOCK
+    kv_nb = np.empty((B, heads, nb), np.int32)
+    kv_inds = np.empty((B, heads, nb, nb), np.int32)
+    diag = np.empty((B, heads, nb, 3), np.int64)
+    mn = np.empty((B, heads, nb, nb), np.uint8) if want_nabla else None
+    st = None if sta is None else np.ascontiguousarray(sta, dtype=np.uint8)
+    rc = _load().orc_block_mask(_ptr(q), _ptr(k), B, S, heads, D, _ptr(st), float(thr),
+                                _ptr(kv_nb), _ptr(kv_inds), _ptr(mn), _ptr(diag))
+    if rc != 0:
+        raise ValueError("oracle block_mask: bad argument")
+    out = {"kv_nb": kv_nb, "kv_inds": kv_inds, "diag": diag}
+    if want_nabla:
+        out["mnabla"] = mn
+    return out
+
+
+def band_rows(diag, thr, width=1e-6):
+    """Rows whose CDF at the cut (c_{i0-1} or c_{i0}) lies within ``width`` of fl32(1-thr)."""
+    cut = float(np.float32(1.0 - thr))
+    c_prev = diag[..., 1].astype(np.float64) / 2.0 ** FIX_BITS
+    c_at = diag[..., 2].astype(np.float64) / 2.0 ** FIX_BITS
+    return (np.abs(c_prev - cut) < width) | (np.abs(c_at - cut) < width)
+
+
+# ---------------------------------------------------------------- O10
+def attention(q, k, v, kv_nb, kv_inds, row_ids=None, scale=0.0):
+    """Dense fp64 attention with disallowed 64x64 blocks at -inf.
+
+    q, k, v [B,S,heads,D] fp32 values; row_ids: q-block row ids
+    (b*heads + h)*nb + i (all rows if None).  Returns (row_ids, o) with
+    o [len(row_ids), 64, D] fp64.
+    """
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, S, heads, D = q.shape
+    nb = S // BLOCK
+    if row_ids is None:
+        row_ids = np.arange(B * heads * nb, dtype=np.int64)
+    row_ids = np.ascontiguousarray(row_ids, dtype=np.int64)
+    kv_nb = np.ascontiguousarray(kv_nb, dtype=np.int32)
+    kv_inds = np.ascontiguousarray(kv_inds, dtype=np.int32)
+    o = np.zeros((row_ids.size, BLOCK, D), np.float64)
+    rc = _load().orc_attention(_ptr(q), _ptr(k), _ptr(v), B, S, heads, D, _ptr(kv_nb),
+                               _ptr(kv_inds), float(scale), _ptr(row_ids), row_ids.size, _ptr(o))
+    if rc != 0:
+        raise ValueError("oracle attention: bad argument")
+    return row_ids, o
+
+
+def rows_to_tokens(o_rows, row_ids, B, S, heads, D):
+    """Scatter [n,64,D] q-block rows into a dense [B,S,heads,D] fp64 array (NaN elsewhere)."""
+    nb = S // BLOCK
+    out = np.full((B, S, heads, D), np.nan)
+    for n, rid in enumerate(np.asarray(row_ids)):
+        b, rem = divmod(int(rid), heads * nb)
+        h, i = divmod(rem, nb)
+        out[b, i * BLOCK:(i + 1) * BLOCK, h, :] = o_rows[n]
+    return out

@@ -1,0 +1,389 @@
+/*
+ * nabla_oracle.c -- plain, slow CPU oracle for the NABLA hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls this file.
+ * Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+ * load it.  It shares no source, header, table or helper with the HIP path.
+ *
+ * What it follows (page titles and sections, no code copied):
+ *   [nabla]  FastVideo API page "nabla": source of nablaT_v2 (map estimation,
+ *            map binarization, BlockMask creation), NablaAttentionImpl.forward
+ *            and the NablaAttentionMetadata fields (sta_mask, P).
+ *   [NABLA]  "NABLA: Neighborhood Adaptive Block-Level Attention" summary page,
+ *            Technical Summary > Methodology (token reordering, pooling,
+ *            reduced attention, CDF thresholding, expansion, STA union).
+ *
+ * Precision readings (the pages run the estimator in the input dtype and do
+ * not fix rounding; these are the readings this oracle and the GPU both take):
+ *   - pool:    fp32, sequential over the 64 tokens of a block, then * 2^-6.
+ *   - score:   fp32, acc = fma(qa[d], ka[d], acc) for d = 0..D-1 from +0,
+ *              then IEEE division by fl32(sqrt(D)); -0 is canonicalised to +0.
+ *   - exp:     nexp(), a Cody-Waite reduction plus a degree-7 Taylor polynomial
+ *              in Horner form with fused multiply-adds; 0 below x = -64.
+ *   - softmax: e_j = nexp(s_j - max s); Z is the exact sum of e_j in 2^-48
+ *              fixed point, rounded to fp32; p_j = e_j / Z (IEEE fp32 division).
+ *   - CDF:     cumulative sums of p in 2^-48 fixed point (exact integer sums),
+ *              compared with fl32(1 - thr) rounded up to the same grid.
+ *   - order:   ascending by (s_j, j); among equal scores the lower block index
+ *              comes first, i.e. is dropped first.
+ *   - the last block in sorted order (the row's arg-max) is always kept.
+ *   - attention: fp64 dense softmax over every key, with disallowed 64x64
+ *              blocks at -inf; scale 1/sqrt(D).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_BLK 64           /* tokens per block: 64 ([nabla] nablaT_v2, map estimation) */
+#define ORC_TILE 8           /* spatial tile edge P = 8: a 1 x 8 x 8 tile holds one block */
+#define ORC_FIX_BITS 48      /* fixed-point grid of the softmax sums: 2^-48 */
+
+/* ------------------------------------------------------------------------- */
+/* threads                                                                    */
+/* ------------------------------------------------------------------------- */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int orc_get_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------- */
+/* O1: fractal flattening ([NABLA] Methodology, "Token Reordering")           */
+/* The tokens of each 8 x 8 spatial patch of one frame become a contiguous    */
+/* run of 64; frames stay in time order; patches go in raster order (patch    */
+/* row, patch column); inside a patch, raster order (row, column).            */
+/* ------------------------------------------------------------------------- */
+int64_t orc_fractal_index(int t, int y, int x, int H, int W) {
+    int Ht = H / ORC_TILE, Wt = W / ORC_TILE;
+    int64_t tile = ((int64_t)t * Ht + y / ORC_TILE) * Wt + x / ORC_TILE;
+    return tile * ORC_BLK + (y % ORC_TILE) * ORC_TILE + (x % ORC_TILE);
+}
+
+/* x, y: one token row = heads*D elements of esize bytes.
+ * inverse == 0: x natural [B][T][H][W][row] -> y fractal [B][S][row]
+ * inverse != 0: x fractal -> y natural. */
+void orc_fractal_permute(const uint8_t *x, uint8_t *y, int64_t esize, int B, int T, int H,
+                         int W, int heads, int D, int inverse) {
+    int64_t row = (int64_t)heads * D * esize;
+    int64_t S = (int64_t)T * H * W;
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < T; ++t)
+            for (int yy = 0; yy < H; ++yy)
+                for (int xx = 0; xx < W; ++xx) {
+                    int64_t nat = (((int64_t)b * T + t) * H + yy) * W + xx;
+                    int64_t fra = (int64_t)b * S + orc_fractal_index(t, yy, xx, H, W);
+                    if (!inverse)
+                        memcpy(y + fra * row, x + nat * row, (size_t)row);
+                    else
+                        memcpy(y + nat * row, x + fra * row, (size_t)row);
+                }
+}
+
+/* ------------------------------------------------------------------------- */
+/* O2: STA block mask ([nabla] NablaAttentionMetadata.sta_mask, "precomputed  */
+/* once per run"; [NABLA] Methodology, "Hybrid Integration with STA").         */
+/* Reading: blocks i, j (tile coordinates (t, ht, wt)) are neighbours when    */
+/* |dt| <= wt, |dh| <= wh and |dw| <= ww; the window is clipped at borders.   */
+/* ------------------------------------------------------------------------- */
+void orc_sta_mask(uint8_t *sta, int Tt, int Ht, int Wt, int win_t, int win_h, int win_w) {
+    int64_t nb = (int64_t)Tt * Ht * Wt;
+    for (int64_t i = 0; i < nb; ++i) {
+        int ti = (int)(i / ((int64_t)Ht * Wt)), hi = (int)((i / Wt) % Ht), wi = (int)(i % Wt);
+        for (int64_t j = 0; j < nb; ++j) {
+            int tj = (int)(j / ((int64_t)Ht * Wt)), hj = (int)((j / Wt) % Ht), wj = (int)(j % Wt);
+            sta[i * nb + j] = (uint8_t)(abs(ti - tj) <= win_t && abs(hi - hj) <= win_h &&
+                                        abs(wi - wj) <= win_w);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* O3: block mean-pool ([nabla] nablaT_v2, map estimation: reshape to blocks  */
+/* of 64 tokens and take the mean).  x [B][S][heads][D] (fp32 values; bf16    */
+/* inputs are widened exactly by the caller) -> xa [B][heads][nb][D].         */
+/* ------------------------------------------------------------------------- */
+void orc_pool(const float *x, float *xa, int B, int S, int heads, int D) {
+    int nb = S / ORC_BLK;
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < heads; ++h)
+            for (int i = 0; i < nb; ++i)
+                for (int d = 0; d < D; ++d) {
+                    float acc = 0.0f;
+                    for (int r = 0; r < ORC_BLK; ++r) {
+                        int64_t tok = (int64_t)b * S + (int64_t)i * ORC_BLK + r;
+                        acc = acc + x[(tok * heads + h) * D + d];
+                    }
+                    xa[(((int64_t)b * heads + h) * nb + i) * D + d] = acc * 0.015625f;
+                }
+}
+
+/* ------------------------------------------------------------------------- */
+/* O4: block scores ([nabla] nablaT_v2: qa @ ka^T, divided by sqrt(D)).       */
+/* qa, ka [B][heads][nb][D] -> s [B][heads][nb][nb].                          */
+/* ------------------------------------------------------------------------- */
+static float orc_score_one(const float *a, const float *k, int D, float sqrt_d) {
+    float acc = 0.0f;
+    for (int d = 0; d < D; ++d) acc = fmaf(a[d], k[d], acc);
+    float s = acc / sqrt_d;
+    return s + 0.0f; /* -0 -> +0 */
+}
+
+void orc_scores(const float *qa, const float *ka, float *s, int B, int heads, int nb, int D) {
+    float sqrt_d = (float)sqrt((double)D);
+    int64_t rows = (int64_t)B * heads * nb;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t bh = r / nb;
+        const float *a = qa + r * D;
+        for (int j = 0; j < nb; ++j)
+            s[r * nb + j] = orc_score_one(a, ka + (bh * nb + j) * D, D, sqrt_d);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* exp used by the softmax: Cody & Waite argument reduction                   */
+/*   n = rint(x log2 e), r = (x - n ln2_hi) - n ln2_lo,                       */
+/* then the Taylor series of e^r to degree 7 in Horner form (fused            */
+/* multiply-add at every step), scaled by 2^n.  Valid for x <= 0; returns 0    */
+/* for x < -64 (those weights fall below the 2^-48 grid anyway).              */
+/* ------------------------------------------------------------------------- */
+float orc_nexp(float x) {
+    if (!(x >= -64.0f)) return 0.0f;
+    const float log2e = 1.44269504088896341f;
+    const float ln2_hi = 0.693145751953125f;      /* 15 significant bits: n*ln2_hi exact */
+    const float ln2_lo = 1.42860682030941723e-6f; /* ln 2 - ln2_hi */
+    float n = rintf(x * log2e);
+    float r = fmaf(-n, ln2_hi, x);
+    r = fmaf(-n, ln2_lo, r);
+    /* e^r = sum_k r^k / k!, k = 0..7 */
+    float p = 1.98412698412698413e-4f; /* 1/5040 */
+    p = fmaf(p, r, 1.38888888888888889e-3f); /* 1/720 */
+    p = fmaf(p, r, 8.33333333333333333e-3f); /* 1/120 */
+    p = fmaf(p, r, 4.16666666666666667e-2f); /* 1/24 */
+    p = fmaf(p, r, 1.66666666666666667e-1f); /* 1/6 */
+    p = fmaf(p, r, 0.5f);
+    p = fmaf(p, r, 1.0f);
+    p = fmaf(p, r, 1.0f);
+    /* 2^n with n in [-93, 0]: a normal float built from its exponent field */
+    int32_t bits = ((int32_t)n + 127) << 23;
+    float two_n;
+    memcpy(&two_n, &bits, sizeof two_n);
+    return p * two_n;
+}
+
+void orc_nexp_vec(const float *x, float *y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = orc_nexp(x[i]);
+}
+
+/* ------------------------------------------------------------------------- */
+/* O5: row softmax ([nabla] nablaT_v2: softmax over the last dimension).      */
+/* e_j = nexp(s_j - m); Z = fl32(sum_j floor(e_j 2^48)) 2^-48; p_j = e_j / Z; */
+/* P_j = floor(p_j 2^48) (the fixed-point weights the CDF adds up).            */
+/* ------------------------------------------------------------------------- */
+static int64_t orc_fix(float v) { /* floor(v * 2^48) for 0 <= v <= 1 */
+    return (int64_t)ldexp((double)v, ORC_FIX_BITS);
+}
+
+void orc_softmax_row(const float *s, int nb, float *e, float *p, int64_t *P, double *Zout) {
+    float m = s[0];
+    for (int j = 1; j < nb; ++j)
+        if (s[j] > m) m = s[j];
+    int64_t ZE = 0;
+    for (int j = 0; j < nb; ++j) {
+        e[j] = orc_nexp(s[j] - m);
+        ZE += orc_fix(e[j]);
+    }
+    float Z = (float)(double)ZE;
+    Z = ldexpf(Z, -ORC_FIX_BITS);
+    for (int j = 0; j < nb; ++j) {
+        p[j] = e[j] / Z;
+        P[j] = orc_fix(p[j]);
+    }
+    if (Zout) *Zout = (double)Z;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O6-O7: sort, cumulative sum, cut, un-sort ([nabla] nablaT_v2, map         */
+/* binarization; [NABLA] Methodology, "CDF Thresholding").                    */
+/* ------------------------------------------------------------------------- */
+typedef struct { float s; int j; } orc_key;
+
+static int orc_key_cmp(const void *a, const void *b) {
+    const orc_key *x = (const orc_key *)a, *y = (const orc_key *)b;
+    if (x->s < y->s) return -1;
+    if (x->s > y->s) return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+/* The cut on the 2^-48 grid: ceil(fl32(1 - thr) * 2^48). */
+int64_t orc_cut_fixed(double thr) {
+    float cut = (float)(1.0 - thr);
+    return (int64_t)ceil(ldexp((double)cut, ORC_FIX_BITS));
+}
+
+/* One row: kept[j] = 1 for kept blocks.  diag (optional, 3 int64):
+ *   diag[0] = i0 (first kept position in sorted order),
+ *   diag[1] = c_{i0-1} (0 when i0 == 0), diag[2] = c_{i0}, both on the 2^-48 grid. */
+void orc_select_row(const float *s, int nb, double thr, uint8_t *kept, int64_t *diag) {
+    float *e = (float *)malloc(sizeof(float) * (size_t)nb);
+    float *p = (float *)malloc(sizeof(float) * (size_t)nb);
+    int64_t *P = (int64_t *)malloc(sizeof(int64_t) * (size_t)nb);
+    orc_key *key = (orc_key *)malloc(sizeof(orc_key) * (size_t)nb);
+    uint8_t *ms = (uint8_t *)malloc((size_t)nb);
+    orc_softmax_row(s, nb, e, p, P, NULL);
+    /* vals, inds = map.sort(-1) */
+    for (int j = 0; j < nb; ++j) { key[j].s = s[j]; key[j].j = j; }
+    qsort(key, (size_t)nb, sizeof(orc_key), orc_key_cmp);
+    /* cvals = cumsum(vals); mask = cvals >= 1 - thr */
+    int64_t CUT = orc_cut_fixed(thr);
+    int64_t c = 0, c_prev = 0, c_at = 0;
+    int i0 = -1;
+    for (int k = 0; k < nb; ++k) {
+        int64_t before = c;
+        c += P[key[k].j];
+        ms[k] = (uint8_t)(c >= CUT);
+        if (ms[k] && i0 < 0) { i0 = k; c_prev = before; c_at = c; }
+    }
+    /* the arg-max block is always kept (exact arithmetic gives c_last = 1) */
+    if (!ms[nb - 1]) {
+        ms[nb - 1] = 1;
+        i0 = nb - 1;
+        c_at = c;
+        c_prev = c - P[key[nb - 1].j];
+    }
+    /* mask = mask.gather(-1, inds.argsort(-1)): back to block order */
+    for (int k = 0; k < nb; ++k) kept[key[k].j] = ms[k];
+    if (diag) { diag[0] = i0; diag[1] = c_prev; diag[2] = c_at; }
+    free(e); free(p); free(P); free(key); free(ms);
+}
+
+/* ------------------------------------------------------------------------- */
+/* O3-O9: the whole estimator.  q, k [B][S][heads][D] fp32 values.            */
+/* sta [nb][nb] (NULL: STA off).  Outputs                                     */
+/*   kv_nb   [B][heads][nb]      number of kept blocks,                       */
+/*   kv_inds [B][heads][nb][nb]  kept block indices ascending, then the       */
+/*                               dropped ones ascending,                      */
+/*   mnabla  [B][heads][nb][nb]  (optional) the mask before the STA union,    */
+/*   diag    [B][heads][nb][3]   (optional) see orc_select_row.               */
+/* Returns 0, or -1 on a bad argument.                                        */
+/* ------------------------------------------------------------------------- */
+int orc_block_mask(const float *q, const float *k, int B, int S, int heads, int D,
+                   const uint8_t *sta, double thr, int32_t *kv_nb, int32_t *kv_inds,
+                   uint8_t *mnabla, int64_t *diag) {
+    if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
+    if (!(thr >= 0.0 && thr <= 1.0)) return -1;
+    int nb = S / ORC_BLK;
+    int64_t nbd = (int64_t)B * heads * nb * D;
+    float *qa = (float *)malloc(sizeof(float) * (size_t)nbd);
+    float *ka = (float *)malloc(sizeof(float) * (size_t)nbd);
+    orc_pool(q, qa, B, S, heads, D);
+    orc_pool(k, ka, B, S, heads, D);
+    float sqrt_d = (float)sqrt((double)D);
+    int64_t rows = (int64_t)B * heads * nb;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t bh = r / nb;
+        int i = (int)(r % nb);
+        float *srow = (float *)malloc(sizeof(float) * (size_t)nb);
+        uint8_t *kept = (uint8_t *)malloc((size_t)nb);
+        for (int j = 0; j < nb; ++j)
+            srow[j] = orc_score_one(qa + r * D, ka + (bh * nb + j) * D, D, sqrt_d);
+        orc_select_row(srow, nb, thr, kept, diag ? diag + r * 3 : NULL);
+        if (mnabla) memcpy(mnabla + r * nb, kept, (size_t)nb);
+        /* mask = logical_or(mask, sta) */
+        if (sta)
+            for (int j = 0; j < nb; ++j) kept[j] = (uint8_t)(kept[j] | (sta[(int64_t)i * nb + j] != 0));
+        /* kv_nb = mask.sum(-1); kv_inds = mask.argsort(descending) */
+        int n = 0;
+        for (int j = 0; j < nb; ++j) n += kept[j];
+        kv_nb[r] = n;
+        int32_t *row = kv_inds + r * nb;
+        int w = 0;
+        for (int j = 0; j < nb; ++j)
+            if (kept[j]) row[w++] = j;
+        for (int j = 0; j < nb; ++j)
+            if (!kept[j]) row[w++] = j;
+        free(srow);
+        free(kept);
+    }
+    free(qa);
+    free(ka);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O10: block-sparse attention as its plain dense definition                  */
+/* ([nabla] NablaAttentionImpl.forward: flex attention with a block mask of   */
+/* full 64 x 64 blocks; [NABLA] Methodology, "Expansion").  For each listed   */
+/* q-block row id = (b*heads + h)*nb + i and each of its 64 query tokens:     */
+/*   z_c = scale * <q, k_c> for every key c whose block is kept, -inf else;   */
+/*   o = sum_c softmax(z)_c v_c, all in fp64.                                 */
+/* o: [nrows][64][D] fp64.  A row whose list is empty yields 0.               */
+/* ------------------------------------------------------------------------- */
+int orc_attention(const float *q, const float *k, const float *v, int B, int S, int heads,
+                  int D, const int32_t *kv_nb, const int32_t *kv_inds, double scale,
+                  const int64_t *row_ids, int64_t nrows, double *o) {
+    if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
+    int nb = S / ORC_BLK;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t rr = 0; rr < nrows; ++rr) {
+        int64_t id = row_ids[rr];
+        if (id < 0 || id >= (int64_t)B * heads * nb) { bad = 1; continue; }
+        int64_t b = id / ((int64_t)heads * nb);
+        int h = (int)((id / nb) % heads);
+        int i = (int)(id % nb);
+        uint8_t *allowed = (uint8_t *)calloc((size_t)nb, 1);
+        int n = kv_nb[id];
+        if (n < 0 || n > nb) { bad = 1; free(allowed); continue; }
+        for (int t = 0; t < n; ++t) {
+            int j = kv_inds[id * nb + t];
+            if (j < 0 || j >= nb) { bad = 1; break; }
+            allowed[j] = 1;
+        }
+        double *z = (double *)malloc(sizeof(double) * (size_t)S);
+        for (int r = 0; r < ORC_BLK; ++r) {
+            int64_t qt = b * S + (int64_t)i * ORC_BLK + r;
+            const float *qr = q + (qt * heads + h) * D;
+            double *orow = o + (rr * ORC_BLK + r) * D;
+            double zmax = -INFINITY;
+            for (int64_t c = 0; c < S; ++c) {
+                if (!allowed[c / ORC_BLK]) { z[c] = -INFINITY; continue; }
+                const float *kc = k + ((b * S + c) * heads + h) * D;
+                double acc = 0.0;
+                for (int d = 0; d < D; ++d) acc += (double)qr[d] * (double)kc[d];
+                z[c] = scale * acc;
+                if (z[c] > zmax) zmax = z[c];
+            }
+            for (int d = 0; d < D; ++d) orow[d] = 0.0;
+            if (zmax == -INFINITY) continue; /* empty list: O = 0 */
+            double sum = 0.0;
+            for (int64_t c = 0; c < S; ++c) {
+                double w = (z[c] == -INFINITY) ? 0.0 : exp(z[c] - zmax);
+                if (w == 0.0) continue;
+                sum += w;
+                const float *vc = v + ((b * S + c) * heads + h) * D;
+                for (int d = 0; d < D; ++d) orow[d] += w * (double)vc[d];
+            }
+            for (int d = 0; d < D; ++d) orow[d] /= sum;
+        }
+        free(z);
+        free(allowed);
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,396 @@
+"""Pins of the CPU oracle to facts the pages and the mathematics fix (CPU only).
+
+Each test ties one oracle function to something other than itself: closed
+forms derived by hand (tests/golden), brute force over subsets, invariants of
+the method, or library routines (libm exp, numpy/torch fp64) on special cases.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_fractal_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FIX = 2.0 ** 48
+
+
+def _rows(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                out.append(line.split())
+    return out
+
+
+# ------------------------------------------------------------------ O1 permute
+def test_fractal_index_golden(orc):
+    rows = _rows("fractal_index.txt")
+    assert len(rows) >= 10
+    for t, y, x, H, W, s in rows:
+        assert orc.fractal_index(int(t), int(y), int(x), int(H), int(W)) == int(s)
+
+
+@pytest.mark.parametrize("T,H,W", [(2, 16, 16), (3, 24, 40), (1, 8, 8)])
+def test_fractal_permutation_is_block_bijection(orc, T, H, W):
+    pos = np.array([[[orc.fractal_index(t, y, x, H, W) for x in range(W)] for y in range(H)]
+                    for t in range(T)])
+    S = T * H * W
+    assert np.array_equal(np.sort(pos.ravel()), np.arange(S))
+    # each 64-token block is exactly one (frame, 8x8 patch)
+    t, y, x = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    blk = pos // 64
+    for b in np.unique(blk):
+        sel = blk == b
+        assert sel.sum() == 64
+        assert len(set(zip(t[sel], y[sel] // 8, x[sel] // 8))) == 1
+    if H == 8 and W == 8:  # one patch per frame: fractal order is the natural order
+        assert np.array_equal(pos.ravel(), np.arange(S))
+
+
+def test_fractal_permute_roundtrip(orc):
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((2, 2, 16, 24, 3, 8)).astype(np.float32)
+    y = orc.fractal_permute(x)
+    back = orc.fractal_permute(y, inverse=True)
+    assert np.array_equal(back, x)
+    # spot-check placement against the index formula
+    B, T, H, W, h, D = x.shape
+    yf = y.reshape(B, T * H * W, h, D)
+    for (b, t, yy, xx) in [(0, 0, 0, 0), (1, 1, 9, 17), (0, 1, 15, 23)]:
+        assert np.array_equal(yf[b, orc.fractal_index(t, yy, xx, H, W)], x[b, t, yy, xx])
+    # dtype-agnostic (bytes): bf16 bit patterns as uint16
+    u = rng.integers(0, 65535, size=(1, 2, 8, 16, 2, 4), dtype=np.uint16)
+    assert np.array_equal(orc.fractal_permute(orc.fractal_permute(u), inverse=True), u)
+
+
+# ------------------------------------------------------------------ O2 STA
+def test_sta_nnz_golden(orc):
+    for name, Tt, Ht, Wt, wt, wh, ww, nnz in _rows("sta_nnz.txt"):
+        m = orc.sta_mask(int(Tt), int(Ht), int(Wt), int(wt), int(wh), int(ww))
+        assert int(m.sum()) == int(nnz), name
+        assert np.array_equal(m, m.T)
+        assert np.all(np.diag(m) == 1)
+
+
+def test_sta_tiny_is_all_ones_and_box_shape(orc):
+    assert orc.sta_mask(2, 2, 2, 1, 1, 1).all()
+    m = orc.sta_mask(5, 4, 6, 1, 0, 2)
+    Tt, Ht, Wt = 5, 4, 6
+    for i in range(Tt * Ht * Wt):
+        ti, hi, wi = i // (Ht * Wt), (i // Wt) % Ht, i % Wt
+        for j in range(Tt * Ht * Wt):
+            tj, hj, wj = j // (Ht * Wt), (j // Wt) % Ht, j % Wt
+            want = abs(ti - tj) <= 1 and hi == hj and abs(wi - wj) <= 2
+            assert m[i, j] == want
+
+
+# ------------------------------------------------------------------ exp
+def test_nexp_against_libm(orc):
+    xs = np.concatenate([np.linspace(-64, 0, 200001, dtype=np.float32),
+                         -np.logspace(-8, 0, 2001).astype(np.float32),
+                         np.array([0.0, -1e-30, -0.5, -1.0, -63.99], np.float32)])
+    y = orc.nexp(xs).astype(np.float64)
+    ref = np.array([math.exp(float(v)) for v in xs])
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    assert np.max(np.abs(y - ref) / ulp) <= 1.0
+    assert orc.nexp(np.array([0.0], np.float32))[0] == 1.0
+    assert np.all(orc.nexp(np.array([-64.5, -100.0, -1e30, -np.inf], np.float32)) == 0.0)
+    ys = orc.nexp(np.sort(xs))
+    assert np.all(np.diff(ys) >= 0)  # monotone
+
+
+# ------------------------------------------------------------------ O3 pool
+def test_pool_constant_and_bound(orc):
+    x = np.full((1, 128, 2, 8), 0.3, np.float32)
+    assert np.all(orc.pool(x) == np.float32(0.3) * 1) or np.allclose(orc.pool(x), 0.3, rtol=0, atol=6e-8)
+    for c in (1.0, -2.5, 0.125, 3.0):  # exactly representable partial sums
+        assert np.all(orc.pool(np.full((1, 128, 2, 8), c, np.float32)) == np.float32(c))
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((2, 256, 3, 16)).astype(np.float32)
+    got = orc.pool(x).astype(np.float64)
+    ref = x.astype(np.float64).reshape(2, 4, 64, 3, 16).mean(axis=2).transpose(0, 2, 1, 3)
+    bound = 64 * 2.0 ** -24 * np.abs(x.astype(np.float64)).reshape(2, 4, 64, 3, 16).mean(
+        axis=2).transpose(0, 2, 1, 3)
+    assert np.all(np.abs(got - ref) <= bound + 1e-12)
+    # block index planted in every token of the block comes back exactly
+    y = np.zeros((1, 256, 1, 4), np.float32)
+    for i in range(4):
+        y[0, 64 * i:64 * (i + 1)] = i
+    assert np.array_equal(orc.pool(y)[0, 0, :, 0], np.arange(4, dtype=np.float32))
+
+
+# ------------------------------------------------------------------ O4 scores
+def test_scores_against_fp64(orc):
+    rng = np.random.default_rng(2)
+    for D in (64, 128):
+        qa = rng.standard_normal((1, 2, 16, D)).astype(np.float32)
+        ka = rng.standard_normal((1, 2, 16, D)).astype(np.float32)
+        s = orc.scores(qa, ka).astype(np.float64)
+        ref = np.einsum("bhid,bhjd->bhij", qa.astype(np.float64), ka.astype(np.float64)) / math.sqrt(D)
+        mag = np.einsum("bhid,bhjd->bhij", np.abs(qa).astype(np.float64),
+                        np.abs(ka).astype(np.float64)) / math.sqrt(D)
+        assert np.all(np.abs(s - ref) <= (D + 2) * 2.0 ** -24 * mag + 1e-30)
+    s0 = orc.scores(np.zeros((1, 1, 4, 64), np.float32), ka[:, :1, :4, :64])
+    assert np.all(s0 == 0) and not np.any(np.signbit(s0))
+
+
+# ------------------------------------------------------------------ O5 softmax
+def test_softmax_row(orc):
+    rng = np.random.default_rng(3)
+    s = (rng.standard_normal(960) * 2).astype(np.float32)
+    e, p, P, Z = orc.softmax_row(s)
+    ref = np.exp(s.astype(np.float64) - s.max())
+    ref /= ref.sum()
+    assert abs(p.astype(np.float64).sum() - 1.0) <= 960 * 2.0 ** -24
+    # error sources: fp32 rounding of s - max (relative |s - max| u in exp), exp (1 ulp),
+    # Z and the division (1 ulp each)
+    x = np.abs(s.astype(np.float64) - s.max())
+    assert np.all(np.abs(p - ref) <= (x + 4.0) * 2.0 ** -24 * ref + 1e-45)
+    assert np.array_equal(P, np.floor(p.astype(np.float64) * FIX).astype(np.int64))
+    assert e[np.argmax(s)] == 1.0
+    for nb in (8, 128, 1024):  # uniform: p = 1/nb exactly
+        _, pu, Pu, Zu = orc.softmax_row(np.zeros(nb, np.float32))
+        assert np.all(pu == np.float32(1.0 / nb)) and Zu == nb
+        assert np.all(Pu == int(FIX) // nb)
+
+
+# ------------------------------------------------------------------ O6-O7 selection
+def _cut_fixed(thr):
+    return math.ceil(float(np.float32(1.0 - thr)) * FIX)
+
+
+def test_cut_fixed(orc):
+    for thr in (0.0, 0.5, 0.7, 0.9, 0.95, 1.0, 0.123456):
+        assert orc.cut_fixed(thr) == _cut_fixed(thr)
+    assert orc.cut_fixed(1.0) == 0
+    assert orc.cut_fixed(0.0) == int(FIX)
+
+
+def test_uniform_keep_golden(orc):
+    for nb, thr, kept in _rows("uniform_keep.txt"):
+        nb, thr, kept = int(nb), float(thr), int(kept)
+        k, diag = orc.select_row(np.zeros(nb, np.float32), thr)
+        assert int(k.sum()) == kept, (nb, thr)
+        assert np.all(k[nb - kept:] == 1) and np.all(k[:nb - kept] == 0)
+        assert diag[0] == nb - kept
+
+
+def _brute_force_kept(P, CUT):
+    """Kept set by exhaustive search: the dropped set is the largest set of blocks whose
+    mass stays below the cut (at most nb-1 blocks); among those, the one of least mass."""
+    nb = len(P)
+    best = ()  # CUT == 0: even the empty set is not below the cut, nothing is dropped
+    for r in range(nb - 1, -1, -1):
+        cands = []
+        for D in itertools.combinations(range(nb), r):
+            m = sum(int(P[j]) for j in D)
+            if m < CUT:
+                cands.append((m, D))
+        if cands:
+            cands.sort()
+            if len(cands) > 1 and cands[0][0] == cands[1][0]:
+                return None  # ambiguous without the index tie-break
+            best = cands[0][1]
+            break
+    kept = np.ones(nb, np.uint8)
+    kept[list(best)] = 0
+    return kept
+
+
+def test_selection_brute_force(orc):
+    rng = np.random.default_rng(4)
+    checked = 0
+    for trial in range(60):
+        nb = int(rng.integers(2, 11))
+        s = (rng.standard_normal(nb) * rng.uniform(0.1, 3.0)).astype(np.float32)
+        thr = float(rng.choice([0.0, 0.3, 0.5, 0.7, 0.9, 0.95, 1.0, rng.uniform()]))
+        _, _, P, _ = orc.softmax_row(s)
+        want = _brute_force_kept(P, _cut_fixed(thr))
+        if want is None:
+            continue
+        got, _ = orc.select_row(s, thr)
+        assert np.array_equal(got, want), (nb, thr, s)
+        checked += 1
+    assert checked >= 50
+
+
+def test_selection_invariants(orc):
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        nb = int(rng.choice([8, 64, 128, 960]))
+        s = (rng.standard_normal(nb) * rng.uniform(0.2, 4.0)).astype(np.float32)
+        _, p, P, _ = orc.softmax_row(s)
+        prev = None
+        for thr in (0.0, 0.5, 0.7, 0.9, 0.95, 1.0):
+            kept, diag = orc.select_row(s, thr)
+            CUT = _cut_fixed(thr)
+            dropped = int(P[kept == 0].sum())
+            assert kept[np.argmax(s)] == 1 and kept.sum() >= 1
+            assert dropped < CUT or kept.sum() == 1 or (kept == 1).all()
+            if kept.sum() > 1 or dropped < CUT:
+                # minimality: adding the smallest kept block to the dropped set reaches the cut
+                kk = np.flatnonzero(kept)
+                smallest = kk[np.lexsort((kk, s[kk]))[0]]
+                assert dropped + int(P[smallest]) >= CUT or kept.sum() == 1
+            # kept blocks all score at least as high as every dropped block
+            if (kept == 0).any():
+                assert s[kept == 1].min() >= s[kept == 0].max()
+            # kept probability mass >= thr (up to the fp32 rounding of p)
+            assert p[kept == 1].astype(np.float64).sum() >= thr - nb * 2.0 ** -23
+            if prev is not None:
+                assert np.all(kept >= prev)  # monotone in thr
+            prev = kept
+        assert orc.select_row(s, 1.0)[0].all()
+
+
+def test_selection_dominant_block(orc):
+    nb, D = 128, 64
+    rng = np.random.default_rng(6)
+    qa = rng.standard_normal((1, 1, nb, D)).astype(np.float32)
+    ka = 0.01 * rng.standard_normal((1, 1, nb, D)).astype(np.float32)
+    ka[0, 0, 37] = 40.0 * qa[0, 0, 5] / np.linalg.norm(qa[0, 0, 5])
+    s = orc.scores(qa, ka)[0, 0, 5]
+    kept, _ = orc.select_row(s, 0.9)
+    assert np.flatnonzero(kept).tolist() == [37]
+
+
+def test_selection_matches_fp64_transcription(orc):
+    """A float64 torch transcription of the binarization steps, with a stable sort."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    nb = 128
+    s = (rng.standard_normal((64, nb)) * 1.5).astype(np.float32)
+    for thr in (0.5, 0.9):
+        m = torch.softmax(torch.from_numpy(s).double(), dim=-1)
+        vals, inds = torch.sort(m, dim=-1, stable=True)
+        c = torch.cumsum(vals, dim=-1)
+        mask = (c >= float(np.float32(1 - thr))).int()
+        mask = mask.gather(-1, torch.argsort(inds, dim=-1)).numpy()
+        for r in range(s.shape[0]):
+            kept, diag = orc.select_row(s[r], thr)
+            c_prev, c_at = diag[1] / FIX, diag[2] / FIX
+            cut = float(np.float32(1 - thr))
+            if min(abs(c_prev - cut), abs(c_at - cut)) < 1e-6:
+                continue
+            assert np.array_equal(kept, mask[r].astype(np.uint8)), (thr, r)
+
+
+# ------------------------------------------------------------------ O3-O9 estimator
+def test_block_mask_structure(orc):
+    w = synth.WORKLOADS["tiny"]
+    q, k, _ = synth.make_qkv(w)
+    qf = orc.fractal_permute(q).reshape(w.B, w.S, w.heads, w.D)
+    kf = orc.fractal_permute(k).reshape(w.B, w.S, w.heads, w.D)
+    sta = orc.sta_mask(*w.tiles, 0, 0, 0)  # diagonal only
+    for thr in (0.5, 0.9):
+        out = orc.block_mask(qf, kf, sta, thr, want_nabla=True)
+        nb = w.nb
+        for b, h, i in itertools.product(range(w.B), range(w.heads), range(nb)):
+            n = out["kv_nb"][b, h, i]
+            row = out["kv_inds"][b, h, i]
+            M = out["mnabla"][b, h, i] | sta[i]
+            assert n == M.sum() >= sta[i].sum()
+            assert np.array_equal(row[:n], np.flatnonzero(M))
+            assert np.array_equal(np.sort(row), np.arange(nb))
+        # the estimator's per-row result equals select_row on the oracle's own scores
+        qa, ka = orc.pool(qf), orc.pool(kf)
+        s = orc.scores(qa, ka)
+        for h, i in itertools.product(range(w.heads), range(nb)):
+            kept, diag = orc.select_row(s[0, h, i], thr)
+            assert np.array_equal(kept, out["mnabla"][0, h, i])
+            assert np.array_equal(diag, out["diag"][0, h, i])
+    # thr = 1 keeps everything; all-ones STA (the tiny window) keeps everything
+    assert np.all(orc.block_mask(qf, kf, None, 1.0)["kv_nb"] == w.nb)
+    assert np.all(orc.block_mask(qf, kf, orc.sta_mask(*w.tiles, *w.sta), 0.9)["kv_nb"] == w.nb)
+
+
+def test_block_mask_rejects_bad_args(orc):
+    q = np.zeros((1, 100, 1, 64), np.float32)
+    with pytest.raises(ValueError):
+        orc.block_mask(q, q, None, 0.9)
+    q = np.zeros((1, 128, 1, 64), np.float32)
+    for thr in (-0.1, 1.5, float("nan")):
+        with pytest.raises(ValueError):
+            orc.block_mask(q, q, None, thr)
+
+
+# ------------------------------------------------------------------ O10 attention
+def _sdpa64(q, k, v, mask=None):
+    torch = pytest.importorskip("torch")
+    # [B,S,h,D] -> [B,h,S,D] in float64 on the CPU
+    Q, K, V = (torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).double()
+               for a in (q, k, v))
+    m = None if mask is None else torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=m)
+    return o.numpy().transpose(0, 2, 1, 3)
+
+
+def _tiny_fractal(orc):
+    w = synth.WORKLOADS["tiny"]
+    q, k, v = synth.make_qkv(w)
+    f = lambda a: orc.fractal_permute(a).reshape(w.B, w.S, w.heads, w.D)
+    return w, f(q), f(k), f(v)
+
+
+def test_attention_full_equals_sdpa(orc):
+    w, q, k, v = _tiny_fractal(orc)
+    full_nb = np.full((w.B, w.heads, w.nb), w.nb, np.int32)
+    full_inds = np.broadcast_to(np.arange(w.nb, dtype=np.int32), (w.B, w.heads, w.nb, w.nb))
+    ids, o = orc.attention(q, k, v, full_nb, full_inds)
+    got = orc.rows_to_tokens(o, ids, w.B, w.S, w.heads, w.D)
+    ref = _sdpa64(q, k, v)
+    assert np.max(np.abs(got - ref)) < 1e-12
+    # the estimator with thr = 1, and with the all-ones tiny STA, both give full attention
+    for sta, thr in ((None, 1.0), (orc.sta_mask(*w.tiles, *w.sta), 0.9)):
+        m = orc.block_mask(q, k, sta, thr)
+        ids, o = orc.attention(q, k, v, m["kv_nb"], m["kv_inds"])
+        assert np.max(np.abs(orc.rows_to_tokens(o, ids, w.B, w.S, w.heads, w.D) - ref)) < 1e-12
+
+
+def test_attention_sta_only_equals_window_sdpa(orc):
+    rng = np.random.default_rng(8)
+    B, T, H, W, h, D = 1, 3, 16, 16, 2, 64
+    q, k, v = (rng.standard_normal((B, T, H, W, h, D)).astype(np.float32) for _ in range(3))
+    f = lambda a: orc.fractal_permute(a).reshape(B, T * H * W, h, D)
+    q, k, v = f(q), f(k), f(v)
+    S, nb = T * H * W, T * H * W // 64
+    sta = orc.sta_mask(T, 2, 2, 1, 0, 0)
+    kv_nb = np.broadcast_to(sta.sum(1).astype(np.int32), (B, h, nb)).copy()
+    kv_inds = np.zeros((B, h, nb, nb), np.int32)
+    for i in range(nb):
+        sel = np.flatnonzero(sta[i])
+        kv_inds[:, :, i, :len(sel)] = sel
+    ids, o = orc.attention(q, k, v, kv_nb, kv_inds)
+    got = orc.rows_to_tokens(o, ids, B, S, h, D)
+    tok_mask = np.kron(sta.astype(bool), np.ones((64, 64), bool))  # [S, S]
+    ref = _sdpa64(q, k, v, tok_mask)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_attention_special_cases(orc):
+    rng = np.random.default_rng(9)
+    B, S, h, D = 1, 256, 1, 64
+    nb = S // 64
+    q = rng.standard_normal((B, S, h, D)).astype(np.float32)
+    k = rng.standard_normal((B, S, h, D)).astype(np.float32)
+    v = rng.standard_normal((B, S, h, D)).astype(np.float32)
+    kv_nb = np.array([[[2, 1, 0, 3]]], np.int32)
+    kv_inds = np.array([[[[3, 1, 0, 2], [2, 0, 1, 3], [0, 1, 2, 3], [0, 1, 3, 2]]]], np.int32)
+    ids, o = orc.attention(q, k, v, kv_nb, kv_inds)
+    # V constant -> O constant
+    _, oc = orc.attention(q, k, np.full_like(v, 0.75), kv_nb, kv_inds)
+    assert np.allclose(oc[[0, 1, 3]], 0.75, atol=1e-14)
+    # empty list -> O = 0
+    assert np.all(o[2] == 0) and np.all(oc[2] == 0)
+    # convex combination of the allowed V rows
+    for r, n in ((0, 2), (1, 1), (3, 3)):
+        rows = np.concatenate([v[0, 64 * j:64 * (j + 1), 0] for j in kv_inds[0, 0, r, :n]])
+        assert np.all(o[r] >= rows.min(0) - 1e-12) and np.all(o[r] <= rows.max(0) + 1e-12)
+    # Q = 0 and one kept block -> mean of that block's V
+    _, o0 = orc.attention(np.zeros_like(q), k, v, kv_nb, kv_inds)
+    assert np.allclose(o0[1], v[0, 128:192, 0].astype(np.float64).mean(0)[None, :], atol=1e-14)
