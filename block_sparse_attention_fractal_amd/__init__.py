@@ -1,0 +1,178 @@
+"""MI355X-native NABLA hot path.
+
+Python binding of ``libnabla.so`` (``include/nabla.h``): argument marshalling
+only.  Every step runs in the library's HIP kernels; PyTorch provides device
+memory and the current stream.  There is no CPU path: a missing library or a
+tensor that is not on the GPU raises.
+
+Calls (same names as the C ABI):
+  nabla_fractal_permute(x, grid=None, inverse=False)
+  nabla_sta_mask(tiles, window, device)
+  nabla_block_mask(q, k, sta, thr=0.9)          -> (kv_nb, kv_inds)
+  nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False) -> o
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = ["nabla_fractal_permute", "nabla_sta_mask", "nabla_block_mask",
+           "nabla_block_mask_workspace", "nabla_sparse_attn_fwd", "NablaError", "lib",
+           "LIB_PATH", "STATUS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnabla.so")
+STATUS = {0: "NABLA_OK", 1: "NABLA_ERR_INVALID_ARG", 2: "NABLA_ERR_UNSUPPORTED",
+          3: "NABLA_ERR_WORKSPACE", 4: "NABLA_ERR_HIP"}
+_FP32, _BF16 = 0, 1
+BLOCK = 64
+
+_lib = None
+
+
+class NablaError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (what, STATUS.get(status, status),
+                                          lib().nabla_status_string(status).decode()))
+
+
+def lib():
+    """The loaded libnabla.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libnabla.so is not built (%s); run "
+                           "`python -m block_sparse_attention_fractal_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, D, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_size_t
+    L.nabla_abi_version.restype = I
+    L.nabla_status_string.argtypes = [I]
+    L.nabla_status_string.restype = ctypes.c_char_p
+    L.nabla_fractal_permute.argtypes = [P, P, I, I, I, I, I, I, I, I, P]
+    L.nabla_fractal_permute.restype = I
+    L.nabla_sta_mask.argtypes = [P, I, I, I, I, I, I, P]
+    L.nabla_sta_mask.restype = I
+    L.nabla_block_mask_workspace.argtypes = [I, I, I, I]
+    L.nabla_block_mask_workspace.restype = Z
+    L.nabla_block_mask.argtypes = [P, P, I, I, I, I, I, P, D, P, P, P, Z, P]
+    L.nabla_block_mask.restype = I
+    L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, P, P]
+    L.nabla_sparse_attn_fwd.restype = I
+    _lib = L
+    return L
+
+
+def _check(status, what):
+    if status != 0:
+        raise NablaError(status, what)
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a GPU tensor (no CPU path)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _FP32
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def nabla_fractal_permute(x, grid=None, inverse=False, out=None):
+    """Fractal token order (8 x 8 patches -> runs of 64 tokens).
+
+    Forward: x [B, T, H, W, heads, D] -> [B, T*H*W, heads, D].
+    Inverse: x [B, S, heads, D] with grid=(T, H, W) -> [B, T, H, W, heads, D].
+    """
+    _dev(x, "x")
+    if not inverse:
+        B, T, H, W, heads, D = x.shape
+        shape = (B, T * H * W, heads, D)
+    else:
+        B, S, heads, D = x.shape
+        T, H, W = grid
+        if T * H * W != S:
+            raise ValueError("grid %s does not match S=%d" % (grid, S))
+        shape = (B, T, H, W, heads, D)
+    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else _dev(out, "out")
+    _check(lib().nabla_fractal_permute(_p(x), _p(y), _dtype_code(x), B, T, H, W, heads, D,
+                                       int(bool(inverse)), _stream(x)), "nabla_fractal_permute")
+    return y
+
+
+def nabla_sta_mask(tiles, window, device="cuda"):
+    """STA block mask [nb, nb] uint8 for a (Tt, Ht, Wt) tile grid and (win_t, win_h, win_w)."""
+    Tt, Ht, Wt = tiles
+    nb = Tt * Ht * Wt
+    sta = torch.empty((nb, nb), dtype=torch.uint8, device=device)
+    _check(lib().nabla_sta_mask(_p(sta), Tt, Ht, Wt, *window, _stream(sta)), "nabla_sta_mask")
+    return sta
+
+
+def nabla_block_mask_workspace(B, S, heads, D):
+    return lib().nabla_block_mask_workspace(B, S, heads, D)
+
+
+def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None):
+    """NABLA estimator: q, k [B, S, heads, D] -> (kv_nb [B,heads,nb] int32, kv_inds [B,heads,nb,nb] int32).
+
+    The first kv_nb entries of each kv_inds row are the kept blocks, ascending.
+    """
+    _dev(q, "q")
+    _dev(k, "k")
+    if q.shape != k.shape or q.dtype != k.dtype:
+        raise ValueError("q and k must match in shape and dtype")
+    B, S, heads, D = q.shape
+    nb = S // BLOCK
+    if sta is not None:
+        _dev(sta, "sta")
+        if sta.dtype != torch.uint8 or sta.numel() != nb * nb:
+            raise ValueError("sta must be uint8 with nb*nb = %d elements" % (nb * nb))
+    need = lib().nabla_block_mask_workspace(B, S, heads, D)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
+                                                             device=q.device)
+    if out is None:
+        kv_nb = torch.empty((B, heads, nb), dtype=torch.int32, device=q.device)
+        kv_inds = torch.empty((B, heads, nb, nb), dtype=torch.int32, device=q.device)
+    else:
+        kv_nb, kv_inds = out
+    _check(lib().nabla_block_mask(_p(q), _p(k), _dtype_code(q), B, S, heads, D, _p(sta),
+                                  float(thr), _p(kv_nb), _p(kv_inds), _p(ws), ws.numel(),
+                                  _stream(q)), "nabla_block_mask")
+    return kv_nb, kv_inds
+
+
+def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, out=None):
+    """Block-sparse attention over the listed 64 x 64 blocks: o [B, S, heads, D] (q's dtype)."""
+    if causal:
+        raise ValueError("NABLA attention does not support causal masking")
+    for name, t in (("q", q), ("k", k), ("v", v), ("kv_nb", kv_nb), ("kv_inds", kv_inds)):
+        _dev(t, name)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must match in shape and dtype")
+    if kv_nb.dtype != torch.int32 or kv_inds.dtype != torch.int32:
+        raise TypeError("kv_nb and kv_inds must be int32")
+    B, S, heads, D = q.shape
+    nb = S // BLOCK
+    if kv_nb.numel() != B * heads * nb or kv_inds.numel() != B * heads * nb * nb:
+        raise ValueError("kv lists do not match q's shape")
+    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    _check(lib().nabla_sparse_attn_fwd(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads, D,
+                                       _p(kv_nb), _p(kv_inds),
+                                       0.0 if scale is None else float(scale), _p(o),
+                                       _stream(q)), "nabla_sparse_attn_fwd")
+    return o

@@ -1,0 +1,419 @@
+// block_mask.hip -- the NABLA block-mask estimator on gfx950.
+//
+// Follows the "nabla" page (FastVideo), nablaT_v2: map estimation (64-token
+// mean pooling of q and k, qa @ ka^T / sqrt(D), row softmax), map binarization
+// (ascending sort, cumulative sum, keep where the cumulative value reaches
+// 1 - thr, back to block order), the STA union and the BlockMask lists
+// (kv_nb = kept count, kv_inds = kept indices first); and the NABLA summary
+// page, Technical Summary > Methodology ("Adaptive Mask Construction",
+// "Hybrid Integration with STA").
+//
+// Precision: fp32 with a fixed order of every rounding step, so the integer
+// outputs are reproducible bit for bit:
+//   pool   sequential fp32 sum over the 64 tokens of a block, then * 2^-6;
+//   score  acc = fma(qa[d], ka[d], acc), d = 0..D-1 from +0, then / fl32(sqrt D);
+//          -0 becomes +0;
+//   exp    Cody-Waite reduction n = rint(x log2 e), r = x - n ln2 (two-part
+//          constant), degree-7 Taylor polynomial in Horner form with fma, times
+//          2^n; 0 below x = -64;
+//   soft   Z = sum of floor(e_j 2^48) (exact integer), rounded to fp32 via
+//          double, times 2^-48; p_j = e_j / Z; P_j = floor(p_j 2^48);
+//   order  ascending by (s_j, j); the cumulative mass is an exact integer sum,
+//          so the first kept position does not depend on summation order.
+// The row's arg-max block is always kept.
+//
+// Kernels
+//   pool_kernel    HBM-bound: each workgroup reads the 64 token rows of one
+//                  block of q or k once (16-byte coalesced loads) and writes
+//                  heads*D fp32 means.
+//   select_kernel  one workgroup (512 lanes) per (b, head, R query blocks):
+//                  R x nb scores on the fp32 VALU (bit-exact order; MFMA would
+//                  not fix the order), then per row: max, exp, Z, a
+//                  histogram-refined search for the cut key over the 64-bit
+//                  keys (orderable(s) << 12 | j) with exact integer masses, the
+//                  STA union, and a ballot compaction of the kept indices.
+#include "nabla_device.h"
+#include "nabla_launch.h"
+
+namespace nabla {
+
+// ---------------------------------------------------------------- pool
+// grid (nb, B, 2): z = 0 pools q into qa, z = 1 pools k into ka.
+template <typename Tin>
+__global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
+                                                   const Tin *__restrict__ k,
+                                                   float *__restrict__ qa,
+                                                   float *__restrict__ ka, int S, int heads,
+                                                   int D) {
+    constexpr int EPC = 16 / sizeof(Tin);  // elements per 16-byte chunk
+    const int nb = S / kBlock;
+    const int i = blockIdx.x, b = blockIdx.y;
+    const Tin *x = blockIdx.z ? k : q;
+    float *xa = blockIdx.z ? ka : qa;
+    const int row_elems = heads * D;
+    const int nchunks = row_elems / EPC;
+    const Tin *base = x + ((int64_t)b * S + (int64_t)i * kBlock) * row_elems;
+    for (int ch = threadIdx.x; ch < nchunks; ch += 256) {
+        float acc[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+        const Tin *p = base + ch * EPC;
+        // 16 rows in flight per lane, then add them in token order
+        for (int r0 = 0; r0 < kBlock; r0 += 16) {
+            uint4 raw[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                raw[u] = *reinterpret_cast<const uint4 *>(p + (int64_t)(r0 + u) * row_elems);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if constexpr (sizeof(Tin) == 2) {
+                    const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[2 * e] = acc[2 * e] + __uint_as_float(wd[e] << 16);
+                        acc[2 * e + 1] = acc[2 * e + 1] + __uint_as_float(wd[e] & 0xffff0000u);
+                    }
+                } else {
+                    acc[0] = acc[0] + __uint_as_float(raw[u].x);
+                    acc[1] = acc[1] + __uint_as_float(raw[u].y);
+                    acc[2] = acc[2] + __uint_as_float(raw[u].z);
+                    acc[3] = acc[3] + __uint_as_float(raw[u].w);
+                }
+            }
+        }
+        const int el = ch * EPC;
+        const int h = el / D, d = el - h * D;
+        float *out = xa + (((int64_t)b * heads + h) * nb + i) * D + d;
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4)
+            *reinterpret_cast<float4 *>(out + e) =
+                make_float4(acc[e] * 0.015625f, acc[e + 1] * 0.015625f, acc[e + 2] * 0.015625f,
+                            acc[e + 3] * 0.015625f);
+    }
+}
+
+// ---------------------------------------------------------------- select helpers
+__device__ __forceinline__ float nabla_exp(float x) {
+    if (!(x >= -64.0f)) return 0.0f;
+    const float log2e = 1.44269504088896341f;
+    const float ln2_hi = 0.693145751953125f;
+    const float ln2_lo = 1.42860682030941723e-6f;
+    const float n = __builtin_rintf(x * log2e);
+    float r = __builtin_fmaf(-n, ln2_hi, x);
+    r = __builtin_fmaf(-n, ln2_lo, r);
+    float p = 1.98412698412698413e-4f;
+    p = __builtin_fmaf(p, r, 1.38888888888888889e-3f);
+    p = __builtin_fmaf(p, r, 8.33333333333333333e-3f);
+    p = __builtin_fmaf(p, r, 4.16666666666666667e-2f);
+    p = __builtin_fmaf(p, r, 1.66666666666666667e-1f);
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    const float two_n = __int_as_float(((int)n + 127) << 23);
+    return p * two_n;
+}
+
+// Monotone map of finite floats to unsigned ints (callers pass no -0).
+__device__ __forceinline__ uint32_t f32_orderable(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_orderable(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+// floor(v * 2^48) for 0 <= v <= 1 (exact through double).
+__device__ __forceinline__ int64_t fix48(float v) { return (int64_t)((double)v * 0x1p48); }
+
+template <int NW>
+struct SelectShared {
+    int64_t hmass[1024];
+    uint64_t hkey[1024];
+    int hcnt[1024];
+    uint64_t red_min[NW], red_max[NW];
+    int64_t red_sum[NW];
+    int64_t wsum[NW];
+    int sel_bin, sel_cnt;
+    int64_t sel_below;
+    uint64_t sel_key;
+};
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const uint64_t o = shfl_xor_u64(v, m);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const uint64_t o = shfl_xor_u64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += (int64_t)shfl_xor_u64((uint64_t)v, m);
+    return v;
+}
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t o = (int64_t)shfl_up_u64((uint64_t)v, d);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------- select
+// grid (ceil(nb / R), B*heads); 512 lanes; lane t owns columns j = c*512 + t, c < CPT.
+template <int D, int CPT, int R>
+__global__ __launch_bounds__(512) void select_kernel(const float *__restrict__ qa,
+                                                     const float *__restrict__ ka, int nb,
+                                                     const uint8_t *__restrict__ sta,
+                                                     float sqrt_d, int64_t cut,
+                                                     int32_t *__restrict__ kv_nb,
+                                                     int32_t *__restrict__ kv_inds) {
+    constexpr int NT = 512, NW = NT / 64;
+    __shared__ __attribute__((aligned(16))) float qs[R][D];
+    __shared__ SelectShared<NW> sh;
+    __shared__ int ccount[CPT][NW];
+
+    const int bh = blockIdx.y;
+    const int row0 = blockIdx.x * R;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int e = tid; e < R * D; e += NT) {
+        const int r = e / D, d = e - r * D;
+        qs[r][d] = (row0 + r < nb) ? qa[((int64_t)bh * nb + row0 + r) * D + d] : 0.0f;
+    }
+    __syncthreads();
+
+    // ---- scores: acc[r][c] = sum_d fma order, d ascending
+    float acc[R][CPT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0f;
+    const float *kab = ka + (int64_t)bh * nb * D;
+    for (int d = 0; d < D; d += 4) {
+        float4 kv[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int j = c * NT + tid;
+            kv[c] = (j < nb) ? *reinterpret_cast<const float4 *>(kab + (int64_t)j * D + d)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float4 q4 = *reinterpret_cast<const float4 *>(&qs[r][d]);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                acc[r][c] = __builtin_fmaf(q4.x, kv[c].x, acc[r][c]);
+                acc[r][c] = __builtin_fmaf(q4.y, kv[c].y, acc[r][c]);
+                acc[r][c] = __builtin_fmaf(q4.z, kv[c].z, acc[r][c]);
+                acc[r][c] = __builtin_fmaf(q4.w, kv[c].w, acc[r][c]);
+            }
+        }
+    }
+
+    // ---- per row selection
+#pragma unroll 1
+    for (int r = 0; r < R; ++r) {
+        const int i = row0 + r;
+        if (i >= nb) break;  // uniform over the workgroup
+        const int64_t row = (int64_t)bh * nb + i;
+
+        float s[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            float a = 0.0f;
+#pragma unroll
+            for (int rr = 0; rr < R; ++rr)
+                if (rr == r) a = acc[rr][c];
+            s[c] = a / sqrt_d + 0.0f;
+        }
+        bool valid[CPT];
+        uint64_t key[CPT];
+        uint64_t kmin = ~0ull, kmax = 0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int j = c * NT + tid;
+            valid[c] = j < nb;
+            key[c] = ((uint64_t)f32_orderable(s[c]) << 12) | (uint64_t)j;
+            if (valid[c]) {
+                kmin = key[c] < kmin ? key[c] : kmin;
+                kmax = key[c] > kmax ? key[c] : kmax;
+            }
+        }
+        kmin = wave_min_u64(kmin);
+        kmax = wave_max_u64(kmax);
+        if (lane == 0) { sh.red_min[wave] = kmin; sh.red_max[wave] = kmax; }
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            kmin = sh.red_min[w] < kmin ? sh.red_min[w] : kmin;
+            kmax = sh.red_max[w] > kmax ? sh.red_max[w] : kmax;
+        }
+        const float smax = f32_from_orderable((uint32_t)(kmax >> 12));
+
+        // softmax weights on the 2^-48 grid
+        float e[CPT];
+        int64_t esum = 0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            e[c] = valid[c] ? nabla_exp(s[c] - smax) : 0.0f;
+            esum += fix48(e[c]);
+        }
+        esum = wave_sum_i64(esum);
+        if (lane == 0) sh.red_sum[wave] = esum;
+        __syncthreads();
+        int64_t ze = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) ze += sh.red_sum[w];
+        const float Z = (float)(double)ze * 0x1p-48f;
+        int64_t P[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? fix48(e[c] / Z) : 0;
+
+        // cut key T: the smallest key whose inclusive prefix mass reaches cut
+        uint64_t T;
+        if (cut <= 0) {
+            T = kmin;
+        } else {
+            uint64_t lo = kmin, hi = kmax;
+            int64_t below = 0;
+            for (;;) {
+                const uint64_t range = hi - lo;
+                const int shift = range < 1024 ? 0 : (64 - __clzll((long long)range) - 10);
+                for (int bn = tid; bn < 1024; bn += NT) {
+                    sh.hmass[bn] = 0;
+                    sh.hcnt[bn] = 0;
+                    sh.hkey[bn] = 0;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    if (valid[c] && key[c] >= lo && key[c] <= hi) {
+                        const int bn = (int)((key[c] - lo) >> shift);
+                        atomicAdd((unsigned long long *)&sh.hmass[bn], (unsigned long long)P[c]);
+                        atomicAdd(&sh.hcnt[bn], 1);
+                        atomicMax((unsigned long long *)&sh.hkey[bn], (unsigned long long)key[c]);
+                    }
+                }
+                __syncthreads();
+                if (tid == 0) sh.sel_bin = -1;
+                const int64_t m0 = sh.hmass[2 * tid], m1 = sh.hmass[2 * tid + 1];
+                const int64_t incl = wave_incl_scan_i64(m0 + m1, lane);
+                if (lane == 63) sh.wsum[wave] = incl;
+                __syncthreads();
+                int64_t before = below + incl - (m0 + m1);
+                for (int w = 0; w < wave; ++w) before += sh.wsum[w];
+                int found = -1;
+                int64_t fb = 0;
+                if (before < cut && before + m0 >= cut) {
+                    found = 2 * tid;
+                    fb = before;
+                } else if (before + m0 < cut && before + m0 + m1 >= cut) {
+                    found = 2 * tid + 1;
+                    fb = before + m0;
+                }
+                if (found >= 0) {
+                    sh.sel_bin = found;
+                    sh.sel_below = fb;
+                    sh.sel_cnt = sh.hcnt[found];
+                    sh.sel_key = sh.hkey[found];
+                }
+                __syncthreads();
+                const int bsel = sh.sel_bin;
+                if (bsel < 0) {  // total mass below the cut: keep only the arg-max
+                    T = kmax;
+                    break;
+                }
+                if (sh.sel_cnt == 1 || shift == 0) {
+                    T = sh.sel_key;
+                    break;
+                }
+                below = sh.sel_below;
+                const uint64_t nlo = lo + ((uint64_t)bsel << shift);
+                const uint64_t nhi = nlo + ((1ull << shift) - 1);
+                lo = nlo;
+                hi = nhi < hi ? nhi : hi;
+            }
+        }
+
+        // kept = sorted position >= cut position, OR the STA window
+        bool kept[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int j = c * NT + tid;
+            kept[c] = valid[c] && (key[c] >= T || (sta != nullptr && sta[(int64_t)i * nb + j] != 0));
+        }
+        // compaction: ascending j = (c, wave, lane)
+        uint64_t ball[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            ball[c] = __ballot(kept[c]);
+            if (lane == 0) ccount[c][wave] = __popcll(ball[c]);
+        }
+        __syncthreads();
+        int base = 0;
+        const uint64_t below_lane = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            int off = base;
+            for (int w = 0; w < wave; ++w) off += ccount[c][w];
+            for (int w = 0; w < NW; ++w) base += ccount[c][w];
+            if (kept[c]) kv_inds[row * nb + off + __popcll(ball[c] & below_lane)] = c * NT + tid;
+        }
+        if (tid == 0) kv_nb[row] = base;
+    }
+}
+
+template <int D, int CPT, int R>
+static hipError_t launch_select_t(const float *qa, const float *ka, int BH, int nb,
+                                  const uint8_t *sta, float sqrt_d, int64_t cut, int32_t *kv_nb,
+                                  int32_t *kv_inds, hipStream_t stream) {
+    dim3 grid((nb + R - 1) / R, BH);
+    hipLaunchKernelGGL((select_kernel<D, CPT, R>), grid, dim3(512), 0, stream, qa, ka, nb, sta,
+                       sqrt_d, cut, kv_nb, kv_inds);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int nb,
+                                  const uint8_t *sta, float sqrt_d, int64_t cut, int32_t *kv_nb,
+                                  int32_t *kv_inds, hipStream_t stream) {
+    if (nb <= 512)
+        return launch_select_t<D, 1, 16>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
+    if (nb <= 1024)
+        return launch_select_t<D, 2, 16>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
+    if (nb <= 2048)
+        return launch_select_t<D, 4, 16>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
+    return launch_select_t<D, 8, 8>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
+}
+
+hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, int S,
+                             int heads, int D, const uint8_t *sta, int64_t cut_fixed,
+                             float sqrt_d, int32_t *kv_nb, int32_t *kv_inds, float *qa,
+                             float *ka, hipStream_t stream) {
+    const int nb = S / kBlock;
+    dim3 pgrid(nb, B, 2);
+    if (bf16_in)
+        hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
+                           (const bf16 *)k, qa, ka, S, heads, D);
+    else
+        hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
+                           (const float *)k, qa, ka, S, heads, D);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int BH = B * heads;
+    if (D == 64)
+        return launch_select_d<64>(qa, ka, BH, nb, sta, sqrt_d, cut_fixed, kv_nb, kv_inds, stream);
+    return launch_select_d<128>(qa, ka, BH, nb, sta, sqrt_d, cut_fixed, kv_nb, kv_inds, stream);
+}
+
+}  // namespace nabla

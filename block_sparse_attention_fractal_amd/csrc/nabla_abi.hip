@@ -1,0 +1,116 @@
+// nabla_abi.hip -- the extern "C" entry points of libnabla.so (declared in
+// include/nabla.h).  Host-side validation happens before any launch; nothing is
+// enqueued unless the call returns NABLA_OK.
+#include <math.h>
+
+#include "../../include/nabla.h"
+#include "nabla_launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kBlock = 64;
+constexpr int kTile = 8;
+constexpr int kMaxBlocks = 4096;  // longest row the selection kernel holds in registers
+
+size_t dtype_bytes(nabla_dtype dt) { return dt == NABLA_BF16 ? 2 : 4; }
+bool dtype_ok(nabla_dtype dt) { return dt == NABLA_BF16 || dt == NABLA_FP32; }
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+nabla_status from_hip(hipError_t e) { return e == hipSuccess ? NABLA_OK : NABLA_ERR_HIP; }
+
+// B*S*heads*head_dim must stay addressable with 64-bit offsets (always) and the
+// number of query blocks must fit a 1-D grid.
+bool sizes_ok(int B, int S, int heads, int head_dim) {
+    if (B < 1 || S < 1 || heads < 1 || head_dim < 1) return false;
+    const long long rows = (long long)B * heads * (S / kBlock);
+    return rows <= 0x7fffffffLL;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nabla_abi_version(void) { return kAbiVersion; }
+
+const char *nabla_status_string(nabla_status s) {
+    switch (s) {
+        case NABLA_OK: return "ok";
+        case NABLA_ERR_INVALID_ARG: return "invalid argument";
+        case NABLA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case NABLA_ERR_WORKSPACE: return "workspace missing or too small";
+        case NABLA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+nabla_status nabla_fractal_permute(const void *x, void *y, nabla_dtype dtype, int B, int T,
+                                   int H, int W, int heads, int head_dim, int inverse,
+                                   void *stream) {
+    if (!x || !y || !dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
+    if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || head_dim < 1)
+        return NABLA_ERR_INVALID_ARG;
+    if (H % kTile || W % kTile) return NABLA_ERR_INVALID_ARG;
+    const long long row_bytes = (long long)heads * head_dim * (long long)dtype_bytes(dtype);
+    if (row_bytes % 16) return NABLA_ERR_UNSUPPORTED;
+    if (row_bytes / 16 > 0x7fffffffLL / kBlock) return NABLA_ERR_UNSUPPORTED;
+    const long long nb = (long long)T * (H / kTile) * (W / kTile);
+    if ((long long)B * nb > 0x7fffffffLL) return NABLA_ERR_UNSUPPORTED;
+    return from_hip(nabla::launch_fractal_permute(x, y, (int)dtype_bytes(dtype), B, T, H, W,
+                                                  heads * head_dim, inverse != 0,
+                                                  as_stream(stream)));
+}
+
+nabla_status nabla_sta_mask(uint8_t *sta, int Tt, int Ht, int Wt, int win_t, int win_h,
+                            int win_w, void *stream) {
+    if (!sta || Tt < 1 || Ht < 1 || Wt < 1 || win_t < 0 || win_h < 0 || win_w < 0)
+        return NABLA_ERR_INVALID_ARG;
+    const long long nb = (long long)Tt * Ht * Wt;
+    if (nb > (1LL << 20)) return NABLA_ERR_UNSUPPORTED;
+    return from_hip(nabla::launch_sta_mask(sta, Tt, Ht, Wt, win_t, win_h, win_w,
+                                           as_stream(stream)));
+}
+
+size_t nabla_block_mask_workspace(int B, int S, int heads, int head_dim) {
+    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return 0;
+    return 2ull * (size_t)B * heads * (size_t)(S / kBlock) * head_dim * sizeof(float);
+}
+
+nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, int B, int S,
+                              int heads, int head_dim, const uint8_t *sta, double thr,
+                              int32_t *kv_nb, int32_t *kv_inds, void *ws, size_t ws_bytes,
+                              void *stream) {
+    if (!q || !k || !kv_nb || !kv_inds || !dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
+    if (!(thr >= 0.0 && thr <= 1.0)) return NABLA_ERR_INVALID_ARG;  // also rejects NaN
+    if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
+    const int nb = S / kBlock;
+    if (nb > kMaxBlocks) return NABLA_ERR_UNSUPPORTED;
+    const size_t need = nabla_block_mask_workspace(B, S, heads, head_dim);
+    if (!ws || ws_bytes < need) return NABLA_ERR_WORKSPACE;
+    // cut on the 2^-48 grid: ceil(fl32(1 - thr) * 2^48), exact in double
+    const float cut32 = (float)(1.0 - thr);
+    const int64_t cut_fixed = (int64_t)ceil(ldexp((double)cut32, 48));
+    const float sqrt_d = (float)sqrt((double)head_dim);
+    float *qa = static_cast<float *>(ws);
+    float *ka = qa + (size_t)B * heads * nb * head_dim;
+    return from_hip(nabla::launch_block_mask(q, k, dtype == NABLA_BF16, B, S, heads, head_dim,
+                                             sta, cut_fixed, sqrt_d, kv_nb, kv_inds, qa, ka,
+                                             as_stream(stream)));
+}
+
+nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
+                                   nabla_dtype dtype, int B, int S, int heads, int head_dim,
+                                   const int32_t *kv_nb, const int32_t *kv_inds, float scale,
+                                   void *o, void *stream) {
+    if (!q || !k || !v || !kv_nb || !kv_inds || !o || !dtype_ok(dtype))
+        return NABLA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
+    if (scale != scale) return NABLA_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
+    if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
+    return from_hip(nabla::launch_sparse_attn(q, k, v, dtype == NABLA_BF16, B, S, heads,
+                                              head_dim, kv_nb, kv_inds, scale, o,
+                                              as_stream(stream)));
+}
+
+}  // extern "C"

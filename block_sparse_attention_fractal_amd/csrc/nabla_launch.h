@@ -1,0 +1,29 @@
+// nabla_launch.h -- host launchers of the libnabla kernels (internal; the public
+// C ABI is include/nabla.h).  Arguments are validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nabla {
+
+hipError_t launch_fractal_permute(const void *x, void *y, int elem_bytes, int B, int T, int H,
+                                  int W, int row_elems, bool inverse, hipStream_t stream);
+
+hipError_t launch_sta_mask(uint8_t *sta, int Tt, int Ht, int Wt, int win_t, int win_h,
+                           int win_w, hipStream_t stream);
+
+// Pooled blocks [B*heads][nb][D] fp32 of q (qa) and k (ka), then per-row
+// selection; cut_fixed = ceil(fl32(1 - thr) * 2^48).
+hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, int S,
+                             int heads, int D, const uint8_t *sta, int64_t cut_fixed,
+                             float sqrt_d, int32_t *kv_nb, int32_t *kv_inds, float *qa,
+                             float *ka, hipStream_t stream);
+
+hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
+                              int B, int S, int heads, int D, const int32_t *kv_nb,
+                              const int32_t *kv_inds, float scale, void *o,
+                              hipStream_t stream);
+
+}  // namespace nabla

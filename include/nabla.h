@@ -1,0 +1,154 @@
+/*
+ * nabla.h -- C ABI of libnabla.so, the MI355X (gfx950) NABLA hot path.
+ *
+ * NABLA ("NABLA: Neighborhood Adaptive Block-Level Attention"; FastVideo API
+ * page "nabla") is data-dependent block-sparse attention for video DiTs:
+ *   1. tokens are put in fractal order (each 8 x 8 spatial patch of a frame
+ *      becomes a contiguous run of 64 tokens),
+ *   2. an estimator mean-pools Q and K over 64-token blocks, softmaxes the
+ *      scaled block-score map per row, keeps the top-mass blocks of each row
+ *      through a sorted-CDF cut at 1 - thr, ORs in a static spatio-temporal
+ *      window (STA) mask, and emits per-row kv block counts and indices,
+ *   3. attention is computed over exactly those 64 x 64 blocks.
+ *
+ * Conventions for every call
+ *   - Tensors are device pointers in HBM, contiguous, row-major, owned by the
+ *     caller.  Inputs are never written.  The library allocates nothing.
+ *   - q, k, v, o use [B, S, heads, head_dim] (the layout of the pages'
+ *     attention forward), S = T*H*W in fractal token order, S % 64 == 0.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns; there is no global mutable
+ *     state, so calls on different streams may run concurrently.
+ *   - Every call validates its arguments on the host before any launch and
+ *     returns a nabla_status; nothing is enqueued unless the result is
+ *     NABLA_OK.  NABLA_ERR_HIP reports a failed launch (hipGetLastError).
+ *   - dtype NABLA_BF16 (bfloat16) or NABLA_FP32; outputs of the attention
+ *     have the input dtype.  Attention runs on bf16 MFMA with fp32
+ *     accumulation (fp32 inputs are rounded to bf16, nearest-even, first).
+ */
+#ifndef NABLA_H
+#define NABLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NABLA_OK = 0,
+    NABLA_ERR_INVALID_ARG = 1, /* null pointer, bad shape, thr outside [0,1] or NaN */
+    NABLA_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    NABLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    NABLA_ERR_HIP = 4          /* a HIP launch failed */
+} nabla_status;
+
+typedef enum { NABLA_FP32 = 0, NABLA_BF16 = 1 } nabla_dtype;
+
+/* Version of this ABI (incremented on any signature change). */
+int nabla_abi_version(void);
+
+/* Static description of a status code (never NULL). */
+const char *nabla_status_string(nabla_status s);
+
+/*
+ * Fractal token reordering (NABLA summary page, Technical Summary >
+ * Methodology, "Token Reordering"; the "nabla" page's forward expects q/k/v
+ * "fractal-ordered by the model").
+ *
+ * inverse == 0: x is [B, T, H, W, heads, head_dim] (natural order), y is
+ *   [B, S, heads, head_dim] with token (t, yy, xx) at
+ *   s = ((t*(H/8) + yy/8) * (W/8) + xx/8) * 64 + (yy%8)*8 + xx%8:
+ *   frames stay in time order, 8 x 8 patches in raster order, and the 64
+ *   tokens of a patch in raster order; each 64-token block is one patch.
+ * inverse != 0: the exact inverse (x fractal, y natural), e.g. for O.
+ * x and y must not overlap.  Errors: INVALID_ARG if a pointer is NULL, a size
+ * is < 1, or H or W is not a multiple of 8; UNSUPPORTED if
+ * heads*head_dim*sizeof(dtype) is not a multiple of 16 bytes.
+ */
+nabla_status nabla_fractal_permute(const void *x, void *y, nabla_dtype dtype, int B, int T,
+                                   int H, int W, int heads, int head_dim, int inverse,
+                                   void *stream);
+
+/*
+ * STA block mask ("nabla" page, NablaAttentionMetadata.sta_mask: a block-level
+ * window mask of S/64 x S/64, precomputed once per run; NABLA summary page,
+ * Methodology, "Hybrid Integration with STA").
+ *
+ * sta[i*nb + j] = 1 when blocks i and j (tile coordinates (t, h, w), block
+ * index i = (t*Ht + h)*Wt + w, nb = Tt*Ht*Wt) satisfy |dt| <= win_t,
+ * |dh| <= win_h and |dw| <= win_w, else 0.  The window is clipped at the
+ * borders.  sta: device buffer of nb*nb bytes.  Errors: INVALID_ARG for a NULL
+ * pointer, a tile count < 1 or a negative window.
+ */
+nabla_status nabla_sta_mask(uint8_t *sta, int Tt, int Ht, int Wt, int win_t, int win_h,
+                            int win_w, void *stream);
+
+/* Bytes of workspace nabla_block_mask needs (pooled Q and K in fp32):
+ * 2 * B * heads * (S/64) * head_dim * 4.  0 if the sizes are invalid. */
+size_t nabla_block_mask_workspace(int B, int S, int heads, int head_dim);
+
+/*
+ * The NABLA block-mask estimator ("nabla" page, nablaT_v2: map estimation,
+ * map binarization, BlockMask creation; NABLA summary page, Methodology,
+ * "Adaptive Mask Construction" and "Hybrid Integration with STA").
+ *
+ * For every (b, head, query block i), with nb = S/64:
+ *   qa_i = mean of the 64 query tokens of block i (fp32; likewise ka_j),
+ *   s_ij = <qa_i, ka_j> / sqrt(head_dim)     (fp32, fixed reduction order),
+ *   p_ij = softmax_j(s_ij),
+ *   blocks sorted ascending by (s_ij, j); block j is kept when the
+ *   cumulative p up to and including it is >= fl32(1 - thr); the row's
+ *   largest block is always kept; finally kept |= sta[i][j].
+ * The cumulative sums are exact on a 2^-48 grid, so the decision does not
+ * depend on summation order.
+ *
+ * q, k:     [B, S, heads, head_dim] (bf16 or fp32), fractal order.
+ * sta:      [nb, nb] uint8 (nonzero = in window), shared by all (b, head);
+ *           NULL means no STA union.
+ * thr:      kept probability mass, in [0, 1] (the pages' default is 0.9).
+ * kv_nb:    out [B, heads, nb] int32, number of kept blocks of each row (>= 1).
+ * kv_inds:  out [B, heads, nb, nb] int32; the first kv_nb entries of each row
+ *           are the kept block indices in ascending order; the rest of the
+ *           row is left untouched (unspecified).
+ * ws:       device workspace of at least nabla_block_mask_workspace() bytes.
+ * Errors: INVALID_ARG (NULL q/k/kv_nb/kv_inds, sizes < 1, S % 64 != 0, thr
+ * NaN or outside [0,1]); UNSUPPORTED (head_dim not 64 or 128, or nb > 4096);
+ * WORKSPACE (ws NULL or ws_bytes too small).
+ */
+nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, int B, int S,
+                              int heads, int head_dim, const uint8_t *sta, double thr,
+                              int32_t *kv_nb, int32_t *kv_inds, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/*
+ * Block-sparse attention forward over the kept blocks ("nabla" page,
+ * NablaAttentionImpl.forward: flex attention with a block mask of full
+ * 64 x 64 blocks, no intra-block masking; NABLA summary page, Methodology,
+ * "Expansion").
+ *
+ * For each (b, head, query block i) and each of its 64 query rows:
+ *   o = softmax(scale * q K_J^T) V_J, J = the tokens of the blocks
+ *   kv_inds[b, head, i, 0 .. kv_nb[b, head, i] - 1].
+ * A row with kv_nb == 0 gets o = 0.  Non-causal only; one kv head per head.
+ *
+ * q, k, v:  [B, S, heads, head_dim] (bf16 or fp32), fractal order.
+ * kv_nb, kv_inds: as produced by nabla_block_mask (or any lists with
+ *           0 <= kv_nb <= nb and entries in [0, nb) without repeats).
+ * scale:    softmax scale; <= 0 selects 1/sqrt(head_dim).
+ * o:        out [B, S, heads, head_dim], same dtype as q; must not overlap inputs.
+ * Errors: INVALID_ARG (NULL pointer, sizes < 1, S % 64 != 0, NaN scale);
+ * UNSUPPORTED (head_dim not 64 or 128).  List contents are not checked on
+ * the host; indices outside [0, nb) are clamped by the kernel.
+ */
+nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
+                                   nabla_dtype dtype, int B, int S, int heads, int head_dim,
+                                   const int32_t *kv_nb, const int32_t *kv_inds, float scale,
+                                   void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NABLA_H */

@@ -54,7 +54,7 @@ def _load():
     lib.orc_cut_fixed.argtypes = [f64]
     lib.orc_cut_fixed.restype = i64
     lib.orc_select_row.argtypes = [P, i32, f64, P, P]
-    lib.orc_block_mask.argtypes = [P, P, i32, i32, i32, i32, P, f64, P, P, P, P]
+    lib.orc_block_mask.argtypes = [P, P, i32, i32, i32, i32, P, f64, P, i64, P, P, P, P]
     lib.orc_block_mask.restype = i32
     lib.orc_attention.argtypes = [P, P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
     lib.orc_attention.restype = i32
@@ -158,23 +158,33 @@ def select_row(s, thr):
 
 
 # ---------------------------------------------------------------- O3-O9
-def block_mask(q, k, sta, thr, want_nabla=False):
+def block_mask(q, k, sta, thr, want_nabla=False, row_ids=None):
     """The estimator.  q, k [B,S,heads,D] fp32 values; sta [nb,nb] uint8 or None.
 
     Returns dict with kv_nb [B,h,nb] int32, kv_inds [B,h,nb,nb] int32
     (kept ascending, then dropped ascending), diag [B,h,nb,3] int64 and,
-    if asked, mnabla [B,h,nb,nb] uint8 (mask before the STA union).
+    if asked, mnabla [B,h,nb,nb] uint8 (mask before the STA union).  With
+    ``row_ids`` (ids (b*heads + h)*nb + i) only those rows are evaluated and
+    the outputs are [len(row_ids), ...].
     """
     q, k = _f32(q), _f32(k)
     B, S, heads, D = q.shape
     nb = S // BLOCK
-    kv_nb = np.empty((B, heads, nb), np.int32)
-    kv_inds = np.empty((B, heads, nb, nb), np.int32)
-    diag = np.empty((B, heads, nb, 3), np.int64)
-    mn = np.empty((B, heads, nb, nb), np.uint8) if want_nabla else None
+    if row_ids is None:
+        lead = (B, heads, nb)
+        n = B * heads * nb
+        rid = None
+    else:
+        rid = np.ascontiguousarray(row_ids, dtype=np.int64)
+        lead = (rid.size,)
+        n = rid.size
+    kv_nb = np.empty(lead, np.int32)
+    kv_inds = np.empty(lead + (nb,), np.int32)
+    diag = np.empty(lead + (3,), np.int64)
+    mn = np.empty(lead + (nb,), np.uint8) if want_nabla else None
     st = None if sta is None else np.ascontiguousarray(sta, dtype=np.uint8)
     rc = _load().orc_block_mask(_ptr(q), _ptr(k), B, S, heads, D, _ptr(st), float(thr),
-                                _ptr(kv_nb), _ptr(kv_inds), _ptr(mn), _ptr(diag))
+                                _ptr(rid), n, _ptr(kv_nb), _ptr(kv_inds), _ptr(mn), _ptr(diag))
     if rc != 0:
         raise ValueError("oracle block_mask: bad argument")
     out = {"kv_nb": kv_nb, "kv_inds": kv_inds, "diag": diag}

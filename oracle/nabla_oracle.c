@@ -273,45 +273,50 @@ void orc_select_row(const float *s, int nb, double thr, uint8_t *kept, int64_t *
 
 /* ------------------------------------------------------------------------- */
 /* O3-O9: the whole estimator.  q, k [B][S][heads][D] fp32 values.            */
-/* sta [nb][nb] (NULL: STA off).  Outputs                                     */
-/*   kv_nb   [B][heads][nb]      number of kept blocks,                       */
-/*   kv_inds [B][heads][nb][nb]  kept block indices ascending, then the       */
+/* sta [nb][nb] (NULL: STA off).  row_ids: the rows (b*heads + h)*nb + i to   */
+/* evaluate (NULL: all rows, in order); output row r belongs to row_ids[r].   */
+/*   kv_nb   [nrows]             number of kept blocks,                       */
+/*   kv_inds [nrows][nb]         kept block indices ascending, then the       */
 /*                               dropped ones ascending,                      */
-/*   mnabla  [B][heads][nb][nb]  (optional) the mask before the STA union,    */
-/*   diag    [B][heads][nb][3]   (optional) see orc_select_row.               */
+/*   mnabla  [nrows][nb]         (optional) the mask before the STA union,    */
+/*   diag    [nrows][3]          (optional) see orc_select_row.               */
 /* Returns 0, or -1 on a bad argument.                                        */
 /* ------------------------------------------------------------------------- */
 int orc_block_mask(const float *q, const float *k, int B, int S, int heads, int D,
-                   const uint8_t *sta, double thr, int32_t *kv_nb, int32_t *kv_inds,
-                   uint8_t *mnabla, int64_t *diag) {
+                   const uint8_t *sta, double thr, const int64_t *row_ids, int64_t nrows,
+                   int32_t *kv_nb, int32_t *kv_inds, uint8_t *mnabla, int64_t *diag) {
     if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
     if (!(thr >= 0.0 && thr <= 1.0)) return -1;
     int nb = S / ORC_BLK;
+    int64_t all = (int64_t)B * heads * nb;
+    if (!row_ids) nrows = all;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (row_ids && (row_ids[r] < 0 || row_ids[r] >= all)) return -1;
     int64_t nbd = (int64_t)B * heads * nb * D;
     float *qa = (float *)malloc(sizeof(float) * (size_t)nbd);
     float *ka = (float *)malloc(sizeof(float) * (size_t)nbd);
     orc_pool(q, qa, B, S, heads, D);
     orc_pool(k, ka, B, S, heads, D);
     float sqrt_d = (float)sqrt((double)D);
-    int64_t rows = (int64_t)B * heads * nb;
 #pragma omp parallel for schedule(dynamic, 4)
-    for (int64_t r = 0; r < rows; ++r) {
-        int64_t bh = r / nb;
-        int i = (int)(r % nb);
+    for (int64_t rr = 0; rr < nrows; ++rr) {
+        int64_t id = row_ids ? row_ids[rr] : rr;
+        int64_t bh = id / nb;
+        int i = (int)(id % nb);
         float *srow = (float *)malloc(sizeof(float) * (size_t)nb);
         uint8_t *kept = (uint8_t *)malloc((size_t)nb);
         for (int j = 0; j < nb; ++j)
-            srow[j] = orc_score_one(qa + r * D, ka + (bh * nb + j) * D, D, sqrt_d);
-        orc_select_row(srow, nb, thr, kept, diag ? diag + r * 3 : NULL);
-        if (mnabla) memcpy(mnabla + r * nb, kept, (size_t)nb);
+            srow[j] = orc_score_one(qa + id * D, ka + (bh * nb + j) * D, D, sqrt_d);
+        orc_select_row(srow, nb, thr, kept, diag ? diag + rr * 3 : NULL);
+        if (mnabla) memcpy(mnabla + rr * nb, kept, (size_t)nb);
         /* mask = logical_or(mask, sta) */
         if (sta)
             for (int j = 0; j < nb; ++j) kept[j] = (uint8_t)(kept[j] | (sta[(int64_t)i * nb + j] != 0));
         /* kv_nb = mask.sum(-1); kv_inds = mask.argsort(descending) */
         int n = 0;
         for (int j = 0; j < nb; ++j) n += kept[j];
-        kv_nb[r] = n;
-        int32_t *row = kv_inds + r * nb;
+        kv_nb[rr] = n;
+        int32_t *row = kv_inds + rr * nb;
         int w = 0;
         for (int j = 0; j < nb; ++j)
             if (kept[j]) row[w++] = j;

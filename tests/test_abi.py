@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every declared symbol, and validates on the host (CPU only).
+
+No call here reaches a kernel launch: every call is rejected by host-side
+validation before the library touches the GPU.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_fractal_amd as nabla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nabla.h")
+OK, INVALID, UNSUP, WS = 0, 1, 2, 3
+BF16, FP32 = 1, 0
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nabla_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nabla.LIB_PATH):
+        from block_sparse_attention_fractal_amd import build
+        build.build()
+    return nabla.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == {"nabla_abi_version", "nabla_status_string", "nabla_fractal_permute",
+                          "nabla_sta_mask", "nabla_block_mask_workspace", "nabla_block_mask",
+                          "nabla_sparse_attn_fwd"}
+    raw = ctypes.CDLL(nabla.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings(L):
+    assert L.nabla_abi_version() == 1
+    for s in range(5):
+        assert L.nabla_status_string(s)
+    assert L.nabla_status_string(99) == b"unknown status"
+
+
+def test_workspace_size(L):
+    assert L.nabla_block_mask_workspace(1, 61440, 16, 128) == 2 * 16 * 960 * 128 * 4
+    assert L.nabla_block_mask_workspace(1, 100, 16, 128) == 0
+    assert L.nabla_block_mask_workspace(0, 64, 1, 64) == 0
+
+
+def test_block_mask_validation(L):
+    f = L.nabla_block_mask
+    good = dict(q=FAKE, k=FAKE, dt=BF16, B=1, S=8192, h=8, D=128, sta=None, thr=0.9,
+                kv_nb=FAKE, kv_inds=FAKE, ws=FAKE, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["q"], a["k"], a["dt"], a["B"], a["S"], a["h"], a["D"], a["sta"], a["thr"],
+                 a["kv_nb"], a["kv_inds"], a["ws"], a["wsb"], None)
+
+    assert call(q=None) == INVALID
+    assert call(kv_inds=None) == INVALID
+    assert call(dt=7) == INVALID
+    assert call(S=8192 + 32) == INVALID          # S % 64 != 0 (the page requires it)
+    assert call(B=0) == INVALID
+    assert call(h=-1) == INVALID
+    for thr in (-0.01, 1.01, math.nan, math.inf):
+        assert call(thr=thr) == INVALID
+    assert call(D=96) == UNSUP
+    assert call(S=64 * 4097) == UNSUP            # longer rows than the selection kernel holds
+    assert call(ws=None) == WS
+    assert call(wsb=L.nabla_block_mask_workspace(1, 8192, 8, 128) - 1) == WS
+
+
+def test_sparse_attn_validation(L):
+    f = L.nabla_sparse_attn_fwd
+
+    def call(q=FAKE, dt=BF16, B=1, S=8192, h=8, D=128, kv_nb=FAKE, scale=0.0, o=FAKE):
+        return f(q, FAKE, FAKE, dt, B, S, h, D, kv_nb, FAKE, scale, o, None)
+
+    assert call(q=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(kv_nb=None) == INVALID
+    assert call(S=100) == INVALID
+    assert call(scale=math.nan) == INVALID
+    assert call(D=32) == UNSUP
+    assert call(D=256) == UNSUP
+
+
+def test_permute_and_sta_validation(L):
+    p = L.nabla_fractal_permute
+    assert p(None, FAKE, BF16, 1, 2, 16, 16, 2, 64, 0, None) == INVALID
+    assert p(FAKE, FAKE, BF16, 1, 2, 12, 16, 2, 64, 0, None) == INVALID   # H % 8
+    assert p(FAKE, FAKE, BF16, 1, 2, 16, 20, 2, 64, 0, None) == INVALID   # W % 8
+    assert p(FAKE, FAKE, BF16, 1, 0, 16, 16, 2, 64, 0, None) == INVALID
+    assert p(FAKE, FAKE, BF16, 1, 2, 16, 16, 1, 2, 0, None) == UNSUP      # 4-byte rows
+    s = L.nabla_sta_mask
+    assert s(None, 2, 2, 2, 1, 1, 1, None) == INVALID
+    assert s(FAKE, 2, 0, 2, 1, 1, 1, None) == INVALID
+    assert s(FAKE, 2, 2, 2, -1, 1, 1, None) == INVALID
+
+
+def test_binding_has_no_cpu_path():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 128, 1, 64)
+    with pytest.raises(TypeError):
+        nabla.nabla_block_mask(q, q, None, 0.9)
+    with pytest.raises(TypeError):
+        nabla.nabla_fractal_permute(torch.zeros(1, 1, 8, 8, 1, 64))
+    kv = torch.zeros(1, 1, 2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        nabla.nabla_sparse_attn_fwd(q, q, q, kv, kv, causal=True)
+    with pytest.raises(TypeError):
+        nabla.nabla_sparse_attn_fwd(q, q, q, kv, kv)

@@ -1,0 +1,314 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded inputs.
+
+Integer outputs (fractal permutation, STA mask, kv_nb and the kv_inds sets)
+must match bit for bit; rows whose CDF lies within 1e-6 of the cut are
+reported and excluded from the exact check.  The attention output (bf16 MFMA,
+fp32 accumulation) must stay within max-abs 2e-2 and mean-abs 2e-3 of the
+fp64 oracle.  Tiny and Small are compared in full; the 720p and long-clip
+shapes on sampled rows (first/last, fewest/most kept blocks, random).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import block_sparse_attention_fractal_amd as nabla
+from block_sparse_attention_fractal_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return torch.device("cuda:0")
+
+
+_CACHE = {}
+
+
+def case(name, orc, dev):
+    """Inputs of a named workload: natural numpy arrays, oracle fractal arrays, GPU tensors."""
+    if name in _CACHE:
+        return _CACHE[name]
+    _CACHE.clear()
+    w = synth.WORKLOADS[name]
+    say("[case] generating", w.describe())
+    q, k, v = synth.make_qkv(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = {n: torch.from_numpy(a).to(tdt).to(dev) for n, a in (("q", q), ("k", k), ("v", v))}
+    f = {n: orc.fractal_permute(a).reshape(w.B, w.S, w.heads, w.D)
+         for n, a in (("q", q), ("k", k), ("v", v))}
+    c = dict(w=w, nat=dict(q=q, k=k, v=v), frac=f, gnat=g)
+    _CACHE[name] = c
+    return c
+
+
+def to_np(t):
+    return t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def sample_rows(kv_nb, rng, per_head=6):
+    """Row ids per (b, h): first, last, fewest and most kept blocks, and random rows."""
+    B, H, nb = kv_nb.shape
+    ids = []
+    for b in range(B):
+        for h in range(H):
+            row = kv_nb[b, h]
+            pick = {0, nb - 1, int(np.argmin(row)), int(np.argmax(row))}
+            pick |= set(rng.choice(nb, size=per_head, replace=False).tolist())
+            ids += [(b * H + h) * nb + i for i in sorted(pick)]
+    return np.array(ids, np.int64)
+
+
+def compare_lists(g_nb, g_inds, o_nb, o_inds, band, label):
+    """Bit-exact kv_nb and kv_inds sets on rows outside the band; returns mismatching band rows."""
+    g_nb = g_nb.reshape(-1)
+    o_nb = o_nb.reshape(-1)
+    nb = g_inds.shape[-1]
+    g_inds = g_inds.reshape(-1, nb)
+    o_inds = o_inds.reshape(-1, nb)
+    band = band.reshape(-1)
+    bad_band = 0
+    for r in range(g_nb.size):
+        n = int(o_nb[r])
+        same = int(g_nb[r]) == n and np.array_equal(g_inds[r, :n], o_inds[r, :n])
+        if band[r]:
+            bad_band += (not same)
+            continue
+        assert same, "%s: row %d differs: gpu n=%d oracle n=%d" % (label, r, g_nb[r], n)
+    say("[%s] rows=%d band rows=%d (mismatching in band: %d)" % (label, g_nb.size, int(band.sum()),
+                                                                  bad_band))
+    return bad_band
+
+
+# ------------------------------------------------------------------ permute + STA
+@pytest.mark.parametrize("name", ["tiny", "small", "720p"])
+def test_fractal_permute_bit_exact(orc, dev, name):
+    c = case(name, orc, dev)
+    w = c["w"]
+    say("[permute]", name)
+    for n in ("q", "k", "v"):
+        y = nabla.nabla_fractal_permute(c["gnat"][n])
+        torch.cuda.synchronize()
+        want = c["frac"][n]
+        got = to_np(y)
+        assert got.shape == want.shape
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), n
+        back = nabla.nabla_fractal_permute(y, grid=(w.T, w.H, w.W), inverse=True)
+        assert torch.equal(back, c["gnat"][n])
+
+
+@pytest.mark.parametrize("tiles,win", [((2, 2, 2), (1, 1, 1)), ((8, 4, 4), (1, 1, 1)),
+                                       ((16, 6, 10), (2, 1, 1)), ((16, 6, 10), (1, 1, 1)),
+                                       ((31, 6, 10), (2, 1, 1)), ((5, 3, 7), (0, 2, 1))])
+def test_sta_mask_bit_exact(orc, dev, tiles, win):
+    say("[sta]", tiles, win)
+    got = nabla.nabla_sta_mask(tiles, win, dev).cpu().numpy()
+    assert np.array_equal(got, orc.sta_mask(*tiles, *win))
+
+
+# ------------------------------------------------------------------ estimator
+def run_mask(c, orc, dev, thr, sta_win, rows=None, rng=None):
+    w = c["w"]
+    qf = nabla.nabla_fractal_permute(c["gnat"]["q"])
+    kf = nabla.nabla_fractal_permute(c["gnat"]["k"])
+    sta_g = None if sta_win is None else nabla.nabla_sta_mask(w.tiles, sta_win, dev)
+    kv_nb, kv_inds = nabla.nabla_block_mask(qf, kf, sta_g, thr)
+    torch.cuda.synchronize()
+    g_nb, g_inds = kv_nb.cpu().numpy(), kv_inds.cpu().numpy()
+    sta_o = None if sta_win is None else orc.sta_mask(*w.tiles, *sta_win)
+    if rows == "all":
+        o = orc.block_mask(c["frac"]["q"], c["frac"]["k"], sta_o, thr)
+        band = orc.band_rows(o["diag"], thr)
+        return (qf, kf), (g_nb, g_inds), (o["kv_nb"], o["kv_inds"]), band, None
+    ids = sample_rows(g_nb, rng)
+    o = orc.block_mask(c["frac"]["q"], c["frac"]["k"], sta_o, thr, row_ids=ids)
+    band = orc.band_rows(o["diag"], thr)
+    nb = w.nb
+    return ((qf, kf), (g_nb.reshape(-1)[ids], g_inds.reshape(-1, nb)[ids]),
+            (o["kv_nb"], o["kv_inds"]), band, ids)
+
+
+@pytest.mark.parametrize("name,thr,sta", [
+    ("tiny", 0.9, (1, 1, 1)), ("tiny", 0.9, None), ("tiny", 0.5, None), ("tiny", 0.0, None),
+    ("tiny", 1.0, None), ("small", 0.9, (1, 1, 1)), ("small", 0.5, None), ("small", 0.95, (0, 0, 0)),
+])
+def test_block_mask_full_parity(orc, dev, name, thr, sta):
+    c = case(name, orc, dev)
+    say("[mask-full]", name, "thr", thr, "sta", sta)
+    _, g, o, band, _ = run_mask(c, orc, dev, thr, sta, rows="all")
+    compare_lists(*g, *o, band, "%s thr=%g sta=%s" % (name, thr, sta))
+    if thr == 1.0:
+        assert np.all(g[0] == c["w"].nb)
+
+
+@pytest.mark.parametrize("name,thr,sta", [("720p", 0.9, (2, 1, 1)), ("720p", 0.5, None),
+                                          ("720p", 0.95, (1, 1, 1)), ("long", 0.9, (2, 1, 1))])
+def test_block_mask_sampled_parity(orc, dev, name, thr, sta):
+    c = case(name, orc, dev)
+    say("[mask-sampled]", name, "thr", thr, "sta", sta)
+    _, g, o, band, ids = run_mask(c, orc, dev, thr, sta, rng=np.random.default_rng(11))
+    compare_lists(*g, *o, band, "%s thr=%g sta=%s" % (name, thr, sta))
+
+
+def test_block_mask_uniform_ties(orc, dev):
+    """Q = 0: every score is exactly 0, so the order is decided by the index tie-break alone."""
+    B, S, h, D = 1, 8192, 2, 128
+    rng = np.random.default_rng(12)
+    k = synth.round_bf16(rng.standard_normal((B, S, h, D)).astype(np.float32))
+    q = np.zeros_like(k)
+    gq = torch.zeros((B, S, h, D), dtype=torch.bfloat16, device=dev)
+    gk = torch.from_numpy(k).to(torch.bfloat16).to(dev)
+    for thr in (0.5, 0.7, 0.9, 0.95):
+        say("[mask-ties] thr", thr)
+        kv_nb, kv_inds = nabla.nabla_block_mask(gq, gk, None, thr)
+        o = orc.block_mask(q, k, None, thr)
+        compare_lists(kv_nb.cpu().numpy(), kv_inds.cpu().numpy(), o["kv_nb"], o["kv_inds"],
+                      np.zeros(o["kv_nb"].shape, bool), "ties thr=%g" % thr)
+        want = {0.5: 65, 0.7: 90, 0.9: 116, 0.95: 122}[thr]
+        assert np.all(kv_nb.cpu().numpy() == want)
+
+
+# ------------------------------------------------------------------ attention
+def check_attention(got, want, label):
+    err = np.abs(got.astype(np.float64) - want)
+    say("[%s] max-abs %.3e mean-abs %.3e over %d values" % (label, err.max(), err.mean(), err.size))
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, label
+
+
+@pytest.mark.parametrize("name,thr,sta", [("tiny", 0.9, (1, 1, 1)), ("tiny", 0.5, None),
+                                          ("small", 0.9, (1, 1, 1))])
+def test_attention_full_parity(orc, dev, name, thr, sta):
+    c = case(name, orc, dev)
+    w = c["w"]
+    say("[attn-full]", name, "thr", thr, "sta", sta)
+    (qf, kf), g, o, band, _ = run_mask(c, orc, dev, thr, sta, rows="all")
+    compare_lists(*g, *o, band, "%s lists" % name)
+    vf = nabla.nabla_fractal_permute(c["gnat"]["v"])
+    kv_nb = torch.from_numpy(g[0]).to(dev)
+    kv_inds = torch.from_numpy(g[1]).to(dev)
+    out = nabla.nabla_sparse_attn_fwd(qf, kf, vf, kv_nb, kv_inds)
+    torch.cuda.synchronize()
+    ids, oo = orc.attention(c["frac"]["q"], c["frac"]["k"], c["frac"]["v"], g[0], g[1])
+    want = orc.rows_to_tokens(oo, ids, w.B, w.S, w.heads, w.D)
+    check_attention(to_np(out), want, "%s attn" % name)
+    # inverse permutation of O back to the natural grid
+    o_nat = nabla.nabla_fractal_permute(out, grid=(w.T, w.H, w.W), inverse=True)
+    assert torch.equal(nabla.nabla_fractal_permute(o_nat), out)
+
+
+@pytest.mark.parametrize("name", ["720p", "long"])
+def test_attention_sampled_parity(orc, dev, name):
+    c = case(name, orc, dev)
+    w = c["w"]
+    say("[attn-sampled]", name)
+    (qf, kf), _, _, _, _ = run_mask(c, orc, dev, w.thr, w.sta, rng=np.random.default_rng(13))
+    sta_g = nabla.nabla_sta_mask(w.tiles, w.sta, dev)
+    kv_nb, kv_inds = nabla.nabla_block_mask(qf, kf, sta_g, w.thr)
+    vf = nabla.nabla_fractal_permute(c["gnat"]["v"])
+    out = nabla.nabla_sparse_attn_fwd(qf, kf, vf, kv_nb, kv_inds)
+    torch.cuda.synchronize()
+    g_nb = kv_nb.cpu().numpy()
+    rng = np.random.default_rng(14)
+    ids = sample_rows(g_nb, rng, per_head=0)
+    ids = ids[rng.choice(ids.size, size=min(ids.size, 48), replace=False)]
+    rid, oo = orc.attention(c["frac"]["q"], c["frac"]["k"], c["frac"]["v"], g_nb,
+                            kv_inds.cpu().numpy(), row_ids=ids)
+    got = to_np(out)
+    nb = w.nb
+    sel = []
+    for rr in rid:
+        b, rem = divmod(int(rr), w.heads * nb)
+        h, i = divmod(rem, nb)
+        sel.append(got[b, 64 * i:64 * (i + 1), h, :])
+    check_attention(np.stack(sel), oo, "%s attn sampled" % name)
+
+
+def test_attention_random_lists_and_edges(orc, dev):
+    """User-supplied lists: empty rows (O = 0), single blocks, full rows, any order."""
+    rng = np.random.default_rng(15)
+    for D, dtype in ((128, torch.bfloat16), (64, torch.bfloat16), (128, torch.float32)):
+        B, S, h = 2, 1280, 3
+        nb = S // 64
+        say("[attn-random] D", D, dtype)
+        q, k, v = (rng.standard_normal((B, S, h, D)).astype(np.float32) for _ in range(3))
+        if dtype == torch.bfloat16:
+            q, k, v = synth.round_bf16(q), synth.round_bf16(k), synth.round_bf16(v)
+        kv_nb, kv_inds = synth.random_lists(rng, B, h, nb, 0.3)
+        kv_nb[0, 0, 0] = 0
+        kv_nb[0, 1, 3] = 1
+        kv_nb[1, 2, 5] = nb
+        kv_inds[1, 2, 5] = rng.permutation(nb)
+        kv_inds[0, 2, 7, :kv_nb[0, 2, 7]] = kv_inds[0, 2, 7, :kv_nb[0, 2, 7]][::-1].copy()
+        g = [torch.from_numpy(a).to(dtype).to(dev) for a in (q, k, v)]
+        out = nabla.nabla_sparse_attn_fwd(*g, torch.from_numpy(kv_nb).to(dev),
+                                          torch.from_numpy(kv_inds).to(dev))
+        torch.cuda.synchronize()
+        qq, kk, vv = (to_np(t) for t in g)  # the values the kernel sees
+        ids, oo = orc.attention(qq, kk, vv, kv_nb, kv_inds)
+        want = orc.rows_to_tokens(oo, ids, B, S, h, D)
+        got = to_np(out)
+        assert np.all(got[0, 0:64, 0] == 0)
+        check_attention(got, want, "random lists D=%d %s" % (D, dtype))
+
+
+def test_attention_sta_only_window(orc, dev):
+    """Lists built from the STA window alone give attention restricted to the window."""
+    c = case("small", orc, dev)
+    w = c["w"]
+    say("[attn-sta-only]")
+    sta = orc.sta_mask(*w.tiles, *w.sta)
+    nb = w.nb
+    kv_nb = np.broadcast_to(sta.sum(1).astype(np.int32), (w.B, w.heads, nb)).copy()
+    kv_inds = np.zeros((w.B, w.heads, nb, nb), np.int32)
+    for i in range(nb):
+        sel = np.flatnonzero(sta[i])
+        kv_inds[:, :, i, :sel.size] = sel
+    qf, kf, vf = (nabla.nabla_fractal_permute(c["gnat"][n]) for n in ("q", "k", "v"))
+    out = nabla.nabla_sparse_attn_fwd(qf, kf, vf, torch.from_numpy(kv_nb).to(dev),
+                                      torch.from_numpy(kv_inds).to(dev))
+    torch.cuda.synchronize()
+    ids, oo = orc.attention(c["frac"]["q"], c["frac"]["k"], c["frac"]["v"], kv_nb, kv_inds)
+    check_attention(to_np(out), orc.rows_to_tokens(oo, ids, w.B, w.S, w.heads, w.D),
+                    "sta-only")
+
+
+def test_run_twice_bitwise(orc, dev):
+    c = case("small", orc, dev)
+    w = c["w"]
+    say("[determinism]")
+    qf, kf, vf = (nabla.nabla_fractal_permute(c["gnat"][n]) for n in ("q", "k", "v"))
+    sta = nabla.nabla_sta_mask(w.tiles, w.sta, dev)
+    a = nabla.nabla_block_mask(qf, kf, sta, 0.9)
+    b = nabla.nabla_block_mask(qf, kf, sta, 0.9)
+    assert torch.equal(a[0], b[0])
+    for r in range(a[0].numel()):
+        n = int(a[0].view(-1)[r])
+        assert torch.equal(a[1].view(-1, w.nb)[r, :n], b[1].view(-1, w.nb)[r, :n])
+    o1 = nabla.nabla_sparse_attn_fwd(qf, kf, vf, *a)
+    o2 = nabla.nabla_sparse_attn_fwd(qf, kf, vf, *a)
+    assert torch.equal(o1, o2)
+
+
+def test_gpu_errors(dev):
+    q = torch.zeros(1, 100, 1, 64, device=dev, dtype=torch.bfloat16)
+    with pytest.raises(nabla.NablaError) as e:
+        nabla.nabla_block_mask(q, q, None, 0.9)
+    assert e.value.status == 1
+    q = torch.zeros(1, 128, 1, 64, device=dev, dtype=torch.bfloat16)
+    with pytest.raises(nabla.NablaError) as e:
+        nabla.nabla_block_mask(q, q, None, float("nan"))
+    assert e.value.status == 1
+    q = torch.zeros(1, 128, 1, 96, device=dev, dtype=torch.bfloat16)
+    with pytest.raises(nabla.NablaError) as e:
+        nabla.nabla_block_mask(q, q, None, 0.9)
+    assert e.value.status == 2
