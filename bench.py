@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the NABLA hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic video-shaped inputs
+already resident in HBM (natural token order):
+  STA block mask -> fractal permute of q, k, v -> nabla_block_mask (pool,
+  scores, softmax, CDF cut, STA union, kv lists) -> nabla_sparse_attn_fwd ->
+  inverse permute of o.
+The default workload is the 720p shape (B=1, 16 heads, D=128, 16 x 48 x 80
+latents = 61440 tokens, 960 blocks, thr 0.9, STA |dt|<=2, |dh|<=1, |dw|<=1).
+
+Prints one JSON line.  ``value`` is the effective throughput of the step:
+kept-block attention FLOPs (4 * 64 * 64 * D per kept (query block, kv block)
+pair) divided by the step time.  ``roofline`` describes the dominant kernel
+(the sparse attention forward) from HIP events around its launches in the
+timed steps; ``cpu_baseline`` is the CPU oracle on the host cores, on a
+bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NABLA sparse attn fwd effective TFLOP/s + mask ms at 720p shape, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", "sparse_attn.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_720p_pmc.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="720p", help="tiny | small | 720p | long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256,
+                    help="query blocks in the oracle attention sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def src_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(launch_flops_bytes):
+    """HBM bytes per attention launch from the committed PMC summary, if it matches this source."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    kv = {}
+    for line in open(PMC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("kernel_sha") != src_sha(ATTN_SRC):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(torch):
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+
+
+def cpu_baseline(w, q, k, v, sta_np, g_nb, rows, flops_per_pair):
+    """The oracle (untuned) on the host: full estimator, attention on a row sample."""
+    import oracle
+    from block_sparse_attention_fractal_amd import synth  # noqa: F401  (inputs only)
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    f = lambda a: oracle.fractal_permute(a).reshape(w.B, w.S, w.heads, w.D)
+    t0 = time.perf_counter()
+    qf, kf, vf = f(q), f(k), f(v)
+    t_perm = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    m = oracle.block_mask(qf, kf, sta_np, w.thr)
+    t_mask = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    total_rows = w.B * w.heads * w.nb
+    ids = np.sort(rng.choice(total_rows, size=min(rows, total_rows), replace=False))
+    t0 = time.perf_counter()
+    oracle.attention(qf, kf, vf, m["kv_nb"], m["kv_inds"], row_ids=ids)
+    t_attn_sample = time.perf_counter() - t0
+    sample_pairs = int(m["kv_nb"].reshape(-1)[ids].sum())
+    all_pairs = int(m["kv_nb"].sum())
+    t_attn_full = t_attn_sample * all_pairs / max(sample_pairs, 1)
+    t_step = t_perm + t_mask + t_attn_full
+    return {
+        "value": all_pairs * flops_per_pair / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.get_threads(),
+        "kind": "oracle",
+        "sample": ("full permute (%.2f s) and full estimator (%.2f s, %d rows) measured; "
+                   "attention measured on %d of %d query blocks (%.2f s, %d of %d kept pairs) "
+                   "and scaled by kept pairs to %.1f s"
+                   % (t_perm, t_mask, total_rows, ids.size, total_rows, t_attn_sample,
+                      sample_pairs, all_pairs, t_attn_full)),
+        "mask_ms": t_mask * 1e3,
+        "lists_match_gpu": bool(np.array_equal(m["kv_nb"], g_nb)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the path shards by (batch, head) across GPUs; that is not built here)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    import block_sparse_attention_fractal_amd as nabla
+    from block_sparse_attention_fractal_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print("[bench] %s" % w.describe(), file=sys.stderr, flush=True)
+    q, k, v = synth.make_qkv(w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    gq, gk, gv = (torch.from_numpy(a).to(tdt).to(dev) for a in (q, k, v))
+    B, S, H, D, nb = w.B, w.S, w.heads, w.D, w.nb
+    qf = torch.empty((B, S, H, D), dtype=tdt, device=dev)
+    kf, vf, of = torch.empty_like(qf), torch.empty_like(qf), torch.empty_like(qf)
+    o_nat = torch.empty_like(gq)
+    sta = torch.empty((nb, nb), dtype=torch.uint8, device=dev)
+    kv_nb = torch.empty((B, H, nb), dtype=torch.int32, device=dev)
+    kv_inds = torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev)
+    ws = torch.empty(nabla.nabla_block_mask_workspace(B, S, H, D), dtype=torch.uint8, device=dev)
+    L = nabla.lib()
+    import ctypes
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    dt_code = 1 if tdt == torch.bfloat16 else 0
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def check(rc, what):
+        if rc != 0:
+            raise nabla.NablaError(rc, what)
+
+    def step(rec=None):
+        """One pass of the path; rec collects (start, end) event pairs per stage."""
+        e = [ev() for _ in range(5)] if rec is not None else None
+        if e: e[0].record(stream)
+        check(L.nabla_sta_mask(P(sta), *w.tiles, *w.sta, sp), "sta")
+        for src, dst in ((gq, qf), (gk, kf), (gv, vf)):
+            check(L.nabla_fractal_permute(P(src), P(dst), dt_code, B, w.T, w.H, w.W, H, D, 0, sp),
+                  "permute")
+        if e: e[1].record(stream)
+        check(L.nabla_block_mask(P(qf), P(kf), dt_code, B, S, H, D, P(sta), w.thr, P(kv_nb),
+                                 P(kv_inds), P(ws), ws.numel(), sp), "mask")
+        if e: e[2].record(stream)
+        check(L.nabla_sparse_attn_fwd(P(qf), P(kf), P(vf), dt_code, B, S, H, D, P(kv_nb),
+                                      P(kv_inds), 0.0, *w.tiles, P(of), sp), "attn")
+        if e: e[3].record(stream)
+        check(L.nabla_fractal_permute(P(of), P(o_nat), dt_code, B, w.T, w.H, w.W, H, D, 1, sp),
+              "unpermute")
+        if e:
+            e[4].record(stream)
+            rec.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # per-stage durations from HIP events recorded on the launch stream
+    rec = []
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    stage = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in rec])
+    perm_ms = float(np.mean(stage[:, 0] + stage[:, 3]))
+    mask_ms = float(np.mean(stage[:, 1]))
+    attn_ms = float(np.mean(stage[:, 2]))
+
+    g_nb = kv_nb.cpu().numpy()
+    pairs = int(g_nb.sum())
+    flops_per_pair = 4.0 * 64 * 64 * D
+    attn_flops = pairs * flops_per_pair
+    density = pairs / float(B * H * nb * nb)
+    value = attn_flops / (ms_per_step * 1e-3) / 1e12
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    esz = 2 if tdt == torch.bfloat16 else 4
+    mask_bytes = 2.0 * B * S * H * D * esz + 4.0 * B * H * nb + 4.0 * pairs + nb * nb
+    traffic = read_traffic(attn_flops)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if tdt == torch.bfloat16 else "fp32",
+        "data": "synthetic (seeded smooth spatio-temporal field + noise, video-shaped)",
+        "config": {"workload": w.describe(), "B": B, "heads": H, "head_dim": D,
+                   "T": w.T, "H": w.H, "W": w.W, "seq_len": S, "blocks": nb, "thr": w.thr,
+                   "sta_window": list(w.sta) if w.sta else None, "kept_pairs": pairs,
+                   "density": round(density, 5)},
+        "mask_ms": round(mask_ms, 4),
+        "attn_ms": round(attn_ms, 4),
+        "permute_ms": round(perm_ms, 4),
+        "attn_tflops": round(attn_tflops, 2),
+        "mask_gbs": round(mask_bytes / (mask_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "sparse_attn_kernel<128, bf16>",
+                     "per_launch": {"flops": attn_flops, "kept_pairs": pairs}},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v,
+                                           None if w.sta is None else
+                                           sta.cpu().numpy(), g_nb, args.cpu_rows,
+                                           flops_per_pair)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,7 +9,7 @@ Calls (same names as the C ABI):
   nabla_fractal_permute(x, grid=None, inverse=False)
   nabla_sta_mask(tiles, window, device)
   nabla_block_mask(q, k, sta, thr=0.9)          -> (kv_nb, kv_inds)
-  nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False) -> o
+  nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, tiles=None) -> o
 """
 import ctypes
 import os
@@ -57,7 +57,7 @@ def lib():
     L.nabla_block_mask_workspace.restype = Z
     L.nabla_block_mask.argtypes = [P, P, I, I, I, I, I, P, D, P, P, P, Z, P]
     L.nabla_block_mask.restype = I
-    L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, P, P]
+    L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P]
     L.nabla_sparse_attn_fwd.restype = I
     _lib = L
     return L
@@ -156,8 +156,13 @@ def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None):
     return kv_nb, kv_inds
 
 
-def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, out=None):
-    """Block-sparse attention over the listed 64 x 64 blocks: o [B, S, heads, D] (q's dtype)."""
+def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, tiles=None,
+                          out=None):
+    """Block-sparse attention over the listed 64 x 64 blocks: o [B, S, heads, D] (q's dtype).
+
+    tiles: the (Tt, Ht, Wt) tile grid of the blocks (lets neighbouring query
+    blocks share K/V tiles on chip); None if unknown.
+    """
     if causal:
         raise ValueError("NABLA attention does not support causal masking")
     for name, t in (("q", q), ("k", k), ("v", v), ("kv_nb", kv_nb), ("kv_inds", kv_inds)):
@@ -171,8 +176,9 @@ def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, out
     if kv_nb.numel() != B * heads * nb or kv_inds.numel() != B * heads * nb * nb:
         raise ValueError("kv lists do not match q's shape")
     o = torch.empty_like(q) if out is None else _dev(out, "out")
+    Tt, Ht, Wt = (0, 0, 0) if tiles is None else tiles
     _check(lib().nabla_sparse_attn_fwd(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads, D,
                                        _p(kv_nb), _p(kv_inds),
-                                       0.0 if scale is None else float(scale), _p(o),
-                                       _stream(q)), "nabla_sparse_attn_fwd")
+                                       0.0 if scale is None else float(scale), Tt, Ht, Wt,
+                                       _p(o), _stream(q)), "nabla_sparse_attn_fwd")
     return o

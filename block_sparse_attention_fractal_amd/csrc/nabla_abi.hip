@@ -8,10 +8,10 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
-constexpr int kMaxBlocks = 4096;  // longest row the selection kernel holds in registers
+constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
 
 size_t dtype_bytes(nabla_dtype dt) { return dt == NABLA_BF16 ? 2 : 4; }
 bool dtype_ok(nabla_dtype dt) { return dt == NABLA_BF16 || dt == NABLA_FP32; }
@@ -101,15 +101,20 @@ nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, i
 nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
                                    nabla_dtype dtype, int B, int S, int heads, int head_dim,
                                    const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                                   void *o, void *stream) {
+                                   int Tt, int Ht, int Wt, void *o, void *stream) {
     if (!q || !k || !v || !kv_nb || !kv_inds || !o || !dtype_ok(dtype))
         return NABLA_ERR_INVALID_ARG;
     if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
     if (scale != scale) return NABLA_ERR_INVALID_ARG;
+    const bool grid_given = Tt != 0 || Ht != 0 || Wt != 0;
+    if (grid_given && (Tt < 1 || Ht < 1 || Wt < 1 ||
+                       (long long)Tt * Ht * Wt != (long long)(S / kBlock)))
+        return NABLA_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
+    if (S / kBlock > kMaxBlocks) return NABLA_ERR_UNSUPPORTED;
     if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
     return from_hip(nabla::launch_sparse_attn(q, k, v, dtype == NABLA_BF16, B, S, heads,
-                                              head_dim, kv_nb, kv_inds, scale, o,
+                                              head_dim, Tt, Ht, Wt, kv_nb, kv_inds, scale, o,
                                               as_stream(stream)));
 }
 

@@ -21,9 +21,10 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
                              float sqrt_d, int32_t *kv_nb, int32_t *kv_inds, float *qa,
                              float *ka, hipStream_t stream);
 
+// Tt, Ht, Wt: tile grid of the query blocks (Tt*Ht*Wt == S/64), or all 0 if unknown.
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
-                              int B, int S, int heads, int D, const int32_t *kv_nb,
-                              const int32_t *kv_inds, float scale, void *o,
+                              int B, int S, int heads, int D, int Tt, int Ht, int Wt,
+                              const int32_t *kv_nb, const int32_t *kv_inds, float scale, void *o,
                               hipStream_t stream);
 
 }  // namespace nabla

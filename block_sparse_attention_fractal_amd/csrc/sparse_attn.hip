@@ -8,234 +8,343 @@
 // Methodology, "Expansion").  Scale defaults to 1/sqrt(D) (the flex-attention
 // default; the forward passes none).
 //
-// Design (CDNA4):
-//   * one workgroup = 4 waves = one query block; wave w owns query rows
-//     16w .. 16w+15 and keeps them in registers as MFMA operands;
-//   * v_mfma_f32_16x16x32_bf16 throughout, fp32 accumulation;
-//   * scores are formed transposed, S^T = K Q^T, so the MFMA output puts one
-//     query row per lane column: the row max needs two lane swaps and the row
-//     sum stays lane-local until the end;
-//   * the K rows feeding score tile mt are permuted (sigma below) so that the
-//     fp32 score registers, packed to bf16, are directly the B operand of the
-//     P V product, whose A operand reads V^T rows of 8 consecutive keys;
-//   * K and V^T tiles are double-buffered in LDS; the next tile's global
-//     loads are issued before the current tile's MFMAs;
-//   * online softmax in fp32 with exp2 and the scale folded into log2 units.
+// Design (CDNA4 / gfx950):
+//   * K/V reuse across query blocks.  The lists of neighbouring query blocks
+//     overlap heavily (the STA window, and content that changes slowly in time
+//     and space).  One workgroup takes a group of G = 4 query blocks -- a
+//     2 (time) x 1 x 2 (width) box of tiles when the tile grid is known, else 4
+//     consecutive blocks -- and walks the union of their lists once in
+//     ascending block order.  Each K/V tile is fetched from HBM/L2 once per
+//     group and shared through LDS by every member that lists it.
+//   * 8 waves = 4 query blocks x 2 halves of 32 query rows; a wave keeps its
+//     32 query rows in registers as MFMA operands for the whole walk and skips
+//     the tiles its block does not list.
+//   * v_mfma_f32_32x32x16_bf16, fp32 accumulation.  Scores are formed
+//     transposed, S^T = K Q^T, so each lane owns one query row and 32 keys of a
+//     tile (the other 32 sit in lane ^ 32): the row max is in-lane work plus
+//     one lane swap, the row sum stays lane-local until the end.
+//   * K rows are read from LDS in a permuted order (sigma) chosen so that the
+//     fp32 score registers j = 8p .. 8p+7, packed to bf16, are the B operand
+//     of the P V product for 16 consecutive keys; V is read back transposed
+//     with ds_read_b64_tr_b16 as the A operand of O^T = V^T P^T.
+//   * Tiles move global -> registers (16-byte loads, fp32 inputs rounded to
+//     bf16 here) -> LDS (XOR-swizzled 16-byte chunks, two stages): the loads
+//     for tile u+2 are in flight while tile u is computed.
+//   * Online softmax in fp32 with exp2 and the scale folded into log2 units;
+//     the reference max is only raised when a tile exceeds it by more than 8
+//     (log2 units), so the O rescale is rare.
 #include "nabla_device.h"
 #include "nabla_launch.h"
 
 namespace nabla {
 
-// MFMA k-slot -> key row of score tile mt (0..3) for output row m (0..15):
-// m = 4g + u maps to key 32*(mt/2) + 8g + 4*(mt%2) + u.
-__device__ __forceinline__ int sigma_row(int mt, int m) {
-    return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+#define NABLA_LDS __attribute__((address_space(3)))
+
+constexpr int kGroup = 4;          // query blocks per workgroup
+constexpr int kAttnWaves = 2 * kGroup;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kMaxWords = 4096 / 64;  // bitmap words for up to 4096 blocks per row
+
+// Key row (within a 32-row score tile) fed to MFMA row m: bit layout
+// m = a(2) hh(1) b(2)  ->  key = (a>>1)<<4 | hh<<3 | (a&1)<<2 | b.
+__device__ __forceinline__ int sigma32(int m) {
+    const int a = m >> 3, hh = (m >> 2) & 1, b = m & 3;
+    return ((a >> 1) << 4) | (hh << 3) | ((a & 1) << 2) | b;
 }
 
-template <int D, typename Tin>
-__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(
-    const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
-    Tin *__restrict__ o, int S, int heads, int nrows, const int32_t *__restrict__ kv_nb,
-    const int32_t *__restrict__ kv_inds, float scale_log2) {
-    constexpr int KS = D / 32;               // MFMA k-steps of the score product
-    constexpr int DT = D / 16;               // output d-tiles
-    constexpr int LDK = D + 8;               // K tile row pitch (bf16)
-    constexpr int LDV = kBlock + 8;          // V^T tile row pitch (bf16)
-    constexpr int KCH = kBlock * D / 8 / 256;  // 16-byte K chunks per thread
-    constexpr int DG = D / 8;                // 8-wide d groups of a V row
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
 
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][kBlock * LDK];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * LDV];
+// 16-byte chunk swizzles (CH chunks per row) of the K and V tiles in LDS.
+template <int CH>
+__device__ __forceinline__ int kswz(int kv) { return kv & (CH - 1); }
+template <int CH>
+__device__ __forceinline__ int vswz(int kv) { return (kv & 3) * (CH / 4); }
+
+template <int D>
+struct AttnShared {
+    bf16 ks[2][kBlock * D];
+    bf16 vs[2][kBlock * D];
+    uint64_t qmask[kGroup][kMaxWords];
+    uint64_t umask[kMaxWords];
+};
+
+template <int D, typename Tin>
+__global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
+    Tin *__restrict__ o, int S, int heads, int Tt, int Ht, int Wt, int groups_per_bh,
+    int ngroups, const int32_t *__restrict__ kv_nb, const int32_t *__restrict__ kv_inds,
+    float scale_log2) {
+    constexpr int KS = D / 16;          // k-steps of the score product (16 dims each)
+    constexpr int DT = D / 32;          // 32-wide output d tiles
+    constexpr int CH = D / 8;           // 16-byte chunks per row
+    constexpr int ROWB = D * 2;         // bytes per K/V row in LDS
+    constexpr int CHUNKS = kBlock * CH; // 16-byte chunks per K (or V) tile
+    constexpr int CPT = CHUNKS / kAttnThreads;  // chunks per thread per tile (K and V each)
+    static_assert(CPT >= 1, "tile too small for the workgroup");
+
+    __shared__ __attribute__((aligned(1024))) AttnShared<D> sh;
 
     const int nb = S / kBlock;
-    const int row = xcd_contiguous(blockIdx.x, nrows);
-    const int i = row % nb;
-    const int bh = row / nb;
+    const int nwords = (nb + 63) >> 6;
+    const int grp = xcd_contiguous(blockIdx.x, ngroups);
+    const int bh = grp / groups_per_bh;
+    const int gi = grp % groups_per_bh;
     const int h = bh % heads;
     const int b = bh / heads;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int g = lane >> 4, l16 = lane & 15;
+    const int l32 = lane & 31, hi = lane >> 5;
 
-    const int64_t tok = (int64_t)heads * D;  // elements between consecutive tokens
+    // the G members of this group (-1 = no block in this slot)
+    int member[kGroup];
+    if (Tt > 0) {
+        const int cw = (Wt + 1) >> 1;
+        const int a = gi / (Ht * cw), hh = (gi / cw) % Ht, c = gi % cw;
+#pragma unroll
+        for (int s = 0; s < kGroup; ++s) {
+            const int t = 2 * a + (s >> 1), ww = 2 * c + (s & 1);
+            member[s] = (t < Tt && ww < Wt) ? (t * Ht + hh) * Wt + ww : -1;
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < kGroup; ++s) {
+            const int i = gi * kGroup + s;
+            member[s] = i < nb ? i : -1;
+        }
+    }
+
+    // ---- per-member bitmaps of listed blocks, and their union
+    for (int e = tid; e < kGroup * kMaxWords; e += kAttnThreads) (&sh.qmask[0][0])[e] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) {
+        if (member[s] < 0) continue;
+        const int64_t row = (int64_t)bh * nb + member[s];
+        int n = kv_nb[row];
+        n = n < 0 ? 0 : (n > nb ? nb : n);
+        const int32_t *list = kv_inds + row * nb;
+        for (int e = tid; e < n; e += kAttnThreads) {
+            int j = list[e];
+            j = j < 0 ? 0 : (j >= nb ? nb - 1 : j);
+            atomicOr((unsigned long long *)&sh.qmask[s][j >> 6], 1ull << (j & 63));
+        }
+    }
+    __syncthreads();
+    for (int wd = tid; wd < nwords; wd += kAttnThreads)
+        sh.umask[wd] = sh.qmask[0][wd] | sh.qmask[1][wd] | sh.qmask[2][wd] | sh.qmask[3][wd];
+    __syncthreads();
+
+    // ---- this wave: member slot and 32-row half
+    const int slot = w >> 1;
+    const int myblk = member[slot];
+    const int64_t tok = (int64_t)heads * D;
     const int64_t head0 = (int64_t)b * S * tok + (int64_t)h * D;
+    const int qtok = (myblk < 0 ? 0 : myblk) * kBlock + (w & 1) * 32 + l32;
 
-    int n = kv_nb[row];
-    n = n < 0 ? 0 : (n > nb ? nb : n);
-    const int32_t *list = kv_inds + (int64_t)row * nb;
-
-    const int qtok = i * kBlock + w * 16 + l16;
-    Tin *orow = o + head0 + (int64_t)qtok * tok;
-
-    if (n == 0) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) orow[16 * dt + 4 * g + u] = (Tin)0.0f;
-        return;
-    }
-
-    // Q rows of this wave as B operands: lane holds Q[qtok][32ks + 8g .. +7]
     bf16x8 qf[KS];
-    {
-        const Tin *qrow = q + head0 + (int64_t)qtok * tok;
+    if (myblk >= 0) {
+        const Tin *qr = q + head0 + (int64_t)qtok * tok + 8 * hi;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = load8_bf16(qrow + 32 * ks + 8 * g);
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = load8_bf16(qr + 16 * ks);
     }
 
-    // staging registers for one K tile and one V tile
-    bf16x8 kreg[KCH];
-    bf16x8 vreg[4];
-    const int kvg = tid & 15, dg = tid >> 4;  // V: keys 4kvg..4kvg+3, dims 8dg..8dg+7
-    const bool v_active = dg < DG;
+    // ---- union cursor (wave-uniform, kept in scalar registers): ascending set bits of umask
+    int cur_word = 0;
+    uint64_t cur_bits = uniform_u64(sh.umask[0]);
+    auto next_block = [&]() -> int {
+        while (cur_bits == 0ull) {
+            if (++cur_word >= nwords) return -1;
+            cur_bits = uniform_u64(sh.umask[cur_word]);
+        }
+        const int bit = __builtin_ctzll(cur_bits);
+        cur_bits &= cur_bits - 1;
+        return (cur_word << 6) | bit;
+    };
 
-    auto clampj = [&](int j) { return j < 0 ? 0 : (j >= nb ? nb - 1 : j); };
+    // ---- staging: K and V chunks of one tile in registers
+    bf16x8 kst[CPT], vst[CPT];
     auto fetch = [&](int j) {
         const Tin *kb = k + head0 + (int64_t)j * kBlock * tok;
         const Tin *vb = v + head0 + (int64_t)j * kBlock * tok;
 #pragma unroll
-        for (int it = 0; it < KCH; ++it) {
-            const int id = it * 256 + tid;
-            const int kr = id / DG, kc = id - kr * DG;
-            kreg[it] = load8_bf16(kb + (int64_t)kr * tok + 8 * kc);
-        }
-        if (v_active) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                vreg[rr] = load8_bf16(vb + (int64_t)(4 * kvg + rr) * tok + 8 * dg);
+        for (int r = 0; r < CPT; ++r) {
+            const int e = r * kAttnThreads + tid;
+            const int kv = e / CH, c = e % CH;
+            kst[r] = load8_bf16(kb + (int64_t)kv * tok + 8 * c);
+            vst[r] = load8_bf16(vb + (int64_t)kv * tok + 8 * c);
         }
     };
-    auto stash = [&](int buf) {
+    auto stash = [&](int stage) {
+        char *kd = reinterpret_cast<char *>(sh.ks[stage]);
+        char *vd = reinterpret_cast<char *>(sh.vs[stage]);
 #pragma unroll
-        for (int it = 0; it < KCH; ++it) {
-            const int id = it * 256 + tid;
-            const int kr = id / DG, kc = id - kr * DG;
-            *reinterpret_cast<bf16x8 *>(&Ks[buf][kr * LDK + 8 * kc]) = kreg[it];
-        }
-        if (v_active) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                bf16x4 col;
-                col[0] = vreg[0][u];
-                col[1] = vreg[1][u];
-                col[2] = vreg[2][u];
-                col[3] = vreg[3][u];
-                *reinterpret_cast<bf16x4 *>(&Vt[buf][(8 * dg + u) * LDV + 4 * kvg]) = col;
-            }
+        for (int r = 0; r < CPT; ++r) {
+            const int e = r * kAttnThreads + tid;
+            const int kv = e / CH, c = e % CH;
+            *reinterpret_cast<bf16x8 *>(kd + kv * ROWB + ((c ^ kswz<CH>(kv)) << 4)) = kst[r];
+            *reinterpret_cast<bf16x8 *>(vd + kv * ROWB + ((c ^ vswz<CH>(kv)) << 4)) = vst[r];
         }
     };
 
-    f32x4 oacc[DT];
+    f32x16 oacc[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[dt][j] = 0.0f;
+    float m_use = -INFINITY;  // reference max in log2 units (raised lazily)
+    float l_run = 0.0f;       // this lane's part of the row sum
 
-    fetch(clampj(list[0]));
-    stash(0);
+    int cur = next_block();
+    int nxt = -1;
+    if (cur >= 0) {
+        fetch(cur);
+        stash(0);
+        nxt = next_block();
+        if (nxt >= 0) fetch(nxt);
+    }
     __syncthreads();
 
-    for (int t = 0; t < n; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < n) fetch(clampj(list[t + 1]));
-
-        // S^T tiles: sacc[mt] holds keys sigma(mt, 4g+u), query l16
-        f32x4 sacc[4];
+    for (int it = 0; cur >= 0; ++it) {
+        const int stage = it & 1;
+        int nxt2 = -1;
+        if (nxt >= 0) {
+            stash(stage ^ 1);  // tile it+1 -> the other stage (free since the last barrier)
+            nxt2 = next_block();
+            if (nxt2 >= 0) fetch(nxt2);
+        }
+        const bool mine =
+            myblk >= 0 && ((uniform_u64(sh.qmask[slot][cur >> 6]) >> (cur & 63)) & 1ull);
+        if (mine) {
+            const char *kb = reinterpret_cast<const char *>(sh.ks[stage]);
+            const char *vb = reinterpret_cast<const char *>(sh.vs[stage]);
+            // S^T = K Q^T for the two 32-key halves of the tile
+            f32x16 sacc[2];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const bf16 *krow = &Ks[buf][sigma_row(mt, l16) * LDK + 8 * g];
+            for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(krow + 32 * ks);
-                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+                for (int j = 0; j < 16; ++j) sacc[mt][j] = 0.0f;
+                const int kv = 32 * mt + sigma32(l32);
+                const char *krow = kb + kv * ROWB;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int c = 2 * ks + hi;
+                    const bf16x8 a =
+                        *reinterpret_cast<const bf16x8 *>(krow + ((c ^ kswz<CH>(kv)) << 4));
+                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+                }
+            }
+            // online softmax in log2 units
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mloc = fmaxf(mloc, sacc[mt][j]);
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32)) * scale_log2;
+            if (mloc > m_use + 8.0f) {  // raise the reference max
+                const float alpha = __builtin_amdgcn_exp2f(m_use - mloc);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+                m_use = mloc;
+            }
+            bf16x8 pb[2][2];
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float p =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[mt][j], scale_log2, -m_use));
+                    l_run += p;
+                    pb[mt][j >> 3][j & 7] = (bf16)p;
+                }
+            // O^T += V^T P^T: 4 k-steps of 16 keys (mt, p)
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        bf16x8 a;
+#pragma unroll
+                        for (int r = 0; r < 2; ++r) {
+                            const int g16 = lane >> 4, s = lane & 15;
+                            const int kv = 32 * mt + 16 * p + 8 * (g16 >> 1) + 4 * r + (s >> 2);
+                            const int d = 32 * dt + 16 * (g16 & 1) + 4 * (s & 3);
+                            const int c = (d >> 3) ^ vswz<CH>(kv);
+                            const char *addr = vb + kv * ROWB + (c << 4) + (d & 7) * 2;
+                            const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                                (NABLA_LDS bf16x4 *)(addr));
+                            a[4 * r + 0] = x[0];
+                            a[4 * r + 1] = x[1];
+                            a[4 * r + 2] = x[2];
+                            a[4 * r + 3] = x[3];
+                        }
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mt][p], oacc[dt],
+                                                                           0, 0, 0);
+                    }
+                }
             }
         }
-
-        // online softmax (log2 units)
-        float mloc = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                sacc[mt][u] *= scale_log2;
-                mloc = fmaxf(mloc, sacc[mt][u]);
-            }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        float psum = 0.0f;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float p = __builtin_amdgcn_exp2f(sacc[mt][u] - m_new);
-                psum += p;
-                pb[mt >> 1][4 * (mt & 1) + u] = (bf16)p;
-            }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const bf16 *vrow = &Vt[buf][(16 * dt + l16) * LDV + 8 * g];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vrow + 32 * kk);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[kk], oacc[dt], 0, 0, 0);
-            }
-        }
-
-        if (t + 1 < n) stash(buf ^ 1);
-        __syncthreads();
+        __syncthreads();  // stage it+1 written; everyone done with stage it
+        cur = nxt;
+        nxt = nxt2;
     }
 
-    float lsum = l_run + __shfl_xor(l_run, 16);
-    lsum += __shfl_xor(lsum, 32);
-    const float inv = 1.0f / lsum;
+    if (myblk < 0) return;
+    const float lsum = l_run + __shfl_xor(l_run, 32);
+    const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;  // empty list -> O = 0
+    Tin *orow = o + head0 + (int64_t)qtok * tok;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-        if constexpr (sizeof(Tin) == 2) {
-            bf16x4 r;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) r[u] = (bf16)(oacc[dt][u] * inv);
-            *reinterpret_cast<bf16x4 *>(orow + 16 * dt + 4 * g) = r;
-        } else {
-            *reinterpret_cast<float4 *>(orow + 16 * dt + 4 * g) =
-                make_float4(oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv,
-                            oacc[dt][3] * inv);
+        for (int jj = 0; jj < 4; ++jj) {
+            Tin *dst = orow + 32 * dt + 8 * jj + 4 * hi;
+            if constexpr (sizeof(Tin) == 2) {
+                bf16x4 r;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) r[u] = (bf16)(oacc[dt][4 * jj + u] * inv);
+                *reinterpret_cast<bf16x4 *>(dst) = r;
+            } else {
+                *reinterpret_cast<float4 *>(dst) =
+                    make_float4(oacc[dt][4 * jj] * inv, oacc[dt][4 * jj + 1] * inv,
+                                oacc[dt][4 * jj + 2] * inv, oacc[dt][4 * jj + 3] * inv);
+            }
         }
     }
 }
 
 template <int D, typename Tin>
 static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int B, int S,
-                                int heads, const int32_t *kv_nb, const int32_t *kv_inds,
-                                float scale_log2, void *o, hipStream_t stream) {
-    const int nrows = B * heads * (S / kBlock);
-    hipLaunchKernelGGL((sparse_attn_kernel<D, Tin>), dim3(nrows), dim3(256), 0, stream,
-                       (const Tin *)q, (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, nrows,
-                       kv_nb, kv_inds, scale_log2);
+                                int heads, int Tt, int Ht, int Wt, const int32_t *kv_nb,
+                                const int32_t *kv_inds, float scale_log2, void *o,
+                                hipStream_t stream) {
+    const int nb = S / kBlock;
+    const int gpb = Tt > 0 ? ((Tt + 1) / 2) * Ht * ((Wt + 1) / 2) : (nb + kGroup - 1) / kGroup;
+    const int ngroups = B * heads * gpb;
+    hipLaunchKernelGGL((sparse_attn_kernel<D, Tin>), dim3(ngroups), dim3(kAttnThreads), 0, stream,
+                       (const Tin *)q, (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, Tt, Ht,
+                       Wt, gpb, ngroups, kv_nb, kv_inds, scale_log2);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
-                              int B, int S, int heads, int D, const int32_t *kv_nb,
-                              const int32_t *kv_inds, float scale, void *o,
+                              int B, int S, int heads, int D, int Tt, int Ht, int Wt,
+                              const int32_t *kv_nb, const int32_t *kv_inds, float scale, void *o,
                               hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
     if (D == 128)
-        return bf16_in ? launch_attn_t<128, bf16>(q, k, v, B, S, heads, kv_nb, kv_inds,
-                                                  scale_log2, o, stream)
-                       : launch_attn_t<128, float>(q, k, v, B, S, heads, kv_nb, kv_inds,
-                                                   scale_log2, o, stream);
-    return bf16_in ? launch_attn_t<64, bf16>(q, k, v, B, S, heads, kv_nb, kv_inds, scale_log2, o,
-                                             stream)
-                   : launch_attn_t<64, float>(q, k, v, B, S, heads, kv_nb, kv_inds, scale_log2,
-                                              o, stream);
+        return bf16_in ? launch_attn_t<128, bf16>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb,
+                                                  kv_inds, scale_log2, o, stream)
+                       : launch_attn_t<128, float>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb,
+                                                   kv_inds, scale_log2, o, stream);
+    return bf16_in ? launch_attn_t<64, bf16>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds,
+                                             scale_log2, o, stream)
+                   : launch_attn_t<64, float>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds,
+                                              scale_log2, o, stream);
 }
 
 }  // namespace nabla

@@ -135,17 +135,23 @@ nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, i
  *
  * q, k, v:  [B, S, heads, head_dim] (bf16 or fp32), fractal order.
  * kv_nb, kv_inds: as produced by nabla_block_mask (or any lists with
- *           0 <= kv_nb <= nb and entries in [0, nb) without repeats).
+ *           0 <= kv_nb <= nb and entries in [0, nb) without repeats, in any
+ *           order; a repeated entry counts once).
  * scale:    softmax scale; <= 0 selects 1/sqrt(head_dim).
+ * Tt, Ht, Wt: the tile grid of the blocks (the pages' visual_shape divided
+ *           by (1, 8, 8)), Tt*Ht*Wt == S/64; it only decides which query
+ *           blocks share K/V tiles on chip.  All three 0 = unknown (blocks
+ *           are then grouped in runs of consecutive indices).
  * o:        out [B, S, heads, head_dim], same dtype as q; must not overlap inputs.
- * Errors: INVALID_ARG (NULL pointer, sizes < 1, S % 64 != 0, NaN scale);
- * UNSUPPORTED (head_dim not 64 or 128).  List contents are not checked on
- * the host; indices outside [0, nb) are clamped by the kernel.
+ * Errors: INVALID_ARG (NULL pointer, sizes < 1, S % 64 != 0, NaN scale, a
+ * tile grid that does not multiply to S/64); UNSUPPORTED (head_dim not 64 or
+ * 128, or S/64 > 4096).  List contents are not checked on the host; entries
+ * outside [0, nb) are clamped by the kernel.
  */
 nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
                                    nabla_dtype dtype, int B, int S, int heads, int head_dim,
                                    const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                                   void *o, void *stream);
+                                   int Tt, int Ht, int Wt, void *o, void *stream);
 
 #ifdef __cplusplus
 }

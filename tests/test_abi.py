@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 1
+    assert L.nabla_abi_version() == 2
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"
@@ -83,16 +83,21 @@ def test_block_mask_validation(L):
 def test_sparse_attn_validation(L):
     f = L.nabla_sparse_attn_fwd
 
-    def call(q=FAKE, dt=BF16, B=1, S=8192, h=8, D=128, kv_nb=FAKE, scale=0.0, o=FAKE):
-        return f(q, FAKE, FAKE, dt, B, S, h, D, kv_nb, FAKE, scale, o, None)
+    def call(q=FAKE, dt=BF16, B=1, S=8192, h=8, D=128, kv_nb=FAKE, scale=0.0, o=FAKE,
+             tiles=(8, 4, 4)):
+        return f(q, FAKE, FAKE, dt, B, S, h, D, kv_nb, FAKE, scale, *tiles, o, None)
 
     assert call(q=None) == INVALID
     assert call(o=None) == INVALID
     assert call(kv_nb=None) == INVALID
     assert call(S=100) == INVALID
     assert call(scale=math.nan) == INVALID
+    assert call(tiles=(8, 4, 3)) == INVALID      # grid does not multiply to S/64
+    assert call(tiles=(0, 4, 4)) == INVALID
+    assert call(tiles=(-8, -4, 4)) == INVALID
     assert call(D=32) == UNSUP
     assert call(D=256) == UNSUP
+    assert call(S=64 * 4097, tiles=(0, 0, 0)) == UNSUP
 
 
 def test_permute_and_sta_validation(L):

@@ -196,7 +196,7 @@ def test_attention_full_parity(orc, dev, name, thr, sta):
     vf = nabla.nabla_fractal_permute(c["gnat"]["v"])
     kv_nb = torch.from_numpy(g[0]).to(dev)
     kv_inds = torch.from_numpy(g[1]).to(dev)
-    out = nabla.nabla_sparse_attn_fwd(qf, kf, vf, kv_nb, kv_inds)
+    out = nabla.nabla_sparse_attn_fwd(qf, kf, vf, kv_nb, kv_inds, tiles=w.tiles)
     torch.cuda.synchronize()
     ids, oo = orc.attention(c["frac"]["q"], c["frac"]["k"], c["frac"]["v"], g[0], g[1])
     want = orc.rows_to_tokens(oo, ids, w.B, w.S, w.heads, w.D)
@@ -215,7 +215,7 @@ def test_attention_sampled_parity(orc, dev, name):
     sta_g = nabla.nabla_sta_mask(w.tiles, w.sta, dev)
     kv_nb, kv_inds = nabla.nabla_block_mask(qf, kf, sta_g, w.thr)
     vf = nabla.nabla_fractal_permute(c["gnat"]["v"])
-    out = nabla.nabla_sparse_attn_fwd(qf, kf, vf, kv_nb, kv_inds)
+    out = nabla.nabla_sparse_attn_fwd(qf, kf, vf, kv_nb, kv_inds, tiles=w.tiles)
     torch.cuda.synchronize()
     g_nb = kv_nb.cpu().numpy()
     rng = np.random.default_rng(14)
@@ -236,10 +236,11 @@ def test_attention_sampled_parity(orc, dev, name):
 def test_attention_random_lists_and_edges(orc, dev):
     """User-supplied lists: empty rows (O = 0), single blocks, full rows, any order."""
     rng = np.random.default_rng(15)
-    for D, dtype in ((128, torch.bfloat16), (64, torch.bfloat16), (128, torch.float32)):
+    for D, dtype, tiles in ((128, torch.bfloat16, (5, 1, 4)), (64, torch.bfloat16, None),
+                            (128, torch.float32, (1, 4, 5)), (128, torch.bfloat16, (5, 2, 2))):
         B, S, h = 2, 1280, 3
         nb = S // 64
-        say("[attn-random] D", D, dtype)
+        say("[attn-random] D", D, dtype, "tiles", tiles)
         q, k, v = (rng.standard_normal((B, S, h, D)).astype(np.float32) for _ in range(3))
         if dtype == torch.bfloat16:
             q, k, v = synth.round_bf16(q), synth.round_bf16(k), synth.round_bf16(v)
@@ -251,14 +252,14 @@ def test_attention_random_lists_and_edges(orc, dev):
         kv_inds[0, 2, 7, :kv_nb[0, 2, 7]] = kv_inds[0, 2, 7, :kv_nb[0, 2, 7]][::-1].copy()
         g = [torch.from_numpy(a).to(dtype).to(dev) for a in (q, k, v)]
         out = nabla.nabla_sparse_attn_fwd(*g, torch.from_numpy(kv_nb).to(dev),
-                                          torch.from_numpy(kv_inds).to(dev))
+                                          torch.from_numpy(kv_inds).to(dev), tiles=tiles)
         torch.cuda.synchronize()
         qq, kk, vv = (to_np(t) for t in g)  # the values the kernel sees
         ids, oo = orc.attention(qq, kk, vv, kv_nb, kv_inds)
         want = orc.rows_to_tokens(oo, ids, B, S, h, D)
         got = to_np(out)
         assert np.all(got[0, 0:64, 0] == 0)
-        check_attention(got, want, "random lists D=%d %s" % (D, dtype))
+        check_attention(got, want, "random lists D=%d %s tiles=%s" % (D, dtype, tiles))
 
 
 def test_attention_sta_only_window(orc, dev):
@@ -275,7 +276,7 @@ def test_attention_sta_only_window(orc, dev):
         kv_inds[:, :, i, :sel.size] = sel
     qf, kf, vf = (nabla.nabla_fractal_permute(c["gnat"][n]) for n in ("q", "k", "v"))
     out = nabla.nabla_sparse_attn_fwd(qf, kf, vf, torch.from_numpy(kv_nb).to(dev),
-                                      torch.from_numpy(kv_inds).to(dev))
+                                      torch.from_numpy(kv_inds).to(dev), tiles=w.tiles)
     torch.cuda.synchronize()
     ids, oo = orc.attention(c["frac"]["q"], c["frac"]["k"], c["frac"]["v"], kv_nb, kv_inds)
     check_attention(to_np(out), orc.rows_to_tokens(oo, ids, w.B, w.S, w.heads, w.D),
@@ -294,9 +295,12 @@ def test_run_twice_bitwise(orc, dev):
     for r in range(a[0].numel()):
         n = int(a[0].view(-1)[r])
         assert torch.equal(a[1].view(-1, w.nb)[r, :n], b[1].view(-1, w.nb)[r, :n])
-    o1 = nabla.nabla_sparse_attn_fwd(qf, kf, vf, *a)
-    o2 = nabla.nabla_sparse_attn_fwd(qf, kf, vf, *a)
+    o1 = nabla.nabla_sparse_attn_fwd(qf, kf, vf, *a, tiles=w.tiles)
+    o2 = nabla.nabla_sparse_attn_fwd(qf, kf, vf, *a, tiles=w.tiles)
     assert torch.equal(o1, o2)
+    # grouping only changes which blocks share tiles on chip, not the result
+    o3 = nabla.nabla_sparse_attn_fwd(qf, kf, vf, *a)
+    assert torch.equal(o1, o3)
 
 
 def test_gpu_errors(dev):
