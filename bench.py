@@ -149,6 +149,8 @@ def main():
     kv_nb = torch.empty((B, H, nb), dtype=torch.int32, device=dev)
     kv_inds = torch.empty((B, H, nb, nb), dtype=torch.int32, device=dev)
     ws = torch.empty(nabla.nabla_block_mask_workspace(B, S, H, D), dtype=torch.uint8, device=dev)
+    ws_attn = torch.empty(nabla.nabla_sparse_attn_workspace(B, S, H, w.tiles), dtype=torch.uint8,
+                          device=dev)
     L = nabla.lib()
     import ctypes
     P = lambda t: ctypes.c_void_p(t.data_ptr())
@@ -174,7 +176,8 @@ def main():
                                  P(kv_inds), P(ws), ws.numel(), sp), "mask")
         if e: e[2].record(stream)
         check(L.nabla_sparse_attn_fwd(P(qf), P(kf), P(vf), dt_code, B, S, H, D, P(kv_nb),
-                                      P(kv_inds), 0.0, *w.tiles, P(of), sp), "attn")
+                                      P(kv_inds), 0.0, *w.tiles, P(of), P(ws_attn),
+                                      ws_attn.numel(), sp), "attn")
         if e: e[3].record(stream)
         check(L.nabla_fractal_permute(P(of), P(o_nat), dt_code, B, w.T, w.H, w.W, H, D, 1, sp),
               "unpermute")

@@ -9,7 +9,8 @@ Calls (same names as the C ABI):
   nabla_fractal_permute(x, grid=None, inverse=False)
   nabla_sta_mask(tiles, window, device)
   nabla_block_mask(q, k, sta, thr=0.9)          -> (kv_nb, kv_inds)
-  nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, tiles=None) -> o
+  nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, tiles=None,
+                        workspace=None, out=None) -> o
 """
 import ctypes
 import os
@@ -17,7 +18,8 @@ import os
 import torch
 
 __all__ = ["nabla_fractal_permute", "nabla_sta_mask", "nabla_block_mask",
-           "nabla_block_mask_workspace", "nabla_sparse_attn_fwd", "NablaError", "lib",
+           "nabla_block_mask_workspace", "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace",
+           "NablaError", "lib",
            "LIB_PATH", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnabla.so")
@@ -57,7 +59,9 @@ def lib():
     L.nabla_block_mask_workspace.restype = Z
     L.nabla_block_mask.argtypes = [P, P, I, I, I, I, I, P, D, P, P, P, Z, P]
     L.nabla_block_mask.restype = I
-    L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P]
+    L.nabla_sparse_attn_workspace.argtypes = [I, I, I, I, I, I]
+    L.nabla_sparse_attn_workspace.restype = Z
+    L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P, Z, P]
     L.nabla_sparse_attn_fwd.restype = I
     _lib = L
     return L
@@ -156,12 +160,19 @@ def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None):
     return kv_nb, kv_inds
 
 
+def nabla_sparse_attn_workspace(B, S, heads, tiles=None):
+    """Bytes of workspace nabla_sparse_attn_fwd needs (0 for invalid sizes)."""
+    Tt, Ht, Wt = (0, 0, 0) if tiles is None else tiles
+    return lib().nabla_sparse_attn_workspace(B, S, heads, Tt, Ht, Wt)
+
+
 def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, tiles=None,
-                          out=None):
+                          workspace=None, out=None):
     """Block-sparse attention over the listed 64 x 64 blocks: o [B, S, heads, D] (q's dtype).
 
     tiles: the (Tt, Ht, Wt) tile grid of the blocks (lets neighbouring query
-    blocks share K/V tiles on chip); None if unknown.
+    blocks share K/V tiles on chip); None if unknown.  workspace: a uint8 GPU
+    tensor of at least nabla_sparse_attn_workspace() bytes (allocated if None).
     """
     if causal:
         raise ValueError("NABLA attention does not support causal masking")
@@ -177,8 +188,14 @@ def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, til
         raise ValueError("kv lists do not match q's shape")
     o = torch.empty_like(q) if out is None else _dev(out, "out")
     Tt, Ht, Wt = (0, 0, 0) if tiles is None else tiles
+    if workspace is None:
+        need = lib().nabla_sparse_attn_workspace(B, S, heads, Tt, Ht, Wt)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _dev(workspace, "workspace")
     _check(lib().nabla_sparse_attn_fwd(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads, D,
                                        _p(kv_nb), _p(kv_inds),
                                        0.0 if scale is None else float(scale), Tt, Ht, Wt,
-                                       _p(o), _stream(q)), "nabla_sparse_attn_fwd")
+                                       _p(o), _p(workspace), workspace.numel(), _stream(q)),
+           "nabla_sparse_attn_fwd")
     return o

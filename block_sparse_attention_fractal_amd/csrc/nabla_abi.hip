@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
 constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
@@ -24,6 +24,12 @@ bool sizes_ok(int B, int S, int heads, int head_dim) {
     if (B < 1 || S < 1 || heads < 1 || head_dim < 1) return false;
     const long long rows = (long long)B * heads * (S / kBlock);
     return rows <= 0x7fffffffLL;
+}
+
+// A tile grid is either all zero (unknown) or positive and multiplies to S/64.
+bool grid_ok(int S, int Tt, int Ht, int Wt) {
+    if (Tt == 0 && Ht == 0 && Wt == 0) return true;
+    return Tt >= 1 && Ht >= 1 && Wt >= 1 && (long long)Tt * Ht * Wt == (long long)(S / kBlock);
 }
 
 }  // namespace
@@ -98,24 +104,29 @@ nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, i
                                              as_stream(stream)));
 }
 
+size_t nabla_sparse_attn_workspace(int B, int S, int heads, int Tt, int Ht, int Wt) {
+    if (!sizes_ok(B, S, heads, 1) || S % kBlock || !grid_ok(S, Tt, Ht, Wt)) return 0;
+    return nabla::sparse_attn_workspace_bytes(B, S, heads, Tt, Ht, Wt);
+}
+
 nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
                                    nabla_dtype dtype, int B, int S, int heads, int head_dim,
                                    const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                                   int Tt, int Ht, int Wt, void *o, void *stream) {
+                                   int Tt, int Ht, int Wt, void *o, void *ws, size_t ws_bytes,
+                                   void *stream) {
     if (!q || !k || !v || !kv_nb || !kv_inds || !o || !dtype_ok(dtype))
         return NABLA_ERR_INVALID_ARG;
     if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
     if (scale != scale) return NABLA_ERR_INVALID_ARG;
-    const bool grid_given = Tt != 0 || Ht != 0 || Wt != 0;
-    if (grid_given && (Tt < 1 || Ht < 1 || Wt < 1 ||
-                       (long long)Tt * Ht * Wt != (long long)(S / kBlock)))
-        return NABLA_ERR_INVALID_ARG;
+    if (!grid_ok(S, Tt, Ht, Wt)) return NABLA_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
     if (S / kBlock > kMaxBlocks) return NABLA_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < nabla::sparse_attn_workspace_bytes(B, S, heads, Tt, Ht, Wt))
+        return NABLA_ERR_WORKSPACE;
     if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
     return from_hip(nabla::launch_sparse_attn(q, k, v, dtype == NABLA_BF16, B, S, heads,
                                               head_dim, Tt, Ht, Wt, kv_nb, kv_inds, scale, o,
-                                              as_stream(stream)));
+                                              ws, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -22,9 +22,11 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
                              float *ka, hipStream_t stream);
 
 // Tt, Ht, Wt: tile grid of the query blocks (Tt*Ht*Wt == S/64), or all 0 if unknown.
+// ws: sparse_attn_workspace_bytes() bytes (schedule: counter, group costs, order).
+size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt);
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
                               int B, int S, int heads, int D, int Tt, int Ht, int Wt,
                               const int32_t *kv_nb, const int32_t *kv_inds, float scale, void *o,
-                              hipStream_t stream);
+                              void *ws, hipStream_t stream);
 
 }  // namespace nabla

@@ -74,20 +74,136 @@ __device__ __forceinline__ int kswz(int kv) { return kv & (CH - 1); }
 template <int CH>
 __device__ __forceinline__ int vswz(int kv) { return (kv & 3) * (CH / 4); }
 
+// Byte offset of a __shared__ object in LDS.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)((const NABLA_LDS char *)p);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's chunk lands at
+// m0 + 16 l (m0 wave-uniform).  Issued from inline asm so that the compiler does not
+// treat every later LDS read as depending on it; completion is awaited explicitly
+// with vm_wait before the barrier that hands the tile to the other waves.  Nothing
+// else in the kernel uses m0.
+__device__ __forceinline__ void lds_direct16(const void *g, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(m0)
+                 : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+constexpr int kStages = 3;  // LDS ring depth: tile k+2 lands while tile k is computed
+
 template <int D>
 struct AttnShared {
-    bf16 ks[2][kBlock * D];
-    bf16 vs[2][kBlock * D];
+    bf16 ks[kStages][kBlock * D];
+    bf16 vs[kStages][kBlock * D];
     uint64_t qmask[kGroup][kMaxWords];
     uint64_t umask[kMaxWords];
+    int slot;  // the schedule position this workgroup works on
 };
+
+// Member s of query-block group gi (-1 = empty slot).  Known tile grid: kGroup 4 takes
+// a 2 (time) x 1 x 2 (width) box of tiles, kGroup 2 the same tile in two consecutive
+// frames; unknown grid (Tt == 0): kGroup consecutive blocks.
+__device__ __forceinline__ int group_member(int gi, int s, int Tt, int Ht, int Wt, int nb) {
+    if (Tt > 0) {
+        const int cw = kGroup == 4 ? (Wt + 1) >> 1 : Wt;
+        const int a = gi / (Ht * cw), hh = (gi / cw) % Ht, c = gi % cw;
+        const int t = 2 * a + (kGroup == 4 ? (s >> 1) : s);
+        const int ww = kGroup == 4 ? 2 * c + (s & 1) : c;
+        return (t < Tt && ww < Wt) ? (t * Ht + hh) * Wt + ww : -1;
+    }
+    const int i = gi * kGroup + s;
+    return i < nb ? i : -1;
+}
+
+__device__ __forceinline__ int clamp_count(int n, int nb) { return n < 0 ? 0 : (n > nb ? nb : n); }
+__device__ __forceinline__ int clamp_block(int j, int nb) { return j < 0 ? 0 : (j >= nb ? nb - 1 : j); }
+
+// ---- schedule.  The cost of a group is the number of tiles in the union of its
+// members' lists (the iterations of its walk).  Groups run longest first (LPT) on
+// persistent workgroups that take the next group from a counter, which keeps every
+// CU busy to the end and balances the XCDs whatever the per-head density.
+
+// grid = ngroups, 256 lanes: cost[g] = |union of the lists of group g|; resets the counter.
+__global__ __launch_bounds__(256) void attn_plan_cost_kernel(
+    const int32_t *__restrict__ kv_nb, const int32_t *__restrict__ kv_inds, int nb, int Tt,
+    int Ht, int Wt, int groups_per_bh, int32_t *__restrict__ cost, int32_t *__restrict__ counter) {
+    __shared__ uint64_t bits[kMaxWords];
+    __shared__ int total;
+    const int g = blockIdx.x, tid = threadIdx.x;
+    const int bh = g / groups_per_bh, gi = g % groups_per_bh;
+    const int nwords = (nb + 63) >> 6;
+    if (g == 0 && tid == 0) *counter = 0;
+    for (int e = tid; e < kMaxWords; e += 256) bits[e] = 0ull;
+    if (tid == 0) total = 0;
+    __syncthreads();
+    for (int s = 0; s < kGroup; ++s) {
+        const int m = group_member(gi, s, Tt, Ht, Wt, nb);
+        if (m < 0) continue;
+        const int64_t row = (int64_t)bh * nb + m;
+        const int n = clamp_count(kv_nb[row], nb);
+        const int32_t *list = kv_inds + row * nb;
+        for (int e = tid; e < n; e += 256) {
+            const int j = clamp_block(list[e], nb);
+            atomicOr((unsigned long long *)&bits[j >> 6], 1ull << (j & 63));
+        }
+    }
+    __syncthreads();
+    int cnt = 0;
+    for (int wd = tid; wd < nwords; wd += 256) cnt += __popcll(bits[wd]);
+    atomicAdd(&total, cnt);
+    __syncthreads();
+    if (tid == 0) cost[g] = total;
+}
+
+// one workgroup of 1024 lanes: order[] = the groups by descending cost (counting sort;
+// the order among equal costs is arbitrary and does not affect any result).
+__global__ __launch_bounds__(1024) void attn_plan_order_kernel(const int32_t *__restrict__ cost,
+                                                              int ngroups, int nb,
+                                                              int32_t *__restrict__ order) {
+    __shared__ int start[kMaxWords * 64 + 1];  // one bin per possible cost 0 .. nb
+    __shared__ int part[2][1024];
+    const int tid = threadIdx.x;
+    const int nbins = nb + 1;
+    for (int c = tid; c < nbins; c += 1024) start[c] = 0;
+    __syncthreads();
+    for (int g = tid; g < ngroups; g += 1024) atomicAdd(&start[clamp_count(cost[g], nb)], 1);
+    __syncthreads();
+    // thread t owns descending positions [t*chunk, (t+1)*chunk), position p = bin nb - p
+    const int chunk = (nbins + 1023) / 1024;
+    int sum = 0;
+    for (int p = tid * chunk; p < (tid + 1) * chunk && p < nbins; ++p) sum += start[nb - p];
+    part[0][tid] = sum;
+    __syncthreads();
+    int src = 0;
+    for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the per-thread sums
+        const int x = part[src][tid] + (tid >= off ? part[src][tid - off] : 0);
+        part[src ^ 1][tid] = x;
+        src ^= 1;
+        __syncthreads();
+    }
+    int run = part[src][tid] - sum;  // exclusive
+    for (int p = tid * chunk; p < (tid + 1) * chunk && p < nbins; ++p) {
+        const int c = nb - p, n = start[c];
+        start[c] = run;
+        run += n;
+    }
+    __syncthreads();
+    for (int g = tid; g < ngroups; g += 1024)
+        order[atomicAdd(&start[clamp_count(cost[g], nb)], 1)] = g;
+}
 
 template <int D, typename Tin>
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     Tin *__restrict__ o, int S, int heads, int Tt, int Ht, int Wt, int groups_per_bh,
     int ngroups, const int32_t *__restrict__ kv_nb, const int32_t *__restrict__ kv_inds,
-    float scale_log2) {
+    float scale_log2, const int32_t *__restrict__ order, int32_t *__restrict__ counter) {
     constexpr int KS = D / 16;          // k-steps of the score product (16 dims each)
     constexpr int DT = D / 32;          // 32-wide output d tiles
     constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -100,33 +216,25 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
 
     const int nb = S / kBlock;
     const int nwords = (nb + 63) >> 6;
-    const int grp = xcd_contiguous(blockIdx.x, ngroups);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    // persistent: take schedule positions until none is left (every wave of the
+    // workgroup sees the same position, so all leave together)
+    for (;;) {
+    if (tid == 0) sh.slot = atomicAdd(counter, 1);
+    __syncthreads();
+    const int pos = sh.slot;
+    if (pos >= ngroups) break;
+    const int grp = order[pos];
     const int bh = grp / groups_per_bh;
     const int gi = grp % groups_per_bh;
     const int h = bh % heads;
     const int b = bh / heads;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int l32 = lane & 31, hi = lane >> 5;
 
-    // the G members of this group (-1 = no block in this slot)
     int member[kGroup];
-    if (Tt > 0) {
-        // kGroup 4: a 2 (time) x 1 x 2 (width) box; kGroup 2: 2 frames of one tile
-        const int cw = kGroup == 4 ? (Wt + 1) >> 1 : Wt;
-        const int a = gi / (Ht * cw), hh = (gi / cw) % Ht, c = gi % cw;
 #pragma unroll
-        for (int s = 0; s < kGroup; ++s) {
-            const int t = 2 * a + (kGroup == 4 ? (s >> 1) : s);
-            const int ww = kGroup == 4 ? 2 * c + (s & 1) : c;
-            member[s] = (t < Tt && ww < Wt) ? (t * Ht + hh) * Wt + ww : -1;
-        }
-    } else {
-#pragma unroll
-        for (int s = 0; s < kGroup; ++s) {
-            const int i = gi * kGroup + s;
-            member[s] = i < nb ? i : -1;
-        }
-    }
+    for (int s = 0; s < kGroup; ++s) member[s] = group_member(gi, s, Tt, Ht, Wt, nb);
 
     // ---- per-member bitmaps of listed blocks, and their union
     for (int e = tid; e < kGroup * kMaxWords; e += kAttnThreads) (&sh.qmask[0][0])[e] = 0ull;
@@ -135,12 +243,10 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     for (int s = 0; s < kGroup; ++s) {
         if (member[s] < 0) continue;
         const int64_t row = (int64_t)bh * nb + member[s];
-        int n = kv_nb[row];
-        n = n < 0 ? 0 : (n > nb ? nb : n);
+        const int n = clamp_count(kv_nb[row], nb);
         const int32_t *list = kv_inds + row * nb;
         for (int e = tid; e < n; e += kAttnThreads) {
-            int j = list[e];
-            j = j < 0 ? 0 : (j >= nb ? nb - 1 : j);
+            const int j = clamp_block(list[e], nb);
             atomicOr((unsigned long long *)&sh.qmask[s][j >> 6], 1ull << (j & 63));
         }
     }
@@ -194,28 +300,52 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     int mword = -1;
     uint64_t mbits = 0ull;
 
-    // ---- staging: K and V chunks of one tile in registers
-    bf16x8 kst[CPT], vst[CPT];
-    auto fetch = [&](int j) {
+    // ---- tile loads.  bf16: straight into LDS (lds_direct16), chunk e = r*threads + tid
+    // of the tile lands at byte 16e of the stage, i.e. row e / CH, swizzled position
+    // e % CH, so the lane fetches global chunk (e % CH) ^ swizzle(row).  fp32: through
+    // registers (rounded to bf16), stored to the stage after the tile's compute.
+    constexpr bool kDirect = sizeof(Tin) == 2;
+    bf16x8 kst[kDirect ? 1 : CPT], vst[kDirect ? 1 : CPT];
+    auto issue = [&](int j, int stage) {
         const Tin *kb = k + head0 + (int64_t)j * kBlock * tok;
         const Tin *vb = v + head0 + (int64_t)j * kBlock * tok;
 #pragma unroll
         for (int r = 0; r < CPT; ++r) {
             const int e = r * kAttnThreads + tid;
-            const int kv = e / CH, c = e % CH;
-            kst[r] = load8_bf16(kb + (int64_t)kv * tok + 8 * c);
-            vst[r] = load8_bf16(vb + (int64_t)kv * tok + 8 * c);
+            const int kv = e / CH, cpos = e % CH;
+            if constexpr (kDirect) {
+                const uint32_t m0k = __builtin_amdgcn_readfirstlane(
+                    lds_offset(sh.ks[stage]) + (r * kAttnThreads + w * 64) * 16);
+                const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+                    lds_offset(sh.vs[stage]) + (r * kAttnThreads + w * 64) * 16);
+                lds_direct16(kb + (int64_t)kv * tok + 8 * (cpos ^ kswz<CH>(kv)), m0k);
+                lds_direct16(vb + (int64_t)kv * tok + 8 * (cpos ^ vswz<CH>(kv)), m0v);
+            } else {
+                kst[r] = load8_bf16(kb + (int64_t)kv * tok + 8 * cpos);
+                vst[r] = load8_bf16(vb + (int64_t)kv * tok + 8 * cpos);
+            }
         }
     };
-    auto stash = [&](int stage) {
-        char *kd = reinterpret_cast<char *>(sh.ks[stage]);
-        char *vd = reinterpret_cast<char *>(sh.vs[stage]);
+    auto land = [&](int stage) {  // fp32 path: registers -> stage
+        if constexpr (!kDirect) {
+            char *kd = reinterpret_cast<char *>(sh.ks[stage]);
+            char *vd = reinterpret_cast<char *>(sh.vs[stage]);
 #pragma unroll
-        for (int r = 0; r < CPT; ++r) {
-            const int e = r * kAttnThreads + tid;
-            const int kv = e / CH, c = e % CH;
-            *reinterpret_cast<bf16x8 *>(kd + kv * ROWB + ((c ^ kswz<CH>(kv)) << 4)) = kst[r];
-            *reinterpret_cast<bf16x8 *>(vd + kv * ROWB + ((c ^ vswz<CH>(kv)) << 4)) = vst[r];
+            for (int r = 0; r < CPT; ++r) {
+                const int e = r * kAttnThreads + tid;
+                const int kv = e / CH, c = e % CH;
+                *reinterpret_cast<bf16x8 *>(kd + kv * ROWB + ((c ^ kswz<CH>(kv)) << 4)) = kst[r];
+                *reinterpret_cast<bf16x8 *>(vd + kv * ROWB + ((c ^ vswz<CH>(kv)) << 4)) = vst[r];
+            }
+        }
+    };
+    // bf16: wait until only the loads issued for the newest tile (if any) are in flight
+    auto settle = [&](bool newest_in_flight) {
+        if constexpr (kDirect) {
+            if (newest_in_flight)
+                vm_wait<2 * CPT>();
+            else
+                vm_wait<0>();
         }
     };
 
@@ -228,24 +358,27 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     bool m_valid = false;     // set by the row's first tile
     float l_run = 0.0f;       // this lane's part of the row sum
 
-    int cur = next_block();
-    int nxt = -1;
+    // ---- the walk over union tiles u_0, u_1, ...; u_k lives in LDS stage k % 3.
+    // Step k: start loading u_{k+2} (its stage held u_{k-1}, released at the last
+    // barrier), compute u_k, make sure u_{k+1} has landed, barrier.
+    int cur = next_block();  // u_k
+    int n1 = -1;             // u_{k+1}
     if (cur >= 0) {
-        fetch(cur);
-        stash(0);
-        nxt = next_block();
-        if (nxt >= 0) fetch(nxt);
+        issue(cur, 0);
+        land(0);
+        n1 = next_block();
+        if (n1 >= 0) {
+            issue(n1, 1);
+            land(1);
+        }
+        settle(n1 >= 0);
     }
     __syncthreads();
 
-    for (int it = 0; cur >= 0; ++it) {
-        const int stage = it & 1;
-        int nxt2 = -1;
-        if (nxt >= 0) {
-            stash(stage ^ 1);  // tile it+1 -> the other stage (free since the last barrier)
-            nxt2 = next_block();
-            if (nxt2 >= 0) fetch(nxt2);
-        }
+    for (int stage = 0; cur >= 0; stage = stage == kStages - 1 ? 0 : stage + 1) {
+        const int n2 = n1 >= 0 ? next_block() : -1;  // u_{k+2}
+        const int stage2 = stage == 0 ? 2 : stage - 1;
+        if (n2 >= 0) issue(n2, stage2);
         if (myblk >= 0 && (cur >> 6) != mword) {
             mword = cur >> 6;
             mbits = uniform_u64(sh.qmask[slot][mword]);
@@ -343,12 +476,14 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
                                                                        oacc[dt], 0, 0, 0);
             }
         }
-        __syncthreads();  // stage it+1 written; everyone done with stage it
-        cur = nxt;
-        nxt = nxt2;
+        if (n2 >= 0) land(stage2);
+        settle(n2 >= 0);
+        __syncthreads();  // u_{k+1} has landed; everyone is done with u_k's stage
+        cur = n1;
+        n1 = n2;
     }
 
-    if (myblk < 0) return;
+    if (myblk >= 0) {
     const float lsum = l_run + __shfl_xor(l_run, 32);
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;  // empty list -> O = 0
     Tin *orow = o + head0 + (int64_t)qtok * tok;
@@ -369,37 +504,84 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
             }
         }
     }
+    }  // myblk >= 0
+    __syncthreads();  // the next group reuses the LDS
+    }  // persistent loop
+}
+
+// ---- host side
+
+static int groups_per_bh(int S, int Tt, int Ht, int Wt) {
+    const int nb = S / kBlock;
+    return Tt > 0 ? ((Tt + 1) / 2) * Ht * (kGroup == 4 ? (Wt + 1) / 2 : Wt)
+                  : (nb + kGroup - 1) / kGroup;
+}
+
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace: [counter | cost[ngroups] | order[ngroups]], each part 256-byte aligned.
+size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt) {
+    const size_t ngroups = (size_t)B * heads * groups_per_bh(S, Tt, Ht, Wt);
+    return 256 + 2 * round256(ngroups * sizeof(int32_t));
+}
+
+// Workgroups of `kernel` the device holds at once (occupancy x CUs), cached per device.
+template <typename K>
+static int resident_workgroups(K kernel) {
+    constexpr int kMaxDevices = 64;
+    static int cache[kMaxDevices];  // 0 = not yet known; a racing first call stores the same value
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    if (cache[dev] > 0) return cache[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kAttnThreads, 0) !=
+            hipSuccess)
+        return 0;
+    cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
+    return cache[dev];
 }
 
 template <int D, typename Tin>
 static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int B, int S,
                                 int heads, int Tt, int Ht, int Wt, const int32_t *kv_nb,
-                                const int32_t *kv_inds, float scale_log2, void *o,
+                                const int32_t *kv_inds, float scale_log2, void *o, void *ws,
                                 hipStream_t stream) {
     const int nb = S / kBlock;
-    const int gpb = Tt > 0 ? ((Tt + 1) / 2) * Ht * (kGroup == 4 ? (Wt + 1) / 2 : Wt)
-                           : (nb + kGroup - 1) / kGroup;
+    const int gpb = groups_per_bh(S, Tt, Ht, Wt);
     const int ngroups = B * heads * gpb;
-    hipLaunchKernelGGL((sparse_attn_kernel<D, Tin>), dim3(ngroups), dim3(kAttnThreads), 0, stream,
-                       (const Tin *)q, (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, Tt, Ht,
-                       Wt, gpb, ngroups, kv_nb, kv_inds, scale_log2);
+    char *wsb = static_cast<char *>(ws);
+    int32_t *counter = reinterpret_cast<int32_t *>(wsb);
+    int32_t *cost = reinterpret_cast<int32_t *>(wsb + 256);
+    int32_t *order = reinterpret_cast<int32_t *>(wsb + 256 + round256((size_t)ngroups * 4));
+    hipLaunchKernelGGL(attn_plan_cost_kernel, dim3(ngroups), dim3(256), 0, stream, kv_nb, kv_inds,
+                       nb, Tt, Ht, Wt, gpb, cost, counter);
+    hipLaunchKernelGGL(attn_plan_order_kernel, dim3(1), dim3(1024), 0, stream, cost, ngroups, nb,
+                       order);
+    const auto kernel = sparse_attn_kernel<D, Tin>;
+    const int resident = resident_workgroups(kernel);
+    if (resident <= 0) return hipErrorInvalidDevice;
+    const int grid = ngroups < resident ? ngroups : resident;
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kAttnThreads), 0, stream, (const Tin *)q,
+                       (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, Tt, Ht, Wt, gpb,
+                       ngroups, kv_nb, kv_inds, scale_log2, order, counter);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
                               int B, int S, int heads, int D, int Tt, int Ht, int Wt,
                               const int32_t *kv_nb, const int32_t *kv_inds, float scale, void *o,
-                              hipStream_t stream) {
+                              void *ws, hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
     if (D == 128)
         return bf16_in ? launch_attn_t<128, bf16>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb,
-                                                  kv_inds, scale_log2, o, stream)
+                                                  kv_inds, scale_log2, o, ws, stream)
                        : launch_attn_t<128, float>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb,
-                                                   kv_inds, scale_log2, o, stream);
+                                                   kv_inds, scale_log2, o, ws, stream);
     return bf16_in ? launch_attn_t<64, bf16>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds,
-                                             scale_log2, o, stream)
+                                             scale_log2, o, ws, stream)
                    : launch_attn_t<64, float>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds,
-                                              scale_log2, o, stream);
+                                              scale_log2, o, ws, stream);
 }
 
 }  // namespace nabla

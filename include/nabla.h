@@ -13,12 +13,15 @@
  *
  * Conventions for every call
  *   - Tensors are device pointers in HBM, contiguous, row-major, owned by the
- *     caller.  Inputs are never written.  The library allocates nothing.
+ *     caller.  Inputs are never written.  The library allocates nothing: the
+ *     calls that need scratch memory take a caller-owned workspace.
  *   - q, k, v, o use [B, S, heads, head_dim] (the layout of the pages'
  *     attention forward), S = T*H*W in fractal token order, S % 64 == 0.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *     enqueues work on that stream and returns; there is no global mutable
- *     state, so calls on different streams may run concurrently.
+ *     enqueues work on that stream and returns.  The library keeps no state
+ *     between calls beyond a per-device cache of the GPU's compute-unit count,
+ *     so calls on different streams (with separate workspaces) may run
+ *     concurrently.
  *   - Every call validates its arguments on the host before any launch and
  *     returns a nabla_status; nothing is enqueued unless the result is
  *     NABLA_OK.  NABLA_ERR_HIP reports a failed launch (hipGetLastError).
@@ -123,6 +126,14 @@ nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, i
                               void *stream);
 
 /*
+ * Bytes of workspace nabla_sparse_attn_fwd needs for the same (B, S, heads) and tile
+ * grid: 256 + 2 * round_up(4 * ngroups, 256), where ngroups = B * heads *
+ * ceil(Tt/2) * Ht * ceil(Wt/2) (tile grid known) or B * heads * ceil(S/256)
+ * (unknown grid).  0 if the sizes or the grid are invalid.
+ */
+size_t nabla_sparse_attn_workspace(int B, int S, int heads, int Tt, int Ht, int Wt);
+
+/*
  * Block-sparse attention forward over the kept blocks ("nabla" page,
  * NablaAttentionImpl.forward: flex attention with a block mask of full
  * 64 x 64 blocks, no intra-block masking; NABLA summary page, Methodology,
@@ -143,15 +154,20 @@ nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, i
  *           blocks share K/V tiles on chip.  All three 0 = unknown (blocks
  *           are then grouped in runs of consecutive indices).
  * o:        out [B, S, heads, head_dim], same dtype as q; must not overlap inputs.
+ * ws:       device workspace of at least nabla_sparse_attn_workspace() bytes
+ *           (the call's work schedule; overwritten, no contents carried between
+ *           calls).  Calls that share one workspace must be on one stream.
  * Errors: INVALID_ARG (NULL pointer, sizes < 1, S % 64 != 0, NaN scale, a
  * tile grid that does not multiply to S/64); UNSUPPORTED (head_dim not 64 or
- * 128, or S/64 > 4096).  List contents are not checked on the host; entries
- * outside [0, nb) are clamped by the kernel.
+ * 128, or S/64 > 4096); WORKSPACE (ws NULL or ws_bytes too small).  List
+ * contents are not checked on the host; entries outside [0, nb) are clamped by
+ * the kernel.
  */
 nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
                                    nabla_dtype dtype, int B, int S, int heads, int head_dim,
                                    const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                                   int Tt, int Ht, int Wt, void *o, void *stream);
+                                   int Tt, int Ht, int Wt, void *o, void *ws, size_t ws_bytes,
+                                   void *stream);
 
 #ifdef __cplusplus
 }

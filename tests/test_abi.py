@@ -37,14 +37,14 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(names) == {"nabla_abi_version", "nabla_status_string", "nabla_fractal_permute",
                           "nabla_sta_mask", "nabla_block_mask_workspace", "nabla_block_mask",
-                          "nabla_sparse_attn_fwd"}
+                          "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 2
+    assert L.nabla_abi_version() == 3
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"
@@ -80,12 +80,23 @@ def test_block_mask_validation(L):
     assert call(wsb=L.nabla_block_mask_workspace(1, 8192, 8, 128) - 1) == WS
 
 
+def test_sparse_attn_workspace_size(L):
+    # 720p tile grid 16 x 6 x 10: 8 * 6 * 5 = 240 groups per head
+    ng = 16 * 240
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert L.nabla_sparse_attn_workspace(1, 61440, 16, 16, 6, 10) == 256 + 2 * rnd(4 * ng)
+    # unknown grid: groups of 4 consecutive blocks
+    assert L.nabla_sparse_attn_workspace(2, 64 * 10, 3, 0, 0, 0) == 256 + 2 * rnd(4 * 2 * 3 * 3)
+    assert L.nabla_sparse_attn_workspace(1, 61440, 16, 16, 6, 9) == 0   # grid != S/64
+    assert L.nabla_sparse_attn_workspace(1, 100, 16, 0, 0, 0) == 0
+
+
 def test_sparse_attn_validation(L):
     f = L.nabla_sparse_attn_fwd
 
     def call(q=FAKE, dt=BF16, B=1, S=8192, h=8, D=128, kv_nb=FAKE, scale=0.0, o=FAKE,
-             tiles=(8, 4, 4)):
-        return f(q, FAKE, FAKE, dt, B, S, h, D, kv_nb, FAKE, scale, *tiles, o, None)
+             tiles=(8, 4, 4), ws=FAKE, wsb=1 << 40):
+        return f(q, FAKE, FAKE, dt, B, S, h, D, kv_nb, FAKE, scale, *tiles, o, ws, wsb, None)
 
     assert call(q=None) == INVALID
     assert call(o=None) == INVALID
@@ -98,6 +109,8 @@ def test_sparse_attn_validation(L):
     assert call(D=32) == UNSUP
     assert call(D=256) == UNSUP
     assert call(S=64 * 4097, tiles=(0, 0, 0)) == UNSUP
+    assert call(ws=None) == WS
+    assert call(wsb=L.nabla_sparse_attn_workspace(1, 8192, 8, 8, 4, 4) - 1) == WS
 
 
 def test_permute_and_sta_validation(L):
