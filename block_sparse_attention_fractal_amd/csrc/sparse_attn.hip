@@ -68,6 +68,39 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ __forceinline__ f32x16 splat16(float x) {
+    f32x16 r;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = x;
+    return r;
+}
+
+__device__ __forceinline__ float max16(const f32x16 &s) {
+    float x = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int j = 2; j < 16; ++j) x = fmaxf(x, s[j]);
+    return x;
+}
+
+// Weights p = exp2(logit) of one 32-key half packed to bf16 (pb[p]: registers 8p ..
+// 8p+7, the P V B operand of 16 consecutive keys); returns their sum, taken as a bf16
+// dot product with ones so that the row sum uses exactly the weights P V uses.
+__device__ __forceinline__ float expand(const f32x16 &s, bf16x8 (&pb)[2]) {
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pb[j >> 3][j & 7] = (bf16)__builtin_amdgcn_exp2f(s[j]);
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    float part[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pb[pp][e], pb[pp][e + 1]};
+            part[pp] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, part[pp], false);
+        }
+    return part[0] + part[1];
+}
+
 // 16-byte chunk swizzles (CH chunks per row) of the K and V tiles in LDS.
 template <int CH>
 __device__ __forceinline__ int kswz(int kv) { return kv & (CH - 1); }
@@ -355,6 +388,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[dt][j] = 0.0f;
     float m_ref = 0.0f;       // reference max of the row, log2 units (raised lazily)
+    f32x16 minit = splat16(0.0f);  // -m_ref in every element: the score accumulators' start
     bool m_valid = false;     // set by the row's first tile
     float l_run = 0.0f;       // this lane's part of the row sum
 
@@ -387,14 +421,12 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
         if (mine) {
             const char *kb = reinterpret_cast<const char *>(sh.ks[stage]);
             const char *vb = reinterpret_cast<const char *>(sh.vs[stage]);
-            // S^T - m = K Q^T (log2 units) for the two 32-key halves of the tile; the
-            // accumulators start at -m so the MFMAs also subtract the reference max
-            const float init = m_valid ? -m_ref : 0.0f;
+            // S^T - m = K Q^T (log2 units) for the two 32-key halves of the tile: the
+            // first k-step reads its accumulator input from the -m block, so the MFMAs
+            // also subtract the reference max
             f32x16 sacc[2];
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-                for (int j = 0; j < 16; ++j) sacc[mt][j] = init;
                 const int kv = 32 * mt + sigma32(l32);
                 const char *krow = kb + kv * ROWB;
 #pragma unroll
@@ -402,18 +434,20 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
                     const int c = 2 * ks + hi;
                     const bf16x8 a =
                         *reinterpret_cast<const bf16x8 *>(krow + ((c ^ kswz<CH>(kv)) << 4));
-                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[mt], 0, 0, 0);
+                    sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a, qf[ks], ks == 0 ? minit : sacc[mt], 0, 0, 0);
                 }
             }
-            // Lazy reference max: only when this lane's logits exceed the reference by
-            // more than 16 (log2 units), or on the row's first tile, is the reference
-            // raised to the row max and O, l rescaled (wave-uniform branch).
-            float lm = fmaxf(sacc[0][0], sacc[1][0]);
-#pragma unroll
-            for (int j = 1; j < 16; ++j) lm = fmaxf(lm, fmaxf(sacc[0][j], sacc[1][j]));
-            const bool need = !m_valid || lm > 16.0f;
-            if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-                const float rm = fmaxf(lm, __shfl_xor(lm, 32));  // row max (shifted units)
+            bf16x8 pb[2][2];
+            float part = expand(sacc[0], pb[0]) + expand(sacc[1], pb[1]);
+            // Lazy reference max.  The weights are formed against the current
+            // reference; only when this lane's 32 weights of the tile sum to more
+            // than 2^16 (a logit far above the reference; also inf), or on the row's
+            // first tile, is the reference raised to the row max, O and l rescaled
+            // and the weights formed again (wave-uniform branch, rare).
+            if (__builtin_amdgcn_ballot_w64(!m_valid || !(part <= 65536.0f)) != 0ull) {
+                const float lm = fmaxf(max16(sacc[0]), max16(sacc[1]));
+                const float rm = fmaxf(lm, __shfl_xor(lm, 32));   // row max (shifted units)
                 const bool row_need = !m_valid || rm > 16.0f;     // same in lanes l, l^32
                 const float delta = row_need ? rm : 0.0f;
                 const float alpha = m_valid ? __builtin_amdgcn_exp2f(-delta) : 0.0f;
@@ -424,29 +458,10 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
                 for (int mt = 0; mt < 2; ++mt) sacc[mt] -= delta;
                 m_ref = (m_valid ? m_ref : 0.0f) + delta;
                 m_valid = true;
+                minit = splat16(-m_ref);
+                part = expand(sacc[0], pb[0]) + expand(sacc[1], pb[1]);
             }
-            bf16x8 pb[2][2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    pb[mt][j >> 3][j & 7] = (bf16)__builtin_amdgcn_exp2f(sacc[mt][j]);
-            // row sum of the bf16 weights the P V product uses (dot with ones)
-            {
-                typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-                float part[2] = {0.0f, 0.0f};
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int p = 0; p < 2; ++p)
-#pragma unroll
-                        for (int e = 0; e < 8; e += 2) {
-                            const bf16x2 pr = {pb[mt][p][e], pb[mt][p][e + 1]};
-                            part[p] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, part[p], false);
-                        }
-                l_run += part[0] + part[1];
-            }
+            l_run += part;
             // O^T += V^T P^T: 4 k-steps of 16 keys (mt, p); the 8 transpose reads of
             // an output d-tile are issued together, ahead of its 4 MFMAs
 #pragma unroll
