@@ -38,7 +38,9 @@
 namespace nabla {
 
 // ---------------------------------------------------------------- pool
-// grid (nb, B, 2): z = 0 pools q into qa, z = 1 pools k into ka.
+// grid (nb, B): block i of q is pooled into qa [B*heads][nb][D] and block i of k into
+// ka [B*heads][D/4][nb][4].  One workgroup does both, so that the whole grid is resident
+// at once (no partial second round of workgroups).
 template <typename Tin>
 __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
                                                    const Tin *__restrict__ k,
@@ -48,12 +50,15 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
     constexpr int EPC = 16 / sizeof(Tin);  // elements per 16-byte chunk
     const int nb = S / kBlock;
     const int i = blockIdx.x, b = blockIdx.y;
-    const Tin *x = blockIdx.z ? k : q;
-    float *xa = blockIdx.z ? ka : qa;
     const int row_elems = heads * D;
     const int nchunks = row_elems / EPC;
+    for (int item = threadIdx.x; item < 2 * nchunks; item += 256) {
+    const int z = item >= nchunks;  // 0: q, 1: k
+    const int ch = item - z * nchunks;
+    const Tin *x = z ? k : q;
+    float *xa = z ? ka : qa;
     const Tin *base = x + ((int64_t)b * S + (int64_t)i * kBlock) * row_elems;
-    for (int ch = threadIdx.x; ch < nchunks; ch += 256) {
+    {
         float acc[EPC];
 #pragma unroll
         for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
@@ -83,12 +88,18 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
         }
         const int el = ch * EPC;
         const int h = el / D, d = el - h * D;
-        float *out = xa + (((int64_t)b * heads + h) * nb + i) * D + d;
+        const int64_t bhh = (int64_t)b * heads + h;
 #pragma unroll
-        for (int e = 0; e < EPC; e += 4)
-            *reinterpret_cast<float4 *>(out + e) =
+        for (int e = 0; e < EPC; e += 4) {
+            // q: row-major [bh][nb][D]; k: [bh][D/4][nb] float4s, so that the score loop
+            // reads the k means of consecutive blocks from consecutive addresses
+            float *out = z ? xa + ((bhh * (D / 4) + (d + e) / 4) * nb + i) * 4
+                           : xa + (bhh * nb + i) * D + d + e;
+            *reinterpret_cast<float4 *>(out) =
                 make_float4(acc[e] * 0.015625f, acc[e + 1] * 0.015625f, acc[e + 2] * 0.015625f,
                             acc[e + 3] * 0.015625f);
+        }
+    }
     }
 }
 
@@ -122,8 +133,19 @@ __device__ __forceinline__ float f32_from_orderable(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// floor(v * 2^48) for 0 <= v <= 1 (exact through double).
-__device__ __forceinline__ int64_t fix48(float v) { return (int64_t)((double)v * 0x1p48); }
+// floor(v * 2^48) for 0 <= v <= 1, exactly: v = m * 2^(u - 23) with the 24-bit
+// significand m and unbiased exponent u <= 0, so v * 2^48 = m * 2^(u + 25), an integer
+// shift of m (right shifts truncate, which is the floor for v >= 0).  Denormals and 0
+// give 0 (below 2^-78).
+__device__ __forceinline__ int64_t fix48(float v) {
+    const uint32_t bits = __float_as_uint(v);
+    const int biased = (int)(bits >> 23) & 0xff;
+    if (biased == 0) return 0;
+    const uint64_t m = (uint64_t)((bits & 0x7fffffu) | 0x800000u);
+    const int sh = biased - 127 + 25;
+    if (sh >= 0) return (int64_t)(m << sh);
+    return sh > -64 ? (int64_t)(m >> -sh) : 0;
+}
 
 template <int NW>
 struct SelectShared {
@@ -168,8 +190,284 @@ __device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
     return v;
 }
 
-// ---------------------------------------------------------------- select
-// grid (ceil(nb / R), B*heads); 512 lanes; lane t owns columns j = c*512 + t, c < CPT.
+// ---------------------------------------------------------------- select (rows <= 2048)
+// One wave owns RW whole rows: lane l holds the scores of columns j = 64c + l (c < CPT)
+// of each of them, so the selection of a row is wave-local work with no barrier.
+//
+// Scores: the k means are read as float4s of consecutive blocks (coalesced, shared by
+// the waves of the workgroup through L1); the q means of the wave's rows sit in LDS
+// and are read as broadcasts.  Every score is the same sequential fma chain over d as
+// above.
+//
+// Cut: the smallest key T whose inclusive prefix mass reaches cut.  One histogram pass
+// over kSelBins bins of the score range [smin, smax] finds the bin holding it (the bin
+// index is a monotone function of the score, so all keys of earlier bins are smaller
+// and their exact mass is the prefix before the bin); the keys of that bin are then
+// ranked exactly (at most 64 of them: one per lane), or, when more share the bin (ties,
+// flat rows), the bin's key range is refined by further histogram passes first.
+constexpr int kSelBins = 256;
+
+struct SelectWaveScratch {
+    int64_t hm[kSelBins];  // bin masses
+    int hc[kSelBins];      // bin counts
+    uint64_t lkey[64];     // keys of the cut bin
+    int64_t lmass[64];
+};
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+__device__ __forceinline__ float wave_min_f32(float v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = fminf(v, __shfl_xor(v, m));
+    return v;
+}
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+    const uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int D, int CPT, int RW>
+__global__ __launch_bounds__(256) void select_rows_kernel(const float *__restrict__ qa,
+                                                          const float *__restrict__ ka, int nb,
+                                                          const uint8_t *__restrict__ sta,
+                                                          float sqrt_d, int64_t cut,
+                                                          int32_t *__restrict__ kv_nb,
+                                                          int32_t *__restrict__ kv_inds) {
+    constexpr int NWV = 4;
+    __shared__ __attribute__((aligned(16))) float qs[NWV][RW][D];
+    __shared__ SelectWaveScratch scr[NWV];
+    const int bh = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int row0 = (blockIdx.x * NWV + wv) * RW;
+    if (row0 >= nb) return;  // no barrier in this kernel: waves are independent
+    SelectWaveScratch &W = scr[wv];
+    const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+
+    for (int e = lane; e < RW * D; e += 64) {
+        const int r = e / D, d = e - r * D;
+        qs[wv][r][d] = row0 + r < nb ? qa[((int64_t)bh * nb + row0 + r) * D + d] : 0.0f;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- scores (before the division by sqrt(D))
+    float acc[RW][CPT];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0f;
+    const float4 *kb = reinterpret_cast<const float4 *>(ka) + (int64_t)bh * (D / 4) * nb;
+#pragma unroll 1
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+        float4 k4[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int j = 64 * c + lane;
+            k4[c] = j < nb ? kb[(int64_t)d4 * nb + j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const float4 q4 = *reinterpret_cast<const float4 *>(&qs[wv][r][4 * d4]);
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                acc[r][c] = __builtin_fmaf(q4.x, k4[c].x, acc[r][c]);
+                acc[r][c] = __builtin_fmaf(q4.y, k4[c].y, acc[r][c]);
+                acc[r][c] = __builtin_fmaf(q4.z, k4[c].z, acc[r][c]);
+                acc[r][c] = __builtin_fmaf(q4.w, k4[c].w, acc[r][c]);
+            }
+        }
+    }
+
+    // ---- per row: softmax on the 2^-48 grid, cut key, STA union, compaction
+#pragma unroll 1
+    for (int r = 0; r < RW; ++r) {
+        const int i = row0 + r;
+        if (i >= nb) break;  // wave-uniform
+        const int64_t row = (int64_t)bh * nb + i;
+        float s[CPT];
+        bool valid[CPT];
+        float smax = -INFINITY, smin = INFINITY;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            float a = 0.0f;
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr)
+                if (rr == r) a = acc[rr][c];
+            s[c] = a / sqrt_d + 0.0f;
+            valid[c] = 64 * c + lane < nb;
+            if (valid[c]) {
+                smax = fmaxf(smax, s[c]);
+                smin = fminf(smin, s[c]);
+            }
+        }
+        smax = wave_max_f32(smax);
+        smin = wave_min_f32(smin);
+        auto key_of = [&](int c) -> uint64_t {
+            return ((uint64_t)f32_orderable(s[c]) << 12) | (uint64_t)(64 * c + lane);
+        };
+
+        // (the weights are formed twice, for Z and for P, rather than kept: fewer
+        // registers live at once)
+        int64_t esum = 0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) esum += fix48(valid[c] ? nabla_exp(s[c] - smax) : 0.0f);
+        esum = wave_sum_i64(esum);
+        const float Z = (float)(double)esum * 0x1p-48f;
+        int64_t P[CPT];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? fix48(nabla_exp(s[c] - smax) / Z) : 0;
+
+        // One histogram pass over the members (inr) into kSelBins bins (bin_of); returns
+        // the bin holding the cut (-1 if the members' mass stays below it) with the mass
+        // before it and its count.
+        auto hist_pass = [&](auto inr, auto bin_of, int64_t below, int64_t &bbelow, int &bcnt) {
+#pragma unroll
+            for (int q = 0; q < kSelBins / 64; ++q) {
+                W.hm[lane * (kSelBins / 64) + q] = 0;
+                W.hc[lane * (kSelBins / 64) + q] = 0;
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                if (inr(c)) {
+                    const int bn = bin_of(c);
+                    atomicAdd((unsigned long long *)&W.hm[bn], (unsigned long long)P[c]);
+                    atomicAdd(&W.hc[bn], 1);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            int64_t m[kSelBins / 64];
+            int64_t tot = 0;
+#pragma unroll
+            for (int q = 0; q < kSelBins / 64; ++q) {
+                m[q] = W.hm[lane * (kSelBins / 64) + q];
+                tot += m[q];
+            }
+            int64_t run = below + wave_incl_scan_i64(tot, lane) - tot;
+            int found = -1, fcnt = 0;
+            int64_t fb = 0;
+#pragma unroll
+            for (int q = 0; q < kSelBins / 64; ++q) {
+                if (found < 0 && run < cut && run + m[q] >= cut) {
+                    found = lane * (kSelBins / 64) + q;
+                    fb = run;
+                    fcnt = W.hc[found];
+                }
+                run += m[q];
+            }
+            const uint64_t bal = __ballot(found >= 0);
+            if (bal == 0ull) return -1;
+            const int src = __builtin_ctzll(bal);
+            bbelow = (int64_t)shfl_u64((uint64_t)fb, src);
+            bcnt = __shfl(fcnt, src);
+            return __shfl(found, src);
+        };
+        // Exact rank of at most 64 members: the smallest key whose prefix reaches the cut.
+        auto rank_list = [&](auto inr, int64_t below) -> uint64_t {
+            int n = 0;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const bool in = inr(c);
+                const uint64_t bal = __ballot(in);
+                if (in) {
+                    const int pos = n + __popcll(bal & lanes_below);
+                    W.lkey[pos] = key_of(c);
+                    W.lmass[pos] = P[c];
+                }
+                n += __popcll(bal);
+            }
+            __builtin_amdgcn_wave_barrier();
+            uint64_t best = ~0ull;
+            if (lane < n) {
+                const uint64_t k0 = W.lkey[lane];
+                int64_t pre = W.lmass[lane];
+#pragma unroll 8
+                for (int m = 0; m < n; ++m) pre += W.lkey[m] < k0 ? W.lmass[m] : 0;
+                if (below + pre >= cut) best = k0;
+            }
+            return wave_min_u64(best);
+        };
+
+        uint64_t T = 0;  // cut <= 0: every block is kept
+        if (cut > 0) {
+            const float range = smax - smin;
+            const float scale = range > 1e-30f ? (float)kSelBins / range : 0.0f;
+            auto bin_f = [&](int c) {
+                const int bi = (int)((s[c] - smin) * scale);
+                return bi > kSelBins - 1 ? kSelBins - 1 : bi;
+            };
+            int64_t below = 0;
+            int cnt = 0;
+            const int b = hist_pass([&](int c) { return valid[c]; }, bin_f, 0, below, cnt);
+            if (b < 0) {  // total mass below the cut: only the arg-max (largest key) stays
+                uint64_t km = 0;
+#pragma unroll
+                for (int c = 0; c < CPT; ++c)
+                    if (valid[c]) km = key_of(c) > km ? key_of(c) : km;
+                T = wave_max_u64(km);
+            } else if (cnt <= 64) {
+                T = rank_list([&](int c) { return valid[c] && bin_f(c) == b; }, below);
+            } else {
+                // many keys share the bin: narrow its key range by histogram passes
+                uint64_t lo = ~0ull, hi = 0;
+#pragma unroll
+                for (int c = 0; c < CPT; ++c)
+                    if (valid[c] && bin_f(c) == b) {
+                        const uint64_t kk = key_of(c);
+                        lo = kk < lo ? kk : lo;
+                        hi = kk > hi ? kk : hi;
+                    }
+                lo = wave_min_u64(lo);
+                hi = wave_max_u64(hi);
+                for (;;) {
+                    const uint64_t span = hi - lo;
+                    const int shift = span < (uint64_t)kSelBins ? 0 : 64 - __clzll((long long)span) - 8;
+                    auto inr = [&](int c) {
+                        const uint64_t kk = key_of(c);
+                        return valid[c] && kk >= lo && kk <= hi;
+                    };
+                    int64_t b2below = 0;
+                    int c2 = 0;
+                    const int b2 = hist_pass(inr, [&](int c) { return (int)((key_of(c) - lo) >> shift); },
+                                             below, b2below, c2);
+                    // b2 >= 0: the range holds the cut by construction
+                    const uint64_t nlo = lo + ((uint64_t)b2 << shift);
+                    const uint64_t nhi0 = nlo + ((1ull << shift) - 1);
+                    const uint64_t nhi = nhi0 < hi ? nhi0 : hi;
+                    if (c2 <= 64 || shift == 0 || b2 < 0) {
+                        T = rank_list([&](int c) {
+                            const uint64_t kk = key_of(c);
+                            return valid[c] && kk >= nlo && kk <= nhi;
+                        }, b2below);
+                        break;
+                    }
+                    lo = nlo;
+                    hi = nhi;
+                    below = b2below;
+                }
+            }
+        }
+
+        // kept = key >= T, or the STA window; kv_inds ascending (j = 64c + lane)
+        int base = 0;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            const int j = 64 * c + lane;
+            const bool kept =
+                valid[c] && (key_of(c) >= T || (sta != nullptr && sta[(int64_t)i * nb + j] != 0));
+            const uint64_t bal = __ballot(kept);
+            if (kept) kv_inds[row * nb + base + __popcll(bal & lanes_below)] = j;
+            base += __popcll(bal);
+        }
+        if (lane == 0) kv_nb[row] = base;
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// ---------------------------------------------------------------- select (long rows)
+// Rows of more than 2048 blocks.  grid (ceil(nb / R), B*heads); 512 lanes; lane t owns
+// columns j = c*512 + t, c < CPT; the whole workgroup works on one row at a time.
 template <int D, int CPT, int R>
 __global__ __launch_bounds__(512) void select_kernel(const float *__restrict__ qa,
                                                      const float *__restrict__ ka, int nb,
@@ -198,14 +496,13 @@ __global__ __launch_bounds__(512) void select_kernel(const float *__restrict__ q
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0f;
-    const float *kab = ka + (int64_t)bh * nb * D;
+    const float4 *kab = reinterpret_cast<const float4 *>(ka) + (int64_t)bh * (D / 4) * nb;
     for (int d = 0; d < D; d += 4) {
         float4 kv[CPT];
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
             const int j = c * NT + tid;
-            kv[c] = (j < nb) ? *reinterpret_cast<const float4 *>(kab + (int64_t)j * D + d)
-                             : make_float4(0.f, 0.f, 0.f, 0.f);
+            kv[c] = (j < nb) ? kab[(int64_t)(d / 4) * nb + j] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -383,16 +680,29 @@ static hipError_t launch_select_t(const float *qa, const float *ka, int BH, int 
     return hipGetLastError();
 }
 
+template <int D, int CPT, int RW>
+static hipError_t launch_rows_t(const float *qa, const float *ka, int BH, int nb,
+                                const uint8_t *sta, float sqrt_d, int64_t cut, int32_t *kv_nb,
+                                int32_t *kv_inds, hipStream_t stream) {
+    dim3 grid((nb + 4 * RW - 1) / (4 * RW), BH);
+    hipLaunchKernelGGL((select_rows_kernel<D, CPT, RW>), grid, dim3(256), 0, stream, qa, ka, nb,
+                       sta, sqrt_d, cut, kv_nb, kv_inds);
+    return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int nb,
                                   const uint8_t *sta, float sqrt_d, int64_t cut, int32_t *kv_nb,
                                   int32_t *kv_inds, hipStream_t stream) {
-    if (nb <= 512)
-        return launch_select_t<D, 1, 16>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
-    if (nb <= 1024)
-        return launch_select_t<D, 2, 16>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
-    if (nb <= 2048)
-        return launch_select_t<D, 4, 16>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
+#define NABLA_ROWS(CPT, RW) \
+    return launch_rows_t<D, CPT, RW>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream)
+    if (nb <= 64) NABLA_ROWS(1, 8);
+    if (nb <= 128) NABLA_ROWS(2, 8);
+    if (nb <= 256) NABLA_ROWS(4, 8);
+    if (nb <= 512) NABLA_ROWS(8, 8);
+    if (nb <= 1024) NABLA_ROWS(16, 4);
+    if (nb <= 2048) NABLA_ROWS(32, 2);
+#undef NABLA_ROWS
     return launch_select_t<D, 8, 8>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
 }
 
@@ -401,7 +711,7 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
                              float sqrt_d, int32_t *kv_nb, int32_t *kv_inds, float *qa,
                              float *ka, hipStream_t stream) {
     const int nb = S / kBlock;
-    dim3 pgrid(nb, B, 2);
+    dim3 pgrid(nb, B);
     if (bf16_in)
         hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
                            (const bf16 *)k, qa, ka, S, heads, D);
