@@ -54,6 +54,7 @@ constexpr int kAttnWaves = 2 * kGroup;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kMaxWords = 4096 / 64;  // bitmap words for up to 4096 blocks per row
 static_assert(kGroup == 2 || kGroup == 4, "group of 2 or 4 query blocks");
+static_assert(kAttnWaves == 8 || kGroup != 4, "the delayed half of the waves is waves 4-7");
 
 // Key row (within a 32-row score tile) fed to MFMA row m: bit layout
 // m = a(2) hh(1) b(2)  ->  key = (a>>1)<<4 | hh<<3 | (a&1)<<2 | b.
@@ -123,19 +124,29 @@ __device__ __forceinline__ void lds_direct16(const void *g, uint32_t m0) {
                  : "v"(g), "s"(m0)
                  : "memory");
 }
+// The same with a wave-uniform base address (SGPR pair) and a 32-bit per-lane byte
+// offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void lds_direct16_sv(const void *base, uint32_t off, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(m0)
+                 : "memory");
+}
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-constexpr int kStages = 3;  // LDS ring depth: tile k+2 lands while tile k is computed
+constexpr int kStages = 4;  // LDS ring: tiles k-1 (delayed P V), k, k+1, k+2 (landing)
 
 template <int D>
 struct AttnShared {
     bf16 ks[kStages][kBlock * D];
     bf16 vs[kStages][kBlock * D];
     uint64_t qmask[kGroup][kMaxWords];
-    uint64_t umask[kMaxWords];
+    uint16_t ulist[kMaxWords * 64];  // the union of the members' lists, ascending
+    uint8_t umem[kMaxWords * 64];    // bit s: member s lists that block
+    int ucount;
     int slot;  // the schedule position this workgroup works on
 };
 
@@ -284,17 +295,42 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
         }
     }
     __syncthreads();
-    for (int wd = tid; wd < nwords; wd += kAttnThreads)
-    {
+    // union list: wave 0, lane = 64-block word (at most 64 words); an exclusive scan
+    // of the words' popcounts places each lane's blocks
+    if (w == 0) {
         uint64_t u = 0ull;
+        if (lane < nwords) {
 #pragma unroll
-        for (int s = 0; s < kGroup; ++s) u |= sh.qmask[s][wd];
-        sh.umask[wd] = u;
+            for (int s = 0; s < kGroup; ++s) u |= sh.qmask[s][lane];
+        }
+        const int cnt = __popcll(u);
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        int pos = incl - cnt;
+        while (u != 0ull) {
+            const int bit = __builtin_ctzll(u);
+            u &= u - 1;
+            int mem = 0;
+#pragma unroll
+            for (int s = 0; s < kGroup; ++s) mem |= (int)((sh.qmask[s][lane] >> bit) & 1ull) << s;
+            sh.ulist[pos] = (uint16_t)(lane * 64 + bit);
+            sh.umem[pos] = (uint8_t)mem;
+            ++pos;
+        }
+        if (lane == 63) sh.ucount = incl;
     }
     __syncthreads();
+    const int U = sh.ucount;  // tiles in the walk
 
     // ---- this wave: member slot and 32-row half
-    const int slot = w >> 1;
+    // Waves w and w + 4 share a SIMD.  They take members of opposite corners of the
+    // 2 x 1 x 2 box (slots 0 and 3, or 1 and 2), whose lists overlap least, so that
+    // the two SIMD pairs of a step carry similar work.
+    const int slot = w < 4 ? (w >> 1) : 3 - ((w - 4) >> 1);
     const int myblk = member[slot];
     const int64_t tok = (int64_t)heads * D;
     const int64_t head0 = (int64_t)b * S * tok + (int64_t)h * D;
@@ -317,43 +353,36 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     // vmcnt) for the K/V prefetch issued just before them.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // ---- union cursor (wave-uniform, kept in scalar registers): ascending set bits of umask
-    int cur_word = 0;
-    uint64_t cur_bits = uniform_u64(sh.umask[0]);
-    auto next_block = [&]() -> int {
-        while (cur_bits == 0ull) {
-            if (++cur_word >= nwords) return -1;
-            cur_bits = uniform_u64(sh.umask[cur_word]);
-        }
-        const int bit = __builtin_ctzll(cur_bits);
-        cur_bits &= cur_bits - 1;
-        return (cur_word << 6) | bit;
-    };
-    // this wave's membership bits of word `mword` (scalar; reloaded when the walk moves on)
-    int mword = -1;
-    uint64_t mbits = 0ull;
-
     // ---- tile loads.  bf16: straight into LDS (lds_direct16), chunk e = r*threads + tid
     // of the tile lands at byte 16e of the stage, i.e. row e / CH, swizzled position
     // e % CH, so the lane fetches global chunk (e % CH) ^ swizzle(row).  fp32: through
     // registers (rounded to bf16), stored to the stage after the tile's compute.
     constexpr bool kDirect = sizeof(Tin) == 2;
     bf16x8 kst[kDirect ? 1 : CPT], vst[kDirect ? 1 : CPT];
-    auto issue = [&](int j, int stage) {
+    // per-lane byte offsets of the chunks within a tile (global side, swizzled)
+    uint32_t koff[CPT], voff[CPT];
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+        const int e = r * kAttnThreads + tid;
+        const int kv = e / CH, cpos = e % CH;
+        koff[r] = (uint32_t)((kv * tok + 8 * (cpos ^ kswz<CH>(kv))) * sizeof(Tin));
+        voff[r] = (uint32_t)((kv * tok + 8 * (cpos ^ vswz<CH>(kv))) * sizeof(Tin));
+    }
+    const uint32_t lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset(sh.ks[0]) + w * 64 * 16);
+    const uint32_t lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset(sh.vs[0]) + w * 64 * 16);
+    auto issue = [&](int jj, int stage) {
+        const int j = __builtin_amdgcn_readfirstlane(jj);  // wave-uniform block index
         const Tin *kb = k + head0 + (int64_t)j * kBlock * tok;
         const Tin *vb = v + head0 + (int64_t)j * kBlock * tok;
 #pragma unroll
         for (int r = 0; r < CPT; ++r) {
-            const int e = r * kAttnThreads + tid;
-            const int kv = e / CH, cpos = e % CH;
             if constexpr (kDirect) {
-                const uint32_t m0k = __builtin_amdgcn_readfirstlane(
-                    lds_offset(sh.ks[stage]) + (r * kAttnThreads + w * 64) * 16);
-                const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-                    lds_offset(sh.vs[stage]) + (r * kAttnThreads + w * 64) * 16);
-                lds_direct16(kb + (int64_t)kv * tok + 8 * (cpos ^ kswz<CH>(kv)), m0k);
-                lds_direct16(vb + (int64_t)kv * tok + 8 * (cpos ^ vswz<CH>(kv)), m0v);
+                const uint32_t sb = stage * (kBlock * D * 2) + r * kAttnThreads * 16;
+                lds_direct16_sv(kb, koff[r], lds_k0 + sb);
+                lds_direct16_sv(vb, voff[r], lds_v0 + sb);
             } else {
+                const int e = r * kAttnThreads + tid;
+                const int kv = e / CH, cpos = e % CH;
                 kst[r] = load8_bf16(kb + (int64_t)kv * tok + 8 * cpos);
                 vst[r] = load8_bf16(vb + (int64_t)kv * tok + 8 * cpos);
             }
@@ -382,6 +411,30 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
         }
     };
 
+    // V^T fragments of output d tile dt (A operands of the 4 P V k-steps kk = 2mt + p):
+    // lane group g16 = lane / 16, s = lane % 16 points at V[key 32mt + 16p + 8(g16/2) +
+    // 4r + s/4][d 32dt + 16(g16%2) + 4(s%4)], so the transpose read returns
+    // V^T[32dt + l32][8 consecutive keys]
+    auto vfrags_dt = [&](const char *vb, int dt, bf16x8 (&va)[4]) {
+        const int g16 = lane >> 4, sl = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int mt = kk >> 1, p = kk & 1;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int kv = 32 * mt + 16 * p + 8 * (g16 >> 1) + 4 * r + (sl >> 2);
+                const int d = 32 * dt + 16 * (g16 & 1) + 4 * (sl & 3);
+                const int c = (d >> 3) ^ vswz<CH>(kv);
+                const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (NABLA_LDS bf16x4 *)(vb + kv * ROWB + (c << 4) + (d & 7) * 2));
+                va[kk][4 * r + 0] = x[0];
+                va[kk][4 * r + 1] = x[1];
+                va[kk][4 * r + 2] = x[2];
+                va[kk][4 * r + 3] = x[3];
+            }
+        }
+    };
+
     f32x16 oacc[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -392,53 +445,43 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     bool m_valid = false;     // set by the row's first tile
     float l_run = 0.0f;       // this lane's part of the row sum
 
-    // ---- the walk over union tiles u_0, u_1, ...; u_k lives in LDS stage k % 3.
-    // Step k: start loading u_{k+2} (its stage held u_{k-1}, released at the last
-    // barrier), compute u_k, make sure u_{k+1} has landed, barrier.
-    int cur = next_block();  // u_k
-    int n1 = -1;             // u_{k+1}
-    if (cur >= 0) {
-        issue(cur, 0);
-        land(0);
-        n1 = next_block();
-        if (n1 >= 0) {
-            issue(n1, 1);
-            land(1);
-        }
-        settle(n1 >= 0);
-    }
-    __syncthreads();
-
-    for (int stage = 0; cur >= 0; stage = stage == kStages - 1 ? 0 : stage + 1) {
-        const int n2 = n1 >= 0 ? next_block() : -1;  // u_{k+2}
-        const int stage2 = stage == 0 ? 2 : stage - 1;
-        if (n2 >= 0) issue(n2, stage2);
-        if (myblk >= 0 && (cur >> 6) != mword) {
-            mword = cur >> 6;
-            mbits = uniform_u64(sh.qmask[slot][mword]);
-        }
-        const bool mine = myblk >= 0 && ((mbits >> (cur & 63)) & 1ull);
-        if (mine) {
+    // scores and softmax of the tile in `stage` -> packed weights pb (and O, l rescaled
+    // when the reference max moves)
+    auto score_softmax = [&](int stage, bf16x8 (&pb)[2][2]) {
             const char *kb = reinterpret_cast<const char *>(sh.ks[stage]);
-            const char *vb = reinterpret_cast<const char *>(sh.vs[stage]);
-            // S^T - m = K Q^T (log2 units) for the two 32-key halves of the tile: the
-            // first k-step reads its accumulator input from the -m block, so the MFMAs
-            // also subtract the reference max
+            // The LDS reads are issued well ahead of the MFMAs that use them (the
+            // sched_barrier fences keep the compiler from sinking them next to their
+            // uses): the K fragments of k-step ks + 3 under the score MFMAs of ks (a
+            // ring of four k-steps), the first d tile's V^T fragments under the last
+            // score MFMAs, and each next d tile's under the P V MFMAs of the current one.
+            constexpr int KLA = 3;  // k-steps of K fragments in flight ahead of the MFMAs
+            const int kv0 = sigma32(l32), kv1 = 32 + sigma32(l32);
+            const char *krow0 = kb + kv0 * ROWB, *krow1 = kb + kv1 * ROWB;
+            bf16x8 kf[KLA + 1][2];
+            auto kread = [&](int ks) {
+                const int c = 2 * ks + hi;
+                kf[ks & KLA][0] =
+                    *reinterpret_cast<const bf16x8 *>(krow0 + ((c ^ kswz<CH>(kv0)) << 4));
+                kf[ks & KLA][1] =
+                    *reinterpret_cast<const bf16x8 *>(krow1 + ((c ^ kswz<CH>(kv1)) << 4));
+            };
+#pragma unroll
+            for (int ks = 0; ks < KLA; ++ks) kread(ks);
+            // S^T - m = K Q^T (log2 units) for the two 32-key halves (two MFMA chains):
+            // the first k-step reads its accumulator input from the -m block, so the
+            // MFMAs also subtract the reference max
             f32x16 sacc[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int kv = 32 * mt + sigma32(l32);
-                const char *krow = kb + kv * ROWB;
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + KLA < KS) kread(ks + KLA);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int c = 2 * ks + hi;
-                    const bf16x8 a =
-                        *reinterpret_cast<const bf16x8 *>(krow + ((c ^ kswz<CH>(kv)) << 4));
+                for (int mt = 0; mt < 2; ++mt)
                     sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        a, qf[ks], ks == 0 ? minit : sacc[mt], 0, 0, 0);
-                }
+                        kf[ks & KLA][mt], qf[ks], ks == 0 ? minit : sacc[mt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            bf16x8 pb[2][2];
+            __builtin_amdgcn_sched_barrier(0);
             float part = expand(sacc[0], pb[0]) + expand(sacc[1], pb[1]);
             // Lazy reference max.  The weights are formed against the current
             // reference; only when this lane's 32 weights of the tile sum to more
@@ -462,41 +505,80 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
                 part = expand(sacc[0], pb[0]) + expand(sacc[1], pb[1]);
             }
             l_run += part;
-            // O^T += V^T P^T: 4 k-steps of 16 keys (mt, p); the 8 transpose reads of
-            // an output d-tile are issued together, ahead of its 4 MFMAs
+    };
+    // O^T += V^T P^T for the tile in `stage`: 4 k-steps of 16 keys (mt, p) per output
+    // d tile; each next d tile's V^T fragments are read under the current one's MFMAs
+    auto pv_tile = [&](int stage, const bf16x8 (&pb)[2][2]) {
+            const char *vb = reinterpret_cast<const char *>(sh.vs[stage]);
+            bf16x8 va[2][4];
+            vfrags_dt(vb, 0, va[0]);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                bf16x8 va[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int mt = kk >> 1, p = kk & 1;
-#pragma unroll
-                    for (int r = 0; r < 2; ++r) {
-                        const int g16 = lane >> 4, s = lane & 15;
-                        const int kv = 32 * mt + 16 * p + 8 * (g16 >> 1) + 4 * r + (s >> 2);
-                        const int d = 32 * dt + 16 * (g16 & 1) + 4 * (s & 3);
-                        const int c = (d >> 3) ^ vswz<CH>(kv);
-                        const char *addr = vb + kv * ROWB + (c << 4) + (d & 7) * 2;
-                        const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                            (NABLA_LDS bf16x4 *)(addr));
-                        va[kk][4 * r + 0] = x[0];
-                        va[kk][4 * r + 1] = x[1];
-                        va[kk][4 * r + 2] = x[2];
-                        va[kk][4 * r + 3] = x[3];
-                    }
-                }
+                if (dt + 1 < DT) vfrags_dt(vb, dt + 1, va[(dt + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], pb[kk >> 1][kk & 1],
-                                                                       oacc[dt], 0, 0, 0);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        va[dt & 1][kk], pb[kk >> 1][kk & 1], oacc[dt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    };
+    bf16x8 pb_prev[2][2];      // packed weights of the previous tile (waves 4-7)
+    bool prev_listed = false;  // waves 4-7: the previous tile's P V is still to do
+    int prev_stage = 0;
+
+    // ---- the walk over union tiles u_0, u_1, ...; u_k lives in LDS stage k % 4.
+    // Step k: start loading u_{k+2} (its stage held u_{k-2}, whose last use, the
+    // delayed P V, was in step k-1), compute, make sure u_{k+1} has landed, barrier.
+    if (U > 0) {
+        issue(sh.ulist[0], 0);
+        land(0);
+        if (U > 1) {
+            issue(sh.ulist[1], 1);
+            land(1);
+        }
+        settle(U > 1);
+    }
+    __syncthreads();
+
+    // block of u_{k+2} and member bits of u_k, read one step ahead
+    int pf_blk = U > 2 ? sh.ulist[2] : -1;
+    int pf_mem = U > 0 ? sh.umem[0] : 0;
+    for (int kk = 0, stage = 0; kk < U; ++kk, stage = (stage + 1) & (kStages - 1)) {
+        const int n2 = __builtin_amdgcn_readfirstlane(pf_blk);  // u_{k+2}
+        const int memk = __builtin_amdgcn_readfirstlane(pf_mem);
+        pf_blk = kk + 3 < U ? sh.ulist[kk + 3] : -1;
+        pf_mem = kk + 1 < U ? sh.umem[kk + 1] : 0;
+        const int stage2 = (stage + 2) & (kStages - 1);
+        if (n2 >= 0) issue(n2, stage2);
+        const bool mine = myblk >= 0 && ((memk >> slot) & 1);
+        // Waves w and w + 4 share a SIMD.  Waves 0-3 do tile k's scores, softmax and
+        // P V in step k; waves 4-7 do tile k-1's P V first and then tile k's scores
+        // and softmax, keeping the packed weights to the next step.  The two waves of
+        // a SIMD are thus half a tile apart: one's softmax (VALU) runs under the
+        // other's MFMAs instead of both waves doing the same phase at once.
+        const bool delayed = w >= 4;
+        if (delayed && prev_listed) pv_tile(prev_stage, pb_prev);
+        if (mine) {
+            bf16x8 pb[2][2];
+            score_softmax(stage, pb);
+            if (delayed) {
+#pragma unroll
+                for (int x = 0; x < 2; ++x)
+#pragma unroll
+                    for (int y = 0; y < 2; ++y) pb_prev[x][y] = pb[x][y];
+            } else {
+                pv_tile(stage, pb);
             }
         }
+        prev_listed = delayed && mine;
+        prev_stage = stage;
         if (n2 >= 0) land(stage2);
         settle(n2 >= 0);
-        __syncthreads();  // u_{k+1} has landed; everyone is done with u_k's stage
-        cur = n1;
-        n1 = n2;
+        __syncthreads();  // u_{k+1} has landed; everyone is done with u_{k-1}'s stage
     }
+    // the last tile's delayed P V (its stage is not reused before the next group)
+    if (prev_listed) pv_tile(prev_stage, pb_prev);
 
     if (myblk >= 0) {
     const float lsum = l_run + __shfl_xor(l_run, 32);
