@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query blocks in the oracle attention sample")
+    ap.add_argument("--sweep", action="store_true",
+                    help="the sparsity sweep on the 720p shape and the long clip, one line per run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -121,24 +123,11 @@ def cpu_baseline(w, q, k, v, sta_np, g_nb, rows, flops_per_pair):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(the path shards by (batch, head) across GPUs; that is not built here)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
-    import torch
-    if args.copy_calibration:
-        copy_calibration(torch)
-        return
-    import block_sparse_attention_fractal_amd as nabla
-    from block_sparse_attention_fractal_amd import synth
-
-    w = synth.WORKLOADS[args.workload]
+def measure(torch, nabla, w, qkv, steps, warmup):
+    """Run the path on workload w for `steps` timed steps; return the measurement dict."""
+    import ctypes
     dev = torch.device("cuda:0")
-    print("[bench] %s" % w.describe(), file=sys.stderr, flush=True)
-    q, k, v = synth.make_qkv(w)
+    q, k, v = qkv
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     gq, gk, gv = (torch.from_numpy(a).to(tdt).to(dev) for a in (q, k, v))
     B, S, H, D, nb = w.B, w.S, w.heads, w.D, w.nb
@@ -152,12 +141,12 @@ def main():
     ws_attn = torch.empty(nabla.nabla_sparse_attn_workspace(B, S, H, w.tiles), dtype=torch.uint8,
                           device=dev)
     L = nabla.lib()
-    import ctypes
     P = lambda t: ctypes.c_void_p(t.data_ptr())
     dt_code = 1 if tdt == torch.bfloat16 else 0
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    sta_p = P(sta) if w.sta is not None else None
 
     def check(rc, what):
         if rc != 0:
@@ -167,12 +156,13 @@ def main():
         """One pass of the path; rec collects (start, end) event pairs per stage."""
         e = [ev() for _ in range(5)] if rec is not None else None
         if e: e[0].record(stream)
-        check(L.nabla_sta_mask(P(sta), *w.tiles, *w.sta, sp), "sta")
+        if w.sta is not None:
+            check(L.nabla_sta_mask(P(sta), *w.tiles, *w.sta, sp), "sta")
         for src, dst in ((gq, qf), (gk, kf), (gv, vf)):
             check(L.nabla_fractal_permute(P(src), P(dst), dt_code, B, w.T, w.H, w.W, H, D, 0, sp),
                   "permute")
         if e: e[1].record(stream)
-        check(L.nabla_block_mask(P(qf), P(kf), dt_code, B, S, H, D, P(sta), w.thr, P(kv_nb),
+        check(L.nabla_block_mask(P(qf), P(kf), dt_code, B, S, H, D, sta_p, w.thr, P(kv_nb),
                                  P(kv_inds), P(ws), ws.numel(), sp), "mask")
         if e: e[2].record(stream)
         check(L.nabla_sparse_attn_fwd(P(qf), P(kf), P(vf), dt_code, B, S, H, D, P(kv_nb),
@@ -185,68 +175,119 @@ def main():
             e[4].record(stream)
             rec.append(e)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     # timed region: exactly `steps` steps; per-stage HIP events are recorded on
     # the launch stream inside the same steps
     rec = []
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step(rec)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
     stage = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in rec])
-    perm_ms = float(np.mean(stage[:, 0] + stage[:, 3]))
-    mask_ms = float(np.mean(stage[:, 1]))
-    attn_ms = float(np.mean(stage[:, 2]))
-
     g_nb = kv_nb.cpu().numpy()
     pairs = int(g_nb.sum())
     flops_per_pair = 4.0 * 64 * 64 * D
-    attn_flops = pairs * flops_per_pair
-    density = pairs / float(B * H * nb * nb)
-    value = attn_flops / (ms_per_step * 1e-3) / 1e12
-    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     esz = 2 if tdt == torch.bfloat16 else 4
+    mask_ms = float(np.mean(stage[:, 1]))
+    attn_ms = float(np.mean(stage[:, 2]))
     mask_bytes = 2.0 * B * S * H * D * esz + 4.0 * B * H * nb + 4.0 * pairs + nb * nb
-    traffic = read_traffic(attn_flops)
+    sta_pairs = int(sta.sum().item()) * B * H if w.sta is not None else 0
+    return {
+        "ms_per_step": wall * 1e3 / steps,
+        "perm_ms": float(np.mean(stage[:, 0] + stage[:, 3])),
+        "mask_ms": mask_ms,
+        "attn_ms": attn_ms,
+        "pairs": pairs,
+        "flops_per_pair": flops_per_pair,
+        "attn_flops": pairs * flops_per_pair,
+        "density": pairs / float(B * H * nb * nb),
+        "sta_density": sta_pairs / float(B * H * nb * nb),
+        "mask_gbs": mask_bytes / (mask_ms * 1e-3) / 1e9,
+        "g_nb": g_nb,
+        "sta_np": None if w.sta is None else sta.cpu().numpy(),
+        "dtype": "bf16" if tdt == torch.bfloat16 else "fp32",
+    }
 
+
+def sweep(torch, nabla, synth, steps, warmup):
+    """The sparsity sweep on the 720p shape and the long clip: one JSON line per run."""
+    cache = {}
+    runs = synth.sweep_workloads() + [synth.WORKLOADS["long"]]
+    for w in runs:
+        key = (w.T, w.H, w.W, w.heads, w.D, w.gen, w.seed, w.sigma_f, w.sigma_n, w.dtype)
+        if key not in cache:
+            cache.clear()
+            print("[bench] generating %s" % w.describe(), file=sys.stderr, flush=True)
+            cache[key] = synth.make_qkv(w)
+        m = measure(torch, nabla, w, cache[key], steps, warmup)
+        line = {"workload": w.describe(), "density": round(m["density"], 5),
+                "sta_density": round(m["sta_density"], 5), "kept_pairs": m["pairs"],
+                "mask_ms": round(m["mask_ms"], 4), "mask_gbs": round(m["mask_gbs"], 1),
+                "attn_ms": round(m["attn_ms"], 4),
+                "attn_tflops": round(m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12, 2),
+                "permute_ms": round(m["perm_ms"], 4), "ms_per_step": round(m["ms_per_step"], 4),
+                "value": round(m["attn_flops"] / (m["ms_per_step"] * 1e-3) / 1e12, 3)}
+        print(json.dumps(line), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the path shards by (batch, head) across GPUs; that is not built here)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+    import block_sparse_attention_fractal_amd as nabla
+    from block_sparse_attention_fractal_amd import synth
+    if args.sweep:
+        sweep(torch, nabla, synth, args.steps, args.warmup)
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    print("[bench] %s" % w.describe(), file=sys.stderr, flush=True)
+    q, k, v = synth.make_qkv(w)
+    m = measure(torch, nabla, w, (q, k, v), args.steps, args.warmup)
+    attn_tflops = m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12
+    traffic = read_traffic(m["attn_flops"])
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": round(m["attn_flops"] / (m["ms_per_step"] * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(m["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if tdt == torch.bfloat16 else "fp32",
+        "dtype": m["dtype"],
         "data": "synthetic (seeded smooth spatio-temporal field + noise, video-shaped)",
-        "config": {"workload": w.describe(), "B": B, "heads": H, "head_dim": D,
-                   "T": w.T, "H": w.H, "W": w.W, "seq_len": S, "blocks": nb, "thr": w.thr,
-                   "sta_window": list(w.sta) if w.sta else None, "kept_pairs": pairs,
-                   "density": round(density, 5)},
-        "mask_ms": round(mask_ms, 4),
-        "attn_ms": round(attn_ms, 4),
-        "permute_ms": round(perm_ms, 4),
+        "config": {"workload": w.describe(), "B": w.B, "heads": w.heads, "head_dim": w.D,
+                   "T": w.T, "H": w.H, "W": w.W, "seq_len": w.S, "blocks": w.nb, "thr": w.thr,
+                   "sta_window": list(w.sta) if w.sta else None, "kept_pairs": m["pairs"],
+                   "density": round(m["density"], 5)},
+        "mask_ms": round(m["mask_ms"], 4),
+        "attn_ms": round(m["attn_ms"], 4),
+        "permute_ms": round(m["perm_ms"], 4),
         "attn_tflops": round(attn_tflops, 2),
-        "mask_gbs": round(mask_bytes / (mask_ms * 1e-3) / 1e9, 1),
+        "mask_gbs": round(m["mask_gbs"], 1),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "sparse_attn_kernel<128, bf16>",
-                     "per_launch": {"flops": attn_flops, "kept_pairs": pairs}},
+                     "per_launch": {"flops": m["attn_flops"], "kept_pairs": m["pairs"]}},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v,
-                                           None if w.sta is None else
-                                           sta.cpu().numpy(), g_nb, args.cpu_rows,
-                                           flops_per_pair)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, m["sta_np"], m["g_nb"], args.cpu_rows,
+                                           m["flops_per_pair"])
     print(json.dumps(out), flush=True)
 
 
