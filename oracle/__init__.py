@@ -11,6 +11,10 @@ NablaAttentionImpl.forward source; the NablaAttentionMetadata fields) and the
 "NABLA: Neighborhood Adaptive Block-Level Attention" summary page (Technical
 Summary, Methodology).
 
+The training pass (attention_lse, attention_dq, attention_bwd) is the gradient of
+that dense masked attention; it is pinned against torch's fp64 autograd and closed
+forms.
+
 Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
 against closed forms, brute force, invariants or library routines
 (nothing here is "parity unpinned").
@@ -58,6 +62,12 @@ def _load():
     lib.orc_block_mask.restype = i32
     lib.orc_attention.argtypes = [P, P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
     lib.orc_attention.restype = i32
+    lib.orc_attention_lse.argtypes = [P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
+    lib.orc_attention_lse.restype = i32
+    lib.orc_attention_dq.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
+    lib.orc_attention_dq.restype = i32
+    lib.orc_attention_bwd.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64, P, P, P, P]
+    lib.orc_attention_bwd.restype = i32
     _lib = lib
     return lib
 
@@ -223,6 +233,63 @@ def attention(q, k, v, kv_nb, kv_inds, row_ids=None, scale=0.0):
     if rc != 0:
         raise ValueError("oracle attention: bad argument")
     return row_ids, o
+
+
+# ---------------------------------------------------------------- O11 training pass
+def _lists(kv_nb, kv_inds):
+    return (np.ascontiguousarray(kv_nb, dtype=np.int32),
+            np.ascontiguousarray(kv_inds, dtype=np.int32))
+
+
+def _rows(row_ids, B, heads, nb):
+    if row_ids is None:
+        row_ids = np.arange(B * heads * nb, dtype=np.int64)
+    return np.ascontiguousarray(row_ids, dtype=np.int64)
+
+
+def attention_lse(q, k, kv_nb, kv_inds, row_ids=None, scale=0.0):
+    """Natural-log log-sum-exp of the scaled allowed scores of every row of the listed
+    q-blocks.  Returns (row_ids, lse [len(row_ids), 64] fp64)."""
+    q, k = _f32(q), _f32(k)
+    B, S, heads, D = q.shape
+    row_ids = _rows(row_ids, B, heads, S // BLOCK)
+    kv_nb, kv_inds = _lists(kv_nb, kv_inds)
+    lse = np.zeros((row_ids.size, BLOCK), np.float64)
+    rc = _load().orc_attention_lse(_ptr(q), _ptr(k), B, S, heads, D, _ptr(kv_nb), _ptr(kv_inds),
+                                   float(scale), _ptr(row_ids), row_ids.size, _ptr(lse))
+    if rc != 0:
+        raise ValueError("oracle attention_lse: bad argument")
+    return row_ids, lse
+
+
+def attention_dq(q, k, v, dout, kv_nb, kv_inds, row_ids=None, scale=0.0):
+    """dq of every row of the listed q-blocks.  Returns (row_ids, dq [n, 64, D] fp64)."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, S, heads, D = q.shape
+    row_ids = _rows(row_ids, B, heads, S // BLOCK)
+    kv_nb, kv_inds = _lists(kv_nb, kv_inds)
+    dq = np.zeros((row_ids.size, BLOCK, D), np.float64)
+    rc = _load().orc_attention_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, S, heads, D,
+                                  _ptr(kv_nb), _ptr(kv_inds), float(scale), _ptr(row_ids),
+                                  row_ids.size, _ptr(dq))
+    if rc != 0:
+        raise ValueError("oracle attention_dq: bad argument")
+    return row_ids, dq
+
+
+def attention_bwd(q, k, v, dout, kv_nb, kv_inds, scale=0.0):
+    """The full training pass: dict(lse [B,heads,S], dq, dk, dv [B,S,heads,D]), fp64."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, S, heads, D = q.shape
+    kv_nb, kv_inds = _lists(kv_nb, kv_inds)
+    lse = np.zeros((B, heads, S), np.float64)
+    dq, dk, dv = (np.zeros((B, S, heads, D), np.float64) for _ in range(3))
+    rc = _load().orc_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, S, heads, D,
+                                   _ptr(kv_nb), _ptr(kv_inds), float(scale), _ptr(lse), _ptr(dq),
+                                   _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle attention_bwd: bad argument")
+    return {"lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
 def rows_to_tokens(o_rows, row_ids, B, S, heads, D):

@@ -29,6 +29,8 @@
  *   - the last block in sorted order (the row's arg-max) is always kept.
  *   - attention: fp64 dense softmax over every key, with disallowed 64x64
  *              blocks at -inf; scale 1/sqrt(D).
+ *   - training pass: lse (natural log) and the gradients dq, dk, dv of that
+ *              dense masked softmax attention, fp64.
  */
 #include <math.h>
 #include <stdint.h>
@@ -390,5 +392,225 @@ int orc_attention(const float *q, const float *k, const float *v, int B, int S, 
         free(z);
         free(allowed);
     }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------- */
+/* O11 attention statistics and gradients (the training pass)                 */
+/* ------------------------------------------------------------------------- */
+/*
+ * The pages train with the same block-sparse attention ([NABLA] Results: the
+ * training speed-up; [nabla] forward runs flex attention, whose backward is the
+ * gradient of that dense masked softmax).  Per (b, h) and query row r, with A_r
+ * the tokens of the blocks listed for r's block:
+ *   z_rc  = scale * q_r . k_c            (c in A_r)
+ *   lse_r = log sum_{c in A_r} exp(z_rc)            (natural log)
+ *   P_rc  = exp(z_rc - lse_r),  o_r = sum_c P_rc v_c
+ * and, for a given output gradient dO,
+ *   dP_rc = dO_r . v_c,   Delta_r = sum_c P_rc dP_rc,   dZ_rc = P_rc (dP_rc - Delta_r)
+ *   dq_r  = scale sum_c dZ_rc k_c
+ *   dk_c  = scale sum_r dZ_rc q_r,   dv_c = sum_r P_rc dO_r   (r over rows with c in A_r).
+ * fp64 throughout.  A row with no allowed key has lse = -inf and zero gradients.
+ */
+
+/* allowed[i * nb + j] = 1 iff block j is listed for query block i of slice (b, h) */
+static int orc_slice_allowed(const int32_t *kv_nb, const int32_t *kv_inds, int64_t slice, int nb,
+                             uint8_t *allowed) {
+    memset(allowed, 0, (size_t)nb * nb);
+    for (int i = 0; i < nb; ++i) {
+        int64_t row = slice * nb + i;
+        int n = kv_nb[row];
+        if (n < 0 || n > nb) return -1;
+        for (int t = 0; t < n; ++t) {
+            int j = kv_inds[row * nb + t];
+            if (j < 0 || j >= nb) return -1;
+            allowed[(size_t)i * nb + j] = 1;
+        }
+    }
+    return 0;
+}
+
+/* Row pass for query row r (token index within the sequence) of slice (b, h):
+ * lse_r, Delta_r and (if dq_row) dq_r.  allowed_row = the row of `allowed` for
+ * r's block; z is scratch of S doubles.  dout may be NULL (lse only). */
+static void orc_row_pass(const float *q, const float *k, const float *v, const float *dout,
+                         int64_t b, int h, int S, int heads, int D, const uint8_t *allowed_row,
+                         double scale, int64_t r, double *z, double *lse, double *delta,
+                         double *dq_row) {
+    const int64_t tq = b * S + r;
+    const float *qr = q + (tq * heads + h) * D;
+    double zmax = -INFINITY;
+    for (int64_t c = 0; c < S; ++c) {
+        if (!allowed_row[c / ORC_BLK]) { z[c] = -INFINITY; continue; }
+        const float *kc = k + ((b * S + c) * heads + h) * D;
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) acc += (double)qr[d] * (double)kc[d];
+        z[c] = scale * acc;
+        if (z[c] > zmax) zmax = z[c];
+    }
+    if (dq_row) for (int d = 0; d < D; ++d) dq_row[d] = 0.0;
+    if (zmax == -INFINITY) {
+        *lse = -INFINITY;
+        if (delta) *delta = 0.0;
+        return;
+    }
+    double sum = 0.0;
+    for (int64_t c = 0; c < S; ++c)
+        if (z[c] != -INFINITY) sum += exp(z[c] - zmax);
+    const double l = zmax + log(sum);
+    *lse = l;
+    if (!dout) return;
+    const float *dor = dout + (tq * heads + h) * D;
+    /* Delta_r = sum_c P_rc dP_rc; then dq_r = scale sum_c P_rc (dP_rc - Delta_r) k_c */
+    double dl = 0.0;
+    for (int64_t c = 0; c < S; ++c) {
+        if (z[c] == -INFINITY) continue;
+        const float *vc = v + ((b * S + c) * heads + h) * D;
+        double dp = 0.0;
+        for (int d = 0; d < D; ++d) dp += (double)dor[d] * (double)vc[d];
+        dl += exp(z[c] - l) * dp;
+    }
+    *delta = dl;
+    if (!dq_row) return;
+    for (int64_t c = 0; c < S; ++c) {
+        if (z[c] == -INFINITY) continue;
+        const float *vc = v + ((b * S + c) * heads + h) * D;
+        const float *kc = k + ((b * S + c) * heads + h) * D;
+        double dp = 0.0;
+        for (int d = 0; d < D; ++d) dp += (double)dor[d] * (double)vc[d];
+        const double dz = exp(z[c] - l) * (dp - dl);
+        for (int d = 0; d < D; ++d) dq_row[d] += scale * dz * (double)kc[d];
+    }
+}
+
+/* lse of the 64 rows of each listed query block id = (b*heads + h)*nb + i: lse[rr*64 + r]. */
+int orc_attention_lse(const float *q, const float *k, int B, int S, int heads, int D,
+                      const int32_t *kv_nb, const int32_t *kv_inds, double scale,
+                      const int64_t *row_ids, int64_t nrows, double *lse) {
+    if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
+    const int nb = S / ORC_BLK;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t rr = 0; rr < nrows; ++rr) {
+        const int64_t id = row_ids[rr];
+        if (id < 0 || id >= (int64_t)B * heads * nb) { bad = 1; continue; }
+        const int64_t b = id / ((int64_t)heads * nb);
+        const int h = (int)((id / nb) % heads);
+        const int i = (int)(id % nb);
+        uint8_t *allowed = (uint8_t *)calloc((size_t)nb, 1);
+        double *z = (double *)malloc(sizeof(double) * (size_t)S);
+        const int n = kv_nb[id];
+        int ok = n >= 0 && n <= nb;
+        for (int t = 0; ok && t < n; ++t) {
+            const int j = kv_inds[id * nb + t];
+            if (j < 0 || j >= nb) ok = 0; else allowed[j] = 1;
+        }
+        if (!ok) bad = 1;
+        else
+            for (int r = 0; r < ORC_BLK; ++r)
+                orc_row_pass(q, k, NULL, NULL, b, h, S, heads, D, allowed, scale,
+                             (int64_t)i * ORC_BLK + r, z, &lse[rr * ORC_BLK + r], NULL, NULL);
+        free(z);
+        free(allowed);
+    }
+    return bad ? -1 : 0;
+}
+
+/* dq of the 64 rows of each listed query block id: dq[(rr*64 + r)*D + d]. */
+int orc_attention_dq(const float *q, const float *k, const float *v, const float *dout, int B,
+                     int S, int heads, int D, const int32_t *kv_nb, const int32_t *kv_inds,
+                     double scale, const int64_t *row_ids, int64_t nrows, double *dq) {
+    if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
+    const int nb = S / ORC_BLK;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t rr = 0; rr < nrows; ++rr) {
+        const int64_t id = row_ids[rr];
+        if (id < 0 || id >= (int64_t)B * heads * nb) { bad = 1; continue; }
+        const int64_t b = id / ((int64_t)heads * nb);
+        const int h = (int)((id / nb) % heads);
+        const int i = (int)(id % nb);
+        uint8_t *allowed = (uint8_t *)calloc((size_t)nb, 1);
+        double *z = (double *)malloc(sizeof(double) * (size_t)S);
+        const int n = kv_nb[id];
+        int ok = n >= 0 && n <= nb;
+        for (int t = 0; ok && t < n; ++t) {
+            const int j = kv_inds[id * nb + t];
+            if (j < 0 || j >= nb) ok = 0; else allowed[j] = 1;
+        }
+        if (!ok) bad = 1;
+        else
+            for (int r = 0; r < ORC_BLK; ++r) {
+                double l, dl;
+                orc_row_pass(q, k, v, dout, b, h, S, heads, D, allowed, scale,
+                             (int64_t)i * ORC_BLK + r, z, &l, &dl, &dq[(rr * ORC_BLK + r) * D]);
+            }
+        free(z);
+        free(allowed);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Full training pass over every (b, h) slice: lse [B,heads,S]; dq, dk, dv [B,S,heads,D].
+ * Row quantities first (parallel over rows), then dk and dv per key (parallel over keys):
+ * key c of block j gathers from every row whose block lists j. */
+int orc_attention_bwd(const float *q, const float *k, const float *v, const float *dout, int B,
+                      int S, int heads, int D, const int32_t *kv_nb, const int32_t *kv_inds,
+                      double scale, double *lse, double *dq, double *dk, double *dv) {
+    if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
+    const int nb = S / ORC_BLK;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    uint8_t *allowed = (uint8_t *)malloc((size_t)nb * nb);
+    double *delta = (double *)malloc(sizeof(double) * (size_t)S);
+    if (!allowed || !delta) { free(allowed); free(delta); return -1; }
+    int bad = 0;
+    for (int64_t b = 0; b < B && !bad; ++b)
+        for (int h = 0; h < heads && !bad; ++h) {
+            const int64_t slice = b * heads + h;
+            if (orc_slice_allowed(kv_nb, kv_inds, slice, nb, allowed) != 0) { bad = 1; break; }
+            double *lse_s = lse + slice * S;
+#pragma omp parallel
+            {
+                double *z = (double *)malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 16)
+                for (int64_t r = 0; r < S; ++r)
+                    orc_row_pass(q, k, v, dout, b, h, S, heads, D,
+                                 allowed + (size_t)(r / ORC_BLK) * nb, scale, r, z, &lse_s[r],
+                                 &delta[r], dq + ((b * S + r) * heads + h) * D);
+                free(z);
+            }
+#pragma omp parallel for schedule(dynamic, 16)
+            for (int64_t c = 0; c < S; ++c) {
+                const int j = (int)(c / ORC_BLK);
+                const float *kc = k + ((b * S + c) * heads + h) * D;
+                const float *vc = v + ((b * S + c) * heads + h) * D;
+                double *dkc = dk + ((b * S + c) * heads + h) * D;
+                double *dvc = dv + ((b * S + c) * heads + h) * D;
+                for (int d = 0; d < D; ++d) { dkc[d] = 0.0; dvc[d] = 0.0; }
+                for (int i = 0; i < nb; ++i) {
+                    if (!allowed[(size_t)i * nb + j]) continue;
+                    for (int rb = 0; rb < ORC_BLK; ++rb) {
+                        const int64_t r = (int64_t)i * ORC_BLK + rb;
+                        const float *qr = q + ((b * S + r) * heads + h) * D;
+                        const float *dor = dout + ((b * S + r) * heads + h) * D;
+                        double zz = 0.0, dp = 0.0;
+                        for (int d = 0; d < D; ++d) {
+                            zz += (double)qr[d] * (double)kc[d];
+                            dp += (double)dor[d] * (double)vc[d];
+                        }
+                        const double p = exp(scale * zz - lse_s[r]);
+                        const double dz = p * (dp - delta[r]);
+                        for (int d = 0; d < D; ++d) {
+                            dvc[d] += p * (double)dor[d];
+                            dkc[d] += scale * dz * (double)qr[d];
+                        }
+                    }
+                }
+            }
+        }
+    free(allowed);
+    free(delta);
     return bad ? -1 : 0;
 }

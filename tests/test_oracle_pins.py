@@ -394,3 +394,104 @@ def test_attention_special_cases(orc):
     # Q = 0 and one kept block -> mean of that block's V
     _, o0 = orc.attention(np.zeros_like(q), k, v, kv_nb, kv_inds)
     assert np.allclose(o0[1], v[0, 128:192, 0].astype(np.float64).mean(0)[None, :], atol=1e-14)
+
+
+# ------------------------------------------------------------------ O11 training pass
+def _random_lists(rng, B, h, nb, empty_row=None):
+    """Random non-empty lists (random subsets, stored in random order), one empty row if asked."""
+    kv_nb = np.zeros((B, h, nb), np.int32)
+    kv_inds = np.zeros((B, h, nb, nb), np.int32)
+    for b in range(B):
+        for hh in range(h):
+            for i in range(nb):
+                n = int(rng.integers(1, nb + 1))
+                if empty_row is not None and (b, hh, i) == empty_row:
+                    n = 0
+                perm = rng.permutation(nb).astype(np.int32)
+                kv_nb[b, hh, i] = n
+                kv_inds[b, hh, i] = perm  # the first n are the list, in random order
+    return kv_nb, kv_inds
+
+
+def _autograd_reference(q, k, v, dout, kv_nb, kv_inds, scale):
+    """torch fp64 autograd of the dense masked softmax attention (rows with no allowed key
+    give O = 0): lse, dq, dk, dv in [B,S,h,D] / [B,h,S] layouts."""
+    torch = pytest.importorskip("torch")
+    B, S, h, D = q.shape
+    nb = S // 64
+    allowed = np.zeros((B, h, nb, nb), bool)
+    for b in range(B):
+        for hh in range(h):
+            for i in range(nb):
+                allowed[b, hh, i, kv_inds[b, hh, i, :kv_nb[b, hh, i]]] = True
+    tok = torch.from_numpy(np.kron(allowed, np.ones((64, 64), bool)))  # [B,h,S,S]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3))).double().requires_grad_()
+    Q, K, V = t(q), t(k), t(v)
+    dO = torch.from_numpy(np.ascontiguousarray(dout.transpose(0, 2, 1, 3))).double()
+    z = scale * (Q @ K.transpose(-1, -2))
+    z = z.masked_fill(~tok, float("-inf"))
+    nonempty = tok.any(-1, keepdim=True)
+    lse = torch.logsumexp(z, dim=-1)
+    p = torch.where(nonempty, torch.softmax(torch.where(nonempty, z, torch.zeros_like(z)).masked_fill(~tok, float("-inf")), dim=-1), torch.zeros_like(z))
+    o = p @ V
+    (o * dO).sum().backward()
+    back = lambda x: x.detach().numpy().transpose(0, 2, 1, 3)
+    return lse.detach().numpy(), back(Q.grad), back(K.grad), back(V.grad)
+
+
+def test_training_pass_matches_torch_autograd(orc):
+    """lse, dq, dk, dv against torch's fp64 autograd of the dense masked attention, on random
+    block lists (one row with an empty list)."""
+    rng = np.random.default_rng(21)
+    B, S, h, D = 1, 256, 2, 16
+    q, k, v, dout = (rng.standard_normal((B, S, h, D)).astype(np.float32) for _ in range(4))
+    kv_nb, kv_inds = _random_lists(rng, B, h, S // 64, empty_row=(0, 1, 2))
+    scale = 0.3
+    got = orc.attention_bwd(q, k, v, dout, kv_nb, kv_inds, scale=scale)
+    lse, dq, dk, dv = _autograd_reference(q, k, v, dout, kv_nb, kv_inds, scale)
+    fin = np.isfinite(lse)
+    assert np.array_equal(fin, np.isfinite(got["lse"])) and (~fin).sum() == 64
+    assert np.max(np.abs(got["lse"][fin] - lse[fin])) < 1e-12
+    for name, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert np.max(np.abs(got[name] - ref)) < 1e-11, name
+    # the empty row has zero dq
+    assert np.all(got["dq"][0, 128:192, 1] == 0.0)
+
+
+def test_training_pass_closed_forms(orc):
+    """Per (b, h): sum over keys of dv = sum of dO over the rows that attend somewhere (each
+    row's weights sum to 1); sum over keys of dk = 0 (each row's dZ sums to 0); V constant ->
+    dq = dk = 0; Q = 0 -> lse = log(64 * kv_nb)."""
+    rng = np.random.default_rng(22)
+    B, S, h, D = 2, 320, 2, 32
+    nb = S // 64
+    q, k, v, dout = (rng.standard_normal((B, S, h, D)).astype(np.float32) for _ in range(4))
+    kv_nb, kv_inds = _random_lists(rng, B, h, nb, empty_row=(1, 0, 4))
+    r = orc.attention_bwd(q, k, v, dout, kv_nb, kv_inds)
+    live = np.repeat(kv_nb > 0, 64, axis=-1).transpose(0, 2, 1)  # [B,S,h]
+    want_dv = (dout.astype(np.float64) * live[..., None]).sum(1)  # [B,h,D]
+    assert np.max(np.abs(r["dv"].sum(1) - want_dv)) < 1e-10
+    assert np.max(np.abs(r["dk"].sum(1))) < 1e-10
+    rc = orc.attention_bwd(q, k, np.full_like(v, -1.25), dout, kv_nb, kv_inds)
+    assert np.max(np.abs(rc["dq"])) < 1e-12 and np.max(np.abs(rc["dk"])) < 1e-12
+    _, lse0 = orc.attention_lse(np.zeros_like(q), k, kv_nb, kv_inds)
+    with np.errstate(divide="ignore"):
+        want = np.log(64.0 * kv_nb.reshape(-1).astype(np.float64))  # -inf for the empty row
+    assert np.allclose(lse0, np.repeat(want[:, None], 64, axis=1), rtol=0, atol=1e-13)
+
+
+def test_training_pass_sampled_functions_agree(orc):
+    """attention_lse and attention_dq on sampled q-blocks equal the full pass at those rows."""
+    rng = np.random.default_rng(23)
+    B, S, h, D = 1, 384, 2, 16
+    nb = S // 64
+    q, k, v, dout = (rng.standard_normal((B, S, h, D)).astype(np.float32) for _ in range(4))
+    kv_nb, kv_inds = _random_lists(rng, B, h, nb)
+    full = orc.attention_bwd(q, k, v, dout, kv_nb, kv_inds)
+    ids = np.array([0, 5, 7, 11], np.int64)
+    _, lse = orc.attention_lse(q, k, kv_nb, kv_inds, row_ids=ids)
+    _, dq = orc.attention_dq(q, k, v, dout, kv_nb, kv_inds, row_ids=ids)
+    for n, rid in enumerate(ids):
+        hh, i = divmod(int(rid), nb)
+        assert np.array_equal(lse[n], full["lse"][0, hh, 64 * i:64 * (i + 1)])
+        assert np.array_equal(dq[n], full["dq"][0, 64 * i:64 * (i + 1), hh])
