@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["nabla_fractal_permute", "nabla_sta_mask", "nabla_block_mask",
            "nabla_block_mask_workspace", "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace",
-           "NablaError", "lib",
+           "nabla_sparse_attn_bwd", "nabla_sparse_attn_bwd_workspace", "NablaError", "lib",
            "LIB_PATH", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnabla.so")
@@ -63,6 +63,13 @@ def lib():
     L.nabla_sparse_attn_workspace.restype = Z
     L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P, Z, P]
     L.nabla_sparse_attn_fwd.restype = I
+    L.nabla_sparse_attn_fwd_lse.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P, P, Z,
+                                            P]
+    L.nabla_sparse_attn_fwd_lse.restype = I
+    L.nabla_sparse_attn_bwd_workspace.argtypes = [I, I, I]
+    L.nabla_sparse_attn_bwd_workspace.restype = Z
+    L.nabla_sparse_attn_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, F, P, P, P, P, Z, P]
+    L.nabla_sparse_attn_bwd.restype = I
     _lib = L
     return L
 
@@ -167,12 +174,14 @@ def nabla_sparse_attn_workspace(B, S, heads, tiles=None):
 
 
 def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, tiles=None,
-                          workspace=None, out=None):
+                          workspace=None, out=None, lse=None):
     """Block-sparse attention over the listed 64 x 64 blocks: o [B, S, heads, D] (q's dtype).
 
     tiles: the (Tt, Ht, Wt) tile grid of the blocks (lets neighbouring query
     blocks share K/V tiles on chip); None if unknown.  workspace: a uint8 GPU
     tensor of at least nabla_sparse_attn_workspace() bytes (allocated if None).
+    lse: None, or a float32 GPU tensor [B, heads, S] that receives each row's
+    log-sum-exp (natural log), as the backward needs it.
     """
     if causal:
         raise ValueError("NABLA attention does not support causal masking")
@@ -193,9 +202,59 @@ def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, til
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     else:
         _dev(workspace, "workspace")
-    _check(lib().nabla_sparse_attn_fwd(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads, D,
-                                       _p(kv_nb), _p(kv_inds),
-                                       0.0 if scale is None else float(scale), Tt, Ht, Wt,
-                                       _p(o), _p(workspace), workspace.numel(), _stream(q)),
+    if lse is not None:
+        _dev(lse, "lse")
+        if lse.dtype != torch.float32 or lse.numel() != B * heads * S:
+            raise ValueError("lse must be float32 with B * heads * S elements")
+    _check(lib().nabla_sparse_attn_fwd_lse(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads, D,
+                                           _p(kv_nb), _p(kv_inds),
+                                           0.0 if scale is None else float(scale), Tt, Ht, Wt,
+                                           _p(o), None if lse is None else _p(lse),
+                                           _p(workspace), workspace.numel(), _stream(q)),
            "nabla_sparse_attn_fwd")
     return o
+
+
+def nabla_sparse_attn_bwd_workspace(B, S, heads):
+    """Bytes of workspace nabla_sparse_attn_bwd needs (0 if the sizes are invalid)."""
+    return lib().nabla_sparse_attn_bwd_workspace(B, S, heads)
+
+
+def nabla_sparse_attn_bwd(q, k, v, o, dout, lse, kv_nb, kv_inds, scale=None, workspace=None,
+                          dq=None, dk=None, dv=None):
+    """Gradients (dq, dk, dv) of the block-sparse attention for output gradient dout.
+
+    q, k, v, o, dout: bf16 [B, S, heads, D] GPU tensors (o and lse from
+    nabla_sparse_attn_fwd(..., lse=...) on the same inputs, lists and scale).
+    Returns three new tensors (or the given dq, dk, dv).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse),
+                    ("kv_nb", kv_nb), ("kv_inds", kv_inds)):
+        _dev(t, name)
+    if not (q.shape == k.shape == v.shape == o.shape == dout.shape):
+        raise ValueError("q, k, v, o, dout must have one shape")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise ValueError("q, k, v, o, dout must have one dtype")
+    if kv_nb.dtype != torch.int32 or kv_inds.dtype != torch.int32:
+        raise TypeError("kv_nb and kv_inds must be int32")
+    B, S, heads, D = q.shape
+    nb = S // BLOCK
+    if kv_nb.numel() != B * heads * nb or kv_inds.numel() != B * heads * nb * nb:
+        raise ValueError("kv lists do not match q's shape")
+    if lse.dtype != torch.float32 or lse.numel() != B * heads * S:
+        raise ValueError("lse must be float32 with B * heads * S elements")
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        outs.append(torch.empty_like(q) if t is None else _dev(t, name))
+    if workspace is None:
+        need = lib().nabla_sparse_attn_bwd_workspace(B, S, heads)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _dev(workspace, "workspace")
+    _check(lib().nabla_sparse_attn_bwd(_p(q), _p(k), _p(v), _p(o), _p(dout), _p(lse),
+                                       _dtype_code(q), B, S, heads, D, _p(kv_nb), _p(kv_inds),
+                                       0.0 if scale is None else float(scale), _p(outs[0]),
+                                       _p(outs[1]), _p(outs[2]), _p(workspace),
+                                       workspace.numel(), _stream(q)),
+           "nabla_sparse_attn_bwd")
+    return tuple(outs)

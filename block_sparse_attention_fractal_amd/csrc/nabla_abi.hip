@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
 constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
@@ -114,6 +114,15 @@ nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
                                    const int32_t *kv_nb, const int32_t *kv_inds, float scale,
                                    int Tt, int Ht, int Wt, void *o, void *ws, size_t ws_bytes,
                                    void *stream) {
+    return nabla_sparse_attn_fwd_lse(q, k, v, dtype, B, S, heads, head_dim, kv_nb, kv_inds,
+                                     scale, Tt, Ht, Wt, o, nullptr, ws, ws_bytes, stream);
+}
+
+nabla_status nabla_sparse_attn_fwd_lse(const void *q, const void *k, const void *v,
+                                       nabla_dtype dtype, int B, int S, int heads, int head_dim,
+                                       const int32_t *kv_nb, const int32_t *kv_inds, float scale,
+                                       int Tt, int Ht, int Wt, void *o, float *lse, void *ws,
+                                       size_t ws_bytes, void *stream) {
     if (!q || !k || !v || !kv_nb || !kv_inds || !o || !dtype_ok(dtype))
         return NABLA_ERR_INVALID_ARG;
     if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
@@ -126,7 +135,33 @@ nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
     if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
     return from_hip(nabla::launch_sparse_attn(q, k, v, dtype == NABLA_BF16, B, S, heads,
                                               head_dim, Tt, Ht, Wt, kv_nb, kv_inds, scale, o,
-                                              ws, as_stream(stream)));
+                                              lse, ws, as_stream(stream)));
+}
+
+size_t nabla_sparse_attn_bwd_workspace(int B, int S, int heads) {
+    if (!sizes_ok(B, S, heads, 1) || S % kBlock || S / kBlock > kMaxBlocks) return 0;
+    return nabla::sparse_attn_bwd_workspace_bytes(B, S, heads);
+}
+
+nabla_status nabla_sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                                   const void *dout, const float *lse, nabla_dtype dtype, int B,
+                                   int S, int heads, int head_dim, const int32_t *kv_nb,
+                                   const int32_t *kv_inds, float scale, void *dq, void *dk,
+                                   void *dv, void *ws, size_t ws_bytes, void *stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !kv_nb || !kv_inds || !dq || !dk || !dv ||
+        !dtype_ok(dtype))
+        return NABLA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
+    if (scale != scale) return NABLA_ERR_INVALID_ARG;
+    if (dtype != NABLA_BF16) return NABLA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
+    if (S / kBlock > kMaxBlocks) return NABLA_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < nabla::sparse_attn_bwd_workspace_bytes(B, S, heads))
+        return NABLA_ERR_WORKSPACE;
+    if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
+    return from_hip(nabla::launch_sparse_attn_bwd(q, k, v, o, dout, lse, B, S, heads, head_dim,
+                                                  kv_nb, kv_inds, scale, dq, dk, dv, ws,
+                                                  as_stream(stream)));
 }
 
 }  // extern "C"

@@ -24,9 +24,19 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
 // Tt, Ht, Wt: tile grid of the query blocks (Tt*Ht*Wt == S/64), or all 0 if unknown.
 // ws: sparse_attn_workspace_bytes() bytes (schedule: counter, group costs, order).
 size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt);
+// lse: [B*heads][S] fp32 natural-log log-sum-exp of each row's scaled scores, or null.
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
                               int B, int S, int heads, int D, int Tt, int Ht, int Wt,
                               const int32_t *kv_nb, const int32_t *kv_inds, float scale, void *o,
-                              void *ws, hipStream_t stream);
+                              float *lse, void *ws, hipStream_t stream);
+
+// Backward (bf16 tensors): dq, dk, dv from q, k, v, o, dO, lse and the kv lists.
+// ws: sparse_attn_bwd_workspace_bytes() bytes (row deltas, transposed lists).
+size_t sparse_attn_bwd_workspace_bytes(int B, int S, int heads);
+hipError_t launch_sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                                  const void *dout, const float *lse, int B, int S, int heads,
+                                  int D, const int32_t *kv_nb, const int32_t *kv_inds,
+                                  float scale, void *dq, void *dk, void *dv, void *ws,
+                                  hipStream_t stream);
 
 }  // namespace nabla

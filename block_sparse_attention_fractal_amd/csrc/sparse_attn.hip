@@ -43,13 +43,11 @@
 //     only raised when a tile exceeds it by more than 16 (and on the row's
 //     first tile), so the O rescale is rare.  The row sum is a bf16 dot
 //     product of the packed weights with ones (the same weights P V uses).
-#include "nabla_device.h"
+#include "attn_tile.h"
 #include "nabla_launch.h"
 
 namespace nabla {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-#define NABLA_LDS __attribute__((address_space(3)))
 
 #ifndef NABLA_ATTN_GROUP
 #define NABLA_ATTN_GROUP 4
@@ -61,25 +59,8 @@ constexpr int kMaxWords = 4096 / 64;  // bitmap words for up to 4096 blocks per 
 static_assert(kGroup == 2 || kGroup == 4, "group of 2 or 4 query blocks");
 static_assert(kAttnWaves == 8 || kGroup != 4, "the delayed half of the waves is waves 4-7");
 
-// Key row (within a 32-row score tile) fed to MFMA row m: bit layout
-// m = a(2) hh(1) b(2)  ->  key = (a>>1)<<4 | hh<<3 | (a&1)<<2 | b.
-__device__ __forceinline__ int sigma32(int m) {
-    const int a = m >> 3, hh = (m >> 2) & 1, b = m & 3;
-    return ((a >> 1) << 4) | (hh << 3) | ((a & 1) << 2) | b;
-}
 
-__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
 
-__device__ __forceinline__ f32x16 splat16(float x) {
-    f32x16 r;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) r[j] = x;
-    return r;
-}
 
 __device__ __forceinline__ float max16(const f32x16 &s) {
     float x = fmaxf(s[0], s[1]);
@@ -107,40 +88,6 @@ __device__ __forceinline__ float expand(const f32x16 &s, bf16x8 (&pb)[2]) {
     return part[0] + part[1];
 }
 
-// 16-byte chunk swizzles (CH chunks per row) of the K and V tiles in LDS.
-template <int CH>
-__device__ __forceinline__ int kswz(int kv) { return kv & (CH - 1); }
-template <int CH>
-__device__ __forceinline__ int vswz(int kv) { return (kv & 3) * (CH / 4); }
-
-// Byte offset of a __shared__ object in LDS.
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-    return (uint32_t)(uintptr_t)((const NABLA_LDS char *)p);
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l's chunk lands at
-// m0 + 16 l (m0 wave-uniform).  Issued from inline asm so that the compiler does not
-// treat every later LDS read as depending on it; completion is awaited explicitly
-// with vm_wait before the barrier that hands the tile to the other waves.  Nothing
-// else in the kernel uses m0.
-__device__ __forceinline__ void lds_direct16(const void *g, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(g), "s"(m0)
-                 : "memory");
-}
-// The same with a wave-uniform base address (SGPR pair) and a 32-bit per-lane byte
-// offset: no per-lane 64-bit address arithmetic.
-__device__ __forceinline__ void lds_direct16_sv(const void *base, uint32_t off, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(off), "s"(base), "s"(m0)
-                 : "memory");
-}
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
 
 constexpr int kStages = 4;  // LDS ring: tiles k-1 (delayed P V), k, k+1, k+2 (landing)
 
@@ -170,8 +117,6 @@ __device__ __forceinline__ int group_member(int gi, int s, int Tt, int Ht, int W
     return i < nb ? i : -1;
 }
 
-__device__ __forceinline__ int clamp_count(int n, int nb) { return n < 0 ? 0 : (n > nb ? nb : n); }
-__device__ __forceinline__ int clamp_block(int j, int nb) { return j < 0 ? 0 : (j >= nb ? nb - 1 : j); }
 
 // ---- schedule.  The cost of a group is the number of tiles in the union of its
 // members' lists (the iterations of its walk).  Persistent workgroups take the next
@@ -261,7 +206,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     Tin *__restrict__ o, int S, int heads, int Tt, int Ht, int Wt, int groups_per_bh,
     int ngroups, const int32_t *__restrict__ kv_nb, const int32_t *__restrict__ kv_inds,
-    float scale_log2, const int32_t *__restrict__ order, int32_t *__restrict__ counter) {
+    float scale_log2, const int32_t *__restrict__ order, int32_t *__restrict__ counter,
+    float *__restrict__ lse) {
     constexpr int KS = D / 16;          // k-steps of the score product (16 dims each)
     constexpr int DT = D / 32;          // 32-wide output d tiles
     constexpr int CH = D / 8;           // 16-byte chunks per row
@@ -597,6 +543,11 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     if (myblk >= 0) {
     const float lsum = l_run + __shfl_xor(l_run, 32);
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;  // empty list -> O = 0
+    // natural-log log-sum-exp of the row's scaled scores: (m_ref + log2 l) * ln 2, with the
+    // row sum of the weights P V used; -inf for an empty list
+    if (lse != nullptr && hi == 0)
+        lse[(int64_t)bh * S + qtok] =
+            lsum > 0.0f ? (m_ref + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
     Tin *orow = o + head0 + (int64_t)qtok * tok;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -656,8 +607,8 @@ static int resident_workgroups(K kernel) {
 template <int D, typename Tin>
 static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int B, int S,
                                 int heads, int Tt, int Ht, int Wt, const int32_t *kv_nb,
-                                const int32_t *kv_inds, float scale_log2, void *o, void *ws,
-                                hipStream_t stream) {
+                                const int32_t *kv_inds, float scale_log2, void *o, float *lse,
+                                void *ws, hipStream_t stream) {
     const int nb = S / kBlock;
     const int gpb = groups_per_bh(S, Tt, Ht, Wt);
     const int ngroups = B * heads * gpb;
@@ -683,24 +634,25 @@ static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int
     const int grid = ngroups < resident ? ngroups : resident;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kAttnThreads), 0, stream, (const Tin *)q,
                        (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, Tt, Ht, Wt, gpb,
-                       ngroups, kv_nb, kv_inds, scale_log2, order, counter);
+                       ngroups, kv_nb, kv_inds, scale_log2, order, counter, lse);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
                               int B, int S, int heads, int D, int Tt, int Ht, int Wt,
                               const int32_t *kv_nb, const int32_t *kv_inds, float scale, void *o,
-                              void *ws, hipStream_t stream) {
+                              float *lse, void *ws, hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
-    if (D == 128)
-        return bf16_in ? launch_attn_t<128, bf16>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb,
-                                                  kv_inds, scale_log2, o, ws, stream)
-                       : launch_attn_t<128, float>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb,
-                                                   kv_inds, scale_log2, o, ws, stream);
-    return bf16_in ? launch_attn_t<64, bf16>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds,
-                                             scale_log2, o, ws, stream)
-                   : launch_attn_t<64, float>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds,
-                                              scale_log2, o, ws, stream);
+#define NABLA_ATTN(DD, T)                                                                   \
+    return launch_attn_t<DD, T>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds, scale_log2, \
+                                o, lse, ws, stream)
+    if (D == 128) {
+        if (bf16_in) NABLA_ATTN(128, bf16);
+        NABLA_ATTN(128, float);
+    }
+    if (bf16_in) NABLA_ATTN(64, bf16);
+    NABLA_ATTN(64, float);
+#undef NABLA_ATTN
 }
 
 }  // namespace nabla

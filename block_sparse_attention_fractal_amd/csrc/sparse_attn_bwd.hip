@@ -1,0 +1,479 @@
+// sparse_attn_bwd.hip -- gradients of the NABLA block-sparse attention on gfx950.
+//
+// The forward (sparse_attn.hip) computes, for each query row r of block i,
+// O_r = softmax(scale q_r K_J^T) V_J over the tokens J of the kv blocks listed for i
+// (full 64 x 64 blocks: "nabla" page, NablaAttentionImpl.forward and nablaT_v2's
+// BlockMask creation).  The pages train with this attention (NABLA summary page,
+// Results: the training speed-up; flex attention's backward is the gradient of the
+// same masked softmax).  With the forward's per-row log-sum-exp lse and a given dO:
+//   P  = exp(scale q k^T - lse),   dP = dO V^T,   Delta = rowsum(dO * O)
+//   dS = P (dP - Delta),   dq = scale dS K,   dk = scale dS^T Q,   dv = P^T dO.
+//
+// Kernels (bf16 tensors, fp32 accumulation, v_mfma_f32_32x32x16_bf16):
+//   bwd_delta_kernel          Delta per (b, h, token) from the stored O and dO.
+//   bwd_tlist_*               transposed lists: for kv block j of (b, h), the query
+//                             blocks whose lists hold j, ascending.
+//   bwd_dq_kernel             one workgroup per query block walks its kv list:
+//                             S^T = K Q^T, dP^T = V dO^T, dS^T, dq^T += K^T dS^T.
+//   bwd_dkdv_kernel           one workgroup per kv block walks its query list:
+//                             S = Q K^T, dP = dO V^T, dS, dv^T += dO^T P, dk^T += Q^T dS.
+// Both gradient kernels recompute S and dP, so every output row is written once by one
+// workgroup in a fixed order: no atomics, and the results are deterministic.
+//
+// Layout tricks shared with the forward: a lane owns one column of each 32 x 32
+// product; the rows fed to the first product are permuted (sigma32) so that its fp32
+// results j = 8p .. 8p+7, packed to bf16, are directly the B operand of the second
+// product over 16 consecutive rows; transposed operands come from ds_read_b64_tr_b16.
+#include "attn_tile.h"
+#include "nabla_launch.h"
+
+namespace nabla {
+
+namespace {
+
+constexpr int kBwdThreads = 128;  // 2 waves: the two 32-row (or 32-key) halves of a block
+constexpr float kLog2e = 1.4426950408889634f;
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Transposing read of a bf16 tile in LDS (rows of ROWB bytes, 16-byte chunks XOR-swizzled
+// by kswz): the A operand [32 (d) x 16 (rows)] of k-step kk = 2 mt + p, output d tile dt,
+// i.e. lane l gets tile[32 mt + 16 p + 8 (l / 32) + 0..7][32 dt + l % 32].
+template <int D>
+__device__ __forceinline__ bf16x8 tfrag(const char *tb, int lane, int dt, int kk) {
+    constexpr int CH = D / 8, ROWB = 2 * D;
+    const int g16 = lane >> 4, sl = lane & 15, mt = kk >> 1, p = kk & 1;
+    bf16x8 a;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int row = 32 * mt + 16 * p + 8 * (g16 >> 1) + 4 * r + (sl >> 2);
+        const int d = 32 * dt + 16 * (g16 & 1) + 4 * (sl & 3);
+        const int c = (d >> 3) ^ kswz<CH>(row);
+        const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (NABLA_LDS bf16x4 *)(tb + row * ROWB + (c << 4) + (d & 7) * 2));
+        a[4 * r + 0] = x[0];
+        a[4 * r + 1] = x[1];
+        a[4 * r + 2] = x[2];
+        a[4 * r + 3] = x[3];
+    }
+    return a;
+}
+
+// Row fragment: lane l gets tile[row][16 ks + 8 (l / 32) + 0..7] (A operand of a product
+// over d for row `row`).
+template <int D>
+__device__ __forceinline__ bf16x8 rfrag(const char *tb, int row, int hi, int ks) {
+    constexpr int CH = D / 8, ROWB = 2 * D;
+    const int c = 2 * ks + hi;
+    return *reinterpret_cast<const bf16x8 *>(tb + row * ROWB + ((c ^ kswz<CH>(row)) << 4));
+}
+
+// Per-lane byte offsets (global side) of the 16-byte chunks this thread moves for one
+// 64-row tile: chunk e = r * 128 + tid lands at byte 16 e of the LDS tile, i.e. row e / CH,
+// position e % CH, so the lane fetches global chunk (e % CH) ^ kswz(row).
+template <int D>
+__device__ __forceinline__ void tile_offsets(int tid, int64_t tok, uint32_t (&off)[kBlock * D / 8 / kBwdThreads]) {
+    constexpr int CH = D / 8;
+#pragma unroll
+    for (int r = 0; r < kBlock * CH / kBwdThreads; ++r) {
+        const int e = r * kBwdThreads + tid;
+        const int row = e / CH, cpos = e % CH;
+        off[r] = (uint32_t)((row * tok + 8 * (cpos ^ kswz<CH>(row))) * 2);
+    }
+}
+
+// Stores a [D x 32] fp32 product tile set (acc[dt]: rows d = 32 dt + ..., column = this
+// lane's row) times `mul` as bf16 into row `dst` (the lane's row, D contiguous values).
+template <int D>
+__device__ __forceinline__ void store_rowT(bf16 *dst, const f32x16 (&acc)[D / 32], int hi, float mul) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            bf16x4 r;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) r[u] = (bf16)(acc[dt][4 * jj + u] * mul);
+            *reinterpret_cast<bf16x4 *>(dst + 32 * dt + 8 * jj + 4 * hi) = r;
+        }
+}
+
+}  // namespace
+
+// ---- Delta[bh][s] = sum_d dO[b, s, h, d] * O[b, s, h, d] (fp32, from the bf16 values).
+// D / 8 lanes per (token, head) row, 8 elements each, reduced by lane shuffles.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16 *__restrict__ o,
+                                                       const bf16 *__restrict__ dout,
+                                                       float *__restrict__ delta, int S,
+                                                       int heads, int64_t nrows) {
+    constexpr int L = D / 8;
+    const int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) / L;
+    const int c = threadIdx.x % L;
+    float acc = 0.0f;
+    if (r < nrows) {
+        const bf16x8 x = load8_bf16(o + r * D + 8 * c);
+        const bf16x8 y = load8_bf16(dout + r * D + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
+    }
+#pragma unroll
+    for (int m = 1; m < L; m <<= 1) acc += __shfl_xor(acc, m);
+    if (c == 0 && r < nrows) {
+        const int64_t tok = r / heads;  // b * S + s
+        const int h = (int)(r % heads);
+        const int64_t b = tok / S, s = tok % S;
+        delta[(b * heads + h) * S + s] = acc;
+    }
+}
+
+// ---- transposed lists.  tmat[bh][j][i] = 1 iff block j is listed for query block i.
+__global__ __launch_bounds__(256) void bwd_tlist_zero_kernel(uint4 *__restrict__ t, int64_t n16) {
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n16; e += (int64_t)gridDim.x * 256)
+        t[e] = z;
+}
+
+// grid = B*heads*nb query rows
+__global__ __launch_bounds__(256) void bwd_tlist_scatter_kernel(const int32_t *__restrict__ kv_nb,
+                                                               const int32_t *__restrict__ kv_inds,
+                                                               int nb, uint8_t *__restrict__ tmat) {
+    const int64_t row = blockIdx.x;
+    const int64_t bh = row / nb;
+    const int i = (int)(row % nb);
+    const int n = clamp_count(kv_nb[row], nb);
+    for (int e = threadIdx.x; e < n; e += 256) {
+        const int j = clamp_block(kv_inds[row * nb + e], nb);
+        tmat[(bh * nb + j) * nb + i] = 1;
+    }
+}
+
+// one wave per kv block (bh, j): q_inds[bh][j][0 .. q_nb) = the i with tmat[bh][j][i], ascending
+__global__ __launch_bounds__(256) void bwd_tlist_compact_kernel(const uint8_t *__restrict__ tmat,
+                                                               int nb, int64_t nrows,
+                                                               int32_t *__restrict__ q_nb,
+                                                               int32_t *__restrict__ q_inds) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= nrows) return;  // wave-uniform; no barrier in this kernel
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const uint8_t *t = tmat + row * nb;
+    int base = 0;
+    for (int c0 = 0; c0 < nb; c0 += 64) {
+        const int i = c0 + lane;
+        const bool bit = i < nb && t[i] != 0;
+        const uint64_t bal = __ballot(bit);
+        if (bit) q_inds[row * nb + base + __popcll(bal & below)] = i;
+        base += __popcll(bal);
+    }
+    if (lane == 0) q_nb[row] = base;
+}
+
+// ---- dq.  One workgroup (2 waves) per query block i of (b, h); wave w owns rows 32 w ..
+// 32 w + 31, lane (l32, hi) row 32 w + l32.  K and V tiles of the listed blocks go through
+// a 2-stage LDS ring (direct global -> LDS loads, one tile ahead).
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
+    bf16 *__restrict__ dq, int S, int heads, const int32_t *__restrict__ kv_nb,
+    const int32_t *__restrict__ kv_inds, float scale, float scale_log2) {
+    constexpr int KS = D / 16, DT = D / 32, CPT = kBlock * D / 8 / kBwdThreads;
+    __shared__ __attribute__((aligned(1024))) bf16 ksh[2][kBlock * D];
+    __shared__ __attribute__((aligned(1024))) bf16 vsh[2][kBlock * D];
+
+    const int nb = S / kBlock;
+    const int64_t row = blockIdx.x;
+    const int bh = (int)(row / nb), i = (int)(row % nb);
+    const int b = bh / heads, h = bh % heads;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+    const int64_t tok = (int64_t)heads * D;
+    const int64_t head0 = (int64_t)b * S * tok + (int64_t)h * D;
+    const int qtok = i * kBlock + 32 * w + l32;
+    const int n = clamp_count(kv_nb[row], nb);
+    const int32_t *list = kv_inds + row * nb;
+
+    // Q^T (times scale * log2 e: the score products give log2-domain logits) and dO^T as
+    // B operands: lane (l32, hi) holds d = 16 ks + 8 hi + 0..7 of its row
+    bf16x8 qf[KS], df[KS];
+    {
+        const bf16 *qr = q + head0 + (int64_t)qtok * tok + 8 * hi;
+        const bf16 *dr = dout + head0 + (int64_t)qtok * tok + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 x = load8_bf16(qr + 16 * ks);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)x[e] * scale_log2);
+            df[ks] = load8_bf16(dr + 16 * ks);
+        }
+    }
+    const float lse2 = lse[(int64_t)bh * S + qtok] * kLog2e;
+    const float dl = delta[(int64_t)bh * S + qtok];
+
+    uint32_t off[CPT];
+    tile_offsets<D>(tid, tok, off);
+    const uint32_t ldk = __builtin_amdgcn_readfirstlane(lds_offset(ksh[0]) + w * 64 * 16);
+    const uint32_t ldv = __builtin_amdgcn_readfirstlane(lds_offset(vsh[0]) + w * 64 * 16);
+    auto issue = [&](int jj, int stage) {
+        const int j = __builtin_amdgcn_readfirstlane(clamp_block(jj, nb));
+        const bf16 *kb = k + head0 + (int64_t)j * kBlock * tok;
+        const bf16 *vb = v + head0 + (int64_t)j * kBlock * tok;
+#pragma unroll
+        for (int r = 0; r < CPT; ++r) {
+            const uint32_t sb = stage * (kBlock * D * 2) + r * kBwdThreads * 16;
+            lds_direct16_sv(kb, off[r], ldk + sb);
+            lds_direct16_sv(vb, off[r], ldv + sb);
+        }
+    };
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = splat16(0.0f);
+
+    if (n > 0) issue(list[0], 0);
+    vm_wait<0>();
+    __syncthreads();
+    const int kv0 = sigma32(l32), kv1 = 32 + sigma32(l32);
+    for (int u = 0; u < n; ++u) {
+        const int st = u & 1;
+        if (u + 1 < n) issue(list[u + 1], st ^ 1);
+        const char *kb = reinterpret_cast<const char *>(ksh[st]);
+        const char *vb = reinterpret_cast<const char *>(vsh[st]);
+        // S^T - lse (log2 units) and dP^T for the two 32-key halves
+        f32x16 sacc[2], pacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = splat16(-lse2);
+            pacc[mt] = splat16(-dl);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 k0 = rfrag<D>(kb, kv0, hi, ks), k1 = rfrag<D>(kb, kv1, hi, ks);
+            const bf16x8 v0 = rfrag<D>(vb, kv0, hi, ks), v1 = rfrag<D>(vb, kv1, hi, ks);
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], sacc[1], 0, 0, 0);
+            pacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, df[ks], pacc[0], 0, 0, 0);
+            pacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, df[ks], pacc[1], 0, 0, 0);
+        }
+        // dS^T = P^T (dP^T - Delta), packed: registers 8p .. 8p+7 = 16 consecutive keys
+        bf16x8 ds[2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                ds[mt][j >> 3][j & 7] = (bf16)(__builtin_amdgcn_exp2f(sacc[mt][j]) * pacc[mt][j]);
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(kb, lane, dt, kk),
+                                                                  ds[kk >> 1][kk & 1], acc[dt], 0, 0, 0);
+        vm_wait<0>();
+        __syncthreads();  // tile u + 1 has landed; everyone is done with tile u's stage
+    }
+    store_rowT<D>(dq + head0 + (int64_t)qtok * tok, acc, hi, scale);
+}
+
+// ---- dk, dv.  One workgroup (2 waves) per kv block j of (b, h); wave w owns keys 32 w ..
+// 32 w + 31, lane (l32, hi) key 32 w + l32.  Q and dO tiles of the query blocks that list
+// j go through a 2-stage LDS ring, with their rows' lse (log2 units) and Delta.
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
+    bf16 *__restrict__ dk, bf16 *__restrict__ dv, int S, int heads,
+    const int32_t *__restrict__ q_nb, const int32_t *__restrict__ q_inds, float scale,
+    float scale_log2) {
+    constexpr int KS = D / 16, DT = D / 32, CPT = kBlock * D / 8 / kBwdThreads;
+    __shared__ __attribute__((aligned(1024))) bf16 qsh[2][kBlock * D];
+    __shared__ __attribute__((aligned(1024))) bf16 dsh[2][kBlock * D];
+    __shared__ __attribute__((aligned(16))) float lsh[2][kBlock];  // lse (log2 units)
+    __shared__ __attribute__((aligned(16))) float esh[2][kBlock];  // Delta
+
+    const int nb = S / kBlock;
+    const int64_t row = blockIdx.x;
+    const int bh = (int)(row / nb), j = (int)(row % nb);
+    const int b = bh / heads, h = bh % heads;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+    const int64_t tok = (int64_t)heads * D;
+    const int64_t head0 = (int64_t)b * S * tok + (int64_t)h * D;
+    const int ktok = j * kBlock + 32 * w + l32;
+    const int n = clamp_count(q_nb[row], nb);
+    const int32_t *list = q_inds + row * nb;
+
+    // K^T (times scale * log2 e) and V^T as B operands: lane (l32, hi) holds d = 16 ks +
+    // 8 hi + 0..7 of its key
+    bf16x8 kf[KS], vf[KS];
+    {
+        const bf16 *kr = k + head0 + (int64_t)ktok * tok + 8 * hi;
+        const bf16 *vr = v + head0 + (int64_t)ktok * tok + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 x = load8_bf16(kr + 16 * ks);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kf[ks][e] = (bf16)((float)x[e] * scale_log2);
+            vf[ks] = load8_bf16(vr + 16 * ks);
+        }
+    }
+
+    uint32_t off[CPT];
+    tile_offsets<D>(tid, tok, off);
+    const uint32_t ldq = __builtin_amdgcn_readfirstlane(lds_offset(qsh[0]) + w * 64 * 16);
+    const uint32_t ldd = __builtin_amdgcn_readfirstlane(lds_offset(dsh[0]) + w * 64 * 16);
+    float stash = 0.0f;  // thread t < 64: lse of row t of the next tile; t >= 64: its Delta
+    auto issue = [&](int ii, int stage) {
+        const int i = __builtin_amdgcn_readfirstlane(clamp_block(ii, nb));
+        const bf16 *qb = q + head0 + (int64_t)i * kBlock * tok;
+        const bf16 *db = dout + head0 + (int64_t)i * kBlock * tok;
+#pragma unroll
+        for (int r = 0; r < CPT; ++r) {
+            const uint32_t sb = stage * (kBlock * D * 2) + r * kBwdThreads * 16;
+            lds_direct16_sv(qb, off[r], ldq + sb);
+            lds_direct16_sv(db, off[r], ldd + sb);
+        }
+        const int64_t rr = (int64_t)bh * S + (int64_t)i * kBlock + (tid & 63);
+        stash = tid < 64 ? lse[rr] * kLog2e : delta[rr];
+    };
+    auto land = [&](int stage) {  // after vm_wait: the row statistics into LDS
+        if (tid < 64)
+            lsh[stage][tid] = stash;
+        else
+            esh[stage][tid - 64] = stash;
+    };
+
+    f32x16 dka[DT], dva[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        dka[dt] = splat16(0.0f);
+        dva[dt] = splat16(0.0f);
+    }
+
+    if (n > 0) {
+        issue(list[0], 0);
+        vm_wait<0>();
+        land(0);
+    }
+    __syncthreads();
+    const int qr0 = sigma32(l32), qr1 = 32 + sigma32(l32);
+    for (int u = 0; u < n; ++u) {
+        const int st = u & 1;
+        if (u + 1 < n) issue(list[u + 1], st ^ 1);
+        const char *qb = reinterpret_cast<const char *>(qsh[st]);
+        const char *db = reinterpret_cast<const char *>(dsh[st]);
+        // S (log2 units) and dP: rows = the tile's queries in sigma order, columns = keys
+        f32x16 sacc[2], pacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = splat16(0.0f);
+            pacc[mt] = splat16(0.0f);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a0 = rfrag<D>(qb, qr0, hi, ks), a1 = rfrag<D>(qb, qr1, hi, ks);
+            const bf16x8 g0 = rfrag<D>(db, qr0, hi, ks), g1 = rfrag<D>(db, qr1, hi, ks);
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, kf[ks], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, kf[ks], sacc[1], 0, 0, 0);
+            pacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g0, vf[ks], pacc[0], 0, 0, 0);
+            pacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g1, vf[ks], pacc[1], 0, 0, 0);
+        }
+        // register 8p + e of half mt holds query 32 mt + 16 p + 8 hi + e
+        bf16x8 pp[2][2], dd[2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int q0 = 32 * mt + 16 * p + 8 * hi;
+                const float4 l0 = *reinterpret_cast<const float4 *>(&lsh[st][q0]);
+                const float4 l1 = *reinterpret_cast<const float4 *>(&lsh[st][q0 + 4]);
+                const float4 e0 = *reinterpret_cast<const float4 *>(&esh[st][q0]);
+                const float4 e1 = *reinterpret_cast<const float4 *>(&esh[st][q0 + 4]);
+                const float lq[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                const float eq[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float pr = __builtin_amdgcn_exp2f(sacc[mt][8 * p + e] - lq[e]);
+                    pp[mt][p][e] = (bf16)pr;
+                    dd[mt][p][e] = (bf16)(pr * (pacc[mt][8 * p + e] - eq[e]));
+                }
+            }
+        // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(db, lane, dt, kk),
+                                                                  pp[kk >> 1][kk & 1], dva[dt], 0, 0, 0);
+                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(qb, lane, dt, kk),
+                                                                  dd[kk >> 1][kk & 1], dka[dt], 0, 0, 0);
+            }
+        vm_wait<0>();
+        if (u + 1 < n) land(st ^ 1);
+        __syncthreads();  // tile u + 1 has landed; everyone is done with tile u's stage
+    }
+    store_rowT<D>(dk + head0 + (int64_t)ktok * tok, dka, hi, scale);
+    store_rowT<D>(dv + head0 + (int64_t)ktok * tok, dva, hi, 1.0f);
+}
+
+// ---- host side
+
+// Workspace: [Delta: B*heads*S fp32 | q_nb: B*heads*nb | q_inds: B*heads*nb*nb int32 |
+// tmat: B*heads*nb*nb bytes], each part 256-byte aligned.
+size_t sparse_attn_bwd_workspace_bytes(int B, int S, int heads) {
+    const size_t bh = (size_t)B * heads, nb = (size_t)S / kBlock;
+    return round256(bh * S * 4) + round256(bh * nb * 4) + round256(bh * nb * nb * 4) +
+           round256(bh * nb * nb);
+}
+
+template <int D>
+static hipError_t launch_bwd_t(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *o,
+                               const bf16 *dout, const float *lse, int B, int S, int heads,
+                               const int32_t *kv_nb, const int32_t *kv_inds, float scale, bf16 *dq,
+                               bf16 *dk, bf16 *dv, void *ws, hipStream_t stream) {
+    const int nb = S / kBlock;
+    const size_t BH = (size_t)B * heads;
+    char *p = static_cast<char *>(ws);
+    float *delta = reinterpret_cast<float *>(p);
+    p += round256(BH * S * 4);
+    int32_t *q_nb = reinterpret_cast<int32_t *>(p);
+    p += round256(BH * nb * 4);
+    int32_t *q_inds = reinterpret_cast<int32_t *>(p);
+    p += round256(BH * nb * nb * 4);
+    uint8_t *tmat = reinterpret_cast<uint8_t *>(p);
+    const int64_t tbytes = (int64_t)round256(BH * nb * nb);
+
+    const int64_t nrows = (int64_t)B * S * heads;
+    const int64_t dgrid = (nrows * (D / 8) + 255) / 256;
+    hipLaunchKernelGGL(bwd_delta_kernel<D>, dim3((unsigned)dgrid), dim3(256), 0, stream, o, dout,
+                       delta, S, heads, nrows);
+    const int64_t n16 = tbytes / 16;
+    const int64_t zgrid = (n16 + 255) / 256;
+    hipLaunchKernelGGL(bwd_tlist_zero_kernel, dim3((unsigned)(zgrid < 8192 ? zgrid : 8192)),
+                       dim3(256), 0, stream, reinterpret_cast<uint4 *>(tmat), n16);
+    const unsigned rows = (unsigned)(BH * nb);
+    hipLaunchKernelGGL(bwd_tlist_scatter_kernel, dim3(rows), dim3(256), 0, stream, kv_nb, kv_inds,
+                       nb, tmat);
+    hipLaunchKernelGGL(bwd_tlist_compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, tmat,
+                       nb, (int64_t)rows, q_nb, q_inds);
+    const float scale_log2 = scale * kLog2e;
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(rows), dim3(kBwdThreads), 0, stream, q, k, v, dout,
+                       lse, delta, dq, S, heads, kv_nb, kv_inds, scale, scale_log2);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(rows), dim3(kBwdThreads), 0, stream, q, k, v,
+                       dout, lse, delta, dk, dv, S, heads, q_nb, q_inds, scale, scale_log2);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                                  const void *dout, const float *lse, int B, int S, int heads,
+                                  int D, const int32_t *kv_nb, const int32_t *kv_inds,
+                                  float scale, void *dq, void *dk, void *dv, void *ws,
+                                  hipStream_t stream) {
+    const auto c = [](const void *x) { return static_cast<const bf16 *>(x); };
+    const auto m = [](void *x) { return static_cast<bf16 *>(x); };
+    if (D == 128)
+        return launch_bwd_t<128>(c(q), c(k), c(v), c(o), c(dout), lse, B, S, heads, kv_nb,
+                                 kv_inds, scale, m(dq), m(dk), m(dv), ws, stream);
+    return launch_bwd_t<64>(c(q), c(k), c(v), c(o), c(dout), lse, B, S, heads, kv_nb, kv_inds,
+                            scale, m(dq), m(dk), m(dv), ws, stream);
+}
+
+}  // namespace nabla

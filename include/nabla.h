@@ -169,6 +169,59 @@ nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
                                    int Tt, int Ht, int Wt, void *o, void *ws, size_t ws_bytes,
                                    void *stream);
 
+/*
+ * The same forward, also writing each row's log-sum-exp, which the backward needs
+ * (the training pass of the same attention: NABLA summary page, Results, training
+ * speed-up; the "nabla" page's forward runs flex attention, whose backward is the
+ * gradient of that masked softmax).
+ *
+ * lse:      out [B, heads, S] fp32: log(sum over the row's allowed keys c of
+ *           exp(scale * q . k_c)), natural log; -inf for a row with kv_nb == 0.
+ *           Computed from the same bf16 products and weights as o.
+ * Everything else, the workspace and the errors are those of nabla_sparse_attn_fwd
+ * (lse NULL behaves exactly like nabla_sparse_attn_fwd).
+ */
+nabla_status nabla_sparse_attn_fwd_lse(const void *q, const void *k, const void *v,
+                                       nabla_dtype dtype, int B, int S, int heads, int head_dim,
+                                       const int32_t *kv_nb, const int32_t *kv_inds, float scale,
+                                       int Tt, int Ht, int Wt, void *o, float *lse, void *ws,
+                                       size_t ws_bytes, void *stream);
+
+/*
+ * Bytes of workspace nabla_sparse_attn_bwd needs: round_up(4 B heads S, 256) +
+ * round_up(4 B heads nb, 256) + round_up(4 B heads nb^2, 256) + round_up(B heads nb^2,
+ * 256), nb = S/64 (row deltas, the transposed lists and their byte matrix).  0 if the
+ * sizes are invalid.
+ */
+size_t nabla_sparse_attn_bwd_workspace(int B, int S, int heads);
+
+/*
+ * Backward of nabla_sparse_attn_fwd: the gradients of o with respect to q, k and v for
+ * a given output gradient dO, over the same lists (fixed; the mask is not
+ * differentiated).  With P = exp(scale q k^T - lse) on the allowed blocks (0 elsewhere),
+ * dP = dO V^T and Delta = rowsum(dO * o):
+ *   dS = P (dP - Delta),   dq = scale dS K,   dk = scale dS^T Q,   dv = P^T dO.
+ *
+ * q, k, v, o, dout: [B, S, heads, head_dim] bf16, fractal order; o and lse as written
+ *           by nabla_sparse_attn_fwd_lse for the same q, k, v, lists and scale.
+ * lse:      [B, heads, S] fp32.
+ * kv_nb, kv_inds, scale: as for the forward.
+ * dq, dk, dv: out [B, S, heads, head_dim] bf16; must not overlap the inputs or each
+ *           other.  Every element is written (rows and keys no list touches get 0).
+ * ws:       device workspace of at least nabla_sparse_attn_bwd_workspace() bytes
+ *           (overwritten; no contents carried between calls; calls sharing one
+ *           workspace must be on one stream).
+ * Deterministic: no atomics; each output element is reduced in a fixed order.
+ * Errors: INVALID_ARG (NULL pointer, sizes < 1, S % 64 != 0, NaN scale);
+ * UNSUPPORTED (dtype not bf16, head_dim not 64 or 128, or S/64 > 4096);
+ * WORKSPACE (ws NULL or ws_bytes too small).
+ */
+nabla_status nabla_sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                                   const void *dout, const float *lse, nabla_dtype dtype, int B,
+                                   int S, int heads, int head_dim, const int32_t *kv_nb,
+                                   const int32_t *kv_inds, float scale, void *dq, void *dk,
+                                   void *dv, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

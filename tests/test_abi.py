@@ -37,14 +37,16 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert set(names) == {"nabla_abi_version", "nabla_status_string", "nabla_fractal_permute",
                           "nabla_sta_mask", "nabla_block_mask_workspace", "nabla_block_mask",
-                          "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace"}
+                          "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace",
+                          "nabla_sparse_attn_fwd_lse", "nabla_sparse_attn_bwd_workspace",
+                          "nabla_sparse_attn_bwd"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 3
+    assert L.nabla_abi_version() == 4
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"
@@ -113,6 +115,48 @@ def test_sparse_attn_validation(L):
     assert call(wsb=L.nabla_sparse_attn_workspace(1, 8192, 8, 8, 4, 4) - 1) == WS
 
 
+def test_sparse_attn_fwd_lse_validation(L):
+    f = L.nabla_sparse_attn_fwd_lse
+
+    def call(q=FAKE, o=FAKE, lse=FAKE, S=8192, D=128, ws=FAKE, wsb=1 << 40):
+        return f(q, FAKE, FAKE, BF16, 1, S, 8, D, FAKE, FAKE, 0.0, 8, 4, 4, o, lse, ws, wsb, None)
+
+    assert call(q=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(S=100) == INVALID
+    assert call(D=96) == UNSUP
+    assert call(ws=None) == WS
+    assert call(lse=None, ws=None) == WS   # lse NULL: the plain forward's checks
+
+
+def test_sparse_attn_bwd_workspace_size(L):
+    rnd = lambda x: (x + 255) // 256 * 256
+    bh, S, nb = 16, 61440, 960
+    want = rnd(4 * bh * S) + rnd(4 * bh * nb) + rnd(4 * bh * nb * nb) + rnd(bh * nb * nb)
+    assert L.nabla_sparse_attn_bwd_workspace(1, S, 16) == want
+    assert L.nabla_sparse_attn_bwd_workspace(1, 100, 16) == 0
+    assert L.nabla_sparse_attn_bwd_workspace(1, 64 * 4097, 1) == 0
+    assert L.nabla_sparse_attn_bwd_workspace(0, 64, 1) == 0
+
+
+def test_sparse_attn_bwd_validation(L):
+    f = L.nabla_sparse_attn_bwd
+
+    def call(q=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dt=BF16, B=1, S=8192, D=128, scale=0.0,
+             dq=FAKE, dv=FAKE, ws=FAKE, wsb=1 << 40):
+        return f(q, FAKE, FAKE, o, dout, lse, dt, B, S, 8, D, FAKE, FAKE, scale, dq, FAKE, dv,
+                 ws, wsb, None)
+
+    for kw in ({"q": None}, {"o": None}, {"dout": None}, {"lse": None}, {"dq": None},
+               {"dv": None}, {"S": 100}, {"B": 0}, {"scale": math.nan}, {"dt": 5}):
+        assert call(**kw) == INVALID, kw
+    assert call(dt=FP32) == UNSUP
+    assert call(D=96) == UNSUP
+    assert call(S=64 * 4097) == UNSUP
+    assert call(ws=None) == WS
+    assert call(wsb=L.nabla_sparse_attn_bwd_workspace(1, 8192, 8) - 1) == WS
+
+
 def test_permute_and_sta_validation(L):
     p = L.nabla_fractal_permute
     assert p(None, FAKE, BF16, 1, 2, 16, 16, 2, 64, 0, None) == INVALID
@@ -138,3 +182,6 @@ def test_binding_has_no_cpu_path():
         nabla.nabla_sparse_attn_fwd(q, q, q, kv, kv, causal=True)
     with pytest.raises(TypeError):
         nabla.nabla_sparse_attn_fwd(q, q, q, kv, kv)
+    lse = torch.zeros(1, 1, 128)
+    with pytest.raises(TypeError):
+        nabla.nabla_sparse_attn_bwd(q, q, q, q, q, lse, kv, kv)
