@@ -31,7 +31,8 @@ sys.path.insert(0, ROOT)
 METRIC = "NABLA sparse attn fwd effective TFLOP/s + mask ms at 720p shape, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-ATTN_SRC = os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", "sparse_attn.hip")
+ATTN_SRC = [os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", f)
+            for f in ("sparse_attn.hip", "attn_tile.h", "nabla_device.h")]
 PMC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_720p_pmc.txt")
 
 
@@ -46,14 +47,20 @@ def parse():
                     help="query blocks in the oracle attention sample")
     ap.add_argument("--sweep", action="store_true",
                     help="the sparsity sweep on the 720p shape and the long clip, one line per run")
+    ap.add_argument("--bwd", action="store_true",
+                    help="the training pass instead: forward with lse, then the backward (one line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
 
 
-def src_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def src_sha(paths):
+    """Hash of the attention kernel's sources (the kernel file and the headers it includes)."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(launch_flops_bytes):
@@ -233,6 +240,78 @@ def sweep(torch, nabla, synth, steps, warmup):
         print(json.dumps(line), flush=True)
 
 
+def train_pass(torch, nabla, synth, w, steps, warmup):
+    """The training pass on workload w: nabla_sparse_attn_fwd with lse, then
+    nabla_sparse_attn_bwd for a seeded dO, on the estimator's lists; one JSON line.
+
+    Backward FLOPs are the algorithmic five products per kept pair (S = Q K^T again,
+    dP = dO V^T, dV += P^T dO, dK += dS^T Q, dQ += dS K), 10 * 64 * 64 * D; the kernels
+    recompute S and dP in both gradient kernels (seven products), which is not counted."""
+    dev = torch.device("cuda:0")
+    q, k, v = synth.make_qkv(w)
+    g = [torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in (q, k, v)]
+    qf, kf, vf = (nabla.nabla_fractal_permute(t) for t in g)
+    sta = nabla.nabla_sta_mask(w.tiles, w.sta, dev) if w.sta is not None else None
+    kv_nb, kv_inds = nabla.nabla_block_mask(qf, kf, sta, w.thr)
+    rng = np.random.default_rng(w.seed + 1000)
+    dout = torch.from_numpy(rng.standard_normal(qf.shape, dtype=np.float32)).to(torch.bfloat16).to(dev)
+    B, S, H, D = qf.shape
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    o = torch.empty_like(qf)
+    dq, dk, dv = torch.empty_like(qf), torch.empty_like(qf), torch.empty_like(qf)
+    ws_f = torch.empty(nabla.nabla_sparse_attn_workspace(B, S, H, w.tiles), dtype=torch.uint8,
+                       device=dev)
+    ws_b = torch.empty(nabla.nabla_sparse_attn_bwd_workspace(B, S, H), dtype=torch.uint8,
+                       device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def one(rec=None):
+        e = [ev() for _ in range(3)] if rec is not None else None
+        if e: e[0].record(stream)
+        nabla.nabla_sparse_attn_fwd(qf, kf, vf, kv_nb, kv_inds, tiles=w.tiles, workspace=ws_f,
+                                    out=o, lse=lse)
+        if e: e[1].record(stream)
+        nabla.nabla_sparse_attn_bwd(qf, kf, vf, o, dout, lse, kv_nb, kv_inds, workspace=ws_b,
+                                    dq=dq, dk=dk, dv=dv)
+        if e:
+            e[2].record(stream)
+            rec.append(e)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    rec = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one(rec)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in rec]))
+    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in rec]))
+    pairs = int(kv_nb.sum().item())
+    f_fwd = 4.0 * 64 * 64 * D * pairs
+    f_bwd = 10.0 * 64 * 64 * D * pairs
+    bwd_tf = f_bwd / (bwd_ms * 1e-3) / 1e12
+    out = {
+        "metric": "NABLA sparse attn training pass (fwd with lse + bwd) effective TFLOP/s, 1 MI355X",
+        "value": round((f_fwd + f_bwd) / (wall * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(wall, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded smooth spatio-temporal field + noise, video-shaped; dO ~ N(0,1))",
+        "config": {"workload": w.describe(), "kept_pairs": pairs,
+                   "density": round(pairs / float(B * H * w.nb * w.nb), 5)},
+        "fwd_lse_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2), "bwd_tflops": round(bwd_tf, 2),
+        "roofline": {"bound": "mfma", "achieved": round(bwd_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel": "nabla_sparse_attn_bwd (all its kernels)",
+                     "per_launch": {"flops": f_bwd, "kept_pairs": pairs}},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -248,6 +327,11 @@ def main():
     from block_sparse_attention_fractal_amd import synth
     if args.sweep:
         sweep(torch, nabla, synth, args.steps, args.warmup)
+        return
+    if args.bwd:
+        w = synth.WORKLOADS[args.workload]
+        print("[bench] training pass %s" % w.describe(), file=sys.stderr, flush=True)
+        train_pass(torch, nabla, synth, w, args.steps, args.warmup)
         return
 
     w = synth.WORKLOADS[args.workload]
