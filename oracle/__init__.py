@@ -62,6 +62,10 @@ def _load():
     lib.orc_block_mask.restype = i32
     lib.orc_attention.argtypes = [P, P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
     lib.orc_attention.restype = i32
+    lib.orc_topk_count.argtypes = [i32, f64]
+    lib.orc_topk_count.restype = i32
+    lib.orc_block_mask_topk.argtypes = [P, P, i32, i32, i32, i32, P, f64, P, i64, P, P]
+    lib.orc_block_mask_topk.restype = i32
     lib.orc_attention_lse.argtypes = [P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
     lib.orc_attention_lse.restype = i32
     lib.orc_attention_dq.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
@@ -201,6 +205,31 @@ def block_mask(q, k, sta, thr, want_nabla=False, row_ids=None):
     if want_nabla:
         out["mnabla"] = mn
     return out
+
+
+def topk_count(nb, ratio) -> int:
+    return _load().orc_topk_count(int(nb), float(ratio))
+
+
+def block_mask_topk(q, k, sta, ratio, row_ids=None):
+    """The top-k estimator variant (smooth-k, pooled scores, the ratio * nb largest per row,
+    STA union).  Returns dict(kv_nb, kv_inds) shaped like block_mask's."""
+    q, k = _f32(q), _f32(k)
+    B, S, heads, D = q.shape
+    nb = S // BLOCK
+    if row_ids is None:
+        lead, n, rid = (B, heads, nb), B * heads * nb, None
+    else:
+        rid = np.ascontiguousarray(row_ids, dtype=np.int64)
+        lead, n = (rid.size,), rid.size
+    kv_nb = np.empty(lead, np.int32)
+    kv_inds = np.empty(lead + (nb,), np.int32)
+    st = None if sta is None else np.ascontiguousarray(sta, dtype=np.uint8)
+    rc = _load().orc_block_mask_topk(_ptr(q), _ptr(k), B, S, heads, D, _ptr(st), float(ratio),
+                                     _ptr(rid), n, _ptr(kv_nb), _ptr(kv_inds))
+    if rc != 0:
+        raise ValueError("oracle block_mask_topk: bad argument")
+    return {"kv_nb": kv_nb, "kv_inds": kv_inds}
 
 
 def band_rows(diag, thr, width=1e-6):

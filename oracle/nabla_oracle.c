@@ -333,6 +333,94 @@ int orc_block_mask(const float *q, const float *k, int B, int S, int heads, int 
 }
 
 /* ------------------------------------------------------------------------- */
+/* O12: the top-k estimator variant ("sla" page, get_block_map: smooth-k,      */
+/* mean-pooled q and k blocks, their dot products, the topk_ratio fraction of  */
+/* key blocks with the largest scores per query block).  Readings:             */
+/*   - blocks of 64 tokens for both q and k (the page's BLKQ = BLKK default);  */
+/*   - smooth-k: km[d] = (sum_j ka_j[d], sequential in j, fp32) / nb (IEEE),   */
+/*     ka'_j = ka_j - km; equal in exact arithmetic to pooling k - mean(k);    */
+/*   - s_ij = sequential fma over d of qa_i[d] * ka'_j[d] from +0, no scale,   */
+/*     -0 -> +0 (the page multiplies the pooled blocks, no softmax, no scale); */
+/*   - k = min(nb, floor(ratio * nb)) with the product in double;             */
+/*   - the k largest by (s_j, j): among equal scores the higher index wins     */
+/*     (lower indices are dropped first, as in the CDF cut);                  */
+/*   - optional STA union and ascending compaction as in orc_block_mask.       */
+/* Selection is invariant to subtracting km in exact arithmetic (a per-row    */
+/* constant); the step only changes rounding, so it is kept as the page has it.*/
+/* ------------------------------------------------------------------------- */
+int orc_topk_count(int nb, double ratio) {
+    double x = ratio * (double)nb;
+    int k = (int)x; /* truncation toward zero, x >= 0 */
+    return k < nb ? k : nb;
+}
+
+static int orc_key_less(float sa, int ja, float sb, int jb) {
+    return sa < sb || (sa == sb && ja < jb);
+}
+
+int orc_block_mask_topk(const float *q, const float *k, int B, int S, int heads, int D,
+                        const uint8_t *sta, double ratio, const int64_t *row_ids, int64_t nrows,
+                        int32_t *kv_nb, int32_t *kv_inds) {
+    if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
+    if (!(ratio >= 0.0 && ratio <= 1.0)) return -1;
+    int nb = S / ORC_BLK;
+    int64_t all = (int64_t)B * heads * nb;
+    if (!row_ids) nrows = all;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (row_ids && (row_ids[r] < 0 || row_ids[r] >= all)) return -1;
+    int64_t nbd = (int64_t)B * heads * nb * D;
+    float *qa = (float *)malloc(sizeof(float) * (size_t)nbd);
+    float *ka = (float *)malloc(sizeof(float) * (size_t)nbd);
+    orc_pool(q, qa, B, S, heads, D);
+    orc_pool(k, ka, B, S, heads, D);
+    for (int64_t bh = 0; bh < (int64_t)B * heads; ++bh)
+        for (int d = 0; d < D; ++d) {
+            float sum = 0.0f;
+            for (int j = 0; j < nb; ++j) sum = sum + ka[(bh * nb + j) * D + d];
+            float km = sum / (float)nb;
+            for (int j = 0; j < nb; ++j) ka[(bh * nb + j) * D + d] -= km;
+        }
+    const int kk = orc_topk_count(nb, ratio);
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t rr = 0; rr < nrows; ++rr) {
+        int64_t id = row_ids ? row_ids[rr] : rr;
+        int64_t bh = id / nb;
+        int i = (int)(id % nb);
+        float *srow = (float *)malloc(sizeof(float) * (size_t)nb);
+        uint8_t *kept = (uint8_t *)calloc((size_t)nb, 1);
+        for (int j = 0; j < nb; ++j) {
+            float acc = 0.0f;
+            const float *a = qa + id * D, *b = ka + (bh * nb + j) * D;
+            for (int d = 0; d < D; ++d) acc = fmaf(a[d], b[d], acc);
+            srow[j] = acc + 0.0f;
+        }
+        /* j is among the k largest iff fewer than k keys are larger than (s_j, j) */
+        for (int j = 0; j < nb; ++j) {
+            int larger = 0;
+            for (int t = 0; t < nb; ++t)
+                if (orc_key_less(srow[j], j, srow[t], t)) ++larger;
+            kept[j] = (uint8_t)(larger < kk);
+        }
+        if (sta)
+            for (int j = 0; j < nb; ++j) kept[j] = (uint8_t)(kept[j] | (sta[(int64_t)i * nb + j] != 0));
+        int n = 0;
+        for (int j = 0; j < nb; ++j) n += kept[j];
+        kv_nb[rr] = n;
+        int32_t *row = kv_inds + rr * nb;
+        int w = 0;
+        for (int j = 0; j < nb; ++j)
+            if (kept[j]) row[w++] = j;
+        for (int j = 0; j < nb; ++j)
+            if (!kept[j]) row[w++] = j;
+        free(srow);
+        free(kept);
+    }
+    free(qa);
+    free(ka);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* O10: block-sparse attention as its plain dense definition                  */
 /* ([nabla] NablaAttentionImpl.forward: flex attention with a block mask of   */
 /* full 64 x 64 blocks; [NABLA] Methodology, "Expansion").  For each listed   */

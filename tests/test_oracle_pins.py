@@ -495,3 +495,71 @@ def test_training_pass_sampled_functions_agree(orc):
         hh, i = divmod(int(rid), nb)
         assert np.array_equal(lse[n], full["lse"][0, hh, 64 * i:64 * (i + 1)])
         assert np.array_equal(dq[n], full["dq"][0, 64 * i:64 * (i + 1), hh])
+
+
+# ------------------------------------------------------------------ O12 top-k variant
+def _pool64(x):
+    B, S, h, D = x.shape
+    return x.astype(np.float64).reshape(B, S // 64, 64, h, D).mean(2).transpose(0, 2, 1, 3)  # [B,h,nb,D]
+
+
+def test_topk_count(orc):
+    """k = min(nb, int(ratio * nb)) as the page computes it (Python int() truncates)."""
+    for nb, r in ((960, 0.1), (960, 0.5), (128, 0.95), (8, 0.24), (8, 1.0), (960, 0.0), (3, 0.999)):
+        assert orc.topk_count(nb, r) == min(nb, int(r * nb))
+
+
+def test_topk_matches_torch_topk_on_separated_scores(orc):
+    """With well separated scores the selection equals torch.topk of fp64 pooled smooth-k scores,
+    and equals the top-k without smooth-k (a per-row constant shift in exact arithmetic)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(51)
+    B, S, h, D = 1, 64 * 24, 2, 64
+    # block-constant keys with distinct, well separated block means; noise-free queries
+    q = np.repeat(rng.standard_normal((B, S // 64, 1, h, D)), 64, axis=2).reshape(B, S, h, D)
+    kb = rng.standard_normal((B, S // 64, 1, h, D)) * np.linspace(1, 3, S // 64)[None, :, None, None, None]
+    k = np.repeat(kb, 64, axis=2).reshape(B, S, h, D)
+    q, k = q.astype(np.float32), k.astype(np.float32)
+    qa, ka = _pool64(q), _pool64(k)
+    s_smooth = qa @ (ka - ka.mean(2, keepdims=True)).transpose(0, 1, 3, 2)
+    s_plain = qa @ ka.transpose(0, 1, 3, 2)
+    for ratio in (0.1, 0.25, 0.5):
+        kk = int(ratio * (S // 64))
+        got = orc.block_mask_topk(q, k, None, ratio)
+        assert np.all(got["kv_nb"] == kk)
+        for s_ref in (s_smooth, s_plain):
+            want = torch.topk(torch.from_numpy(s_ref), kk, dim=-1).indices.numpy()
+            for b in range(B):
+                for hh in range(h):
+                    for i in range(S // 64):
+                        gap = np.sort(s_ref[b, hh, i])[::-1]
+                        assert gap[kk - 1] - gap[kk] > 1e-3  # separated at the cut
+                        assert set(got["kv_inds"][b, hh, i, :kk]) == set(want[b, hh, i])
+
+
+def test_topk_edges_and_ties(orc):
+    """ratio 1 keeps every block; ratio 0 keeps none (only STA); Q = 0 (all scores 0) keeps
+    the k highest indices; the first kv_nb entries are ascending; STA union."""
+    rng = np.random.default_rng(52)
+    B, S, h, D = 1, 64 * 10, 2, 64
+    nb = S // 64
+    q = rng.standard_normal((B, S, h, D)).astype(np.float32)
+    k = rng.standard_normal((B, S, h, D)).astype(np.float32)
+    r = orc.block_mask_topk(q, k, None, 1.0)
+    assert np.all(r["kv_nb"] == nb) and np.all(r["kv_inds"] == np.arange(nb))
+    r = orc.block_mask_topk(q, k, None, 0.0)
+    assert np.all(r["kv_nb"] == 0)
+    sta = orc.sta_mask(10, 1, 1, 1, 0, 0)
+    r = orc.block_mask_topk(q, k, sta, 0.0)
+    assert np.array_equal(r["kv_nb"][0, 0], sta.sum(1))
+    r = orc.block_mask_topk(np.zeros_like(q), k, None, 0.35)
+    assert np.all(r["kv_nb"] == 3) and np.all(r["kv_inds"][..., :3] == [7, 8, 9])
+    r = orc.block_mask_topk(q, k, sta, 0.3)
+    for hh in range(h):
+        for i in range(nb):
+            n = r["kv_nb"][0, hh, i]
+            row = r["kv_inds"][0, hh, i, :n]
+            assert np.all(np.diff(row) > 0)
+            assert set(np.flatnonzero(sta[i])) <= set(row) and 3 <= n <= 3 + sta[i].sum()
+    with pytest.raises(ValueError):
+        orc.block_mask_topk(q, k, None, 1.5)
