@@ -47,6 +47,9 @@ def parse():
                     help="query blocks in the oracle attention sample")
     ap.add_argument("--sweep", action="store_true",
                     help="the sparsity sweep on the 720p shape and the long clip, one line per run")
+    ap.add_argument("--topk", type=float, default=None, metavar="RATIO",
+                    help="the top-k estimator variant with this ratio instead of NABLA's CDF cut "
+                         "(a variant line, not the headline)")
     ap.add_argument("--bwd", action="store_true",
                     help="the training pass instead: forward with lse, then the backward (one line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -130,8 +133,9 @@ def cpu_baseline(w, q, k, v, sta_np, g_nb, rows, flops_per_pair):
     }
 
 
-def measure(torch, nabla, w, qkv, steps, warmup):
-    """Run the path on workload w for `steps` timed steps; return the measurement dict."""
+def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None):
+    """Run the path on workload w for `steps` timed steps; return the measurement dict.
+    With topk_ratio the top-k estimator variant replaces NABLA's CDF estimator."""
     import ctypes
     dev = torch.device("cuda:0")
     q, k, v = qkv
@@ -169,8 +173,12 @@ def measure(torch, nabla, w, qkv, steps, warmup):
             check(L.nabla_fractal_permute(P(src), P(dst), dt_code, B, w.T, w.H, w.W, H, D, 0, sp),
                   "permute")
         if e: e[1].record(stream)
-        check(L.nabla_block_mask(P(qf), P(kf), dt_code, B, S, H, D, sta_p, w.thr, P(kv_nb),
-                                 P(kv_inds), P(ws), ws.numel(), sp), "mask")
+        if topk_ratio is None:
+            check(L.nabla_block_mask(P(qf), P(kf), dt_code, B, S, H, D, sta_p, w.thr, P(kv_nb),
+                                     P(kv_inds), P(ws), ws.numel(), sp), "mask")
+        else:
+            check(L.nabla_block_mask_topk(P(qf), P(kf), dt_code, B, S, H, D, sta_p, topk_ratio,
+                                          P(kv_nb), P(kv_inds), P(ws), ws.numel(), sp), "mask")
         if e: e[2].record(stream)
         check(L.nabla_sparse_attn_fwd(P(qf), P(kf), P(vf), dt_code, B, S, H, D, P(kv_nb),
                                       P(kv_inds), 0.0, *w.tiles, P(of), P(ws_attn),
@@ -337,11 +345,14 @@ def main():
     w = synth.WORKLOADS[args.workload]
     print("[bench] %s" % w.describe(), file=sys.stderr, flush=True)
     q, k, v = synth.make_qkv(w)
-    m = measure(torch, nabla, w, (q, k, v), args.steps, args.warmup)
+    m = measure(torch, nabla, w, (q, k, v), args.steps, args.warmup, topk_ratio=args.topk)
     attn_tflops = m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12
     traffic = read_traffic(m["attn_flops"])
+    metric = METRIC if args.topk is None else (
+        "NABLA path with the top-k estimator (ratio %g): sparse attn fwd effective TFLOP/s + "
+        "mask ms at %s shape, 1 MI355X" % (args.topk, w.name))
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(m["attn_flops"] / (m["ms_per_step"] * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -368,7 +379,7 @@ def main():
                      "kernel": "sparse_attn_kernel<128, bf16>",
                      "per_launch": {"flops": m["attn_flops"], "kept_pairs": m["pairs"]}},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.topk is None:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, m["sta_np"], m["g_nb"], args.cpu_rows,
                                            m["flops_per_pair"])

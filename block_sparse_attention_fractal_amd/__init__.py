@@ -59,6 +59,8 @@ def lib():
     L.nabla_block_mask_workspace.restype = Z
     L.nabla_block_mask.argtypes = [P, P, I, I, I, I, I, P, D, P, P, P, Z, P]
     L.nabla_block_mask.restype = I
+    L.nabla_block_mask_topk.argtypes = [P, P, I, I, I, I, I, P, D, P, P, P, Z, P]
+    L.nabla_block_mask_topk.restype = I
     L.nabla_sparse_attn_workspace.argtypes = [I, I, I, I, I, I]
     L.nabla_sparse_attn_workspace.restype = Z
     L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P, Z, P]
@@ -138,10 +140,13 @@ def nabla_block_mask_workspace(B, S, heads, D):
     return lib().nabla_block_mask_workspace(B, S, heads, D)
 
 
-def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None):
+def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None, topk_ratio=None):
     """NABLA estimator: q, k [B, S, heads, D] -> (kv_nb [B,heads,nb] int32, kv_inds [B,heads,nb,nb] int32).
 
     The first kv_nb entries of each kv_inds row are the kept blocks, ascending.
+    With topk_ratio set, the top-k variant runs instead (nabla_block_mask_topk:
+    smooth-k pooled scores, the int(topk_ratio * nb) largest per row); thr is then
+    not used.
     """
     _dev(q, "q")
     _dev(k, "k")
@@ -161,6 +166,11 @@ def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None):
         kv_inds = torch.empty((B, heads, nb, nb), dtype=torch.int32, device=q.device)
     else:
         kv_nb, kv_inds = out
+    if topk_ratio is not None:
+        _check(lib().nabla_block_mask_topk(_p(q), _p(k), _dtype_code(q), B, S, heads, D, _p(sta),
+                                           float(topk_ratio), _p(kv_nb), _p(kv_inds), _p(ws),
+                                           ws.numel(), _stream(q)), "nabla_block_mask_topk")
+        return kv_nb, kv_inds
     _check(lib().nabla_block_mask(_p(q), _p(k), _dtype_code(q), B, S, heads, D, _p(sta),
                                   float(thr), _p(kv_nb), _p(kv_inds), _p(ws), ws.numel(),
                                   _stream(q)), "nabla_block_mask")

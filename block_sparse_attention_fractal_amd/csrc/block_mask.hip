@@ -229,7 +229,10 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-template <int D, int CPT, int RW>
+// TOPK: the top-k variant ("sla" page, get_block_map): scores without the 1/sqrt(D)
+// scale, every block weighs one unit instead of its softmax weight, and `cut` is
+// nb - k + 1, so the cut keeps exactly the k largest keys (none when k = 0).
+template <int D, int CPT, int RW, bool TOPK = false>
 __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restrict__ qa,
                                                           const float *__restrict__ ka, int nb,
                                                           const uint8_t *__restrict__ sta,
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
 #pragma unroll
             for (int rr = 0; rr < RW; ++rr)
                 if (rr == r) a = acc[rr][c];
-            s[c] = a / sqrt_d + 0.0f;
+            s[c] = (TOPK ? a : a / sqrt_d) + 0.0f;
             valid[c] = 64 * c + lane < nb;
             if (valid[c]) {
                 smax = fmaxf(smax, s[c]);
@@ -309,14 +312,19 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
 
         // (the weights are formed twice, for Z and for P, rather than kept: fewer
         // registers live at once)
-        int64_t esum = 0;
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) esum += fix48(valid[c] ? nabla_exp(s[c] - smax) : 0.0f);
-        esum = wave_sum_i64(esum);
-        const float Z = (float)(double)esum * 0x1p-48f;
         int64_t P[CPT];
+        if constexpr (TOPK) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? fix48(nabla_exp(s[c] - smax) / Z) : 0;
+            for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? 1 : 0;
+        } else {
+            int64_t esum = 0;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) esum += fix48(valid[c] ? nabla_exp(s[c] - smax) : 0.0f);
+            esum = wave_sum_i64(esum);
+            const float Z = (float)(double)esum * 0x1p-48f;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? fix48(nabla_exp(s[c] - smax) / Z) : 0;
+        }
 
         // One histogram pass over the members (inr) into kSelBins bins (bin_of); returns
         // the bin holding the cut (-1 if the members' mass stays below it) with the mass
@@ -400,7 +408,9 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
             int64_t below = 0;
             int cnt = 0;
             const int b = hist_pass([&](int c) { return valid[c]; }, bin_f, 0, below, cnt);
-            if (b < 0) {  // total mass below the cut: only the arg-max (largest key) stays
+            if (b < 0 && TOPK) {  // k = 0: no block is selected
+                T = ~0ull;
+            } else if (b < 0) {  // total mass below the cut: only the arg-max (largest key) stays
                 uint64_t km = 0;
 #pragma unroll
                 for (int c = 0; c < CPT; ++c)
@@ -680,14 +690,67 @@ static hipError_t launch_select_t(const float *qa, const float *ka, int BH, int 
     return hipGetLastError();
 }
 
-template <int D, int CPT, int RW>
+template <int D, int CPT, int RW, bool TOPK = false>
 static hipError_t launch_rows_t(const float *qa, const float *ka, int BH, int nb,
                                 const uint8_t *sta, float sqrt_d, int64_t cut, int32_t *kv_nb,
                                 int32_t *kv_inds, hipStream_t stream) {
     dim3 grid((nb + 4 * RW - 1) / (4 * RW), BH);
-    hipLaunchKernelGGL((select_rows_kernel<D, CPT, RW>), grid, dim3(256), 0, stream, qa, ka, nb,
-                       sta, sqrt_d, cut, kv_nb, kv_inds);
+    hipLaunchKernelGGL((select_rows_kernel<D, CPT, RW, TOPK>), grid, dim3(256), 0, stream, qa, ka,
+                       nb, sta, sqrt_d, cut, kv_nb, kv_inds);
     return hipGetLastError();
+}
+
+// top-k variant: rows of up to 2048 blocks (the caller checks)
+template <int D>
+static hipError_t launch_select_topk_d(const float *qa, const float *ka, int BH, int nb,
+                                       const uint8_t *sta, int64_t cut, int32_t *kv_nb,
+                                       int32_t *kv_inds, hipStream_t stream) {
+#define NABLA_ROWS(CPT, RW) \
+    return launch_rows_t<D, CPT, RW, true>(qa, ka, BH, nb, sta, 1.0f, cut, kv_nb, kv_inds, stream)
+    if (nb <= 64) NABLA_ROWS(1, 8);
+    if (nb <= 128) NABLA_ROWS(2, 8);
+    if (nb <= 256) NABLA_ROWS(4, 8);
+    if (nb <= 512) NABLA_ROWS(8, 8);
+    if (nb <= 1024) NABLA_ROWS(16, 4);
+    NABLA_ROWS(32, 2);
+#undef NABLA_ROWS
+}
+
+// smooth-k for the top-k variant: for every (bh, d) the mean over the nb pooled k blocks
+// (fp32, sequential in j, then an IEEE division by nb) is subtracted from those blocks.
+// ka is the pooled [bh][D/4][nb] float4 layout.  grid = (B*heads, D/32), 256 threads: a
+// workgroup owns 32 dims (8 float4 columns, one contiguous region); it stages 256 blocks
+// at a time in LDS with coalesced loads, threads t < 32 add them in order, then all
+// threads subtract over the region.
+__global__ __launch_bounds__(256) void smooth_k_kernel(float *__restrict__ ka, int nb, int D) {
+    constexpr int DB = 32, JC = 256;
+    __shared__ float buf[JC * DB];
+    __shared__ float km[DB];
+    const int t = threadIdx.x;
+    float4 *reg = reinterpret_cast<float4 *>(ka) + ((int64_t)blockIdx.x * (D / 4) +
+                                                     blockIdx.y * (DB / 4)) * nb;
+    float sum = 0.0f;
+    for (int j0 = 0; j0 < nb; j0 += JC) {
+        const int n = nb - j0 < JC ? nb - j0 : JC;
+        for (int e = t; e < (DB / 4) * n; e += 256) {
+            const int c = e / n, jj = e - c * n;  // column c (4 dims), block j0 + jj
+            const float4 x = reg[(int64_t)c * nb + j0 + jj];
+            float *b = &buf[jj * DB + 4 * c];
+            b[0] = x.x;
+            b[1] = x.y;
+            b[2] = x.z;
+            b[3] = x.w;
+        }
+        __syncthreads();
+        if (t < DB)
+            for (int jj = 0; jj < n; ++jj) sum = sum + buf[jj * DB + t];
+        __syncthreads();
+    }
+    if (t < DB) km[t] = sum / (float)nb;
+    __syncthreads();
+    float *r = reinterpret_cast<float *>(reg);
+    const int64_t len = (int64_t)DB * nb;  // floats: ((c * nb) + j) * 4 + k, dim 4c + k
+    for (int64_t e = t; e < len; e += 256) r[e] = r[e] - km[(int)(e / (4 * (int64_t)nb)) * 4 + (int)(e & 3)];
 }
 
 template <int D>
@@ -704,6 +767,30 @@ static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int 
     if (nb <= 2048) NABLA_ROWS(32, 2);
 #undef NABLA_ROWS
     return launch_select_t<D, 8, 8>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
+}
+
+hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, int B, int S,
+                                  int heads, int D, const uint8_t *sta, int topk, int32_t *kv_nb,
+                                  int32_t *kv_inds, float *qa, float *ka, hipStream_t stream) {
+    const int nb = S / kBlock;
+    dim3 pgrid(nb, B);
+    if (bf16_in)
+        hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
+                           (const bf16 *)k, qa, ka, S, heads, D);
+    else
+        hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
+                           (const float *)k, qa, ka, S, heads, D);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int BH = B * heads;
+    hipLaunchKernelGGL(smooth_k_kernel, dim3(BH, D / 32), dim3(256), 0, stream, ka, nb, D);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // unit masses: the keys at ascending rank >= nb - k + 1 are the k largest
+    const int64_t cut = (int64_t)nb - topk + 1;
+    if (D == 64)
+        return launch_select_topk_d<64>(qa, ka, BH, nb, sta, cut, kv_nb, kv_inds, stream);
+    return launch_select_topk_d<128>(qa, ka, BH, nb, sta, cut, kv_nb, kv_inds, stream);
 }
 
 hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, int S,

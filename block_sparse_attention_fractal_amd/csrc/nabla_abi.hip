@@ -12,6 +12,7 @@ constexpr int kAbiVersion = 4;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
 constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
+constexpr int kMaxTopkBlocks = 2048;  // rows the top-k selection holds (one wave per row)
 
 size_t dtype_bytes(nabla_dtype dt) { return dt == NABLA_BF16 ? 2 : 4; }
 bool dtype_ok(nabla_dtype dt) { return dt == NABLA_BF16 || dt == NABLA_FP32; }
@@ -102,6 +103,28 @@ nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, i
     return from_hip(nabla::launch_block_mask(q, k, dtype == NABLA_BF16, B, S, heads, head_dim,
                                              sta, cut_fixed, sqrt_d, kv_nb, kv_inds, qa, ka,
                                              as_stream(stream)));
+}
+
+nabla_status nabla_block_mask_topk(const void *q, const void *k, nabla_dtype dtype, int B,
+                                   int S, int heads, int head_dim, const uint8_t *sta,
+                                   double topk_ratio, int32_t *kv_nb, int32_t *kv_inds, void *ws,
+                                   size_t ws_bytes, void *stream) {
+    if (!q || !k || !kv_nb || !kv_inds || !dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
+    if (!(topk_ratio >= 0.0 && topk_ratio <= 1.0)) return NABLA_ERR_INVALID_ARG;  // also NaN
+    if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
+    const int nb = S / kBlock;
+    if (nb > kMaxTopkBlocks) return NABLA_ERR_UNSUPPORTED;
+    const size_t need = nabla_block_mask_workspace(B, S, heads, head_dim);
+    if (!ws || ws_bytes < need) return NABLA_ERR_WORKSPACE;
+    // k = min(nb, int(ratio * nb)): the product in double, truncated
+    const double x = topk_ratio * (double)nb;
+    const int topk = x >= (double)nb ? nb : (int)x;
+    float *qa = static_cast<float *>(ws);
+    float *ka = qa + (size_t)B * heads * nb * head_dim;
+    return from_hip(nabla::launch_block_mask_topk(q, k, dtype == NABLA_BF16, B, S, heads,
+                                                  head_dim, sta, topk, kv_nb, kv_inds, qa, ka,
+                                                  as_stream(stream)));
 }
 
 size_t nabla_sparse_attn_workspace(int B, int S, int heads, int Tt, int Ht, int Wt) {

@@ -21,6 +21,12 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
                              float sqrt_d, int32_t *kv_nb, int32_t *kv_inds, float *qa,
                              float *ka, hipStream_t stream);
 
+// The top-k variant: pooled blocks, smooth-k, the topk largest scores per row (k <= nb,
+// nb <= 2048), STA union.
+hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, int B, int S,
+                                  int heads, int D, const uint8_t *sta, int topk, int32_t *kv_nb,
+                                  int32_t *kv_inds, float *qa, float *ka, hipStream_t stream);
+
 // Tt, Ht, Wt: tile grid of the query blocks (Tt*Ht*Wt == S/64), or all 0 if unknown.
 // ws: sparse_attn_workspace_bytes() bytes (schedule: counter, group costs, order).
 size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt);

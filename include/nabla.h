@@ -126,6 +126,29 @@ nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, i
                               void *stream);
 
 /*
+ * The top-k estimator variant (the sibling "sla" backend page, get_block_map:
+ * smooth-k, mean-pooled q and k blocks, their dot products, and per query block
+ * the topk_ratio fraction of key blocks with the largest scores), on 64-token
+ * blocks, with the same list format and optional STA union as nabla_block_mask:
+ *   qa_i, ka_j = block means (fp32, as nabla_block_mask);
+ *   km = (sum over j of ka_j, sequential in j) / nb;  ka'_j = ka_j - km;
+ *   s_ij = <qa_i, ka'_j> (sequential fma over d, no scale);
+ *   k = min(nb, int(topk_ratio * nb)) (double product, truncated);
+ *   block j is kept when it is among the k largest by (s_ij, j) (on equal scores
+ *   the higher index wins), then kept |= sta[i][j].
+ * Every row keeps exactly k blocks before the union (0 when k = 0: with no STA the
+ * lists are empty and the attention gives o = 0 for them).
+ * q, k, sta, kv_nb, kv_inds, ws: as for nabla_block_mask (same workspace size).
+ * Errors: INVALID_ARG (NULL q/k/kv_nb/kv_inds, sizes < 1, S % 64 != 0, topk_ratio
+ * NaN or outside [0, 1]); UNSUPPORTED (head_dim not 64 or 128, or nb > 2048);
+ * WORKSPACE (ws NULL or ws_bytes too small).
+ */
+nabla_status nabla_block_mask_topk(const void *q, const void *k, nabla_dtype dtype, int B,
+                                   int S, int heads, int head_dim, const uint8_t *sta,
+                                   double topk_ratio, int32_t *kv_nb, int32_t *kv_inds, void *ws,
+                                   size_t ws_bytes, void *stream);
+
+/*
  * Bytes of workspace nabla_sparse_attn_fwd needs for the same (B, S, heads) and tile
  * grid: 256 + 2 * round_up(4 * ngroups, 256), where ngroups = B * heads *
  * ceil(Tt/2) * Ht * ceil(Wt/2) (tile grid known) or B * heads * ceil(S/256)

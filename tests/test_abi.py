@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(L):
                           "nabla_sta_mask", "nabla_block_mask_workspace", "nabla_block_mask",
                           "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace",
                           "nabla_sparse_attn_fwd_lse", "nabla_sparse_attn_bwd_workspace",
-                          "nabla_sparse_attn_bwd"}
+                          "nabla_sparse_attn_bwd", "nabla_block_mask_topk"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -78,6 +78,24 @@ def test_block_mask_validation(L):
         assert call(thr=thr) == INVALID
     assert call(D=96) == UNSUP
     assert call(S=64 * 4097) == UNSUP            # longer rows than the selection kernel holds
+    assert call(ws=None) == WS
+    assert call(wsb=L.nabla_block_mask_workspace(1, 8192, 8, 128) - 1) == WS
+
+
+def test_block_mask_topk_validation(L):
+    f = L.nabla_block_mask_topk
+
+    def call(q=FAKE, dt=BF16, B=1, S=8192, D=128, ratio=0.1, kv_nb=FAKE, ws=FAKE, wsb=1 << 40):
+        return f(q, FAKE, dt, B, S, 8, D, None, ratio, kv_nb, FAKE, ws, wsb, None)
+
+    assert call(q=None) == INVALID
+    assert call(kv_nb=None) == INVALID
+    assert call(dt=7) == INVALID
+    assert call(S=8192 + 32) == INVALID
+    for r in (-0.01, 1.01, math.nan):
+        assert call(ratio=r) == INVALID
+    assert call(D=96) == UNSUP
+    assert call(S=64 * 2049) == UNSUP            # one wave holds a row of up to 2048 blocks
     assert call(ws=None) == WS
     assert call(wsb=L.nabla_block_mask_workspace(1, 8192, 8, 128) - 1) == WS
 
