@@ -50,6 +50,19 @@ def _load():
     lib.orc_fractal_permute.argtypes = [P, P, i64, i32, i32, i32, i32, i32, i32, i32]
     lib.orc_sta_mask.argtypes = [P, i32, i32, i32, i32, i32, i32]
     lib.orc_pool.argtypes = [P, P, i32, i32, i32, i32]
+    lib.orc_fractal_len.argtypes = [i32, i32, i32]
+    lib.orc_fractal_len.restype = i64
+    lib.orc_token_valid.argtypes = [i64, i32, i32]
+    lib.orc_token_valid.restype = i32
+    lib.orc_pool_grid.argtypes = [P, P, i32, i32, i32, i32, i32, i32]
+    lib.orc_block_mask_grid.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, f64, P, i64, P, P,
+                                        P, P]
+    lib.orc_block_mask_grid.restype = i32
+    lib.orc_block_mask_topk_grid.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, f64, P, i64,
+                                             P, P]
+    lib.orc_block_mask_topk_grid.restype = i32
+    lib.orc_attention_grid.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, f64, P, i64, P]
+    lib.orc_attention_grid.restype = i32
     lib.orc_scores.argtypes = [P, P, P, i32, i32, i32, i32]
     lib.orc_nexp.argtypes = [ctypes.c_float]
     lib.orc_nexp.restype = ctypes.c_float
@@ -99,15 +112,35 @@ def fractal_index(t, y, x, H, W) -> int:
     return _load().orc_fractal_index(t, y, x, H, W)
 
 
-def fractal_permute(x, inverse=False):
-    """x natural [B,T,H,W,heads,D] -> fractal [B,S,heads,D] (or back).
+def fractal_len(T, H, W) -> int:
+    """Sequence length of the fractal order of a T x H x W grid (padded to whole 8 x 8 patches)."""
+    return _load().orc_fractal_len(T, H, W)
 
-    Any fixed-size dtype (the permutation moves bytes).  For ``inverse`` pass
-    the fractal tensor with shape [B,T,H,W,heads,D] viewed as such.
+
+def token_valid(T, H, W):
+    """bool [S]: which fractal positions of one sequence are tokens (False = patch padding)."""
+    S = fractal_len(T, H, W)
+    lib = _load()
+    return np.array([bool(lib.orc_token_valid(s, H, W)) for s in range(S)])
+
+
+def fractal_permute(x, inverse=False, grid=None):
+    """Forward: x natural [B,T,H,W,heads,D] -> fractal [B,S,heads,D], S = fractal_len(T,H,W)
+    (padding rows of partial patches are 0).  Inverse: x fractal [B,S,heads,D] with
+    grid=(T,H,W) (or a natural-shaped array of a grid of whole patches) -> natural.
+    Any fixed-size dtype (the permutation moves bytes).
     """
     x = np.ascontiguousarray(x)
-    B, T, H, W, heads, D = x.shape
-    y = np.empty_like(x)
+    if not inverse:
+        B, T, H, W, heads, D = x.shape
+        y = np.empty((B, fractal_len(T, H, W), heads, D), dtype=x.dtype)
+    else:
+        if x.ndim == 6:
+            B, T, H, W, heads, D = x.shape
+        else:
+            B, _, heads, D = x.shape
+            T, H, W = grid
+        y = np.empty((B, T, H, W, heads, D), dtype=x.dtype)
     _load().orc_fractal_permute(_ptr(x), _ptr(y), x.itemsize, B, T, H, W, heads, D, int(inverse))
     return y
 
@@ -127,6 +160,16 @@ def pool(x):
     B, S, heads, D = x.shape
     out = np.empty((B, heads, S // BLOCK, D), dtype=np.float32)
     _load().orc_pool(_ptr(x), _ptr(out), B, S, heads, D)
+    return out
+
+
+def pool_grid(x, grid):
+    """x fractal [B,S,heads,D] of a padded T x H x W grid -> [B,heads,nb,D]: means over tokens only."""
+    x = _f32(x)
+    B, S, heads, D = x.shape
+    T, H, W = grid
+    out = np.empty((B, heads, S // BLOCK, D), dtype=np.float32)
+    _load().orc_pool_grid(_ptr(x), _ptr(out), B, T, H, W, heads, D)
     return out
 
 
@@ -205,6 +248,56 @@ def block_mask(q, k, sta, thr, want_nabla=False, row_ids=None):
     if want_nabla:
         out["mnabla"] = mn
     return out
+
+
+def block_mask_grid(q, k, grid, sta, thr, topk_ratio=None, row_ids=None):
+    """Either estimator on the padded fractal layout of grid = (T, H, W): pooled means over
+    tokens only.  Returns dict(kv_nb, kv_inds) (and diag for the CDF estimator)."""
+    q, k = _f32(q), _f32(k)
+    B, S, heads, D = q.shape
+    T, H, W = grid
+    nb = S // BLOCK
+    if row_ids is None:
+        lead, n, rid = (B, heads, nb), B * heads * nb, None
+    else:
+        rid = np.ascontiguousarray(row_ids, dtype=np.int64)
+        lead, n = (rid.size,), rid.size
+    kv_nb = np.empty(lead, np.int32)
+    kv_inds = np.empty(lead + (nb,), np.int32)
+    st = None if sta is None else np.ascontiguousarray(sta, dtype=np.uint8)
+    lib = _load()
+    if topk_ratio is None:
+        diag = np.empty(lead + (3,), np.int64)
+        rc = lib.orc_block_mask_grid(_ptr(q), _ptr(k), B, T, H, W, heads, D, _ptr(st), float(thr),
+                                     _ptr(rid), n, _ptr(kv_nb), _ptr(kv_inds), None, _ptr(diag))
+        out = {"kv_nb": kv_nb, "kv_inds": kv_inds, "diag": diag}
+    else:
+        rc = lib.orc_block_mask_topk_grid(_ptr(q), _ptr(k), B, T, H, W, heads, D, _ptr(st),
+                                          float(topk_ratio), _ptr(rid), n, _ptr(kv_nb),
+                                          _ptr(kv_inds))
+        out = {"kv_nb": kv_nb, "kv_inds": kv_inds}
+    if rc != 0:
+        raise ValueError("oracle block_mask_grid: bad argument")
+    return out
+
+
+def attention_grid(q, k, v, grid, kv_nb, kv_inds, row_ids=None, scale=0.0):
+    """attention() on the padded fractal layout of grid = (T, H, W): padding is never a key."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, S, heads, D = q.shape
+    T, H, W = grid
+    nb = S // BLOCK
+    if row_ids is None:
+        row_ids = np.arange(B * heads * nb, dtype=np.int64)
+    row_ids = np.ascontiguousarray(row_ids, dtype=np.int64)
+    kv_nb, kv_inds = _lists(kv_nb, kv_inds)
+    o = np.zeros((row_ids.size, BLOCK, D), np.float64)
+    rc = _load().orc_attention_grid(_ptr(q), _ptr(k), _ptr(v), B, T, H, W, heads, D, _ptr(kv_nb),
+                                    _ptr(kv_inds), float(scale), _ptr(row_ids), row_ids.size,
+                                    _ptr(o))
+    if rc != 0:
+        raise ValueError("oracle attention_grid: bad argument")
+    return row_ids, o
 
 
 def topk_count(nb, ratio) -> int:

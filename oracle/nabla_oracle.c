@@ -68,20 +68,42 @@ int orc_get_threads(void) {
 /* The tokens of each 8 x 8 spatial patch of one frame become a contiguous    */
 /* run of 64; frames stay in time order; patches go in raster order (patch    */
 /* row, patch column); inside a patch, raster order (row, column).            */
+/* Grids whose H or W is not a multiple of 8 are padded to whole patches       */
+/* (ceil(H/8) x ceil(W/8) per frame, the sibling "video_sparse_attn" page's    */
+/* variable block sizes): the padded positions exist in the fractal order,    */
+/* hold zeros, and are not tokens (see orc_token_valid).                       */
 /* ------------------------------------------------------------------------- */
+static int orc_tiles(int n) { return (n + ORC_TILE - 1) / ORC_TILE; }
+
 int64_t orc_fractal_index(int t, int y, int x, int H, int W) {
-    int Ht = H / ORC_TILE, Wt = W / ORC_TILE;
+    int Ht = orc_tiles(H), Wt = orc_tiles(W);
     int64_t tile = ((int64_t)t * Ht + y / ORC_TILE) * Wt + x / ORC_TILE;
     return tile * ORC_BLK + (y % ORC_TILE) * ORC_TILE + (x % ORC_TILE);
 }
 
-/* x, y: one token row = heads*D elements of esize bytes.
- * inverse == 0: x natural [B][T][H][W][row] -> y fractal [B][S][row]
- * inverse != 0: x fractal -> y natural. */
+/* Sequence length of the fractal order of a T x H x W grid (padded to whole patches). */
+int64_t orc_fractal_len(int T, int H, int W) {
+    return (int64_t)T * orc_tiles(H) * orc_tiles(W) * ORC_BLK;
+}
+
+/* 1 if fractal position s (within one sequence) is a token of the T x H x W grid, 0 if it
+ * is padding of a partial patch. */
+int orc_token_valid(int64_t s, int H, int W) {
+    int Ht = orc_tiles(H), Wt = orc_tiles(W);
+    int64_t blk = s / ORC_BLK;
+    int r = (int)(s % ORC_BLK);
+    int ht = (int)((blk / Wt) % Ht), wt = (int)(blk % Wt);
+    return ht * ORC_TILE + r / ORC_TILE < H && wt * ORC_TILE + r % ORC_TILE < W;
+}
+
+/* x, y: one token row = heads*D elements of esize bytes; S = orc_fractal_len(T, H, W).
+ * inverse == 0: x natural [B][T][H][W][row] -> y fractal [B][S][row] (padding rows 0)
+ * inverse != 0: x fractal -> y natural (padding rows are not read). */
 void orc_fractal_permute(const uint8_t *x, uint8_t *y, int64_t esize, int B, int T, int H,
                          int W, int heads, int D, int inverse) {
     int64_t row = (int64_t)heads * D * esize;
-    int64_t S = (int64_t)T * H * W;
+    int64_t S = orc_fractal_len(T, H, W);
+    if (!inverse) memset(y, 0, (size_t)(B * S * row));
     for (int b = 0; b < B; ++b)
         for (int t = 0; t < T; ++t)
             for (int yy = 0; yy < H; ++yy)
@@ -130,6 +152,30 @@ void orc_pool(const float *x, float *xa, int B, int S, int heads, int D) {
                         acc = acc + x[(tok * heads + h) * D + d];
                     }
                     xa[(((int64_t)b * heads + h) * nb + i) * D + d] = acc * 0.015625f;
+                }
+}
+
+/* O3 on a padded grid: the mean over the block's tokens only (padding excluded): the sum
+ * over its valid positions in fractal order, then an IEEE division by their count (for a
+ * full block the count is 64 and this equals orc_pool).  x [B][S][heads][D] with
+ * S = orc_fractal_len(T, H, W). */
+void orc_pool_grid(const float *x, float *xa, int B, int T, int H, int W, int heads, int D) {
+    int64_t S = orc_fractal_len(T, H, W);
+    int nb = (int)(S / ORC_BLK);
+    for (int b = 0; b < B; ++b)
+        for (int h = 0; h < heads; ++h)
+            for (int i = 0; i < nb; ++i)
+                for (int d = 0; d < D; ++d) {
+                    float acc = 0.0f;
+                    int cnt = 0;
+                    for (int r = 0; r < ORC_BLK; ++r) {
+                        int64_t s_ = (int64_t)i * ORC_BLK + r;
+                        if (!orc_token_valid(s_, H, W)) continue;
+                        int64_t tok = (int64_t)b * S + s_;
+                        acc = acc + x[(tok * heads + h) * D + d];
+                        ++cnt;
+                    }
+                    xa[(((int64_t)b * heads + h) * nb + i) * D + d] = acc / (float)cnt;
                 }
 }
 
@@ -284,9 +330,12 @@ void orc_select_row(const float *s, int nb, double thr, uint8_t *kept, int64_t *
 /*   diag    [nrows][3]          (optional) see orc_select_row.               */
 /* Returns 0, or -1 on a bad argument.                                        */
 /* ------------------------------------------------------------------------- */
-int orc_block_mask(const float *q, const float *k, int B, int S, int heads, int D,
-                   const uint8_t *sta, double thr, const int64_t *row_ids, int64_t nrows,
-                   int32_t *kv_nb, int32_t *kv_inds, uint8_t *mnabla, int64_t *diag) {
+/* gT, gH, gW: the latent grid of a padded layout (pooling over tokens only), or all 0 for
+ * whole 64-token blocks. */
+static int orc_block_mask_impl(const float *q, const float *k, int B, int S, int heads, int D,
+                               int gT, int gH, int gW, const uint8_t *sta, double thr,
+                               const int64_t *row_ids, int64_t nrows, int32_t *kv_nb,
+                               int32_t *kv_inds, uint8_t *mnabla, int64_t *diag) {
     if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
     if (!(thr >= 0.0 && thr <= 1.0)) return -1;
     int nb = S / ORC_BLK;
@@ -297,8 +346,13 @@ int orc_block_mask(const float *q, const float *k, int B, int S, int heads, int 
     int64_t nbd = (int64_t)B * heads * nb * D;
     float *qa = (float *)malloc(sizeof(float) * (size_t)nbd);
     float *ka = (float *)malloc(sizeof(float) * (size_t)nbd);
-    orc_pool(q, qa, B, S, heads, D);
-    orc_pool(k, ka, B, S, heads, D);
+    if (gH > 0) {
+        orc_pool_grid(q, qa, B, gT, gH, gW, heads, D);
+        orc_pool_grid(k, ka, B, gT, gH, gW, heads, D);
+    } else {
+        orc_pool(q, qa, B, S, heads, D);
+        orc_pool(k, ka, B, S, heads, D);
+    }
     float sqrt_d = (float)sqrt((double)D);
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t rr = 0; rr < nrows; ++rr) {
@@ -332,6 +386,23 @@ int orc_block_mask(const float *q, const float *k, int B, int S, int heads, int 
     return 0;
 }
 
+int orc_block_mask(const float *q, const float *k, int B, int S, int heads, int D,
+                   const uint8_t *sta, double thr, const int64_t *row_ids, int64_t nrows,
+                   int32_t *kv_nb, int32_t *kv_inds, uint8_t *mnabla, int64_t *diag) {
+    return orc_block_mask_impl(q, k, B, S, heads, D, 0, 0, 0, sta, thr, row_ids, nrows, kv_nb,
+                               kv_inds, mnabla, diag);
+}
+
+/* The estimator on the padded fractal layout of a T x H x W grid (S = orc_fractal_len). */
+int orc_block_mask_grid(const float *q, const float *k, int B, int T, int H, int W, int heads,
+                        int D, const uint8_t *sta, double thr, const int64_t *row_ids,
+                        int64_t nrows, int32_t *kv_nb, int32_t *kv_inds, uint8_t *mnabla,
+                        int64_t *diag) {
+    if (T <= 0 || H <= 0 || W <= 0) return -1;
+    return orc_block_mask_impl(q, k, B, (int)orc_fractal_len(T, H, W), heads, D, T, H, W, sta,
+                               thr, row_ids, nrows, kv_nb, kv_inds, mnabla, diag);
+}
+
 /* ------------------------------------------------------------------------- */
 /* O12: the top-k estimator variant ("sla" page, get_block_map: smooth-k,      */
 /* mean-pooled q and k blocks, their dot products, the topk_ratio fraction of  */
@@ -358,9 +429,10 @@ static int orc_key_less(float sa, int ja, float sb, int jb) {
     return sa < sb || (sa == sb && ja < jb);
 }
 
-int orc_block_mask_topk(const float *q, const float *k, int B, int S, int heads, int D,
-                        const uint8_t *sta, double ratio, const int64_t *row_ids, int64_t nrows,
-                        int32_t *kv_nb, int32_t *kv_inds) {
+static int orc_block_mask_topk_impl(const float *q, const float *k, int B, int S, int heads,
+                                    int D, int gT, int gH, int gW, const uint8_t *sta,
+                                    double ratio, const int64_t *row_ids, int64_t nrows,
+                                    int32_t *kv_nb, int32_t *kv_inds) {
     if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
     if (!(ratio >= 0.0 && ratio <= 1.0)) return -1;
     int nb = S / ORC_BLK;
@@ -371,8 +443,13 @@ int orc_block_mask_topk(const float *q, const float *k, int B, int S, int heads,
     int64_t nbd = (int64_t)B * heads * nb * D;
     float *qa = (float *)malloc(sizeof(float) * (size_t)nbd);
     float *ka = (float *)malloc(sizeof(float) * (size_t)nbd);
-    orc_pool(q, qa, B, S, heads, D);
-    orc_pool(k, ka, B, S, heads, D);
+    if (gH > 0) {
+        orc_pool_grid(q, qa, B, gT, gH, gW, heads, D);
+        orc_pool_grid(k, ka, B, gT, gH, gW, heads, D);
+    } else {
+        orc_pool(q, qa, B, S, heads, D);
+        orc_pool(k, ka, B, S, heads, D);
+    }
     for (int64_t bh = 0; bh < (int64_t)B * heads; ++bh)
         for (int d = 0; d < D; ++d) {
             float sum = 0.0f;
@@ -420,6 +497,22 @@ int orc_block_mask_topk(const float *q, const float *k, int B, int S, int heads,
     return 0;
 }
 
+int orc_block_mask_topk(const float *q, const float *k, int B, int S, int heads, int D,
+                        const uint8_t *sta, double ratio, const int64_t *row_ids, int64_t nrows,
+                        int32_t *kv_nb, int32_t *kv_inds) {
+    return orc_block_mask_topk_impl(q, k, B, S, heads, D, 0, 0, 0, sta, ratio, row_ids, nrows,
+                                    kv_nb, kv_inds);
+}
+
+int orc_block_mask_topk_grid(const float *q, const float *k, int B, int T, int H, int W,
+                             int heads, int D, const uint8_t *sta, double ratio,
+                             const int64_t *row_ids, int64_t nrows, int32_t *kv_nb,
+                             int32_t *kv_inds) {
+    if (T <= 0 || H <= 0 || W <= 0) return -1;
+    return orc_block_mask_topk_impl(q, k, B, (int)orc_fractal_len(T, H, W), heads, D, T, H, W,
+                                    sta, ratio, row_ids, nrows, kv_nb, kv_inds);
+}
+
 /* ------------------------------------------------------------------------- */
 /* O10: block-sparse attention as its plain dense definition                  */
 /* ([nabla] NablaAttentionImpl.forward: flex attention with a block mask of   */
@@ -429,9 +522,11 @@ int orc_block_mask_topk(const float *q, const float *k, int B, int S, int heads,
 /*   o = sum_c softmax(z)_c v_c, all in fp64.                                 */
 /* o: [nrows][64][D] fp64.  A row whose list is empty yields 0.               */
 /* ------------------------------------------------------------------------- */
-int orc_attention(const float *q, const float *k, const float *v, int B, int S, int heads,
-                  int D, const int32_t *kv_nb, const int32_t *kv_inds, double scale,
-                  const int64_t *row_ids, int64_t nrows, double *o) {
+/* gH, gW: the latent extents of a padded layout (padding positions are not keys), or 0. */
+static int orc_attention_impl(const float *q, const float *k, const float *v, int B, int S,
+                              int heads, int D, int gH, int gW, const int32_t *kv_nb,
+                              const int32_t *kv_inds, double scale, const int64_t *row_ids,
+                              int64_t nrows, double *o) {
     if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
     int nb = S / ORC_BLK;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
@@ -458,7 +553,10 @@ int orc_attention(const float *q, const float *k, const float *v, int B, int S, 
             double *orow = o + (rr * ORC_BLK + r) * D;
             double zmax = -INFINITY;
             for (int64_t c = 0; c < S; ++c) {
-                if (!allowed[c / ORC_BLK]) { z[c] = -INFINITY; continue; }
+                if (!allowed[c / ORC_BLK] || (gH > 0 && !orc_token_valid(c, gH, gW))) {
+                    z[c] = -INFINITY;
+                    continue;
+                }
                 const float *kc = k + ((b * S + c) * heads + h) * D;
                 double acc = 0.0;
                 for (int d = 0; d < D; ++d) acc += (double)qr[d] * (double)kc[d];
@@ -481,6 +579,23 @@ int orc_attention(const float *q, const float *k, const float *v, int B, int S, 
         free(allowed);
     }
     return bad ? -1 : 0;
+}
+
+int orc_attention(const float *q, const float *k, const float *v, int B, int S, int heads,
+                  int D, const int32_t *kv_nb, const int32_t *kv_inds, double scale,
+                  const int64_t *row_ids, int64_t nrows, double *o) {
+    return orc_attention_impl(q, k, v, B, S, heads, D, 0, 0, kv_nb, kv_inds, scale, row_ids,
+                              nrows, o);
+}
+
+/* The attention on the padded fractal layout of a T x H x W grid: padding positions are
+ * never keys (their query rows are computed too; the inverse permute drops them). */
+int orc_attention_grid(const float *q, const float *k, const float *v, int B, int T, int H,
+                       int W, int heads, int D, const int32_t *kv_nb, const int32_t *kv_inds,
+                       double scale, const int64_t *row_ids, int64_t nrows, double *o) {
+    if (T <= 0 || H <= 0 || W <= 0) return -1;
+    return orc_attention_impl(q, k, v, B, (int)orc_fractal_len(T, H, W), heads, D, H, W, kv_nb,
+                              kv_inds, scale, row_ids, nrows, o);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -56,7 +56,7 @@ def test_fractal_permute_roundtrip(orc):
     rng = np.random.default_rng(0)
     x = rng.standard_normal((2, 2, 16, 24, 3, 8)).astype(np.float32)
     y = orc.fractal_permute(x)
-    back = orc.fractal_permute(y, inverse=True)
+    back = orc.fractal_permute(y, inverse=True, grid=x.shape[1:4])
     assert np.array_equal(back, x)
     # spot-check placement against the index formula
     B, T, H, W, h, D = x.shape
@@ -65,7 +65,7 @@ def test_fractal_permute_roundtrip(orc):
         assert np.array_equal(yf[b, orc.fractal_index(t, yy, xx, H, W)], x[b, t, yy, xx])
     # dtype-agnostic (bytes): bf16 bit patterns as uint16
     u = rng.integers(0, 65535, size=(1, 2, 8, 16, 2, 4), dtype=np.uint16)
-    assert np.array_equal(orc.fractal_permute(orc.fractal_permute(u), inverse=True), u)
+    assert np.array_equal(orc.fractal_permute(orc.fractal_permute(u), inverse=True, grid=(2, 8, 16)), u)
 
 
 # ------------------------------------------------------------------ O2 STA
@@ -563,3 +563,104 @@ def test_topk_edges_and_ties(orc):
             assert set(np.flatnonzero(sta[i])) <= set(row) and 3 <= n <= 3 + sta[i].sum()
     with pytest.raises(ValueError):
         orc.block_mask_topk(q, k, None, 1.5)
+
+
+# ------------------------------------------------------------------ padded grids (NEXT-2)
+def test_padded_permute_and_block_sizes(orc):
+    """H, W not multiples of 8: the grid is padded to whole patches; every token lands on a
+    distinct valid position, the padding rows are 0, each block holds
+    min(8, H - 8 ht) * min(8, W - 8 wt) tokens (the sibling page's variable block sizes),
+    and the inverse restores the grid."""
+    rng = np.random.default_rng(71)
+    B, T, H, W, h, D = 2, 3, 20, 12, 2, 4
+    x = rng.standard_normal((B, T, H, W, h, D)).astype(np.float32) + 5.0  # no zeros
+    S = orc.fractal_len(T, H, W)
+    assert S == T * 3 * 2 * 64
+    y = orc.fractal_permute(x)
+    assert y.shape == (B, S, h, D)
+    valid = orc.token_valid(T, H, W)
+    assert valid.sum() == T * H * W
+    assert np.all(y[:, ~valid] == 0) and np.all(y[:, valid] != 0)
+    pos = np.array([[[orc.fractal_index(t, yy, xx, H, W) for xx in range(W)] for yy in range(H)]
+                    for t in range(T)]).ravel()
+    assert len(set(pos.tolist())) == pos.size and np.all(valid[pos])
+    counts = valid.reshape(-1, 64).sum(1)
+    for i, c in enumerate(counts):
+        ht, wt = (i // 2) % 3, i % 2
+        assert c == min(8, H - 8 * ht) * min(8, W - 8 * wt)
+    assert np.array_equal(orc.fractal_permute(y, inverse=True, grid=(T, H, W)), x)
+
+
+def test_pool_grid_excludes_padding(orc):
+    """A constant field gives that constant in every block, partial ones included (padding
+    is not averaged in); general input matches the fp64 mean over tokens within the fp32
+    bound; on a grid of whole patches it equals orc_pool bit for bit."""
+    rng = np.random.default_rng(72)
+    B, T, H, W, h, D = 1, 2, 13, 19, 2, 8
+    c = np.full((B, T, H, W, h, D), 0.375, np.float32)
+    assert np.all(orc.pool_grid(orc.fractal_permute(c), (T, H, W)) == np.float32(0.375))
+    x = rng.standard_normal((B, T, H, W, h, D)).astype(np.float32)
+    xf = orc.fractal_permute(x)
+    got = orc.pool_grid(xf, (T, H, W))
+    valid = orc.token_valid(T, H, W).reshape(-1, 64)
+    xb = xf.astype(np.float64).reshape(B, -1, 64, h, D)
+    want = (xb * valid[None, :, :, None, None]).sum(2) / valid.sum(1)[None, :, None, None]
+    assert np.max(np.abs(got - want.transpose(0, 2, 1, 3))) < 64 * 2.0 ** -23 * np.abs(x).max()
+    x16 = rng.standard_normal((1, 2, 16, 24, 2, 8)).astype(np.float32)
+    f16 = orc.fractal_permute(x16)
+    assert np.array_equal(orc.pool_grid(f16, (2, 16, 24)), orc.pool(f16))
+
+
+def test_attention_grid_equals_natural_order_sdpa(orc):
+    """On a padded grid, the attention over the fractal layout equals torch SDPA (fp64) over
+    the natural token sequence with the block mask mapped to tokens: padding is never a key."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(73)
+    B, T, H, W, h, D = 1, 2, 12, 20, 2, 16
+    nat = [rng.standard_normal((B, T, H, W, h, D)).astype(np.float32) for _ in range(3)]
+    q, k, v = (orc.fractal_permute(a) for a in nat)
+    S = q.shape[1]
+    nb = S // 64
+    kv_nb, kv_inds = _random_lists(rng, B, h, nb)
+    ids, o = orc.attention_grid(q, k, v, (T, H, W), kv_nb, kv_inds)
+    got = orc.rows_to_tokens(o, ids, B, S, h, D)
+    pos = np.array([[[orc.fractal_index(t, yy, xx, H, W) for xx in range(W)] for yy in range(H)]
+                    for t in range(T)]).ravel()  # natural token -> fractal position
+    blk = pos // 64
+    for hh in range(h):
+        allowed = np.zeros((nb, nb), bool)
+        for i in range(nb):
+            allowed[i, kv_inds[0, hh, i, :kv_nb[0, hh, i]]] = True
+        m = torch.from_numpy(allowed[blk][:, blk])  # [N, N] natural tokens
+        Q, K, V = (torch.from_numpy(a[0, :, :, :, hh].reshape(-1, D)).double() for a in nat)
+        ref = torch.nn.functional.scaled_dot_product_attention(Q[None], K[None], V[None],
+                                                               attn_mask=m[None]).numpy()[0]
+        assert np.max(np.abs(got[0, pos, hh] - ref)) < 1e-12
+
+
+def test_block_mask_grid_consistency(orc):
+    """Both estimators on a grid of whole patches equal the plain ones; on a padded grid with a
+    constant k every score of a row is equal, so the CDF estimator keeps the blocks its tie
+    rule keeps (the highest indices) and top-k the k highest indices."""
+    rng = np.random.default_rng(74)
+    B, T, H, W, h, D = 1, 2, 16, 16, 2, 64
+    q, k = (orc.fractal_permute(rng.standard_normal((B, T, H, W, h, D)).astype(np.float32))
+            for _ in range(2))
+    a = orc.block_mask(q, k, None, 0.7)
+    b = orc.block_mask_grid(q, k, (T, H, W), None, 0.7)
+    assert np.array_equal(a["kv_nb"], b["kv_nb"]) and np.array_equal(a["kv_inds"], b["kv_inds"])
+    a = orc.block_mask_topk(q, k, None, 0.5)
+    b = orc.block_mask_grid(q, k, (T, H, W), None, 0.0, topk_ratio=0.5)
+    assert np.array_equal(a["kv_nb"], b["kv_nb"]) and np.array_equal(a["kv_inds"], b["kv_inds"])
+    T, H, W = 2, 11, 21
+    qn = rng.standard_normal((B, T, H, W, h, D)).astype(np.float32)
+    kc = np.full((B, T, H, W, h, D), 0.5, np.float32)
+    q, k = orc.fractal_permute(qn), orc.fractal_permute(kc)
+    nb = q.shape[1] // 64
+    r = orc.block_mask_grid(q, k, (T, H, W), None, 0.0, topk_ratio=0.34)
+    kk = orc.topk_count(nb, 0.34)
+    assert np.all(r["kv_nb"] == kk) and np.all(r["kv_inds"][..., :kk] == np.arange(nb - kk, nb))
+    r = orc.block_mask_grid(q, k, (T, H, W), None, 0.5)
+    n = int(r["kv_nb"].flat[0])
+    assert np.all(r["kv_nb"] == n) and nb // 2 <= n <= nb // 2 + 1
+    assert np.all(r["kv_inds"][..., :n] == np.arange(nb - n, nb))
