@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="720p", help="tiny | small | 720p | long")
+    ap.add_argument("--workload", default="720p", help="tiny | small | 720p | long | small_pad | 720p_pad")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
                     help="query blocks in the oracle attention sample")
@@ -173,16 +173,25 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None):
             check(L.nabla_fractal_permute(P(src), P(dst), dt_code, B, w.T, w.H, w.W, H, D, 0, sp),
                   "permute")
         if e: e[1].record(stream)
-        if topk_ratio is None:
+        if w.padded:  # partial patches: the grid entry points
+            check(L.nabla_block_mask_grid(P(qf), P(kf), dt_code, B, w.T, w.H, w.W, H, D, sta_p,
+                                          w.thr, -1.0 if topk_ratio is None else topk_ratio,
+                                          P(kv_nb), P(kv_inds), P(ws), ws.numel(), sp), "mask")
+        elif topk_ratio is None:
             check(L.nabla_block_mask(P(qf), P(kf), dt_code, B, S, H, D, sta_p, w.thr, P(kv_nb),
                                      P(kv_inds), P(ws), ws.numel(), sp), "mask")
         else:
             check(L.nabla_block_mask_topk(P(qf), P(kf), dt_code, B, S, H, D, sta_p, topk_ratio,
                                           P(kv_nb), P(kv_inds), P(ws), ws.numel(), sp), "mask")
         if e: e[2].record(stream)
-        check(L.nabla_sparse_attn_fwd(P(qf), P(kf), P(vf), dt_code, B, S, H, D, P(kv_nb),
-                                      P(kv_inds), 0.0, *w.tiles, P(of), P(ws_attn),
-                                      ws_attn.numel(), sp), "attn")
+        if w.padded:
+            check(L.nabla_sparse_attn_fwd_grid(P(qf), P(kf), P(vf), dt_code, B, w.T, w.H, w.W, H,
+                                               D, P(kv_nb), P(kv_inds), 0.0, P(of), None,
+                                               P(ws_attn), ws_attn.numel(), sp), "attn")
+        else:
+            check(L.nabla_sparse_attn_fwd(P(qf), P(kf), P(vf), dt_code, B, S, H, D, P(kv_nb),
+                                          P(kv_inds), 0.0, *w.tiles, P(of), P(ws_attn),
+                                          ws_attn.numel(), sp), "attn")
         if e: e[3].record(stream)
         check(L.nabla_fractal_permute(P(of), P(o_nat), dt_code, B, w.T, w.H, w.W, H, D, 1, sp),
               "unpermute")
@@ -379,7 +388,7 @@ def main():
                      "kernel": "sparse_attn_kernel<128, bf16>",
                      "per_launch": {"flops": m["attn_flops"], "kept_pairs": m["pairs"]}},
     }
-    if not args.no_cpu_baseline and args.topk is None:
+    if not args.no_cpu_baseline and args.topk is None and not w.padded:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, m["sta_np"], m["g_nb"], args.cpu_rows,
                                            m["flops_per_pair"])

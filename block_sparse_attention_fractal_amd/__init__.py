@@ -19,7 +19,8 @@ import torch
 
 __all__ = ["nabla_fractal_permute", "nabla_sta_mask", "nabla_block_mask",
            "nabla_block_mask_workspace", "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace",
-           "nabla_sparse_attn_bwd", "nabla_sparse_attn_bwd_workspace", "NablaError", "lib",
+           "nabla_sparse_attn_bwd", "nabla_sparse_attn_bwd_workspace", "fractal_len",
+           "NablaError", "lib",
            "LIB_PATH", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnabla.so")
@@ -61,6 +62,12 @@ def lib():
     L.nabla_block_mask.restype = I
     L.nabla_block_mask_topk.argtypes = [P, P, I, I, I, I, I, P, D, P, P, P, Z, P]
     L.nabla_block_mask_topk.restype = I
+    L.nabla_block_mask_grid.argtypes = [P, P, I, I, I, I, I, I, I, P, D, D, P, P, P, Z, P]
+    L.nabla_block_mask_grid.restype = I
+    L.nabla_sparse_attn_workspace_grid.argtypes = [I, I, I, I, I]
+    L.nabla_sparse_attn_workspace_grid.restype = Z
+    L.nabla_sparse_attn_fwd_grid.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, F, P, P, P, Z, P]
+    L.nabla_sparse_attn_fwd_grid.restype = I
     L.nabla_sparse_attn_workspace.argtypes = [I, I, I, I, I, I]
     L.nabla_sparse_attn_workspace.restype = Z
     L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P, Z, P]
@@ -105,20 +112,26 @@ def _p(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def fractal_len(T, H, W):
+    """Tokens of the fractal layout of a T x H x W grid: T * ceil(H/8) * ceil(W/8) * 64."""
+    return T * ((H + 7) // 8) * ((W + 7) // 8) * BLOCK
+
+
 def nabla_fractal_permute(x, grid=None, inverse=False, out=None):
     """Fractal token order (8 x 8 patches -> runs of 64 tokens).
 
-    Forward: x [B, T, H, W, heads, D] -> [B, T*H*W, heads, D].
+    Forward: x [B, T, H, W, heads, D] -> [B, fractal_len(T, H, W), heads, D]; when 8 does
+    not divide H or W the partial patches are padded with zeros.
     Inverse: x [B, S, heads, D] with grid=(T, H, W) -> [B, T, H, W, heads, D].
     """
     _dev(x, "x")
     if not inverse:
         B, T, H, W, heads, D = x.shape
-        shape = (B, T * H * W, heads, D)
+        shape = (B, fractal_len(T, H, W), heads, D)
     else:
         B, S, heads, D = x.shape
         T, H, W = grid
-        if T * H * W != S:
+        if fractal_len(T, H, W) != S:
             raise ValueError("grid %s does not match S=%d" % (grid, S))
         shape = (B, T, H, W, heads, D)
     y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else _dev(out, "out")
@@ -140,13 +153,15 @@ def nabla_block_mask_workspace(B, S, heads, D):
     return lib().nabla_block_mask_workspace(B, S, heads, D)
 
 
-def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None, topk_ratio=None):
+def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None, topk_ratio=None,
+                     grid=None):
     """NABLA estimator: q, k [B, S, heads, D] -> (kv_nb [B,heads,nb] int32, kv_inds [B,heads,nb,nb] int32).
 
     The first kv_nb entries of each kv_inds row are the kept blocks, ascending.
     With topk_ratio set, the top-k variant runs instead (nabla_block_mask_topk:
     smooth-k pooled scores, the int(topk_ratio * nb) largest per row); thr is then
-    not used.
+    not used.  grid=(T, H, W): q, k are the padded fractal layout of that latent grid
+    (nabla_block_mask_grid: blocks average their tokens only).
     """
     _dev(q, "q")
     _dev(k, "k")
@@ -166,6 +181,16 @@ def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None, topk_rat
         kv_inds = torch.empty((B, heads, nb, nb), dtype=torch.int32, device=q.device)
     else:
         kv_nb, kv_inds = out
+    if grid is not None:
+        T, H, W = grid
+        if fractal_len(T, H, W) != S:
+            raise ValueError("grid %s does not match S=%d" % (grid, S))
+        _check(lib().nabla_block_mask_grid(_p(q), _p(k), _dtype_code(q), B, T, H, W, heads, D,
+                                           _p(sta), float(thr),
+                                           -1.0 if topk_ratio is None else float(topk_ratio),
+                                           _p(kv_nb), _p(kv_inds), _p(ws), ws.numel(),
+                                           _stream(q)), "nabla_block_mask_grid")
+        return kv_nb, kv_inds
     if topk_ratio is not None:
         _check(lib().nabla_block_mask_topk(_p(q), _p(k), _dtype_code(q), B, S, heads, D, _p(sta),
                                            float(topk_ratio), _p(kv_nb), _p(kv_inds), _p(ws),
@@ -184,14 +209,16 @@ def nabla_sparse_attn_workspace(B, S, heads, tiles=None):
 
 
 def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, tiles=None,
-                          workspace=None, out=None, lse=None):
+                          workspace=None, out=None, lse=None, grid=None):
     """Block-sparse attention over the listed 64 x 64 blocks: o [B, S, heads, D] (q's dtype).
 
     tiles: the (Tt, Ht, Wt) tile grid of the blocks (lets neighbouring query
     blocks share K/V tiles on chip); None if unknown.  workspace: a uint8 GPU
     tensor of at least nabla_sparse_attn_workspace() bytes (allocated if None).
     lse: None, or a float32 GPU tensor [B, heads, S] that receives each row's
-    log-sum-exp (natural log), as the backward needs it.
+    log-sum-exp (natural log), as the backward needs it.  grid=(T, H, W): q, k, v are
+    the padded fractal layout of that latent grid (nabla_sparse_attn_fwd_grid: padding
+    is never a key; tiles is then implied).
     """
     if causal:
         raise ValueError("NABLA attention does not support causal masking")
@@ -206,6 +233,11 @@ def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, til
     if kv_nb.numel() != B * heads * nb or kv_inds.numel() != B * heads * nb * nb:
         raise ValueError("kv lists do not match q's shape")
     o = torch.empty_like(q) if out is None else _dev(out, "out")
+    if grid is not None:
+        T, H, W = grid
+        if fractal_len(T, H, W) != S:
+            raise ValueError("grid %s does not match S=%d" % (grid, S))
+        tiles = (T, (H + 7) // 8, (W + 7) // 8)
     Tt, Ht, Wt = (0, 0, 0) if tiles is None else tiles
     if workspace is None:
         need = lib().nabla_sparse_attn_workspace(B, S, heads, Tt, Ht, Wt)
@@ -216,6 +248,14 @@ def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, til
         _dev(lse, "lse")
         if lse.dtype != torch.float32 or lse.numel() != B * heads * S:
             raise ValueError("lse must be float32 with B * heads * S elements")
+    if grid is not None:
+        _check(lib().nabla_sparse_attn_fwd_grid(_p(q), _p(k), _p(v), _dtype_code(q), B, *grid,
+                                                heads, D, _p(kv_nb), _p(kv_inds),
+                                                0.0 if scale is None else float(scale), _p(o),
+                                                None if lse is None else _p(lse), _p(workspace),
+                                                workspace.numel(), _stream(q)),
+               "nabla_sparse_attn_fwd_grid")
+        return o
     _check(lib().nabla_sparse_attn_fwd_lse(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads, D,
                                            _p(kv_nb), _p(kv_inds),
                                            0.0 if scale is None else float(scale), Tt, Ht, Wt,

@@ -41,17 +41,29 @@ namespace nabla {
 // grid (nb, B): block i of q is pooled into qa [B*heads][nb][D] and block i of k into
 // ka [B*heads][D/4][nb][4].  One workgroup does both, so that the whole grid is resident
 // at once (no partial second round of workgroups).
+// H, W > 0: the latent grid of a padded fractal layout (Wt = ceil(W/8) patches per row
+// of patches): a block averages its tokens only, summed in order and divided by their
+// count min(8, H - 8 ht) * min(8, W - 8 wt).  H = W = 0: whole 64-token blocks.
 template <typename Tin>
 __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
                                                    const Tin *__restrict__ k,
                                                    float *__restrict__ qa,
                                                    float *__restrict__ ka, int S, int heads,
-                                                   int D) {
+                                                   int D, int H, int W) {
     constexpr int EPC = 16 / sizeof(Tin);  // elements per 16-byte chunk
     const int nb = S / kBlock;
     const int i = blockIdx.x, b = blockIdx.y;
     const int row_elems = heads * D;
     const int nchunks = row_elems / EPC;
+    int vrows = kTile, vcols = kTile;
+    if (H > 0) {
+        const int Ht = (H + kTile - 1) / kTile, Wt = (W + kTile - 1) / kTile;
+        const int th = (i / Wt) % Ht, tw = i % Wt;
+        vrows = min(kTile, H - th * kTile);
+        vcols = min(kTile, W - tw * kTile);
+    }
+    const bool whole = vrows == kTile && vcols == kTile;
+    const int cnt = vrows * vcols;
     for (int item = threadIdx.x; item < 2 * nchunks; item += 256) {
     const int z = item >= nchunks;  // 0: q, 1: k
     const int ch = item - z * nchunks;
@@ -71,6 +83,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
                 raw[u] = *reinterpret_cast<const uint4 *>(p + (int64_t)(r0 + u) * row_elems);
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
+                const int r = r0 + u;
+                if (!whole && !((r >> 3) < vrows && (r & 7) < vcols)) continue;  // padding
                 if constexpr (sizeof(Tin) == 2) {
                     const uint32_t wd[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
@@ -95,9 +109,12 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
             // reads the k means of consecutive blocks from consecutive addresses
             float *out = z ? xa + ((bhh * (D / 4) + (d + e) / 4) * nb + i) * 4
                            : xa + (bhh * nb + i) * D + d + e;
-            *reinterpret_cast<float4 *>(out) =
-                make_float4(acc[e] * 0.015625f, acc[e + 1] * 0.015625f, acc[e + 2] * 0.015625f,
-                            acc[e + 3] * 0.015625f);
+            // mean: * 2^-6 on whole blocks (exact, equal to / 64), else / token count
+            float m[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                m[u] = whole ? acc[e + u] * 0.015625f : acc[e + u] / (float)cnt;
+            *reinterpret_cast<float4 *>(out) = make_float4(m[0], m[1], m[2], m[3]);
         }
     }
     }
@@ -770,16 +787,17 @@ static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int 
 }
 
 hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, int B, int S,
-                                  int heads, int D, const uint8_t *sta, int topk, int32_t *kv_nb,
-                                  int32_t *kv_inds, float *qa, float *ka, hipStream_t stream) {
+                                  int heads, int D, int H, int W, const uint8_t *sta, int topk,
+                                  int32_t *kv_nb, int32_t *kv_inds, float *qa, float *ka,
+                                  hipStream_t stream) {
     const int nb = S / kBlock;
     dim3 pgrid(nb, B);
     if (bf16_in)
         hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, qa, ka, S, heads, D);
+                           (const bf16 *)k, qa, ka, S, heads, D, H, W);
     else
         hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
-                           (const float *)k, qa, ka, S, heads, D);
+                           (const float *)k, qa, ka, S, heads, D, H, W);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int BH = B * heads;
@@ -794,17 +812,17 @@ hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, in
 }
 
 hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, int S,
-                             int heads, int D, const uint8_t *sta, int64_t cut_fixed,
-                             float sqrt_d, int32_t *kv_nb, int32_t *kv_inds, float *qa,
-                             float *ka, hipStream_t stream) {
+                             int heads, int D, int H, int W, const uint8_t *sta,
+                             int64_t cut_fixed, float sqrt_d, int32_t *kv_nb, int32_t *kv_inds,
+                             float *qa, float *ka, hipStream_t stream) {
     const int nb = S / kBlock;
     dim3 pgrid(nb, B);
     if (bf16_in)
         hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, qa, ka, S, heads, D);
+                           (const bf16 *)k, qa, ka, S, heads, D, H, W);
     else
         hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
-                           (const float *)k, qa, ka, S, heads, D);
+                           (const float *)k, qa, ka, S, heads, D, H, W);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int BH = B * heads;

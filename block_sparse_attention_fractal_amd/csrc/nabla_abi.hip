@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
 constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
@@ -26,6 +26,9 @@ bool sizes_ok(int B, int S, int heads, int head_dim) {
     const long long rows = (long long)B * heads * (S / kBlock);
     return rows <= 0x7fffffffLL;
 }
+
+// Patches along an axis of n latent positions (the last one partial when 8 does not divide n).
+long long tiles(int n) { return ((long long)n + kTile - 1) / kTile; }
 
 // A tile grid is either all zero (unknown) or positive and multiplies to S/64.
 bool grid_ok(int S, int Tt, int Ht, int Wt) {
@@ -56,11 +59,10 @@ nabla_status nabla_fractal_permute(const void *x, void *y, nabla_dtype dtype, in
     if (!x || !y || !dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
     if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || head_dim < 1)
         return NABLA_ERR_INVALID_ARG;
-    if (H % kTile || W % kTile) return NABLA_ERR_INVALID_ARG;
     const long long row_bytes = (long long)heads * head_dim * (long long)dtype_bytes(dtype);
     if (row_bytes % 16) return NABLA_ERR_UNSUPPORTED;
     if (row_bytes / 16 > 0x7fffffffLL / kBlock) return NABLA_ERR_UNSUPPORTED;
-    const long long nb = (long long)T * (H / kTile) * (W / kTile);
+    const long long nb = (long long)T * tiles(H) * tiles(W);
     if ((long long)B * nb > 0x7fffffffLL) return NABLA_ERR_UNSUPPORTED;
     return from_hip(nabla::launch_fractal_permute(x, y, (int)dtype_bytes(dtype), B, T, H, W,
                                                   heads * head_dim, inverse != 0,
@@ -82,49 +84,83 @@ size_t nabla_block_mask_workspace(int B, int S, int heads, int head_dim) {
     return 2ull * (size_t)B * heads * (size_t)(S / kBlock) * head_dim * sizeof(float);
 }
 
-nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, int B, int S,
-                              int heads, int head_dim, const uint8_t *sta, double thr,
-                              int32_t *kv_nb, int32_t *kv_inds, void *ws, size_t ws_bytes,
-                              void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Both estimators; ratio < 0 selects the CDF cut (thr), ratio >= 0 the top-k variant.
+// H, W > 0: the latent grid of a padded fractal layout (pooling over tokens only).
+nabla_status estimate(const void *q, const void *k, nabla_dtype dtype, int B, int S, int heads,
+                      int head_dim, int H, int W, const uint8_t *sta, double thr, double ratio,
+                      int32_t *kv_nb, int32_t *kv_inds, void *ws, size_t ws_bytes,
+                      void *stream) {
     if (!q || !k || !kv_nb || !kv_inds || !dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
     if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
-    if (!(thr >= 0.0 && thr <= 1.0)) return NABLA_ERR_INVALID_ARG;  // also rejects NaN
+    const bool topk = ratio >= 0.0;
+    if (!topk && !(thr >= 0.0 && thr <= 1.0)) return NABLA_ERR_INVALID_ARG;  // also NaN
+    if (topk && !(ratio <= 1.0)) return NABLA_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
     const int nb = S / kBlock;
-    if (nb > kMaxBlocks) return NABLA_ERR_UNSUPPORTED;
+    if (nb > (topk ? kMaxTopkBlocks : kMaxBlocks)) return NABLA_ERR_UNSUPPORTED;
     const size_t need = nabla_block_mask_workspace(B, S, heads, head_dim);
     if (!ws || ws_bytes < need) return NABLA_ERR_WORKSPACE;
+    float *qa = static_cast<float *>(ws);
+    float *ka = qa + (size_t)B * heads * nb * head_dim;
+    if (topk) {
+        // k = min(nb, int(ratio * nb)): the product in double, truncated
+        const double x = ratio * (double)nb;
+        const int kk = x >= (double)nb ? nb : (int)x;
+        return from_hip(nabla::launch_block_mask_topk(q, k, dtype == NABLA_BF16, B, S, heads,
+                                                      head_dim, H, W, sta, kk, kv_nb, kv_inds,
+                                                      qa, ka, as_stream(stream)));
+    }
     // cut on the 2^-48 grid: ceil(fl32(1 - thr) * 2^48), exact in double
     const float cut32 = (float)(1.0 - thr);
     const int64_t cut_fixed = (int64_t)ceil(ldexp((double)cut32, 48));
     const float sqrt_d = (float)sqrt((double)head_dim);
-    float *qa = static_cast<float *>(ws);
-    float *ka = qa + (size_t)B * heads * nb * head_dim;
     return from_hip(nabla::launch_block_mask(q, k, dtype == NABLA_BF16, B, S, heads, head_dim,
-                                             sta, cut_fixed, sqrt_d, kv_nb, kv_inds, qa, ka,
-                                             as_stream(stream)));
+                                             H, W, sta, cut_fixed, sqrt_d, kv_nb, kv_inds, qa,
+                                             ka, as_stream(stream)));
+}
+
+// S of the padded fractal layout of a T x H x W grid, or -1 when the sizes are invalid.
+long long grid_len(int B, int T, int H, int W, int heads, int head_dim) {
+    if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || head_dim < 1) return -1;
+    const long long S = (long long)T * tiles(H) * tiles(W) * kBlock;
+    if (S > 0x7fffffffLL || !sizes_ok(B, (int)S, heads, head_dim)) return -1;
+    return S;
+}
+
+}  // namespace
+
+extern "C" {
+
+nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, int B, int S,
+                              int heads, int head_dim, const uint8_t *sta, double thr,
+                              int32_t *kv_nb, int32_t *kv_inds, void *ws, size_t ws_bytes,
+                              void *stream) {
+    return estimate(q, k, dtype, B, S, heads, head_dim, 0, 0, sta, thr, -1.0, kv_nb, kv_inds, ws,
+                    ws_bytes, stream);
 }
 
 nabla_status nabla_block_mask_topk(const void *q, const void *k, nabla_dtype dtype, int B,
                                    int S, int heads, int head_dim, const uint8_t *sta,
                                    double topk_ratio, int32_t *kv_nb, int32_t *kv_inds, void *ws,
                                    size_t ws_bytes, void *stream) {
-    if (!q || !k || !kv_nb || !kv_inds || !dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
-    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
     if (!(topk_ratio >= 0.0 && topk_ratio <= 1.0)) return NABLA_ERR_INVALID_ARG;  // also NaN
-    if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
-    const int nb = S / kBlock;
-    if (nb > kMaxTopkBlocks) return NABLA_ERR_UNSUPPORTED;
-    const size_t need = nabla_block_mask_workspace(B, S, heads, head_dim);
-    if (!ws || ws_bytes < need) return NABLA_ERR_WORKSPACE;
-    // k = min(nb, int(ratio * nb)): the product in double, truncated
-    const double x = topk_ratio * (double)nb;
-    const int topk = x >= (double)nb ? nb : (int)x;
-    float *qa = static_cast<float *>(ws);
-    float *ka = qa + (size_t)B * heads * nb * head_dim;
-    return from_hip(nabla::launch_block_mask_topk(q, k, dtype == NABLA_BF16, B, S, heads,
-                                                  head_dim, sta, topk, kv_nb, kv_inds, qa, ka,
-                                                  as_stream(stream)));
+    return estimate(q, k, dtype, B, S, heads, head_dim, 0, 0, sta, 0.0, topk_ratio, kv_nb,
+                    kv_inds, ws, ws_bytes, stream);
+}
+
+nabla_status nabla_block_mask_grid(const void *q, const void *k, nabla_dtype dtype, int B,
+                                   int T, int H, int W, int heads, int head_dim,
+                                   const uint8_t *sta, double thr, double topk_ratio,
+                                   int32_t *kv_nb, int32_t *kv_inds, void *ws, size_t ws_bytes,
+                                   void *stream) {
+    const long long S = grid_len(B, T, H, W, heads, head_dim);
+    if (S < 0 || topk_ratio != topk_ratio) return NABLA_ERR_INVALID_ARG;
+    return estimate(q, k, dtype, B, (int)S, heads, head_dim, H, W, sta, thr,
+                    topk_ratio < 0.0 ? -1.0 : topk_ratio, kv_nb, kv_inds, ws, ws_bytes, stream);
 }
 
 size_t nabla_sparse_attn_workspace(int B, int S, int heads, int Tt, int Ht, int Wt) {
@@ -141,11 +177,14 @@ nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
                                      scale, Tt, Ht, Wt, o, nullptr, ws, ws_bytes, stream);
 }
 
-nabla_status nabla_sparse_attn_fwd_lse(const void *q, const void *k, const void *v,
-                                       nabla_dtype dtype, int B, int S, int heads, int head_dim,
-                                       const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                                       int Tt, int Ht, int Wt, void *o, float *lse, void *ws,
-                                       size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+nabla_status attn_fwd(const void *q, const void *k, const void *v, nabla_dtype dtype, int B,
+                      int S, int heads, int head_dim, const int32_t *kv_nb,
+                      const int32_t *kv_inds, float scale, int Tt, int Ht, int Wt, int H, int W,
+                      void *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
     if (!q || !k || !v || !kv_nb || !kv_inds || !o || !dtype_ok(dtype))
         return NABLA_ERR_INVALID_ARG;
     if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
@@ -157,8 +196,38 @@ nabla_status nabla_sparse_attn_fwd_lse(const void *q, const void *k, const void 
         return NABLA_ERR_WORKSPACE;
     if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
     return from_hip(nabla::launch_sparse_attn(q, k, v, dtype == NABLA_BF16, B, S, heads,
-                                              head_dim, Tt, Ht, Wt, kv_nb, kv_inds, scale, o,
-                                              lse, ws, as_stream(stream)));
+                                              head_dim, Tt, Ht, Wt, H, W, kv_nb, kv_inds, scale,
+                                              o, lse, ws, as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+nabla_status nabla_sparse_attn_fwd_lse(const void *q, const void *k, const void *v,
+                                       nabla_dtype dtype, int B, int S, int heads, int head_dim,
+                                       const int32_t *kv_nb, const int32_t *kv_inds, float scale,
+                                       int Tt, int Ht, int Wt, void *o, float *lse, void *ws,
+                                       size_t ws_bytes, void *stream) {
+    return attn_fwd(q, k, v, dtype, B, S, heads, head_dim, kv_nb, kv_inds, scale, Tt, Ht, Wt, 0,
+                    0, o, lse, ws, ws_bytes, stream);
+}
+
+size_t nabla_sparse_attn_workspace_grid(int B, int T, int H, int W, int heads) {
+    const long long S = grid_len(B, T, H, W, heads, 1);
+    if (S < 0) return 0;
+    return nabla_sparse_attn_workspace(B, (int)S, heads, T, (int)tiles(H), (int)tiles(W));
+}
+
+nabla_status nabla_sparse_attn_fwd_grid(const void *q, const void *k, const void *v,
+                                        nabla_dtype dtype, int B, int T, int H, int W, int heads,
+                                        int head_dim, const int32_t *kv_nb,
+                                        const int32_t *kv_inds, float scale, void *o, float *lse,
+                                        void *ws, size_t ws_bytes, void *stream) {
+    const long long S = grid_len(B, T, H, W, heads, head_dim);
+    if (S < 0) return NABLA_ERR_INVALID_ARG;
+    return attn_fwd(q, k, v, dtype, B, (int)S, heads, head_dim, kv_nb, kv_inds, scale, T,
+                    (int)tiles(H), (int)tiles(W), H, W, o, lse, ws, ws_bytes, stream);
 }
 
 size_t nabla_sparse_attn_bwd_workspace(int B, int S, int heads) {

@@ -15,26 +15,30 @@ hipError_t launch_sta_mask(uint8_t *sta, int Tt, int Ht, int Wt, int win_t, int 
                            int win_w, hipStream_t stream);
 
 // Pooled blocks [B*heads][nb][D] fp32 of q (qa) and k (ka), then per-row
-// selection; cut_fixed = ceil(fl32(1 - thr) * 2^48).
+// selection; cut_fixed = ceil(fl32(1 - thr) * 2^48).  H, W > 0: the latent grid of a
+// padded fractal layout (blocks average their tokens only); 0: whole 64-token blocks.
 hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, int S,
-                             int heads, int D, const uint8_t *sta, int64_t cut_fixed,
-                             float sqrt_d, int32_t *kv_nb, int32_t *kv_inds, float *qa,
-                             float *ka, hipStream_t stream);
+                             int heads, int D, int H, int W, const uint8_t *sta,
+                             int64_t cut_fixed, float sqrt_d, int32_t *kv_nb, int32_t *kv_inds,
+                             float *qa, float *ka, hipStream_t stream);
 
 // The top-k variant: pooled blocks, smooth-k, the topk largest scores per row (k <= nb,
-// nb <= 2048), STA union.
+// nb <= 2048), STA union.  H, W as for launch_block_mask.
 hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, int B, int S,
-                                  int heads, int D, const uint8_t *sta, int topk, int32_t *kv_nb,
-                                  int32_t *kv_inds, float *qa, float *ka, hipStream_t stream);
+                                  int heads, int D, int H, int W, const uint8_t *sta, int topk,
+                                  int32_t *kv_nb, int32_t *kv_inds, float *qa, float *ka,
+                                  hipStream_t stream);
 
 // Tt, Ht, Wt: tile grid of the query blocks (Tt*Ht*Wt == S/64), or all 0 if unknown.
 // ws: sparse_attn_workspace_bytes() bytes (schedule: counter, group costs, order).
 size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt);
 // lse: [B*heads][S] fp32 natural-log log-sum-exp of each row's scaled scores, or null.
+// H, W > 0: the latent grid of a padded fractal layout over the tile grid (Tt, Ht, Wt):
+// padding positions of partial patches are never keys.  0: whole blocks.
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
-                              int B, int S, int heads, int D, int Tt, int Ht, int Wt,
-                              const int32_t *kv_nb, const int32_t *kv_inds, float scale, void *o,
-                              float *lse, void *ws, hipStream_t stream);
+                              int B, int S, int heads, int D, int Tt, int Ht, int Wt, int H,
+                              int W, const int32_t *kv_nb, const int32_t *kv_inds, float scale,
+                              void *o, float *lse, void *ws, hipStream_t stream);
 
 // Backward (bf16 tensors): dq, dk, dv from q, k, v, o, dO, lse and the kv lists.
 // ws: sparse_attn_bwd_workspace_bytes() bytes (row deltas, transposed lists).

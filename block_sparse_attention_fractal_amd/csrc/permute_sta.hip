@@ -30,23 +30,41 @@ __device__ __forceinline__ void permute_addr(int id, int row_chunks, int64_t nat
     dst = inverse ? nat : fra;
 }
 
+// H and W need not be multiples of 8: each frame is padded to ceil(H/8) x ceil(W/8)
+// patches (the sibling "video_sparse_attn" page's variable block sizes).  A padding
+// position of a partial patch is written as 0 going to fractal order and is not read
+// going back.  Whole patches take the unchecked path.
 template <bool kFull>
 __global__ __launch_bounds__(256) void fractal_permute_kernel(const uint4 *__restrict__ x,
                                                               uint4 *__restrict__ y,
                                                               int T, int H, int W,
                                                               int row_chunks, int inverse) {
     constexpr int U = 8;
-    const int Ht = H / kTile, Wt = W / kTile;
+    const int Ht = (H + kTile - 1) / kTile, Wt = (W + kTile - 1) / kTile;
     const int nb = T * Ht * Wt;
     const int b = blockIdx.x / nb;
     const int tile = blockIdx.x % nb;
     const int t = tile / (Ht * Wt);
     const int th = (tile / Wt) % Ht;
     const int tw = tile % Wt;
-    const int64_t S = (int64_t)T * H * W;
+    const int64_t S = (int64_t)nb * kBlock;
     const int64_t frac0 = ((int64_t)b * S + (int64_t)tile * kBlock) * row_chunks;
     const int64_t nat_row0 = (((int64_t)b * T + t) * H + th * kTile) * W + tw * kTile;
     const int total = kBlock * row_chunks;
+    const int vrows = H - th * kTile, vcols = W - tw * kTile;  // >= 1; >= 8 on whole patches
+    if (vrows < kTile || vcols < kTile) {  // partial patch (workgroup-uniform)
+        for (int id = threadIdx.x; id < total; id += 256) {
+            const int w = id / row_chunks;
+            const bool tok = (w >> 3) < vrows && (w & 7) < vcols;
+            int64_t s, d;
+            permute_addr(id, row_chunks, nat_row0, W, frac0, inverse, s, d);
+            if (tok)
+                y[d] = x[s];
+            else if (!inverse)
+                y[d] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        return;
+    }
     if constexpr (kFull) {  // total is a multiple of 256 * U
         for (int base = threadIdx.x; base < total; base += 256 * U) {
             uint4 v0, v1, v2, v3, v4, v5, v6, v7;
@@ -76,7 +94,7 @@ __global__ __launch_bounds__(256) void fractal_permute_kernel(const uint4 *__res
 hipError_t launch_fractal_permute(const void *x, void *y, int elem_bytes, int B, int T, int H,
                                   int W, int row_elems, bool inverse, hipStream_t stream) {
     const int row_chunks = row_elems * elem_bytes / 16;
-    const int nb = T * (H / kTile) * (W / kTile);
+    const int nb = T * ((H + kTile - 1) / kTile) * ((W + kTile - 1) / kTile);
     const int64_t grid = (int64_t)B * nb;
     if ((kBlock * row_chunks) % (256 * 8) == 0)
         hipLaunchKernelGGL(fractal_permute_kernel<true>, dim3((unsigned)grid), dim3(256), 0,

@@ -201,10 +201,13 @@ __global__ __launch_bounds__(1024) void attn_plan_order_kernel(const int32_t *__
     for (int i = tid; i < n; i += 1024) out[atomicAdd(&start[clamp_count(c[i], nb)], 1)] = g0 + i;
 }
 
-template <int D, typename Tin>
+// kPad: the layout is a padded grid (Hv x Wv latents, partial patches); padding keys are
+// masked.  The instance without it carries none of that code.
+template <int D, typename Tin, bool kPad>
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
-    Tin *__restrict__ o, int S, int heads, int Tt, int Ht, int Wt, int groups_per_bh,
+    Tin *__restrict__ o, int S, int heads, int Tt, int Ht, int Wt, int Hv, int Wv,
+    int groups_per_bh,
     int ngroups, const int32_t *__restrict__ kv_nb, const int32_t *__restrict__ kv_inds,
     float scale_log2, const int32_t *__restrict__ order, int32_t *__restrict__ counter,
     float *__restrict__ lse) {
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
 
     // scores and softmax of the tile in `stage` -> packed weights pb (and O, l rescaled
     // when the reference max moves)
-    auto score_softmax = [&](int stage, bf16x8 (&pb)[2][2]) {
+    auto score_softmax = [&](int stage, bf16x8 (&pb)[2][2], int vr, int vc) {
             const char *kb = reinterpret_cast<const char *>(sh.ks[stage]);
             // The LDS reads are issued well ahead of the MFMAs that use them (the
             // sched_barrier fences keep the compiler from sinking them next to their
@@ -442,6 +445,18 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
                 __builtin_amdgcn_sched_barrier(0);
             }
             __builtin_amdgcn_sched_barrier(0);
+            // a partial patch of a padded grid (vr rows x vc columns of tokens): its padding
+            // positions are not keys (register j of half mt holds key 32 mt + 16 (j / 8) +
+            // 8 hi + j % 8)
+            if (kPad && (vr < kTile || vc < kTile)) {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = 32 * mt + 16 * (j >> 3) + 8 * hi + (j & 7);
+                        if (!((key >> 3) < vr && (key & 7) < vc)) sacc[mt][j] = -INFINITY;
+                    }
+            }
             float part = expand(sacc[0], pb[0]) + expand(sacc[1], pb[1]);
             // Lazy reference max.  The weights are formed against the current
             // reference; only when this lane's 32 weights of the tile sum to more
@@ -520,8 +535,15 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
         const bool delayed = w >= 4;
         if (delayed && prev_listed) pv_tile(prev_stage, pb_prev);
         if (mine) {
+            int vr = kTile, vc = kTile;  // token rows / columns of the tile's patch
+            if (kPad) {
+                const int blk = __builtin_amdgcn_readfirstlane((int)sh.ulist[kk]);
+                const int th = (blk / Wt) % Ht, tw = blk % Wt;
+                vr = min(kTile, Hv - th * kTile);
+                vc = min(kTile, Wv - tw * kTile);
+            }
             bf16x8 pb[2][2];
-            score_softmax(stage, pb);
+            score_softmax(stage, pb, vr, vc);
             if (delayed) {
 #pragma unroll
                 for (int x = 0; x < 2; ++x)
@@ -604,9 +626,10 @@ static int resident_workgroups(K kernel) {
     return cache[dev];
 }
 
-template <int D, typename Tin>
+template <int D, typename Tin, bool kPad>
 static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int B, int S,
-                                int heads, int Tt, int Ht, int Wt, const int32_t *kv_nb,
+                                int heads, int Tt, int Ht, int Wt, int Hv, int Wv,
+                                const int32_t *kv_nb,
                                 const int32_t *kv_inds, float scale_log2, void *o, float *lse,
                                 void *ws, hipStream_t stream) {
     const int nb = S / kBlock;
@@ -618,7 +641,7 @@ static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int
     int32_t *order = reinterpret_cast<int32_t *>(wsb + 256 + round256((size_t)ngroups * 4));
     hipLaunchKernelGGL(attn_plan_cost_kernel, dim3(ngroups), dim3(256), 0, stream, kv_nb, kv_inds,
                        nb, Tt, Ht, Wt, gpb, cost, counter);
-    const auto kernel = sparse_attn_kernel<D, Tin>;
+    const auto kernel = sparse_attn_kernel<D, Tin, kPad>;
     const int resident = resident_workgroups(kernel);
     if (resident <= 0) return hipErrorInvalidDevice;
     // Heads per phase: enough groups that the phase, and above all the last one, keeps
@@ -633,19 +656,23 @@ static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int
                        dim3(1024), 0, stream, cost, ngroups, per_phase, nb, order);
     const int grid = ngroups < resident ? ngroups : resident;
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kAttnThreads), 0, stream, (const Tin *)q,
-                       (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, Tt, Ht, Wt, gpb,
+                       (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, Tt, Ht, Wt, Hv, Wv,
+                       gpb,
                        ngroups, kv_nb, kv_inds, scale_log2, order, counter, lse);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
-                              int B, int S, int heads, int D, int Tt, int Ht, int Wt,
-                              const int32_t *kv_nb, const int32_t *kv_inds, float scale, void *o,
-                              float *lse, void *ws, hipStream_t stream) {
+                              int B, int S, int heads, int D, int Tt, int Ht, int Wt, int H,
+                              int W, const int32_t *kv_nb, const int32_t *kv_inds, float scale,
+                              void *o, float *lse, void *ws, hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
-#define NABLA_ATTN(DD, T)                                                                   \
-    return launch_attn_t<DD, T>(q, k, v, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds, scale_log2, \
-                                o, lse, ws, stream)
+    const bool pad = H > 0 && (H % kTile != 0 || W % kTile != 0);
+#define NABLA_ATTN(DD, T)                                                                      \
+    return pad ? launch_attn_t<DD, T, true>(q, k, v, B, S, heads, Tt, Ht, Wt, H, W, kv_nb,      \
+                                            kv_inds, scale_log2, o, lse, ws, stream)            \
+               : launch_attn_t<DD, T, false>(q, k, v, B, S, heads, Tt, Ht, Wt, 0, 0, kv_nb,     \
+                                             kv_inds, scale_log2, o, lse, ws, stream)
     if (D == 128) {
         if (bf16_in) NABLA_ATTN(128, bf16);
         NABLA_ATTN(128, float);

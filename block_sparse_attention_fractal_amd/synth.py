@@ -47,16 +47,27 @@ class Workload:
     sigma_n: float = 0.5
 
     @property
+    def tiles(self):
+        """(T, ceil(H/8), ceil(W/8)): the patch grid; partial patches when 8 does not divide H, W."""
+        return (self.T, -(-self.H // TILE), -(-self.W // TILE))
+
+    @property
     def S(self):
+        """Length of the fractal layout (padded to whole patches)."""
+        Tt, Ht, Wt = self.tiles
+        return Tt * Ht * Wt * BLOCK
+
+    @property
+    def tokens(self):
         return self.T * self.H * self.W
+
+    @property
+    def padded(self):
+        return self.H % TILE != 0 or self.W % TILE != 0
 
     @property
     def nb(self):
         return self.S // BLOCK
-
-    @property
-    def tiles(self):
-        return (self.T, self.H // TILE, self.W // TILE)
 
     def describe(self):
         sta = "off" if self.sta is None else "|dt|<=%d,|dh|<=%d,|dw|<=%d" % self.sta
@@ -70,6 +81,9 @@ WORKLOADS = {
     "small": Workload("small", 1, 8, 128, 8, 32, 32, "bf16", "smooth", 1, 0.9, (1, 1, 1)),
     "720p": Workload("720p", 1, 16, 128, 16, 48, 80, "bf16", "smooth", 2, 0.9, (2, 1, 1)),
     "long": Workload("long", 1, 16, 128, 31, 48, 80, "bf16", "smooth", 3, 0.9, (2, 1, 1)),
+    # H, W not multiples of 8: the last patch row / column of each frame is partial
+    "small_pad": Workload("small_pad", 1, 4, 128, 4, 20, 28, "bf16", "smooth", 7, 0.9, (1, 1, 1)),
+    "720p_pad": Workload("720p_pad", 1, 16, 128, 16, 44, 76, "bf16", "smooth", 8, 0.9, (2, 1, 1)),
 }
 
 

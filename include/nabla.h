@@ -60,15 +60,20 @@ const char *nabla_status_string(nabla_status s);
  * Methodology, "Token Reordering"; the "nabla" page's forward expects q/k/v
  * "fractal-ordered by the model").
  *
+ * With Ht = ceil(H/8), Wt = ceil(W/8) and S = T * Ht * Wt * 64:
  * inverse == 0: x is [B, T, H, W, heads, head_dim] (natural order), y is
  *   [B, S, heads, head_dim] with token (t, yy, xx) at
- *   s = ((t*(H/8) + yy/8) * (W/8) + xx/8) * 64 + (yy%8)*8 + xx%8:
+ *   s = ((t*Ht + yy/8) * Wt + xx/8) * 64 + (yy%8)*8 + xx%8:
  *   frames stay in time order, 8 x 8 patches in raster order, and the 64
  *   tokens of a patch in raster order; each 64-token block is one patch.
- * inverse != 0: the exact inverse (x fractal, y natural), e.g. for O.
- * x and y must not overlap.  Errors: INVALID_ARG if a pointer is NULL, a size
- * is < 1, or H or W is not a multiple of 8; UNSUPPORTED if
- * heads*head_dim*sizeof(dtype) is not a multiple of 16 bytes.
+ *   When 8 does not divide H or W, the last patch row / column is partial
+ *   (the sibling "video_sparse_attn" page's variable block sizes): its padding
+ *   positions are written as 0 and are not tokens (S > T*H*W).
+ * inverse != 0: the inverse (x fractal [B, S, ...], y natural), e.g. for O;
+ *   padding positions are not read.
+ * x and y must not overlap.  Errors: INVALID_ARG if a pointer is NULL or a
+ * size is < 1; UNSUPPORTED if heads*head_dim*sizeof(dtype) is not a multiple
+ * of 16 bytes.
  */
 nabla_status nabla_fractal_permute(const void *x, void *y, nabla_dtype dtype, int B, int T,
                                    int H, int W, int heads, int head_dim, int inverse,
@@ -149,6 +154,24 @@ nabla_status nabla_block_mask_topk(const void *q, const void *k, nabla_dtype dty
                                    size_t ws_bytes, void *stream);
 
 /*
+ * Either estimator on the fractal layout of a T x H x W latent grid whose H or W need
+ * not be multiples of 8 (S = T * ceil(H/8) * ceil(W/8) * 64, as nabla_fractal_permute
+ * writes it; the sibling "video_sparse_attn" page's variable block sizes): a block's
+ * mean is taken over its tokens only (their sum in fractal order divided by their
+ * count min(8, H - 8 ht) * min(8, W - 8 wt)); everything else is nabla_block_mask
+ * (topk_ratio < 0; thr as there) or nabla_block_mask_topk (topk_ratio in [0, 1]; thr
+ * not used).  On a grid of whole patches the lists equal those of the plain calls.
+ * Workspace: nabla_block_mask_workspace(B, S, heads, head_dim).
+ * Errors: those of the chosen estimator; INVALID_ARG also for T, H or W < 1 or a NaN
+ * topk_ratio.
+ */
+nabla_status nabla_block_mask_grid(const void *q, const void *k, nabla_dtype dtype, int B,
+                                   int T, int H, int W, int heads, int head_dim,
+                                   const uint8_t *sta, double thr, double topk_ratio,
+                                   int32_t *kv_nb, int32_t *kv_inds, void *ws, size_t ws_bytes,
+                                   void *stream);
+
+/*
  * Bytes of workspace nabla_sparse_attn_fwd needs for the same (B, S, heads) and tile
  * grid: 256 + 2 * round_up(4 * ngroups, 256), where ngroups = B * heads *
  * ceil(Tt/2) * Ht * ceil(Wt/2) (tile grid known) or B * heads * ceil(S/256)
@@ -210,6 +233,25 @@ nabla_status nabla_sparse_attn_fwd_lse(const void *q, const void *k, const void 
                                        int Tt, int Ht, int Wt, void *o, float *lse, void *ws,
                                        size_t ws_bytes, void *stream);
 
+/* Bytes of workspace nabla_sparse_attn_fwd_grid needs for a T x H x W grid (the tile grid
+ * is (T, ceil(H/8), ceil(W/8))).  0 if the sizes are invalid. */
+size_t nabla_sparse_attn_workspace_grid(int B, int T, int H, int W, int heads);
+
+/*
+ * The forward (with optional lse) on the fractal layout of a T x H x W latent grid whose
+ * H or W need not be multiples of 8 (S = T * ceil(H/8) * ceil(W/8) * 64; tile grid
+ * (T, ceil(H/8), ceil(W/8))): the padding positions of partial patches are never keys.
+ * Query rows at padding positions are computed as well (their q is 0 as the permute
+ * writes it) and are dropped by the inverse permute.  Everything else is
+ * nabla_sparse_attn_fwd_lse; on a grid of whole patches the result equals it.
+ * Errors: those of nabla_sparse_attn_fwd_lse; INVALID_ARG also for T, H or W < 1.
+ */
+nabla_status nabla_sparse_attn_fwd_grid(const void *q, const void *k, const void *v,
+                                        nabla_dtype dtype, int B, int T, int H, int W, int heads,
+                                        int head_dim, const int32_t *kv_nb,
+                                        const int32_t *kv_inds, float scale, void *o, float *lse,
+                                        void *ws, size_t ws_bytes, void *stream);
+
 /*
  * Bytes of workspace nabla_sparse_attn_bwd needs: round_up(4 B heads S, 256) +
  * round_up(4 B heads nb, 256) + round_up(4 B heads nb^2, 256) + round_up(B heads nb^2,
@@ -226,7 +268,9 @@ size_t nabla_sparse_attn_bwd_workspace(int B, int S, int heads);
  *   dS = P (dP - Delta),   dq = scale dS K,   dk = scale dS^T Q,   dv = P^T dO.
  *
  * q, k, v, o, dout: [B, S, heads, head_dim] bf16, fractal order; o and lse as written
- *           by nabla_sparse_attn_fwd_lse for the same q, k, v, lists and scale.
+ *           by nabla_sparse_attn_fwd_lse for the same q, k, v, lists and scale.  Whole
+ *           64-token blocks only (the padded layouts of nabla_sparse_attn_fwd_grid are
+ *           not handled: their padding positions would count as keys).
  * lse:      [B, heads, S] fp32.
  * kv_nb, kv_inds, scale: as for the forward.
  * dq, dk, dv: out [B, S, heads, head_dim] bf16; must not overlap the inputs or each

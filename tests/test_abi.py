@@ -39,14 +39,16 @@ def test_exports_every_declared_symbol(L):
                           "nabla_sta_mask", "nabla_block_mask_workspace", "nabla_block_mask",
                           "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace",
                           "nabla_sparse_attn_fwd_lse", "nabla_sparse_attn_bwd_workspace",
-                          "nabla_sparse_attn_bwd", "nabla_block_mask_topk"}
+                          "nabla_sparse_attn_bwd", "nabla_block_mask_topk",
+                          "nabla_block_mask_grid", "nabla_sparse_attn_workspace_grid",
+                          "nabla_sparse_attn_fwd_grid"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 4
+    assert L.nabla_abi_version() == 5
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"
@@ -98,6 +100,35 @@ def test_block_mask_topk_validation(L):
     assert call(S=64 * 2049) == UNSUP            # one wave holds a row of up to 2048 blocks
     assert call(ws=None) == WS
     assert call(wsb=L.nabla_block_mask_workspace(1, 8192, 8, 128) - 1) == WS
+
+
+def test_grid_entry_points_validation(L):
+    g = L.nabla_block_mask_grid
+
+    def mask(q=FAKE, T=2, H=44, W=76, thr=0.9, ratio=-1.0, ws=FAKE, wsb=1 << 40):
+        return g(q, FAKE, BF16, 1, T, H, W, 8, 128, None, thr, ratio, FAKE, FAKE, ws, wsb, None)
+
+    assert mask(q=None) == INVALID
+    assert mask(T=0) == INVALID
+    assert mask(H=0) == INVALID
+    assert mask(thr=1.5) == INVALID               # the CDF estimator checks thr
+    assert mask(ratio=1.5) == INVALID             # the top-k variant checks its ratio
+    assert mask(ratio=math.nan) == INVALID
+    S = 2 * 6 * 10 * 64                           # 44 x 76 -> 6 x 10 patches
+    assert mask(wsb=L.nabla_block_mask_workspace(1, S, 8, 128) - 1) == WS
+    f = L.nabla_sparse_attn_fwd_grid
+
+    def fwd(q=FAKE, T=2, H=44, W=76, D=128, o=FAKE, ws=FAKE, wsb=1 << 40):
+        return f(q, FAKE, FAKE, BF16, 1, T, H, W, 8, D, FAKE, FAKE, 0.0, o, None, ws, wsb, None)
+
+    assert fwd(q=None) == INVALID
+    assert fwd(o=None) == INVALID
+    assert fwd(W=-3) == INVALID
+    assert fwd(D=96) == UNSUP
+    need = L.nabla_sparse_attn_workspace_grid(1, 2, 44, 76, 8)
+    assert need == L.nabla_sparse_attn_workspace(1, S, 8, 2, 6, 10) > 0
+    assert fwd(wsb=need - 1) == WS
+    assert L.nabla_sparse_attn_workspace_grid(1, 0, 44, 76, 8) == 0
 
 
 def test_sparse_attn_workspace_size(L):
@@ -178,8 +209,8 @@ def test_sparse_attn_bwd_validation(L):
 def test_permute_and_sta_validation(L):
     p = L.nabla_fractal_permute
     assert p(None, FAKE, BF16, 1, 2, 16, 16, 2, 64, 0, None) == INVALID
-    assert p(FAKE, FAKE, BF16, 1, 2, 12, 16, 2, 64, 0, None) == INVALID   # H % 8
-    assert p(FAKE, FAKE, BF16, 1, 2, 16, 20, 2, 64, 0, None) == INVALID   # W % 8
+    assert p(FAKE, FAKE, BF16, 1, 2, 12, 0, 2, 64, 0, None) == INVALID    # W < 1
+    assert p(FAKE, FAKE, BF16, 0, 2, 12, 20, 2, 64, 0, None) == INVALID   # B < 1
     assert p(FAKE, FAKE, BF16, 1, 0, 16, 16, 2, 64, 0, None) == INVALID
     assert p(FAKE, FAKE, BF16, 1, 2, 16, 16, 1, 2, 0, None) == UNSUP      # 4-byte rows
     s = L.nabla_sta_mask
