@@ -15,6 +15,12 @@ The training pass (attention_lse, attention_dq, attention_bwd) is the gradient o
 that dense masked attention; it is pinned against torch's fp64 autograd and closed
 forms.
 
+The quantized variant (fp8_e4m3, quant_qkv, attention_q8) follows the sibling
+"sla" backend page's SageSLA forward: INT8 Q and K per 64-token block after the
+mean of K is subtracted, FP8 e4m3 V per channel, FP8 P; the encoders are pinned
+against torch's float8_e4m3fn cast and round-trip bounds, the attention against
+closed forms and the plain attention on the dequantized codes.
+
 Parity pins: every function here is checked in ``tests/test_oracle_pins.py``
 against closed forms, brute force, invariants or library routines
 (nothing here is "parity unpinned").
@@ -85,6 +91,15 @@ def _load():
     lib.orc_attention_dq.restype = i32
     lib.orc_attention_bwd.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64, P, P, P, P]
     lib.orc_attention_bwd.restype = i32
+    lib.orc_fp8_e4m3.argtypes = [f64]
+    lib.orc_fp8_e4m3.restype = ctypes.c_uint8
+    lib.orc_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.orc_fp8_e4m3_value.restype = f64
+    lib.orc_fp8_e4m3_vec.argtypes = [P, P, i64]
+    lib.orc_quant_qkv.argtypes = [P, P, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
+    lib.orc_quant_qkv.restype = i32
+    lib.orc_attention_q8.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
+    lib.orc_attention_q8.restype = i32
     _lib = lib
     return lib
 
@@ -423,3 +438,70 @@ def rows_to_tokens(o_rows, row_ids, B, S, heads, D):
         h, i = divmod(rem, nb)
         out[b, i * BLOCK:(i + 1) * BLOCK, h, :] = o_rows[n]
     return out
+
+
+# ---------------------------------------------------------------- O12 quantized variant
+def fp8_e4m3(x):
+    """OCP FP8 e4m3fn codes (uint8) of float64 values, round to nearest even."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty(x.shape, np.uint8)
+    _load().orc_fp8_e4m3_vec(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def fp8_e4m3_value(codes):
+    """float64 values of e4m3fn codes."""
+    lib = _load()
+    table = np.array([lib.orc_fp8_e4m3_value(c) for c in range(256)])
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def quant_qkv(q, k, v):
+    """INT8 q, k per 64-token block (k after subtracting its sequence mean), FP8 e4m3 v per
+    channel.  q, k, v [B,S,heads,D] fp32 values.  Returns dict(q8, qs, k8, ks, v8, vs, km):
+    q8, k8 [B,heads,nb,64,D] int8; qs, ks [B,heads,nb] fp32; v8 [B,heads,nb,D,64] uint8 codes;
+    vs, km [B,heads,D] fp32."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, S, heads, D = q.shape
+    nb = S // BLOCK
+    out = {"q8": np.empty((B, heads, nb, BLOCK, D), np.int8), "qs": np.empty((B, heads, nb), np.float32),
+           "k8": np.empty((B, heads, nb, BLOCK, D), np.int8), "ks": np.empty((B, heads, nb), np.float32),
+           "v8": np.empty((B, heads, nb, D, BLOCK), np.uint8), "vs": np.empty((B, heads, D), np.float32),
+           "km": np.empty((B, heads, D), np.float32)}
+    rc = _load().orc_quant_qkv(_ptr(q), _ptr(k), _ptr(v), B, S, heads, D, _ptr(out["q8"]),
+                               _ptr(out["qs"]), _ptr(out["k8"]), _ptr(out["ks"]), _ptr(out["v8"]),
+                               _ptr(out["vs"]), _ptr(out["km"]))
+    if rc != 0:
+        raise ValueError("oracle quant_qkv: bad argument")
+    return out
+
+
+def attention_q8(qz, kv_nb, kv_inds, row_ids=None, scale=0.0):
+    """The block-sparse attention on quant_qkv()'s codes (FP8 P, fp64 sums).
+    Returns (row_ids, o [len(row_ids), 64, D] fp64) like attention()."""
+    q8 = np.ascontiguousarray(qz["q8"], dtype=np.int8)
+    B, heads, nb, _, D = q8.shape
+    S = nb * BLOCK
+    arrs = [np.ascontiguousarray(qz[n], dtype=t) for n, t in
+            (("qs", np.float32), ("k8", np.int8), ("ks", np.float32), ("v8", np.uint8),
+             ("vs", np.float32))]
+    row_ids = _rows(row_ids, B, heads, nb)
+    kv_nb, kv_inds = _lists(kv_nb, kv_inds)
+    o = np.zeros((row_ids.size, BLOCK, D), np.float64)
+    rc = _load().orc_attention_q8(_ptr(q8), *[_ptr(a) for a in arrs], B, S, heads, D, _ptr(kv_nb),
+                                  _ptr(kv_inds), float(scale), _ptr(row_ids), row_ids.size,
+                                  _ptr(o))
+    if rc != 0:
+        raise ValueError("oracle attention_q8: bad argument")
+    return row_ids, o
+
+
+def dequant_qkv(qz):
+    """The values the codes stand for, as fp64 [B,S,heads,D] arrays (q, k - k_mean, v)."""
+    B, heads, nb, _, D = qz["q8"].shape
+    S = nb * BLOCK
+    q = (qz["q8"].astype(np.float64) * qz["qs"][..., None, None]).reshape(B, heads, S, D)
+    k = (qz["k8"].astype(np.float64) * qz["ks"][..., None, None]).reshape(B, heads, S, D)
+    vv = fp8_e4m3_value(qz["v8"]) * qz["vs"][:, :, None, :, None]      # [B,h,nb,D,64]
+    v = vv.transpose(0, 1, 2, 4, 3).reshape(B, heads, S, D)
+    return tuple(np.ascontiguousarray(x.transpose(0, 2, 1, 3)) for x in (q, k, v))

@@ -817,3 +817,196 @@ int orc_attention_bwd(const float *q, const float *k, const float *v, const floa
     free(delta);
     return bad ? -1 : 0;
 }
+
+/* ------------------------------------------------------------------------- */
+/* O12 the quantized attention variant (the sibling "sla" backend page, the    */
+/* SageSLA forward: Q and K to INT8 with one scale per block after the mean of */
+/* K over the sequence is subtracted, V to FP8 e4m3 with one scale per channel */
+/* (scale maximum 2.25, the value that page passes), then the block-sparse     */
+/* attention on the codes).  Readings (the page shows the calls, not their     */
+/* arithmetic):                                                               */
+/*   - blocks: the 64-token blocks of the kv lists, for q and for k;          */
+/*   - k_mean[d] = (sum over blocks j of bs_j[d]) / S, bs_j[d] the sum of the  */
+/*     block's 64 tokens; both sums sequential in fp32 from +0, then an IEEE   */
+/*     fp32 division by S; k' = k - k_mean (fp32);                            */
+/*   - INT8: scale = amax / 127 (fp32), code = clamp(rint(x / scale), +-127)   */
+/*     with an IEEE fp32 division and round-half-even; amax = 0 gives scale 0  */
+/*     and codes 0;                                                           */
+/*   - FP8 V: scale[d] = amax_d / 2.25 over all S tokens of channel d,        */
+/*     code = e4m3(v / scale) (fp32 division, then round-to-nearest-even to   */
+/*     OCP FP8 e4m3fn: 3 mantissa bits, bias 7, largest finite 448, no        */
+/*     infinities);                                                           */
+/*   - scores z = scale_sm * qs_i * ks_j * <q8, k8> (the integer dot exact);   */
+/*   - P = exp(z - rowmax) is stored as e4m3(448 P) (the FP8 P of that page's  */
+/*     "sv_f8" kernels, full range at P = 1); the row sum is taken over the    */
+/*     same quantized weights, so o is a convex combination of the V codes:   */
+/*     o[d] = vs[d] * sum_c p8_c v8_cd / sum_c p8_c, all in fp64.             */
+/* ------------------------------------------------------------------------- */
+
+/* OCP FP8 e4m3fn encoding of x, round to nearest, ties to the even code;     */
+/* |x| > 448 saturates to 448 (never reached by the method's inputs); NaN     */
+/* gives 0x7f with x's sign.                                                  */
+uint8_t orc_fp8_e4m3(double x) {
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs(x);
+    if (a != a) return sign | 0x7f;
+    if (a >= 448.0) return sign | 0x7e;
+    if (a < 0.015625) { /* below 2^-6: subnormal codes m * 2^-9, m = 0..8 (8 = 2^-6) */
+        double m = rint(a * 512.0); /* exact scaling; rint rounds half to even */
+        return sign | (uint8_t)m;
+    }
+    int e2;
+    double fr = frexp(a, &e2);        /* a = fr * 2^e2, fr in [0.5, 1) */
+    int e = e2 - 1;                   /* a = (2 fr) * 2^e, 2 fr in [1, 2) */
+    double m = rint((2.0 * fr - 1.0) * 8.0); /* 3 mantissa bits, half to even */
+    if (m == 8.0) { m = 0.0; e += 1; }
+    int code = ((e + 7) << 3) | (int)m;
+    if (code > 0x7e) code = 0x7e;
+    return sign | (uint8_t)code;
+}
+
+double orc_fp8_e4m3_value(uint8_t c) {
+    double s = (c & 0x80) ? -1.0 : 1.0;
+    int E = (c >> 3) & 15, m = c & 7;
+    if (E == 15 && m == 7) return NAN;
+    if (E == 0) return s * ldexp((double)m, -9);
+    return s * ldexp(1.0 + m / 8.0, E - 7);
+}
+
+void orc_fp8_e4m3_vec(const double *x, uint8_t *y, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) y[i] = orc_fp8_e4m3(x[i]);
+}
+
+static int8_t orc_int8_code(float x, float scale) {
+    if (scale == 0.0f) return 0;
+    float r = rintf(x / scale);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)r;
+}
+
+/* q8, k8: [B][heads][nb][64][D] int8; qs, ks: [B][heads][nb]; v8: [B][heads][nb][D][64]   */
+/* e4m3 codes (each block transposed); vs, km: [B][heads][D]. */
+int orc_quant_qkv(const float *q, const float *k, const float *v, int B, int S, int heads, int D,
+                  int8_t *q8, float *qs, int8_t *k8, float *ks, uint8_t *v8, float *vs,
+                  float *km) {
+    if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
+    int nb = S / ORC_BLK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)B * heads; ++bh) {
+        int64_t b = bh / heads;
+        int h = (int)(bh % heads);
+        float *kmean = km + bh * D;
+        /* k_mean: block sums, then their sum, then / S */
+        for (int d = 0; d < D; ++d) {
+            float tot = 0.0f;
+            for (int j = 0; j < nb; ++j) {
+                float bs = 0.0f;
+                for (int r = 0; r < ORC_BLK; ++r)
+                    bs += k[((b * S + (int64_t)j * ORC_BLK + r) * heads + h) * D + d];
+                tot += bs;
+            }
+            kmean[d] = tot / (float)S;
+        }
+        /* q and k' = k - k_mean per block */
+        float *xs = (float *)malloc(sizeof(float) * ORC_BLK * D);
+        for (int which = 0; which < 2; ++which) {
+            const float *x = which == 0 ? q : k;
+            int8_t *x8 = which == 0 ? q8 : k8;
+            float *xsc = which == 0 ? qs : ks;
+            for (int j = 0; j < nb; ++j) {
+                float amax = 0.0f;
+                for (int r = 0; r < ORC_BLK; ++r)
+                    for (int d = 0; d < D; ++d) {
+                        float val = x[((b * S + (int64_t)j * ORC_BLK + r) * heads + h) * D + d];
+                        if (which == 1) val = val - kmean[d];
+                        xs[r * D + d] = val;
+                        if (fabsf(val) > amax) amax = fabsf(val);
+                    }
+                float sc = amax / 127.0f;
+                xsc[bh * nb + j] = sc;
+                int8_t *dst = x8 + (bh * nb + j) * (int64_t)ORC_BLK * D;
+                for (int e = 0; e < ORC_BLK * D; ++e) dst[e] = orc_int8_code(xs[e], sc);
+            }
+        }
+        free(xs);
+        /* v: per-channel scale over the whole sequence, then codes, blocks transposed */
+        for (int d = 0; d < D; ++d) {
+            float amax = 0.0f;
+            for (int64_t s = 0; s < S; ++s) {
+                float a = fabsf(v[((b * S + s) * heads + h) * D + d]);
+                if (a > amax) amax = a;
+            }
+            float sc = amax / 2.25f;
+            vs[bh * D + d] = sc;
+            for (int64_t s = 0; s < S; ++s) {
+                float val = v[((b * S + s) * heads + h) * D + d];
+                float r = sc == 0.0f ? 0.0f : val / sc;
+                int64_t j = s / ORC_BLK, key = s % ORC_BLK;
+                v8[((bh * nb + j) * D + d) * ORC_BLK + key] = orc_fp8_e4m3((double)r);
+            }
+        }
+    }
+    return 0;
+}
+
+/* The attention on the codes for the q-block rows row_ids (as orc_attention); o [nrows][64][D]. */
+int orc_attention_q8(const int8_t *q8, const float *qs, const int8_t *k8, const float *ks,
+                     const uint8_t *v8, const float *vs, int B, int S, int heads, int D,
+                     const int32_t *kv_nb, const int32_t *kv_inds, double scale,
+                     const int64_t *row_ids, int64_t nrows, double *o) {
+    if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
+    int nb = S / ORC_BLK;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    double vdec[256];
+    for (int c = 0; c < 256; ++c) vdec[c] = orc_fp8_e4m3_value((uint8_t)c);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t rr = 0; rr < nrows; ++rr) {
+        int64_t id = row_ids[rr];
+        if (id < 0 || id >= (int64_t)B * heads * nb) { bad = 1; continue; }
+        int64_t bh = id / nb;
+        int i = (int)(id % nb);
+        int n = kv_nb[id];
+        if (n < 0 || n > nb) { bad = 1; continue; }
+        uint8_t *allowed = (uint8_t *)calloc((size_t)nb, 1);
+        for (int t = 0; t < n; ++t) {
+            int j = kv_inds[id * nb + t];
+            if (j < 0 || j >= nb) { bad = 1; break; }
+            allowed[j] = 1;
+        }
+        double *z = (double *)malloc(sizeof(double) * (size_t)S);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+        for (int r = 0; r < ORC_BLK; ++r) {
+            const int8_t *qr = q8 + ((bh * nb + i) * ORC_BLK + r) * (int64_t)D;
+            double *orow = o + (rr * ORC_BLK + r) * D;
+            double zmax = -INFINITY;
+            for (int64_t c = 0; c < S; ++c) {
+                int j = (int)(c / ORC_BLK);
+                if (!allowed[j]) { z[c] = -INFINITY; continue; }
+                const int8_t *kc = k8 + (bh * nb * ORC_BLK + c) * (int64_t)D;
+                int64_t dot = 0;
+                for (int d = 0; d < D; ++d) dot += (int64_t)qr[d] * (int64_t)kc[d];
+                z[c] = scale * (double)qs[bh * nb + i] * (double)ks[bh * nb + j] * (double)dot;
+                if (z[c] > zmax) zmax = z[c];
+            }
+            for (int d = 0; d < D; ++d) { orow[d] = 0.0; acc[d] = 0.0; }
+            if (zmax == -INFINITY) continue; /* empty list: O = 0 */
+            double wsum = 0.0;
+            for (int64_t c = 0; c < S; ++c) {
+                if (z[c] == -INFINITY) continue;
+                double w = vdec[orc_fp8_e4m3(448.0 * exp(z[c] - zmax))];
+                if (w == 0.0) continue;
+                wsum += w;
+                int64_t j = c / ORC_BLK, key = c % ORC_BLK;
+                const uint8_t *vb = v8 + (bh * nb + j) * (int64_t)D * ORC_BLK;
+                for (int d = 0; d < D; ++d) acc[d] += w * vdec[vb[d * ORC_BLK + key]];
+            }
+            for (int d = 0; d < D; ++d) orow[d] = (double)vs[bh * D + d] * acc[d] / wsum;
+        }
+        free(acc);
+        free(z);
+        free(allowed);
+    }
+    return bad ? -1 : 0;
+}

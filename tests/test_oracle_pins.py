@@ -664,3 +664,179 @@ def test_block_mask_grid_consistency(orc):
     n = int(r["kv_nb"].flat[0])
     assert np.all(r["kv_nb"] == n) and nb // 2 <= n <= nb // 2 + 1
     assert np.all(r["kv_inds"][..., :n] == np.arange(nb - n, nb))
+
+
+# ------------------------------------------------------------------ O12 quantized variant
+def test_fp8_e4m3_against_torch(orc):
+    """The e4m3 encoder and decoder against torch's float8_e4m3fn (an independent routine)."""
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    tval = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
+    dec = orc.fp8_e4m3_value(codes)
+    finite = ~np.isnan(tval)
+    assert finite.sum() == 254                     # only S.1111.111 is NaN
+    assert np.array_equal(dec[finite], tval[finite]) and np.isnan(dec[~finite]).all()
+    assert dec[0x7e] == 448.0 and dec[0x01] == 2.0 ** -9 and dec[0x38] == 1.0 and dec[0x41] == 2.25
+    # every finite code round-trips; midpoints of neighbours go to the even code
+    assert np.array_equal(orc.fp8_e4m3(dec[finite]), codes[finite])
+    pos = np.arange(0, 0x7e)
+    mids = (dec[pos] + dec[pos + 1]) / 2
+    want = np.where(pos % 2 == 0, pos, pos + 1).astype(np.uint8)
+    assert np.array_equal(orc.fp8_e4m3(mids), want)
+    assert np.array_equal(orc.fp8_e4m3(-mids), want | 0x80)
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.uniform(-0.03, 0.03, 20000)])
+    x = x.astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.fp8_e4m3(x.astype(np.float64)), ref)
+
+
+def _quant_inputs(B=1, S=256, heads=2, D=64, seed=12):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, S, heads, D)).astype(np.float32)
+    k = (rng.standard_normal((B, S, heads, D)) + 0.7).astype(np.float32)   # a mean to remove
+    v = (rng.standard_normal((B, S, heads, D)) * 2.0).astype(np.float32)
+    return q, k, v
+
+
+def test_quant_qkv_codes_and_scales(orc):
+    """INT8 per block (k after its sequence mean) and FP8 per channel: scales from the block /
+    channel maxima, codes within half a step, the extreme element at full scale."""
+    q, k, v = _quant_inputs()
+    B, S, heads, D = q.shape
+    nb = S // 64
+    z = orc.quant_qkv(q, k, v)
+    km64 = k.astype(np.float64).mean(axis=1)                      # [B, heads, D]
+    assert np.allclose(z["km"], km64, rtol=0, atol=1e-5)
+    for name, x in (("q", q), ("k", k - z["km"][:, None, :, :])):
+        codes, sc = z[name + "8"], z[name + "s"]
+        xb = x.transpose(0, 2, 1, 3).reshape(B, heads, nb, 64, D)    # [B,h,nb,64,D]
+        amax = np.abs(xb).max(axis=(3, 4))
+        assert np.array_equal(sc, (amax / np.float32(127)).astype(np.float32))
+        assert np.abs(codes.astype(np.int32)).max() <= 127
+        assert (np.abs(codes.astype(np.int32)).max(axis=(3, 4)) == 127).all()
+        err = np.abs(xb - codes.astype(np.float64) * sc[..., None, None])
+        assert (err <= 0.5 * sc[..., None, None] * (1 + 1e-5) + 1e-12).all()
+    amax_v = np.abs(v).max(axis=1)                                 # [B, heads, D]
+    assert np.array_equal(z["vs"], (amax_v / np.float32(2.25)).astype(np.float32))
+    vt = v.transpose(0, 2, 1, 3).reshape(B, heads, nb, 64, D).transpose(0, 1, 2, 4, 3)
+    ratio = vt / z["vs"][:, :, None, :, None]
+    dec = orc.fp8_e4m3_value(z["v8"])
+    assert (np.abs(dec - ratio) <= np.abs(ratio) * 2.0 ** -4 + 2.0 ** -10).all()
+    assert np.abs(dec).max() == 2.25
+
+
+def test_quant_qkv_degenerate_blocks(orc):
+    """Zero blocks quantize to scale 0 and code 0; a constant k has k - mean = 0."""
+    q, k, v = _quant_inputs()
+    q[:, :64] = 0.0
+    k[:] = 1.5
+    v[..., 3] = 0.0
+    z = orc.quant_qkv(q, k, v)
+    assert (z["qs"][:, :, 0] == 0).all() and (z["q8"][:, :, 0] == 0).all()
+    assert (z["qs"][:, :, 1:] > 0).all()
+    assert (z["km"] == 1.5).all() and (z["ks"] == 0).all() and (z["k8"] == 0).all()
+    assert (z["vs"][..., 3] == 0).all() and (z["v8"][:, :, :, 3, :] == 0).all()
+
+
+def test_attention_q8_exact_on_power_of_two_weights(orc):
+    """With scale ln 2, unit scales and small integer dots every weight is a power of two that
+    e4m3 holds exactly, so the output is sum 2^dot v / sum 2^dot, computed here independently."""
+    rng = np.random.default_rng(13)
+    B, heads, nb, D = 1, 2, 4, 64
+    S = nb * 64
+    q8 = np.zeros((B, heads, nb, 64, D), np.int8)
+    k8 = np.zeros((B, heads, nb, 64, D), np.int8)
+    for a in (q8, k8):           # four +-1 entries per row: dots in [-4, 4]
+        for idx in np.ndindex(a.shape[:4]):
+            pos = rng.choice(D, 4, replace=False)
+            a[idx + (slice(None),)][pos] = rng.choice([-1, 1], 4)
+    v8 = rng.integers(0, 0x7e, (B, heads, nb, D, 64)).astype(np.uint8)
+    v8 |= (rng.integers(0, 2, v8.shape) * 0x80).astype(np.uint8)
+    qz = {"q8": q8, "qs": np.ones((B, heads, nb), np.float32), "k8": k8,
+          "ks": np.ones((B, heads, nb), np.float32), "v8": v8,
+          "vs": np.full((B, heads, D), 0.5, np.float32)}
+    kv_nb = np.array([[[2, 4, 0, 1], [3, 1, 2, 4]]], np.int32)
+    kv_inds = np.zeros((B, heads, nb, nb), np.int32)
+    for h in range(heads):
+        for i in range(nb):
+            kv_inds[0, h, i] = rng.permutation(nb)
+    ids, o = orc.attention_q8(qz, kv_nb, kv_inds, scale=math.log(2.0))
+    vdec = orc.fp8_e4m3_value(v8).transpose(0, 1, 2, 4, 3).reshape(B, heads, S, D)
+    kf = k8.reshape(B, heads, S, D).astype(np.int64)
+    for n, rid in enumerate(ids):
+        h, i = divmod(int(rid), nb)
+        keys = np.concatenate([np.arange(64 * j, 64 * j + 64) for j in kv_inds[0, h, i, :kv_nb[0, h, i]]]) \
+            if kv_nb[0, h, i] else np.zeros(0, np.int64)
+        if keys.size == 0:
+            assert (o[n] == 0).all()
+            continue
+        dots = q8[0, h, i].astype(np.int64) @ kf[0, h, keys].T            # [64, keys]
+        w = np.exp2((dots - dots.max(axis=1, keepdims=True)).astype(np.float64))
+        want = 0.5 * (w @ vdec[0, h, keys]) / w.sum(axis=1, keepdims=True)
+        assert np.allclose(o[n], want, rtol=1e-13, atol=1e-13)
+
+
+def test_attention_q8_closed_forms(orc):
+    """Constant v gives that constant; q = 0 gives the mean of the dequantized v of the listed
+    blocks; an empty list gives 0."""
+    q, k, v = _quant_inputs(S=256)
+    B, S, heads, D = q.shape
+    nb = S // 64
+    c = np.linspace(-3.0, 2.0, D).astype(np.float32)
+    kv_nb = np.array([[[1, 3, 0, 4], [2, 2, 1, 3]]], np.int32)
+    kv_inds = np.tile(np.array([3, 0, 2, 1], np.int32), (B, heads, nb, 1))
+    vc = np.broadcast_to(c, v.shape).copy()
+    ids, o = orc.attention_q8(orc.quant_qkv(q, k, vc), kv_nb, kv_inds)
+    for n, rid in enumerate(ids):
+        h, i = divmod(int(rid), nb)
+        if kv_nb[0, h, i] == 0:
+            assert (o[n] == 0).all()
+        else:
+            assert np.allclose(o[n], np.broadcast_to(c, (64, D)), rtol=2e-7, atol=0)
+    z = orc.quant_qkv(np.zeros_like(q), k, v)
+    ids, o = orc.attention_q8(z, kv_nb, kv_inds)
+    _, _, vdq = orc.dequant_qkv(z)
+    for n, rid in enumerate(ids):
+        h, i = divmod(int(rid), nb)
+        blocks = kv_inds[0, h, i, :kv_nb[0, h, i]]
+        if blocks.size == 0:
+            continue
+        keys = np.concatenate([np.arange(64 * j, 64 * j + 64) for j in blocks])
+        want = vdq[0, keys, h, :].mean(axis=0)
+        assert np.allclose(o[n], np.broadcast_to(want, (64, D)), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_q8_within_p_rounding_of_plain_attention(orc):
+    """On the dequantized codes the quantized attention differs from the plain fp64 attention
+    only by the e4m3 rounding of P (relative error <= 2^-4 per weight, or 2^-10 / 448 absolute
+    below the normal range), hence |o' - o| <= (2^-4 + 2^-10 n / 448) / (1 - 2^-4) * max|v - o|
+    per element; the quantized result also stays close to the unquantized inputs' attention."""
+    q, k, v = _quant_inputs(S=512, seed=14)
+    B, S, heads, D = q.shape
+    nb = S // 64
+    rng = np.random.default_rng(15)
+    kv_nb, kv_inds = synth.random_lists(rng, B, heads, nb, 0.5)
+    kv_nb[0, 0, 0] = nb
+    z = orc.quant_qkv(q, k, v)
+    ids, o8 = orc.attention_q8(z, kv_nb, kv_inds)
+    qd, kd, vd = orc.dequant_qkv(z)
+    _, o = orc.attention(qd, kd, vd, kv_nb, kv_inds)
+    for n, rid in enumerate(ids):
+        b, rem = divmod(int(rid), heads * nb)
+        h, i = divmod(rem, nb)
+        cnt = kv_nb[b, h, i]
+        if cnt == 0:
+            assert (o8[n] == 0).all()
+            continue
+        keys = np.concatenate([np.arange(64 * j, 64 * j + 64) for j in kv_inds[b, h, i, :cnt]])
+        vk = vd[b, keys, h, :].astype(np.float64)                           # [keys, D]
+        spread = np.abs(vk[None, :, :] - o[n][:, None, :]).max(axis=1)      # [64, D]
+        bound = (2.0 ** -4 + 2.0 ** -10 * keys.size / 448.0) / (1 - 2.0 ** -4) * spread
+        assert (np.abs(o8[n] - o[n]) <= bound + 1e-9).all()
+    err = np.abs(o8 - o)
+    assert err.mean() < 0.1 * np.abs(o).mean()      # the rounding errors average out
+    # against the unquantized inputs (k's mean removal does not change attention)
+    _, of = orc.attention(q, k, v, kv_nb, kv_inds)
+    cos = (o8 * of).sum() / np.sqrt((o8 * o8).sum() * (of * of).sum())
+    assert cos > 0.99
