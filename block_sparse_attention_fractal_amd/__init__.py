@@ -11,6 +11,8 @@ Calls (same names as the C ABI):
   nabla_block_mask(q, k, sta, thr=0.9)          -> (kv_nb, kv_inds)
   nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, tiles=None,
                         workspace=None, out=None) -> o
+  nabla_quant_qkv(q, k, v)                      -> dict of INT8 / FP8 codes and scales
+  nabla_sparse_attn_fwd_q8(qz, kv_nb, kv_inds, scale=None, tiles=None) -> o (bf16)
 """
 import ctypes
 import os
@@ -20,6 +22,7 @@ import torch
 __all__ = ["nabla_fractal_permute", "nabla_sta_mask", "nabla_block_mask",
            "nabla_block_mask_workspace", "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace",
            "nabla_sparse_attn_bwd", "nabla_sparse_attn_bwd_workspace", "fractal_len",
+           "nabla_quant_qkv", "nabla_sparse_attn_fwd_q8",
            "NablaError", "lib",
            "LIB_PATH", "STATUS"]
 
@@ -79,6 +82,15 @@ def lib():
     L.nabla_sparse_attn_bwd_workspace.restype = Z
     L.nabla_sparse_attn_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, F, P, P, P, P, Z, P]
     L.nabla_sparse_attn_bwd.restype = I
+    L.nabla_quant_qkv_workspace.argtypes = [I, I, I, I]
+    L.nabla_quant_qkv_workspace.restype = Z
+    L.nabla_quant_qkv.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]
+    L.nabla_quant_qkv.restype = I
+    L.nabla_sparse_attn_q8_workspace.argtypes = [I, I, I, I, I, I]
+    L.nabla_sparse_attn_q8_workspace.restype = Z
+    L.nabla_sparse_attn_fwd_q8.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, F, I, I, I, P, P, Z,
+                                           P]
+    L.nabla_sparse_attn_fwd_q8.restype = I
     _lib = L
     return L
 
@@ -308,3 +320,72 @@ def nabla_sparse_attn_bwd(q, k, v, o, dout, lse, kv_nb, kv_inds, scale=None, wor
                                        workspace.numel(), _stream(q)),
            "nabla_sparse_attn_bwd")
     return tuple(outs)
+
+
+def nabla_quant_qkv(q, k, v, workspace=None):
+    """The quantizer of the quantized variant: q, k, v [B, S, heads, D] (bf16 or fp32) ->
+    dict(q8, q_scale, k8, k_scale, v8, v_scale, k_mean) with q8, k8 int8 [B, heads, nb, 64, D]
+    (k after subtracting its sequence mean), q_scale, k_scale float32 [B, heads, nb], v8 uint8
+    e4m3 codes [B, heads, nb, D, 64] (blocks transposed), v_scale, k_mean float32 [B, heads, D].
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must match in shape and dtype")
+    B, S, heads, D = q.shape
+    nb = S // BLOCK
+    dev = q.device
+    out = {"q8": torch.empty((B, heads, nb, BLOCK, D), dtype=torch.int8, device=dev),
+           "q_scale": torch.empty((B, heads, nb), dtype=torch.float32, device=dev),
+           "k8": torch.empty((B, heads, nb, BLOCK, D), dtype=torch.int8, device=dev),
+           "k_scale": torch.empty((B, heads, nb), dtype=torch.float32, device=dev),
+           "v8": torch.empty((B, heads, nb, D, BLOCK), dtype=torch.uint8, device=dev),
+           "v_scale": torch.empty((B, heads, D), dtype=torch.float32, device=dev),
+           "k_mean": torch.empty((B, heads, D), dtype=torch.float32, device=dev)}
+    if workspace is None:
+        need = lib().nabla_quant_qkv_workspace(B, S, heads, D)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _dev(workspace, "workspace")
+    _check(lib().nabla_quant_qkv(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads, D,
+                                 _p(out["q8"]), _p(out["q_scale"]), _p(out["k8"]),
+                                 _p(out["k_scale"]), _p(out["v8"]), _p(out["v_scale"]),
+                                 _p(out["k_mean"]), _p(workspace), workspace.numel(), _stream(q)),
+           "nabla_quant_qkv")
+    return out
+
+
+def nabla_sparse_attn_fwd_q8(qz, kv_nb, kv_inds, scale=None, tiles=None, workspace=None,
+                             out=None):
+    """Block-sparse attention of the quantized variant over the listed 64 x 64 blocks, on the
+    codes of nabla_quant_qkv (qz): o [B, S, heads, D] bfloat16."""
+    names = ("q8", "q_scale", "k8", "k_scale", "v8", "v_scale")
+    for name in names:
+        _dev(qz[name], name)
+    _dev(kv_nb, "kv_nb")
+    _dev(kv_inds, "kv_inds")
+    q8 = qz["q8"]
+    if q8.dtype != torch.int8 or q8.dim() != 5 or q8.shape[3] != BLOCK:
+        raise ValueError("q8 must be int8 [B, heads, nb, 64, D]")
+    B, heads, nb, _, D = q8.shape
+    S = nb * BLOCK
+    if kv_nb.dtype != torch.int32 or kv_inds.dtype != torch.int32:
+        raise TypeError("kv_nb and kv_inds must be int32")
+    if kv_nb.numel() != B * heads * nb or kv_inds.numel() != B * heads * nb * nb:
+        raise ValueError("kv lists do not match the codes' shape")
+    if qz["k8"].shape != q8.shape or qz["v8"].numel() != q8.numel():
+        raise ValueError("q8, k8, v8 must have one shape")
+    o = torch.empty((B, S, heads, D), dtype=torch.bfloat16, device=q8.device) if out is None \
+        else _dev(out, "out")
+    Tt, Ht, Wt = (0, 0, 0) if tiles is None else tiles
+    if workspace is None:
+        need = lib().nabla_sparse_attn_q8_workspace(B, S, heads, Tt, Ht, Wt)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q8.device)
+    else:
+        _dev(workspace, "workspace")
+    _check(lib().nabla_sparse_attn_fwd_q8(*[_p(qz[n]) for n in names], B, S, heads, D,
+                                          _p(kv_nb), _p(kv_inds),
+                                          0.0 if scale is None else float(scale), Tt, Ht, Wt,
+                                          _p(o), _p(workspace), workspace.numel(), _stream(q8)),
+           "nabla_sparse_attn_fwd_q8")
+    return o

@@ -52,6 +52,34 @@ __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Query blocks per attention workgroup: kGroup 4 takes a 2 (time) x 1 x 2 (width) box of
+// tiles, kGroup 2 the same tile in two consecutive frames.
+#ifndef NABLA_ATTN_GROUP
+#define NABLA_ATTN_GROUP 4
+#endif
+constexpr int kGroup = NABLA_ATTN_GROUP;
+constexpr int kAttnWaves = 2 * kGroup;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kMaxWords = 4096 / 64;  // bitmap words for up to 4096 blocks per row
+static_assert(kGroup == 2 || kGroup == 4, "group of 2 or 4 query blocks");
+static_assert(kAttnWaves == 8 || kGroup != 4, "the delayed half of the waves is waves 4-7");
+
+// Member s of query-block group gi (-1 = empty slot).  Known tile grid: kGroup 4 takes
+// a 2 (time) x 1 x 2 (width) box of tiles, kGroup 2 the same tile in two consecutive
+// frames; unknown grid (Tt == 0): kGroup consecutive blocks.
+__device__ __forceinline__ int group_member(int gi, int s, int Tt, int Ht, int Wt, int nb) {
+    if (Tt > 0) {
+        const int cw = kGroup == 4 ? (Wt + 1) >> 1 : Wt;
+        const int a = gi / (Ht * cw), hh = (gi / cw) % Ht, c = gi % cw;
+        const int t = 2 * a + (kGroup == 4 ? (s >> 1) : s);
+        const int ww = kGroup == 4 ? 2 * c + (s & 1) : c;
+        return (t < Tt && ww < Wt) ? (t * Ht + hh) * Wt + ww : -1;
+    }
+    const int i = gi * kGroup + s;
+    return i < nb ? i : -1;
+}
+
+
 // A list length / block index from kv lists, clamped into range (bad lists cannot
 // address memory outside the tensors).
 __device__ __forceinline__ int clamp_count(int n, int nb) { return n < 0 ? 0 : (n > nb ? nb : n); }

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
 constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
@@ -254,6 +254,53 @@ nabla_status nabla_sparse_attn_bwd(const void *q, const void *k, const void *v, 
     return from_hip(nabla::launch_sparse_attn_bwd(q, k, v, o, dout, lse, B, S, heads, head_dim,
                                                   kv_nb, kv_inds, scale, dq, dk, dv, ws,
                                                   as_stream(stream)));
+}
+
+size_t nabla_quant_qkv_workspace(int B, int S, int heads, int head_dim) {
+    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return 0;
+    return nabla::quant_workspace_bytes(B, S, heads, head_dim);
+}
+
+nabla_status nabla_quant_qkv(const void *q, const void *k, const void *v, nabla_dtype dtype,
+                             int B, int S, int heads, int head_dim, int8_t *q8, float *q_scale,
+                             int8_t *k8, float *k_scale, uint8_t *v8, float *v_scale,
+                             float *k_mean, void *ws, size_t ws_bytes, void *stream) {
+    if (!q || !k || !v || !q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || !k_mean ||
+        !dtype_ok(dtype))
+        return NABLA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < nabla::quant_workspace_bytes(B, S, heads, head_dim))
+        return NABLA_ERR_WORKSPACE;
+    return from_hip(nabla::launch_quant_qkv(q, k, v, dtype == NABLA_BF16, B, S, heads, head_dim,
+                                            q8, q_scale, k8, k_scale, v8, v_scale, k_mean, ws,
+                                            as_stream(stream)));
+}
+
+size_t nabla_sparse_attn_q8_workspace(int B, int S, int heads, int Tt, int Ht, int Wt) {
+    if (!sizes_ok(B, S, heads, 1) || S % kBlock || !grid_ok(S, Tt, Ht, Wt)) return 0;
+    return nabla::sparse_attn_q8_workspace_bytes(B, S, heads, Tt, Ht, Wt);
+}
+
+nabla_status nabla_sparse_attn_fwd_q8(const int8_t *q8, const float *q_scale, const int8_t *k8,
+                                      const float *k_scale, const uint8_t *v8,
+                                      const float *v_scale, int B, int S, int heads,
+                                      int head_dim, const int32_t *kv_nb, const int32_t *kv_inds,
+                                      float scale, int Tt, int Ht, int Wt, void *o, void *ws,
+                                      size_t ws_bytes, void *stream) {
+    if (!q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || !kv_nb || !kv_inds || !o)
+        return NABLA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
+    if (scale != scale) return NABLA_ERR_INVALID_ARG;
+    if (!grid_ok(S, Tt, Ht, Wt)) return NABLA_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
+    if (S / kBlock > kMaxBlocks) return NABLA_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < nabla::sparse_attn_q8_workspace_bytes(B, S, heads, Tt, Ht, Wt))
+        return NABLA_ERR_WORKSPACE;
+    if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
+    return from_hip(nabla::launch_sparse_attn_q8(q8, q_scale, k8, k_scale, v8, v_scale, B, S,
+                                                 heads, head_dim, Tt, Ht, Wt, kv_nb, kv_inds,
+                                                 scale, o, ws, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -29,6 +29,37 @@ hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, in
                                   int32_t *kv_nb, int32_t *kv_inds, float *qa, float *ka,
                                   hipStream_t stream);
 
+// Workgroups of kernel K (of `threads` lanes) the device holds at once (occupancy x CUs),
+// cached per device and kernel; 0 if the query fails.
+template <auto K>
+int resident_workgroups(int threads) {
+    constexpr int kMaxDevices = 64;
+    static int cache[kMaxDevices];  // 0 = not yet known; a racing first call stores the same value
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    if (cache[dev] > 0) return cache[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, 0) != hipSuccess)
+        return 0;
+    cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
+    return cache[dev];
+}
+
+// The attention walk's schedule (groups of neighbouring query blocks, phases of a few
+// heads, longest first): plan kernels write the group order and reset the take counter
+// in a workspace of attn_schedule_bytes(); the walk kernel takes groups from it.
+struct AttnSchedule {
+    int groups_per_bh, ngroups, grid;
+    int32_t *order, *counter;
+};
+int attn_groups_per_bh(int S, int Tt, int Ht, int Wt);
+size_t attn_schedule_bytes(int B, int S, int heads, int Tt, int Ht, int Wt);
+// resident: workgroups of the walk kernel the device holds at once (sets the phase size).
+AttnSchedule launch_attn_plan(const int32_t *kv_nb, const int32_t *kv_inds, int B, int S,
+                              int heads, int Tt, int Ht, int Wt, int resident, void *ws,
+                              hipStream_t stream);
+
 // Tt, Ht, Wt: tile grid of the query blocks (Tt*Ht*Wt == S/64), or all 0 if unknown.
 // ws: sparse_attn_workspace_bytes() bytes (schedule: counter, group costs, order).
 size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt);
@@ -48,5 +79,20 @@ hipError_t launch_sparse_attn_bwd(const void *q, const void *k, const void *v, c
                                   int D, const int32_t *kv_nb, const int32_t *kv_inds,
                                   float scale, void *dq, void *dk, void *dv, void *ws,
                                   hipStream_t stream);
+
+// The quantized variant.  Codes and scales of q, k, v (layouts in nabla.h,
+// nabla_quant_qkv); ws: quant_workspace_bytes() bytes (k block sums, partial v maxima).
+size_t quant_workspace_bytes(int B, int S, int heads, int D);
+hipError_t launch_quant_qkv(const void *q, const void *k, const void *v, bool bf16_in, int B,
+                            int S, int heads, int D, int8_t *q8, float *qs, int8_t *k8,
+                            float *ks, uint8_t *v8, float *vs, float *km, void *ws,
+                            hipStream_t stream);
+// The attention on those codes (bf16 o); ws: sparse_attn_q8_workspace_bytes() bytes.
+size_t sparse_attn_q8_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt);
+hipError_t launch_sparse_attn_q8(const int8_t *q8, const float *qs, const int8_t *k8,
+                                 const float *ks, const uint8_t *v8, const float *vs, int B,
+                                 int S, int heads, int D, int Tt, int Ht, int Wt,
+                                 const int32_t *kv_nb, const int32_t *kv_inds, float scale,
+                                 void *o, void *ws, hipStream_t stream);
 
 }  // namespace nabla

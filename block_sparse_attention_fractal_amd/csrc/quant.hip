@@ -1,0 +1,239 @@
+// quant.hip -- the quantizer of the quantized attention variant on gfx950.
+//
+// The sibling "sla" backend page's SageSLA forward quantizes Q and K to INT8
+// (one scale per block, after subtracting the mean of K over the sequence) and
+// V to FP8 e4m3 (one scale per channel; the page passes a scale maximum of
+// 2.25), then runs its block-sparse attention on the codes.  Here the blocks are
+// the 64-token blocks of the kv lists.  Every rounding is fixed so that the codes
+// and scales are reproducible bit for bit:
+//   k_mean[d] = (sum_j bs_j[d]) / S, bs_j[d] = sum of the 64 tokens of block j,
+//               both sums sequential in fp32 from +0, IEEE division;
+//   INT8:       scale = amax / 127, code = clamp(rint(x / scale), -127, 127)
+//               (IEEE fp32 division, round half to even); amax = 0 -> 0;
+//   FP8 V:      scale[d] = amax_d / 2.25 over the whole sequence,
+//               code = e4m3fn(v / scale[d]), round to nearest even
+//               (v_cvt_pk_fp8_f32); scale 0 -> code 0.
+// Outputs: q8, k8 [B][heads][nb][64][D] int8; q_scale, k_scale [B][heads][nb];
+// v8 [B][heads][nb][D][64] (each block transposed, the layout the attention's
+// P V product reads); v_scale, k_mean [B][heads][D].
+// All kernels are HBM-bound passes with coalesced 16-byte accesses.
+#include "nabla_device.h"
+#include "nabla_launch.h"
+
+namespace nabla {
+
+constexpr int kQuantChunk = 1024;  // tokens per partial channel maximum of v
+
+// bs[item][d] = sequential fp32 sum of the block's 64 tokens, item = (b*heads + h)*nb + j.
+// One workgroup of D lanes per block; lane d walks the 64 rows (stride heads*D).
+template <int D, typename Tin>
+__global__ __launch_bounds__(D) void quant_ksum_kernel(const Tin *__restrict__ k,
+                                                       float *__restrict__ bs, int S, int heads) {
+    const int nb = S / kBlock;
+    const int64_t item = blockIdx.x;
+    const int j = (int)(item % nb), bh = (int)(item / nb);
+    const int b = bh / heads, h = bh % heads, d = threadIdx.x;
+    const int64_t tok = (int64_t)heads * D;
+    const Tin *src = k + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D + d;
+    float x[kBlock];
+#pragma unroll
+    for (int r = 0; r < kBlock; ++r) x[r] = (float)src[r * tok];
+    float acc = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kBlock; ++r) acc += x[r];
+    bs[item * D + d] = acc;
+}
+
+// km[bh][d] = (sequential sum over blocks of bs) / S.  One workgroup of D lanes per (b, head).
+template <int D>
+__global__ __launch_bounds__(D) void quant_kmean_kernel(const float *__restrict__ bs,
+                                                        float *__restrict__ km, int S) {
+    const int nb = S / kBlock;
+    const int64_t bh = blockIdx.x;
+    const int d = threadIdx.x;
+    const float *p = bs + bh * nb * D + d;
+    float acc = 0.0f;
+    for (int j = 0; j < nb; ++j) acc += p[(int64_t)j * D];
+    km[bh * D + d] = acc / (float)S;
+}
+
+__device__ __forceinline__ int8_t int8_code(float x, float scale) {
+    if (scale == 0.0f) return 0;
+    const float r = fminf(fmaxf(__builtin_rintf(x / scale), -127.0f), 127.0f);
+    return (int8_t)(int)r;
+}
+
+// One workgroup of 256 lanes per (block, tensor): blockIdx.y = 0 quantizes q, 1 quantizes
+// k - k_mean.  Lane t holds the 16-byte chunks e = r*256 + t (row e / (D/8)) in registers,
+// the block maximum comes from a wave reduction and LDS, then the codes are written as
+// 8-byte runs in the same row-major order.
+template <int D, typename Tin>
+__global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q,
+                                                       const Tin *__restrict__ k,
+                                                       const float *__restrict__ km,
+                                                       int8_t *__restrict__ q8,
+                                                       float *__restrict__ qs,
+                                                       int8_t *__restrict__ k8,
+                                                       float *__restrict__ ks, int S, int heads) {
+    constexpr int CH = D / 8;                  // 8-element chunks per row
+    constexpr int CPT = kBlock * CH / 256;     // chunks per lane
+    __shared__ float wmax[4];
+    const int nb = S / kBlock;
+    const int64_t item = blockIdx.x;
+    const bool is_k = blockIdx.y == 1;
+    const int j = (int)(item % nb), bh = (int)(item / nb);
+    const int b = bh / heads, h = bh % heads, tid = threadIdx.x;
+    const int64_t tok = (int64_t)heads * D;
+    const Tin *src = (is_k ? k : q) + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D;
+    float x[CPT][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+        const int e = r * 256 + tid, row = e / CH, c = e % CH;
+        const Tin *p = src + row * tok + 8 * c;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float val = (float)p[i];
+            if (is_k) val = val - km[(int64_t)bh * D + 8 * c + i];
+            x[r][i] = val;
+            amax = fmaxf(amax, fabsf(val));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float scale = amax / 127.0f;
+    int8_t *dst = (is_k ? k8 : q8) + item * (kBlock * D);
+    if (tid == 0) (is_k ? ks : qs)[item] = scale;
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+        const int e = r * 256 + tid;
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w0 |= (uint32_t)(uint8_t)int8_code(x[r][i], scale) << (8 * i);
+            w1 |= (uint32_t)(uint8_t)int8_code(x[r][4 + i], scale) << (8 * i);
+        }
+        *reinterpret_cast<uint2 *>(dst + 8 * e) = make_uint2(w0, w1);
+    }
+}
+
+// part[(bh * nchunk + c) * D + d] = max |v| over tokens [c*1024, (c+1)*1024) of channel d.
+template <int D, typename Tin>
+__global__ __launch_bounds__(D) void quant_vmax_kernel(const Tin *__restrict__ v,
+                                                       float *__restrict__ part, int S,
+                                                       int heads, int nchunk) {
+    const int64_t item = blockIdx.x;  // bh * nchunk + c
+    const int c = (int)(item % nchunk), bh = (int)(item / nchunk);
+    const int b = bh / heads, h = bh % heads, d = threadIdx.x;
+    const int64_t tok = (int64_t)heads * D;
+    const int t0 = c * kQuantChunk, t1 = min(S, t0 + kQuantChunk);
+    const Tin *src = v + (int64_t)b * S * tok + (int64_t)h * D + d;
+    float m = 0.0f;
+    for (int t = t0; t < t1; ++t) m = fmaxf(m, fabsf((float)src[(int64_t)t * tok]));
+    part[item * D + d] = m;
+}
+
+// vs[bh][d] = (max over chunks) / 2.25.  One workgroup of D lanes per (b, head).
+template <int D>
+__global__ __launch_bounds__(D) void quant_vscale_kernel(const float *__restrict__ part,
+                                                         float *__restrict__ vs, int nchunk) {
+    const int64_t bh = blockIdx.x;
+    const int d = threadIdx.x;
+    float m = 0.0f;
+    for (int c = 0; c < nchunk; ++c) m = fmaxf(m, part[(bh * nchunk + c) * D + d]);
+    vs[bh * D + d] = m / 2.25f;
+}
+
+// One workgroup of 256 lanes per (b, head, block): the block's [64][D] values go to LDS,
+// then each lane writes 16-byte runs of the transposed codes (row d, keys 16c .. 16c+15).
+template <int D, typename Tin>
+__global__ __launch_bounds__(256) void quant_v_kernel(const Tin *__restrict__ v,
+                                                      const float *__restrict__ vs,
+                                                      uint8_t *__restrict__ v8, int S,
+                                                      int heads) {
+    constexpr int CH = D / 8;
+    __shared__ float tile[kBlock][D + 1];
+    const int nb = S / kBlock;
+    const int64_t item = blockIdx.x;
+    const int j = (int)(item % nb), bh = (int)(item / nb);
+    const int b = bh / heads, h = bh % heads, tid = threadIdx.x;
+    const int64_t tok = (int64_t)heads * D;
+    const Tin *src = v + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D;
+    for (int e = tid; e < kBlock * CH; e += 256) {
+        const int row = e / CH, c = e % CH;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[row][8 * c + i] = (float)src[row * tok + 8 * c + i];
+    }
+    __syncthreads();
+    uint8_t *dst = v8 + item * (kBlock * D);
+    for (int e = tid; e < D * 4; e += 256) {  // 4 runs of 16 keys per channel
+        const int d = e >> 2, c = e & 3;
+        const float sc = vs[(int64_t)bh * D + d];
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float f[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                f[i] = sc == 0.0f ? 0.0f : tile[16 * c + 4 * u + i][d] / sc;
+            int pk = 0;
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], pk, false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pk, true);
+            w[u] = (uint32_t)pk;
+        }
+        *reinterpret_cast<uint4 *>(dst + 16 * e) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+static size_t round256q(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t quant_workspace_bytes(int B, int S, int heads, int D) {
+    const size_t nb = S / kBlock, nchunk = (S + kQuantChunk - 1) / kQuantChunk;
+    return round256q((size_t)B * heads * nb * D * 4) + round256q((size_t)B * heads * nchunk * D * 4);
+}
+
+template <int D, typename Tin>
+static hipError_t launch_quant_t(const void *q, const void *k, const void *v, int B, int S,
+                                 int heads, int8_t *q8, float *qs, int8_t *k8, float *ks,
+                                 uint8_t *v8, float *vs, float *km, void *ws, hipStream_t st) {
+    const int nb = S / kBlock;
+    const int nchunk = (S + kQuantChunk - 1) / kQuantChunk;
+    const int64_t items = (int64_t)B * heads * nb;
+    float *bs = static_cast<float *>(ws);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                            round256q((size_t)items * D * 4));
+    const Tin *qi = static_cast<const Tin *>(q), *ki = static_cast<const Tin *>(k),
+              *vi = static_cast<const Tin *>(v);
+    hipLaunchKernelGGL((quant_ksum_kernel<D, Tin>), dim3(items), dim3(D), 0, st, ki, bs, S,
+                       heads);
+    hipLaunchKernelGGL((quant_kmean_kernel<D>), dim3(B * heads), dim3(D), 0, st, bs, km, S);
+    hipLaunchKernelGGL((quant_qk_kernel<D, Tin>), dim3(items, 2), dim3(256), 0, st, qi, ki, km,
+                       q8, qs, k8, ks, S, heads);
+    hipLaunchKernelGGL((quant_vmax_kernel<D, Tin>), dim3(B * heads * nchunk), dim3(D), 0, st, vi,
+                       part, S, heads, nchunk);
+    hipLaunchKernelGGL((quant_vscale_kernel<D>), dim3(B * heads), dim3(D), 0, st, part, vs,
+                       nchunk);
+    hipLaunchKernelGGL((quant_v_kernel<D, Tin>), dim3(items), dim3(256), 0, st, vi, vs, v8, S,
+                       heads);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_qkv(const void *q, const void *k, const void *v, bool bf16_in, int B,
+                            int S, int heads, int D, int8_t *q8, float *qs, int8_t *k8,
+                            float *ks, uint8_t *v8, float *vs, float *km, void *ws,
+                            hipStream_t stream) {
+#define NABLA_QUANT(DD, T)                                                                     \
+    return launch_quant_t<DD, T>(q, k, v, B, S, heads, q8, qs, k8, ks, v8, vs, km, ws, stream)
+    if (D == 128) {
+        if (bf16_in) NABLA_QUANT(128, bf16);
+        NABLA_QUANT(128, float);
+    }
+    if (bf16_in) NABLA_QUANT(64, bf16);
+    NABLA_QUANT(64, float);
+#undef NABLA_QUANT
+}
+
+}  // namespace nabla

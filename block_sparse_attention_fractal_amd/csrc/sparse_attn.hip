@@ -49,15 +49,6 @@
 namespace nabla {
 
 
-#ifndef NABLA_ATTN_GROUP
-#define NABLA_ATTN_GROUP 4
-#endif
-constexpr int kGroup = NABLA_ATTN_GROUP;  // query blocks per workgroup (2 or 4)
-constexpr int kAttnWaves = 2 * kGroup;
-constexpr int kAttnThreads = 64 * kAttnWaves;
-constexpr int kMaxWords = 4096 / 64;  // bitmap words for up to 4096 blocks per row
-static_assert(kGroup == 2 || kGroup == 4, "group of 2 or 4 query blocks");
-static_assert(kAttnWaves == 8 || kGroup != 4, "the delayed half of the waves is waves 4-7");
 
 
 
@@ -101,22 +92,6 @@ struct AttnShared {
     int ucount;
     int slot;  // the schedule position this workgroup works on
 };
-
-// Member s of query-block group gi (-1 = empty slot).  Known tile grid: kGroup 4 takes
-// a 2 (time) x 1 x 2 (width) box of tiles, kGroup 2 the same tile in two consecutive
-// frames; unknown grid (Tt == 0): kGroup consecutive blocks.
-__device__ __forceinline__ int group_member(int gi, int s, int Tt, int Ht, int Wt, int nb) {
-    if (Tt > 0) {
-        const int cw = kGroup == 4 ? (Wt + 1) >> 1 : Wt;
-        const int a = gi / (Ht * cw), hh = (gi / cw) % Ht, c = gi % cw;
-        const int t = 2 * a + (kGroup == 4 ? (s >> 1) : s);
-        const int ww = kGroup == 4 ? 2 * c + (s & 1) : c;
-        return (t < Tt && ww < Wt) ? (t * Ht + hh) * Wt + ww : -1;
-    }
-    const int i = gi * kGroup + s;
-    return i < nb ? i : -1;
-}
-
 
 // ---- schedule.  The cost of a group is the number of tiles in the union of its
 // members' lists (the iterations of its walk).  Persistent workgroups take the next
@@ -595,7 +570,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
 
 // ---- host side
 
-static int groups_per_bh(int S, int Tt, int Ht, int Wt) {
+int attn_groups_per_bh(int S, int Tt, int Ht, int Wt) {
     const int nb = S / kBlock;
     return Tt > 0 ? ((Tt + 1) / 2) * Ht * (kGroup == 4 ? (Wt + 1) / 2 : Wt)
                   : (nb + kGroup - 1) / kGroup;
@@ -603,27 +578,42 @@ static int groups_per_bh(int S, int Tt, int Ht, int Wt) {
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace: [counter | cost[ngroups] | order[ngroups]], each part 256-byte aligned.
-size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt) {
-    const size_t ngroups = (size_t)B * heads * groups_per_bh(S, Tt, Ht, Wt);
+// Schedule: [counter | cost[ngroups] | order[ngroups]], each part 256-byte aligned.
+size_t attn_schedule_bytes(int B, int S, int heads, int Tt, int Ht, int Wt) {
+    const size_t ngroups = (size_t)B * heads * attn_groups_per_bh(S, Tt, Ht, Wt);
     return 256 + 2 * round256(ngroups * sizeof(int32_t));
 }
 
-// Workgroups of `kernel` the device holds at once (occupancy x CUs), cached per device.
-template <typename K>
-static int resident_workgroups(K kernel) {
-    constexpr int kMaxDevices = 64;
-    static int cache[kMaxDevices];  // 0 = not yet known; a racing first call stores the same value
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-    if (cache[dev] > 0) return cache[dev];
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kAttnThreads, 0) !=
-            hipSuccess)
-        return 0;
-    cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
-    return cache[dev];
+size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt) {
+    return attn_schedule_bytes(B, S, heads, Tt, Ht, Wt);
+}
+
+AttnSchedule launch_attn_plan(const int32_t *kv_nb, const int32_t *kv_inds, int B, int S,
+                              int heads, int Tt, int Ht, int Wt, int resident, void *ws,
+                              hipStream_t stream) {
+    AttnSchedule sc;
+    const int nb = S / kBlock;
+    sc.groups_per_bh = attn_groups_per_bh(S, Tt, Ht, Wt);
+    sc.ngroups = B * heads * sc.groups_per_bh;
+    char *wsb = static_cast<char *>(ws);
+    sc.counter = reinterpret_cast<int32_t *>(wsb);
+    int32_t *cost = reinterpret_cast<int32_t *>(wsb + 256);
+    sc.order = reinterpret_cast<int32_t *>(wsb + 256 + round256((size_t)sc.ngroups * 4));
+    hipLaunchKernelGGL(attn_plan_cost_kernel, dim3(sc.ngroups), dim3(256), 0, stream, kv_nb,
+                       kv_inds, nb, Tt, Ht, Wt, sc.groups_per_bh, cost, sc.counter);
+    // Heads per phase: enough groups that the phase, and above all the last one, keeps
+    // every CU busy with room for longest-first packing (three groups per resident
+    // workgroup), and at least two heads.
+    const int gpb = sc.groups_per_bh;
+    const int bh_total = B * heads;
+    int hpp = (3 * resident + gpb - 1) / gpb;
+    hpp = hpp < 2 ? 2 : (hpp > bh_total ? bh_total : hpp);
+    const int nphases = bh_total / hpp;  // the remainder joins the last phase
+    const int per_phase = hpp * gpb;
+    hipLaunchKernelGGL(attn_plan_order_kernel, dim3(nphases), dim3(1024), 0, stream, cost,
+                       sc.ngroups, per_phase, nb, sc.order);
+    sc.grid = sc.ngroups < resident ? sc.ngroups : resident;
+    return sc;
 }
 
 template <int D, typename Tin, bool kPad>
@@ -632,33 +622,15 @@ static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int
                                 const int32_t *kv_nb,
                                 const int32_t *kv_inds, float scale_log2, void *o, float *lse,
                                 void *ws, hipStream_t stream) {
-    const int nb = S / kBlock;
-    const int gpb = groups_per_bh(S, Tt, Ht, Wt);
-    const int ngroups = B * heads * gpb;
-    char *wsb = static_cast<char *>(ws);
-    int32_t *counter = reinterpret_cast<int32_t *>(wsb);
-    int32_t *cost = reinterpret_cast<int32_t *>(wsb + 256);
-    int32_t *order = reinterpret_cast<int32_t *>(wsb + 256 + round256((size_t)ngroups * 4));
-    hipLaunchKernelGGL(attn_plan_cost_kernel, dim3(ngroups), dim3(256), 0, stream, kv_nb, kv_inds,
-                       nb, Tt, Ht, Wt, gpb, cost, counter);
     const auto kernel = sparse_attn_kernel<D, Tin, kPad>;
-    const int resident = resident_workgroups(kernel);
+    const int resident = resident_workgroups<sparse_attn_kernel<D, Tin, kPad>>(kAttnThreads);
     if (resident <= 0) return hipErrorInvalidDevice;
-    // Heads per phase: enough groups that the phase, and above all the last one, keeps
-    // every CU busy with room for longest-first packing (three groups per resident
-    // workgroup), and at least two heads.
-    const int bh_total = B * heads;
-    int hpp = (3 * resident + gpb - 1) / gpb;
-    hpp = hpp < 2 ? 2 : (hpp > bh_total ? bh_total : hpp);
-    const int nphases = bh_total / hpp;  // the remainder joins the last phase
-    const int per_phase = hpp * gpb;
-    hipLaunchKernelGGL(attn_plan_order_kernel, dim3(nphases),
-                       dim3(1024), 0, stream, cost, ngroups, per_phase, nb, order);
-    const int grid = ngroups < resident ? ngroups : resident;
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kAttnThreads), 0, stream, (const Tin *)q,
+    const AttnSchedule sc =
+        launch_attn_plan(kv_nb, kv_inds, B, S, heads, Tt, Ht, Wt, resident, ws, stream);
+    hipLaunchKernelGGL(kernel, dim3(sc.grid), dim3(kAttnThreads), 0, stream, (const Tin *)q,
                        (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, Tt, Ht, Wt, Hv, Wv,
-                       gpb,
-                       ngroups, kv_nb, kv_inds, scale_log2, order, counter, lse);
+                       sc.groups_per_bh, sc.ngroups, kv_nb, kv_inds, scale_log2, sc.order,
+                       sc.counter, lse);
     return hipGetLastError();
 }
 

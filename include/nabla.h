@@ -289,6 +289,73 @@ nabla_status nabla_sparse_attn_bwd(const void *q, const void *k, const void *v, 
                                    const int32_t *kv_inds, float scale, void *dq, void *dk,
                                    void *dv, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * The quantized variant (the sibling "sla" backend page, the SageSLA forward: Q and K
+ * in INT8 with one scale per block after the mean of K over the sequence is
+ * subtracted, V in FP8 e4m3 with one scale per channel, then the block-sparse
+ * attention on the codes with FP8 weights).  Blocks are the 64-token blocks of the
+ * kv lists.
+ *
+ * Bytes of workspace nabla_quant_qkv needs: round_up(4 * B * heads * (S/64) * head_dim,
+ * 256) + round_up(4 * B * heads * ceil(S/1024) * head_dim, 256) (block sums of k, partial
+ * channel maxima of v).  0 if the sizes are invalid.
+ */
+size_t nabla_quant_qkv_workspace(int B, int S, int heads, int head_dim);
+/*
+ * Quantizes q, k, v ([B, S, heads, head_dim], bf16 or fp32, fractal order).  With
+ * nb = S/64, per (b, head):
+ *   k_mean[d] = (sum over blocks j of bs_j[d]) / S, bs_j[d] the sum of block j's 64
+ *               tokens (both sums sequential in fp32 from +0; IEEE fp32 division);
+ *   per block, for x = q and for x = k - k_mean (fp32):
+ *               scale = amax|x| / 127 (fp32), code = clamp(rint(x / scale), -127, 127)
+ *               (IEEE fp32 division, round half to even; amax = 0 gives scale 0, code 0);
+ *   per channel d of v, over all S tokens:
+ *               v_scale[d] = amax|v[:, d]| / 2.25, code = e4m3fn(v / v_scale[d]) (round to
+ *               nearest even; OCP FP8 e4m3, largest finite 448; scale 0 gives code 0).
+ * The codes and scales are exactly reproducible (fixed rounding and summation order).
+ * Outputs (device, caller-owned, must not overlap the inputs):
+ *   q8, k8:           [B, heads, nb, 64, head_dim] int8 (each block's rows in token order)
+ *   q_scale, k_scale: [B, heads, nb] fp32
+ *   v8:               [B, heads, nb, head_dim, 64] uint8 e4m3 codes (each block transposed)
+ *   v_scale, k_mean:  [B, heads, head_dim] fp32
+ * ws: device workspace of at least nabla_quant_qkv_workspace() bytes (overwritten).
+ * Errors: INVALID_ARG (NULL pointer, sizes < 1, S % 64 != 0); UNSUPPORTED (head_dim not
+ * 64 or 128); WORKSPACE (ws NULL or ws_bytes too small).
+ */
+nabla_status nabla_quant_qkv(const void *q, const void *k, const void *v, nabla_dtype dtype,
+                             int B, int S, int heads, int head_dim, int8_t *q8, float *q_scale,
+                             int8_t *k8, float *k_scale, uint8_t *v8, float *v_scale,
+                             float *k_mean, void *ws, size_t ws_bytes, void *stream);
+/* Bytes of workspace nabla_sparse_attn_fwd_q8 needs (its work schedule; the same formula
+ * as nabla_sparse_attn_workspace).  0 if the sizes or the grid are invalid. */
+size_t nabla_sparse_attn_q8_workspace(int B, int S, int heads, int Tt, int Ht, int Wt);
+/*
+ * Block-sparse attention on the codes of nabla_quant_qkv (INT8 Q K^T with exact int32
+ * sums, FP8 P V with fp32 accumulation).  For each (b, head, query block i) and query
+ * row, over the keys c of the blocks j listed in kv_inds[b, head, i, 0 .. kv_nb - 1]:
+ *   z_c  = scale * q_scale_i * k_scale_j * <q8_row, k8_c>
+ *   w_c  = e4m3(C * exp(z_c - m))   with m within log(4) of the row maximum (the
+ *          reference is raised lazily) and C * exp(z_c - m) <= 448
+ *   o[d] = v_scale[d] * (sum_c w_c v8_cd) / (sum_c w_c)
+ * A row with kv_nb == 0 gets o = 0.  The rounding of the weights depends on the
+ * reference, so o matches the plain definition (weights rounded against the row
+ * maximum) to within the weights' e4m3 rounding, not bit for bit.
+ * q8 .. v_scale: as written by nabla_quant_qkv.
+ * kv_nb, kv_inds, Tt, Ht, Wt: as for nabla_sparse_attn_fwd.
+ * scale:    softmax scale; <= 0 selects 1/sqrt(head_dim).
+ * o:        out [B, S, heads, head_dim] bf16.
+ * ws:       device workspace of at least nabla_sparse_attn_q8_workspace() bytes.
+ * Errors: INVALID_ARG (NULL pointer, sizes < 1, S % 64 != 0, NaN scale, a tile grid that
+ * does not multiply to S/64); UNSUPPORTED (head_dim not 64 or 128, or S/64 > 4096);
+ * WORKSPACE (ws NULL or ws_bytes too small).
+ */
+nabla_status nabla_sparse_attn_fwd_q8(const int8_t *q8, const float *q_scale, const int8_t *k8,
+                                      const float *k_scale, const uint8_t *v8,
+                                      const float *v_scale, int B, int S, int heads,
+                                      int head_dim, const int32_t *kv_nb, const int32_t *kv_inds,
+                                      float scale, int Tt, int Ht, int Wt, void *o, void *ws,
+                                      size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

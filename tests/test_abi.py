@@ -41,14 +41,16 @@ def test_exports_every_declared_symbol(L):
                           "nabla_sparse_attn_fwd_lse", "nabla_sparse_attn_bwd_workspace",
                           "nabla_sparse_attn_bwd", "nabla_block_mask_topk",
                           "nabla_block_mask_grid", "nabla_sparse_attn_workspace_grid",
-                          "nabla_sparse_attn_fwd_grid"}
+                          "nabla_sparse_attn_fwd_grid", "nabla_quant_qkv_workspace",
+                          "nabla_quant_qkv", "nabla_sparse_attn_q8_workspace",
+                          "nabla_sparse_attn_fwd_q8"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 5
+    assert L.nabla_abi_version() == 6
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"
@@ -204,6 +206,55 @@ def test_sparse_attn_bwd_validation(L):
     assert call(S=64 * 4097) == UNSUP
     assert call(ws=None) == WS
     assert call(wsb=L.nabla_sparse_attn_bwd_workspace(1, 8192, 8) - 1) == WS
+
+
+def test_quant_workspace_size(L):
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert L.nabla_quant_qkv_workspace(1, 61440, 16, 128) == \
+        rnd(4 * 16 * 960 * 128) + rnd(4 * 16 * 60 * 128)
+    assert L.nabla_quant_qkv_workspace(2, 640, 3, 64) == rnd(4 * 6 * 10 * 64) + rnd(4 * 6 * 1 * 64)
+    assert L.nabla_quant_qkv_workspace(1, 100, 16, 128) == 0
+    assert L.nabla_sparse_attn_q8_workspace(1, 61440, 16, 16, 6, 10) == \
+        L.nabla_sparse_attn_workspace(1, 61440, 16, 16, 6, 10)
+    assert L.nabla_sparse_attn_q8_workspace(1, 61440, 16, 16, 6, 9) == 0
+
+
+def test_quant_validation(L):
+    f = L.nabla_quant_qkv
+
+    def call(q=FAKE, v=FAKE, dt=BF16, S=8192, D=128, q8=FAKE, km=FAKE, ws=FAKE, wsb=1 << 40):
+        return f(q, FAKE, v, dt, 1, S, 8, D, q8, FAKE, FAKE, FAKE, FAKE, FAKE, km, ws, wsb, None)
+
+    assert call(q=None) == INVALID
+    assert call(v=None) == INVALID
+    assert call(q8=None) == INVALID
+    assert call(km=None) == INVALID
+    assert call(dt=7) == INVALID
+    assert call(S=100) == INVALID
+    assert call(D=96) == UNSUP
+    assert call(ws=None) == WS
+    assert call(wsb=L.nabla_quant_qkv_workspace(1, 8192, 8, 128) - 1) == WS
+
+
+def test_sparse_attn_q8_validation(L):
+    f = L.nabla_sparse_attn_fwd_q8
+
+    def call(q8=FAKE, v8=FAKE, S=8192, D=128, kv_nb=FAKE, scale=0.0, tiles=(8, 4, 4), o=FAKE,
+             ws=FAKE, wsb=1 << 40):
+        return f(q8, FAKE, FAKE, FAKE, v8, FAKE, 1, S, 8, D, kv_nb, FAKE, scale, *tiles, o, ws,
+                 wsb, None)
+
+    assert call(q8=None) == INVALID
+    assert call(v8=None) == INVALID
+    assert call(kv_nb=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(S=100) == INVALID
+    assert call(scale=math.nan) == INVALID
+    assert call(tiles=(8, 4, 3)) == INVALID
+    assert call(D=32) == UNSUP
+    assert call(S=64 * 4097, tiles=(0, 0, 0)) == UNSUP
+    assert call(ws=None) == WS
+    assert call(wsb=L.nabla_sparse_attn_q8_workspace(1, 8192, 8, 8, 4, 4) - 1) == WS
 
 
 def test_permute_and_sta_validation(L):
