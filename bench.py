@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "NABLA sparse attn fwd effective TFLOP/s + mask ms at 720p shape, 1 MI355X"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA (int8: 5000 TOP/s)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ATTN_SRC = [os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", f)
             for f in ("sparse_attn.hip", "attn_tile.h", "nabla_device.h")]
@@ -50,6 +51,9 @@ def parse():
     ap.add_argument("--topk", type=float, default=None, metavar="RATIO",
                     help="the top-k estimator variant with this ratio instead of NABLA's CDF cut "
                          "(a variant line, not the headline)")
+    ap.add_argument("--q8", action="store_true",
+                    help="the quantized variant: INT8 Q K^T / FP8 P V attention on the codes of "
+                         "nabla_quant_qkv (quantizer inside the step; a variant line)")
     ap.add_argument("--bwd", action="store_true",
                     help="the training pass instead: forward with lse, then the backward (one line)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -133,9 +137,10 @@ def cpu_baseline(w, q, k, v, sta_np, g_nb, rows, flops_per_pair):
     }
 
 
-def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None):
+def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False):
     """Run the path on workload w for `steps` timed steps; return the measurement dict.
-    With topk_ratio the top-k estimator variant replaces NABLA's CDF estimator."""
+    With topk_ratio the top-k estimator variant replaces NABLA's CDF estimator; with quant
+    the quantizer and the INT8 / FP8 attention replace the bf16 attention."""
     import ctypes
     dev = torch.device("cuda:0")
     q, k, v = qkv
@@ -158,6 +163,17 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None):
     sp = ctypes.c_void_p(stream.cuda_stream)
     ev = lambda: torch.cuda.Event(enable_timing=True)
     sta_p = P(sta) if w.sta is not None else None
+    if quant:
+        qz = {"q8": torch.empty((B, H, nb, 64, D), dtype=torch.int8, device=dev),
+              "k8": torch.empty((B, H, nb, 64, D), dtype=torch.int8, device=dev),
+              "v8": torch.empty((B, H, nb, D, 64), dtype=torch.uint8, device=dev)}
+        for n in ("qs", "ks"):
+            qz[n] = torch.empty((B, H, nb), dtype=torch.float32, device=dev)
+        for n in ("vs", "km"):
+            qz[n] = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+        ws_q = torch.empty(L.nabla_quant_qkv_workspace(B, S, H, D), dtype=torch.uint8, device=dev)
+        ws_q8 = torch.empty(L.nabla_sparse_attn_q8_workspace(B, S, H, *w.tiles), dtype=torch.uint8,
+                            device=dev)
 
     def check(rc, what):
         if rc != 0:
@@ -165,7 +181,7 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None):
 
     def step(rec=None):
         """One pass of the path; rec collects (start, end) event pairs per stage."""
-        e = [ev() for _ in range(5)] if rec is not None else None
+        e = [ev() for _ in range(6)] if rec is not None else None
         if e: e[0].record(stream)
         if w.sta is not None:
             check(L.nabla_sta_mask(P(sta), *w.tiles, *w.sta, sp), "sta")
@@ -184,7 +200,17 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None):
             check(L.nabla_block_mask_topk(P(qf), P(kf), dt_code, B, S, H, D, sta_p, topk_ratio,
                                           P(kv_nb), P(kv_inds), P(ws), ws.numel(), sp), "mask")
         if e: e[2].record(stream)
-        if w.padded:
+        if quant:
+            check(L.nabla_quant_qkv(P(qf), P(kf), P(vf), dt_code, B, S, H, D, P(qz["q8"]),
+                                    P(qz["qs"]), P(qz["k8"]), P(qz["ks"]), P(qz["v8"]),
+                                    P(qz["vs"]), P(qz["km"]), P(ws_q), ws_q.numel(), sp), "quant")
+        if e: e[3].record(stream)
+        if quant:
+            check(L.nabla_sparse_attn_fwd_q8(P(qz["q8"]), P(qz["qs"]), P(qz["k8"]), P(qz["ks"]),
+                                             P(qz["v8"]), P(qz["vs"]), B, S, H, D, P(kv_nb),
+                                             P(kv_inds), 0.0, *w.tiles, P(of), P(ws_q8),
+                                             ws_q8.numel(), sp), "attn q8")
+        elif w.padded:
             check(L.nabla_sparse_attn_fwd_grid(P(qf), P(kf), P(vf), dt_code, B, w.T, w.H, w.W, H,
                                                D, P(kv_nb), P(kv_inds), 0.0, P(of), None,
                                                P(ws_attn), ws_attn.numel(), sp), "attn")
@@ -192,11 +218,11 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None):
             check(L.nabla_sparse_attn_fwd(P(qf), P(kf), P(vf), dt_code, B, S, H, D, P(kv_nb),
                                           P(kv_inds), 0.0, *w.tiles, P(of), P(ws_attn),
                                           ws_attn.numel(), sp), "attn")
-        if e: e[3].record(stream)
+        if e: e[4].record(stream)
         check(L.nabla_fractal_permute(P(of), P(o_nat), dt_code, B, w.T, w.H, w.W, H, D, 1, sp),
               "unpermute")
         if e:
-            e[4].record(stream)
+            e[5].record(stream)
             rec.append(e)
 
     for _ in range(warmup):
@@ -216,13 +242,15 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None):
     flops_per_pair = 4.0 * 64 * 64 * D
     esz = 2 if tdt == torch.bfloat16 else 4
     mask_ms = float(np.mean(stage[:, 1]))
-    attn_ms = float(np.mean(stage[:, 2]))
+    quant_ms = float(np.mean(stage[:, 2]))
+    attn_ms = float(np.mean(stage[:, 3]))
     mask_bytes = 2.0 * B * S * H * D * esz + 4.0 * B * H * nb + 4.0 * pairs + nb * nb
     sta_pairs = int(sta.sum().item()) * B * H if w.sta is not None else 0
     return {
         "ms_per_step": wall * 1e3 / steps,
-        "perm_ms": float(np.mean(stage[:, 0] + stage[:, 3])),
+        "perm_ms": float(np.mean(stage[:, 0] + stage[:, 4])),
         "mask_ms": mask_ms,
+        "quant_ms": quant_ms,
         "attn_ms": attn_ms,
         "pairs": pairs,
         "flops_per_pair": flops_per_pair,
@@ -354,12 +382,16 @@ def main():
     w = synth.WORKLOADS[args.workload]
     print("[bench] %s" % w.describe(), file=sys.stderr, flush=True)
     q, k, v = synth.make_qkv(w)
-    m = measure(torch, nabla, w, (q, k, v), args.steps, args.warmup, topk_ratio=args.topk)
+    m = measure(torch, nabla, w, (q, k, v), args.steps, args.warmup, topk_ratio=args.topk,
+                quant=args.q8)
     attn_tflops = m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12
-    traffic = read_traffic(m["attn_flops"])
+    traffic = None if args.q8 else read_traffic(m["attn_flops"])
     metric = METRIC if args.topk is None else (
         "NABLA path with the top-k estimator (ratio %g): sparse attn fwd effective TFLOP/s + "
         "mask ms at %s shape, 1 MI355X" % (args.topk, w.name))
+    if args.q8:
+        metric = ("NABLA path with the quantized attention (INT8 Q K^T, FP8 P V): sparse attn fwd "
+                  "effective TFLOP/s + mask ms at %s shape, 1 MI355X" % w.name)
     out = {
         "metric": metric,
         "value": round(m["attn_flops"] / (m["ms_per_step"] * 1e-3) / 1e12, 3),
@@ -388,7 +420,13 @@ def main():
                      "kernel": "sparse_attn_kernel<128, bf16>",
                      "per_launch": {"flops": m["attn_flops"], "kept_pairs": m["pairs"]}},
     }
-    if not args.no_cpu_baseline and args.topk is None and not w.padded:
+    if args.q8:
+        out["dtype"] = "int8 (Q K^T) / fp8 e4m3 (P V)"
+        out["quant_ms"] = round(m["quant_ms"], 4)
+        out["roofline"].update({"peak": PEAK_FP8_TFLOPS,
+                                "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
+                                "kernel": "sparse_attn_q8_kernel<128>"})
+    if not args.no_cpu_baseline and args.topk is None and not args.q8 and not w.padded:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, m["sta_np"], m["g_nb"], args.cpu_rows,
                                            m["flops_per_pair"])

@@ -16,7 +16,7 @@
 // Outputs: q8, k8 [B][heads][nb][64][D] int8; q_scale, k_scale [B][heads][nb];
 // v8 [B][heads][nb][D][64] (each block transposed, the layout the attention's
 // P V product reads); v_scale, k_mean [B][heads][D].
-// All kernels are HBM-bound passes with coalesced 16-byte accesses.
+// All kernels are HBM-bound passes with coalesced 16-byte loads.
 #include "nabla_device.h"
 #include "nabla_launch.h"
 
@@ -24,49 +24,87 @@ namespace nabla {
 
 constexpr int kQuantChunk = 1024;  // tokens per partial channel maximum of v
 
+// Eight consecutive input elements widened to fp32 (exact for bf16 and fp32); one 16-byte
+// load for bf16, two for fp32.
+__device__ __forceinline__ void load8_f32(const bf16 *p, float (&x)[8]) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+}
+__device__ __forceinline__ void load8_f32(const float *p, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 // bs[item][d] = sequential fp32 sum of the block's 64 tokens, item = (b*heads + h)*nb + j.
-// One workgroup of D lanes per block; lane d walks the 64 rows (stride heads*D).
+// 256 lanes = 16 blocks x D/8 lanes of 8 channels (16-byte loads); each lane adds its 64
+// rows in token order, 16 rows of loads in flight at a time.
 template <int D, typename Tin>
-__global__ __launch_bounds__(D) void quant_ksum_kernel(const Tin *__restrict__ k,
-                                                       float *__restrict__ bs, int S, int heads) {
+__global__ __launch_bounds__(256) void quant_ksum_kernel(const Tin *__restrict__ k,
+                                                         float *__restrict__ bs, int S,
+                                                         int heads, int64_t items) {
+    constexpr int CG = D / 8;                // lanes per block
+    constexpr int BPW = 256 / CG;            // blocks per workgroup
     const int nb = S / kBlock;
-    const int64_t item = blockIdx.x;
+    const int64_t item = (int64_t)blockIdx.x * BPW + threadIdx.x / CG;
+    if (item >= items) return;
+    const int cg = threadIdx.x % CG;
     const int j = (int)(item % nb), bh = (int)(item / nb);
-    const int b = bh / heads, h = bh % heads, d = threadIdx.x;
+    const int b = bh / heads, h = bh % heads;
     const int64_t tok = (int64_t)heads * D;
-    const Tin *src = k + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D + d;
-    float x[kBlock];
+    const Tin *src = k + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D + 8 * cg;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r0 = 0; r0 < kBlock; r0 += 16) {
+        float x[16][8];
 #pragma unroll
-    for (int r = 0; r < kBlock; ++r) x[r] = (float)src[r * tok];
-    float acc = 0.0f;
+        for (int r = 0; r < 16; ++r) load8_f32(src + (int64_t)(r0 + r) * tok, x[r]);
 #pragma unroll
-    for (int r = 0; r < kBlock; ++r) acc += x[r];
-    bs[item * D + d] = acc;
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += x[r][i];
+    }
+    float *dst = bs + item * D + 8 * cg;
+    *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4 *>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
-// km[bh][d] = (sequential sum over blocks of bs) / S.  One workgroup of D lanes per (b, head).
+// km[bh][d] = (sequential sum over blocks of bs) / S.  One workgroup per (b, head) and
+// 32 channels: the 256 lanes stage runs of 128 blocks into LDS (coalesced), then 32 lanes
+// add them in block order.
 template <int D>
-__global__ __launch_bounds__(D) void quant_kmean_kernel(const float *__restrict__ bs,
-                                                        float *__restrict__ km, int S) {
+__global__ __launch_bounds__(256) void quant_kmean_kernel(const float *__restrict__ bs,
+                                                          float *__restrict__ km, int S) {
+    constexpr int RUN = 128;
+    __shared__ float stage[RUN][33];
     const int nb = S / kBlock;
-    const int64_t bh = blockIdx.x;
-    const int d = threadIdx.x;
-    const float *p = bs + bh * nb * D + d;
+    const int64_t bh = blockIdx.x / (D / 32);
+    const int d0 = 32 * (blockIdx.x % (D / 32));
+    const int tid = threadIdx.x;
+    const float *p = bs + bh * nb * D + d0;
     float acc = 0.0f;
-    for (int j = 0; j < nb; ++j) acc += p[(int64_t)j * D];
-    km[bh * D + d] = acc / (float)S;
+    for (int j0 = 0; j0 < nb; j0 += RUN) {
+        const int n = min(RUN, nb - j0);
+        __syncthreads();
+        for (int e = tid; e < n * 32; e += 256) stage[e >> 5][e & 31] = p[(int64_t)(j0 + (e >> 5)) * D + (e & 31)];
+        __syncthreads();
+        if (tid < 32)
+            for (int j = 0; j < n; ++j) acc += stage[j][tid];
+    }
+    if (tid < 32) km[bh * D + d0 + tid] = acc / (float)S;
 }
 
-__device__ __forceinline__ int8_t int8_code(float x, float scale) {
-    if (scale == 0.0f) return 0;
+__device__ __forceinline__ uint32_t int8_code(float x, float scale) {
+    if (scale == 0.0f) return 0u;
     const float r = fminf(fmaxf(__builtin_rintf(x / scale), -127.0f), 127.0f);
-    return (int8_t)(int)r;
+    return (uint32_t)(uint8_t)(int8_t)(int)r;
 }
 
 // One workgroup of 256 lanes per (block, tensor): blockIdx.y = 0 quantizes q, 1 quantizes
-// k - k_mean.  Lane t holds the 16-byte chunks e = r*256 + t (row e / (D/8)) in registers,
-// the block maximum comes from a wave reduction and LDS, then the codes are written as
-// 8-byte runs in the same row-major order.
+// k - k_mean.  Lane t holds the 8-element chunks e = r*256 + t (row e / (D/8)) in
+// registers, the block maximum comes from a wave reduction and LDS, then the codes are
+// written as 8-byte runs in the same row-major order.
 template <int D, typename Tin>
 __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q,
                                                        const Tin *__restrict__ k,
@@ -90,15 +128,21 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
         const int e = r * 256 + tid, row = e / CH, c = e % CH;
-        const Tin *p = src + row * tok + 8 * c;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float val = (float)p[i];
-            if (is_k) val = val - km[(int64_t)bh * D + 8 * c + i];
-            x[r][i] = val;
-            amax = fmaxf(amax, fabsf(val));
-        }
+        load8_f32(src + row * tok + 8 * c, x[r]);
     }
+    if (is_k) {
+        const int c = tid % CH;  // the same channel chunk for every r (256 % CH == 0)
+        float m[8];
+        load8_f32(km + (int64_t)bh * D + 8 * c, m);
+#pragma unroll
+        for (int r = 0; r < CPT; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[r][i] = x[r][i] - m[i];
+    }
+#pragma unroll
+    for (int r = 0; r < CPT; ++r)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[r][i]));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if ((tid & 63) == 0) wmax[tid >> 6] = amax;
@@ -113,27 +157,53 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q
         uint32_t w0 = 0, w1 = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            w0 |= (uint32_t)(uint8_t)int8_code(x[r][i], scale) << (8 * i);
-            w1 |= (uint32_t)(uint8_t)int8_code(x[r][4 + i], scale) << (8 * i);
+            w0 |= int8_code(x[r][i], scale) << (8 * i);
+            w1 |= int8_code(x[r][4 + i], scale) << (8 * i);
         }
         *reinterpret_cast<uint2 *>(dst + 8 * e) = make_uint2(w0, w1);
     }
 }
 
 // part[(bh * nchunk + c) * D + d] = max |v| over tokens [c*1024, (c+1)*1024) of channel d.
+// 256 lanes = 256 / (D/8) token rows x D/8 lanes of 8 channels (16-byte loads); the rows'
+// maxima meet in LDS.
 template <int D, typename Tin>
-__global__ __launch_bounds__(D) void quant_vmax_kernel(const Tin *__restrict__ v,
-                                                       float *__restrict__ part, int S,
-                                                       int heads, int nchunk) {
+__global__ __launch_bounds__(256) void quant_vmax_kernel(const Tin *__restrict__ v,
+                                                         float *__restrict__ part, int S,
+                                                         int heads, int nchunk) {
+    constexpr int CG = D / 8, ROWS = 256 / CG;
+    __shared__ float red[ROWS][D + 1];
     const int64_t item = blockIdx.x;  // bh * nchunk + c
     const int c = (int)(item % nchunk), bh = (int)(item / nchunk);
-    const int b = bh / heads, h = bh % heads, d = threadIdx.x;
+    const int b = bh / heads, h = bh % heads, tid = threadIdx.x;
+    const int cg = tid % CG, r0 = tid / CG;
     const int64_t tok = (int64_t)heads * D;
     const int t0 = c * kQuantChunk, t1 = min(S, t0 + kQuantChunk);
-    const Tin *src = v + (int64_t)b * S * tok + (int64_t)h * D + d;
-    float m = 0.0f;
-    for (int t = t0; t < t1; ++t) m = fmaxf(m, fabsf((float)src[(int64_t)t * tok]));
-    part[item * D + d] = m;
+    const Tin *src = v + (int64_t)b * S * tok + (int64_t)h * D + 8 * cg;
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t = t0 + r0; t < t1; t += 4 * ROWS) {
+        float x[4][8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (t + u * ROWS < t1)
+                load8_f32(src + (int64_t)(t + u * ROWS) * tok, x[u]);
+            else
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(x[u][i]));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) red[r0][8 * cg + i] = m[i];
+    __syncthreads();
+    if (tid < D) {
+        float mm = 0.0f;
+        for (int r = 0; r < ROWS; ++r) mm = fmaxf(mm, red[r][tid]);
+        part[item * D + tid] = mm;
+    }
 }
 
 // vs[bh][d] = (max over chunks) / 2.25.  One workgroup of D lanes per (b, head).
@@ -147,8 +217,9 @@ __global__ __launch_bounds__(D) void quant_vscale_kernel(const float *__restrict
     vs[bh * D + d] = m / 2.25f;
 }
 
-// One workgroup of 256 lanes per (b, head, block): the block's [64][D] values go to LDS,
-// then each lane writes 16-byte runs of the transposed codes (row d, keys 16c .. 16c+15).
+// One workgroup of 256 lanes per (b, head, block): the block's [64][D] values go to LDS
+// (16-byte loads), then each lane writes 16-byte runs of the transposed codes (row d,
+// keys 16c .. 16c+15).
 template <int D, typename Tin>
 __global__ __launch_bounds__(256) void quant_v_kernel(const Tin *__restrict__ v,
                                                       const float *__restrict__ vs,
@@ -162,14 +233,19 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const Tin *__restrict__ v,
     const int b = bh / heads, h = bh % heads, tid = threadIdx.x;
     const int64_t tok = (int64_t)heads * D;
     const Tin *src = v + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D;
-    for (int e = tid; e < kBlock * CH; e += 256) {
-        const int row = e / CH, c = e % CH;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tile[row][8 * c + i] = (float)src[row * tok + 8 * c + i];
+    for (int r = 0; r < kBlock * CH / 256; ++r) {
+        const int e = r * 256 + tid, row = e / CH, c = e % CH;
+        float x[8];
+        load8_f32(src + row * tok + 8 * c, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[row][8 * c + i] = x[i];
     }
     __syncthreads();
     uint8_t *dst = v8 + item * (kBlock * D);
-    for (int e = tid; e < D * 4; e += 256) {  // 4 runs of 16 keys per channel
+#pragma unroll
+    for (int r = 0; r < D * 4 / 256; ++r) {  // 4 runs of 16 keys per channel
+        const int e = r * 256 + tid;
         const int d = e >> 2, c = e & 3;
         const float sc = vs[(int64_t)bh * D + d];
         uint32_t w[4];
@@ -207,13 +283,15 @@ static hipError_t launch_quant_t(const void *q, const void *k, const void *v, in
                                             round256q((size_t)items * D * 4));
     const Tin *qi = static_cast<const Tin *>(q), *ki = static_cast<const Tin *>(k),
               *vi = static_cast<const Tin *>(v);
-    hipLaunchKernelGGL((quant_ksum_kernel<D, Tin>), dim3(items), dim3(D), 0, st, ki, bs, S,
-                       heads);
-    hipLaunchKernelGGL((quant_kmean_kernel<D>), dim3(B * heads), dim3(D), 0, st, bs, km, S);
+    constexpr int kBlocksPerWg = 256 / (D / 8);
+    hipLaunchKernelGGL((quant_ksum_kernel<D, Tin>), dim3((items + kBlocksPerWg - 1) / kBlocksPerWg),
+                       dim3(256), 0, st, ki, bs, S, heads, items);
+    hipLaunchKernelGGL((quant_kmean_kernel<D>), dim3(B * heads * (D / 32)), dim3(256), 0, st, bs,
+                       km, S);
     hipLaunchKernelGGL((quant_qk_kernel<D, Tin>), dim3(items, 2), dim3(256), 0, st, qi, ki, km,
                        q8, qs, k8, ks, S, heads);
-    hipLaunchKernelGGL((quant_vmax_kernel<D, Tin>), dim3(B * heads * nchunk), dim3(D), 0, st, vi,
-                       part, S, heads, nchunk);
+    hipLaunchKernelGGL((quant_vmax_kernel<D, Tin>), dim3(B * heads * nchunk), dim3(256), 0, st,
+                       vi, part, S, heads, nchunk);
     hipLaunchKernelGGL((quant_vscale_kernel<D>), dim3(B * heads), dim3(D), 0, st, part, vs,
                        nchunk);
     hipLaunchKernelGGL((quant_v_kernel<D, Tin>), dim3(items), dim3(256), 0, st, vi, vs, v8, S,

@@ -24,6 +24,10 @@
 //     64-lane ds_read_b128 of 1 KiB of consecutive bytes (no bank conflicts); the
 //     global -> LDS loads (global_load_lds_dwordx4) gather the 16-byte chunks into
 //     that order.
+//   * Every wave runs one tile behind in its softmax: at each step it issues the score
+//     MFMAs of the new tile and, while they run, does the softmax and P V of the tile
+//     it listed at the step before, so the VALU work overlaps its own MFMAs (and the
+//     other wave's on the SIMD).
 //   * Softmax in fp32, log2 domain, with a lazy reference max: the reference m is
 //     raised to the row max only when a tile's max exceeds it by more than 2 (and on
 //     the row's first tile), so the weights 2^(s - m) stay <= 4 and c = 112 keeps the
@@ -47,6 +51,7 @@ template <int D>
 struct AttnQ8Shared {
     int8_t ks[kQStages][kBlock * D];   // K tiles, MFMA-operand order
     uint8_t vs[kQStages][D * kBlock];  // V^T tiles (e4m3 codes), MFMA-operand order
+    int8_t qs[kAttnWaves][32 * D];     // each wave's 32 query rows, MFMA-operand order
     uint64_t qmask[kGroup][kMaxWords];
     uint16_t ulist[kMaxWords * 64];    // the union of the members' lists, ascending
     uint8_t umem[kMaxWords * 64];      // bit s: member s lists that block
@@ -60,6 +65,7 @@ __device__ __forceinline__ int imax16(const i32x16 &s) {
     for (int j = 2; j < 16; ++j) x = max(x, s[j]);
     return x;
 }
+
 
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
@@ -174,13 +180,16 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     const int myblk = member[slot];
     const int64_t qrow = (int64_t)bh * nb + (myblk < 0 ? 0 : myblk);
     const int qtok = (myblk < 0 ? 0 : myblk) * kBlock + (w & 1) * 32 + l32;
-    // Q^T as B operands: lane (n, hi), k-step ks: dims 32 ks + 16 hi .. + 15 of row n
-    i32x4 qf[KS];
+    // Q^T as B operands, kept in this wave's LDS slice: lane (n, hi), k-step ks holds dims
+    // 32 ks + 16 hi .. + 15 of row n, at ((ks * 64) + lane) * 16
+    char *qlds = reinterpret_cast<char *>(sh.qs[w]);
     float qscale = 0.0f;
     if (myblk >= 0) {
         const int8_t *qr = q8 + (qrow * kBlock + (w & 1) * 32 + l32) * D + 16 * hi;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const i32x4 *>(qr + 32 * ks);
+        for (int ks = 0; ks < KS; ++ks)
+            *reinterpret_cast<i32x4 *>(qlds + (ks * 64 + lane) * 16) =
+                *reinterpret_cast<const i32x4 *>(qr + 32 * ks);
         qscale = qsc[qrow] * scale_log2;
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): retire the Q loads before the walk
@@ -214,23 +223,50 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     float m_ref = 0.0f;           // reference max of the row, log2 units
     bool m_valid = false;
 
-    // scores of the tile in `stage` -> packed e4m3 weights pb (B operand of P V: byte t of
-    // lane (n, hi) is key 32 hi + t); O and the row sum rescaled when the reference moves
-    auto score_softmax = [&](int stage, i32x8 &pb, float unit) {
+    i32x8 pb = {0, 0, 0, 0, 0, 0, 0, 0};     // packed weights (every byte rewritten per tile)
+    bool pend = false;      // a listed tile's scores wait for their softmax and P V
+    int pend_stage = 0;
+    float pend_unit = 0.0f;
+
+    // K fragments of the tile in `stage`: (mt, ks) is one contiguous 1 KiB read
+    auto kread = [&](int stage, i32x4 (&kf)[2][KS]) {
         const char *kb = reinterpret_cast<const char *>(sh.ks[stage]);
-        i32x16 sacc[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) sacc[mt][j] = 0;
+            for (int ks = 0; ks < KS; ++ks)
+                kf[mt][ks] = *reinterpret_cast<const i32x4 *>(kb + ((mt * KS + ks) * 64 + lane) * 16);
+    };
+    // V^T fragments of d tiles dt0 .. dt0 + DT/2 - 1 of the tile in `stage`: each d tile is
+    // two contiguous 1 KiB reads
+    constexpr int DH = DT / 2;
+    auto vread = [&](int stage, int dt0, i32x8 (&va)[DH]) {
+        const char *vb = reinterpret_cast<const char *>(sh.vs[stage]);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const i32x4 kf =
-                    *reinterpret_cast<const i32x4 *>(kb + ((mt * KS + ks) * 64 + lane) * 16);
-                sacc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[ks], sacc[mt], 0, 0, 0);
-            }
+        for (int u = 0; u < DH; ++u) {
+            const int dt = dt0 + u;
+            const i32x4 a0 = *reinterpret_cast<const i32x4 *>(vb + ((dt * 2) * 64 + lane) * 16);
+            const i32x4 a1 = *reinterpret_cast<const i32x4 *>(vb + ((dt * 2 + 1) * 64 + lane) * 16);
+            va[u] = (i32x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
         }
-        const float tmax = (float)max(imax16(sacc[0]), imax16(sacc[1])) * unit;
+    };
+    // scores S^T = K Q^T of one tile (int32, exact)
+    auto qk = [&](const i32x4 (&kf)[2][KS], i32x16 (&sacc)[2]) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const i32x4 qf = *reinterpret_cast<const i32x4 *>(qlds + (ks * 64 + lane) * 16);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                sacc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[mt][ks], qf,
+                                                                 ks == 0 ? i32x16{} : sacc[mt],
+                                                                 0, 0, 0);
+        }
+    };
+    // scores -> packed e4m3 weights pb (B operand of P V: byte t of lane (n, hi) is key
+    // 32 hi + t); O and the row sum rescaled when the reference moves
+    auto softmax = [&](const i32x16 (&sacc)[2], float unit) {
+        const int imax = max(imax16(sacc[0]), imax16(sacc[1]));
+        const float tmax = (float)imax * unit;
         const float rm = fmaxf(tmax, __shfl_xor(tmax, 32));  // the row's tile max
         if (__builtin_amdgcn_ballot_w64(!m_valid || rm > m_ref + kQLazy) != 0ull) {
             const bool need = !m_valid || rm > m_ref + kQLazy;  // same in lanes l, l ^ 32
@@ -250,31 +286,33 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 f[i] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[mt][j0 + i], unit, off));
-            int pk = 0;
-            pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], pk, false);
-            pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pk, true);
-            pb[q4] = pk;
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], pb[q4], false);
+            pb[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pk, true);
         }
     };
-    // O^T += V^T P^T and the row sums, for the tile in `stage`
-    auto pv_tile = [&](int stage, const i32x8 &pb) {
-        const char *vb = reinterpret_cast<const char *>(sh.vs[stage]);
+    // O^T += V^T P^T for d tiles dt0 .. dt0 + DT/2 - 1
+    auto pv = [&](int dt0, const i32x8 (&va)[DH], const i32x8 &w8) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const i32x4 a0 = *reinterpret_cast<const i32x4 *>(vb + ((dt * 2) * 64 + lane) * 16);
-            const i32x4 a1 = *reinterpret_cast<const i32x4 *>(vb + ((dt * 2 + 1) * 64 + lane) * 16);
-            const i32x8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            oacc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, oacc[dt], 0, 0, 0, 0,
-                                                                      0, 0);
-        }
+        for (int u = 0; u < DH; ++u)
+            oacc[dt0 + u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[u], w8, oacc[dt0 + u],
+                                                                           0, 0, 0, 0, 0, 0);
+    };
+    // the pending tile (scores in sold): softmax, then P V and the row sums; the first half
+    // of the V^T fragments is read before the softmax, the second half after it
+    auto finish = [&](const i32x16 (&sold)[2]) {
+        i32x8 va[DH];
+        vread(pend_stage, 0, va);
+        softmax(sold, pend_unit);
+        pv(0, va, pb);
+        vread(pend_stage, DH, va);
+        pv(DH, va, pb);
         lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 0, 0, 0, 0, 0, 0);
     };
-    i32x8 pb_prev;            // packed weights of the previous tile (waves 4-7)
-    bool prev_listed = false; // waves 4-7: the previous tile's P V is still to do
-    int prev_stage = 0;
-
     // ---- the walk over union tiles u_0, u_1, ...; u_k lives in LDS stage k % 4.
-    // Step k: start loading u_{k+2}, compute, make sure u_{k+1} has landed, barrier.
+    // Step k: start loading u_{k+2}; issue the score MFMAs of u_k (if this wave's block
+    // lists it); while they run, the softmax and P V of the wave's pending tile (the one
+    // it listed at step k-1, still in its stage); make sure u_{k+1} has landed; barrier.
+    // The ring holds u_{k-1} .. u_{k+2}, so the pending tile's V^T is still in LDS.
     if (U > 0) {
         issue(sh.ulist[0], 0);
         if (U > 1) issue(sh.ulist[1], 1);
@@ -285,7 +323,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     int pf_blk = U > 2 ? sh.ulist[2] : -1;
     int pf_mem = U > 0 ? sh.umem[0] : 0;
     int pf_j = U > 0 ? sh.ulist[0] : 0;
-    for (int kk = 0, stage = 0; kk < U; ++kk, stage = (stage + 1) & (kQStages - 1)) {
+    // one step; the scores of u_k go to snew, the pending tile's are in sold
+    auto step = [&](int kk, int stage, i32x16 (&snew)[2], const i32x16 (&sold)[2]) {
         const int n2 = __builtin_amdgcn_readfirstlane(pf_blk);  // u_{k+2}
         const int memk = __builtin_amdgcn_readfirstlane(pf_mem);
         const int jk = __builtin_amdgcn_readfirstlane(pf_j);     // u_k
@@ -295,25 +334,37 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
         const int stage2 = (stage + 2) & (kQStages - 1);
         if (n2 >= 0) issue(n2, stage2);
         const bool mine = myblk >= 0 && ((memk >> slot) & 1);
-        // waves 4-7 run one P V behind waves 0-3 (the two waves of a SIMD are half a tile
-        // apart: one's softmax runs under the other's MFMAs)
-        const bool delayed = w >= 4;
-        if (delayed && prev_listed) pv_tile(prev_stage, pb_prev);
         if (mine) {
-            const float unit = qscale * ksc[(int64_t)bh * nb + jk];
-            i32x8 pb;
-            score_softmax(stage, pb, unit);
-            if (delayed)
-                pb_prev = pb;
-            else
-                pv_tile(stage, pb);
+            i32x4 kf[2][KS];
+            kread(stage, kf);
+            qk(kf, snew);
         }
-        prev_listed = delayed && mine;
-        prev_stage = stage;
+        __builtin_amdgcn_sched_barrier(0);
+        if (pend) finish(sold);
+        pend = mine;
+        pend_stage = stage;
+        pend_unit = qscale * ksc[(int64_t)bh * nb + jk];
         settle(n2 >= 0);
         __syncthreads();  // u_{k+1} has landed; everyone is done with u_{k-1}'s stage
+    };
+    // unrolled by two so that the two score buffers swap roles without copies
+    i32x16 sa[2], sb[2];
+    int kk = 0, stage = 0;
+    for (; kk + 1 < U; kk += 2, stage = (stage + 2) & (kQStages - 1)) {
+        step(kk, stage, sa, sb);
+        step(kk + 1, (stage + 1) & (kQStages - 1), sb, sa);
     }
-    if (prev_listed) pv_tile(prev_stage, pb_prev);
+    bool last_in_a = false;  // the pending scores (if any) after the walk: in sa or sb
+    if (kk < U) {
+        step(kk, stage, sa, sb);
+        last_in_a = true;
+    }
+    if (pend) {  // the last listed tile
+        if (last_in_a)
+            finish(sa);
+        else
+            finish(sb);
+    }
 
     if (myblk >= 0) {
         const float lsum = __shfl(lacc[0], l32);  // row 0 of the sum product, lane n
