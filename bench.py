@@ -35,6 +35,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 ATTN_SRC = [os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", f)
             for f in ("sparse_attn.hip", "attn_tile.h", "nabla_device.h")]
 PMC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_720p_pmc.txt")
+Q8_SRC = [os.path.join(ROOT, "block_sparse_attention_fractal_amd", "csrc", f)
+          for f in ("sparse_attn_q8.hip", "attn_tile.h", "nabla_device.h")]
+Q8_PMC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_q8_720p_pmc.txt")
 
 
 def parse():
@@ -70,16 +73,16 @@ def src_sha(paths):
     return h.hexdigest()[:16]
 
 
-def read_traffic(launch_flops_bytes):
+def read_traffic(pmc_file=PMC_FILE, src=ATTN_SRC):
     """HBM bytes per attention launch from the committed PMC summary, if it matches this source."""
-    if not os.path.exists(PMC_FILE):
+    if not os.path.exists(pmc_file):
         return None
     kv = {}
-    for line in open(PMC_FILE):
+    for line in open(pmc_file):
         if "=" in line and not line.lstrip().startswith("#"):
             a, b = line.split("=", 1)
             kv[a.strip()] = b.strip()
-    if kv.get("kernel_sha") != src_sha(ATTN_SRC):
+    if kv.get("kernel_sha") != src_sha(src):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -385,7 +388,7 @@ def main():
     m = measure(torch, nabla, w, (q, k, v), args.steps, args.warmup, topk_ratio=args.topk,
                 quant=args.q8)
     attn_tflops = m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12
-    traffic = None if args.q8 else read_traffic(m["attn_flops"])
+    traffic = read_traffic(Q8_PMC_FILE, Q8_SRC) if args.q8 else read_traffic()
     metric = METRIC if args.topk is None else (
         "NABLA path with the top-k estimator (ratio %g): sparse attn fwd effective TFLOP/s + "
         "mask ms at %s shape, 1 MI355X" % (args.topk, w.name))

@@ -31,6 +31,9 @@
  *              blocks at -inf; scale 1/sqrt(D).
  *   - training pass: lse (natural log) and the gradients dq, dk, dv of that
  *              dense masked softmax attention, fp64.
+ *   - quantized variant (the sibling "sla" page, SageSLA forward): INT8 q and
+ *              k - mean(k) per block, FP8 e4m3 v per channel (see O12 below),
+ *              fp64 attention with FP8 weights e4m3(448 exp(z - rowmax)).
  */
 #include <math.h>
 #include <stdint.h>
