@@ -238,22 +238,40 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
         if (u + 1 < n) issue(list[u + 1], st ^ 1);
         const char *kb = reinterpret_cast<const char *>(ksh[st]);
         const char *vb = reinterpret_cast<const char *>(vsh[st]);
-        // S^T - lse (log2 units) and dP^T for the two 32-key halves
+        // S^T - lse (log2 units) and dP^T for the two 32-key halves.  The K and V row
+        // fragments are read KLA k-steps ahead of their MFMAs (a ring of KLA + 1 k-steps;
+        // the sched_barrier fences keep the reads from sinking next to their uses).
         f32x16 sacc[2], pacc[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             sacc[mt] = splat16(-lse2);
             pacc[mt] = splat16(-dl);
         }
+        constexpr int KLA = 3;
+        bf16x8 fr[KLA + 1][4];
+        auto fread = [&](int ks) {
+            fr[ks & KLA][0] = rfrag<D>(kb, kv0, hi, ks);
+            fr[ks & KLA][1] = rfrag<D>(kb, kv1, hi, ks);
+            fr[ks & KLA][2] = rfrag<D>(vb, kv0, hi, ks);
+            fr[ks & KLA][3] = rfrag<D>(vb, kv1, hi, ks);
+        };
+#pragma unroll
+        for (int ks = 0; ks < KLA; ++ks) fread(ks);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 k0 = rfrag<D>(kb, kv0, hi, ks), k1 = rfrag<D>(kb, kv1, hi, ks);
-            const bf16x8 v0 = rfrag<D>(vb, kv0, hi, ks), v1 = rfrag<D>(vb, kv1, hi, ks);
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], sacc[1], 0, 0, 0);
-            pacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, df[ks], pacc[0], 0, 0, 0);
-            pacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, df[ks], pacc[1], 0, 0, 0);
+            if (ks + KLA < KS) fread(ks + KLA);
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8(&f)[4] = fr[ks & KLA];
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], qf[ks], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[1], qf[ks], sacc[1], 0, 0, 0);
+            pacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[2], df[ks], pacc[0], 0, 0, 0);
+            pacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[3], df[ks], pacc[1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // the first d tile's K^T fragments, read under the VALU work below
+        bf16x8 kt[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kt[0][kk] = tfrag<D>(kb, lane, 0, kk);
         // dS^T = P^T (dP^T - Delta), packed: registers 8p .. 8p+7 = 16 consecutive keys
         bf16x8 ds[2][2];
 #pragma unroll
@@ -261,13 +279,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 ds[mt][j >> 3][j & 7] = (bf16)(__builtin_amdgcn_exp2f(sacc[mt][j]) * pacc[mt][j]);
-        // dQ^T += K^T dS^T
+        // dQ^T += K^T dS^T; each next d tile's K^T fragments are read under the current
+        // one's MFMAs
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt) {
+            if (dt + 1 < DT) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) kt[(dt + 1) & 1][kk] = tfrag<D>(kb, lane, dt + 1, kk);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(kb, lane, dt, kk),
-                                                                  ds[kk >> 1][kk & 1], acc[dt], 0, 0, 0);
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[dt & 1][kk], ds[kk >> 1][kk & 1],
+                                                                  acc[dt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         vm_wait<0>();
         __syncthreads();  // tile u + 1 has landed; everyone is done with tile u's stage
     }
@@ -367,14 +393,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
             sacc[mt] = splat16(0.0f);
             pacc[mt] = splat16(0.0f);
         }
+        // Q and dO row fragments read KLA k-steps ahead of their MFMAs (as in dq)
+        constexpr int KLA = 3;
+        bf16x8 fr[KLA + 1][4];
+        auto fread = [&](int ks) {
+            fr[ks & KLA][0] = rfrag<D>(qb, qr0, hi, ks);
+            fr[ks & KLA][1] = rfrag<D>(qb, qr1, hi, ks);
+            fr[ks & KLA][2] = rfrag<D>(db, qr0, hi, ks);
+            fr[ks & KLA][3] = rfrag<D>(db, qr1, hi, ks);
+        };
+#pragma unroll
+        for (int ks = 0; ks < KLA; ++ks) fread(ks);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a0 = rfrag<D>(qb, qr0, hi, ks), a1 = rfrag<D>(qb, qr1, hi, ks);
-            const bf16x8 g0 = rfrag<D>(db, qr0, hi, ks), g1 = rfrag<D>(db, qr1, hi, ks);
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, kf[ks], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, kf[ks], sacc[1], 0, 0, 0);
-            pacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g0, vf[ks], pacc[0], 0, 0, 0);
-            pacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g1, vf[ks], pacc[1], 0, 0, 0);
+            if (ks + KLA < KS) fread(ks + KLA);
+            __builtin_amdgcn_sched_barrier(0);
+            const bf16x8(&f)[4] = fr[ks & KLA];
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], kf[ks], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[1], kf[ks], sacc[1], 0, 0, 0);
+            pacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[2], vf[ks], pacc[0], 0, 0, 0);
+            pacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[3], vf[ks], pacc[1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // the first d tile's dO^T and Q^T fragments, read under the VALU work below
+        bf16x8 gt[2][4], qt[2][4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            gt[0][kk] = tfrag<D>(db, lane, 0, kk);
+            qt[0][kk] = tfrag<D>(qb, lane, 0, kk);
         }
         // register 8p + e of half mt holds query 32 mt + 16 p + 8 hi + e
         bf16x8 pp[2][2], dd[2][2];
@@ -396,16 +442,27 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
                     dd[mt][p][e] = (bf16)(pr * (pacc[mt][8 * p + e] - eq[e]));
                 }
             }
-        // dV^T += dO^T P and dK^T += Q^T dS
+        // dV^T += dO^T P and dK^T += Q^T dS; each next d tile's fragments are read under
+        // the current one's MFMAs
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt) {
+            if (dt + 1 < DT) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    gt[(dt + 1) & 1][kk] = tfrag<D>(db, lane, dt + 1, kk);
+                    qt[(dt + 1) & 1][kk] = tfrag<D>(qb, lane, dt + 1, kk);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(db, lane, dt, kk),
-                                                                  pp[kk >> 1][kk & 1], dva[dt], 0, 0, 0);
-                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tfrag<D>(qb, lane, dt, kk),
-                                                                  dd[kk >> 1][kk & 1], dka[dt], 0, 0, 0);
+                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt[dt & 1][kk], pp[kk >> 1][kk & 1],
+                                                                  dva[dt], 0, 0, 0);
+                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[dt & 1][kk], dd[kk >> 1][kk & 1],
+                                                                  dka[dt], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         vm_wait<0>();
         if (u + 1 < n) land(st ^ 1);
         __syncthreads();  // tile u + 1 has landed; everyone is done with tile u's stage
