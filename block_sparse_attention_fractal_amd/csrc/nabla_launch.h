@@ -54,6 +54,10 @@ struct AttnSchedule {
     int32_t *order, *counter;
 };
 int attn_groups_per_bh(int S, int Tt, int Ht, int Wt);
+// order[0 .. n) = 0 .. n-1 arranged longest first (by cost[], each in [0, maxcost], maxcost
+// < 4096) within phases of per_phase consecutive items (the remainder joins the last phase).
+hipError_t launch_longest_first(const int32_t *cost, int n, int per_phase, int maxcost,
+                                int32_t *order, hipStream_t stream);
 size_t attn_schedule_bytes(int B, int S, int heads, int Tt, int Ht, int Wt);
 // resident: workgroups of the walk kernel the device holds at once (sets the phase size).
 AttnSchedule launch_attn_plan(const int32_t *kv_nb, const int32_t *kv_inds, int B, int S,

@@ -588,6 +588,14 @@ size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int 
     return attn_schedule_bytes(B, S, heads, Tt, Ht, Wt);
 }
 
+hipError_t launch_longest_first(const int32_t *cost, int n, int per_phase, int maxcost,
+                                int32_t *order, hipStream_t stream) {
+    const int nphases = n / per_phase > 0 ? n / per_phase : 1;
+    hipLaunchKernelGGL(attn_plan_order_kernel, dim3(nphases), dim3(1024), 0, stream, cost, n,
+                       per_phase < n ? per_phase : n, maxcost, order);
+    return hipGetLastError();
+}
+
 AttnSchedule launch_attn_plan(const int32_t *kv_nb, const int32_t *kv_inds, int B, int S,
                               int heads, int Tt, int Ht, int Wt, int resident, void *ws,
                               hipStream_t stream) {

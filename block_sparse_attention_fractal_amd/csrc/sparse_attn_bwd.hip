@@ -176,13 +176,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     bf16 *__restrict__ dq, int S, int heads, const int32_t *__restrict__ kv_nb,
-    const int32_t *__restrict__ kv_inds, float scale, float scale_log2) {
+    const int32_t *__restrict__ kv_inds, const int32_t *__restrict__ order, float scale,
+    float scale_log2) {
     constexpr int KS = D / 16, DT = D / 32, CPT = kBlock * D / 8 / kBwdThreads;
     __shared__ __attribute__((aligned(1024))) bf16 ksh[2][kBlock * D];
     __shared__ __attribute__((aligned(1024))) bf16 vsh[2][kBlock * D];
 
     const int nb = S / kBlock;
-    const int64_t row = blockIdx.x;
+    const int64_t row = order[blockIdx.x];  // longest lists first, within phases of heads
     const int bh = (int)(row / nb), i = (int)(row % nb);
     const int b = bh / heads, h = bh % heads;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
@@ -308,8 +309,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     bf16 *__restrict__ dk, bf16 *__restrict__ dv, int S, int heads,
-    const int32_t *__restrict__ q_nb, const int32_t *__restrict__ q_inds, float scale,
-    float scale_log2) {
+    const int32_t *__restrict__ q_nb, const int32_t *__restrict__ q_inds,
+    const int32_t *__restrict__ order, float scale, float scale_log2) {
     constexpr int KS = D / 16, DT = D / 32, CPT = kBlock * D / 8 / kBwdThreads;
     __shared__ __attribute__((aligned(1024))) bf16 qsh[2][kBlock * D];
     __shared__ __attribute__((aligned(1024))) bf16 dsh[2][kBlock * D];
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(16))) float esh[2][kBlock];  // Delta
 
     const int nb = S / kBlock;
-    const int64_t row = blockIdx.x;
+    const int64_t row = order[blockIdx.x];  // longest lists first, within phases of heads
     const int bh = (int)(row / nb), j = (int)(row % nb);
     const int b = bh / heads, h = bh % heads;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
@@ -474,11 +475,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
 // ---- host side
 
 // Workspace: [Delta: B*heads*S fp32 | q_nb: B*heads*nb | q_inds: B*heads*nb*nb int32 |
-// tmat: B*heads*nb*nb bytes], each part 256-byte aligned.
+// tmat: B*heads*nb*nb bytes | dq order, dk/dv order: B*heads*nb int32 each], each part
+// 256-byte aligned.
 size_t sparse_attn_bwd_workspace_bytes(int B, int S, int heads) {
     const size_t bh = (size_t)B * heads, nb = (size_t)S / kBlock;
     return round256(bh * S * 4) + round256(bh * nb * 4) + round256(bh * nb * nb * 4) +
-           round256(bh * nb * nb);
+           round256(bh * nb * nb) + 2 * round256(bh * nb * 4);
 }
 
 template <int D>
@@ -497,6 +499,10 @@ static hipError_t launch_bwd_t(const bf16 *q, const bf16 *k, const bf16 *v, cons
     p += round256(BH * nb * nb * 4);
     uint8_t *tmat = reinterpret_cast<uint8_t *>(p);
     const int64_t tbytes = (int64_t)round256(BH * nb * nb);
+    p += tbytes;
+    int32_t *order_q = reinterpret_cast<int32_t *>(p);
+    p += round256(BH * nb * 4);
+    int32_t *order_k = reinterpret_cast<int32_t *>(p);
 
     const int64_t nrows = (int64_t)B * S * heads;
     const int64_t dgrid = (nrows * (D / 8) + 255) / 256;
@@ -511,11 +517,23 @@ static hipError_t launch_bwd_t(const bf16 *q, const bf16 *k, const bf16 *v, cons
                        nb, tmat);
     hipLaunchKernelGGL(bwd_tlist_compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, tmat,
                        nb, (int64_t)rows, q_nb, q_inds);
+    // Launch orders: longest lists first within phases of a few heads (enough rows for
+    // three rounds of the resident workgroups), so that the long rows do not start last
+    // and the K/V (or Q/dO) tiles read together stay in the caches.
+    const int resident = resident_workgroups<bwd_dq_kernel<D>>(kBwdThreads);
+    if (resident <= 0) return hipErrorInvalidDevice;
+    int hpp = (3 * resident + nb - 1) / nb;
+    hpp = hpp < 1 ? 1 : (hpp > (int)BH ? (int)BH : hpp);
+    hipError_t e = launch_longest_first(kv_nb, (int)rows, hpp * nb, nb, order_q, stream);
+    if (e != hipSuccess) return e;
+    e = launch_longest_first(q_nb, (int)rows, hpp * nb, nb, order_k, stream);
+    if (e != hipSuccess) return e;
     const float scale_log2 = scale * kLog2e;
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(rows), dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                       lse, delta, dq, S, heads, kv_nb, kv_inds, scale, scale_log2);
+                       lse, delta, dq, S, heads, kv_nb, kv_inds, order_q, scale, scale_log2);
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(rows), dim3(kBwdThreads), 0, stream, q, k, v,
-                       dout, lse, delta, dk, dv, S, heads, q_nb, q_inds, scale, scale_log2);
+                       dout, lse, delta, dk, dv, S, heads, q_nb, q_inds, order_k, scale,
+                       scale_log2);
     return hipGetLastError();
 }
 

@@ -255,8 +255,9 @@ nabla_status nabla_sparse_attn_fwd_grid(const void *q, const void *k, const void
 /*
  * Bytes of workspace nabla_sparse_attn_bwd needs: round_up(4 B heads S, 256) +
  * round_up(4 B heads nb, 256) + round_up(4 B heads nb^2, 256) + round_up(B heads nb^2,
- * 256), nb = S/64 (row deltas, the transposed lists and their byte matrix).  0 if the
- * sizes are invalid.
+ * 256) + 2 round_up(4 B heads nb, 256), nb = S/64 (row deltas, the transposed lists and
+ * their byte matrix, the two gradient kernels' launch orders).  0 if the sizes are
+ * invalid.
  */
 size_t nabla_sparse_attn_bwd_workspace(int B, int S, int heads);
 
