@@ -267,8 +267,9 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False):
     }
 
 
-def sweep(torch, nabla, synth, steps, warmup):
-    """The sparsity sweep on the 720p shape and the long clip: one JSON line per run."""
+def sweep(torch, nabla, synth, steps, warmup, quant=False):
+    """The sparsity sweep on the 720p shape and the long clip: one JSON line per run (with
+    quant, the quantizer and the quantized attention in place of the bf16 attention)."""
     cache = {}
     runs = synth.sweep_workloads() + [synth.WORKLOADS["long"]]
     for w in runs:
@@ -277,13 +278,15 @@ def sweep(torch, nabla, synth, steps, warmup):
             cache.clear()
             print("[bench] generating %s" % w.describe(), file=sys.stderr, flush=True)
             cache[key] = synth.make_qkv(w)
-        m = measure(torch, nabla, w, cache[key], steps, warmup)
-        line = {"workload": w.describe(), "density": round(m["density"], 5),
+        m = measure(torch, nabla, w, cache[key], steps, warmup, quant=quant)
+        line = {"workload": w.describe(), "attention": "int8/fp8" if quant else "bf16",
+                "density": round(m["density"], 5),
                 "sta_density": round(m["sta_density"], 5), "kept_pairs": m["pairs"],
                 "mask_ms": round(m["mask_ms"], 4), "mask_gbs": round(m["mask_gbs"], 1),
                 "attn_ms": round(m["attn_ms"], 4),
                 "attn_tflops": round(m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12, 2),
                 "permute_ms": round(m["perm_ms"], 4), "ms_per_step": round(m["ms_per_step"], 4),
+                **({"quant_ms": round(m["quant_ms"], 4)} if quant else {}),
                 "value": round(m["attn_flops"] / (m["ms_per_step"] * 1e-3) / 1e12, 3)}
         print(json.dumps(line), flush=True)
 
@@ -374,7 +377,7 @@ def main():
     import block_sparse_attention_fractal_amd as nabla
     from block_sparse_attention_fractal_amd import synth
     if args.sweep:
-        sweep(torch, nabla, synth, args.steps, args.warmup)
+        sweep(torch, nabla, synth, args.steps, args.warmup, quant=args.q8)
         return
     if args.bwd:
         w = synth.WORKLOADS[args.workload]
