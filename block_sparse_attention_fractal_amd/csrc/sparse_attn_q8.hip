@@ -46,6 +46,11 @@ typedef int i32x16 __attribute__((ext_vector_type(16)));
 constexpr int kQStages = 4;
 constexpr float kQLazy = 2.0f;                 // log2 units the weights may exceed the reference
 constexpr float kQLog2C = 6.807354922057604f;  // log2(112): 112 * 2^2 = 448, the largest e4m3
+// The INT8 score products start from this bias: the int32 result acc + 0x4B400000, read as
+// fp32, is exactly 1.5 * 2^23 + acc for |acc| < 2^22 (|acc| <= 127^2 D < 2^21 here), so one
+// fma turns it into the logit, with no int -> float conversion.
+constexpr int kQBias = 0x4B400000;
+constexpr float kQBiasF = 12582912.0f;  // 1.5 * 2^23
 
 template <int D>
 struct AttnQ8Shared {
@@ -58,6 +63,13 @@ struct AttnQ8Shared {
     int ucount;
     int slot;
 };
+
+__device__ __forceinline__ i32x16 splat16i(int x) {
+    i32x16 r;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = x;
+    return r;
+}
 
 __device__ __forceinline__ int imax16(const i32x16 &s) {
     int x = max(s[0], s[1]);
@@ -224,6 +236,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     bool m_valid = false;
 
     i32x8 pb = {0, 0, 0, 0, 0, 0, 0, 0};     // packed weights (every byte rewritten per tile)
+    const i32x16 bias16 = splat16i(kQBias);  // accumulator start of the score products
     bool pend = false;      // a listed tile's scores wait for their softmax and P V
     int pend_stage = 0;
     float pend_unit = 0.0f;
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
             va[u] = (i32x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
         }
     };
-    // scores S^T = K Q^T of one tile (int32, exact)
+    // scores S^T = K Q^T of one tile (biased int32, exact; see kQBias)
     auto qk = [&](const i32x4 (&kf)[2][KS], i32x16 (&sacc)[2]) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -258,7 +271,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
                 sacc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[mt][ks], qf,
-                                                                 ks == 0 ? i32x16{} : sacc[mt],
+                                                                 ks == 0 ? bias16 : sacc[mt],
                                                                  0, 0, 0);
         }
     };
@@ -266,7 +279,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     // 32 hi + t); O and the row sum rescaled when the reference moves
     auto softmax = [&](const i32x16 (&sacc)[2], float unit) {
         const int imax = max(imax16(sacc[0]), imax16(sacc[1]));
-        const float tmax = (float)imax * unit;
+        const float tmax = (__int_as_float(imax) - kQBiasF) * unit;
         const float rm = fmaxf(tmax, __shfl_xor(tmax, 32));  // the row's tile max
         if (__builtin_amdgcn_ballot_w64(!m_valid || rm > m_ref + kQLazy) != 0ull) {
             const bool need = !m_valid || rm > m_ref + kQLazy;  // same in lanes l, l ^ 32
@@ -278,14 +291,16 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
             m_ref = mnew;
             m_valid = true;
         }
-        const float off = kQLog2C - m_ref;
+        // logit = (as_float(biased) - 1.5 * 2^23) * unit + log2(112) - m in one fma
+        const float off = __builtin_fmaf(-kQBiasF, unit, kQLog2C - m_ref);
 #pragma unroll
         for (int q4 = 0; q4 < 8; ++q4) {
             const int mt = q4 >> 2, j0 = 4 * (q4 & 3);
             float f[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                f[i] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sacc[mt][j0 + i], unit, off));
+                f[i] = __builtin_amdgcn_exp2f(
+                    __builtin_fmaf(__int_as_float(sacc[mt][j0 + i]), unit, off));
             int pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], pb[q4], false);
             pb[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pk, true);
         }
