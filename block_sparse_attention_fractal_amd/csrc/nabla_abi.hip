@@ -63,7 +63,8 @@ nabla_status nabla_fractal_permute(const void *x, void *y, nabla_dtype dtype, in
     if (row_bytes % 16) return NABLA_ERR_UNSUPPORTED;
     if (row_bytes / 16 > 0x7fffffffLL / kBlock) return NABLA_ERR_UNSUPPORTED;
     const long long nb = (long long)T * tiles(H) * tiles(W);
-    if ((long long)B * nb > 0x7fffffffLL) return NABLA_ERR_UNSUPPORTED;
+    // one 256-lane workgroup per patch: the launch's lane count must fit 32 bits
+    if ((long long)B * nb * 256 > 0xffffffffLL) return NABLA_ERR_UNSUPPORTED;
     return from_hip(nabla::launch_fractal_permute(x, y, (int)dtype_bytes(dtype), B, T, H, W,
                                                   heads * head_dim, inverse != 0,
                                                   as_stream(stream)));
@@ -100,6 +101,8 @@ nabla_status estimate(const void *q, const void *k, nabla_dtype dtype, int B, in
     if (!topk && !(thr >= 0.0 && thr <= 1.0)) return NABLA_ERR_INVALID_ARG;  // also NaN
     if (topk && !(ratio <= 1.0)) return NABLA_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
+    // the selection grid has B * heads workgroups along y
+    if ((long long)B * heads > 65535) return NABLA_ERR_UNSUPPORTED;
     const int nb = S / kBlock;
     if (nb > (topk ? kMaxTopkBlocks : kMaxBlocks)) return NABLA_ERR_UNSUPPORTED;
     const size_t need = nabla_block_mask_workspace(B, S, heads, head_dim);

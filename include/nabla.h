@@ -73,7 +73,8 @@ const char *nabla_status_string(nabla_status s);
  *   padding positions are not read.
  * x and y must not overlap.  Errors: INVALID_ARG if a pointer is NULL or a
  * size is < 1; UNSUPPORTED if heads*head_dim*sizeof(dtype) is not a multiple
- * of 16 bytes.
+ * of 16 bytes or B * T * Ht * Wt exceeds 2^24 - 1 patches (one launch of
+ * 256-lane workgroups, one per patch).
  */
 nabla_status nabla_fractal_permute(const void *x, void *y, nabla_dtype dtype, int B, int T,
                                    int H, int W, int heads, int head_dim, int inverse,
@@ -122,8 +123,8 @@ size_t nabla_block_mask_workspace(int B, int S, int heads, int head_dim);
  *           row is left untouched (unspecified).
  * ws:       device workspace of at least nabla_block_mask_workspace() bytes.
  * Errors: INVALID_ARG (NULL q/k/kv_nb/kv_inds, sizes < 1, S % 64 != 0, thr
- * NaN or outside [0,1]); UNSUPPORTED (head_dim not 64 or 128, or nb > 4096);
- * WORKSPACE (ws NULL or ws_bytes too small).
+ * NaN or outside [0,1]); UNSUPPORTED (head_dim not 64 or 128, nb > 4096, or
+ * B * heads > 65535); WORKSPACE (ws NULL or ws_bytes too small).
  */
 nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, int B, int S,
                               int heads, int head_dim, const uint8_t *sta, double thr,

@@ -82,6 +82,7 @@ def test_block_mask_validation(L):
         assert call(thr=thr) == INVALID
     assert call(D=96) == UNSUP
     assert call(S=64 * 4097) == UNSUP            # longer rows than the selection kernel holds
+    assert call(B=8192, S=64) == UNSUP           # B * heads = 65536: more than a grid's y extent
     assert call(ws=None) == WS
     assert call(wsb=L.nabla_block_mask_workspace(1, 8192, 8, 128) - 1) == WS
 
@@ -265,6 +266,7 @@ def test_permute_and_sta_validation(L):
     assert p(FAKE, FAKE, BF16, 0, 2, 12, 20, 2, 64, 0, None) == INVALID   # B < 1
     assert p(FAKE, FAKE, BF16, 1, 0, 16, 16, 2, 64, 0, None) == INVALID
     assert p(FAKE, FAKE, BF16, 1, 2, 16, 16, 1, 2, 0, None) == UNSUP      # 4-byte rows
+    assert p(FAKE, FAKE, BF16, 1, 16384, 256, 256, 1, 64, 0, None) == UNSUP  # 2^24 patches
     s = L.nabla_sta_mask
     assert s(None, 2, 2, 2, 1, 1, 1, None) == INVALID
     assert s(FAKE, 2, 0, 2, 1, 1, 1, None) == INVALID
