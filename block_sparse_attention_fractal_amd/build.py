@@ -6,7 +6,11 @@
 Flags:
   -ffp-contract=off   the estimator's fp32 rounding order is fixed; the only
                       fused multiply-adds are explicit ``__builtin_fmaf`` calls;
-  -packed-fp32-ops    off: packed fp32 VALU forms are not emitted.
+  -packed-fp32-ops    off: packed fp32 VALU forms are not emitted;
+  -amdgpu-mfma-vgpr-form=1
+                      MFMAs written as builtins take their accumulators in VGPRs
+                      (the score products, which VALU code reads); accumulators
+                      meant to stay in AGPRs use inline-asm MFMAs.
 """
 import glob
 import os
@@ -22,6 +26,7 @@ HIPFLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 

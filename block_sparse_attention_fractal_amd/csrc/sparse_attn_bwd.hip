@@ -82,6 +82,29 @@ __device__ __forceinline__ void tile_offsets(int tid, int64_t tok, uint32_t (&of
     }
 }
 
+// Gradient accumulators live in AGPRs for the whole walk: their MFMAs are issued from
+// inline asm with the accumulator bound to AGPRs ("+a"), while the score products stay
+// compiler builtins in VGPRs (the build selects the VGPR form for MFMAs), which the softmax
+// reads.  acc += a b (v_mfma_f32_32x32x16_bf16).  The compiler does not see the asm's
+// hazards, so the asm waits itself: s_nop 4 first covers operands that VALU instructions
+// have just written (the packed weights, the zeroed accumulators); a chain on one
+// accumulator needs no wait between MFMAs of the same shape.
+__device__ __forceinline__ void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
+    asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Waits out the last MFMAs writing the accumulators before VALU instructions read them
+// (more than the 8-pass MFMA's write latency).  The asm names every accumulator as in and
+// out, so no read of them can be scheduled above it.
+template <int DT>
+__device__ __forceinline__ void acc_settle(f32x16 (&acc)[DT]) {
+    static_assert(DT == 2 || DT == 4, "2 or 4 d tiles");
+    if constexpr (DT == 4)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                     : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]), "+a"(acc[1]));
+}
+
 // Stores a [D x 32] fp32 product tile set (acc[dt]: rows d = 32 dt + ..., column = this
 // lane's row) times `mul` as bf16 into row `dst` (the lane's row, D contiguous values).
 template <int D>
@@ -290,14 +313,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[dt & 1][kk], ds[kk >> 1][kk & 1],
-                                                                  acc[dt], 0, 0, 0);
+            for (int kk = 0; kk < 4; ++kk) mfma_acc(acc[dt], kt[dt & 1][kk], ds[kk >> 1][kk & 1]);
             __builtin_amdgcn_sched_barrier(0);
         }
         vm_wait<0>();
         __syncthreads();  // tile u + 1 has landed; everyone is done with tile u's stage
     }
+    acc_settle(acc);
     store_rowT<D>(dq + head0 + (int64_t)qtok * tok, acc, hi, scale);
 }
 
@@ -387,13 +409,28 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
         if (u + 1 < n) issue(list[u + 1], st ^ 1);
         const char *qb = reinterpret_cast<const char *>(qsh[st]);
         const char *db = reinterpret_cast<const char *>(dsh[st]);
-        // S (log2 units) and dP: rows = the tile's queries in sigma order, columns = keys
+        // S - lse (log2 units) and dP - Delta: rows = the tile's queries in sigma order,
+        // columns = keys.  The accumulators start at minus the row statistics (register
+        // 8p + e of half mt holds query 32 mt + 16 p + 8 hi + e), so the products give the
+        // exponent of P and the factor of dS directly.
         f32x16 sacc[2], pacc[2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            sacc[mt] = splat16(0.0f);
-            pacc[mt] = splat16(0.0f);
-        }
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int q0 = 32 * mt + 16 * p + 8 * hi;
+                const float4 l0 = *reinterpret_cast<const float4 *>(&lsh[st][q0]);
+                const float4 l1 = *reinterpret_cast<const float4 *>(&lsh[st][q0 + 4]);
+                const float4 e0 = *reinterpret_cast<const float4 *>(&esh[st][q0]);
+                const float4 e1 = *reinterpret_cast<const float4 *>(&esh[st][q0 + 4]);
+                const float lq[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                const float eq[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    sacc[mt][8 * p + e] = -lq[e];
+                    pacc[mt][8 * p + e] = -eq[e];
+                }
+            }
         // Q and dO row fragments read KLA k-steps ahead of their MFMAs (as in dq)
         constexpr int KLA = 3;
         bf16x8 fr[KLA + 1][4];
@@ -423,26 +460,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
             gt[0][kk] = tfrag<D>(db, lane, 0, kk);
             qt[0][kk] = tfrag<D>(qb, lane, 0, kk);
         }
-        // register 8p + e of half mt holds query 32 mt + 16 p + 8 hi + e
+        // P and dS = P (dP - Delta), packed (register 8p + e of half mt: query
+        // 32 mt + 16 p + 8 hi + e)
         bf16x8 pp[2][2], dd[2][2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int q0 = 32 * mt + 16 * p + 8 * hi;
-                const float4 l0 = *reinterpret_cast<const float4 *>(&lsh[st][q0]);
-                const float4 l1 = *reinterpret_cast<const float4 *>(&lsh[st][q0 + 4]);
-                const float4 e0 = *reinterpret_cast<const float4 *>(&esh[st][q0]);
-                const float4 e1 = *reinterpret_cast<const float4 *>(&esh[st][q0 + 4]);
-                const float lq[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-                const float eq[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+            for (int p = 0; p < 2; ++p)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float pr = __builtin_amdgcn_exp2f(sacc[mt][8 * p + e] - lq[e]);
+                    const float pr = __builtin_amdgcn_exp2f(sacc[mt][8 * p + e]);
                     pp[mt][p][e] = (bf16)pr;
-                    dd[mt][p][e] = (bf16)(pr * (pacc[mt][8 * p + e] - eq[e]));
+                    dd[mt][p][e] = (bf16)(pr * pacc[mt][8 * p + e]);
                 }
-            }
         // dV^T += dO^T P and dK^T += Q^T dS; each next d tile's fragments are read under
         // the current one's MFMAs
 #pragma unroll
@@ -457,10 +487,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                dva[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt[dt & 1][kk], pp[kk >> 1][kk & 1],
-                                                                  dva[dt], 0, 0, 0);
-                dka[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[dt & 1][kk], dd[kk >> 1][kk & 1],
-                                                                  dka[dt], 0, 0, 0);
+                mfma_acc(dva[dt], gt[dt & 1][kk], pp[kk >> 1][kk & 1]);
+                mfma_acc(dka[dt], qt[dt & 1][kk], dd[kk >> 1][kk & 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -468,6 +496,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
         if (u + 1 < n) land(st ^ 1);
         __syncthreads();  // tile u + 1 has landed; everyone is done with tile u's stage
     }
+    acc_settle(dka);
+    acc_settle(dva);
     store_rowT<D>(dk + head0 + (int64_t)ktok * tok, dka, hi, scale);
     store_rowT<D>(dv + head0 + (int64_t)ktok * tok, dva, hi, 1.0f);
 }
