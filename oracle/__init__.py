@@ -11,9 +11,10 @@ NablaAttentionImpl.forward source; the NablaAttentionMetadata fields) and the
 "NABLA: Neighborhood Adaptive Block-Level Attention" summary page (Technical
 Summary, Methodology).
 
-The training pass (attention_lse, attention_dq, attention_bwd) is the gradient of
-that dense masked attention; it is pinned against torch's fp64 autograd and closed
-forms.
+The training pass (attention_lse, attention_dq, attention_bwd, and attention_bwd_grid
+on padded layouts) is the gradient of that dense masked attention; it is pinned
+against torch's fp64 autograd (over the natural token order for padded grids) and
+closed forms.
 
 The quantized variant (fp8_e4m3, quant_qkv, attention_q8) follows the sibling
 "sla" backend page's SageSLA forward: INT8 Q and K per 64-token block after the
@@ -91,6 +92,8 @@ def _load():
     lib.orc_attention_dq.restype = i32
     lib.orc_attention_bwd.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64, P, P, P, P]
     lib.orc_attention_bwd.restype = i32
+    lib.orc_attention_bwd_grid.argtypes = [P, P, P, P] + [i32] * 6 + [P, P, f64, P, P, P, P]
+    lib.orc_attention_bwd_grid.restype = i32
     lib.orc_fp8_e4m3.argtypes = [f64]
     lib.orc_fp8_e4m3.restype = ctypes.c_uint8
     lib.orc_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
@@ -426,6 +429,23 @@ def attention_bwd(q, k, v, dout, kv_nb, kv_inds, scale=0.0):
                                    _ptr(dk), _ptr(dv))
     if rc != 0:
         raise ValueError("oracle attention_bwd: bad argument")
+    return {"lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def attention_bwd_grid(q, k, v, dout, grid, kv_nb, kv_inds, scale=0.0):
+    """attention_bwd() on the padded fractal layout of grid = (T, H, W): the gradients of
+    attention_grid's output; padding positions are never keys (their dk, dv are 0)."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, S, heads, D = q.shape
+    T, H, W = grid
+    kv_nb, kv_inds = _lists(kv_nb, kv_inds)
+    lse = np.zeros((B, heads, S), np.float64)
+    dq, dk, dv = (np.zeros((B, S, heads, D), np.float64) for _ in range(3))
+    rc = _load().orc_attention_bwd_grid(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, T, H, W,
+                                        heads, D, _ptr(kv_nb), _ptr(kv_inds), float(scale),
+                                        _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle attention_bwd_grid: bad argument")
     return {"lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 

@@ -639,15 +639,19 @@ static int orc_slice_allowed(const int32_t *kv_nb, const int32_t *kv_inds, int64
 /* Row pass for query row r (token index within the sequence) of slice (b, h):
  * lse_r, Delta_r and (if dq_row) dq_r.  allowed_row = the row of `allowed` for
  * r's block; z is scratch of S doubles.  dout may be NULL (lse only). */
+/* gH, gW: the latent extents of a padded layout (its padding positions are not keys), or 0. */
 static void orc_row_pass(const float *q, const float *k, const float *v, const float *dout,
-                         int64_t b, int h, int S, int heads, int D, const uint8_t *allowed_row,
-                         double scale, int64_t r, double *z, double *lse, double *delta,
-                         double *dq_row) {
+                         int64_t b, int h, int S, int heads, int D, int gH, int gW,
+                         const uint8_t *allowed_row, double scale, int64_t r, double *z,
+                         double *lse, double *delta, double *dq_row) {
     const int64_t tq = b * S + r;
     const float *qr = q + (tq * heads + h) * D;
     double zmax = -INFINITY;
     for (int64_t c = 0; c < S; ++c) {
-        if (!allowed_row[c / ORC_BLK]) { z[c] = -INFINITY; continue; }
+        if (!allowed_row[c / ORC_BLK] || (gH > 0 && !orc_token_valid(c, gH, gW))) {
+            z[c] = -INFINITY;
+            continue;
+        }
         const float *kc = k + ((b * S + c) * heads + h) * D;
         double acc = 0.0;
         for (int d = 0; d < D; ++d) acc += (double)qr[d] * (double)kc[d];
@@ -715,7 +719,7 @@ int orc_attention_lse(const float *q, const float *k, int B, int S, int heads, i
         if (!ok) bad = 1;
         else
             for (int r = 0; r < ORC_BLK; ++r)
-                orc_row_pass(q, k, NULL, NULL, b, h, S, heads, D, allowed, scale,
+                orc_row_pass(q, k, NULL, NULL, b, h, S, heads, D, 0, 0, allowed, scale,
                              (int64_t)i * ORC_BLK + r, z, &lse[rr * ORC_BLK + r], NULL, NULL);
         free(z);
         free(allowed);
@@ -750,7 +754,7 @@ int orc_attention_dq(const float *q, const float *k, const float *v, const float
         else
             for (int r = 0; r < ORC_BLK; ++r) {
                 double l, dl;
-                orc_row_pass(q, k, v, dout, b, h, S, heads, D, allowed, scale,
+                orc_row_pass(q, k, v, dout, b, h, S, heads, D, 0, 0, allowed, scale,
                              (int64_t)i * ORC_BLK + r, z, &l, &dl, &dq[(rr * ORC_BLK + r) * D]);
             }
         free(z);
@@ -761,10 +765,14 @@ int orc_attention_dq(const float *q, const float *k, const float *v, const float
 
 /* Full training pass over every (b, h) slice: lse [B,heads,S]; dq, dk, dv [B,S,heads,D].
  * Row quantities first (parallel over rows), then dk and dv per key (parallel over keys):
- * key c of block j gathers from every row whose block lists j. */
-int orc_attention_bwd(const float *q, const float *k, const float *v, const float *dout, int B,
-                      int S, int heads, int D, const int32_t *kv_nb, const int32_t *kv_inds,
-                      double scale, double *lse, double *dq, double *dk, double *dv) {
+ * key c of block j gathers from every row whose block lists j.  gH, gW: the latent extents
+ * of a padded layout, whose padding positions are never keys (their dk and dv are 0; their
+ * query rows are rows like any other), or 0. */
+static int orc_attention_bwd_impl(const float *q, const float *k, const float *v,
+                                  const float *dout, int B, int S, int heads, int D, int gH,
+                                  int gW, const int32_t *kv_nb, const int32_t *kv_inds,
+                                  double scale, double *lse, double *dq, double *dk,
+                                  double *dv) {
     if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
     const int nb = S / ORC_BLK;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
@@ -782,7 +790,7 @@ int orc_attention_bwd(const float *q, const float *k, const float *v, const floa
                 double *z = (double *)malloc(sizeof(double) * (size_t)S);
 #pragma omp for schedule(dynamic, 16)
                 for (int64_t r = 0; r < S; ++r)
-                    orc_row_pass(q, k, v, dout, b, h, S, heads, D,
+                    orc_row_pass(q, k, v, dout, b, h, S, heads, D, gH, gW,
                                  allowed + (size_t)(r / ORC_BLK) * nb, scale, r, z, &lse_s[r],
                                  &delta[r], dq + ((b * S + r) * heads + h) * D);
                 free(z);
@@ -795,6 +803,7 @@ int orc_attention_bwd(const float *q, const float *k, const float *v, const floa
                 double *dkc = dk + ((b * S + c) * heads + h) * D;
                 double *dvc = dv + ((b * S + c) * heads + h) * D;
                 for (int d = 0; d < D; ++d) { dkc[d] = 0.0; dvc[d] = 0.0; }
+                if (gH > 0 && !orc_token_valid(c, gH, gW)) continue; /* not a key */
                 for (int i = 0; i < nb; ++i) {
                     if (!allowed[(size_t)i * nb + j]) continue;
                     for (int rb = 0; rb < ORC_BLK; ++rb) {
@@ -819,6 +828,24 @@ int orc_attention_bwd(const float *q, const float *k, const float *v, const floa
     free(allowed);
     free(delta);
     return bad ? -1 : 0;
+}
+
+int orc_attention_bwd(const float *q, const float *k, const float *v, const float *dout, int B,
+                      int S, int heads, int D, const int32_t *kv_nb, const int32_t *kv_inds,
+                      double scale, double *lse, double *dq, double *dk, double *dv) {
+    return orc_attention_bwd_impl(q, k, v, dout, B, S, heads, D, 0, 0, kv_nb, kv_inds, scale,
+                                  lse, dq, dk, dv);
+}
+
+/* The training pass on the padded fractal layout of a T x H x W grid (the gradient of
+ * orc_attention_grid's output): padding positions are never keys. */
+int orc_attention_bwd_grid(const float *q, const float *k, const float *v, const float *dout,
+                           int B, int T, int H, int W, int heads, int D, const int32_t *kv_nb,
+                           const int32_t *kv_inds, double scale, double *lse, double *dq,
+                           double *dk, double *dv) {
+    if (T <= 0 || H <= 0 || W <= 0) return -1;
+    return orc_attention_bwd_impl(q, k, v, dout, B, (int)orc_fractal_len(T, H, W), heads, D, H,
+                                  W, kv_nb, kv_inds, scale, lse, dq, dk, dv);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -638,6 +638,53 @@ def test_attention_grid_equals_natural_order_sdpa(orc):
         assert np.max(np.abs(got[0, pos, hh] - ref)) < 1e-12
 
 
+def test_training_pass_grid_matches_natural_autograd(orc):
+    """On a padded grid, lse, dq, dk and dv of the fractal layout equal torch's fp64 autograd
+    of the dense masked attention over the natural token sequence (block mask mapped to
+    tokens, padding absent), with dO = 0 at padding positions as the permute writes it.
+    Padding positions get dk = dv = dq = 0; on a grid of whole patches the padded pass is
+    the plain one."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(74)
+    B, T, H, W, h, D = 1, 2, 12, 20, 2, 16
+    nat = [rng.standard_normal((B, T, H, W, h, D)).astype(np.float32) for _ in range(4)]
+    q, k, v, dout = (orc.fractal_permute(a) for a in nat)
+    S = q.shape[1]
+    nb = S // 64
+    kv_nb, kv_inds = _random_lists(rng, B, h, nb)
+    scale = 0.35
+    got = orc.attention_bwd_grid(q, k, v, dout, (T, H, W), kv_nb, kv_inds, scale=scale)
+    pos = np.array([[[orc.fractal_index(t, yy, xx, H, W) for xx in range(W)] for yy in range(H)]
+                    for t in range(T)]).ravel()  # natural token -> fractal position
+    pad = np.ones(S, bool)
+    pad[pos] = False
+    blk = pos // 64
+    for hh in range(h):
+        allowed = np.zeros((nb, nb), bool)
+        for i in range(nb):
+            allowed[i, kv_inds[0, hh, i, :kv_nb[0, hh, i]]] = True
+        m = torch.from_numpy(allowed[blk][:, blk])  # [N, N] natural tokens
+        Q, K, V = (torch.from_numpy(a[0, :, :, :, hh].reshape(-1, D)).double().requires_grad_()
+                   for a in nat[:3])
+        dO = torch.from_numpy(nat[3][0, :, :, :, hh].reshape(-1, D)).double()
+        z = (scale * (Q @ K.T)).masked_fill(~m, float("-inf"))
+        lse = torch.logsumexp(z, dim=-1)
+        o = torch.softmax(z, dim=-1) @ V
+        (o * dO).sum().backward()
+        assert np.max(np.abs(got["lse"][0, hh, pos] - lse.detach().numpy())) < 1e-12
+        for name, ref in (("dq", Q.grad), ("dk", K.grad), ("dv", V.grad)):
+            assert np.max(np.abs(got[name][0, pos, hh] - ref.numpy())) < 1e-11, name
+            assert np.all(got[name][0, pad, hh] == 0.0), name
+    # a grid of whole patches: the plain pass, bit for bit
+    nat16 = [rng.standard_normal((1, 2, 16, 8, 2, 16)).astype(np.float32) for _ in range(4)]
+    f16 = [orc.fractal_permute(a) for a in nat16]
+    kv_nb16, kv_inds16 = _random_lists(rng, 1, 2, f16[0].shape[1] // 64)
+    a = orc.attention_bwd_grid(*f16, (2, 16, 8), kv_nb16, kv_inds16)
+    b = orc.attention_bwd(*f16, kv_nb16, kv_inds16)
+    for name in ("lse", "dq", "dk", "dv"):
+        assert np.array_equal(a[name], b[name]), name
+
+
 def test_block_mask_grid_consistency(orc):
     """Both estimators on a grid of whole patches equal the plain ones; on a padded grid with a
     constant k every score of a row is equal, so the CDF estimator keeps the blocks its tie
