@@ -82,6 +82,8 @@ def lib():
     L.nabla_sparse_attn_bwd_workspace.restype = Z
     L.nabla_sparse_attn_bwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, P, F, P, P, P, P, Z, P]
     L.nabla_sparse_attn_bwd.restype = I
+    L.nabla_sparse_attn_bwd_grid.argtypes = [P] * 6 + [I] * 7 + [P, P, F, P, P, P, P, Z, P]
+    L.nabla_sparse_attn_bwd_grid.restype = I
     L.nabla_quant_qkv_workspace.argtypes = [I, I, I, I]
     L.nabla_quant_qkv_workspace.restype = Z
     L.nabla_quant_qkv.argtypes = [P, P, P, I, I, I, I, I, P, P, P, P, P, P, P, P, Z, P]
@@ -283,11 +285,14 @@ def nabla_sparse_attn_bwd_workspace(B, S, heads):
 
 
 def nabla_sparse_attn_bwd(q, k, v, o, dout, lse, kv_nb, kv_inds, scale=None, workspace=None,
-                          dq=None, dk=None, dv=None):
+                          dq=None, dk=None, dv=None, grid=None):
     """Gradients (dq, dk, dv) of the block-sparse attention for output gradient dout.
 
     q, k, v, o, dout: bf16 [B, S, heads, D] GPU tensors (o and lse from
     nabla_sparse_attn_fwd(..., lse=...) on the same inputs, lists and scale).
+    grid=(T, H, W): the padded fractal layout of that latent grid
+    (nabla_sparse_attn_bwd_grid: padding is never a key; o and lse from
+    nabla_sparse_attn_fwd(..., grid=grid)).
     Returns three new tensors (or the given dq, dk, dv).
     """
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse),
@@ -305,6 +310,8 @@ def nabla_sparse_attn_bwd(q, k, v, o, dout, lse, kv_nb, kv_inds, scale=None, wor
         raise ValueError("kv lists do not match q's shape")
     if lse.dtype != torch.float32 or lse.numel() != B * heads * S:
         raise ValueError("lse must be float32 with B * heads * S elements")
+    if grid is not None and fractal_len(*grid) != S:
+        raise ValueError("grid %s does not match S=%d" % (grid, S))
     outs = []
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         outs.append(torch.empty_like(q) if t is None else _dev(t, name))
@@ -313,10 +320,18 @@ def nabla_sparse_attn_bwd(q, k, v, o, dout, lse, kv_nb, kv_inds, scale=None, wor
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     else:
         _dev(workspace, "workspace")
+    sc = 0.0 if scale is None else float(scale)
+    if grid is not None:
+        _check(lib().nabla_sparse_attn_bwd_grid(_p(q), _p(k), _p(v), _p(o), _p(dout), _p(lse),
+                                                _dtype_code(q), B, *grid, heads, D, _p(kv_nb),
+                                                _p(kv_inds), sc, _p(outs[0]), _p(outs[1]),
+                                                _p(outs[2]), _p(workspace), workspace.numel(),
+                                                _stream(q)),
+               "nabla_sparse_attn_bwd_grid")
+        return tuple(outs)
     _check(lib().nabla_sparse_attn_bwd(_p(q), _p(k), _p(v), _p(o), _p(dout), _p(lse),
                                        _dtype_code(q), B, S, heads, D, _p(kv_nb), _p(kv_inds),
-                                       0.0 if scale is None else float(scale), _p(outs[0]),
-                                       _p(outs[1]), _p(outs[2]), _p(workspace),
+                                       sc, _p(outs[0]), _p(outs[1]), _p(outs[2]), _p(workspace),
                                        workspace.numel(), _stream(q)),
            "nabla_sparse_attn_bwd")
     return tuple(outs)

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
 constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
@@ -238,11 +238,14 @@ size_t nabla_sparse_attn_bwd_workspace(int B, int S, int heads) {
     return nabla::sparse_attn_bwd_workspace_bytes(B, S, heads);
 }
 
-nabla_status nabla_sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
-                                   const void *dout, const float *lse, nabla_dtype dtype, int B,
-                                   int S, int heads, int head_dim, const int32_t *kv_nb,
-                                   const int32_t *kv_inds, float scale, void *dq, void *dk,
-                                   void *dv, void *ws, size_t ws_bytes, void *stream) {
+namespace {
+
+// Hv > 0: a padded layout (Hv x Wv latents, tile grid (., Ht, Wt)); 0: whole blocks.
+nabla_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, nabla_dtype dtype, int B, int S,
+                      int heads, int head_dim, const int32_t *kv_nb, const int32_t *kv_inds,
+                      float scale, void *dq, void *dk, void *dv, int Ht, int Wt, int Hv, int Wv,
+                      void *ws, size_t ws_bytes, void *stream) {
     if (!q || !k || !v || !o || !dout || !lse || !kv_nb || !kv_inds || !dq || !dk || !dv ||
         !dtype_ok(dtype))
         return NABLA_ERR_INVALID_ARG;
@@ -255,8 +258,31 @@ nabla_status nabla_sparse_attn_bwd(const void *q, const void *k, const void *v, 
         return NABLA_ERR_WORKSPACE;
     if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
     return from_hip(nabla::launch_sparse_attn_bwd(q, k, v, o, dout, lse, B, S, heads, head_dim,
-                                                  kv_nb, kv_inds, scale, dq, dk, dv, ws,
-                                                  as_stream(stream)));
+                                                  kv_nb, kv_inds, scale, dq, dk, dv, Ht, Wt, Hv,
+                                                  Wv, ws, as_stream(stream)));
+}
+
+}  // namespace
+
+nabla_status nabla_sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                                   const void *dout, const float *lse, nabla_dtype dtype, int B,
+                                   int S, int heads, int head_dim, const int32_t *kv_nb,
+                                   const int32_t *kv_inds, float scale, void *dq, void *dk,
+                                   void *dv, void *ws, size_t ws_bytes, void *stream) {
+    return attn_bwd(q, k, v, o, dout, lse, dtype, B, S, heads, head_dim, kv_nb, kv_inds, scale,
+                    dq, dk, dv, 0, 0, 0, 0, ws, ws_bytes, stream);
+}
+
+nabla_status nabla_sparse_attn_bwd_grid(const void *q, const void *k, const void *v,
+                                        const void *o, const void *dout, const float *lse,
+                                        nabla_dtype dtype, int B, int T, int H, int W, int heads,
+                                        int head_dim, const int32_t *kv_nb,
+                                        const int32_t *kv_inds, float scale, void *dq, void *dk,
+                                        void *dv, void *ws, size_t ws_bytes, void *stream) {
+    const long long S = grid_len(B, T, H, W, heads, head_dim);
+    if (S < 0) return NABLA_ERR_INVALID_ARG;
+    return attn_bwd(q, k, v, o, dout, lse, dtype, B, (int)S, heads, head_dim, kv_nb, kv_inds,
+                    scale, dq, dk, dv, (int)tiles(H), (int)tiles(W), H, W, ws, ws_bytes, stream);
 }
 
 size_t nabla_quant_qkv_workspace(int B, int S, int heads, int head_dim) {

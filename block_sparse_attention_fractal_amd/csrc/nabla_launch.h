@@ -76,13 +76,15 @@ hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool 
                               void *o, float *lse, void *ws, hipStream_t stream);
 
 // Backward (bf16 tensors): dq, dk, dv from q, k, v, o, dO, lse and the kv lists.
+// Hv > 0: a padded layout of Hv x Wv latents on a tile grid (., Ht, Wt), whose padding
+// positions are not keys; Hv = 0: whole blocks (Ht, Wt unused).
 // ws: sparse_attn_bwd_workspace_bytes() bytes (row deltas, transposed lists).
 size_t sparse_attn_bwd_workspace_bytes(int B, int S, int heads);
 hipError_t launch_sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
                                   const void *dout, const float *lse, int B, int S, int heads,
                                   int D, const int32_t *kv_nb, const int32_t *kv_inds,
-                                  float scale, void *dq, void *dk, void *dv, void *ws,
-                                  hipStream_t stream);
+                                  float scale, void *dq, void *dk, void *dv, int Ht, int Wt,
+                                  int Hv, int Wv, void *ws, hipStream_t stream);
 
 // The quantized variant.  Codes and scales of q, k, v (layouts in nabla.h,
 // nabla_quant_qkv); ws: quant_workspace_bytes() bytes (k block sums, partial v maxima).

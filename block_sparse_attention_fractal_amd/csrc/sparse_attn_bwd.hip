@@ -20,6 +20,12 @@
 // Both gradient kernels recompute S and dP, so every output row is written once by one
 // workgroup in a fixed order: no atomics, and the results are deterministic.
 //
+// Padded layouts (a T x H x W latent grid whose H or W is not a multiple of 8: the last
+// patch row / column is partial, the sibling "video_sparse_attn" page's variable block
+// sizes): the padding positions are never keys, as in the forward.  dq sets dS to 0 at
+// them on partial tiles; dk and dv are 0 there.  The instances without kPad carry none
+// of that code.
+//
 // Layout tricks shared with the forward: a lane owns one column of each 32 x 32
 // product; the rows fed to the first product are permuted (sigma32) so that its fp32
 // results j = 8p .. 8p+7, packed to bf16, are directly the B operand of the second
@@ -194,13 +200,21 @@ __global__ __launch_bounds__(256) void bwd_tlist_compact_kernel(const uint8_t *_
 // ---- dq.  One workgroup (2 waves) per query block i of (b, h); wave w owns rows 32 w ..
 // 32 w + 31, lane (l32, hi) row 32 w + l32.  K and V tiles of the listed blocks go through
 // a 2-stage LDS ring (direct global -> LDS loads, one tile ahead).
-template <int D>
+// Patch rows / columns of block j that are tokens (8 x 8 unless the grid is padded).
+__device__ __forceinline__ void patch_extent(int j, int Ht, int Wt, int Hv, int Wv, int &vr,
+                                             int &vc) {
+    const int th = (j / Wt) % Ht, tw = j % Wt;
+    vr = min(kTile, Hv - th * kTile);
+    vc = min(kTile, Wv - tw * kTile);
+}
+
+template <int D, bool kPad>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     bf16 *__restrict__ dq, int S, int heads, const int32_t *__restrict__ kv_nb,
     const int32_t *__restrict__ kv_inds, const int32_t *__restrict__ order, float scale,
-    float scale_log2) {
+    float scale_log2, int Ht, int Wt, int Hv, int Wv) {
     constexpr int KS = D / 16, DT = D / 32, CPT = kBlock * D / 8 / kBwdThreads;
     __shared__ __attribute__((aligned(1024))) bf16 ksh[2][kBlock * D];
     __shared__ __attribute__((aligned(1024))) bf16 vsh[2][kBlock * D];
@@ -303,6 +317,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
 #pragma unroll
             for (int j = 0; j < 16; ++j)
                 ds[mt][j >> 3][j & 7] = (bf16)(__builtin_amdgcn_exp2f(sacc[mt][j]) * pacc[mt][j]);
+        if constexpr (kPad) {
+            // a partial patch: its padding positions are not keys (register j of half mt
+            // holds key 32 mt + 16 (j / 8) + 8 hi + j % 8 of the block)
+            int vr, vc;
+            patch_extent(clamp_block(list[u], nb), Ht, Wt, Hv, Wv, vr, vc);
+            if (vr < kTile || vc < kTile) {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = 32 * mt + 16 * (j >> 3) + 8 * hi + (j & 7);
+                        if (!((key >> 3) < vr && (key & 7) < vc)) ds[mt][j >> 3][j & 7] = (bf16)0.0f;
+                    }
+            }
+        }
         // dQ^T += K^T dS^T; each next d tile's K^T fragments are read under the current
         // one's MFMAs
 #pragma unroll
@@ -326,13 +355,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
 // ---- dk, dv.  One workgroup (2 waves) per kv block j of (b, h); wave w owns keys 32 w ..
 // 32 w + 31, lane (l32, hi) key 32 w + l32.  Q and dO tiles of the query blocks that list
 // j go through a 2-stage LDS ring, with their rows' lse (log2 units) and Delta.
-template <int D>
+template <int D, bool kPad>
 __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
     bf16 *__restrict__ dk, bf16 *__restrict__ dv, int S, int heads,
     const int32_t *__restrict__ q_nb, const int32_t *__restrict__ q_inds,
-    const int32_t *__restrict__ order, float scale, float scale_log2) {
+    const int32_t *__restrict__ order, float scale, float scale_log2, int Ht, int Wt, int Hv,
+    int Wv) {
     constexpr int KS = D / 16, DT = D / 32, CPT = kBlock * D / 8 / kBwdThreads;
     __shared__ __attribute__((aligned(1024))) bf16 qsh[2][kBlock * D];
     __shared__ __attribute__((aligned(1024))) bf16 dsh[2][kBlock * D];
@@ -498,8 +528,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     }
     acc_settle(dka);
     acc_settle(dva);
-    store_rowT<D>(dk + head0 + (int64_t)ktok * tok, dka, hi, scale);
-    store_rowT<D>(dv + head0 + (int64_t)ktok * tok, dva, hi, 1.0f);
+    float kmul = scale, vmul = 1.0f;
+    if constexpr (kPad) {
+        // this lane's key (32 w + l32 of block j) at a padding position: dk = dv = 0
+        int vr, vc;
+        patch_extent(j, Ht, Wt, Hv, Wv, vr, vc);
+        const int key = 32 * w + l32;
+        if (!((key >> 3) < vr && (key & 7) < vc)) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                dka[dt] = splat16(0.0f);
+                dva[dt] = splat16(0.0f);
+            }
+            kmul = 0.0f;
+            vmul = 0.0f;
+        }
+    }
+    store_rowT<D>(dk + head0 + (int64_t)ktok * tok, dka, hi, kmul);
+    store_rowT<D>(dv + head0 + (int64_t)ktok * tok, dva, hi, vmul);
 }
 
 // ---- host side
@@ -513,11 +559,12 @@ size_t sparse_attn_bwd_workspace_bytes(int B, int S, int heads) {
            round256(bh * nb * nb) + 2 * round256(bh * nb * 4);
 }
 
-template <int D>
+template <int D, bool kPad>
 static hipError_t launch_bwd_t(const bf16 *q, const bf16 *k, const bf16 *v, const bf16 *o,
                                const bf16 *dout, const float *lse, int B, int S, int heads,
                                const int32_t *kv_nb, const int32_t *kv_inds, float scale, bf16 *dq,
-                               bf16 *dk, bf16 *dv, void *ws, hipStream_t stream) {
+                               bf16 *dk, bf16 *dv, int Ht, int Wt, int Hv, int Wv, void *ws,
+                               hipStream_t stream) {
     const int nb = S / kBlock;
     const size_t BH = (size_t)B * heads;
     char *p = static_cast<char *>(ws);
@@ -550,7 +597,7 @@ static hipError_t launch_bwd_t(const bf16 *q, const bf16 *k, const bf16 *v, cons
     // Launch orders: longest lists first within phases of a few heads (enough rows for
     // three rounds of the resident workgroups), so that the long rows do not start last
     // and the K/V (or Q/dO) tiles read together stay in the caches.
-    const int resident = resident_workgroups<bwd_dq_kernel<D>>(kBwdThreads);
+    const int resident = resident_workgroups<bwd_dq_kernel<D, kPad>>(kBwdThreads);
     if (resident <= 0) return hipErrorInvalidDevice;
     int hpp = (3 * resident + nb - 1) / nb;
     hpp = hpp < 1 ? 1 : (hpp > (int)BH ? (int)BH : hpp);
@@ -559,26 +606,38 @@ static hipError_t launch_bwd_t(const bf16 *q, const bf16 *k, const bf16 *v, cons
     e = launch_longest_first(q_nb, (int)rows, hpp * nb, nb, order_k, stream);
     if (e != hipSuccess) return e;
     const float scale_log2 = scale * kLog2e;
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(rows), dim3(kBwdThreads), 0, stream, q, k, v, dout,
-                       lse, delta, dq, S, heads, kv_nb, kv_inds, order_q, scale, scale_log2);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(rows), dim3(kBwdThreads), 0, stream, q, k, v,
-                       dout, lse, delta, dk, dv, S, heads, q_nb, q_inds, order_k, scale,
-                       scale_log2);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, kPad>), dim3(rows), dim3(kBwdThreads), 0, stream, q, k,
+                       v, dout, lse, delta, dq, S, heads, kv_nb, kv_inds, order_q, scale,
+                       scale_log2, Ht, Wt, Hv, Wv);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kPad>), dim3(rows), dim3(kBwdThreads), 0, stream, q, k,
+                       v, dout, lse, delta, dk, dv, S, heads, q_nb, q_inds, order_k, scale,
+                       scale_log2, Ht, Wt, Hv, Wv);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
                                   const void *dout, const float *lse, int B, int S, int heads,
                                   int D, const int32_t *kv_nb, const int32_t *kv_inds,
-                                  float scale, void *dq, void *dk, void *dv, void *ws,
-                                  hipStream_t stream) {
+                                  float scale, void *dq, void *dk, void *dv, int Ht, int Wt,
+                                  int Hv, int Wv, void *ws, hipStream_t stream) {
     const auto c = [](const void *x) { return static_cast<const bf16 *>(x); };
     const auto m = [](void *x) { return static_cast<bf16 *>(x); };
-    if (D == 128)
-        return launch_bwd_t<128>(c(q), c(k), c(v), c(o), c(dout), lse, B, S, heads, kv_nb,
-                                 kv_inds, scale, m(dq), m(dk), m(dv), ws, stream);
-    return launch_bwd_t<64>(c(q), c(k), c(v), c(o), c(dout), lse, B, S, heads, kv_nb, kv_inds,
-                            scale, m(dq), m(dk), m(dv), ws, stream);
+    const bool pad = Hv > 0;
+    if (D == 128) {
+        if (pad)
+            return launch_bwd_t<128, true>(c(q), c(k), c(v), c(o), c(dout), lse, B, S, heads,
+                                           kv_nb, kv_inds, scale, m(dq), m(dk), m(dv), Ht, Wt,
+                                           Hv, Wv, ws, stream);
+        return launch_bwd_t<128, false>(c(q), c(k), c(v), c(o), c(dout), lse, B, S, heads, kv_nb,
+                                        kv_inds, scale, m(dq), m(dk), m(dv), 0, 0, 0, 0, ws,
+                                        stream);
+    }
+    if (pad)
+        return launch_bwd_t<64, true>(c(q), c(k), c(v), c(o), c(dout), lse, B, S, heads, kv_nb,
+                                      kv_inds, scale, m(dq), m(dk), m(dv), Ht, Wt, Hv, Wv, ws,
+                                      stream);
+    return launch_bwd_t<64, false>(c(q), c(k), c(v), c(o), c(dout), lse, B, S, heads, kv_nb,
+                                   kv_inds, scale, m(dq), m(dk), m(dv), 0, 0, 0, 0, ws, stream);
 }
 
 }  // namespace nabla

@@ -271,8 +271,7 @@ size_t nabla_sparse_attn_bwd_workspace(int B, int S, int heads);
  *
  * q, k, v, o, dout: [B, S, heads, head_dim] bf16, fractal order; o and lse as written
  *           by nabla_sparse_attn_fwd_lse for the same q, k, v, lists and scale.  Whole
- *           64-token blocks only (the padded layouts of nabla_sparse_attn_fwd_grid are
- *           not handled: their padding positions would count as keys).
+ *           64-token blocks (padded layouts: nabla_sparse_attn_bwd_grid).
  * lse:      [B, heads, S] fp32.
  * kv_nb, kv_inds, scale: as for the forward.
  * dq, dk, dv: out [B, S, heads, head_dim] bf16; must not overlap the inputs or each
@@ -290,6 +289,25 @@ nabla_status nabla_sparse_attn_bwd(const void *q, const void *k, const void *v, 
                                    int S, int heads, int head_dim, const int32_t *kv_nb,
                                    const int32_t *kv_inds, float scale, void *dq, void *dk,
                                    void *dv, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The backward of nabla_sparse_attn_fwd_grid: the training pass on the fractal layout of a
+ * T x H x W latent grid whose H or W need not be multiples of 8 (S = T * ceil(H/8) *
+ * ceil(W/8) * 64; the sibling "video_sparse_attn" page's variable block sizes).  The
+ * padding positions of partial patches are never keys: their dk and dv are 0.  Query rows
+ * at padding positions are rows like any other (with dO = 0 there, as nabla_fractal_permute
+ * writes a permuted gradient, their dq is 0 and they add nothing to dk or dv).  o and lse
+ * as written by nabla_sparse_attn_fwd_grid.  Everything else is nabla_sparse_attn_bwd; the
+ * workspace is nabla_sparse_attn_bwd_workspace(B, S, heads) for that S.  On a grid of
+ * whole patches the result equals nabla_sparse_attn_bwd.
+ * Errors: those of nabla_sparse_attn_bwd; INVALID_ARG also for T, H or W < 1.
+ */
+nabla_status nabla_sparse_attn_bwd_grid(const void *q, const void *k, const void *v,
+                                        const void *o, const void *dout, const float *lse,
+                                        nabla_dtype dtype, int B, int T, int H, int W, int heads,
+                                        int head_dim, const int32_t *kv_nb,
+                                        const int32_t *kv_inds, float scale, void *dq, void *dk,
+                                        void *dv, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * The quantized variant (the sibling "sla" backend page, the SageSLA forward: Q and K

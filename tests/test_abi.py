@@ -43,14 +43,14 @@ def test_exports_every_declared_symbol(L):
                           "nabla_block_mask_grid", "nabla_sparse_attn_workspace_grid",
                           "nabla_sparse_attn_fwd_grid", "nabla_quant_qkv_workspace",
                           "nabla_quant_qkv", "nabla_sparse_attn_q8_workspace",
-                          "nabla_sparse_attn_fwd_q8"}
+                          "nabla_sparse_attn_fwd_q8", "nabla_sparse_attn_bwd_grid"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 6
+    assert L.nabla_abi_version() == 7
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"
@@ -208,6 +208,18 @@ def test_sparse_attn_bwd_validation(L):
     assert call(S=64 * 4097) == UNSUP
     assert call(ws=None) == WS
     assert call(wsb=L.nabla_sparse_attn_bwd_workspace(1, 8192, 8) - 1) == WS
+    g = L.nabla_sparse_attn_bwd_grid
+
+    def gcall(T=2, H=12, W=20, q=FAKE, dt=BF16, D=128, ws=FAKE, wsb=1 << 40):
+        return g(q, FAKE, FAKE, FAKE, FAKE, FAKE, dt, 1, T, H, W, 8, D, FAKE, FAKE, 0.0, FAKE,
+                 FAKE, FAKE, ws, wsb, None)
+
+    for kw in ({"T": 0}, {"H": 0}, {"W": -1}, {"q": None}):
+        assert gcall(**kw) == INVALID, kw
+    assert gcall(dt=FP32) == UNSUP
+    assert gcall(D=96) == UNSUP
+    S = 2 * 2 * 3 * 64  # 2 frames of 2 x 3 patches (12 x 20 latents)
+    assert gcall(wsb=L.nabla_sparse_attn_bwd_workspace(1, S, 8) - 1) == WS
 
 
 def test_quant_workspace_size(L):

@@ -63,15 +63,16 @@ def random_lists(rng, B, h, nb, empty=(), full=()):
     return kv_nb, kv_inds
 
 
-def run_gpu(dev, tq, tk, tv, tdo, kv_nb, kv_inds, scale=None):
+def run_gpu(dev, tq, tk, tv, tdo, kv_nb, kv_inds, scale=None, grid=None):
     g = lambda t: t.to(dev)
     q, k, v, do = g(tq), g(tk), g(tv), g(tdo)
     nb_t = torch.from_numpy(kv_nb).to(dev)
     inds_t = torch.from_numpy(kv_inds).to(dev)
     B, S, h, D = q.shape
     lse = torch.empty((B, h, S), dtype=torch.float32, device=dev)
-    o = nabla.nabla_sparse_attn_fwd(q, k, v, nb_t, inds_t, scale=scale, lse=lse)
-    dq, dk, dv = nabla.nabla_sparse_attn_bwd(q, k, v, o, do, lse, nb_t, inds_t, scale=scale)
+    o = nabla.nabla_sparse_attn_fwd(q, k, v, nb_t, inds_t, scale=scale, lse=lse, grid=grid)
+    dq, dk, dv = nabla.nabla_sparse_attn_bwd(q, k, v, o, do, lse, nb_t, inds_t, scale=scale,
+                                             grid=grid)
     torch.cuda.synchronize()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
     return dict(lse=lse.cpu().numpy().astype(np.float64), dq=f(dq), dk=f(dk), dv=f(dv), o=o)
@@ -210,6 +211,70 @@ def test_bwd_deterministic(dev):
     arrs = [bf16_round(rng.standard_normal((B, S, h, D)).astype(np.float32))[1] for _ in range(4)]
     kv_nb, kv_inds = random_lists(rng, B, h, S // 64)
     a = run_gpu(dev, *arrs, kv_nb, kv_inds)
+    b = run_gpu(dev, *arrs, kv_nb, kv_inds)
+    for n in ("lse", "dq", "dk", "dv"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+# ---- padded fractal layouts (H or W not a multiple of 8): padding is never a key
+
+def padded_inputs(orc, rng, B, T, H, W, h, D):
+    """Natural-order seeded q, k, v, dO permuted by the oracle (padding rows 0), bf16."""
+    nat = [rng.standard_normal((B, T, H, W, h, D)).astype(np.float32) for _ in range(4)]
+    return [bf16_round(orc.fractal_permute(a)) for a in nat]
+
+
+@pytest.mark.parametrize("T,H,W,h,D,seed", [(2, 12, 20, 2, 128, 51), (1, 20, 28, 3, 64, 52)])
+def test_bwd_padded_full_parity(orc, dev, T, H, W, h, D, seed):
+    """Every lse, dq, dk, dv element of the padded training pass (nabla_sparse_attn_fwd_grid +
+    nabla_sparse_attn_bwd_grid) against oracle.attention_bwd_grid on random lists; padding
+    positions get exactly zero dk and dv (they are never keys) and zero dq (dO = 0 there)."""
+    rng = np.random.default_rng(seed)
+    B = 1
+    (q, tq), (k, tk), (v, tv), (do, tdo) = padded_inputs(orc, rng, B, T, H, W, h, D)
+    S = q.shape[1]
+    nb = S // 64
+    say("[bwd padded] T=%d H=%d W=%d heads=%d D=%d (S=%d)" % (T, H, W, h, D, S))
+    kv_nb, kv_inds = random_lists(rng, B, h, nb, empty={(0, h - 1, 0)}, full={(0, 0, nb - 1)})
+    got = run_gpu(dev, tq, tk, tv, tdo, kv_nb, kv_inds, grid=(T, H, W))
+    want = orc.attention_bwd_grid(q, k, v, do, (T, H, W), kv_nb, kv_inds)
+    lse_check(got["lse"], want["lse"], "lse padded")
+    for n in ("dq", "dk", "dv"):
+        rel_check(got[n], want[n], n + " padded")
+    pad = ~orc.token_valid(T, H, W)
+    for n in ("dq", "dk", "dv"):
+        assert np.all(got[n][0, pad] == 0.0), n
+
+
+def test_bwd_padded_estimator_lists(orc, dev):
+    """The padded small workload (4 frames of 20 x 28 latents) with the oracle's padded
+    estimator lists: every gradient element."""
+    w = synth.WORKLOADS["small_pad"]
+    say("[bwd padded estimator]", w.describe())
+    grid = (w.T, w.H, w.W)
+    qn, kn, vn = synth.make_qkv(w)
+    q, tq = bf16_round(orc.fractal_permute(qn))
+    k, tk = bf16_round(orc.fractal_permute(kn))
+    v, tv = bf16_round(orc.fractal_permute(vn))
+    don = np.random.default_rng(53).standard_normal(qn.shape).astype(np.float32)
+    do, tdo = bf16_round(orc.fractal_permute(don))
+    Ht, Wt = (w.H + 7) // 8, (w.W + 7) // 8
+    m = orc.block_mask_grid(q, k, grid, orc.sta_mask(w.T, Ht, Wt, *w.sta), w.thr)
+    got = run_gpu(dev, tq, tk, tv, tdo, m["kv_nb"], m["kv_inds"], grid=grid)
+    want = orc.attention_bwd_grid(q, k, v, do, grid, m["kv_nb"], m["kv_inds"])
+    lse_check(got["lse"], want["lse"], "lse padded small")
+    for n in ("dq", "dk", "dv"):
+        rel_check(got[n], want[n], n + " padded small")
+
+
+def test_bwd_grid_of_whole_patches_is_plain(dev):
+    """On a grid of whole patches the grid entry point gives the plain call's bits."""
+    rng = np.random.default_rng(54)
+    T, H, W, h, D = 2, 16, 24, 2, 128
+    S = T * H * W
+    arrs = [bf16_round(rng.standard_normal((1, S, h, D)).astype(np.float32))[1] for _ in range(4)]
+    kv_nb, kv_inds = random_lists(rng, 1, h, S // 64)
+    a = run_gpu(dev, *arrs, kv_nb, kv_inds, grid=(T, H, W))
     b = run_gpu(dev, *arrs, kv_nb, kv_inds)
     for n in ("lse", "dq", "dk", "dv"):
         assert np.array_equal(a[n], b[n]), n
