@@ -293,7 +293,8 @@ def sweep(torch, nabla, synth, steps, warmup, quant=False):
 
 def train_pass(torch, nabla, synth, w, steps, warmup):
     """The training pass on workload w: nabla_sparse_attn_fwd with lse, then
-    nabla_sparse_attn_bwd for a seeded dO, on the estimator's lists; one JSON line.
+    nabla_sparse_attn_bwd for a seeded dO, on the estimator's lists (the grid entry
+    points on a padded layout); one JSON line.
 
     Backward FLOPs are the algorithmic five products per kept pair (S = Q K^T again,
     dP = dO V^T, dV += P^T dO, dK += dS^T Q, dQ += dS K), 10 * 64 * 64 * D; the kernels
@@ -302,10 +303,14 @@ def train_pass(torch, nabla, synth, w, steps, warmup):
     q, k, v = synth.make_qkv(w)
     g = [torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in (q, k, v)]
     qf, kf, vf = (nabla.nabla_fractal_permute(t) for t in g)
+    # a padded layout (partial patches) goes through the grid entry points
+    grid = (w.T, w.H, w.W) if w.padded else None
     sta = nabla.nabla_sta_mask(w.tiles, w.sta, dev) if w.sta is not None else None
-    kv_nb, kv_inds = nabla.nabla_block_mask(qf, kf, sta, w.thr)
+    kv_nb, kv_inds = nabla.nabla_block_mask(qf, kf, sta, w.thr, grid=grid)
     rng = np.random.default_rng(w.seed + 1000)
-    dout = torch.from_numpy(rng.standard_normal(qf.shape, dtype=np.float32)).to(torch.bfloat16).to(dev)
+    # dO drawn in natural order and permuted, so it is 0 at padding positions
+    dnat = torch.from_numpy(rng.standard_normal(q.shape, dtype=np.float32)).to(torch.bfloat16)
+    dout = nabla.nabla_fractal_permute(dnat.to(dev))
     B, S, H, D = qf.shape
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     o = torch.empty_like(qf)
@@ -321,10 +326,10 @@ def train_pass(torch, nabla, synth, w, steps, warmup):
         e = [ev() for _ in range(3)] if rec is not None else None
         if e: e[0].record(stream)
         nabla.nabla_sparse_attn_fwd(qf, kf, vf, kv_nb, kv_inds, tiles=w.tiles, workspace=ws_f,
-                                    out=o, lse=lse)
+                                    out=o, lse=lse, grid=grid)
         if e: e[1].record(stream)
         nabla.nabla_sparse_attn_bwd(qf, kf, vf, o, dout, lse, kv_nb, kv_inds, workspace=ws_b,
-                                    dq=dq, dk=dk, dv=dv)
+                                    dq=dq, dk=dk, dv=dv, grid=grid)
         if e:
             e[2].record(stream)
             rec.append(e)
