@@ -103,6 +103,10 @@ def _load():
     lib.orc_quant_qkv.restype = i32
     lib.orc_attention_q8.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P, P, f64, P, i64, P]
     lib.orc_attention_q8.restype = i32
+    lib.orc_quant_qkv_grid.argtypes = [P, P, P] + [i32] * 6 + [P] * 7
+    lib.orc_quant_qkv_grid.restype = i32
+    lib.orc_attention_q8_grid.argtypes = [P] * 6 + [i32] * 6 + [P, P, f64, P, i64, P]
+    lib.orc_attention_q8_grid.restype = i32
     _lib = lib
     return lib
 
@@ -476,11 +480,12 @@ def fp8_e4m3_value(codes):
     return table[np.asarray(codes, dtype=np.uint8)]
 
 
-def quant_qkv(q, k, v):
+def quant_qkv(q, k, v, grid=None):
     """INT8 q, k per 64-token block (k after subtracting its sequence mean), FP8 e4m3 v per
     channel.  q, k, v [B,S,heads,D] fp32 values.  Returns dict(q8, qs, k8, ks, v8, vs, km):
     q8, k8 [B,heads,nb,64,D] int8; qs, ks [B,heads,nb] fp32; v8 [B,heads,nb,D,64] uint8 codes;
-    vs, km [B,heads,D] fp32."""
+    vs, km [B,heads,D] fp32.  grid=(T, H, W): the padded fractal layout of that grid, whose
+    padding positions are not tokens (left out of the mean and the maxima, codes 0)."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     B, S, heads, D = q.shape
     nb = S // BLOCK
@@ -488,17 +493,20 @@ def quant_qkv(q, k, v):
            "k8": np.empty((B, heads, nb, BLOCK, D), np.int8), "ks": np.empty((B, heads, nb), np.float32),
            "v8": np.empty((B, heads, nb, D, BLOCK), np.uint8), "vs": np.empty((B, heads, D), np.float32),
            "km": np.empty((B, heads, D), np.float32)}
-    rc = _load().orc_quant_qkv(_ptr(q), _ptr(k), _ptr(v), B, S, heads, D, _ptr(out["q8"]),
-                               _ptr(out["qs"]), _ptr(out["k8"]), _ptr(out["ks"]), _ptr(out["v8"]),
-                               _ptr(out["vs"]), _ptr(out["km"]))
+    outs = [_ptr(out[n]) for n in ("q8", "qs", "k8", "ks", "v8", "vs", "km")]
+    if grid is None:
+        rc = _load().orc_quant_qkv(_ptr(q), _ptr(k), _ptr(v), B, S, heads, D, *outs)
+    else:
+        rc = _load().orc_quant_qkv_grid(_ptr(q), _ptr(k), _ptr(v), B, *grid, heads, D, *outs)
     if rc != 0:
         raise ValueError("oracle quant_qkv: bad argument")
     return out
 
 
-def attention_q8(qz, kv_nb, kv_inds, row_ids=None, scale=0.0):
+def attention_q8(qz, kv_nb, kv_inds, row_ids=None, scale=0.0, grid=None):
     """The block-sparse attention on quant_qkv()'s codes (FP8 P, fp64 sums).
-    Returns (row_ids, o [len(row_ids), 64, D] fp64) like attention()."""
+    Returns (row_ids, o [len(row_ids), 64, D] fp64) like attention().  grid=(T, H, W): the
+    padded fractal layout of that grid (padding positions are never keys)."""
     q8 = np.ascontiguousarray(qz["q8"], dtype=np.int8)
     B, heads, nb, _, D = q8.shape
     S = nb * BLOCK
@@ -508,9 +516,14 @@ def attention_q8(qz, kv_nb, kv_inds, row_ids=None, scale=0.0):
     row_ids = _rows(row_ids, B, heads, nb)
     kv_nb, kv_inds = _lists(kv_nb, kv_inds)
     o = np.zeros((row_ids.size, BLOCK, D), np.float64)
-    rc = _load().orc_attention_q8(_ptr(q8), *[_ptr(a) for a in arrs], B, S, heads, D, _ptr(kv_nb),
-                                  _ptr(kv_inds), float(scale), _ptr(row_ids), row_ids.size,
-                                  _ptr(o))
+    if grid is None:
+        rc = _load().orc_attention_q8(_ptr(q8), *[_ptr(a) for a in arrs], B, S, heads, D,
+                                      _ptr(kv_nb), _ptr(kv_inds), float(scale), _ptr(row_ids),
+                                      row_ids.size, _ptr(o))
+    else:
+        rc = _load().orc_attention_q8_grid(_ptr(q8), *[_ptr(a) for a in arrs], B, *grid, heads,
+                                           D, _ptr(kv_nb), _ptr(kv_inds), float(scale),
+                                           _ptr(row_ids), row_ids.size, _ptr(o))
     if rc != 0:
         raise ValueError("oracle attention_q8: bad argument")
     return row_ids, o

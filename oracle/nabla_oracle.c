@@ -870,7 +870,10 @@ int orc_attention_bwd_grid(const float *q, const float *k, const float *v, const
 /*   - P = exp(z - rowmax) is stored as e4m3(448 P) (the FP8 P of that page's  */
 /*     "sv_f8" kernels, full range at P = 1); the row sum is taken over the    */
 /*     same quantized weights, so o is a convex combination of the V codes:   */
-/*     o[d] = vs[d] * sum_c p8_c v8_cd / sum_c p8_c, all in fp64.             */
+/*     o[d] = vs[d] * sum_c p8_c v8_cd / sum_c p8_c, all in fp64;             */
+/*   - padded layouts (Q7): padding positions are not tokens, so they are left */
+/*     out of the k mean (divided by the token count) and of every maximum,  */
+/*     their codes are 0, and they are never keys.                            */
 /* ------------------------------------------------------------------------- */
 
 /* OCP FP8 e4m3fn encoding of x, round to nearest, ties to the even code;     */
@@ -917,26 +920,37 @@ static int8_t orc_int8_code(float x, float scale) {
 
 /* q8, k8: [B][heads][nb][64][D] int8; qs, ks: [B][heads][nb]; v8: [B][heads][nb][D][64]   */
 /* e4m3 codes (each block transposed); vs, km: [B][heads][D]. */
-int orc_quant_qkv(const float *q, const float *k, const float *v, int B, int S, int heads, int D,
-                  int8_t *q8, float *qs, int8_t *k8, float *ks, uint8_t *v8, float *vs,
-                  float *km) {
+/* gH, gW: the latent extents of a padded layout, whose padding positions are not tokens
+ * (Q7): they are left out of the k mean (its divisor is the token count) and of every
+ * maximum, and their codes are 0.  0: every position is a token. */
+static int orc_quant_qkv_impl(const float *q, const float *k, const float *v, int B, int S,
+                              int heads, int D, int gH, int gW, int8_t *q8, float *qs,
+                              int8_t *k8, float *ks, uint8_t *v8, float *vs, float *km) {
     if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
     int nb = S / ORC_BLK;
+    uint8_t *tok = (uint8_t *)malloc((size_t)S);
+    if (!tok) return -1;
+    int64_t ntok = 0;
+    for (int64_t s = 0; s < S; ++s) {
+        tok[s] = (uint8_t)(gH <= 0 || orc_token_valid(s, gH, gW));
+        ntok += tok[s];
+    }
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t bh = 0; bh < (int64_t)B * heads; ++bh) {
         int64_t b = bh / heads;
         int h = (int)(bh % heads);
         float *kmean = km + bh * D;
-        /* k_mean: block sums, then their sum, then / S */
+        /* k_mean: block sums over the tokens, then their sum, then / the token count */
         for (int d = 0; d < D; ++d) {
             float tot = 0.0f;
             for (int j = 0; j < nb; ++j) {
                 float bs = 0.0f;
                 for (int r = 0; r < ORC_BLK; ++r)
-                    bs += k[((b * S + (int64_t)j * ORC_BLK + r) * heads + h) * D + d];
+                    if (tok[(int64_t)j * ORC_BLK + r])
+                        bs += k[((b * S + (int64_t)j * ORC_BLK + r) * heads + h) * D + d];
                 tot += bs;
             }
-            kmean[d] = tot / (float)S;
+            kmean[d] = tot / (float)ntok;
         }
         /* q and k' = k - k_mean per block */
         float *xs = (float *)malloc(sizeof(float) * ORC_BLK * D);
@@ -948,8 +962,11 @@ int orc_quant_qkv(const float *q, const float *k, const float *v, int B, int S, 
                 float amax = 0.0f;
                 for (int r = 0; r < ORC_BLK; ++r)
                     for (int d = 0; d < D; ++d) {
-                        float val = x[((b * S + (int64_t)j * ORC_BLK + r) * heads + h) * D + d];
-                        if (which == 1) val = val - kmean[d];
+                        float val = 0.0f;
+                        if (tok[(int64_t)j * ORC_BLK + r]) {
+                            val = x[((b * S + (int64_t)j * ORC_BLK + r) * heads + h) * D + d];
+                            if (which == 1) val = val - kmean[d];
+                        }
                         xs[r * D + d] = val;
                         if (fabsf(val) > amax) amax = fabsf(val);
                     }
@@ -964,27 +981,46 @@ int orc_quant_qkv(const float *q, const float *k, const float *v, int B, int S, 
         for (int d = 0; d < D; ++d) {
             float amax = 0.0f;
             for (int64_t s = 0; s < S; ++s) {
+                if (!tok[s]) continue;
                 float a = fabsf(v[((b * S + s) * heads + h) * D + d]);
                 if (a > amax) amax = a;
             }
             float sc = amax / 2.25f;
             vs[bh * D + d] = sc;
             for (int64_t s = 0; s < S; ++s) {
-                float val = v[((b * S + s) * heads + h) * D + d];
+                float val = tok[s] ? v[((b * S + s) * heads + h) * D + d] : 0.0f;
                 float r = sc == 0.0f ? 0.0f : val / sc;
                 int64_t j = s / ORC_BLK, key = s % ORC_BLK;
                 v8[((bh * nb + j) * D + d) * ORC_BLK + key] = orc_fp8_e4m3((double)r);
             }
         }
     }
+    free(tok);
     return 0;
 }
 
-/* The attention on the codes for the q-block rows row_ids (as orc_attention); o [nrows][64][D]. */
-int orc_attention_q8(const int8_t *q8, const float *qs, const int8_t *k8, const float *ks,
-                     const uint8_t *v8, const float *vs, int B, int S, int heads, int D,
-                     const int32_t *kv_nb, const int32_t *kv_inds, double scale,
-                     const int64_t *row_ids, int64_t nrows, double *o) {
+int orc_quant_qkv(const float *q, const float *k, const float *v, int B, int S, int heads, int D,
+                  int8_t *q8, float *qs, int8_t *k8, float *ks, uint8_t *v8, float *vs,
+                  float *km) {
+    return orc_quant_qkv_impl(q, k, v, B, S, heads, D, 0, 0, q8, qs, k8, ks, v8, vs, km);
+}
+
+/* The quantizer on the padded fractal layout of a T x H x W grid (Q7). */
+int orc_quant_qkv_grid(const float *q, const float *k, const float *v, int B, int T, int H,
+                       int W, int heads, int D, int8_t *q8, float *qs, int8_t *k8, float *ks,
+                       uint8_t *v8, float *vs, float *km) {
+    if (T <= 0 || H <= 0 || W <= 0) return -1;
+    return orc_quant_qkv_impl(q, k, v, B, (int)orc_fractal_len(T, H, W), heads, D, H, W, q8,
+                              qs, k8, ks, v8, vs, km);
+}
+
+/* The attention on the codes for the q-block rows row_ids (as orc_attention); o [nrows][64][D].
+ * gH, gW: the latent extents of a padded layout (padding positions are never keys), or 0. */
+static int orc_attention_q8_impl(const int8_t *q8, const float *qs, const int8_t *k8,
+                                 const float *ks, const uint8_t *v8, const float *vs, int B,
+                                 int S, int heads, int D, int gH, int gW, const int32_t *kv_nb,
+                                 const int32_t *kv_inds, double scale, const int64_t *row_ids,
+                                 int64_t nrows, double *o) {
     if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0) return -1;
     int nb = S / ORC_BLK;
     if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
@@ -1013,7 +1049,10 @@ int orc_attention_q8(const int8_t *q8, const float *qs, const int8_t *k8, const 
             double zmax = -INFINITY;
             for (int64_t c = 0; c < S; ++c) {
                 int j = (int)(c / ORC_BLK);
-                if (!allowed[j]) { z[c] = -INFINITY; continue; }
+                if (!allowed[j] || (gH > 0 && !orc_token_valid(c, gH, gW))) {
+                    z[c] = -INFINITY;
+                    continue;
+                }
                 const int8_t *kc = k8 + (bh * nb * ORC_BLK + c) * (int64_t)D;
                 int64_t dot = 0;
                 for (int d = 0; d < D; ++d) dot += (int64_t)qr[d] * (int64_t)kc[d];
@@ -1039,4 +1078,22 @@ int orc_attention_q8(const int8_t *q8, const float *qs, const int8_t *k8, const 
         free(allowed);
     }
     return bad ? -1 : 0;
+}
+
+int orc_attention_q8(const int8_t *q8, const float *qs, const int8_t *k8, const float *ks,
+                     const uint8_t *v8, const float *vs, int B, int S, int heads, int D,
+                     const int32_t *kv_nb, const int32_t *kv_inds, double scale,
+                     const int64_t *row_ids, int64_t nrows, double *o) {
+    return orc_attention_q8_impl(q8, qs, k8, ks, v8, vs, B, S, heads, D, 0, 0, kv_nb, kv_inds,
+                                 scale, row_ids, nrows, o);
+}
+
+/* The attention on the codes of a padded T x H x W grid: padding positions are never keys. */
+int orc_attention_q8_grid(const int8_t *q8, const float *qs, const int8_t *k8, const float *ks,
+                          const uint8_t *v8, const float *vs, int B, int T, int H, int W,
+                          int heads, int D, const int32_t *kv_nb, const int32_t *kv_inds,
+                          double scale, const int64_t *row_ids, int64_t nrows, double *o) {
+    if (T <= 0 || H <= 0 || W <= 0) return -1;
+    return orc_attention_q8_impl(q8, qs, k8, ks, v8, vs, B, (int)orc_fractal_len(T, H, W), heads,
+                                 D, H, W, kv_nb, kv_inds, scale, row_ids, nrows, o);
 }

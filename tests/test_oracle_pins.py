@@ -786,6 +786,78 @@ def test_quant_qkv_degenerate_blocks(orc):
     assert (z["vs"][..., 3] == 0).all() and (z["v8"][:, :, :, 3, :] == 0).all()
 
 
+def test_quant_qkv_grid_tokens_only(orc):
+    """On a padded grid the quantizer sees tokens only: the k mean over the T*H*W tokens, block
+    and channel maxima over tokens (padding filled with a large value to show it is ignored),
+    padding codes 0; on a grid of whole patches it is the plain quantizer bit for bit."""
+    rng = np.random.default_rng(76)
+    B, T, H, W, h, D = 1, 2, 12, 20, 2, 16
+    nat = [rng.standard_normal((B, T, H, W, h, D)).astype(np.float32) for _ in range(3)]
+    q, k, v = (orc.fractal_permute(a) for a in nat)
+    S = q.shape[1]
+    nb = S // 64
+    valid = orc.token_valid(T, H, W)
+    for x in (q, k, v):
+        x[:, ~valid] = 7.0  # not tokens: must not enter any mean, maximum or code
+    z = orc.quant_qkv(q, k, v, grid=(T, H, W))
+    km64 = nat[1].astype(np.float64).reshape(B, -1, h, D).mean(axis=1)  # [B, h, D]
+    assert np.allclose(z["km"], km64, rtol=0, atol=1e-5)
+    vb = valid.reshape(nb, 64)
+    for name, x in (("q", q), ("k", k - z["km"][:, None, :, :])):
+        xb = x.transpose(0, 2, 1, 3).reshape(B, h, nb, 64, D)
+        xb = np.where(vb[None, None, :, :, None], xb, np.float32(0))
+        amax = np.abs(xb).max(axis=(3, 4))
+        assert np.array_equal(z[name + "s"], (amax / np.float32(127)).astype(np.float32)), name
+        assert np.all(z[name + "8"][:, :, ~vb] == 0), name
+    amax_v = np.abs(v[:, valid]).max(axis=1)                             # [B, h, D]
+    assert np.array_equal(z["vs"], (amax_v / np.float32(2.25)).astype(np.float32))
+    assert np.all(z["v8"].transpose(0, 1, 2, 4, 3)[:, :, ~vb] == 0)
+    nat16 = [rng.standard_normal((1, 2, 16, 8, 2, 16)).astype(np.float32) for _ in range(3)]
+    f16 = [orc.fractal_permute(a) for a in nat16]
+    a = orc.quant_qkv(*f16, grid=(2, 16, 8))
+    b = orc.quant_qkv(*f16)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_attention_q8_grid_padding_never_a_key(orc):
+    """On a padded grid the quantized attention equals the plain fp64 attention of the padded
+    layout on the dequantized codes within the e4m3 rounding bound of the weights (over the
+    listed blocks' tokens only); on a grid of whole patches it is the plain one bit for bit."""
+    rng = np.random.default_rng(77)
+    B, T, H, W, h, D = 1, 2, 12, 20, 2, 16
+    nat = [rng.standard_normal((B, T, H, W, h, D)).astype(np.float32) for _ in range(3)]
+    q, k, v = (orc.fractal_permute(a) for a in nat)
+    S = q.shape[1]
+    nb = S // 64
+    grid = (T, H, W)
+    kv_nb, kv_inds = synth.random_lists(rng, B, h, nb, 0.5)
+    z = orc.quant_qkv(q, k, v, grid=grid)
+    ids, o8 = orc.attention_q8(z, kv_nb, kv_inds, grid=grid)
+    qd, kd, vd = orc.dequant_qkv(z)
+    _, o = orc.attention_grid(qd, kd, vd, grid, kv_nb, kv_inds)
+    valid = orc.token_valid(T, H, W)
+    for n, rid in enumerate(ids):
+        hh, i = divmod(int(rid), nb)
+        cnt = kv_nb[0, hh, i]
+        if cnt == 0:
+            assert (o8[n] == 0).all()
+            continue
+        keys = np.concatenate([np.arange(64 * j, 64 * j + 64) for j in kv_inds[0, hh, i, :cnt]])
+        keys = keys[valid[keys]]
+        vk = vd[0, keys, hh, :].astype(np.float64)
+        spread = np.abs(vk[None, :, :] - o[n][:, None, :]).max(axis=1)
+        bound = (2.0 ** -4 + 2.0 ** -10 * keys.size / 448.0) / (1 - 2.0 ** -4) * spread
+        assert (np.abs(o8[n] - o[n]) <= bound + 1e-9).all()
+    nat16 = [rng.standard_normal((1, 2, 16, 8, 2, 16)).astype(np.float32) for _ in range(3)]
+    f16 = [orc.fractal_permute(a) for a in nat16]
+    kv_nb16, kv_inds16 = synth.random_lists(rng, 1, 2, f16[0].shape[1] // 64, 0.5)
+    zz = orc.quant_qkv(*f16)
+    _, a = orc.attention_q8(zz, kv_nb16, kv_inds16, grid=(2, 16, 8))
+    _, b = orc.attention_q8(zz, kv_nb16, kv_inds16)
+    assert np.array_equal(a, b)
+
+
 def test_attention_q8_exact_on_power_of_two_weights(orc):
     """With scale ln 2, unit scales and small integer dots every weight is a power of two that
     e4m3 holds exactly, so the output is sum 2^dot v / sum 2^dot, computed here independently."""
