@@ -203,16 +203,22 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False):
             check(L.nabla_block_mask_topk(P(qf), P(kf), dt_code, B, S, H, D, sta_p, topk_ratio,
                                           P(kv_nb), P(kv_inds), P(ws), ws.numel(), sp), "mask")
         if e: e[2].record(stream)
-        if quant:
-            check(L.nabla_quant_qkv(P(qf), P(kf), P(vf), dt_code, B, S, H, D, P(qz["q8"]),
-                                    P(qz["qs"]), P(qz["k8"]), P(qz["ks"]), P(qz["v8"]),
-                                    P(qz["vs"]), P(qz["km"]), P(ws_q), ws_q.numel(), sp), "quant")
+        codes = [P(qz[n]) for n in ("q8", "qs", "k8", "ks", "v8", "vs")] if quant else None
+        if quant and w.padded:
+            check(L.nabla_quant_qkv_grid(P(qf), P(kf), P(vf), dt_code, B, w.T, w.H, w.W, H, D,
+                                         *codes, P(qz["km"]), P(ws_q), ws_q.numel(), sp), "quant")
+        elif quant:
+            check(L.nabla_quant_qkv(P(qf), P(kf), P(vf), dt_code, B, S, H, D, *codes,
+                                    P(qz["km"]), P(ws_q), ws_q.numel(), sp), "quant")
         if e: e[3].record(stream)
-        if quant:
-            check(L.nabla_sparse_attn_fwd_q8(P(qz["q8"]), P(qz["qs"]), P(qz["k8"]), P(qz["ks"]),
-                                             P(qz["v8"]), P(qz["vs"]), B, S, H, D, P(kv_nb),
-                                             P(kv_inds), 0.0, *w.tiles, P(of), P(ws_q8),
-                                             ws_q8.numel(), sp), "attn q8")
+        if quant and w.padded:
+            check(L.nabla_sparse_attn_fwd_q8_grid(*codes, B, w.T, w.H, w.W, H, D, P(kv_nb),
+                                                  P(kv_inds), 0.0, P(of), P(ws_q8),
+                                                  ws_q8.numel(), sp), "attn q8")
+        elif quant:
+            check(L.nabla_sparse_attn_fwd_q8(*codes, B, S, H, D, P(kv_nb), P(kv_inds), 0.0,
+                                             *w.tiles, P(of), P(ws_q8), ws_q8.numel(), sp),
+                  "attn q8")
         elif w.padded:
             check(L.nabla_sparse_attn_fwd_grid(P(qf), P(kf), P(vf), dt_code, B, w.T, w.H, w.W, H,
                                                D, P(kv_nb), P(kv_inds), 0.0, P(of), None,

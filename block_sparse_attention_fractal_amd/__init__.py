@@ -93,6 +93,10 @@ def lib():
     L.nabla_sparse_attn_fwd_q8.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, F, I, I, I, P, P, Z,
                                            P]
     L.nabla_sparse_attn_fwd_q8.restype = I
+    L.nabla_quant_qkv_grid.argtypes = [P, P, P] + [I] * 7 + [P] * 7 + [P, Z, P]
+    L.nabla_quant_qkv_grid.restype = I
+    L.nabla_sparse_attn_fwd_q8_grid.argtypes = [P] * 6 + [I] * 6 + [P, P, F, P, P, Z, P]
+    L.nabla_sparse_attn_fwd_q8_grid.restype = I
     _lib = L
     return L
 
@@ -337,11 +341,13 @@ def nabla_sparse_attn_bwd(q, k, v, o, dout, lse, kv_nb, kv_inds, scale=None, wor
     return tuple(outs)
 
 
-def nabla_quant_qkv(q, k, v, workspace=None):
+def nabla_quant_qkv(q, k, v, workspace=None, grid=None):
     """The quantizer of the quantized variant: q, k, v [B, S, heads, D] (bf16 or fp32) ->
     dict(q8, q_scale, k8, k_scale, v8, v_scale, k_mean) with q8, k8 int8 [B, heads, nb, 64, D]
     (k after subtracting its sequence mean), q_scale, k_scale float32 [B, heads, nb], v8 uint8
     e4m3 codes [B, heads, nb, D, 64] (blocks transposed), v_scale, k_mean float32 [B, heads, D].
+    grid=(T, H, W): the padded fractal layout of that latent grid (nabla_quant_qkv_grid:
+    padding positions are not tokens).
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _dev(t, name)
@@ -362,18 +368,27 @@ def nabla_quant_qkv(q, k, v, workspace=None):
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _dev(workspace, "workspace")
-    _check(lib().nabla_quant_qkv(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads, D,
-                                 _p(out["q8"]), _p(out["q_scale"]), _p(out["k8"]),
-                                 _p(out["k_scale"]), _p(out["v8"]), _p(out["v_scale"]),
-                                 _p(out["k_mean"]), _p(workspace), workspace.numel(), _stream(q)),
+    codes = [_p(out[n]) for n in ("q8", "q_scale", "k8", "k_scale", "v8", "v_scale", "k_mean")]
+    if grid is not None:
+        if fractal_len(*grid) != S:
+            raise ValueError("grid %s does not match S=%d" % (grid, S))
+        _check(lib().nabla_quant_qkv_grid(_p(q), _p(k), _p(v), _dtype_code(q), B, *grid, heads,
+                                          D, *codes, _p(workspace), workspace.numel(),
+                                          _stream(q)),
+               "nabla_quant_qkv_grid")
+        return out
+    _check(lib().nabla_quant_qkv(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads, D, *codes,
+                                 _p(workspace), workspace.numel(), _stream(q)),
            "nabla_quant_qkv")
     return out
 
 
 def nabla_sparse_attn_fwd_q8(qz, kv_nb, kv_inds, scale=None, tiles=None, workspace=None,
-                             out=None):
+                             out=None, grid=None):
     """Block-sparse attention of the quantized variant over the listed 64 x 64 blocks, on the
-    codes of nabla_quant_qkv (qz): o [B, S, heads, D] bfloat16."""
+    codes of nabla_quant_qkv (qz): o [B, S, heads, D] bfloat16.  grid=(T, H, W): the padded
+    fractal layout of that latent grid (nabla_sparse_attn_fwd_q8_grid: padding is never a
+    key; tiles is then implied)."""
     names = ("q8", "q_scale", "k8", "k_scale", "v8", "v_scale")
     for name in names:
         _dev(qz[name], name)
@@ -392,12 +407,25 @@ def nabla_sparse_attn_fwd_q8(qz, kv_nb, kv_inds, scale=None, tiles=None, workspa
         raise ValueError("q8, k8, v8 must have one shape")
     o = torch.empty((B, S, heads, D), dtype=torch.bfloat16, device=q8.device) if out is None \
         else _dev(out, "out")
+    if grid is not None:
+        T, H, W = grid
+        if fractal_len(T, H, W) != S:
+            raise ValueError("grid %s does not match S=%d" % (grid, S))
+        tiles = (T, (H + 7) // 8, (W + 7) // 8)
     Tt, Ht, Wt = (0, 0, 0) if tiles is None else tiles
     if workspace is None:
         need = lib().nabla_sparse_attn_q8_workspace(B, S, heads, Tt, Ht, Wt)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q8.device)
     else:
         _dev(workspace, "workspace")
+    if grid is not None:
+        _check(lib().nabla_sparse_attn_fwd_q8_grid(*[_p(qz[n]) for n in names], B, *grid, heads,
+                                                   D, _p(kv_nb), _p(kv_inds),
+                                                   0.0 if scale is None else float(scale), _p(o),
+                                                   _p(workspace), workspace.numel(),
+                                                   _stream(q8)),
+               "nabla_sparse_attn_fwd_q8_grid")
+        return o
     _check(lib().nabla_sparse_attn_fwd_q8(*[_p(qz[n]) for n in names], B, S, heads, D,
                                           _p(kv_nb), _p(kv_inds),
                                           0.0 if scale is None else float(scale), Tt, Ht, Wt,

@@ -16,6 +16,10 @@
 // Outputs: q8, k8 [B][heads][nb][64][D] int8; q_scale, k_scale [B][heads][nb];
 // v8 [B][heads][nb][D][64] (each block transposed, the layout the attention's
 // P V product reads); v_scale, k_mean [B][heads][D].
+// Padded layouts (a T x H x W grid whose H or W is not a multiple of 8, the sibling
+// "video_sparse_attn" page's variable block sizes): padding positions are not tokens.
+// They are left out of the block sums, the maxima and the k mean, whose divisor is the
+// token count, and their codes are 0.  The instances without kPad carry none of that.
 // All kernels are HBM-bound passes with coalesced 16-byte loads.
 #include "nabla_device.h"
 #include "nabla_launch.h"
@@ -23,6 +27,20 @@
 namespace nabla {
 
 constexpr int kQuantChunk = 1024;  // tokens per partial channel maximum of v
+
+// The patch grid of a padded layout: Hv x Wv latents on Ht x Wt patches per frame.
+struct QuantPad {
+    int Ht, Wt, Hv, Wv;
+};
+// Patch rows / columns of block j that are tokens.
+__device__ __forceinline__ void qpatch(const QuantPad &g, int j, int &vr, int &vc) {
+    const int th = (j / g.Wt) % g.Ht, tw = j % g.Wt;
+    vr = min(kTile, g.Hv - th * kTile);
+    vc = min(kTile, g.Wv - tw * kTile);
+}
+__device__ __forceinline__ bool qrow_ok(int r, int vr, int vc) {
+    return (r >> 3) < vr && (r & 7) < vc;
+}
 
 // Eight consecutive input elements widened to fp32 (exact for bf16 and fp32); one 16-byte
 // load for bf16, two for fp32.
@@ -41,10 +59,10 @@ __device__ __forceinline__ void load8_f32(const float *p, float (&x)[8]) {
 // bs[item][d] = sequential fp32 sum of the block's 64 tokens, item = (b*heads + h)*nb + j.
 // 256 lanes = 16 blocks x D/8 lanes of 8 channels (16-byte loads); each lane adds its 64
 // rows in token order, 16 rows of loads in flight at a time.
-template <int D, typename Tin>
+template <int D, typename Tin, bool kPad>
 __global__ __launch_bounds__(256) void quant_ksum_kernel(const Tin *__restrict__ k,
                                                          float *__restrict__ bs, int S,
-                                                         int heads, int64_t items) {
+                                                         int heads, int64_t items, QuantPad g) {
     constexpr int CG = D / 8;                // lanes per block
     constexpr int BPW = 256 / CG;            // blocks per workgroup
     const int nb = S / kBlock;
@@ -56,26 +74,31 @@ __global__ __launch_bounds__(256) void quant_ksum_kernel(const Tin *__restrict__
     const int64_t tok = (int64_t)heads * D;
     const Tin *src = k + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D + 8 * cg;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int vr = kTile, vc = kTile;
+    if constexpr (kPad) qpatch(g, j, vr, vc);
     for (int r0 = 0; r0 < kBlock; r0 += 16) {
         float x[16][8];
 #pragma unroll
         for (int r = 0; r < 16; ++r) load8_f32(src + (int64_t)(r0 + r) * tok, x[r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
+        for (int r = 0; r < 16; ++r) {
+            if (kPad && !qrow_ok(r0 + r, vr, vc)) continue;  // padding: not a token
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] += x[r][i];
+        }
     }
     float *dst = bs + item * D + 8 * cg;
     *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     *reinterpret_cast<float4 *>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
-// km[bh][d] = (sequential sum over blocks of bs) / S.  One workgroup per (b, head) and
+// km[bh][d] = (sequential sum over blocks of bs) / ntok (S unless the layout is padded).  One workgroup per (b, head) and
 // 32 channels: the 256 lanes stage runs of 128 blocks into LDS (coalesced), then 32 lanes
 // add them in block order.
 template <int D>
 __global__ __launch_bounds__(256) void quant_kmean_kernel(const float *__restrict__ bs,
-                                                          float *__restrict__ km, int S) {
+                                                          float *__restrict__ km, int S,
+                                                          int ntok) {
     constexpr int RUN = 128;
     __shared__ float stage[RUN][33];
     const int nb = S / kBlock;
@@ -92,7 +115,7 @@ __global__ __launch_bounds__(256) void quant_kmean_kernel(const float *__restric
         if (tid < 32)
             for (int j = 0; j < n; ++j) acc += stage[j][tid];
     }
-    if (tid < 32) km[bh * D + d0 + tid] = acc / (float)S;
+    if (tid < 32) km[bh * D + d0 + tid] = acc / (float)ntok;  // ntok: the token count
 }
 
 __device__ __forceinline__ uint32_t int8_code(float x, float scale) {
@@ -105,14 +128,15 @@ __device__ __forceinline__ uint32_t int8_code(float x, float scale) {
 // k - k_mean.  Lane t holds the 8-element chunks e = r*256 + t (row e / (D/8)) in
 // registers, the block maximum comes from a wave reduction and LDS, then the codes are
 // written as 8-byte runs in the same row-major order.
-template <int D, typename Tin>
+template <int D, typename Tin, bool kPad>
 __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q,
                                                        const Tin *__restrict__ k,
                                                        const float *__restrict__ km,
                                                        int8_t *__restrict__ q8,
                                                        float *__restrict__ qs,
                                                        int8_t *__restrict__ k8,
-                                                       float *__restrict__ ks, int S, int heads) {
+                                                       float *__restrict__ ks, int S, int heads,
+                                                       QuantPad g) {
     constexpr int CH = D / 8;                  // 8-element chunks per row
     constexpr int CPT = kBlock * CH / 256;     // chunks per lane
     __shared__ float wmax[4];
@@ -138,6 +162,15 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q
         for (int r = 0; r < CPT; ++r)
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[r][i] = x[r][i] - m[i];
+    }
+    if constexpr (kPad) {  // padding rows: not tokens, value 0 (no maximum, code 0)
+        int vr, vc;
+        qpatch(g, j, vr, vc);
+#pragma unroll
+        for (int r = 0; r < CPT; ++r)
+            if (!qrow_ok((r * 256 + tid) / CH, vr, vc))
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[r][i] = 0.0f;
     }
 #pragma unroll
     for (int r = 0; r < CPT; ++r)
@@ -167,10 +200,10 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q
 // part[(bh * nchunk + c) * D + d] = max |v| over tokens [c*1024, (c+1)*1024) of channel d.
 // 256 lanes = 256 / (D/8) token rows x D/8 lanes of 8 channels (16-byte loads); the rows'
 // maxima meet in LDS.
-template <int D, typename Tin>
+template <int D, typename Tin, bool kPad>
 __global__ __launch_bounds__(256) void quant_vmax_kernel(const Tin *__restrict__ v,
                                                          float *__restrict__ part, int S,
-                                                         int heads, int nchunk) {
+                                                         int heads, int nchunk, QuantPad g) {
     constexpr int CG = D / 8, ROWS = 256 / CG;
     __shared__ float red[ROWS][D + 1];
     const int64_t item = blockIdx.x;  // bh * nchunk + c
@@ -185,8 +218,15 @@ __global__ __launch_bounds__(256) void quant_vmax_kernel(const Tin *__restrict__
         float x[4][8];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            if (t + u * ROWS < t1)
-                load8_f32(src + (int64_t)(t + u * ROWS) * tok, x[u]);
+            const int tu = t + u * ROWS;
+            bool ok = tu < t1;
+            if (kPad && ok) {  // a padding position is not a token
+                int vr, vc;
+                qpatch(g, tu / kBlock, vr, vc);
+                ok = qrow_ok(tu % kBlock, vr, vc);
+            }
+            if (ok)
+                load8_f32(src + (int64_t)tu * tok, x[u]);
             else
 #pragma unroll
                 for (int i = 0; i < 8; ++i) x[u][i] = 0.0f;
@@ -220,11 +260,11 @@ __global__ __launch_bounds__(D) void quant_vscale_kernel(const float *__restrict
 // One workgroup of 256 lanes per (b, head, block): the block's [64][D] values go to LDS
 // (16-byte loads), then each lane writes 16-byte runs of the transposed codes (row d,
 // keys 16c .. 16c+15).
-template <int D, typename Tin>
+template <int D, typename Tin, bool kPad>
 __global__ __launch_bounds__(256) void quant_v_kernel(const Tin *__restrict__ v,
                                                       const float *__restrict__ vs,
                                                       uint8_t *__restrict__ v8, int S,
-                                                      int heads) {
+                                                      int heads, QuantPad g) {
     constexpr int CH = D / 8;
     __shared__ float tile[kBlock][D + 1];
     const int nb = S / kBlock;
@@ -233,11 +273,16 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const Tin *__restrict__ v,
     const int b = bh / heads, h = bh % heads, tid = threadIdx.x;
     const int64_t tok = (int64_t)heads * D;
     const Tin *src = v + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D;
+    int vr = kTile, vc = kTile;
+    if constexpr (kPad) qpatch(g, j, vr, vc);
 #pragma unroll
     for (int r = 0; r < kBlock * CH / 256; ++r) {
         const int e = r * 256 + tid, row = e / CH, c = e % CH;
         float x[8];
         load8_f32(src + row * tok + 8 * c, x);
+        if (kPad && !qrow_ok(row, vr, vc))  // padding: code 0
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) tile[row][8 * c + i] = x[i];
     }
@@ -271,10 +316,11 @@ size_t quant_workspace_bytes(int B, int S, int heads, int D) {
     return round256q((size_t)B * heads * nb * D * 4) + round256q((size_t)B * heads * nchunk * D * 4);
 }
 
-template <int D, typename Tin>
+template <int D, typename Tin, bool kPad>
 static hipError_t launch_quant_t(const void *q, const void *k, const void *v, int B, int S,
                                  int heads, int8_t *q8, float *qs, int8_t *k8, float *ks,
-                                 uint8_t *v8, float *vs, float *km, void *ws, hipStream_t st) {
+                                 uint8_t *v8, float *vs, float *km, int ntok, QuantPad g,
+                                 void *ws, hipStream_t st) {
     const int nb = S / kBlock;
     const int nchunk = (S + kQuantChunk - 1) / kQuantChunk;
     const int64_t items = (int64_t)B * heads * nb;
@@ -284,33 +330,48 @@ static hipError_t launch_quant_t(const void *q, const void *k, const void *v, in
     const Tin *qi = static_cast<const Tin *>(q), *ki = static_cast<const Tin *>(k),
               *vi = static_cast<const Tin *>(v);
     constexpr int kBlocksPerWg = 256 / (D / 8);
-    hipLaunchKernelGGL((quant_ksum_kernel<D, Tin>), dim3((items + kBlocksPerWg - 1) / kBlocksPerWg),
-                       dim3(256), 0, st, ki, bs, S, heads, items);
+    hipLaunchKernelGGL((quant_ksum_kernel<D, Tin, kPad>),
+                       dim3((items + kBlocksPerWg - 1) / kBlocksPerWg), dim3(256), 0, st, ki, bs,
+                       S, heads, items, g);
     hipLaunchKernelGGL((quant_kmean_kernel<D>), dim3(B * heads * (D / 32)), dim3(256), 0, st, bs,
-                       km, S);
-    hipLaunchKernelGGL((quant_qk_kernel<D, Tin>), dim3(items, 2), dim3(256), 0, st, qi, ki, km,
-                       q8, qs, k8, ks, S, heads);
-    hipLaunchKernelGGL((quant_vmax_kernel<D, Tin>), dim3(B * heads * nchunk), dim3(256), 0, st,
-                       vi, part, S, heads, nchunk);
+                       km, S, ntok);
+    hipLaunchKernelGGL((quant_qk_kernel<D, Tin, kPad>), dim3(items, 2), dim3(256), 0, st, qi, ki,
+                       km, q8, qs, k8, ks, S, heads, g);
+    hipLaunchKernelGGL((quant_vmax_kernel<D, Tin, kPad>), dim3(B * heads * nchunk), dim3(256), 0,
+                       st, vi, part, S, heads, nchunk, g);
     hipLaunchKernelGGL((quant_vscale_kernel<D>), dim3(B * heads), dim3(D), 0, st, part, vs,
                        nchunk);
-    hipLaunchKernelGGL((quant_v_kernel<D, Tin>), dim3(items), dim3(256), 0, st, vi, vs, v8, S,
-                       heads);
+    hipLaunchKernelGGL((quant_v_kernel<D, Tin, kPad>), dim3(items), dim3(256), 0, st, vi, vs, v8,
+                       S, heads, g);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_qkv(const void *q, const void *k, const void *v, bool bf16_in, int B,
                             int S, int heads, int D, int8_t *q8, float *qs, int8_t *k8,
-                            float *ks, uint8_t *v8, float *vs, float *km, void *ws,
-                            hipStream_t stream) {
-#define NABLA_QUANT(DD, T)                                                                     \
-    return launch_quant_t<DD, T>(q, k, v, B, S, heads, q8, qs, k8, ks, v8, vs, km, ws, stream)
-    if (D == 128) {
-        if (bf16_in) NABLA_QUANT(128, bf16);
-        NABLA_QUANT(128, float);
+                            float *ks, uint8_t *v8, float *vs, float *km, int T, int Hv, int Wv,
+                            void *ws, hipStream_t stream) {
+    const bool pad = Hv > 0;
+    QuantPad g{0, 0, 0, 0};
+    int ntok = S;
+    if (pad) {
+        g = QuantPad{(Hv + kTile - 1) / kTile, (Wv + kTile - 1) / kTile, Hv, Wv};
+        ntok = T * Hv * Wv;
     }
-    if (bf16_in) NABLA_QUANT(64, bf16);
-    NABLA_QUANT(64, float);
+#define NABLA_QUANT(DD, TT, P)                                                                  \
+    return launch_quant_t<DD, TT, P>(q, k, v, B, S, heads, q8, qs, k8, ks, v8, vs, km, ntok, g, \
+                                     ws, stream)
+#define NABLA_QUANT_PAD(DD, TT)                                                                 \
+    do {                                                                                        \
+        if (pad) NABLA_QUANT(DD, TT, true);                                                     \
+        NABLA_QUANT(DD, TT, false);                                                             \
+    } while (0)
+    if (D == 128) {
+        if (bf16_in) NABLA_QUANT_PAD(128, bf16);
+        NABLA_QUANT_PAD(128, float);
+    }
+    if (bf16_in) NABLA_QUANT_PAD(64, bf16);
+    NABLA_QUANT_PAD(64, float);
+#undef NABLA_QUANT_PAD
 #undef NABLA_QUANT
 }
 

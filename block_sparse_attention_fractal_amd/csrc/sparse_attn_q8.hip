@@ -51,6 +51,8 @@ constexpr float kQLog2C = 6.807354922057604f;  // log2(112): 112 * 2^2 = 448, th
 // fma turns it into the logit, with no int -> float conversion.
 constexpr int kQBias = 0x4B400000;
 constexpr float kQBiasF = 12582912.0f;  // 1.5 * 2^23
+// A padding key's score: below every biased score, so it never sets the tile maximum.
+constexpr int kQMasked = (int)0x80000000u;
 
 template <int D>
 struct AttnQ8Shared {
@@ -79,12 +81,14 @@ __device__ __forceinline__ int imax16(const i32x16 &s) {
 }
 
 
-template <int D>
+// kPad: the layout is a padded grid (Hv x Wv latents, partial patches); padding keys are
+// never keys.  The instance without it carries none of that code.
+template <int D, bool kPad>
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     const int8_t *__restrict__ q8, const float *__restrict__ qsc, const int8_t *__restrict__ k8,
     const float *__restrict__ ksc, const uint8_t *__restrict__ v8,
     const float *__restrict__ vsc, bf16 *__restrict__ o, int S, int heads, int Tt, int Ht,
-    int Wt, int groups_per_bh, int ngroups, const int32_t *__restrict__ kv_nb,
+    int Wt, int Hv, int Wv, int groups_per_bh, int ngroups, const int32_t *__restrict__ kv_nb,
     const int32_t *__restrict__ kv_inds, float scale_log2, const int32_t *__restrict__ order,
     int32_t *__restrict__ counter) {
     constexpr int KS = D / 32;                 // k-steps of the INT8 score product
@@ -240,6 +244,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     bool pend = false;      // a listed tile's scores wait for their softmax and P V
     int pend_stage = 0;
     float pend_unit = 0.0f;
+    int pend_j = 0;  // the pending tile's block (padded layouts: its patch extent)
 
     // K fragments of the tile in `stage`: (mt, ks) is one contiguous 1 KiB read
     auto kread = [&](int stage, i32x4 (&kf)[2][KS]) {
@@ -314,10 +319,44 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     };
     // the pending tile (scores in sold): softmax, then P V and the row sums; the first half
     // of the V^T fragments is read before the softmax, the second half after it
-    auto finish = [&](const i32x16 (&sold)[2]) {
+    auto finish = [&](i32x16 (&sold)[2]) {
         i32x8 va[DH];
         vread(pend_stage, 0, va);
+        // a partial patch of a padded grid: its padding positions are not keys (lane
+        // (n, hi) holds key 32 hi + 16 mt + j in register j of half mt, and byte t of the
+        // packed weights is key 32 hi + t): their scores drop out of the tile maximum, and
+        // their weights are cleared after packing (a 0 block scale could turn a forced
+        // -inf logit into NaN)
+        int vr = kTile, vc = kTile;
+        if constexpr (kPad) {
+            const int th = (pend_j / Wt) % Ht, tw = pend_j % Wt;
+            vr = min(kTile, Hv - th * kTile);
+            vc = min(kTile, Wv - tw * kTile);
+            if (vr < kTile || vc < kTile) {
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj) {
+                        const int key = 32 * hi + 16 * mt + jj;
+                        if (!((key >> 3) < vr && (key & 7) < vc)) sold[mt][jj] = kQMasked;
+                    }
+            }
+        }
         softmax(sold, pend_unit);
+        if constexpr (kPad) {
+            if (vr < kTile || vc < kTile) {
+#pragma unroll
+                for (int q4 = 0; q4 < 8; ++q4) {
+                    uint32_t keep = 0u;
+#pragma unroll
+                    for (int b4 = 0; b4 < 4; ++b4) {
+                        const int key = 32 * hi + 4 * q4 + b4;
+                        if ((key >> 3) < vr && (key & 7) < vc) keep |= 0xFFu << (8 * b4);
+                    }
+                    pb[q4] = (int)((uint32_t)pb[q4] & keep);
+                }
+            }
+        }
         pv(0, va, pb);
         vread(pend_stage, DH, va);
         pv(DH, va, pb);
@@ -339,7 +378,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     int pf_mem = U > 0 ? sh.umem[0] : 0;
     int pf_j = U > 0 ? sh.ulist[0] : 0;
     // one step; the scores of u_k go to snew, the pending tile's are in sold
-    auto step = [&](int kk, int stage, i32x16 (&snew)[2], const i32x16 (&sold)[2]) {
+    auto step = [&](int kk, int stage, i32x16 (&snew)[2], i32x16 (&sold)[2]) {
         const int n2 = __builtin_amdgcn_readfirstlane(pf_blk);  // u_{k+2}
         const int memk = __builtin_amdgcn_readfirstlane(pf_mem);
         const int jk = __builtin_amdgcn_readfirstlane(pf_j);     // u_k
@@ -359,6 +398,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
         pend = mine;
         pend_stage = stage;
         pend_unit = qscale * ksc[(int64_t)bh * nb + jk];
+        pend_j = jk;
         settle(n2 >= 0);
         __syncthreads();  // u_{k+1} has landed; everyone is done with u_{k-1}'s stage
     };
@@ -412,17 +452,23 @@ size_t sparse_attn_q8_workspace_bytes(int B, int S, int heads, int Tt, int Ht, i
 template <int D>
 static hipError_t launch_q8_t(const int8_t *q8, const float *qs, const int8_t *k8,
                               const float *ks, const uint8_t *v8, const float *vs, int B, int S,
-                              int heads, int Tt, int Ht, int Wt, const int32_t *kv_nb,
-                              const int32_t *kv_inds, float scale_log2, void *o, void *ws,
-                              hipStream_t stream) {
-    const int resident = resident_workgroups<sparse_attn_q8_kernel<D>>(kAttnThreads);
+                              int heads, int Tt, int Ht, int Wt, int Hv, int Wv,
+                              const int32_t *kv_nb, const int32_t *kv_inds, float scale_log2,
+                              void *o, void *ws, hipStream_t stream) {
+    const int resident = resident_workgroups<sparse_attn_q8_kernel<D, false>>(kAttnThreads);
     if (resident <= 0) return hipErrorInvalidDevice;
     const AttnSchedule sc =
         launch_attn_plan(kv_nb, kv_inds, B, S, heads, Tt, Ht, Wt, resident, ws, stream);
-    hipLaunchKernelGGL(sparse_attn_q8_kernel<D>, dim3(sc.grid), dim3(kAttnThreads), 0, stream,
-                       q8, qs, k8, ks, v8, vs, static_cast<bf16 *>(o), S, heads, Tt, Ht, Wt,
-                       sc.groups_per_bh, sc.ngroups, kv_nb, kv_inds, scale_log2, sc.order,
-                       sc.counter);
+    if (Hv > 0)
+        hipLaunchKernelGGL((sparse_attn_q8_kernel<D, true>), dim3(sc.grid), dim3(kAttnThreads), 0,
+                           stream, q8, qs, k8, ks, v8, vs, static_cast<bf16 *>(o), S, heads, Tt,
+                           Ht, Wt, Hv, Wv, sc.groups_per_bh, sc.ngroups, kv_nb, kv_inds,
+                           scale_log2, sc.order, sc.counter);
+    else
+        hipLaunchKernelGGL((sparse_attn_q8_kernel<D, false>), dim3(sc.grid), dim3(kAttnThreads),
+                           0, stream, q8, qs, k8, ks, v8, vs, static_cast<bf16 *>(o), S, heads,
+                           Tt, Ht, Wt, 0, 0, sc.groups_per_bh, sc.ngroups, kv_nb, kv_inds,
+                           scale_log2, sc.order, sc.counter);
     return hipGetLastError();
 }
 
@@ -430,13 +476,13 @@ hipError_t launch_sparse_attn_q8(const int8_t *q8, const float *qs, const int8_t
                                  const float *ks, const uint8_t *v8, const float *vs, int B,
                                  int S, int heads, int D, int Tt, int Ht, int Wt,
                                  const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                                 void *o, void *ws, hipStream_t stream) {
+                                 int Hv, int Wv, void *o, void *ws, hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
     if (D == 128)
-        return launch_q8_t<128>(q8, qs, k8, ks, v8, vs, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds,
-                                scale_log2, o, ws, stream);
-    return launch_q8_t<64>(q8, qs, k8, ks, v8, vs, B, S, heads, Tt, Ht, Wt, kv_nb, kv_inds,
-                           scale_log2, o, ws, stream);
+        return launch_q8_t<128>(q8, qs, k8, ks, v8, vs, B, S, heads, Tt, Ht, Wt, Hv, Wv, kv_nb,
+                                kv_inds, scale_log2, o, ws, stream);
+    return launch_q8_t<64>(q8, qs, k8, ks, v8, vs, B, S, heads, Tt, Ht, Wt, Hv, Wv, kv_nb,
+                           kv_inds, scale_log2, o, ws, stream);
 }
 
 }  // namespace nabla

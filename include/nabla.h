@@ -346,6 +346,21 @@ nabla_status nabla_quant_qkv(const void *q, const void *k, const void *v, nabla_
                              int B, int S, int heads, int head_dim, int8_t *q8, float *q_scale,
                              int8_t *k8, float *k_scale, uint8_t *v8, float *v_scale,
                              float *k_mean, void *ws, size_t ws_bytes, void *stream);
+/*
+ * The quantizer on the fractal layout of a T x H x W latent grid whose H or W need not be
+ * multiples of 8 (S = T * ceil(H/8) * ceil(W/8) * 64; the sibling "video_sparse_attn"
+ * page's variable block sizes).  Padding positions of partial patches are not tokens:
+ * they are left out of the block sums and the k mean, whose divisor is the token count
+ * T * H * W, and out of every block and channel maximum; their codes are 0 whatever the
+ * inputs hold there.  Everything else is nabla_quant_qkv (its workspace for this S); on a
+ * grid of whole patches the result equals it.
+ * Errors: those of nabla_quant_qkv; INVALID_ARG also for T, H or W < 1.
+ */
+nabla_status nabla_quant_qkv_grid(const void *q, const void *k, const void *v,
+                                  nabla_dtype dtype, int B, int T, int H, int W, int heads,
+                                  int head_dim, int8_t *q8, float *q_scale, int8_t *k8,
+                                  float *k_scale, uint8_t *v8, float *v_scale, float *k_mean,
+                                  void *ws, size_t ws_bytes, void *stream);
 /* Bytes of workspace nabla_sparse_attn_fwd_q8 needs (its work schedule; the same formula
  * as nabla_sparse_attn_workspace).  0 if the sizes or the grid are invalid. */
 size_t nabla_sparse_attn_q8_workspace(int B, int S, int heads, int Tt, int Ht, int Wt);
@@ -375,6 +390,24 @@ nabla_status nabla_sparse_attn_fwd_q8(const int8_t *q8, const float *q_scale, co
                                       int head_dim, const int32_t *kv_nb, const int32_t *kv_inds,
                                       float scale, int Tt, int Ht, int Wt, void *o, void *ws,
                                       size_t ws_bytes, void *stream);
+
+/*
+ * The quantized attention on the codes of nabla_quant_qkv_grid for a T x H x W grid
+ * (S = T * ceil(H/8) * ceil(W/8) * 64; tile grid (T, ceil(H/8), ceil(W/8))): padding
+ * positions of partial patches are never keys (their weights are 0).  Query rows at
+ * padding positions are computed too and are dropped by the inverse permute.  Everything
+ * else is nabla_sparse_attn_fwd_q8 with that tile grid (workspace:
+ * nabla_sparse_attn_q8_workspace(B, S, heads, T, ceil(H/8), ceil(W/8))); on a grid of
+ * whole patches the result equals it.
+ * Errors: those of nabla_sparse_attn_fwd_q8; INVALID_ARG also for T, H or W < 1.
+ */
+nabla_status nabla_sparse_attn_fwd_q8_grid(const int8_t *q8, const float *q_scale,
+                                           const int8_t *k8, const float *k_scale,
+                                           const uint8_t *v8, const float *v_scale, int B, int T,
+                                           int H, int W, int heads, int head_dim,
+                                           const int32_t *kv_nb, const int32_t *kv_inds,
+                                           float scale, void *o, void *ws, size_t ws_bytes,
+                                           void *stream);
 
 #ifdef __cplusplus
 }

@@ -871,7 +871,7 @@ int orc_attention_bwd_grid(const float *q, const float *k, const float *v, const
 /*     "sv_f8" kernels, full range at P = 1); the row sum is taken over the    */
 /*     same quantized weights, so o is a convex combination of the V codes:   */
 /*     o[d] = vs[d] * sum_c p8_c v8_cd / sum_c p8_c, all in fp64;             */
-/*   - padded layouts (Q7): padding positions are not tokens, so they are left */
+/*   - padded layouts (Q9): padding positions are not tokens, so they are left */
 /*     out of the k mean (divided by the token count) and of every maximum,  */
 /*     their codes are 0, and they are never keys.                            */
 /* ------------------------------------------------------------------------- */
@@ -921,7 +921,7 @@ static int8_t orc_int8_code(float x, float scale) {
 /* q8, k8: [B][heads][nb][64][D] int8; qs, ks: [B][heads][nb]; v8: [B][heads][nb][D][64]   */
 /* e4m3 codes (each block transposed); vs, km: [B][heads][D]. */
 /* gH, gW: the latent extents of a padded layout, whose padding positions are not tokens
- * (Q7): they are left out of the k mean (its divisor is the token count) and of every
+ * (Q9): they are left out of the k mean (its divisor is the token count) and of every
  * maximum, and their codes are 0.  0: every position is a token. */
 static int orc_quant_qkv_impl(const float *q, const float *k, const float *v, int B, int S,
                               int heads, int D, int gH, int gW, int8_t *q8, float *qs,
@@ -1005,7 +1005,7 @@ int orc_quant_qkv(const float *q, const float *k, const float *v, int B, int S, 
     return orc_quant_qkv_impl(q, k, v, B, S, heads, D, 0, 0, q8, qs, k8, ks, v8, vs, km);
 }
 
-/* The quantizer on the padded fractal layout of a T x H x W grid (Q7). */
+/* The quantizer on the padded fractal layout of a T x H x W grid (Q9). */
 int orc_quant_qkv_grid(const float *q, const float *k, const float *v, int B, int T, int H,
                        int W, int heads, int D, int8_t *q8, float *qs, int8_t *k8, float *ks,
                        uint8_t *v8, float *vs, float *km) {

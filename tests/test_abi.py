@@ -43,14 +43,15 @@ def test_exports_every_declared_symbol(L):
                           "nabla_block_mask_grid", "nabla_sparse_attn_workspace_grid",
                           "nabla_sparse_attn_fwd_grid", "nabla_quant_qkv_workspace",
                           "nabla_quant_qkv", "nabla_sparse_attn_q8_workspace",
-                          "nabla_sparse_attn_fwd_q8", "nabla_sparse_attn_bwd_grid"}
+                          "nabla_sparse_attn_fwd_q8", "nabla_sparse_attn_bwd_grid",
+                          "nabla_quant_qkv_grid", "nabla_sparse_attn_fwd_q8_grid"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 7
+    assert L.nabla_abi_version() == 8
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"
@@ -248,6 +249,16 @@ def test_quant_validation(L):
     assert call(D=96) == UNSUP
     assert call(ws=None) == WS
     assert call(wsb=L.nabla_quant_qkv_workspace(1, 8192, 8, 128) - 1) == WS
+    g = L.nabla_quant_qkv_grid
+
+    def gcall(T=2, H=12, W=20, q=FAKE, dt=BF16, D=128, wsb=1 << 40):
+        return g(q, FAKE, FAKE, dt, 1, T, H, W, 8, D, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, wsb, None)
+
+    for kw in ({"T": 0}, {"H": 0}, {"W": -2}, {"q": None}, {"dt": 7}):
+        assert gcall(**kw) == INVALID, kw
+    assert gcall(D=96) == UNSUP
+    assert gcall(wsb=L.nabla_quant_qkv_workspace(1, 2 * 2 * 3 * 64, 8, 128) - 1) == WS
 
 
 def test_sparse_attn_q8_validation(L):
@@ -269,6 +280,16 @@ def test_sparse_attn_q8_validation(L):
     assert call(S=64 * 4097, tiles=(0, 0, 0)) == UNSUP
     assert call(ws=None) == WS
     assert call(wsb=L.nabla_sparse_attn_q8_workspace(1, 8192, 8, 8, 4, 4) - 1) == WS
+    g = L.nabla_sparse_attn_fwd_q8_grid
+
+    def gcall(T=2, H=12, W=20, q8=FAKE, D=128, scale=0.0, wsb=1 << 40):
+        return g(q8, FAKE, FAKE, FAKE, FAKE, FAKE, 1, T, H, W, 8, D, FAKE, FAKE, scale, FAKE,
+                 FAKE, wsb, None)
+
+    for kw in ({"T": 0}, {"W": 0}, {"q8": None}, {"scale": math.nan}):
+        assert gcall(**kw) == INVALID, kw
+    assert gcall(D=32) == UNSUP
+    assert gcall(wsb=L.nabla_sparse_attn_q8_workspace(1, 2 * 2 * 3 * 64, 8, 2, 2, 3) - 1) == WS
 
 
 def test_permute_and_sta_validation(L):

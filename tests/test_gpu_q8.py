@@ -77,8 +77,9 @@ def case(name, orc, dev):
     return c
 
 
-def q8_bound(orc, oz, kv_nb, kv_inds, row_ids, o, scale=0.0):
-    """Per-element bound [len(row_ids), 64, D] on |o_kernel - o_oracle| (module docstring)."""
+def q8_bound(orc, oz, kv_nb, kv_inds, row_ids, o, scale=0.0, valid=None):
+    """Per-element bound [len(row_ids), 64, D] on |o_kernel - o_oracle| (module docstring).
+    valid: bool [S] of a padded layout (padding positions are never keys), or None."""
     q8, k8 = oz["q8"], oz["k8"]
     B, heads, nb, _, D = q8.shape
     if not scale or scale <= 0:
@@ -96,6 +97,9 @@ def q8_bound(orc, oz, kv_nb, kv_inds, row_ids, o, scale=0.0):
         kk = k8[b, h, blocks].reshape(-1, D).astype(np.int64)             # [keys, D]
         dots = q8[b, h, i].astype(np.int64) @ kk.T                          # [64, keys]
         z = scale * float(oz["qs"][b, h, i]) * (dots * np.repeat(oz["ks"][b, h, blocks], 64))
+        if valid is not None:
+            keys = (64 * blocks[:, None] + np.arange(64)[None, :]).ravel()
+            z = np.where(valid[keys][None, :], z, -np.inf)
         P = np.exp(z - z.max(axis=1, keepdims=True))
         sp = P.sum(axis=1, keepdims=True)
         v = vdec[b, h, blocks].transpose(0, 2, 1).reshape(-1, D)            # [keys, D]
@@ -248,3 +252,60 @@ def test_q8_run_twice_bitwise(orc, dev):
     assert torch.equal(o1, o2)
     o3 = nabla.nabla_sparse_attn_fwd_q8(c["gz"], *lists)  # other grouping, same result
     assert torch.equal(o1, o3)
+
+
+# ---- padded fractal layouts (H or W not a multiple of 8): padding is not a token
+
+@pytest.mark.parametrize("T,H,W,h,D,seed", [(2, 12, 20, 2, 128, 61), (1, 20, 28, 3, 64, 62)])
+def test_q8_padded_quantizer_and_attention(orc, dev, T, H, W, h, D, seed):
+    """The grid entry points on a padded layout whose padding positions hold a large value
+    (7.0) that must be ignored: codes and scales bit-exact against oracle.quant_qkv(grid=...),
+    attention within the e4m3 bound of oracle.attention_q8(grid=...) on every element."""
+    rng = np.random.default_rng(seed)
+    grid = (T, H, W)
+    nat = [rng.standard_normal((1, T, H, W, h, D)).astype(np.float32) for _ in range(3)]
+    valid = orc.token_valid(T, H, W)
+    frac = []
+    for a in nat:
+        x = orc.fractal_permute(a)
+        x[:, ~valid] = 7.0
+        frac.append(torch.from_numpy(x).to(torch.bfloat16))
+    S = frac[0].shape[1]
+    nb = S // 64
+    say("[q8 padded] T=%d H=%d W=%d heads=%d D=%d (S=%d)" % (T, H, W, h, D, S))
+    gz = nabla.nabla_quant_qkv(*[t.to(dev) for t in frac], grid=grid)
+    torch.cuda.synchronize()
+    oz = orc.quant_qkv(*[t.float().numpy() for t in frac], grid=grid)
+    for gk, ok in zip(QUANT_KEYS, ORC_KEYS):
+        a = gz[gk].cpu().numpy()
+        assert np.array_equal(a.view(np.uint8), oz[ok].view(np.uint8)), gk
+    kv_nb, kv_inds = synth.random_lists(rng, 1, h, nb, 0.5)
+    kv_nb[0, 0, 0] = 0
+    kv_nb[0, h - 1, nb - 1] = nb
+    o = nabla.nabla_sparse_attn_fwd_q8(gz, torch.from_numpy(kv_nb).to(dev),
+                                       torch.from_numpy(kv_inds).to(dev), grid=grid)
+    torch.cuda.synchronize()
+    ids, want = orc.attention_q8(oz, kv_nb, kv_inds, grid=grid)
+    gt = o.float().cpu().numpy()
+    got = np.stack([gt[0, 64 * (int(r) % nb):64 * (int(r) % nb + 1), int(r) // nb] for r in ids])
+    bound = q8_bound(orc, oz, kv_nb, kv_inds, ids, want, valid=valid)
+    check(got, want, bound, "q8 padded")
+
+
+def test_q8_grid_of_whole_patches_is_plain(orc, dev):
+    """On a grid of whole patches the grid entry points give the plain calls' bits."""
+    rng = np.random.default_rng(63)
+    T, H, W, h, D = 2, 16, 8, 2, 128
+    S = T * H * W
+    g = [torch.from_numpy(rng.standard_normal((1, S, h, D)).astype(np.float32)).to(torch.bfloat16).to(dev)
+         for _ in range(3)]
+    za = nabla.nabla_quant_qkv(*g, grid=(T, H, W))
+    zb = nabla.nabla_quant_qkv(*g)
+    for n in QUANT_KEYS:
+        assert torch.equal(za[n], zb[n]), n
+    kv_nb, kv_inds = synth.random_lists(rng, 1, h, S // 64, 0.5)
+    nb_t, inds_t = torch.from_numpy(kv_nb).to(dev), torch.from_numpy(kv_inds).to(dev)
+    oa = nabla.nabla_sparse_attn_fwd_q8(za, nb_t, inds_t, grid=(T, H, W))
+    ob = nabla.nabla_sparse_attn_fwd_q8(za, nb_t, inds_t, tiles=(T, H // 8, W // 8))
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
