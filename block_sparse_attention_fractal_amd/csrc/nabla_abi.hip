@@ -205,6 +205,32 @@ nabla_status attn_fwd(const void *q, const void *k, const void *v, nabla_dtype d
 
 }  // namespace
 
+namespace {
+
+// Hv > 0: a padded layout (Hv x Wv latents, tile grid (., Ht, Wt)); 0: whole blocks.
+nabla_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
+                      const void *dout, const float *lse, nabla_dtype dtype, int B, int S,
+                      int heads, int head_dim, const int32_t *kv_nb, const int32_t *kv_inds,
+                      float scale, void *dq, void *dk, void *dv, int Ht, int Wt, int Hv, int Wv,
+                      void *ws, size_t ws_bytes, void *stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !kv_nb || !kv_inds || !dq || !dk || !dv ||
+        !dtype_ok(dtype))
+        return NABLA_ERR_INVALID_ARG;
+    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
+    if (scale != scale) return NABLA_ERR_INVALID_ARG;
+    if (dtype != NABLA_BF16) return NABLA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
+    if (S / kBlock > kMaxBlocks) return NABLA_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < nabla::sparse_attn_bwd_workspace_bytes(B, S, heads))
+        return NABLA_ERR_WORKSPACE;
+    if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
+    return from_hip(nabla::launch_sparse_attn_bwd(q, k, v, o, dout, lse, B, S, heads, head_dim,
+                                                  kv_nb, kv_inds, scale, dq, dk, dv, Ht, Wt, Hv,
+                                                  Wv, ws, as_stream(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 nabla_status nabla_sparse_attn_fwd_lse(const void *q, const void *k, const void *v,
@@ -237,32 +263,6 @@ size_t nabla_sparse_attn_bwd_workspace(int B, int S, int heads) {
     if (!sizes_ok(B, S, heads, 1) || S % kBlock || S / kBlock > kMaxBlocks) return 0;
     return nabla::sparse_attn_bwd_workspace_bytes(B, S, heads);
 }
-
-namespace {
-
-// Hv > 0: a padded layout (Hv x Wv latents, tile grid (., Ht, Wt)); 0: whole blocks.
-nabla_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
-                      const void *dout, const float *lse, nabla_dtype dtype, int B, int S,
-                      int heads, int head_dim, const int32_t *kv_nb, const int32_t *kv_inds,
-                      float scale, void *dq, void *dk, void *dv, int Ht, int Wt, int Hv, int Wv,
-                      void *ws, size_t ws_bytes, void *stream) {
-    if (!q || !k || !v || !o || !dout || !lse || !kv_nb || !kv_inds || !dq || !dk || !dv ||
-        !dtype_ok(dtype))
-        return NABLA_ERR_INVALID_ARG;
-    if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
-    if (scale != scale) return NABLA_ERR_INVALID_ARG;
-    if (dtype != NABLA_BF16) return NABLA_ERR_UNSUPPORTED;
-    if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
-    if (S / kBlock > kMaxBlocks) return NABLA_ERR_UNSUPPORTED;
-    if (!ws || ws_bytes < nabla::sparse_attn_bwd_workspace_bytes(B, S, heads))
-        return NABLA_ERR_WORKSPACE;
-    if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
-    return from_hip(nabla::launch_sparse_attn_bwd(q, k, v, o, dout, lse, B, S, heads, head_dim,
-                                                  kv_nb, kv_inds, scale, dq, dk, dv, Ht, Wt, Hv,
-                                                  Wv, ws, as_stream(stream)));
-}
-
-}  // namespace
 
 nabla_status nabla_sparse_attn_bwd(const void *q, const void *k, const void *v, const void *o,
                                    const void *dout, const float *lse, nabla_dtype dtype, int B,
