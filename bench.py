@@ -59,6 +59,11 @@ def parse():
                          "nabla_quant_qkv (quantizer inside the step; a variant line)")
     ap.add_argument("--bwd", action="store_true",
                     help="the training pass instead: forward with lse, then the backward (one line)")
+    ap.add_argument("--separate-permutes", action="store_true",
+                    help="permute q, k, v and o with nabla_fractal_permute around fractal-order "
+                         "calls, instead of the natural-order calls that fold the permutes into "
+                         "the estimator's and the attention's addressing (grids of whole "
+                         "patches; padded grids and --q8 always permute)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -140,10 +145,12 @@ def cpu_baseline(w, q, k, v, sta_np, g_nb, rows, flops_per_pair):
     }
 
 
-def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False):
+def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False, fold=True):
     """Run the path on workload w for `steps` timed steps; return the measurement dict.
     With topk_ratio the top-k estimator variant replaces NABLA's CDF estimator; with quant
-    the quantizer and the INT8 / FP8 attention replace the bf16 attention."""
+    the quantizer and the INT8 / FP8 attention replace the bf16 attention.  fold: on a grid
+    of whole patches (bf16 or fp32 attention), the natural-order calls read q, k, v and write
+    o where the fractal permutes would have moved them (the same rows, the same results)."""
     import ctypes
     dev = torch.device("cuda:0")
     q, k, v = qkv
@@ -182,17 +189,24 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False):
         if rc != 0:
             raise nabla.NablaError(rc, what)
 
+    fold = fold and not w.padded and not quant
+
     def step(rec=None):
         """One pass of the path; rec collects (start, end) event pairs per stage."""
         e = [ev() for _ in range(6)] if rec is not None else None
         if e: e[0].record(stream)
         if w.sta is not None:
             check(L.nabla_sta_mask(P(sta), *w.tiles, *w.sta, sp), "sta")
-        for src, dst in ((gq, qf), (gk, kf), (gv, vf)):
+        for src, dst in ((gq, qf), (gk, kf), (gv, vf)) if not fold else ():
             check(L.nabla_fractal_permute(P(src), P(dst), dt_code, B, w.T, w.H, w.W, H, D, 0, sp),
                   "permute")
         if e: e[1].record(stream)
-        if w.padded:  # partial patches: the grid entry points
+        if fold:
+            check(L.nabla_block_mask_natural(P(gq), P(gk), dt_code, B, w.T, w.H, w.W, H, D, sta_p,
+                                             w.thr, -1.0 if topk_ratio is None else topk_ratio,
+                                             P(kv_nb), P(kv_inds), P(ws), ws.numel(), sp),
+                  "mask")
+        elif w.padded:  # partial patches: the grid entry points
             check(L.nabla_block_mask_grid(P(qf), P(kf), dt_code, B, w.T, w.H, w.W, H, D, sta_p,
                                           w.thr, -1.0 if topk_ratio is None else topk_ratio,
                                           P(kv_nb), P(kv_inds), P(ws), ws.numel(), sp), "mask")
@@ -219,6 +233,10 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False):
             check(L.nabla_sparse_attn_fwd_q8(*codes, B, S, H, D, P(kv_nb), P(kv_inds), 0.0,
                                              *w.tiles, P(of), P(ws_q8), ws_q8.numel(), sp),
                   "attn q8")
+        elif fold:
+            check(L.nabla_sparse_attn_fwd_natural(P(gq), P(gk), P(gv), dt_code, B, w.T, w.H, w.W,
+                                                  H, D, P(kv_nb), P(kv_inds), 0.0, P(o_nat), None,
+                                                  P(ws_attn), ws_attn.numel(), sp), "attn")
         elif w.padded:
             check(L.nabla_sparse_attn_fwd_grid(P(qf), P(kf), P(vf), dt_code, B, w.T, w.H, w.W, H,
                                                D, P(kv_nb), P(kv_inds), 0.0, P(of), None,
@@ -228,8 +246,9 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False):
                                           P(kv_inds), 0.0, *w.tiles, P(of), P(ws_attn),
                                           ws_attn.numel(), sp), "attn")
         if e: e[4].record(stream)
-        check(L.nabla_fractal_permute(P(of), P(o_nat), dt_code, B, w.T, w.H, w.W, H, D, 1, sp),
-              "unpermute")
+        if not fold:
+            check(L.nabla_fractal_permute(P(of), P(o_nat), dt_code, B, w.T, w.H, w.W, H, D, 1, sp),
+                  "unpermute")
         if e:
             e[5].record(stream)
             rec.append(e)
@@ -270,6 +289,7 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False):
         "g_nb": g_nb,
         "sta_np": None if w.sta is None else sta.cpu().numpy(),
         "dtype": "bf16" if tdt == torch.bfloat16 else "fp32",
+        "fold": fold,
     }
 
 
@@ -400,7 +420,7 @@ def main():
     print("[bench] %s" % w.describe(), file=sys.stderr, flush=True)
     q, k, v = synth.make_qkv(w)
     m = measure(torch, nabla, w, (q, k, v), args.steps, args.warmup, topk_ratio=args.topk,
-                quant=args.q8)
+                quant=args.q8, fold=not args.separate_permutes)
     attn_tflops = m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12
     traffic = read_traffic(Q8_PMC_FILE, Q8_SRC) if args.q8 else read_traffic()
     metric = METRIC if args.topk is None else (
@@ -425,7 +445,9 @@ def main():
         "config": {"workload": w.describe(), "B": w.B, "heads": w.heads, "head_dim": w.D,
                    "T": w.T, "H": w.H, "W": w.W, "seq_len": w.S, "blocks": w.nb, "thr": w.thr,
                    "sta_window": list(w.sta) if w.sta else None, "kept_pairs": m["pairs"],
-                   "density": round(m["density"], 5)},
+                   "density": round(m["density"], 5),
+                   "permutes": "folded into the estimator's and the attention's addressing"
+                   if m["fold"] else "nabla_fractal_permute kernels"},
         "mask_ms": round(m["mask_ms"], 4),
         "attn_ms": round(m["attn_ms"], 4),
         "permute_ms": round(m["perm_ms"], 4),
@@ -434,7 +456,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "sparse_attn_kernel<128, bf16>",
+                     "kernel": "sparse_attn_kernel<128, bf16, false, %s>" % str(m["fold"]).lower(),
                      "per_launch": {"flops": m["attn_flops"], "kept_pairs": m["pairs"]}},
     }
     if args.q8:

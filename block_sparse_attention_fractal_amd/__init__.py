@@ -22,7 +22,8 @@ import torch
 __all__ = ["nabla_fractal_permute", "nabla_sta_mask", "nabla_block_mask",
            "nabla_block_mask_workspace", "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace",
            "nabla_sparse_attn_bwd", "nabla_sparse_attn_bwd_workspace", "fractal_len",
-           "nabla_quant_qkv", "nabla_sparse_attn_fwd_q8",
+           "nabla_quant_qkv", "nabla_sparse_attn_fwd_q8", "nabla_block_mask_natural",
+           "nabla_sparse_attn_fwd_natural",
            "NablaError", "lib",
            "LIB_PATH", "STATUS"]
 
@@ -71,6 +72,10 @@ def lib():
     L.nabla_sparse_attn_workspace_grid.restype = Z
     L.nabla_sparse_attn_fwd_grid.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, F, P, P, P, Z, P]
     L.nabla_sparse_attn_fwd_grid.restype = I
+    L.nabla_block_mask_natural.argtypes = [P, P, I, I, I, I, I, I, I, P, D, D, P, P, P, Z, P]
+    L.nabla_block_mask_natural.restype = I
+    L.nabla_sparse_attn_fwd_natural.argtypes = [P, P, P] + [I] * 7 + [P, P, F, P, P, P, Z, P]
+    L.nabla_sparse_attn_fwd_natural.restype = I
     L.nabla_sparse_attn_workspace.argtypes = [I, I, I, I, I, I]
     L.nabla_sparse_attn_workspace.restype = Z
     L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P, Z, P]
@@ -280,6 +285,84 @@ def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, til
                                            _p(o), None if lse is None else _p(lse),
                                            _p(workspace), workspace.numel(), _stream(q)),
            "nabla_sparse_attn_fwd")
+    return o
+
+
+def _natural_shape(q, name="q"):
+    if q.dim() != 6:
+        raise ValueError("%s must be natural-order [B, T, H, W, heads, D]" % name)
+    B, T, H, W, heads, D = q.shape
+    if H % 8 or W % 8:
+        raise ValueError("natural-order calls need H and W multiples of 8 (whole patches); "
+                         "use nabla_fractal_permute and the grid= calls instead")
+    return B, T, H, W, heads, D
+
+
+def nabla_block_mask_natural(q, k, sta=None, thr=0.9, topk_ratio=None, workspace=None,
+                             out=None):
+    """Either estimator on q, k in natural order [B, T, H, W, heads, D] (H, W multiples of 8),
+    with the fractal permute folded into the pooling (nabla_block_mask_natural): the lists
+    over fractal block indices equal nabla_block_mask's on the permuted q and k."""
+    _dev(q, "q")
+    _dev(k, "k")
+    if q.shape != k.shape or q.dtype != k.dtype:
+        raise ValueError("q and k must match in shape and dtype")
+    B, T, H, W, heads, D = _natural_shape(q)
+    nb = T * (H // 8) * (W // 8)
+    S = nb * BLOCK
+    if sta is not None:
+        _dev(sta, "sta")
+        if sta.dtype != torch.uint8 or sta.numel() != nb * nb:
+            raise ValueError("sta must be uint8 with nb*nb = %d elements" % (nb * nb))
+    need = lib().nabla_block_mask_workspace(B, S, heads, D)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
+                                                             device=q.device)
+    if out is None:
+        kv_nb = torch.empty((B, heads, nb), dtype=torch.int32, device=q.device)
+        kv_inds = torch.empty((B, heads, nb, nb), dtype=torch.int32, device=q.device)
+    else:
+        kv_nb, kv_inds = out
+    _check(lib().nabla_block_mask_natural(_p(q), _p(k), _dtype_code(q), B, T, H, W, heads, D,
+                                          _p(sta), float(thr),
+                                          -1.0 if topk_ratio is None else float(topk_ratio),
+                                          _p(kv_nb), _p(kv_inds), _p(ws), ws.numel(),
+                                          _stream(q)), "nabla_block_mask_natural")
+    return kv_nb, kv_inds
+
+
+def nabla_sparse_attn_fwd_natural(q, k, v, kv_nb, kv_inds, scale=None, workspace=None,
+                                  out=None, lse=None):
+    """The forward on q, k, v in natural order [B, T, H, W, heads, D] (H, W multiples of 8),
+    with the fractal permutes folded into the kernel (nabla_sparse_attn_fwd_natural):
+    o in natural order, bit-identical to the inverse permute of nabla_sparse_attn_fwd on
+    the permuted inputs; lse (optional, [B, heads, S] fp32) stays in fractal order."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("kv_nb", kv_nb), ("kv_inds", kv_inds)):
+        _dev(t, name)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must match in shape and dtype")
+    if kv_nb.dtype != torch.int32 or kv_inds.dtype != torch.int32:
+        raise TypeError("kv_nb and kv_inds must be int32")
+    B, T, H, W, heads, D = _natural_shape(q)
+    nb = T * (H // 8) * (W // 8)
+    S = nb * BLOCK
+    if kv_nb.numel() != B * heads * nb or kv_inds.numel() != B * heads * nb * nb:
+        raise ValueError("kv lists do not match q's shape")
+    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    if workspace is None:
+        need = lib().nabla_sparse_attn_workspace_grid(B, T, H, W, heads)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _dev(workspace, "workspace")
+    if lse is not None:
+        _dev(lse, "lse")
+        if lse.dtype != torch.float32 or lse.numel() != B * heads * S:
+            raise ValueError("lse must be float32 with B * heads * S elements")
+    _check(lib().nabla_sparse_attn_fwd_natural(_p(q), _p(k), _p(v), _dtype_code(q), B, T, H, W,
+                                               heads, D, _p(kv_nb), _p(kv_inds),
+                                               0.0 if scale is None else float(scale), _p(o),
+                                               None if lse is None else _p(lse),
+                                               _p(workspace), workspace.numel(), _stream(q)),
+           "nabla_sparse_attn_fwd_natural")
     return o
 
 

@@ -44,12 +44,14 @@ namespace nabla {
 // H, W > 0: the latent grid of a padded fractal layout (Wt = ceil(W/8) patches per row
 // of patches): a block averages its tokens only, summed in order and divided by their
 // count min(8, H - 8 ht) * min(8, W - 8 wt).  H = W = 0: whole 64-token blocks.
+// ng.W > 0: q and k are in natural order (whole patches, rows of ng.W tokens); block i's
+// rows are read where the fractal permute would have taken them from, in the same order.
 template <typename Tin>
 __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
                                                    const Tin *__restrict__ k,
                                                    float *__restrict__ qa,
                                                    float *__restrict__ ka, int S, int heads,
-                                                   int D, int H, int W) {
+                                                   int D, int H, int W, NatGrid ng) {
     constexpr int EPC = 16 / sizeof(Tin);  // elements per 16-byte chunk
     const int nb = S / kBlock;
     const int i = blockIdx.x, b = blockIdx.y;
@@ -69,7 +71,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
     const int ch = item - z * nchunks;
     const Tin *x = z ? k : q;
     float *xa = z ? ka : qa;
-    const Tin *base = x + ((int64_t)b * S + (int64_t)i * kBlock) * row_elems;
+    const bool nat = ng.W > 0;
+    const int rstep = nat ? ng.W : kTile;  // tokens between rows of a patch
+    const int64_t blk0 = nat ? nat_block_base(i, ng) : (int64_t)i * kBlock;
+    const Tin *base = x + ((int64_t)b * S + blk0) * row_elems;
     {
         float acc[EPC];
 #pragma unroll
@@ -80,7 +85,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
             uint4 raw[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u)
-                raw[u] = *reinterpret_cast<const uint4 *>(p + (int64_t)(r0 + u) * row_elems);
+                raw[u] = *reinterpret_cast<const uint4 *>(
+                    p + (int64_t)(((r0 + u) >> 3) * rstep + ((r0 + u) & 7)) * row_elems);
 #pragma unroll
             for (int u = 0; u < 16; ++u) {
                 const int r = r0 + u;
@@ -787,17 +793,20 @@ static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int 
 }
 
 hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, int B, int S,
-                                  int heads, int D, int H, int W, const uint8_t *sta, int topk,
+                                  int heads, int D, int H, int W, bool natural,
+                                  const uint8_t *sta, int topk,
                                   int32_t *kv_nb, int32_t *kv_inds, float *qa, float *ka,
                                   hipStream_t stream) {
     const int nb = S / kBlock;
     dim3 pgrid(nb, B);
     if (bf16_in)
         hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, qa, ka, S, heads, D, H, W);
+                           (const bf16 *)k, qa, ka, S, heads, D, natural ? 0 : H,
+                           natural ? 0 : W, nat_grid(natural ? W : 0));
     else
         hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
-                           (const float *)k, qa, ka, S, heads, D, H, W);
+                           (const float *)k, qa, ka, S, heads, D, natural ? 0 : H,
+                           natural ? 0 : W, nat_grid(natural ? W : 0));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int BH = B * heads;
@@ -812,17 +821,19 @@ hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, in
 }
 
 hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, int S,
-                             int heads, int D, int H, int W, const uint8_t *sta,
+                             int heads, int D, int H, int W, bool natural, const uint8_t *sta,
                              int64_t cut_fixed, float sqrt_d, int32_t *kv_nb, int32_t *kv_inds,
                              float *qa, float *ka, hipStream_t stream) {
     const int nb = S / kBlock;
     dim3 pgrid(nb, B);
     if (bf16_in)
         hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, qa, ka, S, heads, D, H, W);
+                           (const bf16 *)k, qa, ka, S, heads, D, natural ? 0 : H,
+                           natural ? 0 : W, nat_grid(natural ? W : 0));
     else
         hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
-                           (const float *)k, qa, ka, S, heads, D, H, W);
+                           (const float *)k, qa, ka, S, heads, D, natural ? 0 : H,
+                           natural ? 0 : W, nat_grid(natural ? W : 0));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int BH = B * heads;

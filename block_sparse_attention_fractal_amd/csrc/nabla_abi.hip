@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
 constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
@@ -90,9 +90,11 @@ size_t nabla_block_mask_workspace(int B, int S, int heads, int head_dim) {
 namespace {
 
 // Both estimators; ratio < 0 selects the CDF cut (thr), ratio >= 0 the top-k variant.
-// H, W > 0: the latent grid of a padded fractal layout (pooling over tokens only).
+// H, W > 0: the latent grid of a padded fractal layout (pooling over tokens only), or with
+// natural, the grid of q and k in natural order.
 nabla_status estimate(const void *q, const void *k, nabla_dtype dtype, int B, int S, int heads,
-                      int head_dim, int H, int W, const uint8_t *sta, double thr, double ratio,
+                      int head_dim, int H, int W, bool natural, const uint8_t *sta, double thr,
+                      double ratio,
                       int32_t *kv_nb, int32_t *kv_inds, void *ws, size_t ws_bytes,
                       void *stream) {
     if (!q || !k || !kv_nb || !kv_inds || !dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
@@ -114,7 +116,8 @@ nabla_status estimate(const void *q, const void *k, nabla_dtype dtype, int B, in
         const double x = ratio * (double)nb;
         const int kk = x >= (double)nb ? nb : (int)x;
         return from_hip(nabla::launch_block_mask_topk(q, k, dtype == NABLA_BF16, B, S, heads,
-                                                      head_dim, H, W, sta, kk, kv_nb, kv_inds,
+                                                      head_dim, H, W, natural, sta, kk, kv_nb,
+                                                      kv_inds,
                                                       qa, ka, as_stream(stream)));
     }
     // cut on the 2^-48 grid: ceil(fl32(1 - thr) * 2^48), exact in double
@@ -122,7 +125,8 @@ nabla_status estimate(const void *q, const void *k, nabla_dtype dtype, int B, in
     const int64_t cut_fixed = (int64_t)ceil(ldexp((double)cut32, 48));
     const float sqrt_d = (float)sqrt((double)head_dim);
     return from_hip(nabla::launch_block_mask(q, k, dtype == NABLA_BF16, B, S, heads, head_dim,
-                                             H, W, sta, cut_fixed, sqrt_d, kv_nb, kv_inds, qa,
+                                             H, W, natural, sta, cut_fixed, sqrt_d, kv_nb,
+                                             kv_inds, qa,
                                              ka, as_stream(stream)));
 }
 
@@ -134,6 +138,17 @@ long long grid_len(int B, int T, int H, int W, int heads, int head_dim) {
     return S;
 }
 
+// S = T*H*W of a natural-order [B][T][H][W][heads][head_dim] grid read in place of its
+// fractal permute; -1 when the sizes are invalid, -2 when the grid has partial patches or
+// a patch's rows lie too far apart for the kernels' 32-bit in-tile offsets.
+long long natural_len(int B, int T, int H, int W, int heads, int head_dim, size_t esize) {
+    const long long S = grid_len(B, T, H, W, heads, head_dim);
+    if (S < 0) return -1;
+    if (H % kTile || W % kTile) return -2;
+    if (((long long)kTile * W) * heads * head_dim * (long long)esize > 0xffffffffLL) return -2;
+    return S;
+}
+
 }  // namespace
 
 extern "C" {
@@ -142,8 +157,8 @@ nabla_status nabla_block_mask(const void *q, const void *k, nabla_dtype dtype, i
                               int heads, int head_dim, const uint8_t *sta, double thr,
                               int32_t *kv_nb, int32_t *kv_inds, void *ws, size_t ws_bytes,
                               void *stream) {
-    return estimate(q, k, dtype, B, S, heads, head_dim, 0, 0, sta, thr, -1.0, kv_nb, kv_inds, ws,
-                    ws_bytes, stream);
+    return estimate(q, k, dtype, B, S, heads, head_dim, 0, 0, false, sta, thr, -1.0, kv_nb,
+                    kv_inds, ws, ws_bytes, stream);
 }
 
 nabla_status nabla_block_mask_topk(const void *q, const void *k, nabla_dtype dtype, int B,
@@ -151,8 +166,8 @@ nabla_status nabla_block_mask_topk(const void *q, const void *k, nabla_dtype dty
                                    double topk_ratio, int32_t *kv_nb, int32_t *kv_inds, void *ws,
                                    size_t ws_bytes, void *stream) {
     if (!(topk_ratio >= 0.0 && topk_ratio <= 1.0)) return NABLA_ERR_INVALID_ARG;  // also NaN
-    return estimate(q, k, dtype, B, S, heads, head_dim, 0, 0, sta, 0.0, topk_ratio, kv_nb,
-                    kv_inds, ws, ws_bytes, stream);
+    return estimate(q, k, dtype, B, S, heads, head_dim, 0, 0, false, sta, 0.0, topk_ratio,
+                    kv_nb, kv_inds, ws, ws_bytes, stream);
 }
 
 nabla_status nabla_block_mask_grid(const void *q, const void *k, nabla_dtype dtype, int B,
@@ -162,7 +177,20 @@ nabla_status nabla_block_mask_grid(const void *q, const void *k, nabla_dtype dty
                                    void *stream) {
     const long long S = grid_len(B, T, H, W, heads, head_dim);
     if (S < 0 || topk_ratio != topk_ratio) return NABLA_ERR_INVALID_ARG;
-    return estimate(q, k, dtype, B, (int)S, heads, head_dim, H, W, sta, thr,
+    return estimate(q, k, dtype, B, (int)S, heads, head_dim, H, W, false, sta, thr,
+                    topk_ratio < 0.0 ? -1.0 : topk_ratio, kv_nb, kv_inds, ws, ws_bytes, stream);
+}
+
+nabla_status nabla_block_mask_natural(const void *q, const void *k, nabla_dtype dtype, int B,
+                                      int T, int H, int W, int heads, int head_dim,
+                                      const uint8_t *sta, double thr, double topk_ratio,
+                                      int32_t *kv_nb, int32_t *kv_inds, void *ws,
+                                      size_t ws_bytes, void *stream) {
+    if (!dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
+    const long long S = natural_len(B, T, H, W, heads, head_dim, dtype_bytes(dtype));
+    if (S == -1 || topk_ratio != topk_ratio) return NABLA_ERR_INVALID_ARG;
+    if (S < 0) return NABLA_ERR_UNSUPPORTED;
+    return estimate(q, k, dtype, B, (int)S, heads, head_dim, H, W, true, sta, thr,
                     topk_ratio < 0.0 ? -1.0 : topk_ratio, kv_nb, kv_inds, ws, ws_bytes, stream);
 }
 
@@ -187,7 +215,8 @@ namespace {
 nabla_status attn_fwd(const void *q, const void *k, const void *v, nabla_dtype dtype, int B,
                       int S, int heads, int head_dim, const int32_t *kv_nb,
                       const int32_t *kv_inds, float scale, int Tt, int Ht, int Wt, int H, int W,
-                      void *o, float *lse, void *ws, size_t ws_bytes, void *stream) {
+                      bool natural, void *o, float *lse, void *ws, size_t ws_bytes,
+                      void *stream) {
     if (!q || !k || !v || !kv_nb || !kv_inds || !o || !dtype_ok(dtype))
         return NABLA_ERR_INVALID_ARG;
     if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
@@ -199,8 +228,8 @@ nabla_status attn_fwd(const void *q, const void *k, const void *v, nabla_dtype d
         return NABLA_ERR_WORKSPACE;
     if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
     return from_hip(nabla::launch_sparse_attn(q, k, v, dtype == NABLA_BF16, B, S, heads,
-                                              head_dim, Tt, Ht, Wt, H, W, kv_nb, kv_inds, scale,
-                                              o, lse, ws, as_stream(stream)));
+                                              head_dim, Tt, Ht, Wt, H, W, natural, kv_nb,
+                                              kv_inds, scale, o, lse, ws, as_stream(stream)));
 }
 
 }  // namespace
@@ -239,7 +268,7 @@ nabla_status nabla_sparse_attn_fwd_lse(const void *q, const void *k, const void 
                                        int Tt, int Ht, int Wt, void *o, float *lse, void *ws,
                                        size_t ws_bytes, void *stream) {
     return attn_fwd(q, k, v, dtype, B, S, heads, head_dim, kv_nb, kv_inds, scale, Tt, Ht, Wt, 0,
-                    0, o, lse, ws, ws_bytes, stream);
+                    0, false, o, lse, ws, ws_bytes, stream);
 }
 
 size_t nabla_sparse_attn_workspace_grid(int B, int T, int H, int W, int heads) {
@@ -256,7 +285,21 @@ nabla_status nabla_sparse_attn_fwd_grid(const void *q, const void *k, const void
     const long long S = grid_len(B, T, H, W, heads, head_dim);
     if (S < 0) return NABLA_ERR_INVALID_ARG;
     return attn_fwd(q, k, v, dtype, B, (int)S, heads, head_dim, kv_nb, kv_inds, scale, T,
-                    (int)tiles(H), (int)tiles(W), H, W, o, lse, ws, ws_bytes, stream);
+                    (int)tiles(H), (int)tiles(W), H, W, false, o, lse, ws, ws_bytes, stream);
+}
+
+nabla_status nabla_sparse_attn_fwd_natural(const void *q, const void *k, const void *v,
+                                           nabla_dtype dtype, int B, int T, int H, int W,
+                                           int heads, int head_dim, const int32_t *kv_nb,
+                                           const int32_t *kv_inds, float scale, void *o,
+                                           float *lse, void *ws, size_t ws_bytes,
+                                           void *stream) {
+    if (!dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
+    const long long S = natural_len(B, T, H, W, heads, head_dim, dtype_bytes(dtype));
+    if (S == -1) return NABLA_ERR_INVALID_ARG;
+    if (S < 0) return NABLA_ERR_UNSUPPORTED;
+    return attn_fwd(q, k, v, dtype, B, (int)S, heads, head_dim, kv_nb, kv_inds, scale, T,
+                    H / kTile, W / kTile, 0, 0, true, o, lse, ws, ws_bytes, stream);
 }
 
 size_t nabla_sparse_attn_bwd_workspace(int B, int S, int heads) {

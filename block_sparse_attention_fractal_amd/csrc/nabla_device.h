@@ -56,4 +56,31 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
     return x * q + min(x, r) + k;
 }
 
+// Natural-order addressing of a grid of whole 8 x 8 patches (T frames of H = 8 Ht rows and
+// W = 8 Wt columns, tokens row-major as (t, y, x)).  Fractal block j = (t Ht + ht) Wt + wt
+// starts at natural token (t H + 8 ht) W + 8 wt = 64 p Wt + 8 wt, where p = j / Wt counts
+// the patch rows before it over all frames; its row r = 8 y' + x' lies (r >> 3) W + (r & 7)
+// tokens further on.  p is a multiply-high by m = floor(2^32 / Wt) + 1, passed as its high
+// (0 or 1) and low words: exact while j < 2^12 and Wt < 2^20 (the error of j m / 2^32 is
+// below j / 2^32 <= 2^-20 < 1 / Wt).
+struct NatGrid {
+    int W, Wt;
+    uint32_t mhi, mlo;
+};
+inline NatGrid nat_grid(int W) {
+    NatGrid g;
+    g.W = W;
+    g.Wt = W / kTile;
+    const uint64_t m = (g.Wt > 0 ? (uint64_t)0x100000000ull / (uint64_t)g.Wt : 0) + 1;
+    g.mhi = (uint32_t)(m >> 32);
+    g.mlo = (uint32_t)m;
+    return g;
+}
+__device__ __forceinline__ int nat_block_base(int j, const NatGrid &g) {
+    const uint32_t uj = (uint32_t)j;
+    const uint32_t p = uj * g.mhi + __umulhi(uj, g.mlo);
+    return (int)(64u * p * (uint32_t)g.Wt + 8u * (uj - p * (uint32_t)g.Wt));
+}
+__device__ __forceinline__ int nat_row_off(int r, int W) { return (r >> 3) * W + (r & 7); }
+
 }  // namespace nabla

@@ -17,15 +17,18 @@ hipError_t launch_sta_mask(uint8_t *sta, int Tt, int Ht, int Wt, int win_t, int 
 // Pooled blocks [B*heads][nb][D] fp32 of q (qa) and k (ka), then per-row
 // selection; cut_fixed = ceil(fl32(1 - thr) * 2^48).  H, W > 0: the latent grid of a
 // padded fractal layout (blocks average their tokens only); 0: whole 64-token blocks.
+// natural: q and k are in natural order [B][T][H][W][heads][D] (H, W multiples of 8,
+// S = T*H*W), read in place of their fractal permute.
 hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, int S,
-                             int heads, int D, int H, int W, const uint8_t *sta,
+                             int heads, int D, int H, int W, bool natural, const uint8_t *sta,
                              int64_t cut_fixed, float sqrt_d, int32_t *kv_nb, int32_t *kv_inds,
                              float *qa, float *ka, hipStream_t stream);
 
 // The top-k variant: pooled blocks, smooth-k, the topk largest scores per row (k <= nb,
 // nb <= 2048), STA union.  H, W as for launch_block_mask.
 hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, int B, int S,
-                                  int heads, int D, int H, int W, const uint8_t *sta, int topk,
+                                  int heads, int D, int H, int W, bool natural,
+                                  const uint8_t *sta, int topk,
                                   int32_t *kv_nb, int32_t *kv_inds, float *qa, float *ka,
                                   hipStream_t stream);
 
@@ -70,10 +73,13 @@ size_t sparse_attn_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int 
 // lse: [B*heads][S] fp32 natural-log log-sum-exp of each row's scaled scores, or null.
 // H, W > 0: the latent grid of a padded fractal layout over the tile grid (Tt, Ht, Wt):
 // padding positions of partial patches are never keys.  0: whole blocks.
+// natural: q, k, v and o are in natural order [B][T][H][W][heads][D] (whole patches,
+// H = 8 Ht, W = 8 Wt); lse stays in fractal order.
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
                               int B, int S, int heads, int D, int Tt, int Ht, int Wt, int H,
-                              int W, const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                              void *o, float *lse, void *ws, hipStream_t stream);
+                              int W, bool natural, const int32_t *kv_nb,
+                              const int32_t *kv_inds, float scale, void *o, float *lse, void *ws,
+                              hipStream_t stream);
 
 // Backward (bf16 tensors): dq, dk, dv from q, k, v, o, dO, lse and the kv lists.
 // Hv > 0: a padded layout of Hv x Wv latents on a tile grid (., Ht, Wt), whose padding

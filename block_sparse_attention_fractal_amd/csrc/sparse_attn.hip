@@ -178,10 +178,13 @@ __global__ __launch_bounds__(1024) void attn_plan_order_kernel(const int32_t *__
 
 // kPad: the layout is a padded grid (Hv x Wv latents, partial patches); padding keys are
 // masked.  The instance without it carries none of that code.
-template <int D, typename Tin, bool kPad>
+// kNat: q, k, v and o are in natural order (a grid of whole patches, rows of ng.W tokens);
+// every row is read and written where the fractal permute would have moved it, so the
+// arithmetic, and the result, are those of the fractal layout.  lse stays in fractal order.
+template <int D, typename Tin, bool kPad, bool kNat>
 __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
-    Tin *__restrict__ o, int S, int heads, int Tt, int Ht, int Wt, int Hv, int Wv,
+    Tin *__restrict__ o, int S, int heads, int Tt, int Ht, int Wt, int Hv, int Wv, NatGrid ng,
     int groups_per_bh,
     int ngroups, const int32_t *__restrict__ kv_nb, const int32_t *__restrict__ kv_inds,
     float scale_log2, const int32_t *__restrict__ order, int32_t *__restrict__ counter,
@@ -193,6 +196,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     constexpr int CHUNKS = kBlock * CH; // 16-byte chunks per K (or V) tile
     constexpr int CPT = CHUNKS / kAttnThreads;  // chunks per thread per tile (K and V each)
     static_assert(CPT >= 1, "tile too small for the workgroup");
+    static_assert(!(kPad && kNat), "the natural layout holds whole patches only");
 
     __shared__ __attribute__((aligned(1024))) AttnShared<D> sh;
 
@@ -273,12 +277,16 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     const int64_t tok = (int64_t)heads * D;
     const int64_t head0 = (int64_t)b * S * tok + (int64_t)h * D;
     const int qtok = (myblk < 0 ? 0 : myblk) * kBlock + (w & 1) * 32 + l32;
+    // the row's token in the layout of q and o
+    const int64_t qrow = kNat ? (int64_t)nat_block_base(myblk < 0 ? 0 : myblk, ng) +
+                                    nat_row_off((w & 1) * 32 + l32, ng.W)
+                              : (int64_t)qtok;
 
     // Q^T as B operands, pre-multiplied by scale * log2(e) so that the score
     // MFMAs produce log2-domain logits directly
     bf16x8 qf[KS];
     if (myblk >= 0) {
-        const Tin *qr = q + head0 + (int64_t)qtok * tok + 8 * hi;
+        const Tin *qr = q + head0 + qrow * tok + 8 * hi;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 x = load8_bf16(qr + 16 * ks);
@@ -303,15 +311,17 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     for (int r = 0; r < CPT; ++r) {
         const int e = r * kAttnThreads + tid;
         const int kv = e / CH, cpos = e % CH;
-        koff[r] = (uint32_t)((kv * tok + 8 * (cpos ^ kswz<CH>(kv))) * sizeof(Tin));
-        voff[r] = (uint32_t)((kv * tok + 8 * (cpos ^ vswz<CH>(kv))) * sizeof(Tin));
+        const int64_t kvrow = kNat ? nat_row_off(kv, ng.W) : kv;
+        koff[r] = (uint32_t)((kvrow * tok + 8 * (cpos ^ kswz<CH>(kv))) * sizeof(Tin));
+        voff[r] = (uint32_t)((kvrow * tok + 8 * (cpos ^ vswz<CH>(kv))) * sizeof(Tin));
     }
     const uint32_t lds_k0 = __builtin_amdgcn_readfirstlane(lds_offset(sh.ks[0]) + w * 64 * 16);
     const uint32_t lds_v0 = __builtin_amdgcn_readfirstlane(lds_offset(sh.vs[0]) + w * 64 * 16);
     auto issue = [&](int jj, int stage) {
         const int j = __builtin_amdgcn_readfirstlane(jj);  // wave-uniform block index
-        const Tin *kb = k + head0 + (int64_t)j * kBlock * tok;
-        const Tin *vb = v + head0 + (int64_t)j * kBlock * tok;
+        const int64_t jrow = kNat ? (int64_t)nat_block_base(j, ng) : (int64_t)j * kBlock;
+        const Tin *kb = k + head0 + jrow * tok;
+        const Tin *vb = v + head0 + jrow * tok;
 #pragma unroll
         for (int r = 0; r < CPT; ++r) {
             if constexpr (kDirect) {
@@ -321,8 +331,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
             } else {
                 const int e = r * kAttnThreads + tid;
                 const int kv = e / CH, cpos = e % CH;
-                kst[r] = load8_bf16(kb + (int64_t)kv * tok + 8 * cpos);
-                vst[r] = load8_bf16(vb + (int64_t)kv * tok + 8 * cpos);
+                const int64_t kvrow = kNat ? nat_row_off(kv, ng.W) : kv;
+                kst[r] = load8_bf16(kb + kvrow * tok + 8 * cpos);
+                vst[r] = load8_bf16(vb + kvrow * tok + 8 * cpos);
             }
         }
     };
@@ -545,7 +556,7 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     if (lse != nullptr && hi == 0)
         lse[(int64_t)bh * S + qtok] =
             lsum > 0.0f ? (m_ref + log2f(lsum)) * 0.6931471805599453f : -INFINITY;
-    Tin *orow = o + head0 + (int64_t)qtok * tok;
+    Tin *orow = o + head0 + qrow * tok;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -624,19 +635,21 @@ AttnSchedule launch_attn_plan(const int32_t *kv_nb, const int32_t *kv_inds, int 
     return sc;
 }
 
-template <int D, typename Tin, bool kPad>
+template <int D, typename Tin, bool kPad, bool kNat>
 static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int B, int S,
                                 int heads, int Tt, int Ht, int Wt, int Hv, int Wv,
                                 const int32_t *kv_nb,
                                 const int32_t *kv_inds, float scale_log2, void *o, float *lse,
                                 void *ws, hipStream_t stream) {
-    const auto kernel = sparse_attn_kernel<D, Tin, kPad>;
-    const int resident = resident_workgroups<sparse_attn_kernel<D, Tin, kPad>>(kAttnThreads);
+    const auto kernel = sparse_attn_kernel<D, Tin, kPad, kNat>;
+    const int resident =
+        resident_workgroups<sparse_attn_kernel<D, Tin, kPad, kNat>>(kAttnThreads);
+    const NatGrid ng = nat_grid(kNat ? kTile * Wt : 0);
     if (resident <= 0) return hipErrorInvalidDevice;
     const AttnSchedule sc =
         launch_attn_plan(kv_nb, kv_inds, B, S, heads, Tt, Ht, Wt, resident, ws, stream);
     hipLaunchKernelGGL(kernel, dim3(sc.grid), dim3(kAttnThreads), 0, stream, (const Tin *)q,
-                       (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, Tt, Ht, Wt, Hv, Wv,
+                       (const Tin *)k, (const Tin *)v, (Tin *)o, S, heads, Tt, Ht, Wt, Hv, Wv, ng,
                        sc.groups_per_bh, sc.ngroups, kv_nb, kv_inds, scale_log2, sc.order,
                        sc.counter, lse);
     return hipGetLastError();
@@ -644,15 +657,18 @@ static hipError_t launch_attn_t(const void *q, const void *k, const void *v, int
 
 hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool bf16_in,
                               int B, int S, int heads, int D, int Tt, int Ht, int Wt, int H,
-                              int W, const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                              void *o, float *lse, void *ws, hipStream_t stream) {
+                              int W, bool natural, const int32_t *kv_nb,
+                              const int32_t *kv_inds, float scale, void *o, float *lse, void *ws,
+                              hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
     const bool pad = H > 0 && (H % kTile != 0 || W % kTile != 0);
-#define NABLA_ATTN(DD, T)                                                                      \
-    return pad ? launch_attn_t<DD, T, true>(q, k, v, B, S, heads, Tt, Ht, Wt, H, W, kv_nb,      \
-                                            kv_inds, scale_log2, o, lse, ws, stream)            \
-               : launch_attn_t<DD, T, false>(q, k, v, B, S, heads, Tt, Ht, Wt, 0, 0, kv_nb,     \
-                                             kv_inds, scale_log2, o, lse, ws, stream)
+#define NABLA_ATTN_T(DD, T, P, N, HV, WV) \
+    launch_attn_t<DD, T, P, N>(q, k, v, B, S, heads, Tt, Ht, Wt, HV, WV, kv_nb, kv_inds, \
+                               scale_log2, o, lse, ws, stream)
+#define NABLA_ATTN(DD, T)                                        \
+    return pad       ? NABLA_ATTN_T(DD, T, true, false, H, W)    \
+           : natural ? NABLA_ATTN_T(DD, T, false, true, 0, 0)    \
+                     : NABLA_ATTN_T(DD, T, false, false, 0, 0)
     if (D == 128) {
         if (bf16_in) NABLA_ATTN(128, bf16);
         NABLA_ATTN(128, float);
@@ -660,6 +676,7 @@ hipError_t launch_sparse_attn(const void *q, const void *k, const void *v, bool 
     if (bf16_in) NABLA_ATTN(64, bf16);
     NABLA_ATTN(64, float);
 #undef NABLA_ATTN
+#undef NABLA_ATTN_T
 }
 
 }  // namespace nabla

@@ -173,6 +173,24 @@ nabla_status nabla_block_mask_grid(const void *q, const void *k, nabla_dtype dty
                                    void *stream);
 
 /*
+ * Either estimator on q and k left in natural order, with the fractal permute folded into
+ * the pooling's addressing (the "nabla" page's fractal flattening reorders tokens only, so
+ * each 64-token block is read where the permute would take its rows from, in the same
+ * order).  H and W must be multiples of 8 (whole patches); S = T * H * W.
+ * q, k:     [B, T, H, W, heads, head_dim] (bf16 or fp32), natural order.
+ * The block indices, lists, sta, thr / topk_ratio (as nabla_block_mask_grid) and the
+ * workspace (nabla_block_mask_workspace(B, S, heads, head_dim)) are those of the fractal
+ * layout: the lists are identical to nabla_block_mask_grid's on the permuted q and k.
+ * Errors: those of nabla_block_mask_grid; UNSUPPORTED also for H or W not a multiple of 8,
+ * or 8 * W * heads * head_dim * element size >= 2^32.
+ */
+nabla_status nabla_block_mask_natural(const void *q, const void *k, nabla_dtype dtype, int B,
+                                      int T, int H, int W, int heads, int head_dim,
+                                      const uint8_t *sta, double thr, double topk_ratio,
+                                      int32_t *kv_nb, int32_t *kv_inds, void *ws,
+                                      size_t ws_bytes, void *stream);
+
+/*
  * Bytes of workspace nabla_sparse_attn_fwd needs for the same (B, S, heads) and tile
  * grid: 256 + 2 * round_up(4 * ngroups, 256), where ngroups = B * heads *
  * ceil(Tt/2) * Ht * ceil(Wt/2) (tile grid known) or B * heads * ceil(S/256)
@@ -252,6 +270,27 @@ nabla_status nabla_sparse_attn_fwd_grid(const void *q, const void *k, const void
                                         int head_dim, const int32_t *kv_nb,
                                         const int32_t *kv_inds, float scale, void *o, float *lse,
                                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The forward (with optional lse) on q, k, v and o in natural order, with the fractal
+ * permute and its inverse folded into the kernel's addressing: every token row is read
+ * and written where the permutes would have moved it, so o equals, bit for bit, the
+ * inverse permute of nabla_sparse_attn_fwd_lse's output on the permuted inputs (tile grid
+ * (T, H/8, W/8)).  H and W must be multiples of 8; S = T * H * W.
+ * q, k, v:  [B, T, H, W, heads, head_dim] (bf16 or fp32), natural order.
+ * kv_nb, kv_inds: lists over fractal block indices, as nabla_block_mask_natural writes them.
+ * o:        out [B, T, H, W, heads, head_dim], natural order; must not overlap inputs.
+ * lse:      out [B, heads, S] fp32 in fractal order (as nabla_sparse_attn_fwd_lse), or NULL.
+ * ws:       nabla_sparse_attn_workspace_grid(B, T, H, W, heads) bytes.
+ * Errors: those of nabla_sparse_attn_fwd_grid; UNSUPPORTED also for H or W not a multiple
+ * of 8, or 8 * W * heads * head_dim * element size >= 2^32.
+ */
+nabla_status nabla_sparse_attn_fwd_natural(const void *q, const void *k, const void *v,
+                                           nabla_dtype dtype, int B, int T, int H, int W,
+                                           int heads, int head_dim, const int32_t *kv_nb,
+                                           const int32_t *kv_inds, float scale, void *o,
+                                           float *lse, void *ws, size_t ws_bytes,
+                                           void *stream);
 
 /*
  * Bytes of workspace nabla_sparse_attn_bwd needs: round_up(4 B heads S, 256) +

@@ -44,14 +44,15 @@ def test_exports_every_declared_symbol(L):
                           "nabla_sparse_attn_fwd_grid", "nabla_quant_qkv_workspace",
                           "nabla_quant_qkv", "nabla_sparse_attn_q8_workspace",
                           "nabla_sparse_attn_fwd_q8", "nabla_sparse_attn_bwd_grid",
-                          "nabla_quant_qkv_grid", "nabla_sparse_attn_fwd_q8_grid"}
+                          "nabla_quant_qkv_grid", "nabla_sparse_attn_fwd_q8_grid",
+                          "nabla_block_mask_natural", "nabla_sparse_attn_fwd_natural"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 8
+    assert L.nabla_abi_version() == 9
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"
@@ -133,6 +134,39 @@ def test_grid_entry_points_validation(L):
     assert need == L.nabla_sparse_attn_workspace(1, S, 8, 2, 6, 10) > 0
     assert fwd(wsb=need - 1) == WS
     assert L.nabla_sparse_attn_workspace_grid(1, 0, 44, 76, 8) == 0
+
+
+def test_natural_entry_points_validation(L):
+    g = L.nabla_block_mask_natural
+
+    def mask(q=FAKE, T=2, H=48, W=80, heads=8, D=128, dt=BF16, thr=0.9, ratio=-1.0, ws=FAKE,
+             wsb=1 << 40):
+        return g(q, FAKE, dt, 1, T, H, W, heads, D, None, thr, ratio, FAKE, FAKE, ws, wsb, None)
+
+    assert mask(q=None) == INVALID
+    assert mask(T=0) == INVALID
+    assert mask(dt=7) == INVALID
+    assert mask(ratio=math.nan) == INVALID
+    assert mask(thr=-0.5) == INVALID
+    assert mask(H=44) == UNSUP                    # partial patches: permute + the grid calls
+    assert mask(W=76) == UNSUP
+    assert mask(W=8 * 65536, heads=8, D=128) == UNSUP   # rows of a patch 2^32 bytes apart
+    S = 2 * 6 * 10 * 64
+    assert mask(wsb=L.nabla_block_mask_workspace(1, S, 8, 128) - 1) == WS
+    f = L.nabla_sparse_attn_fwd_natural
+
+    def fwd(q=FAKE, T=2, H=48, W=80, D=128, dt=BF16, o=FAKE, ws=FAKE, wsb=1 << 40):
+        return f(q, FAKE, FAKE, dt, 1, T, H, W, 8, D, FAKE, FAKE, 0.0, o, None, ws, wsb, None)
+
+    assert fwd(q=None) == INVALID
+    assert fwd(o=None) == INVALID
+    assert fwd(T=-1) == INVALID
+    assert fwd(dt=5) == INVALID
+    assert fwd(H=20) == UNSUP
+    assert fwd(D=96) == UNSUP
+    need = L.nabla_sparse_attn_workspace_grid(1, 2, 48, 80, 8)
+    assert need > 0
+    assert fwd(wsb=need - 1) == WS
 
 
 def test_sparse_attn_workspace_size(L):
