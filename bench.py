@@ -63,7 +63,7 @@ def parse():
                     help="permute q, k, v and o with nabla_fractal_permute around fractal-order "
                          "calls, instead of the natural-order calls that fold the permutes into "
                          "the estimator's and the attention's addressing (grids of whole "
-                         "patches; padded grids and --q8 always permute)")
+                         "patches; padded grids always permute)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -189,7 +189,7 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False, f
         if rc != 0:
             raise nabla.NablaError(rc, what)
 
-    fold = fold and not w.padded and not quant
+    fold = fold and not w.padded
 
     def step(rec=None):
         """One pass of the path; rec collects (start, end) event pairs per stage."""
@@ -218,14 +218,22 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False, f
                                           P(kv_nb), P(kv_inds), P(ws), ws.numel(), sp), "mask")
         if e: e[2].record(stream)
         codes = [P(qz[n]) for n in ("q8", "qs", "k8", "ks", "v8", "vs")] if quant else None
-        if quant and w.padded:
+        if quant and fold:
+            check(L.nabla_quant_qkv_natural(P(gq), P(gk), P(gv), dt_code, B, w.T, w.H, w.W, H, D,
+                                            *codes, P(qz["km"]), P(ws_q), ws_q.numel(), sp),
+                  "quant")
+        elif quant and w.padded:
             check(L.nabla_quant_qkv_grid(P(qf), P(kf), P(vf), dt_code, B, w.T, w.H, w.W, H, D,
                                          *codes, P(qz["km"]), P(ws_q), ws_q.numel(), sp), "quant")
         elif quant:
             check(L.nabla_quant_qkv(P(qf), P(kf), P(vf), dt_code, B, S, H, D, *codes,
                                     P(qz["km"]), P(ws_q), ws_q.numel(), sp), "quant")
         if e: e[3].record(stream)
-        if quant and w.padded:
+        if quant and fold:
+            check(L.nabla_sparse_attn_fwd_q8_natural(*codes, B, w.T, w.H, w.W, H, D, P(kv_nb),
+                                                     P(kv_inds), 0.0, P(o_nat), P(ws_q8),
+                                                     ws_q8.numel(), sp), "attn q8")
+        elif quant and w.padded:
             check(L.nabla_sparse_attn_fwd_q8_grid(*codes, B, w.T, w.H, w.W, H, D, P(kv_nb),
                                                   P(kv_inds), 0.0, P(of), P(ws_q8),
                                                   ws_q8.numel(), sp), "attn q8")
@@ -446,7 +454,7 @@ def main():
                    "T": w.T, "H": w.H, "W": w.W, "seq_len": w.S, "blocks": w.nb, "thr": w.thr,
                    "sta_window": list(w.sta) if w.sta else None, "kept_pairs": m["pairs"],
                    "density": round(m["density"], 5),
-                   "permutes": "folded into the estimator's and the attention's addressing"
+                   "permutes": "folded into the kernels' addressing (natural-order calls)"
                    if m["fold"] else "nabla_fractal_permute kernels"},
         "mask_ms": round(m["mask_ms"], 4),
         "attn_ms": round(m["attn_ms"], 4),

@@ -76,6 +76,10 @@ def lib():
     L.nabla_block_mask_natural.restype = I
     L.nabla_sparse_attn_fwd_natural.argtypes = [P, P, P] + [I] * 7 + [P, P, F, P, P, P, Z, P]
     L.nabla_sparse_attn_fwd_natural.restype = I
+    L.nabla_quant_qkv_natural.argtypes = [P, P, P] + [I] * 7 + [P] * 7 + [P, Z, P]
+    L.nabla_quant_qkv_natural.restype = I
+    L.nabla_sparse_attn_fwd_q8_natural.argtypes = [P] * 6 + [I] * 6 + [P, P, F, P, P, Z, P]
+    L.nabla_sparse_attn_fwd_q8_natural.restype = I
     L.nabla_sparse_attn_workspace.argtypes = [I, I, I, I, I, I]
     L.nabla_sparse_attn_workspace.restype = Z
     L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P, Z, P]
@@ -430,13 +434,21 @@ def nabla_quant_qkv(q, k, v, workspace=None, grid=None):
     (k after subtracting its sequence mean), q_scale, k_scale float32 [B, heads, nb], v8 uint8
     e4m3 codes [B, heads, nb, D, 64] (blocks transposed), v_scale, k_mean float32 [B, heads, D].
     grid=(T, H, W): the padded fractal layout of that latent grid (nabla_quant_qkv_grid:
-    padding positions are not tokens).
+    padding positions are not tokens).  q, k, v of 6 dims [B, T, H, W, heads, D] (H, W
+    multiples of 8): natural order, read in place of their permute (nabla_quant_qkv_natural;
+    the same codes).
     """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _dev(t, name)
     if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must match in shape and dtype")
-    B, S, heads, D = q.shape
+    nat = None
+    if q.dim() == 6:
+        B, T, H, W, heads, D = _natural_shape(q)
+        nat = (T, H, W)
+        S = T * H * W
+    else:
+        B, S, heads, D = q.shape
     nb = S // BLOCK
     dev = q.device
     out = {"q8": torch.empty((B, heads, nb, BLOCK, D), dtype=torch.int8, device=dev),
@@ -452,6 +464,12 @@ def nabla_quant_qkv(q, k, v, workspace=None, grid=None):
     else:
         _dev(workspace, "workspace")
     codes = [_p(out[n]) for n in ("q8", "q_scale", "k8", "k_scale", "v8", "v_scale", "k_mean")]
+    if nat is not None:
+        _check(lib().nabla_quant_qkv_natural(_p(q), _p(k), _p(v), _dtype_code(q), B, *nat, heads,
+                                             D, *codes, _p(workspace), workspace.numel(),
+                                             _stream(q)),
+               "nabla_quant_qkv_natural")
+        return out
     if grid is not None:
         if fractal_len(*grid) != S:
             raise ValueError("grid %s does not match S=%d" % (grid, S))
@@ -467,11 +485,12 @@ def nabla_quant_qkv(q, k, v, workspace=None, grid=None):
 
 
 def nabla_sparse_attn_fwd_q8(qz, kv_nb, kv_inds, scale=None, tiles=None, workspace=None,
-                             out=None, grid=None):
+                             out=None, grid=None, natural=None):
     """Block-sparse attention of the quantized variant over the listed 64 x 64 blocks, on the
     codes of nabla_quant_qkv (qz): o [B, S, heads, D] bfloat16.  grid=(T, H, W): the padded
     fractal layout of that latent grid (nabla_sparse_attn_fwd_q8_grid: padding is never a
-    key; tiles is then implied)."""
+    key; tiles is then implied).  natural=(T, H, W) (H, W multiples of 8): o is written in
+    natural order [B, T, H, W, heads, D] (nabla_sparse_attn_fwd_q8_natural)."""
     names = ("q8", "q_scale", "k8", "k_scale", "v8", "v_scale")
     for name in names:
         _dev(qz[name], name)
@@ -488,7 +507,15 @@ def nabla_sparse_attn_fwd_q8(qz, kv_nb, kv_inds, scale=None, tiles=None, workspa
         raise ValueError("kv lists do not match the codes' shape")
     if qz["k8"].shape != q8.shape or qz["v8"].numel() != q8.numel():
         raise ValueError("q8, k8, v8 must have one shape")
-    o = torch.empty((B, S, heads, D), dtype=torch.bfloat16, device=q8.device) if out is None \
+    if natural is not None:
+        T, H, W = natural
+        if H % 8 or W % 8 or T * H * W != S:
+            raise ValueError("natural grid %s must be whole patches with T*H*W = S" % (natural,))
+        grid_shape = (B, T, H, W, heads, D)
+        tiles = (T, H // 8, W // 8)
+    else:
+        grid_shape = (B, S, heads, D)
+    o = torch.empty(grid_shape, dtype=torch.bfloat16, device=q8.device) if out is None \
         else _dev(out, "out")
     if grid is not None:
         T, H, W = grid
@@ -501,6 +528,14 @@ def nabla_sparse_attn_fwd_q8(qz, kv_nb, kv_inds, scale=None, tiles=None, workspa
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q8.device)
     else:
         _dev(workspace, "workspace")
+    if natural is not None:
+        _check(lib().nabla_sparse_attn_fwd_q8_natural(*[_p(qz[n]) for n in names], B, *natural,
+                                                      heads, D, _p(kv_nb), _p(kv_inds),
+                                                      0.0 if scale is None else float(scale),
+                                                      _p(o), _p(workspace), workspace.numel(),
+                                                      _stream(q8)),
+               "nabla_sparse_attn_fwd_q8_natural")
+        return o
     if grid is not None:
         _check(lib().nabla_sparse_attn_fwd_q8_grid(*[_p(qz[n]) for n in names], B, *grid, heads,
                                                    D, _p(kv_nb), _p(kv_inds),

@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 10;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
 constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
@@ -341,7 +341,7 @@ namespace {
 nabla_status quant_qkv(const void *q, const void *k, const void *v, nabla_dtype dtype, int B,
                        int S, int heads, int head_dim, int8_t *q8, float *q_scale, int8_t *k8,
                        float *k_scale, uint8_t *v8, float *v_scale, float *k_mean, int T,
-                       int Hv, int Wv, void *ws, size_t ws_bytes, void *stream) {
+                       int Hv, int Wv, int natW, void *ws, size_t ws_bytes, void *stream) {
     if (!q || !k || !v || !q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || !k_mean ||
         !dtype_ok(dtype))
         return NABLA_ERR_INVALID_ARG;
@@ -351,14 +351,15 @@ nabla_status quant_qkv(const void *q, const void *k, const void *v, nabla_dtype 
         return NABLA_ERR_WORKSPACE;
     return from_hip(nabla::launch_quant_qkv(q, k, v, dtype == NABLA_BF16, B, S, heads, head_dim,
                                             q8, q_scale, k8, k_scale, v8, v_scale, k_mean, T, Hv,
-                                            Wv, ws, as_stream(stream)));
+                                            Wv, natW, ws, as_stream(stream)));
 }
 
 nabla_status attn_fwd_q8(const int8_t *q8, const float *q_scale, const int8_t *k8,
                          const float *k_scale, const uint8_t *v8, const float *v_scale, int B,
                          int S, int heads, int head_dim, const int32_t *kv_nb,
                          const int32_t *kv_inds, float scale, int Tt, int Ht, int Wt, int Hv,
-                         int Wv, void *o, void *ws, size_t ws_bytes, void *stream) {
+                         int Wv, bool natural, void *o, void *ws, size_t ws_bytes,
+                         void *stream) {
     if (!q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || !kv_nb || !kv_inds || !o)
         return NABLA_ERR_INVALID_ARG;
     if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
@@ -371,7 +372,8 @@ nabla_status attn_fwd_q8(const int8_t *q8, const float *q_scale, const int8_t *k
     if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));
     return from_hip(nabla::launch_sparse_attn_q8(q8, q_scale, k8, k_scale, v8, v_scale, B, S,
                                                  heads, head_dim, Tt, Ht, Wt, kv_nb, kv_inds,
-                                                 scale, Hv, Wv, o, ws, as_stream(stream)));
+                                                 scale, Hv, Wv, natural, o, ws,
+                                                 as_stream(stream)));
 }
 
 }  // namespace
@@ -383,7 +385,20 @@ nabla_status nabla_quant_qkv(const void *q, const void *k, const void *v, nabla_
                              int8_t *k8, float *k_scale, uint8_t *v8, float *v_scale,
                              float *k_mean, void *ws, size_t ws_bytes, void *stream) {
     return quant_qkv(q, k, v, dtype, B, S, heads, head_dim, q8, q_scale, k8, k_scale, v8,
-                     v_scale, k_mean, 0, 0, 0, ws, ws_bytes, stream);
+                     v_scale, k_mean, 0, 0, 0, 0, ws, ws_bytes, stream);
+}
+
+nabla_status nabla_quant_qkv_natural(const void *q, const void *k, const void *v,
+                                     nabla_dtype dtype, int B, int T, int H, int W, int heads,
+                                     int head_dim, int8_t *q8, float *q_scale, int8_t *k8,
+                                     float *k_scale, uint8_t *v8, float *v_scale, float *k_mean,
+                                     void *ws, size_t ws_bytes, void *stream) {
+    if (!dtype_ok(dtype)) return NABLA_ERR_INVALID_ARG;
+    const long long S = natural_len(B, T, H, W, heads, head_dim, dtype_bytes(dtype));
+    if (S == -1) return NABLA_ERR_INVALID_ARG;
+    if (S < 0) return NABLA_ERR_UNSUPPORTED;
+    return quant_qkv(q, k, v, dtype, B, (int)S, heads, head_dim, q8, q_scale, k8, k_scale, v8,
+                     v_scale, k_mean, 0, 0, 0, W, ws, ws_bytes, stream);
 }
 
 nabla_status nabla_quant_qkv_grid(const void *q, const void *k, const void *v,
@@ -394,7 +409,7 @@ nabla_status nabla_quant_qkv_grid(const void *q, const void *k, const void *v,
     const long long S = grid_len(B, T, H, W, heads, head_dim);
     if (S < 0) return NABLA_ERR_INVALID_ARG;
     return quant_qkv(q, k, v, dtype, B, (int)S, heads, head_dim, q8, q_scale, k8, k_scale, v8,
-                     v_scale, k_mean, T, H, W, ws, ws_bytes, stream);
+                     v_scale, k_mean, T, H, W, 0, ws, ws_bytes, stream);
 }
 
 size_t nabla_sparse_attn_q8_workspace(int B, int S, int heads, int Tt, int Ht, int Wt) {
@@ -409,7 +424,22 @@ nabla_status nabla_sparse_attn_fwd_q8(const int8_t *q8, const float *q_scale, co
                                       float scale, int Tt, int Ht, int Wt, void *o, void *ws,
                                       size_t ws_bytes, void *stream) {
     return attn_fwd_q8(q8, q_scale, k8, k_scale, v8, v_scale, B, S, heads, head_dim, kv_nb,
-                       kv_inds, scale, Tt, Ht, Wt, 0, 0, o, ws, ws_bytes, stream);
+                       kv_inds, scale, Tt, Ht, Wt, 0, 0, false, o, ws, ws_bytes, stream);
+}
+
+nabla_status nabla_sparse_attn_fwd_q8_natural(const int8_t *q8, const float *q_scale,
+                                              const int8_t *k8, const float *k_scale,
+                                              const uint8_t *v8, const float *v_scale, int B,
+                                              int T, int H, int W, int heads, int head_dim,
+                                              const int32_t *kv_nb, const int32_t *kv_inds,
+                                              float scale, void *o, void *ws, size_t ws_bytes,
+                                              void *stream) {
+    const long long S = natural_len(B, T, H, W, heads, head_dim, 2);
+    if (S == -1) return NABLA_ERR_INVALID_ARG;
+    if (S < 0) return NABLA_ERR_UNSUPPORTED;
+    return attn_fwd_q8(q8, q_scale, k8, k_scale, v8, v_scale, B, (int)S, heads, head_dim, kv_nb,
+                       kv_inds, scale, T, H / kTile, W / kTile, 0, 0, true, o, ws, ws_bytes,
+                       stream);
 }
 
 nabla_status nabla_sparse_attn_fwd_q8_grid(const int8_t *q8, const float *q_scale,
@@ -422,8 +452,8 @@ nabla_status nabla_sparse_attn_fwd_q8_grid(const int8_t *q8, const float *q_scal
     const long long S = grid_len(B, T, H, W, heads, head_dim);
     if (S < 0) return NABLA_ERR_INVALID_ARG;
     return attn_fwd_q8(q8, q_scale, k8, k_scale, v8, v_scale, B, (int)S, heads, head_dim, kv_nb,
-                       kv_inds, scale, T, (int)tiles(H), (int)tiles(W), H, W, o, ws, ws_bytes,
-                       stream);
+                       kv_inds, scale, T, (int)tiles(H), (int)tiles(W), H, W, false, o, ws,
+                       ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -82,5 +82,11 @@ __device__ __forceinline__ int nat_block_base(int j, const NatGrid &g) {
     return (int)(64u * p * (uint32_t)g.Wt + 8u * (uj - p * (uint32_t)g.Wt));
 }
 __device__ __forceinline__ int nat_row_off(int r, int W) { return (r >> 3) * W + (r & 7); }
+// Token index of row r of fractal block j: in the fractal order (g.W == 0), or in the natural
+// order of a grid of whole patches (g.W > 0).
+__device__ __forceinline__ int64_t block_row_token(int j, int r, const NatGrid &g) {
+    return g.W > 0 ? (int64_t)nat_block_base(j, g) + nat_row_off(r, g.W)
+                   : (int64_t)j * kBlock + r;
+}
 
 }  // namespace nabla

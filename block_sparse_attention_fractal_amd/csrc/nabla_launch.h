@@ -96,17 +96,20 @@ hipError_t launch_sparse_attn_bwd(const void *q, const void *k, const void *v, c
 // nabla_quant_qkv); ws: quant_workspace_bytes() bytes (k block sums, partial v maxima).
 size_t quant_workspace_bytes(int B, int S, int heads, int D);
 // Hv > 0: a padded layout of T frames of Hv x Wv latents, whose padding positions are not
-// tokens; Hv = 0: whole blocks (T unused).
+// tokens; Hv = 0: whole blocks (T unused).  natW > 0 (with Hv = 0): q, k, v in natural order
+// with rows of natW tokens (whole patches), read in place of their fractal permute.
 hipError_t launch_quant_qkv(const void *q, const void *k, const void *v, bool bf16_in, int B,
                             int S, int heads, int D, int8_t *q8, float *qs, int8_t *k8,
                             float *ks, uint8_t *v8, float *vs, float *km, int T, int Hv, int Wv,
-                            void *ws, hipStream_t stream);
+                            int natW, void *ws, hipStream_t stream);
 // The attention on those codes (bf16 o); ws: sparse_attn_q8_workspace_bytes() bytes.
+// natural (with Hv = 0): o is written in natural order (rows of 8 Wt tokens).
 size_t sparse_attn_q8_workspace_bytes(int B, int S, int heads, int Tt, int Ht, int Wt);
 hipError_t launch_sparse_attn_q8(const int8_t *q8, const float *qs, const int8_t *k8,
                                  const float *ks, const uint8_t *v8, const float *vs, int B,
                                  int S, int heads, int D, int Tt, int Ht, int Wt,
                                  const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                                 int Hv, int Wv, void *o, void *ws, hipStream_t stream);
+                                 int Hv, int Wv, bool natural, void *o, void *ws,
+                                 hipStream_t stream);
 
 }  // namespace nabla

@@ -29,8 +29,10 @@ namespace nabla {
 constexpr int kQuantChunk = 1024;  // tokens per partial channel maximum of v
 
 // The patch grid of a padded layout: Hv x Wv latents on Ht x Wt patches per frame.
+// ng.W > 0: q, k, v in natural order (a grid of whole patches; no padding then).
 struct QuantPad {
     int Ht, Wt, Hv, Wv;
+    NatGrid ng;
 };
 // Patch rows / columns of block j that are tokens.
 __device__ __forceinline__ void qpatch(const QuantPad &g, int j, int &vr, int &vc) {
@@ -72,14 +74,14 @@ __global__ __launch_bounds__(256) void quant_ksum_kernel(const Tin *__restrict__
     const int j = (int)(item % nb), bh = (int)(item / nb);
     const int b = bh / heads, h = bh % heads;
     const int64_t tok = (int64_t)heads * D;
-    const Tin *src = k + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D + 8 * cg;
+    const Tin *src = k + (int64_t)b * S * tok + (int64_t)h * D + 8 * cg;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int vr = kTile, vc = kTile;
     if constexpr (kPad) qpatch(g, j, vr, vc);
     for (int r0 = 0; r0 < kBlock; r0 += 16) {
         float x[16][8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) load8_f32(src + (int64_t)(r0 + r) * tok, x[r]);
+        for (int r = 0; r < 16; ++r) load8_f32(src + block_row_token(j, r0 + r, g.ng) * tok, x[r]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             if (kPad && !qrow_ok(r0 + r, vr, vc)) continue;  // padding: not a token
@@ -146,13 +148,13 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q
     const int j = (int)(item % nb), bh = (int)(item / nb);
     const int b = bh / heads, h = bh % heads, tid = threadIdx.x;
     const int64_t tok = (int64_t)heads * D;
-    const Tin *src = (is_k ? k : q) + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D;
+    const Tin *src = (is_k ? k : q) + (int64_t)b * S * tok + (int64_t)h * D;
     float x[CPT][8];
     float amax = 0.0f;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
         const int e = r * 256 + tid, row = e / CH, c = e % CH;
-        load8_f32(src + row * tok + 8 * c, x[r]);
+        load8_f32(src + block_row_token(j, row, g.ng) * tok + 8 * c, x[r]);
     }
     if (is_k) {
         const int c = tid % CH;  // the same channel chunk for every r (256 % CH == 0)
@@ -272,14 +274,14 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const Tin *__restrict__ v,
     const int j = (int)(item % nb), bh = (int)(item / nb);
     const int b = bh / heads, h = bh % heads, tid = threadIdx.x;
     const int64_t tok = (int64_t)heads * D;
-    const Tin *src = v + ((int64_t)b * S + (int64_t)j * kBlock) * tok + (int64_t)h * D;
+    const Tin *src = v + (int64_t)b * S * tok + (int64_t)h * D;
     int vr = kTile, vc = kTile;
     if constexpr (kPad) qpatch(g, j, vr, vc);
 #pragma unroll
     for (int r = 0; r < kBlock * CH / 256; ++r) {
         const int e = r * 256 + tid, row = e / CH, c = e % CH;
         float x[8];
-        load8_f32(src + row * tok + 8 * c, x);
+        load8_f32(src + block_row_token(j, row, g.ng) * tok + 8 * c, x);
         if (kPad && !qrow_ok(row, vr, vc))  // padding: code 0
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = 0.0f;
@@ -349,14 +351,15 @@ static hipError_t launch_quant_t(const void *q, const void *k, const void *v, in
 hipError_t launch_quant_qkv(const void *q, const void *k, const void *v, bool bf16_in, int B,
                             int S, int heads, int D, int8_t *q8, float *qs, int8_t *k8,
                             float *ks, uint8_t *v8, float *vs, float *km, int T, int Hv, int Wv,
-                            void *ws, hipStream_t stream) {
+                            int natW, void *ws, hipStream_t stream) {
     const bool pad = Hv > 0;
-    QuantPad g{0, 0, 0, 0};
+    QuantPad g{0, 0, 0, 0, nat_grid(0)};
     int ntok = S;
     if (pad) {
         g = QuantPad{(Hv + kTile - 1) / kTile, (Wv + kTile - 1) / kTile, Hv, Wv};
         ntok = T * Hv * Wv;
     }
+    g.ng = nat_grid(pad ? 0 : natW);
 #define NABLA_QUANT(DD, TT, P)                                                                  \
     return launch_quant_t<DD, TT, P>(q, k, v, B, S, heads, q8, qs, k8, ks, v8, vs, km, ntok, g, \
                                      ws, stream)

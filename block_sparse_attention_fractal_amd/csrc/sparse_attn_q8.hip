@@ -88,7 +88,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     const int8_t *__restrict__ q8, const float *__restrict__ qsc, const int8_t *__restrict__ k8,
     const float *__restrict__ ksc, const uint8_t *__restrict__ v8,
     const float *__restrict__ vsc, bf16 *__restrict__ o, int S, int heads, int Tt, int Ht,
-    int Wt, int Hv, int Wv, int groups_per_bh, int ngroups, const int32_t *__restrict__ kv_nb,
+    int Wt, int Hv, int Wv, NatGrid ng, int groups_per_bh, int ngroups,
+    const int32_t *__restrict__ kv_nb,
     const int32_t *__restrict__ kv_inds, float scale_log2, const int32_t *__restrict__ order,
     int32_t *__restrict__ counter) {
     constexpr int KS = D / 32;                 // k-steps of the INT8 score product
@@ -424,7 +425,9 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_q8_kernel(
     if (myblk >= 0) {
         const float lsum = __shfl(lacc[0], l32);  // row 0 of the sum product, lane n
         const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;  // empty list -> O = 0
-        bf16 *orow = o + ((int64_t)b * S + qtok) * ((int64_t)heads * D) + (int64_t)h * D;
+        // the row's token in o's layout (natural order when ng.W > 0)
+        const int64_t otok = block_row_token(qtok / kBlock, qtok % kBlock, ng);
+        bf16 *orow = o + ((int64_t)b * S + otok) * ((int64_t)heads * D) + (int64_t)h * D;
         const float *vsr = vsc + (int64_t)bh * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
@@ -452,9 +455,10 @@ size_t sparse_attn_q8_workspace_bytes(int B, int S, int heads, int Tt, int Ht, i
 template <int D>
 static hipError_t launch_q8_t(const int8_t *q8, const float *qs, const int8_t *k8,
                               const float *ks, const uint8_t *v8, const float *vs, int B, int S,
-                              int heads, int Tt, int Ht, int Wt, int Hv, int Wv,
+                              int heads, int Tt, int Ht, int Wt, int Hv, int Wv, bool natural,
                               const int32_t *kv_nb, const int32_t *kv_inds, float scale_log2,
                               void *o, void *ws, hipStream_t stream) {
+    const NatGrid ng = nat_grid(natural && Hv == 0 ? kTile * Wt : 0);
     const int resident = resident_workgroups<sparse_attn_q8_kernel<D, false>>(kAttnThreads);
     if (resident <= 0) return hipErrorInvalidDevice;
     const AttnSchedule sc =
@@ -462,12 +466,12 @@ static hipError_t launch_q8_t(const int8_t *q8, const float *qs, const int8_t *k
     if (Hv > 0)
         hipLaunchKernelGGL((sparse_attn_q8_kernel<D, true>), dim3(sc.grid), dim3(kAttnThreads), 0,
                            stream, q8, qs, k8, ks, v8, vs, static_cast<bf16 *>(o), S, heads, Tt,
-                           Ht, Wt, Hv, Wv, sc.groups_per_bh, sc.ngroups, kv_nb, kv_inds,
+                           Ht, Wt, Hv, Wv, ng, sc.groups_per_bh, sc.ngroups, kv_nb, kv_inds,
                            scale_log2, sc.order, sc.counter);
     else
         hipLaunchKernelGGL((sparse_attn_q8_kernel<D, false>), dim3(sc.grid), dim3(kAttnThreads),
                            0, stream, q8, qs, k8, ks, v8, vs, static_cast<bf16 *>(o), S, heads,
-                           Tt, Ht, Wt, 0, 0, sc.groups_per_bh, sc.ngroups, kv_nb, kv_inds,
+                           Tt, Ht, Wt, 0, 0, ng, sc.groups_per_bh, sc.ngroups, kv_nb, kv_inds,
                            scale_log2, sc.order, sc.counter);
     return hipGetLastError();
 }
@@ -476,13 +480,14 @@ hipError_t launch_sparse_attn_q8(const int8_t *q8, const float *qs, const int8_t
                                  const float *ks, const uint8_t *v8, const float *vs, int B,
                                  int S, int heads, int D, int Tt, int Ht, int Wt,
                                  const int32_t *kv_nb, const int32_t *kv_inds, float scale,
-                                 int Hv, int Wv, void *o, void *ws, hipStream_t stream) {
+                                 int Hv, int Wv, bool natural, void *o, void *ws,
+                                 hipStream_t stream) {
     const float scale_log2 = scale * 1.4426950408889634f;
     if (D == 128)
-        return launch_q8_t<128>(q8, qs, k8, ks, v8, vs, B, S, heads, Tt, Ht, Wt, Hv, Wv, kv_nb,
-                                kv_inds, scale_log2, o, ws, stream);
-    return launch_q8_t<64>(q8, qs, k8, ks, v8, vs, B, S, heads, Tt, Ht, Wt, Hv, Wv, kv_nb,
-                           kv_inds, scale_log2, o, ws, stream);
+        return launch_q8_t<128>(q8, qs, k8, ks, v8, vs, B, S, heads, Tt, Ht, Wt, Hv, Wv, natural,
+                                kv_nb, kv_inds, scale_log2, o, ws, stream);
+    return launch_q8_t<64>(q8, qs, k8, ks, v8, vs, B, S, heads, Tt, Ht, Wt, Hv, Wv, natural,
+                           kv_nb, kv_inds, scale_log2, o, ws, stream);
 }
 
 }  // namespace nabla

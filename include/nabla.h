@@ -448,6 +448,38 @@ nabla_status nabla_sparse_attn_fwd_q8_grid(const int8_t *q8, const float *q_scal
                                            float scale, void *o, void *ws, size_t ws_bytes,
                                            void *stream);
 
+/*
+ * The quantizer on q, k, v in natural order [B, T, H, W, heads, head_dim] (H, W multiples of
+ * 8; S = T * H * W), with the fractal permute folded into its reads: the codes, scales and
+ * k mean (in the fractal block layout of nabla_quant_qkv) are bit-identical to
+ * nabla_quant_qkv's on the permuted tensors.  Workspace: nabla_quant_qkv_workspace(B, S,
+ * heads, head_dim).  Errors: those of nabla_quant_qkv; INVALID_ARG also for T, H or W < 1;
+ * UNSUPPORTED also for H or W not a multiple of 8, or 8 * W * heads * head_dim * element
+ * size >= 2^32.
+ */
+nabla_status nabla_quant_qkv_natural(const void *q, const void *k, const void *v,
+                                     nabla_dtype dtype, int B, int T, int H, int W, int heads,
+                                     int head_dim, int8_t *q8, float *q_scale, int8_t *k8,
+                                     float *k_scale, uint8_t *v8, float *v_scale, float *k_mean,
+                                     void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The quantized forward writing o in natural order [B, T, H, W, heads, head_dim] bf16 (H, W
+ * multiples of 8; tile grid (T, H/8, W/8)), with the inverse permute folded into its stores:
+ * o is bit-identical to the inverse permute of nabla_sparse_attn_fwd_q8's output on the same
+ * codes and lists.  Codes, scales, lists and workspace
+ * (nabla_sparse_attn_q8_workspace(B, S, heads, T, H/8, W/8)) as for nabla_sparse_attn_fwd_q8.
+ * Errors: those of nabla_sparse_attn_fwd_q8; INVALID_ARG also for T, H or W < 1;
+ * UNSUPPORTED also for H or W not a multiple of 8.
+ */
+nabla_status nabla_sparse_attn_fwd_q8_natural(const int8_t *q8, const float *q_scale,
+                                              const int8_t *k8, const float *k_scale,
+                                              const uint8_t *v8, const float *v_scale, int B,
+                                              int T, int H, int W, int heads, int head_dim,
+                                              const int32_t *kv_nb, const int32_t *kv_inds,
+                                              float scale, void *o, void *ws, size_t ws_bytes,
+                                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,14 +45,15 @@ def test_exports_every_declared_symbol(L):
                           "nabla_quant_qkv", "nabla_sparse_attn_q8_workspace",
                           "nabla_sparse_attn_fwd_q8", "nabla_sparse_attn_bwd_grid",
                           "nabla_quant_qkv_grid", "nabla_sparse_attn_fwd_q8_grid",
-                          "nabla_block_mask_natural", "nabla_sparse_attn_fwd_natural"}
+                          "nabla_block_mask_natural", "nabla_sparse_attn_fwd_natural",
+                          "nabla_quant_qkv_natural", "nabla_sparse_attn_fwd_q8_natural"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 9
+    assert L.nabla_abi_version() == 10
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"

@@ -159,3 +159,31 @@ def test_natural_rejects_partial_patches(dev):
                                     0.9, -1.0, nabla._p(x), nabla._p(x), nabla._p(x), 1 << 20,
                                     None)
     assert nabla.STATUS[st] == "NABLA_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("shape,dt,seed", [((2, 3, 24, 40, 3, 128), torch.bfloat16, 96),
+                                           ((1, 2, 16, 16, 2, 64), torch.float32, 97)])
+def test_natural_quantized(orc, dev, shape, dt, seed):
+    """nabla_quant_qkv on natural q, k, v: the oracle's codes (bit-exact) and those of the
+    permuted call; nabla_sparse_attn_fwd_q8_natural: the permuted call's o, inverse-permuted."""
+    B, T, H, W, heads, D = shape
+    tiles = (T, H // 8, W // 8)
+    say("[natural q8] shape", shape, dt, "seed", seed)
+    g, vals = natural_inputs(shape, dt, seed, dev)
+    qz_n = nabla.nabla_quant_qkv(*g)
+    qf = [nabla.nabla_fractal_permute(t) for t in g]
+    qz_f = nabla.nabla_quant_qkv(*qf)
+    sta = nabla.nabla_sta_mask(tiles, (1, 1, 1), dev)
+    kv_nb, kv_inds = nabla.nabla_block_mask(qf[0], qf[1], sta, 0.9)
+    o_n = nabla.nabla_sparse_attn_fwd_q8(qz_n, kv_nb, kv_inds, natural=(T, H, W))
+    o_f = nabla.nabla_sparse_attn_fwd_q8(qz_f, kv_nb, kv_inds, tiles=tiles)
+    o_fn = nabla.nabla_fractal_permute(o_f, grid=(T, H, W), inverse=True)
+    torch.cuda.synchronize()
+    oz = orc.quant_qkv(*[orc.fractal_permute(x) for x in vals])
+    for gk, okey in (("q8", "q8"), ("q_scale", "qs"), ("k8", "k8"), ("k_scale", "ks"),
+                     ("v8", "v8"), ("v_scale", "vs"), ("k_mean", "km")):
+        a = qz_n[gk].cpu().numpy()
+        assert np.array_equal(a.view(np.uint8), oz[okey].view(np.uint8)), gk
+        assert torch.equal(qz_n[gk], qz_f[gk]), gk
+    assert o_n.shape == (B, T, H, W, heads, D)
+    assert torch.equal(o_n, o_fn), "natural q8 o differs from the permuted path's"
