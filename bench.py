@@ -107,7 +107,25 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
 
 
-def cpu_baseline(w, q, k, v, sta_np, g_nb, rows, flops_per_pair):
+def lists_vs_oracle(m, g_nb, g_inds, thr):
+    """The GPU lists against the oracle estimator's (m): kv_nb and the kv_inds sets on every
+    row; rows whose CDF lies within 1e-6 of the cut (band rows) are counted, listed, and
+    compared separately."""
+    import oracle
+    band = oracle.band_rows(m["diag"], thr).reshape(-1)
+    o_nb = m["kv_nb"].reshape(-1)
+    nb = g_inds.shape[-1]
+    live = np.arange(nb)[None, :] < o_nb[:, None]
+    same = (g_nb.reshape(-1) == o_nb) & np.all(
+        (g_inds.reshape(-1, nb) == m["kv_inds"].reshape(-1, nb)) | ~live, axis=1)
+    return {"band_rows": int(band.sum()),
+            "band_row_ids": np.flatnonzero(band)[:64].tolist(),
+            "lists_match_gpu": bool(same[~band].all()),
+            "lists_match_gpu_in_band": bool(same[band].all()),
+            "rows_compared": int(same.size)}
+
+
+def cpu_baseline(w, q, k, v, sta_np, g_nb, g_inds, rows, flops_per_pair):
     """The oracle (untuned) on the host: full estimator, attention on a row sample."""
     import oracle
     from block_sparse_attention_fractal_amd import synth  # noqa: F401  (inputs only)
@@ -141,7 +159,7 @@ def cpu_baseline(w, q, k, v, sta_np, g_nb, rows, flops_per_pair):
                    % (t_perm, t_mask, total_rows, ids.size, total_rows, t_attn_sample,
                       sample_pairs, all_pairs, t_attn_full)),
         "mask_ms": t_mask * 1e3,
-        "lists_match_gpu": bool(np.array_equal(m["kv_nb"], g_nb)),
+        **lists_vs_oracle(m, g_nb, g_inds, w.thr),
     }
 
 
@@ -274,6 +292,7 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False, f
     wall = time.perf_counter() - t0
     stage = np.array([[a.elapsed_time(b) for a, b in zip(e[:-1], e[1:])] for e in rec])
     g_nb = kv_nb.cpu().numpy()
+    g_inds = kv_inds.cpu().numpy()
     pairs = int(g_nb.sum())
     flops_per_pair = 4.0 * 64 * 64 * D
     esz = 2 if tdt == torch.bfloat16 else 4
@@ -295,15 +314,18 @@ def measure(torch, nabla, w, qkv, steps, warmup, topk_ratio=None, quant=False, f
         "sta_density": sta_pairs / float(B * H * nb * nb),
         "mask_gbs": mask_bytes / (mask_ms * 1e-3) / 1e9,
         "g_nb": g_nb,
+        "g_inds": g_inds,
         "sta_np": None if w.sta is None else sta.cpu().numpy(),
         "dtype": "bf16" if tdt == torch.bfloat16 else "fp32",
         "fold": fold,
     }
 
 
-def sweep(torch, nabla, synth, steps, warmup, quant=False):
+def sweep(torch, nabla, synth, steps, warmup, quant=False, oracle_lists=True):
     """The sparsity sweep on the 720p shape and the long clip: one JSON line per run (with
-    quant, the quantizer and the quantized attention in place of the bf16 attention)."""
+    quant, the quantizer and the quantized attention in place of the bf16 attention).  With
+    oracle_lists, each run's lists are also compared with the oracle estimator's on every row
+    (band rows counted and listed)."""
     cache = {}
     runs = synth.sweep_workloads() + [synth.WORKLOADS["long"]]
     for w in runs:
@@ -322,6 +344,13 @@ def sweep(torch, nabla, synth, steps, warmup, quant=False):
                 "permute_ms": round(m["perm_ms"], 4), "ms_per_step": round(m["ms_per_step"], 4),
                 **({"quant_ms": round(m["quant_ms"], 4)} if quant else {}),
                 "value": round(m["attn_flops"] / (m["ms_per_step"] * 1e-3) / 1e12, 3)}
+        if oracle_lists:
+            import oracle
+            oracle.set_threads(len(os.sched_getaffinity(0)))
+            q, k, _ = cache[key]
+            f = lambda a: oracle.fractal_permute(a).reshape(w.B, w.S, w.heads, w.D)
+            orc = oracle.block_mask(f(q), f(k), m["sta_np"], w.thr)
+            line.update(lists_vs_oracle(orc, m["g_nb"], m["g_inds"], w.thr))
         print(json.dumps(line), flush=True)
 
 
@@ -416,7 +445,8 @@ def main():
     import block_sparse_attention_fractal_amd as nabla
     from block_sparse_attention_fractal_amd import synth
     if args.sweep:
-        sweep(torch, nabla, synth, args.steps, args.warmup, quant=args.q8)
+        sweep(torch, nabla, synth, args.steps, args.warmup, quant=args.q8,
+              oracle_lists=not args.no_cpu_baseline)
         return
     if args.bwd:
         w = synth.WORKLOADS[args.workload]
@@ -461,6 +491,7 @@ def main():
         "permute_ms": round(m["perm_ms"], 4),
         "attn_tflops": round(attn_tflops, 2),
         "mask_gbs": round(m["mask_gbs"], 1),
+        "mask_hbm_frac": round(m["mask_gbs"] / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
@@ -475,8 +506,9 @@ def main():
                                 "kernel": "sparse_attn_q8_kernel<128>"})
     if not args.no_cpu_baseline and args.topk is None and not args.q8 and not w.padded:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, m["sta_np"], m["g_nb"], args.cpu_rows,
-                                           m["flops_per_pair"])
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, m["sta_np"], m["g_nb"], m["g_inds"],
+                                           args.cpu_rows, m["flops_per_pair"])
+        out["band_rows"] = out["cpu_baseline"]["band_rows"]
     print(json.dumps(out), flush=True)
 
 

@@ -123,6 +123,25 @@ def _dev(t, name):
     return t
 
 
+def _out(t, name, shape, dtype, device):
+    """A caller-supplied output tensor: on `device`, contiguous, of exactly `dtype` and `shape`
+    (the kernels write that many elements; anything smaller would be overrun)."""
+    _dev(t, name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, not %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, not %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s must be on %s, not %s" % (name, device, t.device))
+    return t
+
+
+def _same_device(device, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError("%s must be on %s, not %s" % (name, device, t.device))
+
+
 def _dtype_code(t):
     if t.dtype == torch.bfloat16:
         return _BF16
@@ -133,6 +152,18 @@ def _dtype_code(t):
 
 def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _workspace(ws, need, device):
+    """The caller's workspace (a uint8 GPU tensor on `device`; its size is checked by the
+    library) or a new one of `need` bytes."""
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace")
+    if ws.dtype != torch.uint8:
+        raise TypeError("workspace must be uint8")
+    _same_device(device, workspace=ws)
+    return ws
 
 
 def _p(t):
@@ -161,7 +192,8 @@ def nabla_fractal_permute(x, grid=None, inverse=False, out=None):
         if fractal_len(T, H, W) != S:
             raise ValueError("grid %s does not match S=%d" % (grid, S))
         shape = (B, T, H, W, heads, D)
-    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else _dev(out, "out")
+    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else \
+        _out(out, "out", shape, x.dtype, x.device)
     _check(lib().nabla_fractal_permute(_p(x), _p(y), _dtype_code(x), B, T, H, W, heads, D,
                                        int(bool(inverse)), _stream(x)), "nabla_fractal_permute")
     return y
@@ -201,13 +233,14 @@ def nabla_block_mask(q, k, sta=None, thr=0.9, workspace=None, out=None, topk_rat
         if sta.dtype != torch.uint8 or sta.numel() != nb * nb:
             raise ValueError("sta must be uint8 with nb*nb = %d elements" % (nb * nb))
     need = lib().nabla_block_mask_workspace(B, S, heads, D)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
-                                                             device=q.device)
+    ws = _workspace(workspace, need, q.device)
+    _same_device(q.device, k=k, sta=sta)
     if out is None:
         kv_nb = torch.empty((B, heads, nb), dtype=torch.int32, device=q.device)
         kv_inds = torch.empty((B, heads, nb, nb), dtype=torch.int32, device=q.device)
     else:
-        kv_nb, kv_inds = out
+        kv_nb = _out(out[0], "kv_nb", (B, heads, nb), torch.int32, q.device)
+        kv_inds = _out(out[1], "kv_inds", (B, heads, nb, nb), torch.int32, q.device)
     if grid is not None:
         T, H, W = grid
         if fractal_len(T, H, W) != S:
@@ -248,7 +281,8 @@ def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, til
     is never a key; tiles is then implied).
     """
     if causal:
-        raise ValueError("NABLA attention does not support causal masking")
+        raise ValueError("causal=True is not available: the block lists define the whole "
+                         "mask and carry no causal part")
     for name, t in (("q", q), ("k", k), ("v", v), ("kv_nb", kv_nb), ("kv_inds", kv_inds)):
         _dev(t, name)
     if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
@@ -259,18 +293,16 @@ def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, til
     nb = S // BLOCK
     if kv_nb.numel() != B * heads * nb or kv_inds.numel() != B * heads * nb * nb:
         raise ValueError("kv lists do not match q's shape")
-    o = torch.empty_like(q) if out is None else _dev(out, "out")
+    _same_device(q.device, k=k, v=v, kv_nb=kv_nb, kv_inds=kv_inds, lse=lse)
+    o = torch.empty_like(q) if out is None else _out(out, "out", q.shape, q.dtype, q.device)
     if grid is not None:
         T, H, W = grid
         if fractal_len(T, H, W) != S:
             raise ValueError("grid %s does not match S=%d" % (grid, S))
         tiles = (T, (H + 7) // 8, (W + 7) // 8)
     Tt, Ht, Wt = (0, 0, 0) if tiles is None else tiles
-    if workspace is None:
-        need = lib().nabla_sparse_attn_workspace(B, S, heads, Tt, Ht, Wt)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    else:
-        _dev(workspace, "workspace")
+    workspace = _workspace(workspace, lib().nabla_sparse_attn_workspace(B, S, heads, Tt, Ht, Wt),
+                           q.device)
     if lse is not None:
         _dev(lse, "lse")
         if lse.dtype != torch.float32 or lse.numel() != B * heads * S:
@@ -319,13 +351,14 @@ def nabla_block_mask_natural(q, k, sta=None, thr=0.9, topk_ratio=None, workspace
         if sta.dtype != torch.uint8 or sta.numel() != nb * nb:
             raise ValueError("sta must be uint8 with nb*nb = %d elements" % (nb * nb))
     need = lib().nabla_block_mask_workspace(B, S, heads, D)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8,
-                                                             device=q.device)
+    ws = _workspace(workspace, need, q.device)
+    _same_device(q.device, k=k, sta=sta)
     if out is None:
         kv_nb = torch.empty((B, heads, nb), dtype=torch.int32, device=q.device)
         kv_inds = torch.empty((B, heads, nb, nb), dtype=torch.int32, device=q.device)
     else:
-        kv_nb, kv_inds = out
+        kv_nb = _out(out[0], "kv_nb", (B, heads, nb), torch.int32, q.device)
+        kv_inds = _out(out[1], "kv_inds", (B, heads, nb, nb), torch.int32, q.device)
     _check(lib().nabla_block_mask_natural(_p(q), _p(k), _dtype_code(q), B, T, H, W, heads, D,
                                           _p(sta), float(thr),
                                           -1.0 if topk_ratio is None else float(topk_ratio),
@@ -351,12 +384,10 @@ def nabla_sparse_attn_fwd_natural(q, k, v, kv_nb, kv_inds, scale=None, workspace
     S = nb * BLOCK
     if kv_nb.numel() != B * heads * nb or kv_inds.numel() != B * heads * nb * nb:
         raise ValueError("kv lists do not match q's shape")
-    o = torch.empty_like(q) if out is None else _dev(out, "out")
-    if workspace is None:
-        need = lib().nabla_sparse_attn_workspace_grid(B, T, H, W, heads)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    else:
-        _dev(workspace, "workspace")
+    _same_device(q.device, k=k, v=v, kv_nb=kv_nb, kv_inds=kv_inds, lse=lse)
+    o = torch.empty_like(q) if out is None else _out(out, "out", q.shape, q.dtype, q.device)
+    workspace = _workspace(workspace, lib().nabla_sparse_attn_workspace_grid(B, T, H, W, heads),
+                           q.device)
     if lse is not None:
         _dev(lse, "lse")
         if lse.dtype != torch.float32 or lse.numel() != B * heads * S:
@@ -403,14 +434,13 @@ def nabla_sparse_attn_bwd(q, k, v, o, dout, lse, kv_nb, kv_inds, scale=None, wor
         raise ValueError("lse must be float32 with B * heads * S elements")
     if grid is not None and fractal_len(*grid) != S:
         raise ValueError("grid %s does not match S=%d" % (grid, S))
+    _same_device(q.device, k=k, v=v, o=o, dout=dout, lse=lse, kv_nb=kv_nb, kv_inds=kv_inds)
     outs = []
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        outs.append(torch.empty_like(q) if t is None else _dev(t, name))
-    if workspace is None:
-        need = lib().nabla_sparse_attn_bwd_workspace(B, S, heads)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    else:
-        _dev(workspace, "workspace")
+        outs.append(torch.empty_like(q) if t is None else _out(t, name, q.shape, q.dtype,
+                                                                q.device))
+    workspace = _workspace(workspace, lib().nabla_sparse_attn_bwd_workspace(B, S, heads),
+                           q.device)
     sc = 0.0 if scale is None else float(scale)
     if grid is not None:
         _check(lib().nabla_sparse_attn_bwd_grid(_p(q), _p(k), _p(v), _p(o), _p(dout), _p(lse),
@@ -458,11 +488,8 @@ def nabla_quant_qkv(q, k, v, workspace=None, grid=None):
            "v8": torch.empty((B, heads, nb, D, BLOCK), dtype=torch.uint8, device=dev),
            "v_scale": torch.empty((B, heads, D), dtype=torch.float32, device=dev),
            "k_mean": torch.empty((B, heads, D), dtype=torch.float32, device=dev)}
-    if workspace is None:
-        need = lib().nabla_quant_qkv_workspace(B, S, heads, D)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    else:
-        _dev(workspace, "workspace")
+    _same_device(dev, k=k, v=v)
+    workspace = _workspace(workspace, lib().nabla_quant_qkv_workspace(B, S, heads, D), dev)
     codes = [_p(out[n]) for n in ("q8", "q_scale", "k8", "k_scale", "v8", "v_scale", "k_mean")]
     if nat is not None:
         _check(lib().nabla_quant_qkv_natural(_p(q), _p(k), _p(v), _dtype_code(q), B, *nat, heads,
@@ -507,6 +534,12 @@ def nabla_sparse_attn_fwd_q8(qz, kv_nb, kv_inds, scale=None, tiles=None, workspa
         raise ValueError("kv lists do not match the codes' shape")
     if qz["k8"].shape != q8.shape or qz["v8"].numel() != q8.numel():
         raise ValueError("q8, k8, v8 must have one shape")
+    for name, dt, n in (("k8", torch.int8, q8.numel()), ("v8", torch.uint8, q8.numel()),
+                        ("q_scale", torch.float32, B * heads * nb),
+                        ("k_scale", torch.float32, B * heads * nb),
+                        ("v_scale", torch.float32, B * heads * D)):
+        if qz[name].dtype != dt or qz[name].numel() != n:
+            raise ValueError("%s must be %s with %d elements" % (name, dt, n))
     if natural is not None:
         T, H, W = natural
         if H % 8 or W % 8 or T * H * W != S:
@@ -515,19 +548,19 @@ def nabla_sparse_attn_fwd_q8(qz, kv_nb, kv_inds, scale=None, tiles=None, workspa
         tiles = (T, H // 8, W // 8)
     else:
         grid_shape = (B, S, heads, D)
+    _same_device(q8.device, kv_nb=kv_nb, kv_inds=kv_inds,
+                 **{n: qz[n] for n in names if n != "q8"})
     o = torch.empty(grid_shape, dtype=torch.bfloat16, device=q8.device) if out is None \
-        else _dev(out, "out")
+        else _out(out, "out", grid_shape, torch.bfloat16, q8.device)
     if grid is not None:
         T, H, W = grid
         if fractal_len(T, H, W) != S:
             raise ValueError("grid %s does not match S=%d" % (grid, S))
         tiles = (T, (H + 7) // 8, (W + 7) // 8)
     Tt, Ht, Wt = (0, 0, 0) if tiles is None else tiles
-    if workspace is None:
-        need = lib().nabla_sparse_attn_q8_workspace(B, S, heads, Tt, Ht, Wt)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q8.device)
-    else:
-        _dev(workspace, "workspace")
+    workspace = _workspace(workspace,
+                           lib().nabla_sparse_attn_q8_workspace(B, S, heads, Tt, Ht, Wt),
+                           q8.device)
     if natural is not None:
         _check(lib().nabla_sparse_attn_fwd_q8_natural(*[_p(qz[n]) for n in names], B, *natural,
                                                       heads, D, _p(kv_nb), _p(kv_inds),

@@ -139,13 +139,16 @@ long long grid_len(int B, int T, int H, int W, int heads, int head_dim) {
 }
 
 // S = T*H*W of a natural-order [B][T][H][W][heads][head_dim] grid read in place of its
-// fractal permute; -1 when the sizes are invalid, -2 when the grid has partial patches or
-// a patch's rows lie too far apart for the kernels' 32-bit in-tile offsets.
+// fractal permute; -1 when the sizes are invalid, -2 when the grid has partial patches, a
+// patch's rows lie too far apart for the kernels' 32-bit in-tile offsets, or the sequence
+// has more than kMaxBlocks blocks (the kernels find a block's patch row j / Wt by a
+// multiply-high that is exact while j * Wt < 2^32; j < 4096 and Wt < 2^20 keep it so).
 long long natural_len(int B, int T, int H, int W, int heads, int head_dim, size_t esize) {
     const long long S = grid_len(B, T, H, W, heads, head_dim);
     if (S < 0) return -1;
     if (H % kTile || W % kTile) return -2;
     if (((long long)kTile * W) * heads * head_dim * (long long)esize > 0xffffffffLL) return -2;
+    if (S / kBlock > kMaxBlocks || W / kTile >= (1 << 20)) return -2;
     return S;
 }
 
@@ -212,11 +215,11 @@ nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
 
 namespace {
 
-nabla_status attn_fwd(const void *q, const void *k, const void *v, nabla_dtype dtype, int B,
-                      int S, int heads, int head_dim, const int32_t *kv_nb,
-                      const int32_t *kv_inds, float scale, int Tt, int Ht, int Wt, int H, int W,
-                      bool natural, void *o, float *lse, void *ws, size_t ws_bytes,
-                      void *stream) {
+// Every check of the forward's arguments except the workspace.
+nabla_status attn_fwd_check(const void *q, const void *k, const void *v, nabla_dtype dtype, int B,
+                            int S, int heads, int head_dim, const int32_t *kv_nb,
+                            const int32_t *kv_inds, float scale, int Tt, int Ht, int Wt,
+                            const void *o) {
     if (!q || !k || !v || !kv_nb || !kv_inds || !o || !dtype_ok(dtype))
         return NABLA_ERR_INVALID_ARG;
     if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return NABLA_ERR_INVALID_ARG;
@@ -224,6 +227,17 @@ nabla_status attn_fwd(const void *q, const void *k, const void *v, nabla_dtype d
     if (!grid_ok(S, Tt, Ht, Wt)) return NABLA_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return NABLA_ERR_UNSUPPORTED;
     if (S / kBlock > kMaxBlocks) return NABLA_ERR_UNSUPPORTED;
+    return NABLA_OK;
+}
+
+nabla_status attn_fwd(const void *q, const void *k, const void *v, nabla_dtype dtype, int B,
+                      int S, int heads, int head_dim, const int32_t *kv_nb,
+                      const int32_t *kv_inds, float scale, int Tt, int Ht, int Wt, int H, int W,
+                      bool natural, void *o, float *lse, void *ws, size_t ws_bytes,
+                      void *stream) {
+    const nabla_status st = attn_fwd_check(q, k, v, dtype, B, S, heads, head_dim, kv_nb,
+                                           kv_inds, scale, Tt, Ht, Wt, o);
+    if (st != NABLA_OK) return st;
     if (!ws || ws_bytes < nabla::sparse_attn_workspace_bytes(B, S, heads, Tt, Ht, Wt))
         return NABLA_ERR_WORKSPACE;
     if (!(scale > 0.0f)) scale = (float)(1.0 / sqrt((double)head_dim));

@@ -61,8 +61,9 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
 // starts at natural token (t H + 8 ht) W + 8 wt = 64 p Wt + 8 wt, where p = j / Wt counts
 // the patch rows before it over all frames; its row r = 8 y' + x' lies (r >> 3) W + (r & 7)
 // tokens further on.  p is a multiply-high by m = floor(2^32 / Wt) + 1, passed as its high
-// (0 or 1) and low words: exact while j < 2^12 and Wt < 2^20 (the error of j m / 2^32 is
-// below j / 2^32 <= 2^-20 < 1 / Wt).
+// (0 or 1) and low words: j m / 2^32 exceeds j / Wt by less than j / 2^32, and the fraction
+// of j / Wt is at most 1 - 1 / Wt, so the floor is exact while j Wt < 2^32.  The host allows
+// at most 4096 blocks per sequence and Wt < 2^20.
 struct NatGrid {
     int W, Wt;
     uint32_t mhi, mlo;

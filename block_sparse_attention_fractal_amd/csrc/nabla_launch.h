@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+
+#include <atomic>
 #include <stdint.h>
 
 namespace nabla {
@@ -34,19 +36,23 @@ hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, in
 
 // Workgroups of kernel K (of `threads` lanes) the device holds at once (occupancy x CUs),
 // cached per device and kernel; 0 if the query fails.
+// The cache entries are atomics: calls on different streams or threads may query and fill
+// them at the same time; a racing first call computes and stores the same value.
 template <auto K>
 int resident_workgroups(int threads) {
     constexpr int kMaxDevices = 64;
-    static int cache[kMaxDevices];  // 0 = not yet known; a racing first call stores the same value
+    static std::atomic<int> cache[kMaxDevices];  // 0 = not yet known
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-    if (cache[dev] > 0) return cache[dev];
+    const int known = cache[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, 0) != hipSuccess)
         return 0;
-    cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
-    return cache[dev];
+    const int value = cus * (per_cu > 0 ? per_cu : 1);
+    cache[dev].store(value, std::memory_order_relaxed);
+    return value;
 }
 
 // The attention walk's schedule (groups of neighbouring query blocks, phases of a few

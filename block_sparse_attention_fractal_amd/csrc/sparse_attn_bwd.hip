@@ -91,16 +91,30 @@ __device__ __forceinline__ void tile_offsets(int tid, int64_t tok, uint32_t (&of
 // Gradient accumulators live in AGPRs for the whole walk: their MFMAs are issued from
 // inline asm with the accumulator bound to AGPRs ("+a"), while the score products stay
 // compiler builtins in VGPRs (the build selects the VGPR form for MFMAs), which the softmax
-// reads.  acc += a b (v_mfma_f32_32x32x16_bf16).  The compiler does not see the asm's
-// hazards, so the asm waits itself: s_nop 4 first covers operands that VALU instructions
-// have just written (the packed weights, the zeroed accumulators); a chain on one
-// accumulator needs no wait between MFMAs of the same shape.
+// reads.  acc += a b (v_mfma_f32_32x32x16_bf16).
+//
+// The compiler's hazard recognizer does not look inside inline asm, so these asm blocks
+// supply the wait states the CDNA3/CDNA4 ISA's table of required independent instructions
+// asks for around XDL (matrix) ops; every case that can occur here:
+//   * a and b written by a VALU instruction just before (dS and P packed to bf16, Q^T / K^T
+//     fragments assembled in registers): VALU write -> MFMA read of SrcA/B needs 2 wait
+//     states; `s_nop 4` gives 5.
+//   * a and b read from LDS: the compiler itself waits (lgkmcnt) for the value, as for any
+//     use of an asm input operand.
+//   * acc zeroed by v_accvgpr_write before the walk: a VALU-class write read as SrcC; the
+//     same 5 wait states cover it.
+//   * consecutive mfma_acc on one accumulator: SrcC is exactly the previous op's vdst and the
+//     ops have one opcode, the back-to-back case the hardware forwards (0 wait states);
+//     chains on different accumulators have no dependence.
+//   * the walk never writes an accumulator from VALU code while an MFMA reads it (no
+//     write-after-read case): the accumulators are only read after acc_settle below.
 __device__ __forceinline__ void mfma_acc(f32x16 &acc, const bf16x8 &a, const bf16x8 &b) {
     asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-// Waits out the last MFMAs writing the accumulators before VALU instructions read them
-// (more than the 8-pass MFMA's write latency).  The asm names every accumulator as in and
-// out, so no read of them can be scheduled above it.
+// Waits out the last MFMAs writing the accumulators before VALU instructions (or
+// v_accvgpr_read) read them: an XDL op's vdst read by VALU needs its pass count + 2 wait
+// states, at most 18 for the 16-pass 32 x 32 shapes; three `s_nop 7` give 24.  The asm names
+// every accumulator as in and out, so no read of them can be scheduled above it.
 template <int DT>
 __device__ __forceinline__ void acc_settle(f32x16 (&acc)[DT]) {
     static_assert(DT == 2 || DT == 4, "2 or 4 d tiles");

@@ -182,7 +182,7 @@ nabla_status nabla_block_mask_grid(const void *q, const void *k, nabla_dtype dty
  * workspace (nabla_block_mask_workspace(B, S, heads, head_dim)) are those of the fractal
  * layout: the lists are identical to nabla_block_mask_grid's on the permuted q and k.
  * Errors: those of nabla_block_mask_grid; UNSUPPORTED also for H or W not a multiple of 8,
- * or 8 * W * heads * head_dim * element size >= 2^32.
+ * 8 * W * heads * head_dim * element size >= 2^32, or more than 4096 blocks (S/64).
  */
 nabla_status nabla_block_mask_natural(const void *q, const void *k, nabla_dtype dtype, int B,
                                       int T, int H, int W, int heads, int head_dim,
@@ -283,7 +283,8 @@ nabla_status nabla_sparse_attn_fwd_grid(const void *q, const void *k, const void
  * lse:      out [B, heads, S] fp32 in fractal order (as nabla_sparse_attn_fwd_lse), or NULL.
  * ws:       nabla_sparse_attn_workspace_grid(B, T, H, W, heads) bytes.
  * Errors: those of nabla_sparse_attn_fwd_grid; UNSUPPORTED also for H or W not a multiple
- * of 8, or 8 * W * heads * head_dim * element size >= 2^32.
+ * of 8, 8 * W * heads * head_dim * element size >= 2^32, or
+ * more than 4096 blocks (S/64).
  */
 nabla_status nabla_sparse_attn_fwd_natural(const void *q, const void *k, const void *v,
                                            nabla_dtype dtype, int B, int T, int H, int W,
@@ -454,8 +455,8 @@ nabla_status nabla_sparse_attn_fwd_q8_grid(const int8_t *q8, const float *q_scal
  * k mean (in the fractal block layout of nabla_quant_qkv) are bit-identical to
  * nabla_quant_qkv's on the permuted tensors.  Workspace: nabla_quant_qkv_workspace(B, S,
  * heads, head_dim).  Errors: those of nabla_quant_qkv; INVALID_ARG also for T, H or W < 1;
- * UNSUPPORTED also for H or W not a multiple of 8, or 8 * W * heads * head_dim * element
- * size >= 2^32.
+ * UNSUPPORTED also for H or W not a multiple of 8, 8 * W * heads * head_dim * element
+ * size >= 2^32, or more than 4096 blocks (S/64).
  */
 nabla_status nabla_quant_qkv_natural(const void *q, const void *k, const void *v,
                                      nabla_dtype dtype, int B, int T, int H, int W, int heads,
@@ -470,7 +471,7 @@ nabla_status nabla_quant_qkv_natural(const void *q, const void *k, const void *v
  * codes and lists.  Codes, scales, lists and workspace
  * (nabla_sparse_attn_q8_workspace(B, S, heads, T, H/8, W/8)) as for nabla_sparse_attn_fwd_q8.
  * Errors: those of nabla_sparse_attn_fwd_q8; INVALID_ARG also for T, H or W < 1;
- * UNSUPPORTED also for H or W not a multiple of 8.
+ * UNSUPPORTED also for H or W not a multiple of 8, or more than 4096 blocks (S/64).
  */
 nabla_status nabla_sparse_attn_fwd_q8_natural(const int8_t *q8, const float *q_scale,
                                               const int8_t *k8, const float *k_scale,

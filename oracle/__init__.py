@@ -94,6 +94,8 @@ def _load():
     lib.orc_attention_bwd.restype = i32
     lib.orc_attention_bwd_grid.argtypes = [P, P, P, P] + [i32] * 6 + [P, P, f64, P, P, P, P]
     lib.orc_attention_bwd_grid.restype = i32
+    lib.orc_attention_dkdv.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, f64, P, i64, P, P]
+    lib.orc_attention_dkdv.restype = i32
     lib.orc_fp8_e4m3.argtypes = [f64]
     lib.orc_fp8_e4m3.restype = ctypes.c_uint8
     lib.orc_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
@@ -434,6 +436,23 @@ def attention_bwd(q, k, v, dout, kv_nb, kv_inds, scale=0.0):
     if rc != 0:
         raise ValueError("oracle attention_bwd: bad argument")
     return {"lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def attention_dkdv(q, k, v, dout, kv_nb, kv_inds, col_ids, scale=0.0):
+    """dk and dv of the 64 keys of each listed key block id (b*heads + h)*nb + j, from every
+    query row whose block lists j.  Returns (col_ids, dk [n, 64, D], dv [n, 64, D]) fp64."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    B, S, heads, D = q.shape
+    kv_nb, kv_inds = _lists(kv_nb, kv_inds)
+    col_ids = np.ascontiguousarray(col_ids, dtype=np.int64)
+    dk = np.zeros((col_ids.size, BLOCK, D), np.float64)
+    dv = np.zeros((col_ids.size, BLOCK, D), np.float64)
+    rc = _load().orc_attention_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, S, heads, D,
+                                    _ptr(kv_nb), _ptr(kv_inds), float(scale), _ptr(col_ids),
+                                    col_ids.size, _ptr(dk), _ptr(dv))
+    if rc != 0:
+        raise ValueError("oracle attention_dkdv: bad argument")
+    return col_ids, dk, dv
 
 
 def attention_bwd_grid(q, k, v, dout, grid, kv_nb, kv_inds, scale=0.0):

@@ -837,6 +837,94 @@ int orc_attention_bwd(const float *q, const float *k, const float *v, const floa
                                   lse, dq, dk, dv);
 }
 
+/* dk and dv of the 64 keys of each listed key block id = (b*heads + h)*nb + j only
+ * (dk[(cc*64 + c)*D + d], likewise dv), for checks at sizes where the full pass is too
+ * slow.  The definition is the one above: key c of block j gathers, in ascending row
+ * order, from every query row whose block lists j, with that row's lse and Delta taken
+ * from its own full row pass.  Per (b, h) slice, only the rows of blocks that list one of
+ * the requested key blocks get a row pass.  Returns 0, or -1 on a bad argument. */
+int orc_attention_dkdv(const float *q, const float *k, const float *v, const float *dout,
+                       int B, int S, int heads, int D, const int32_t *kv_nb,
+                       const int32_t *kv_inds, double scale, const int64_t *col_ids,
+                       int64_t ncols, double *dk, double *dv) {
+    if (B <= 0 || heads <= 0 || D <= 0 || S <= 0 || S % ORC_BLK != 0 || ncols < 0) return -1;
+    const int nb = S / ORC_BLK;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    for (int64_t cc = 0; cc < ncols; ++cc)
+        if (col_ids[cc] < 0 || col_ids[cc] >= (int64_t)B * heads * nb) return -1;
+    uint8_t *allowed = (uint8_t *)malloc((size_t)nb * nb);
+    uint8_t *need = (uint8_t *)malloc((size_t)nb);
+    double *lse = (double *)malloc(sizeof(double) * (size_t)S);
+    double *delta = (double *)malloc(sizeof(double) * (size_t)S);
+    if (!allowed || !need || !lse || !delta) {
+        free(allowed); free(need); free(lse); free(delta);
+        return -1;
+    }
+    int bad = 0;
+    for (int64_t slice = 0; slice < (int64_t)B * heads && !bad; ++slice) {
+        int any = 0;
+        for (int64_t cc = 0; cc < ncols; ++cc) any |= col_ids[cc] / nb == slice;
+        if (!any) continue;
+        const int64_t b = slice / heads;
+        const int h = (int)(slice % heads);
+        if (orc_slice_allowed(kv_nb, kv_inds, slice, nb, allowed) != 0) { bad = 1; break; }
+        /* the query blocks whose lists hold a requested key block of this slice */
+        memset(need, 0, (size_t)nb);
+        for (int64_t cc = 0; cc < ncols; ++cc) {
+            if (col_ids[cc] / nb != slice) continue;
+            const int j = (int)(col_ids[cc] % nb);
+            for (int i = 0; i < nb; ++i) need[i] |= allowed[(size_t)i * nb + j];
+        }
+#pragma omp parallel
+        {
+            double *z = (double *)malloc(sizeof(double) * (size_t)S);
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t r = 0; r < S; ++r)
+                if (need[r / ORC_BLK])
+                    orc_row_pass(q, k, v, dout, b, h, S, heads, D, 0, 0,
+                                 allowed + (size_t)(r / ORC_BLK) * nb, scale, r, z, &lse[r],
+                                 &delta[r], NULL);
+            free(z);
+        }
+#pragma omp parallel for schedule(dynamic, 4) collapse(2)
+        for (int64_t cc = 0; cc < ncols; ++cc)
+            for (int kc = 0; kc < ORC_BLK; ++kc) {
+                if (col_ids[cc] / nb != slice) continue;
+                const int j = (int)(col_ids[cc] % nb);
+                const int64_t c = (int64_t)j * ORC_BLK + kc;
+                const float *kr = k + ((b * S + c) * heads + h) * D;
+                const float *vr = v + ((b * S + c) * heads + h) * D;
+                double *dkc = dk + (cc * ORC_BLK + kc) * D;
+                double *dvc = dv + (cc * ORC_BLK + kc) * D;
+                for (int d = 0; d < D; ++d) { dkc[d] = 0.0; dvc[d] = 0.0; }
+                for (int i = 0; i < nb; ++i) {
+                    if (!allowed[(size_t)i * nb + j]) continue;
+                    for (int rb = 0; rb < ORC_BLK; ++rb) {
+                        const int64_t r = (int64_t)i * ORC_BLK + rb;
+                        const float *qr = q + ((b * S + r) * heads + h) * D;
+                        const float *dor = dout + ((b * S + r) * heads + h) * D;
+                        double zz = 0.0, dp = 0.0;
+                        for (int d = 0; d < D; ++d) {
+                            zz += (double)qr[d] * (double)kr[d];
+                            dp += (double)dor[d] * (double)vr[d];
+                        }
+                        const double p = exp(scale * zz - lse[r]);
+                        const double dz = p * (dp - delta[r]);
+                        for (int d = 0; d < D; ++d) {
+                            dvc[d] += p * (double)dor[d];
+                            dkc[d] += scale * dz * (double)qr[d];
+                        }
+                    }
+                }
+            }
+    }
+    free(allowed);
+    free(need);
+    free(lse);
+    free(delta);
+    return bad ? -1 : 0;
+}
+
 /* The training pass on the padded fractal layout of a T x H x W grid (the gradient of
  * orc_attention_grid's output): padding positions are never keys. */
 int orc_attention_bwd_grid(const float *q, const float *k, const float *v, const float *dout,

@@ -294,6 +294,18 @@ def test_quant_validation(L):
         assert gcall(**kw) == INVALID, kw
     assert gcall(D=96) == UNSUP
     assert gcall(wsb=L.nabla_quant_qkv_workspace(1, 2 * 2 * 3 * 64, 8, 128) - 1) == WS
+    n = L.nabla_quant_qkv_natural
+
+    def ncall(T=2, H=48, W=80, wsb=1 << 40):
+        return n(FAKE, FAKE, FAKE, BF16, 1, T, H, W, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, wsb, None)
+
+    assert ncall(T=0) == INVALID
+    assert ncall(H=44) == UNSUP
+    # more than 4096 blocks in a sequence: the natural-order block addressing is not exact
+    assert ncall(T=69, H=48, W=80) == UNSUP        # 69 * 60 = 4140 blocks
+    assert ncall(T=1, H=8, W=8 * 4097) == UNSUP    # one row of 4097 patches
+    assert ncall(T=68, wsb=L.nabla_quant_qkv_workspace(1, 68 * 48 * 80, 8, 128) - 1) == WS
 
 
 def test_sparse_attn_q8_validation(L):

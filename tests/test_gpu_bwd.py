@@ -161,9 +161,10 @@ def test_bwd_estimator_lists_small(orc, dev):
 
 
 def test_bwd_720p_sampled_and_sums(orc, dev):
-    """720p with the oracle estimator's lists: lse and dq on sampled query blocks against the
-    oracle; per (b, h) the sum of dv over all keys equals the sum of dO over all rows, and the
-    sum of dk is 0 (properties of the exact gradient at any size)."""
+    """720p with the oracle estimator's lists: lse and dq on sampled query blocks, dk and dv on
+    sampled key blocks (among them the key block that the most query blocks list) against the
+    oracle, element by element; per (b, h) the sum of dv over all keys equals the sum of dO over
+    all rows, and the sum of dk is 0 (properties of the exact gradient at any size)."""
     w = synth.WORKLOADS["720p"]
     say("[bwd 720p]", w.describe())
     qn, kn, vn = synth.make_qkv(w)
@@ -191,6 +192,25 @@ def test_bwd_720p_sampled_and_sums(orc, dev):
     dq_g = np.stack([got["dq"][0, 64 * (int(r) % nb):64 * (int(r) % nb + 1), int(r) // nb] for r in ids])
     lse_check(lse_g, lse_o, "lse 720p sampled")
     rel_check(dq_g, dq_o, "dq 720p sampled")
+    # dk, dv: key block j of head h gathers from every query block whose list holds j
+    held = np.zeros((w.heads, nb), np.int64)  # how many query blocks list each key block
+    for hh in range(w.heads):
+        for i in range(nb):
+            held[hh, m["kv_inds"][0, hh, i, :m["kv_nb"][0, hh, i]]] += 1
+    h_top = int(np.argmax(held.max(1)))
+    h_other = (h_top + 1 + int(rng.integers(w.heads - 1))) % w.heads
+    # the most and the least listed key blocks of that head, and a random one of another head
+    # (each costs the oracle a full row pass of every query block that lists it)
+    cols = {h_top * nb + int(np.argmax(held[h_top])), h_top * nb + int(np.argmin(held[h_top])),
+            h_other * nb + int(rng.integers(nb))}
+    cols = np.array(sorted(cols), np.int64)
+    say("[bwd 720p] oracle dk, dv on %d key blocks (listed by %s query blocks)"
+        % (cols.size, [int(held.reshape(-1)[c]) for c in cols]))
+    _, dk_o, dv_o = orc.attention_dkdv(q, k, v, do, m["kv_nb"], m["kv_inds"], cols)
+    key_rows = lambda g: np.stack([g[0, 64 * (int(c) % nb):64 * (int(c) % nb + 1), int(c) // nb]
+                                   for c in cols])
+    rel_check(key_rows(got["dk"]), dk_o, "dk 720p sampled key blocks")
+    rel_check(key_rows(got["dv"]), dv_o, "dv 720p sampled key blocks")
     sum_do = do.astype(np.float64).sum(1)  # [B, h, D]; every 720p row lists >= 1 block
     sum_dv = got["dv"].sum(1)
     sum_dk = got["dk"].sum(1)

@@ -259,25 +259,55 @@ def test_selection_dominant_block(orc):
     assert np.flatnonzero(kept).tolist() == [37]
 
 
-def test_selection_matches_fp64_transcription(orc):
-    """A float64 torch transcription of the binarization steps, with a stable sort."""
-    torch = pytest.importorskip("torch")
+def test_selection_matches_definition_in_fp64(orc):
+    """The kept set from its definition, computed independently in fp64: with p the softmax of
+    the row, block j is kept when the mass of every block that comes at or before j in
+    ascending (p, index) order reaches fl32(1 - thr) ("nabla" page, nablaT_v2, map
+    binarization).  The mass before each block is found by comparing every pair of blocks,
+    with no sort.  Rows whose CDF at the cut lies within 1e-6 of it are skipped (there the
+    fp32 and fp64 masses may fall on different sides)."""
     rng = np.random.default_rng(7)
     nb = 128
+    idx = np.arange(nb)
     s = (rng.standard_normal((64, nb)) * 1.5).astype(np.float32)
+    checked = 0
     for thr in (0.5, 0.9):
-        m = torch.softmax(torch.from_numpy(s).double(), dim=-1)
-        vals, inds = torch.sort(m, dim=-1, stable=True)
-        c = torch.cumsum(vals, dim=-1)
-        mask = (c >= float(np.float32(1 - thr))).int()
-        mask = mask.gather(-1, torch.argsort(inds, dim=-1)).numpy()
+        cut = float(np.float32(1 - thr))
         for r in range(s.shape[0]):
+            z = s[r].astype(np.float64)
+            p = np.exp(z - z.max())
+            p /= p.sum()
+            # at_or_before[j, l]: block l comes at or before block j in (p, index) order
+            at_or_before = (p[None, :] < p[:, None]) | ((p[None, :] == p[:, None]) &
+                                                       (idx[None, :] <= idx[:, None]))
+            mass = (at_or_before * p[None, :]).sum(axis=1)
+            want = (mass >= cut).astype(np.uint8)
             kept, diag = orc.select_row(s[r], thr)
             c_prev, c_at = diag[1] / FIX, diag[2] / FIX
-            cut = float(np.float32(1 - thr))
             if min(abs(c_prev - cut), abs(c_at - cut)) < 1e-6:
                 continue
-            assert np.array_equal(kept, mask[r].astype(np.uint8)), (thr, r)
+            assert np.array_equal(kept, want), (thr, r)
+            checked += 1
+    assert checked >= 120
+
+
+def test_band_rows_flags_rows_at_the_cut(orc):
+    """band_rows marks a row when its CDF just before or at the cut position lies within the
+    width of fl32(1 - thr).  Uniform rows give closed forms: with nb = 8 equal scores the
+    sorted CDF is k/8, so thr = 0.5 puts c = 0.5 exactly on the cut (a band row), thr = 0.9
+    leaves the nearest c (1/8) 0.025 away (not one); with nb = 5 and thr = 0.6 the cut
+    fl32(0.4) lies 6e-9 from c = 2/5."""
+    for nb, thr, want in ((8, 0.5, True), (8, 0.9, False), (5, 0.6, True), (8, 0.95, False)):
+        _, diag = orc.select_row(np.zeros(nb, np.float32), thr)
+        assert bool(orc.band_rows(diag[None, :], thr)[0]) is want, (nb, thr)
+    # a peaked row: the only candidates are far from the cut
+    s = np.array([0.0, 0.0, 0.0, 9.0], np.float32)
+    _, diag = orc.select_row(s, 0.9)
+    assert not orc.band_rows(diag[None, :], 0.9)[0]
+    # the width is honoured: a diag exactly 2e-6 away is flagged at width 3e-6 only
+    cut = float(np.float32(0.1))
+    d = np.array([[1, int(round((cut - 2e-6) * FIX)), int(round((cut + 0.3) * FIX))]], np.int64)
+    assert not orc.band_rows(d, 0.9)[0] and orc.band_rows(d, 0.9, width=3e-6)[0]
 
 
 # ------------------------------------------------------------------ O3-O9 estimator
@@ -495,6 +525,40 @@ def test_training_pass_sampled_functions_agree(orc):
         hh, i = divmod(int(rid), nb)
         assert np.array_equal(lse[n], full["lse"][0, hh, 64 * i:64 * (i + 1)])
         assert np.array_equal(dq[n], full["dq"][0, 64 * i:64 * (i + 1), hh])
+
+
+def test_training_pass_dkdv_sampled_key_blocks(orc):
+    """attention_dkdv on sampled key blocks equals the full pass at those keys bit for bit
+    (the same definition, gathered from the same rows in the same order), and torch's fp64
+    autograd within 1e-11; a key block that no list holds gets dk = dv = 0."""
+    rng = np.random.default_rng(24)
+    B, S, h, D = 2, 448, 2, 16
+    nb = S // 64
+    q, k, v, dout = (rng.standard_normal((B, S, h, D)).astype(np.float32) for _ in range(4))
+    kv_nb, kv_inds = _random_lists(rng, B, h, nb, empty_row=(1, 1, 3))
+    # block 2 of slice (0, 1) is listed by no row
+    for i in range(nb):
+        row = [x for x in kv_inds[0, 1, i] if x != 2] + [2]
+        kv_inds[0, 1, i] = row
+        kv_nb[0, 1, i] = min(kv_nb[0, 1, i], nb - 1)
+    scale = 0.4
+    full = orc.attention_bwd(q, k, v, dout, kv_nb, kv_inds, scale=scale)
+    _, dq_a, dk_a, dv_a = _autograd_reference(q, k, v, dout, kv_nb, kv_inds, scale)
+    cols = np.array([0 * nb + 5, 1 * nb + 2, 1 * nb + 0, 2 * nb + 6, 3 * nb + 3, 3 * nb + 4],
+                    np.int64)  # ids (b*h + hh)*nb + j
+    _, dk, dv = orc.attention_dkdv(q, k, v, dout, kv_nb, kv_inds, cols, scale=scale)
+    for n, c in enumerate(cols):
+        bh, j = divmod(int(c), nb)
+        b, hh = divmod(bh, h)
+        sl = slice(64 * j, 64 * (j + 1))
+        assert np.array_equal(dk[n], full["dk"][b, sl, hh]), c
+        assert np.array_equal(dv[n], full["dv"][b, sl, hh]), c
+        assert np.max(np.abs(dk[n] - dk_a[b, sl, hh])) < 1e-11, c
+        assert np.max(np.abs(dv[n] - dv_a[b, sl, hh])) < 1e-11, c
+    assert np.all(dk[1] == 0.0) and np.all(dv[1] == 0.0)  # slice (0, 1), block 2: unlisted
+    assert np.abs(dv[0]).max() > 0.0
+    with pytest.raises(ValueError):
+        orc.attention_dkdv(q, k, v, dout, kv_nb, kv_inds, np.array([B * h * nb], np.int64))
 
 
 # ------------------------------------------------------------------ O12 top-k variant
