@@ -23,7 +23,7 @@ __all__ = ["nabla_fractal_permute", "nabla_sta_mask", "nabla_block_mask",
            "nabla_block_mask_workspace", "nabla_sparse_attn_fwd", "nabla_sparse_attn_workspace",
            "nabla_sparse_attn_bwd", "nabla_sparse_attn_bwd_workspace", "fractal_len",
            "nabla_quant_qkv", "nabla_sparse_attn_fwd_q8", "nabla_block_mask_natural",
-           "nabla_sparse_attn_fwd_natural",
+           "nabla_sparse_attn_fwd_natural", "nabla_sparse_attn_fwd_noalloc",
            "NablaError", "lib",
            "LIB_PATH", "STATUS"]
 
@@ -84,6 +84,8 @@ def lib():
     L.nabla_sparse_attn_workspace.restype = Z
     L.nabla_sparse_attn_fwd.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P, Z, P]
     L.nabla_sparse_attn_fwd.restype = I
+    L.nabla_sparse_attn_fwd_noalloc.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P]
+    L.nabla_sparse_attn_fwd_noalloc.restype = I
     L.nabla_sparse_attn_fwd_lse.argtypes = [P, P, P, I, I, I, I, I, P, P, F, I, I, I, P, P, P, Z,
                                             P]
     L.nabla_sparse_attn_fwd_lse.restype = I
@@ -321,6 +323,32 @@ def nabla_sparse_attn_fwd(q, k, v, kv_nb, kv_inds, scale=None, causal=False, til
                                            _p(o), None if lse is None else _p(lse),
                                            _p(workspace), workspace.numel(), _stream(q)),
            "nabla_sparse_attn_fwd")
+    return o
+
+
+def nabla_sparse_attn_fwd_noalloc(q, k, v, kv_nb, kv_inds, out, scale=None, tiles=None):
+    """nabla_sparse_attn_fwd into the caller's `out` with no allocation at all: the library
+    keeps the call's work schedule in a static 1 MiB device array per GPU (calls that overlap
+    on one GPU race).  Raises NablaError (NABLA_ERR_WORKSPACE) when the schedule of this
+    shape does not fit."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("kv_nb", kv_nb), ("kv_inds", kv_inds)):
+        _dev(t, name)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must match in shape and dtype")
+    if kv_nb.dtype != torch.int32 or kv_inds.dtype != torch.int32:
+        raise TypeError("kv_nb and kv_inds must be int32")
+    B, S, heads, D = q.shape
+    nb = S // BLOCK
+    if kv_nb.numel() != B * heads * nb or kv_inds.numel() != B * heads * nb * nb:
+        raise ValueError("kv lists do not match q's shape")
+    _same_device(q.device, k=k, v=v, kv_nb=kv_nb, kv_inds=kv_inds)
+    o = _out(out, "out", q.shape, q.dtype, q.device)
+    Tt, Ht, Wt = (0, 0, 0) if tiles is None else tiles
+    _check(lib().nabla_sparse_attn_fwd_noalloc(_p(q), _p(k), _p(v), _dtype_code(q), B, S, heads,
+                                               D, _p(kv_nb), _p(kv_inds),
+                                               0.0 if scale is None else float(scale), Tt, Ht,
+                                               Wt, _p(o), _stream(q)),
+           "nabla_sparse_attn_fwd_noalloc")
     return o
 
 

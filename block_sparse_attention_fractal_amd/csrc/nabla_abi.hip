@@ -3,12 +3,14 @@
 // enqueued unless the call returns NABLA_OK.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/nabla.h"
 #include "nabla_launch.h"
 
 namespace {
 
-constexpr int kAbiVersion = 10;
+constexpr int kAbiVersion = 11;
 constexpr int kBlock = 64;
 constexpr int kTile = 8;
 constexpr int kMaxBlocks = 4096;  // longest list row the kernels support (64 x 64-bit words)
@@ -468,6 +470,64 @@ nabla_status nabla_sparse_attn_fwd_q8_grid(const int8_t *q8, const float *q_scal
     return attn_fwd_q8(q8, q_scale, k8, k_scale, v8, v_scale, B, (int)S, heads, head_dim, kv_nb,
                        kv_inds, scale, T, (int)tiles(H), (int)tiles(W), H, W, false, o, ws,
                        ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the forward without allocation.  Its only scratch memory, the work schedule (take
+// counter, group costs, group order), lives in a file-scope device array: every GPU the
+// library runs on holds its own copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only stands for the symbol): the device address
+// comes from hipGetSymbolAddress, once per device, and is kept per device.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)1 << 20;  // 1 MiB: up to 131 008 query-block groups
+constexpr int kMaxScratchDevices = 64;
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices];  // device address of `scratch` per device, or null
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// The current device's address of `scratch`, looked up on the first call on that device.
+nabla_status scratch_for_current_device(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return NABLA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return NABLA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return NABLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nabla_status nabla_sparse_attn_fwd_noalloc(const void *q, const void *k, const void *v,
+                                           nabla_dtype dtype, int B, int S, int heads,
+                                           int head_dim, const int32_t *kv_nb,
+                                           const int32_t *kv_inds, float scale, int Tt, int Ht,
+                                           int Wt, void *o, void *stream) {
+    const nabla_status st = attn_fwd_check(q, k, v, dtype, B, S, heads, head_dim, kv_nb,
+                                           kv_inds, scale, Tt, Ht, Wt, o);
+    if (st != NABLA_OK) return st;
+    if (nabla::sparse_attn_workspace_bytes(B, S, heads, Tt, Ht, Wt) > kScratchBytes)
+        return NABLA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const nabla_status got = scratch_for_current_device(&ws);
+    if (got != NABLA_OK) return got;
+    return attn_fwd(q, k, v, dtype, B, S, heads, head_dim, kv_nb, kv_inds, scale, Tt, Ht, Wt, 0,
+                    0, false, o, nullptr, ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -235,6 +235,29 @@ nabla_status nabla_sparse_attn_fwd(const void *q, const void *k, const void *v,
                                    void *stream);
 
 /*
+ * nabla_sparse_attn_fwd without allocation or a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The call's only scratch memory, its work schedule, lives in a static
+ * 1 MiB device array that the library holds on every GPU it runs on until the process ends
+ * (its address is looked up once per device, on the first call there).  The call itself
+ * allocates nothing.
+ * Arguments, layouts, results and the other errors are those of nabla_sparse_attn_fwd; the
+ * output equals nabla_sparse_attn_fwd's bit for bit.
+ * Limit: the schedule, nabla_sparse_attn_workspace(B, S, heads, Tt, Ht, Wt) bytes, must fit
+ * in 1 MiB (up to 131 008 groups of query blocks, e.g. B * heads <= 545 on the 720p tile grid
+ * 16 x 6 x 10, whose 960 blocks form 240 groups per head), else NABLA_ERR_WORKSPACE.  NABLA_ERR_HIP also if the array's address
+ * cannot be looked up.
+ * Every call on one GPU shares that GPU's array and overwrites it (nothing is carried between
+ * calls): calls that overlap on one GPU, e.g. on two streams, race and must be serialized by
+ * the caller.
+ */
+nabla_status nabla_sparse_attn_fwd_noalloc(const void *q, const void *k, const void *v,
+                                           nabla_dtype dtype, int B, int S, int heads,
+                                           int head_dim, const int32_t *kv_nb,
+                                           const int32_t *kv_inds, float scale, int Tt, int Ht,
+                                           int Wt, void *o, void *stream);
+
+/*
  * The same forward, also writing each row's log-sum-exp, which the backward needs
  * (the training pass of the same attention: NABLA summary page, Results, training
  * speed-up; the "nabla" page's forward runs flex attention, whose backward is the

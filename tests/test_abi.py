@@ -46,14 +46,15 @@ def test_exports_every_declared_symbol(L):
                           "nabla_sparse_attn_fwd_q8", "nabla_sparse_attn_bwd_grid",
                           "nabla_quant_qkv_grid", "nabla_sparse_attn_fwd_q8_grid",
                           "nabla_block_mask_natural", "nabla_sparse_attn_fwd_natural",
-                          "nabla_quant_qkv_natural", "nabla_sparse_attn_fwd_q8_natural"}
+                          "nabla_quant_qkv_natural", "nabla_sparse_attn_fwd_q8_natural",
+                          "nabla_sparse_attn_fwd_noalloc"}
     raw = ctypes.CDLL(nabla.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
 
 
 def test_version_and_status_strings(L):
-    assert L.nabla_abi_version() == 10
+    assert L.nabla_abi_version() == 11
     for s in range(5):
         assert L.nabla_status_string(s)
     assert L.nabla_status_string(99) == b"unknown status"
@@ -168,6 +169,32 @@ def test_natural_entry_points_validation(L):
     need = L.nabla_sparse_attn_workspace_grid(1, 2, 48, 80, 8)
     assert need > 0
     assert fwd(wsb=need - 1) == WS
+
+
+def test_sparse_attn_noalloc_validation(L):
+    """The no-allocation forward validates like nabla_sparse_attn_fwd, and rejects shapes whose
+    schedule does not fit its static 1 MiB scratch, all before touching the GPU."""
+    f = L.nabla_sparse_attn_fwd_noalloc
+
+    def call(q=FAKE, o=FAKE, B=1, S=61440, heads=16, D=128, tiles=(16, 6, 10), dt=BF16,
+             scale=0.0):
+        return f(q, FAKE, FAKE, dt, B, S, heads, D, FAKE, FAKE, scale, *tiles, o, None)
+
+    assert call(q=None) == INVALID
+    assert call(o=None) == INVALID
+    assert call(dt=9) == INVALID
+    assert call(S=1000) == INVALID
+    assert call(scale=math.nan) == INVALID
+    assert call(tiles=(16, 6, 9)) == INVALID
+    assert call(D=96) == UNSUP
+    # 546 (b, head) slices of the 720p tile grid: 546 * 240 groups > 131 008
+    assert L.nabla_sparse_attn_workspace(546, 61440, 1, 16, 6, 10) > (1 << 20)
+    assert call(B=546, heads=1) == WS
+    assert L.nabla_sparse_attn_workspace(1, 61440, 545, 16, 6, 10) <= (1 << 20)
+    # unknown grid (groups of 4 consecutive blocks): 33 sequences of 4096 blocks = 33 792 groups
+    # fit, 33 * 4 = 132 sequences do not
+    assert L.nabla_sparse_attn_workspace(132, 4096 * 64, 1, 0, 0, 0) > (1 << 20)
+    assert call(B=132, S=4096 * 64, heads=1, tiles=(0, 0, 0)) == WS
 
 
 def test_sparse_attn_workspace_size(L):
