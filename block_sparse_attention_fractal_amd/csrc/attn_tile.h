@@ -7,7 +7,6 @@
 namespace nabla {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-#define NABLA_LDS __attribute__((address_space(3)))
 
 // Key row (within a 32-row score tile) fed to MFMA row m: bit layout
 // m = a(2) hh(1) b(2)  ->  key = (a>>1)<<4 | hh<<3 | (a&1)<<2 | b.
@@ -28,29 +27,6 @@ template <int CH>
 __device__ __forceinline__ int kswz(int kv) { return kv & (CH - 1); }
 template <int CH>
 __device__ __forceinline__ int vswz(int kv) { return (kv & 3) * (CH / 4); }
-
-// Byte offset of a __shared__ object in LDS.
-__device__ __forceinline__ uint32_t lds_offset(const void *p) {
-    return (uint32_t)(uintptr_t)((const NABLA_LDS char *)p);
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane l's chunk lands at
-// m0 + 16 l (m0 wave-uniform).  Issued from inline asm so that the compiler does not
-// treat every later LDS read as depending on it; completion is awaited explicitly
-// with vm_wait before the barrier that hands the tile to the other waves.  Nothing
-// else in the kernel uses m0.
-// The base address is wave-uniform (SGPR pair) and each lane gives a 32-bit byte offset:
-// no per-lane 64-bit address arithmetic.
-__device__ __forceinline__ void lds_direct16_sv(const void *base, uint32_t off, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(off), "s"(base), "s"(m0)
-                 : "memory");
-}
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
 
 // Query blocks per attention workgroup: kGroup 4 takes a 2 (time) x 1 x 2 (width) box of
 // tiles, kGroup 2 the same tile in two consecutive frames.

@@ -183,34 +183,58 @@ struct SelectShared {
     uint64_t sel_key;
 };
 
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const uint64_t o = shfl_xor_u64(v, m);
-        v = o < v ? o : v;
-    }
+// ---- wave-wide reductions and scans on DPP.  Each step is one VALU operation whose
+// source is another lane of the wave: row_shr:k (within 16-lane rows), then row_bcast15
+// (lane 15 of a row into the next row; rows 1 and 3 written) and row_bcast31 (lane 31 into
+// rows 2 and 3).  Six steps give an inclusive scan over all 64 lanes; lane 63 then holds the
+// whole-wave result, read back with v_readlane.  No LDS round trip.  Lanes without a
+// source lane (the first k of a row, and the rows a broadcast does not write) keep `old`.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+__device__ __forceinline__ uint64_t u64_of(uint32_t lo, uint32_t hi) {
+    return ((uint64_t)hi << 32) | lo;
+}
+// one scan step of a 64-bit value: v op= (the value at the DPP source lane, or `idle`
+// where there is none)
+template <int CTRL, int ROWS, typename Op>
+__device__ __forceinline__ uint64_t dpp_step_u64(uint64_t v, uint64_t idle, Op op) {
+    const uint32_t lo = dpp_u32<CTRL, ROWS>((uint32_t)idle, (uint32_t)v);
+    const uint32_t hi = dpp_u32<CTRL, ROWS>((uint32_t)(idle >> 32), (uint32_t)(v >> 32));
+    return op(v, u64_of(lo, hi));
+}
+template <typename Op>
+__device__ __forceinline__ uint64_t wave_scan_u64(uint64_t v, uint64_t idle, Op op) {
+    v = dpp_step_u64<kRowShr1, 0xF>(v, idle, op);
+    v = dpp_step_u64<kRowShr2, 0xF>(v, idle, op);
+    v = dpp_step_u64<kRowShr4, 0xF>(v, idle, op);
+    v = dpp_step_u64<kRowShr8, 0xF>(v, idle, op);
+    v = dpp_step_u64<kRowBcast15, 0xA>(v, idle, op);
+    v = dpp_step_u64<kRowBcast31, 0xC>(v, idle, op);
     return v;
+}
+__device__ __forceinline__ uint64_t lane63_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return u64_of(lo, hi);
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+    // identity ~0: lanes without a source compare against the largest value
+    return lane63_u64(wave_scan_u64(v, ~0ull, [](uint64_t a, uint64_t b) { return b < a ? b : a; }));
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const uint64_t o = shfl_xor_u64(v, m);
-        v = o > v ? o : v;
-    }
-    return v;
+    return lane63_u64(wave_scan_u64(v, 0ull, [](uint64_t a, uint64_t b) { return b > a ? b : a; }));
+}
+// inclusive prefix sum over the lanes (exact integer sums)
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int /*lane*/) {
+    return (int64_t)wave_scan_u64((uint64_t)v, 0ull, [](uint64_t a, uint64_t b) { return a + b; });
 }
 __device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v += (int64_t)shfl_xor_u64((uint64_t)v, m);
-    return v;
-}
-__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int64_t o = (int64_t)shfl_up_u64((uint64_t)v, d);
-        if (lane >= d) v += o;
-    }
-    return v;
+    return (int64_t)lane63_u64((uint64_t)wave_incl_scan_i64(v, 0));
 }
 
 // ---------------------------------------------------------------- select (rows <= 2048)
@@ -232,29 +256,43 @@ constexpr int kSelBins = 256;
 
 struct SelectWaveScratch {
     int64_t hm[kSelBins];  // bin masses
-    int hc[kSelBins];      // bin counts
+    int hc[kSelBins];      // bin counts (rows of more than 1024 blocks)
     uint64_t lkey[64];     // keys of the cut bin
     int64_t lmass[64];
 };
 
-__device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
+// fp32 max / min over the wave on DPP (lanes without a source keep their own value);
+// exact whatever the order
+template <bool MAX>
+__device__ __forceinline__ float wave_ext_f32(float v) {
+    auto step = [&](uint32_t t) {
+        const float o = __uint_as_float(t);
+        v = MAX ? fmaxf(v, o) : fminf(v, o);
+    };
+    step(dpp_u32<kRowShr1, 0xF>(__float_as_uint(v), __float_as_uint(v)));
+    step(dpp_u32<kRowShr2, 0xF>(__float_as_uint(v), __float_as_uint(v)));
+    step(dpp_u32<kRowShr4, 0xF>(__float_as_uint(v), __float_as_uint(v)));
+    step(dpp_u32<kRowShr8, 0xF>(__float_as_uint(v), __float_as_uint(v)));
+    step(dpp_u32<kRowBcast15, 0xA>(__float_as_uint(v), __float_as_uint(v)));
+    step(dpp_u32<kRowBcast31, 0xC>(__float_as_uint(v), __float_as_uint(v)));
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 63));
 }
-__device__ __forceinline__ float wave_min_f32(float v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v = fminf(v, __shfl_xor(v, m));
-    return v;
-}
+__device__ __forceinline__ float wave_max_f32(float v) { return wave_ext_f32<true>(v); }
+__device__ __forceinline__ float wave_min_f32(float v) { return wave_ext_f32<false>(v); }
+// the value of lane `src` (wave-uniform) in every lane
 __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
-    const uint32_t lo = __shfl((uint32_t)v, src), hi = __shfl((uint32_t)(v >> 32), src);
-    return ((uint64_t)hi << 32) | lo;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
+    return u64_of(lo, hi);
 }
 
 // TOPK: the top-k variant ("sla" page, get_block_map): scores without the 1/sqrt(D)
 // scale, every block weighs one unit instead of its softmax weight, and `cut` is
 // nb - k + 1, so the cut keeps exactly the k largest keys (none when k = 0).
+// KST (rows of 129 .. 1024 blocks): the k means of one float4 column (4 dims of every
+// block) are staged in LDS once per workgroup, double-buffered and loaded straight from
+// memory into LDS, and the four waves read them from there; other rows read them from
+// global memory through L1 (measured at 2048 blocks: single-buffered staging is no faster).
 template <int D, int CPT, int RW, bool TOPK = false>
 __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restrict__ qa,
                                                           const float *__restrict__ ka, int nb,
@@ -263,11 +301,15 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
                                                           int32_t *__restrict__ kv_nb,
                                                           int32_t *__restrict__ kv_inds) {
     constexpr int NWV = 4;
+    constexpr bool KST = CPT >= 4 && CPT <= 16;
+    constexpr int KCOL = KST ? 64 * CPT : 1;  // float4s of one staged column (>= 256)
     __shared__ __attribute__((aligned(16))) float qs[NWV][RW][D];
     __shared__ SelectWaveScratch scr[NWV];
+    __shared__ __attribute__((aligned(1024))) float4 kst[2][KCOL];
     const int bh = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * NWV + wv) * RW;
-    if (row0 >= nb) return;  // no barrier in this kernel: waves are independent
+    // with KST every wave takes part in the staging (loads and barriers) of the scores
+    if (!KST && row0 >= nb) return;
     SelectWaveScratch &W = scr[wv];
     const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 
@@ -284,13 +326,38 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
 #pragma unroll
         for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0f;
     const float4 *kb = reinterpret_cast<const float4 *>(ka) + (int64_t)bh * (D / 4) * nb;
+    // column d4 of the k means into buffer `buf`: float4 e = 256 r + tid lands at kst[buf][e]
+    // (a wave's 64 lanes fill one contiguous KiB); lanes past the last block load the last
+    // block's value again, so every wave issues the same number of loads (the staged values
+    // past nb feed only columns that are not blocks)
+    const uint32_t kst0 = __builtin_amdgcn_readfirstlane(lds_offset(&kst[0][0]) + wv * 1024);
+    auto stage_col = [&](int d4, int buf) {
+        if constexpr (KST) {
+            const float4 *src = kb + (int64_t)d4 * nb;
+#pragma unroll
+            for (int r = 0; r < KCOL / 256; ++r) {
+                const int e = r * 256 + (int)threadIdx.x;
+                lds_direct16_sv(src, (uint32_t)(e < nb ? e : nb - 1) * 16u,
+                                kst0 + (uint32_t)(buf * KCOL * 16 + r * 4096));
+            }
+        }
+    };
+    stage_col(0, 0);
 #pragma unroll 1
     for (int d4 = 0; d4 < D / 4; ++d4) {
         float4 k4[CPT];
+        if constexpr (KST) {
+            vm_wait<0>();      // this wave's part of column d4 has landed
+            __syncthreads();   // all of it has; every wave is done with column d4 - 1
+            if (d4 + 1 < D / 4) stage_col(d4 + 1, (d4 + 1) & 1);
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const int j = 64 * c + lane;
-            k4[c] = j < nb ? kb[(int64_t)d4 * nb + j] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int c = 0; c < CPT; ++c) k4[c] = kst[d4 & 1][64 * c + lane];
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                const int j = 64 * c + lane;
+                k4[c] = j < nb ? kb[(int64_t)d4 * nb + j] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
@@ -304,6 +371,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
             }
         }
     }
+    if (KST && row0 >= nb) return;  // no barrier below: waves are independent
 
     // ---- per row: softmax on the 2^-48 grid, cut key, STA union, compaction
 #pragma unroll 1
@@ -333,13 +401,15 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
             return ((uint64_t)f32_orderable(s[c]) << 12) | (uint64_t)(64 * c + lane);
         };
 
-        // (the weights are formed twice, for Z and for P, rather than kept: fewer
-        // registers live at once)
+        // LEAN (rows of up to 1024 blocks): the weights are formed once and kept, and the cut
+        // bin's members are counted with ballots.  Longer rows, already past 256 registers,
+        // form the weights twice (for Z and for P) and count with LDS atomics instead.
+        constexpr bool LEAN = CPT <= 16;
         int64_t P[CPT];
         if constexpr (TOPK) {
 #pragma unroll
             for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? 1 : 0;
-        } else {
+        } else if constexpr (!LEAN) {
             int64_t esum = 0;
 #pragma unroll
             for (int c = 0; c < CPT; ++c) esum += fix48(valid[c] ? nabla_exp(s[c] - smax) : 0.0f);
@@ -347,26 +417,37 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
             const float Z = (float)(double)esum * 0x1p-48f;
 #pragma unroll
             for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? fix48(nabla_exp(s[c] - smax) / Z) : 0;
+        } else {
+            float e[CPT];
+            int64_t esum = 0;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                e[c] = valid[c] ? nabla_exp(s[c] - smax) : 0.0f;
+                esum += fix48(e[c]);
+            }
+            esum = wave_sum_i64(esum);
+            const float Z = (float)(double)esum * 0x1p-48f;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? fix48(e[c] / Z) : 0;
         }
 
         // One histogram pass over the members (inr) into kSelBins bins (bin_of); returns
         // the bin holding the cut (-1 if the members' mass stays below it) with the mass
-        // before it and its count.
+        // before it and its count (counted with ballots once the bin is known).
         auto hist_pass = [&](auto inr, auto bin_of, int64_t below, int64_t &bbelow, int &bcnt) {
 #pragma unroll
             for (int q = 0; q < kSelBins / 64; ++q) {
                 W.hm[lane * (kSelBins / 64) + q] = 0;
-                W.hc[lane * (kSelBins / 64) + q] = 0;
+                if (!LEAN) W.hc[lane * (kSelBins / 64) + q] = 0;
             }
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) {
+            for (int c = 0; c < CPT; ++c)
                 if (inr(c)) {
                     const int bn = bin_of(c);
                     atomicAdd((unsigned long long *)&W.hm[bn], (unsigned long long)P[c]);
-                    atomicAdd(&W.hc[bn], 1);
+                    if (!LEAN) atomicAdd(&W.hc[bn], 1);
                 }
-            }
             __builtin_amdgcn_wave_barrier();
             int64_t m[kSelBins / 64];
             int64_t tot = 0;
@@ -376,14 +457,13 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
                 tot += m[q];
             }
             int64_t run = below + wave_incl_scan_i64(tot, lane) - tot;
-            int found = -1, fcnt = 0;
+            int found = -1;
             int64_t fb = 0;
 #pragma unroll
             for (int q = 0; q < kSelBins / 64; ++q) {
                 if (found < 0 && run < cut && run + m[q] >= cut) {
                     found = lane * (kSelBins / 64) + q;
                     fb = run;
-                    fcnt = W.hc[found];
                 }
                 run += m[q];
             }
@@ -391,8 +471,16 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
             if (bal == 0ull) return -1;
             const int src = __builtin_ctzll(bal);
             bbelow = (int64_t)shfl_u64((uint64_t)fb, src);
-            bcnt = __shfl(fcnt, src);
-            return __shfl(found, src);
+            const int fbin = __builtin_amdgcn_readlane(found, src);
+            if constexpr (LEAN) {
+                int n = 0;
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) n += __popcll(__ballot(inr(c) && bin_of(c) == fbin));
+                bcnt = n;
+            } else {
+                bcnt = W.hc[fbin];
+            }
+            return fbin;
         };
         // Exact rank of at most 64 members: the smallest key whose prefix reaches the cut.
         auto rank_list = [&](auto inr, int64_t below) -> uint64_t {

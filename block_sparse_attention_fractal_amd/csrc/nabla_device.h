@@ -33,6 +33,31 @@ __device__ __forceinline__ bf16x8 load8_bf16(const float *p) {
     return r;
 }
 
+#define NABLA_LDS __attribute__((address_space(3)))
+
+// Byte offset of a __shared__ object in LDS.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return (uint32_t)(uintptr_t)((const NABLA_LDS char *)p);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's chunk lands at
+// m0 + 16 l (m0 wave-uniform).  Issued from inline asm so that the compiler does not
+// treat every later LDS read as depending on it; completion is awaited explicitly
+// with vm_wait before the barrier that hands the tile to the other waves.  The asm
+// declares m0 clobbered.
+// The base address is wave-uniform (SGPR pair) and each lane gives a 32-bit byte offset:
+// no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void lds_direct16_sv(const void *base, uint32_t off, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(m0)
+                 : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // 64-bit lane shuffles built from two 32-bit ones.
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
     uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
