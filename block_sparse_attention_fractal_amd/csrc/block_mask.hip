@@ -46,12 +46,13 @@ namespace nabla {
 // count min(8, H - 8 ht) * min(8, W - 8 wt).  H = W = 0: whole 64-token blocks.
 // ng.W > 0: q and k are in natural order (whole patches, rows of ng.W tokens); block i's
 // rows are read where the fractal permute would have taken them from, in the same order.
+// first = 1: k only (the selection kernel pools q itself).
 template <typename Tin>
 __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
                                                    const Tin *__restrict__ k,
                                                    float *__restrict__ qa,
                                                    float *__restrict__ ka, int S, int heads,
-                                                   int D, int H, int W, NatGrid ng) {
+                                                   int D, int H, int W, NatGrid ng, int first) {
     constexpr int EPC = 16 / sizeof(Tin);  // elements per 16-byte chunk
     const int nb = S / kBlock;
     const int i = blockIdx.x, b = blockIdx.y;
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
     }
     const bool whole = vrows == kTile && vcols == kTile;
     const int cnt = vrows * vcols;
-    for (int item = threadIdx.x; item < 2 * nchunks; item += 256) {
+    for (int item = threadIdx.x + first * nchunks; item < 2 * nchunks; item += 256) {
     const int z = item >= nchunks;  // 0: q, 1: k
     const int ch = item - z * nchunks;
     const Tin *x = z ? k : q;
@@ -293,13 +294,22 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
 // block) are staged in LDS once per workgroup, double-buffered and loaded straight from
 // memory into LDS, and the four waves read them from there; other rows read them from
 // global memory through L1 (measured at 2048 blocks: single-buffered staging is no faster).
+//
+// q != null (bf16, whole blocks; configurations whose lanes cover a row in 16-byte chunks):
+// each wave pools its own RW query blocks from q (in place of reading qa), with the same
+// arithmetic as pool_kernel (a sequential fp32 sum over the 64 tokens in token order, then
+// * 2^-6): 64 / RW lanes per block, each summing D * RW / 64 dimensions.  The q reads then
+// overlap the selection work of the other resident waves, and the pooling pass reads k only.
+// S, heads, ng: q's layout (as pool_kernel).
 template <int D, int CPT, int RW, bool TOPK = false>
 __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restrict__ qa,
                                                           const float *__restrict__ ka, int nb,
                                                           const uint8_t *__restrict__ sta,
                                                           float sqrt_d, int64_t cut,
                                                           int32_t *__restrict__ kv_nb,
-                                                          int32_t *__restrict__ kv_inds) {
+                                                          int32_t *__restrict__ kv_inds,
+                                                          const bf16 *__restrict__ q, int S,
+                                                          int heads, NatGrid ng) {
     constexpr int NWV = 4;
     constexpr bool KST = CPT >= 4 && CPT <= 16;
     constexpr int KCOL = KST ? 64 * CPT : 1;  // float4s of one staged column (>= 256)
@@ -313,10 +323,59 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
     SelectWaveScratch &W = scr[wv];
     const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 
-    for (int e = lane; e < RW * D; e += 64) {
-        const int r = e / D, d = e - r * D;
-        qs[wv][r][d] = row0 + r < nb ? qa[((int64_t)bh * nb + row0 + r) * D + d] : 0.0f;
+    constexpr int LPB = 64 / RW, DPL = D / LPB;  // lanes per query block, dims per lane
+    constexpr int NCH = DPL / 8;                  // 16-byte chunks per lane and row
+    bool pooled = false;
+    if constexpr (DPL % 8 == 0) {
+        if (q != nullptr) {
+            pooled = true;
+            const int g = lane / LPB, li = lane - g * LPB, i = row0 + g;
+            const int b = bh / heads, h = bh - b * heads;
+            float acc[DPL];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[e] = 0.0f;
+            if (i < nb) {
+                const bool nat = ng.W > 0;
+                const int rstep = nat ? ng.W : kTile;  // tokens between rows of a patch
+                const int64_t blk0 = nat ? nat_block_base(i, ng) : (int64_t)i * kBlock;
+                const int64_t tok = (int64_t)heads * D;
+                const bf16 *base = q + ((int64_t)b * S + blk0) * tok + (int64_t)h * D + 8 * li;
+                constexpr int FL = 16 / NCH;  // rows in flight
+                for (int r0 = 0; r0 < kBlock; r0 += FL) {
+                    uint4 raw[FL][NCH];
+#pragma unroll
+                    for (int u = 0; u < FL; ++u)
+#pragma unroll
+                        for (int ch = 0; ch < NCH; ++ch)
+                            raw[u][ch] = *reinterpret_cast<const uint4 *>(
+                                base + (int64_t)(((r0 + u) >> 3) * rstep + ((r0 + u) & 7)) * tok +
+                                8 * LPB * ch);
+#pragma unroll
+                    for (int u = 0; u < FL; ++u)
+#pragma unroll
+                        for (int ch = 0; ch < NCH; ++ch) {
+                            const uint32_t wd[4] = {raw[u][ch].x, raw[u][ch].y, raw[u][ch].z,
+                                                    raw[u][ch].w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float &a0 = acc[8 * ch + 2 * e], &a1 = acc[8 * ch + 2 * e + 1];
+                                a0 = a0 + __uint_as_float(wd[e] << 16);
+                                a1 = a1 + __uint_as_float(wd[e] & 0xffff0000u);
+                            }
+                        }
+                }
+            }
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qs[wv][g][8 * LPB * ch + 8 * li + e] = acc[8 * ch + e] * 0.015625f;
+        }
     }
+    if (!pooled)
+        for (int e = lane; e < RW * D; e += 64) {
+            const int r = e / D, d = e - r * D;
+            qs[wv][r][d] = row0 + r < nb ? qa[((int64_t)bh * nb + row0 + r) * D + d] : 0.0f;
+        }
     __builtin_amdgcn_wave_barrier();
 
     // ---- scores (before the division by sqrt(D))
@@ -801,13 +860,20 @@ static hipError_t launch_select_t(const float *qa, const float *ka, int BH, int 
     return hipGetLastError();
 }
 
+// The query layout the selection kernel pools q from (q null: it reads the pooled qa).
+struct QSource {
+    const bf16 *q;
+    int S, heads;
+    NatGrid ng;
+};
+
 template <int D, int CPT, int RW, bool TOPK = false>
 static hipError_t launch_rows_t(const float *qa, const float *ka, int BH, int nb,
                                 const uint8_t *sta, float sqrt_d, int64_t cut, int32_t *kv_nb,
-                                int32_t *kv_inds, hipStream_t stream) {
+                                int32_t *kv_inds, hipStream_t stream, QSource qsrc = {}) {
     dim3 grid((nb + 4 * RW - 1) / (4 * RW), BH);
     hipLaunchKernelGGL((select_rows_kernel<D, CPT, RW, TOPK>), grid, dim3(256), 0, stream, qa, ka,
-                       nb, sta, sqrt_d, cut, kv_nb, kv_inds);
+                       nb, sta, sqrt_d, cut, kv_nb, kv_inds, qsrc.q, qsrc.S, qsrc.heads, qsrc.ng);
     return hipGetLastError();
 }
 
@@ -864,12 +930,20 @@ __global__ __launch_bounds__(256) void smooth_k_kernel(float *__restrict__ ka, i
     for (int64_t e = t; e < len; e += 256) r[e] = r[e] - km[(int)(e / (4 * (int64_t)nb)) * 4 + (int)(e & 3)];
 }
 
+// Rows per wave of the selection for rows of nb blocks (as launch_select_d chooses), and
+// whether that configuration can pool q itself (16-byte chunks per lane and row).
+static int select_rows_per_wave(int nb) { return nb <= 512 ? 8 : (nb <= 1024 ? 4 : 2); }
+static bool select_pools_q(int D, int nb) {
+    return nb <= 2048 && (D * select_rows_per_wave(nb) / 64) % 8 == 0;
+}
+
 template <int D>
 static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int nb,
                                   const uint8_t *sta, float sqrt_d, int64_t cut, int32_t *kv_nb,
-                                  int32_t *kv_inds, hipStream_t stream) {
+                                  int32_t *kv_inds, hipStream_t stream, QSource qsrc = {}) {
 #define NABLA_ROWS(CPT, RW) \
-    return launch_rows_t<D, CPT, RW>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream)
+    return launch_rows_t<D, CPT, RW>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream, \
+                                     qsrc)
     if (nb <= 64) NABLA_ROWS(1, 8);
     if (nb <= 128) NABLA_ROWS(2, 8);
     if (nb <= 256) NABLA_ROWS(4, 8);
@@ -890,11 +964,11 @@ hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, in
     if (bf16_in)
         hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
                            (const bf16 *)k, qa, ka, S, heads, D, natural ? 0 : H,
-                           natural ? 0 : W, nat_grid(natural ? W : 0));
+                           natural ? 0 : W, nat_grid(natural ? W : 0), 0);
     else
         hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
                            (const float *)k, qa, ka, S, heads, D, natural ? 0 : H,
-                           natural ? 0 : W, nat_grid(natural ? W : 0));
+                           natural ? 0 : W, nat_grid(natural ? W : 0), 0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int BH = B * heads;
@@ -914,20 +988,28 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
                              float *qa, float *ka, hipStream_t stream) {
     const int nb = S / kBlock;
     dim3 pgrid(nb, B);
+    // bf16 whole blocks: the selection kernel pools q itself, the pooling pass only k
+    const bool padded = !natural && H > 0;
+    const bool qfused = bf16_in && !padded && select_pools_q(D, nb);
+    const NatGrid ng = nat_grid(natural ? W : 0);
     if (bf16_in)
         hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
                            (const bf16 *)k, qa, ka, S, heads, D, natural ? 0 : H,
-                           natural ? 0 : W, nat_grid(natural ? W : 0));
+                           natural ? 0 : W, ng, qfused ? 1 : 0);
     else
         hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
                            (const float *)k, qa, ka, S, heads, D, natural ? 0 : H,
-                           natural ? 0 : W, nat_grid(natural ? W : 0));
+                           natural ? 0 : W, ng, 0);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int BH = B * heads;
+    QSource qsrc = {};
+    if (qfused) qsrc = QSource{(const bf16 *)q, S, heads, ng};
     if (D == 64)
-        return launch_select_d<64>(qa, ka, BH, nb, sta, sqrt_d, cut_fixed, kv_nb, kv_inds, stream);
-    return launch_select_d<128>(qa, ka, BH, nb, sta, sqrt_d, cut_fixed, kv_nb, kv_inds, stream);
+        return launch_select_d<64>(qa, ka, BH, nb, sta, sqrt_d, cut_fixed, kv_nb, kv_inds, stream,
+                                   qsrc);
+    return launch_select_d<128>(qa, ka, BH, nb, sta, sqrt_d, cut_fixed, kv_nb, kv_inds, stream,
+                                qsrc);
 }
 
 }  // namespace nabla
