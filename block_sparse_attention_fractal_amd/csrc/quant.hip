@@ -126,10 +126,24 @@ __device__ __forceinline__ uint32_t int8_code(float x, float scale) {
     return (uint32_t)(uint8_t)(int8_t)(int)r;
 }
 
-// One workgroup of 256 lanes per (block, tensor): blockIdx.y = 0 quantizes q, 1 quantizes
-// k - k_mean.  Lane t holds the 8-element chunks e = r*256 + t (row e / (D/8)) in
-// registers, the block maximum comes from a wave reduction and LDS, then the codes are
-// written as 8-byte runs in the same row-major order.
+// The maximum of a non-negative value over the wave, on DPP row shifts and row broadcasts
+// (no LDS round trip; exact in any order), read back from lane 63.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    auto step = [&](int t) { v = fmaxf(v, __int_as_float(t)); };
+    step(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, false));  // row_shr:1
+    step(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, false));  // row_shr:2
+    step(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, false));  // row_shr:4
+    step(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, false));  // row_shr:8
+    step(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+    step(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// One wave per (block, tensor): blockIdx.y = 0 quantizes q, 1 quantizes k - k_mean; the four
+// waves of a workgroup take four consecutive blocks.  Lane l holds the 8-element chunks
+// e = 64 r + l (row e / (D/8)) in registers, so each load instruction of the wave reads whole
+// rows; the block maximum is a wave reduction, then the codes are written as 8-byte runs in
+// the same row-major order.  No barrier.
 template <int D, typename Tin, bool kPad>
 __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q,
                                                        const Tin *__restrict__ k,
@@ -138,30 +152,30 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q
                                                        float *__restrict__ qs,
                                                        int8_t *__restrict__ k8,
                                                        float *__restrict__ ks, int S, int heads,
-                                                       QuantPad g) {
+                                                       int64_t items, QuantPad g) {
     constexpr int CH = D / 8;                  // 8-element chunks per row
-    constexpr int CPT = kBlock * CH / 256;     // chunks per lane
-    __shared__ float wmax[4];
+    constexpr int CPL = kBlock * CH / 64;      // chunks per lane
     const int nb = S / kBlock;
-    const int64_t item = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= items) return;  // wave-uniform; no barrier in this kernel
     const bool is_k = blockIdx.y == 1;
     const int j = (int)(item % nb), bh = (int)(item / nb);
-    const int b = bh / heads, h = bh % heads, tid = threadIdx.x;
+    const int b = bh / heads, h = bh % heads;
     const int64_t tok = (int64_t)heads * D;
     const Tin *src = (is_k ? k : q) + (int64_t)b * S * tok + (int64_t)h * D;
-    float x[CPT][8];
-    float amax = 0.0f;
+    const int c = lane % CH;  // the same channel chunk for every r (64 % CH == 0)
+    float x[CPL][8];
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-        const int e = r * 256 + tid, row = e / CH, c = e % CH;
+    for (int r = 0; r < CPL; ++r) {
+        const int row = (64 * r + lane) / CH;
         load8_f32(src + block_row_token(j, row, g.ng) * tok + 8 * c, x[r]);
     }
     if (is_k) {
-        const int c = tid % CH;  // the same channel chunk for every r (256 % CH == 0)
         float m[8];
         load8_f32(km + (int64_t)bh * D + 8 * c, m);
 #pragma unroll
-        for (int r = 0; r < CPT; ++r)
+        for (int r = 0; r < CPL; ++r)
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[r][i] = x[r][i] - m[i];
     }
@@ -169,26 +183,23 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q
         int vr, vc;
         qpatch(g, j, vr, vc);
 #pragma unroll
-        for (int r = 0; r < CPT; ++r)
-            if (!qrow_ok((r * 256 + tid) / CH, vr, vc))
+        for (int r = 0; r < CPL; ++r)
+            if (!qrow_ok((64 * r + lane) / CH, vr, vc))
 #pragma unroll
                 for (int i = 0; i < 8; ++i) x[r][i] = 0.0f;
     }
+    float amax = 0.0f;
 #pragma unroll
-    for (int r = 0; r < CPT; ++r)
+    for (int r = 0; r < CPL; ++r)
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[r][i]));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    if ((tid & 63) == 0) wmax[tid >> 6] = amax;
-    __syncthreads();
-    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    amax = wave_max_nonneg(amax);
     const float scale = amax / 127.0f;
     int8_t *dst = (is_k ? k8 : q8) + item * (kBlock * D);
-    if (tid == 0) (is_k ? ks : qs)[item] = scale;
+    if (lane == 0) (is_k ? ks : qs)[item] = scale;
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-        const int e = r * 256 + tid;
+    for (int r = 0; r < CPL; ++r) {
+        const int e = 64 * r + lane;
         uint32_t w0 = 0, w1 = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -255,7 +266,14 @@ __global__ __launch_bounds__(D) void quant_vscale_kernel(const float *__restrict
     const int64_t bh = blockIdx.x;
     const int d = threadIdx.x;
     float m = 0.0f;
-    for (int c = 0; c < nchunk; ++c) m = fmaxf(m, part[(bh * nchunk + c) * D + d]);
+    for (int c0 = 0; c0 < nchunk; c0 += 16) {  // 16 loads in flight (a maximum: any order)
+        float x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            x[u] = c0 + u < nchunk ? part[(bh * nchunk + c0 + u) * D + d] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) m = fmaxf(m, x[u]);
+    }
     vs[bh * D + d] = m / 2.25f;
 }
 
@@ -337,8 +355,9 @@ static hipError_t launch_quant_t(const void *q, const void *k, const void *v, in
                        S, heads, items, g);
     hipLaunchKernelGGL((quant_kmean_kernel<D>), dim3(B * heads * (D / 32)), dim3(256), 0, st, bs,
                        km, S, ntok);
-    hipLaunchKernelGGL((quant_qk_kernel<D, Tin, kPad>), dim3(items, 2), dim3(256), 0, st, qi, ki,
-                       km, q8, qs, k8, ks, S, heads, g);
+    hipLaunchKernelGGL((quant_qk_kernel<D, Tin, kPad>), dim3((items + 3) / 4, 2), dim3(256), 0, st,
+                       qi, ki, km, q8, qs, k8, ks, S, heads, items, g);
+    // v's maxima right before its codes, so that the codes pass finds v in the caches
     hipLaunchKernelGGL((quant_vmax_kernel<D, Tin, kPad>), dim3(B * heads * nchunk), dim3(256), 0,
                        st, vi, part, S, heads, nchunk, g);
     hipLaunchKernelGGL((quant_vscale_kernel<D>), dim3(B * heads), dim3(D), 0, st, part, vs,
