@@ -460,7 +460,14 @@ def main():
     m = measure(torch, nabla, w, (q, k, v), args.steps, args.warmup, topk_ratio=args.topk,
                 quant=args.q8, fold=not args.separate_permutes)
     attn_tflops = m["attn_flops"] / (m["attn_ms"] * 1e-3) / 1e12
-    traffic = read_traffic(Q8_PMC_FILE, Q8_SRC) if args.q8 else read_traffic()
+    # the committed PMC summaries cover the 720p workload with the natural-order calls only
+    pmc_case = w.name == "720p" and m["fold"] and args.topk is None
+    traffic = None
+    if pmc_case:
+        traffic = read_traffic(Q8_PMC_FILE, Q8_SRC) if args.q8 else read_traffic()
+    kname = "sparse_attn_kernel<%d, %s, %s, %s>" % (
+        w.D, "bf16" if w.dtype == "bf16" else "float", str(w.padded).lower(),
+        str(m["fold"]).lower())
     metric = METRIC if args.topk is None else (
         "NABLA path with the top-k estimator (ratio %g): sparse attn fwd effective TFLOP/s + "
         "mask ms at %s shape, 1 MI355X" % (args.topk, w.name))
@@ -495,7 +502,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "sparse_attn_kernel<128, bf16, false, %s>" % str(m["fold"]).lower(),
+                     "kernel": kname,
                      "per_launch": {"flops": m["attn_flops"], "kept_pairs": m["pairs"]}},
     }
     if args.q8:
@@ -503,7 +510,8 @@ def main():
         out["quant_ms"] = round(m["quant_ms"], 4)
         out["roofline"].update({"peak": PEAK_FP8_TFLOPS,
                                 "frac": round(attn_tflops / PEAK_FP8_TFLOPS, 4),
-                                "kernel": "sparse_attn_q8_kernel<128>"})
+                                "kernel": "sparse_attn_q8_kernel<%d, %s>" % (
+                                    w.D, str(w.padded).lower())})
     if not args.no_cpu_baseline and args.topk is None and not args.q8 and not w.padded:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, m["sta_np"], m["g_nb"], m["g_inds"],
