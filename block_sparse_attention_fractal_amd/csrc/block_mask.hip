@@ -313,9 +313,10 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
     constexpr int NWV = 4;
     constexpr bool KST = CPT >= 4 && CPT <= 16;
     constexpr int KCOL = KST ? 64 * CPT : 1;  // float4s of one staged column (>= 256)
+    constexpr int KRND = (KCOL + 255) / 256;   // staging rounds of 256 float4s (KCOL rounded up)
     __shared__ __attribute__((aligned(16))) float qs[NWV][RW][D];
     __shared__ SelectWaveScratch scr[NWV];
-    __shared__ __attribute__((aligned(1024))) float4 kst[2][KCOL];
+    __shared__ __attribute__((aligned(1024))) float4 kst[2][KST ? KRND * 256 : 1];
     const int bh = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * NWV + wv) * RW;
     // with KST every wave takes part in the staging (loads and barriers) of the scores
@@ -394,10 +395,10 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
         if constexpr (KST) {
             const float4 *src = kb + (int64_t)d4 * nb;
 #pragma unroll
-            for (int r = 0; r < KCOL / 256; ++r) {
+            for (int r = 0; r < KRND; ++r) {
                 const int e = r * 256 + (int)threadIdx.x;
                 lds_direct16_sv(src, (uint32_t)(e < nb ? e : nb - 1) * 16u,
-                                kst0 + (uint32_t)(buf * KCOL * 16 + r * 4096));
+                                kst0 + (uint32_t)(buf * KRND * 4096 + r * 4096));
             }
         }
     };
@@ -948,7 +949,11 @@ static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int 
     if (nb <= 128) NABLA_ROWS(2, 8);
     if (nb <= 256) NABLA_ROWS(4, 8);
     if (nb <= 512) NABLA_ROWS(8, 8);
+    // 15 and 30 column groups for rows of 897-960 and 1857-1920 blocks (the 720p and the
+    // long-clip shapes): the next power of two would score one or two groups holding no block
+    if (nb > 896 && nb <= 960) NABLA_ROWS(15, 4);
     if (nb <= 1024) NABLA_ROWS(16, 4);
+    if (nb > 1856 && nb <= 1920) NABLA_ROWS(30, 2);
     if (nb <= 2048) NABLA_ROWS(32, 2);
 #undef NABLA_ROWS
     return launch_select_t<D, 8, 8>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);

@@ -94,30 +94,58 @@ __global__ __launch_bounds__(256) void quant_ksum_kernel(const Tin *__restrict__
     *reinterpret_cast<float4 *>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
-// km[bh][d] = (sequential sum over blocks of bs) / ntok (S unless the layout is padded).  One workgroup per (b, head) and
-// 32 channels: the 256 lanes stage runs of 128 blocks into LDS (coalesced), then 32 lanes
-// add them in block order.
+// km[bh][d] = (sequential sum over blocks of bs) / ntok (S unless the layout is padded).  One
+// workgroup per (b, head) and 8 channels, so that a launch has B * heads * D / 8 workgroups: the
+// 256 lanes stage runs of up to 1024 blocks (32 bytes of each) into LDS with all their loads
+// issued before the first store, then 8 lanes add them in block order, reading the next 8 values
+// while they add the current 8.  The staged run is padded with +0 to a multiple of 8 blocks:
+// the sum starts at +0 and so never is -0, and adding +0 leaves it unchanged.
 template <int D>
 __global__ __launch_bounds__(256) void quant_kmean_kernel(const float *__restrict__ bs,
                                                           float *__restrict__ km, int S,
                                                           int ntok) {
-    constexpr int RUN = 128;
-    __shared__ float stage[RUN][33];
+    constexpr int RUN = 1024, CW = 8, LPL = RUN * 2 / 256;  // float4 loads per lane and run
+    __shared__ float4 stage[RUN][CW / 4];
     const int nb = S / kBlock;
-    const int64_t bh = blockIdx.x / (D / 32);
-    const int d0 = 32 * (blockIdx.x % (D / 32));
+    const int64_t bh = blockIdx.x / (D / CW);
+    const int d0 = CW * (blockIdx.x % (D / CW));
     const int tid = threadIdx.x;
     const float *p = bs + bh * nb * D + d0;
     float acc = 0.0f;
     for (int j0 = 0; j0 < nb; j0 += RUN) {
-        const int n = min(RUN, nb - j0);
+        const int n = min(RUN, nb - j0), n8 = (n + 7) & ~7;
         __syncthreads();
-        for (int e = tid; e < n * 32; e += 256) stage[e >> 5][e & 31] = p[(int64_t)(j0 + (e >> 5)) * D + (e & 31)];
+        float4 x[LPL];
+#pragma unroll
+        for (int u = 0; u < LPL; ++u) {
+            const int e = u * 256 + tid, j = e >> 1;
+            x[u] = j < n ? *reinterpret_cast<const float4 *>(p + (int64_t)(j0 + j) * D + 4 * (e & 1))
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < LPL; ++u) {
+            const int e = u * 256 + tid, j = e >> 1;
+            if (j < n8) stage[j][e & 1] = x[u];
+        }
         __syncthreads();
-        if (tid < 32)
-            for (int j = 0; j < n; ++j) acc += stage[j][tid];
+        if (tid < CW) {
+            const float *col = reinterpret_cast<const float *>(&stage[0][0]) + tid;
+            float cur[8], nxt[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) cur[u] = col[u * CW];
+            for (int j = 8; j < n8; j += 8) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) nxt[u] = col[(j + u) * CW];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc += cur[u];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) cur[u] = nxt[u];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc += cur[u];
+        }
     }
-    if (tid < 32) km[bh * D + d0 + tid] = acc / (float)ntok;  // ntok: the token count
+    if (tid < CW) km[bh * D + d0 + tid] = acc / (float)ntok;  // ntok: the token count
 }
 
 __device__ __forceinline__ uint32_t int8_code(float x, float scale) {
@@ -353,7 +381,7 @@ static hipError_t launch_quant_t(const void *q, const void *k, const void *v, in
     hipLaunchKernelGGL((quant_ksum_kernel<D, Tin, kPad>),
                        dim3((items + kBlocksPerWg - 1) / kBlocksPerWg), dim3(256), 0, st, ki, bs,
                        S, heads, items, g);
-    hipLaunchKernelGGL((quant_kmean_kernel<D>), dim3(B * heads * (D / 32)), dim3(256), 0, st, bs,
+    hipLaunchKernelGGL((quant_kmean_kernel<D>), dim3(B * heads * (D / 8)), dim3(256), 0, st, bs,
                        km, S, ntok);
     hipLaunchKernelGGL((quant_qk_kernel<D, Tin, kPad>), dim3((items + 3) / 4, 2), dim3(256), 0, st,
                        qi, ki, km, q8, qs, k8, ks, S, heads, items, g);
