@@ -379,12 +379,28 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
         }
     __builtin_amdgcn_wave_barrier();
 
-    // ---- scores (before the division by sqrt(D))
-    float acc[RW][CPT];
+    // ---- scores (before the division by sqrt(D)) on the fp32 matrix cores.
+    // v_mfma_f32_4x4x1_16b_f32 runs 16 blocks b = lane / 4 of D[4][4] += A[4][1] B[1][4]:
+    // lane 4b + i supplies A_b[i], lane 4b + j supplies B_b[j], and register r of lane 4b + j
+    // receives D_b[r][j], each step one fused multiply-add (measured on gfx950: bit-identical
+    // to fmaf chained in step order, subnormals included).  With A = the q mean of row
+    // (lane & 3) at dimension d and B = the k mean of block 64c + lane at d, for d ascending,
+    // register r of chain (q, c) in lane l is the fp32 fma chain of row 4q + r against block
+    // 64c + l: the score of the readings, at twice the unpacked vector fma rate and off the
+    // vector ALU.  Waves of RW = 2 rows (rows of more than 1024 blocks) would leave half of
+    // each quad unused at twice the accumulator registers; they keep the vector fma chain.
+    constexpr bool MF = RW % 4 == 0;
+    constexpr int NQ = MF ? RW / 4 : 1;
+    f32x4 acc[NQ][MF ? CPT : 1];
+    float vacc[MF ? 1 : RW][MF ? 1 : CPT];
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
+    for (int qd = 0; qd < NQ; ++qd)
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) acc[r][c] = 0.0f;
+        for (int c = 0; c < (MF ? CPT : 1); ++c) acc[qd][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < (MF ? 1 : RW); ++r)
+#pragma unroll
+        for (int c = 0; c < (MF ? 1 : CPT); ++c) vacc[r][c] = 0.0f;
     const float4 *kb = reinterpret_cast<const float4 *>(ka) + (int64_t)bh * (D / 4) * nb;
     // column d4 of the k means into buffer `buf`: float4 e = 256 r + tid lands at kst[buf][e]
     // (a wave's 64 lanes fill one contiguous KiB); lanes past the last block load the last
@@ -419,15 +435,35 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
                 k4[c] = j < nb ? kb[(int64_t)d4 * nb + j] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
+        if constexpr (MF) {
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const float4 q4 = *reinterpret_cast<const float4 *>(&qs[wv][r][4 * d4]);
+            for (int qd = 0; qd < NQ; ++qd) {
+                const float4 q4 =
+                    *reinterpret_cast<const float4 *>(&qs[wv][4 * qd + (lane & 3)][4 * d4]);
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                acc[r][c] = __builtin_fmaf(q4.x, k4[c].x, acc[r][c]);
-                acc[r][c] = __builtin_fmaf(q4.y, k4[c].y, acc[r][c]);
-                acc[r][c] = __builtin_fmaf(q4.z, k4[c].z, acc[r][c]);
-                acc[r][c] = __builtin_fmaf(q4.w, k4[c].w, acc[r][c]);
+                for (int c = 0; c < CPT; ++c)
+                    acc[qd][c] = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.x, k4[c].x, acc[qd][c], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c)
+                    acc[qd][c] = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.y, k4[c].y, acc[qd][c], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c)
+                    acc[qd][c] = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.z, k4[c].z, acc[qd][c], 0, 0, 0);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c)
+                    acc[qd][c] = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.w, k4[c].w, acc[qd][c], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                const float4 q4 = *reinterpret_cast<const float4 *>(&qs[wv][r][4 * d4]);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    vacc[r][c] = __builtin_fmaf(q4.x, k4[c].x, vacc[r][c]);
+                    vacc[r][c] = __builtin_fmaf(q4.y, k4[c].y, vacc[r][c]);
+                    vacc[r][c] = __builtin_fmaf(q4.z, k4[c].z, vacc[r][c]);
+                    vacc[r][c] = __builtin_fmaf(q4.w, k4[c].w, vacc[r][c]);
+                }
             }
         }
     }
@@ -447,7 +483,12 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
             float a = 0.0f;
 #pragma unroll
             for (int rr = 0; rr < RW; ++rr)
-                if (rr == r) a = acc[rr][c];
+                if (rr == r) {
+                    if constexpr (MF)
+                        a = acc[rr >> 2][c][rr & 3];
+                    else
+                        a = vacc[rr][c];
+                }
             s[c] = (TOPK ? a : a / sqrt_d) + 0.0f;
             valid[c] = 64 * c + lane < nb;
             if (valid[c]) {
