@@ -102,36 +102,62 @@ struct AttnShared {
 // a few heads, which the memory-side cache holds (measured at 720p: 3.7 % less time
 // than one longest-first order over all heads; one head per phase packs badly).
 
-// grid = ngroups, 256 lanes: cost[g] = |union of the lists of group g|; resets the counter.
+// grid = ceil(ngroups / 4), 256 lanes: wave w of workgroup x takes group 4x + w and ORs its
+// members' lists into a bitmap of its own in LDS (no barrier); cost[g] = |union of the lists of
+// group g|.  Workgroup 0 resets the counter.
 __global__ __launch_bounds__(256) void attn_plan_cost_kernel(
     const int32_t *__restrict__ kv_nb, const int32_t *__restrict__ kv_inds, int nb, int Tt,
-    int Ht, int Wt, int groups_per_bh, int32_t *__restrict__ cost, int32_t *__restrict__ counter) {
-    __shared__ uint64_t bits[kMaxWords];
-    __shared__ int total;
-    const int g = blockIdx.x, tid = threadIdx.x;
+    int Ht, int Wt, int groups_per_bh, int ngroups, int32_t *__restrict__ cost,
+    int32_t *__restrict__ counter) {
+    __shared__ uint64_t bits[4][kMaxWords];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int g = blockIdx.x * 4 + w;
+    if (blockIdx.x == 0 && threadIdx.x == 0) *counter = 0;
+    if (g >= ngroups) return;  // wave-uniform; nothing below synchronizes waves
     const int bh = g / groups_per_bh, gi = g % groups_per_bh;
-    const int nwords = (nb + 63) >> 6;
-    if (g == 0 && tid == 0) *counter = 0;
-    for (int e = tid; e < kMaxWords; e += 256) bits[e] = 0ull;
-    if (tid == 0) total = 0;
-    __syncthreads();
+    uint64_t *bw = bits[w];
+#pragma unroll
+    for (int e = lane; e < kMaxWords; e += 64) bw[e] = 0ull;
+    __builtin_amdgcn_wave_barrier();
+    int n[kGroup];
+    const int32_t *list[kGroup];
+#pragma unroll
     for (int s = 0; s < kGroup; ++s) {
         const int m = group_member(gi, s, Tt, Ht, Wt, nb);
-        if (m < 0) continue;
-        const int64_t row = (int64_t)bh * nb + m;
-        const int n = clamp_count(kv_nb[row], nb);
-        const int32_t *list = kv_inds + row * nb;
-        for (int e = tid; e < n; e += 256) {
-            const int j = clamp_block(list[e], nb);
-            atomicOr((unsigned long long *)&bits[j >> 6], 1ull << (j & 63));
-        }
+        const int64_t row = (int64_t)bh * nb + (m < 0 ? 0 : m);
+        n[s] = m < 0 ? 0 : clamp_count(kv_nb[row], nb);
+        list[s] = kv_inds + row * nb;
     }
-    __syncthreads();
+    int nmax = 0;
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) nmax = max(nmax, n[s]);
+    // 256 entries of every member per pass: all their loads issued before the first atomic
+    constexpr int PL = 4;  // loads per lane and member
+    for (int e0 = 0; e0 < nmax; e0 += 64 * PL) {
+        int jj[kGroup][PL];
+#pragma unroll
+        for (int s = 0; s < kGroup; ++s)
+#pragma unroll
+            for (int u = 0; u < PL; ++u) {
+                const int e = e0 + 64 * u + lane;
+                jj[s][u] = e < n[s] ? list[s][e] : -1;
+            }
+#pragma unroll
+        for (int s = 0; s < kGroup; ++s)
+#pragma unroll
+            for (int u = 0; u < PL; ++u)
+                if (e0 + 64 * u + lane < n[s]) {
+                    const int j = clamp_block(jj[s][u], nb);
+                    atomicOr((unsigned long long *)&bw[j >> 6], 1ull << (j & 63));
+                }
+    }
+    __builtin_amdgcn_wave_barrier();
     int cnt = 0;
-    for (int wd = tid; wd < nwords; wd += 256) cnt += __popcll(bits[wd]);
-    atomicAdd(&total, cnt);
-    __syncthreads();
-    if (tid == 0) cost[g] = total;
+#pragma unroll
+    for (int wd = lane; wd < kMaxWords; wd += 64) cnt += __popcll(bw[wd]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if (lane == 0) cost[g] = cnt;
 }
 
 // One workgroup of 1024 lanes per phase.  Phase p holds the groups g of [p * per_phase,
@@ -618,8 +644,9 @@ AttnSchedule launch_attn_plan(const int32_t *kv_nb, const int32_t *kv_inds, int 
     sc.counter = reinterpret_cast<int32_t *>(wsb);
     int32_t *cost = reinterpret_cast<int32_t *>(wsb + 256);
     sc.order = reinterpret_cast<int32_t *>(wsb + 256 + round256((size_t)sc.ngroups * 4));
-    hipLaunchKernelGGL(attn_plan_cost_kernel, dim3(sc.ngroups), dim3(256), 0, stream, kv_nb,
-                       kv_inds, nb, Tt, Ht, Wt, sc.groups_per_bh, cost, sc.counter);
+    hipLaunchKernelGGL(attn_plan_cost_kernel, dim3((sc.ngroups + 3) / 4), dim3(256), 0, stream,
+                       kv_nb, kv_inds, nb, Tt, Ht, Wt, sc.groups_per_bh, sc.ngroups, cost,
+                       sc.counter);
     // Heads per phase: enough groups that the phase, and above all the last one, keeps
     // every CU busy with room for longest-first packing (three groups per resident
     // workgroup), and at least two heads.
