@@ -24,6 +24,8 @@
 #include "nabla_device.h"
 #include "nabla_launch.h"
 
+#include <type_traits>
+
 namespace nabla {
 
 constexpr int kQuantChunk = 1024;  // tokens per partial channel maximum of v
@@ -314,7 +316,12 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const Tin *__restrict__ v,
                                                       uint8_t *__restrict__ v8, int S,
                                                       int heads, QuantPad g) {
     constexpr int CH = D / 8;
-    __shared__ float tile[kBlock][D + 1];
+    // bf16 inputs stay bf16 in LDS (widened exactly when read): half the LDS, twice the
+    // workgroups per CU; rows padded to a multiple of 16 bytes.  fp32 rows padded by one.
+    constexpr bool kB16 = sizeof(Tin) == 2;
+    typedef typename std::conditional<kB16, bf16, float>::type TT;
+    constexpr int PITCH = kB16 ? D + 8 : D + 1;
+    __shared__ __attribute__((aligned(16))) TT tile[kBlock][PITCH];
     const int nb = S / kBlock;
     const int64_t item = blockIdx.x;
     const int j = (int)(item % nb), bh = (int)(item / nb);
@@ -326,13 +333,21 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const Tin *__restrict__ v,
 #pragma unroll
     for (int r = 0; r < kBlock * CH / 256; ++r) {
         const int e = r * 256 + tid, row = e / CH, c = e % CH;
-        float x[8];
-        load8_f32(src + block_row_token(j, row, g.ng) * tok + 8 * c, x);
-        if (kPad && !qrow_ok(row, vr, vc))  // padding: code 0
+        const Tin *p = src + block_row_token(j, row, g.ng) * tok + 8 * c;
+        const bool pad = kPad && !qrow_ok(row, vr, vc);  // padding: code 0
+        if constexpr (kB16) {
+            bf16x8 x = *reinterpret_cast<const bf16x8 *>(p);
+            if (pad) x = bf16x8{};
+            *reinterpret_cast<bf16x8 *>(&tile[row][8 * c]) = x;
+        } else {
+            float x[8];
+            load8_f32(p, x);
+            if (pad)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+                for (int i = 0; i < 8; ++i) x[i] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tile[row][8 * c + i] = x[i];
+            for (int i = 0; i < 8; ++i) tile[row][8 * c + i] = x[i];
+        }
     }
     __syncthreads();
     uint8_t *dst = v8 + item * (kBlock * D);
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const Tin *__restrict__ v,
             float f[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                f[i] = sc == 0.0f ? 0.0f : tile[16 * c + 4 * u + i][d] / sc;
+                f[i] = sc == 0.0f ? 0.0f : (float)tile[16 * c + 4 * u + i][d] / sc;
             int pk = 0;
             pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], pk, false);
             pk = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pk, true);
