@@ -7,7 +7,9 @@ for every run; both sides compute the softmax with one exp method and exact
 fixed-point sums, so band rows must match as well.  The attention output (bf16
 MFMA, fp32 accumulation) must stay within max-abs 2e-2 and mean-abs 2e-3 of
 the fp64 oracle.  The lists are compared on every row of every workload (tiny,
-small, 720p, the long clip and all fifteen runs of the 720p sparsity sweep);
+small, 720p, the long clip and all fifteen runs of the 720p sparsity sweep) and
+of row lengths that hit each column-group count of the selection kernel with a
+partial last group;
 the attention in full on tiny and small and on sampled query blocks (first and
 last, fewest and most kept blocks, random) on the larger shapes.
 """
@@ -184,6 +186,39 @@ def test_block_mask_uniform_ties(orc, dev):
 
 
 # ------------------------------------------------------------------ attention
+@pytest.mark.parametrize("nb,D,dtype,B", [
+    (1, 128, "bf16", 1),      # one column group, one block
+    (65, 128, "bf16", 2),     # 2 groups, the second holds one block; batch offset
+    (300, 128, "bf16", 1),    # 8 groups, eight rows per wave (two row quads on the matrix cores)
+    (897, 128, "bf16", 1),    # 15 groups, the last holds one block
+    (1000, 64, "bf16", 1),    # 16 groups, D = 64 (q pooled by the pooling pass)
+    (1857, 128, "bf16", 1),   # 30 groups, two rows per wave (vector scores)
+    (1921, 128, "fp32", 1),   # 32 groups, fp32 inputs
+])
+def test_block_mask_row_lengths(orc, dev, nb, D, dtype, B):
+    """Rows of every column-group count of the selection kernel, each with a partial last
+    group, against the oracle estimator on every row (fractal-order call, band STA)."""
+    h, S = 2, nb * 64
+    rng = np.random.default_rng(1000 + nb)
+    # a shared direction per head plus noise: scores spread, so the cut moves between rows
+    base = rng.standard_normal((1, 1, h, D)).astype(np.float32)
+    q = (rng.standard_normal((B, S, h, D)) + 2.0 * base).astype(np.float32)
+    k = (rng.standard_normal((B, S, h, D)) + 1.5 * base * rng.standard_normal((B, S, h, 1))).astype(np.float32)
+    if dtype == "bf16":
+        q, k = synth.round_bf16(q), synth.round_bf16(k)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    gq, gk = (torch.from_numpy(a).to(tdt).to(dev) for a in (q, k))
+    ii = np.arange(nb)
+    sta = (np.abs(ii[:, None] - ii[None, :]) <= 2).astype(np.uint8)
+    for thr in (0.9, 0.5):
+        say("[mask-rows] nb", nb, "D", D, dtype, "B", B, "thr", thr)
+        kv_nb, kv_inds = nabla.nabla_block_mask(gq, gk, torch.from_numpy(sta).to(dev), thr)
+        o = orc.block_mask(q, k, sta, thr)
+        band = orc.band_rows(o["diag"], thr)
+        compare_lists(kv_nb.cpu().numpy(), kv_inds.cpu().numpy(), o["kv_nb"], o["kv_inds"], band,
+                      "rows nb=%d D=%d %s thr=%g" % (nb, D, dtype, thr))
+
+
 def check_attention(got, want, label):
     err = np.abs(got.astype(np.float64) - want)
     say("[%s] max-abs %.3e mean-abs %.3e over %d values" % (label, err.max(), err.mean(), err.size))
