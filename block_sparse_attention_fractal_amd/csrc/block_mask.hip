@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
                                                           const bf16 *__restrict__ q, int S,
                                                           int heads, NatGrid ng) {
     constexpr int NWV = 4;
-    constexpr bool KST = CPT >= 4 && CPT <= 16;
+    constexpr bool KST = CPT >= 4;
     constexpr int KCOL = KST ? 64 * CPT : 1;  // float4s of one staged column (>= 256)
     constexpr int KRND = (KCOL + 255) / 256;   // staging rounds of 256 float4s (KCOL rounded up)
     __shared__ __attribute__((aligned(16))) float qs[NWV][RW][D];
@@ -974,7 +974,7 @@ __global__ __launch_bounds__(256) void smooth_k_kernel(float *__restrict__ ka, i
 
 // Rows per wave of the selection for rows of nb blocks (as launch_select_d chooses), and
 // whether that configuration can pool q itself (16-byte chunks per lane and row).
-static int select_rows_per_wave(int nb) { return nb <= 512 ? 8 : (nb <= 1024 ? 4 : 2); }
+static int select_rows_per_wave(int nb) { return nb <= 512 ? 8 : 4; }
 static bool select_pools_q(int D, int nb) {
     return nb <= 2048 && (D * select_rows_per_wave(nb) / 64) % 8 == 0;
 }
@@ -994,8 +994,8 @@ static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int 
     // long-clip shapes): the next power of two would score one or two groups holding no block
     if (nb > 896 && nb <= 960) NABLA_ROWS(15, 4);
     if (nb <= 1024) NABLA_ROWS(16, 4);
-    if (nb > 1856 && nb <= 1920) NABLA_ROWS(30, 2);
-    if (nb <= 2048) NABLA_ROWS(32, 2);
+    if (nb > 1856 && nb <= 1920) NABLA_ROWS(30, 4);
+    if (nb <= 2048) NABLA_ROWS(32, 4);
 #undef NABLA_ROWS
     return launch_select_t<D, 8, 8>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
 }
