@@ -301,31 +301,56 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
 // * 2^-6): 64 / RW lanes per block, each summing D * RW / 64 dimensions.  The q reads then
 // overlap the selection work of the other resident waves, and the pooling pass reads k only.
 // S, heads, ng: q's layout (as pool_kernel).
-template <int D, int CPT, int RW, bool TOPK = false>
-__global__ __launch_bounds__(256) void select_rows_kernel(const float *__restrict__ qa,
-                                                          const float *__restrict__ ka, int nb,
-                                                          const uint8_t *__restrict__ sta,
-                                                          float sqrt_d, int64_t cut,
-                                                          int32_t *__restrict__ kv_nb,
-                                                          int32_t *__restrict__ kv_inds,
-                                                          const bf16 *__restrict__ q, int S,
-                                                          int heads, NatGrid ng) {
+template <int D, int CPT, int RW, bool TOPK, int PH>
+__device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
+                                                 const float *__restrict__ ka, int nb,
+                                                 const uint8_t *__restrict__ sta, float sqrt_d,
+                                                 int64_t cut, int32_t *__restrict__ kv_nb,
+                                                 int32_t *__restrict__ kv_inds,
+                                                 const bf16 *__restrict__ q, int S, int heads,
+                                                 NatGrid ng, float *__restrict__ sbuf) {
     constexpr int NWV = 4;
-    constexpr bool KST = CPT >= 4;
+    constexpr bool SC = PH != 2;  // this launch computes the scores
+    constexpr bool SL = PH != 1;  // this launch selects
+    constexpr bool KST = SC && CPT >= 4;
     constexpr int KCOL = KST ? 64 * CPT : 1;  // float4s of one staged column (>= 256)
     constexpr int KRND = (KCOL + 255) / 256;   // staging rounds of 256 float4s (KCOL rounded up)
-    __shared__ __attribute__((aligned(16))) float qs[NWV][RW][D];
-    __shared__ SelectWaveScratch scr[NWV];
+    __shared__ __attribute__((aligned(16))) float qs[NWV][SC ? RW : 1][SC ? D : 4];
+    __shared__ SelectWaveScratch scr[SL ? NWV : 1];
     __shared__ __attribute__((aligned(1024))) float4 kst[2][KST ? KRND * 256 : 1];
     const int bh = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * NWV + wv) * RW;
     // with KST every wave takes part in the staging (loads and barriers) of the scores
     if (!KST && row0 >= nb) return;
-    SelectWaveScratch &W = scr[wv];
+    SelectWaveScratch &W = scr[SL ? wv : 0];
     const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 
     constexpr int LPB = 64 / RW, DPL = D / LPB;  // lanes per query block, dims per lane
     constexpr int NCH = DPL / 8;                  // 16-byte chunks per lane and row
+    // ---- scores (before the division by sqrt(D)) on the fp32 matrix cores.
+    // v_mfma_f32_4x4x1_16b_f32 runs 16 blocks b = lane / 4 of D[4][4] += A[4][1] B[1][4]:
+    // lane 4b + i supplies A_b[i], lane 4b + j supplies B_b[j], and register r of lane 4b + j
+    // receives D_b[r][j], each step one fused multiply-add (measured on gfx950: bit-identical
+    // to fmaf chained in step order, subnormals included).  With A = the q mean of row
+    // (lane & 3) at dimension d and B = the k mean of block 64c + lane at d, for d ascending,
+    // register r of chain (q, c) in lane l is the fp32 fma chain of row 4q + r against block
+    // 64c + l: the score of the readings, at twice the unpacked vector fma rate and off the
+    // vector ALU.  Waves of RW = 2 rows (the top-k variant's rows of more than 1024 blocks)
+    // would leave half of each quad unused at twice the accumulator registers; they keep the
+    // vector fma chain.
+    constexpr bool MF = RW % 4 == 0;
+    constexpr int NQ = MF ? RW / 4 : 1;
+    f32x4 acc[NQ][MF ? CPT : 1];
+    float vacc[MF ? 1 : RW][MF ? 1 : CPT];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd)
+#pragma unroll
+        for (int c = 0; c < (MF ? CPT : 1); ++c) acc[qd][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < (MF ? 1 : RW); ++r)
+#pragma unroll
+        for (int c = 0; c < (MF ? 1 : CPT); ++c) vacc[r][c] = 0.0f;
+    if constexpr (SC) {  // ---- q means, then the scores
     bool pooled = false;
     if constexpr (DPL % 8 == 0) {
         if (q != nullptr) {
@@ -379,28 +404,6 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
         }
     __builtin_amdgcn_wave_barrier();
 
-    // ---- scores (before the division by sqrt(D)) on the fp32 matrix cores.
-    // v_mfma_f32_4x4x1_16b_f32 runs 16 blocks b = lane / 4 of D[4][4] += A[4][1] B[1][4]:
-    // lane 4b + i supplies A_b[i], lane 4b + j supplies B_b[j], and register r of lane 4b + j
-    // receives D_b[r][j], each step one fused multiply-add (measured on gfx950: bit-identical
-    // to fmaf chained in step order, subnormals included).  With A = the q mean of row
-    // (lane & 3) at dimension d and B = the k mean of block 64c + lane at d, for d ascending,
-    // register r of chain (q, c) in lane l is the fp32 fma chain of row 4q + r against block
-    // 64c + l: the score of the readings, at twice the unpacked vector fma rate and off the
-    // vector ALU.  Waves of RW = 2 rows (rows of more than 1024 blocks) would leave half of
-    // each quad unused at twice the accumulator registers; they keep the vector fma chain.
-    constexpr bool MF = RW % 4 == 0;
-    constexpr int NQ = MF ? RW / 4 : 1;
-    f32x4 acc[NQ][MF ? CPT : 1];
-    float vacc[MF ? 1 : RW][MF ? 1 : CPT];
-#pragma unroll
-    for (int qd = 0; qd < NQ; ++qd)
-#pragma unroll
-        for (int c = 0; c < (MF ? CPT : 1); ++c) acc[qd][c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int r = 0; r < (MF ? 1 : RW); ++r)
-#pragma unroll
-        for (int c = 0; c < (MF ? 1 : CPT); ++c) vacc[r][c] = 0.0f;
     const float4 *kb = reinterpret_cast<const float4 *>(ka) + (int64_t)bh * (D / 4) * nb;
     // column d4 of the k means into buffer `buf`: float4 e = 256 r + tid lands at kst[buf][e]
     // (a wave's 64 lanes fill one contiguous KiB); lanes past the last block load the last
@@ -467,6 +470,31 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
             }
         }
     }
+    }  // SC
+    if constexpr (PH == 1) {
+        // scores launch: the rows' scores (divided by sqrt(D), -0 as +0) to sbuf [bh][nb][nb]
+        if (row0 >= nb) return;
+#pragma unroll 1
+        for (int r = 0; r < RW; ++r) {
+            const int i = row0 + r;
+            if (i >= nb) break;  // wave-uniform
+            float *srow = sbuf + ((int64_t)bh * nb + i) * nb;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                float a = 0.0f;
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr)
+                    if (rr == r) {
+                        if constexpr (MF)
+                            a = acc[rr >> 2][c][rr & 3];
+                        else
+                            a = vacc[rr][c];
+                    }
+                if (64 * c + lane < nb) srow[64 * c + lane] = (TOPK ? a : a / sqrt_d) + 0.0f;
+            }
+        }
+        return;
+    }
     if (KST && row0 >= nb) return;  // no barrier below: waves are independent
 
     // ---- per row: softmax on the 2^-48 grid, cut key, STA union, compaction
@@ -480,17 +508,21 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
         float smax = -INFINITY, smin = INFINITY;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            float a = 0.0f;
-#pragma unroll
-            for (int rr = 0; rr < RW; ++rr)
-                if (rr == r) {
-                    if constexpr (MF)
-                        a = acc[rr >> 2][c][rr & 3];
-                    else
-                        a = vacc[rr][c];
-                }
-            s[c] = (TOPK ? a : a / sqrt_d) + 0.0f;
             valid[c] = 64 * c + lane < nb;
+            if constexpr (PH == 2) {
+                s[c] = valid[c] ? sbuf[row * nb + 64 * c + lane] : 0.0f;
+            } else {
+                float a = 0.0f;
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr)
+                    if (rr == r) {
+                        if constexpr (MF)
+                            a = acc[rr >> 2][c][rr & 3];
+                        else
+                            a = vacc[rr][c];
+                    }
+                s[c] = (TOPK ? a : a / sqrt_d) + 0.0f;
+            }
             if (valid[c]) {
                 smax = fmaxf(smax, s[c]);
                 smin = fminf(smin, s[c]);
@@ -686,6 +718,25 @@ __global__ __launch_bounds__(256) void select_rows_kernel(const float *__restric
         __builtin_amdgcn_wave_barrier();
     }
 }
+
+#define NABLA_SELECT_ARGS                                                                      \
+    const float *__restrict__ qa, const float *__restrict__ ka, int nb,                        \
+        const uint8_t *__restrict__ sta, float sqrt_d, int64_t cut,                            \
+        int32_t *__restrict__ kv_nb, int32_t *__restrict__ kv_inds, const bf16 *__restrict__ q, \
+        int S, int heads, NatGrid ng, float *__restrict__ sbuf
+template <int D, int CPT, int RW, bool TOPK = false, int PH = 0>
+__global__ __launch_bounds__(256) void select_rows_kernel(NABLA_SELECT_ARGS) {
+    select_rows_body<D, CPT, RW, TOPK, PH>(qa, ka, nb, sta, sqrt_d, cut, kv_nb, kv_inds, q, S,
+                                           heads, ng, sbuf);
+}
+// The selection launch of the two-launch path for rows of up to 16 column groups, held to
+// 128 registers so that four waves per SIMD are resident.
+template <int D, int CPT>
+__global__ __launch_bounds__(256, 4) void select_rows_w4_kernel(NABLA_SELECT_ARGS) {
+    select_rows_body<D, CPT, 1, false, 2>(qa, ka, nb, sta, sqrt_d, cut, kv_nb, kv_inds, q, S,
+                                          heads, ng, sbuf);
+}
+#undef NABLA_SELECT_ARGS
 
 // ---------------------------------------------------------------- select (long rows)
 // Rows of more than 2048 blocks.  grid (ceil(nb / R), B*heads); 512 lanes; lane t owns
@@ -909,14 +960,40 @@ struct QSource {
     NatGrid ng;
 };
 
-template <int D, int CPT, int RW, bool TOPK = false>
+template <int D, int CPT, int RW, bool TOPK = false, int PH = 0>
 static hipError_t launch_rows_t(const float *qa, const float *ka, int BH, int nb,
                                 const uint8_t *sta, float sqrt_d, int64_t cut, int32_t *kv_nb,
-                                int32_t *kv_inds, hipStream_t stream, QSource qsrc = {}) {
+                                int32_t *kv_inds, hipStream_t stream, QSource qsrc = {},
+                                float *sbuf = nullptr) {
     dim3 grid((nb + 4 * RW - 1) / (4 * RW), BH);
-    hipLaunchKernelGGL((select_rows_kernel<D, CPT, RW, TOPK>), grid, dim3(256), 0, stream, qa, ka,
-                       nb, sta, sqrt_d, cut, kv_nb, kv_inds, qsrc.q, qsrc.S, qsrc.heads, qsrc.ng);
+    hipLaunchKernelGGL((select_rows_kernel<D, CPT, RW, TOPK, PH>), grid, dim3(256), 0, stream, qa,
+                       ka, nb, sta, sqrt_d, cut, kv_nb, kv_inds, qsrc.q, qsrc.S, qsrc.heads,
+                       qsrc.ng, sbuf);
     return hipGetLastError();
+}
+
+// Rows of 513-2048 blocks in two launches through the score buffer sbuf [BH][nb][nb]: the
+// scores launch (q means, staged k means, matrix-core scores) holds the score accumulators
+// and the staged columns, which leave room for two waves per SIMD; the selection launch
+// reads one row per wave and, without them, keeps four waves per SIMD resident to hide the
+// latency of its reductions, LDS histograms and ballots.
+template <int D, int CPT, int RW>
+static hipError_t launch_rows_split_t(const float *qa, const float *ka, int BH, int nb,
+                                      const uint8_t *sta, float sqrt_d, int64_t cut,
+                                      int32_t *kv_nb, int32_t *kv_inds, hipStream_t stream,
+                                      QSource qsrc, float *sbuf) {
+    hipError_t e = launch_rows_t<D, CPT, RW, false, 1>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb,
+                                                      kv_inds, stream, qsrc, sbuf);
+    if (e != hipSuccess) return e;
+    if constexpr (CPT <= 16) {
+        hipLaunchKernelGGL((select_rows_w4_kernel<D, CPT>), dim3((nb + 3) / 4, BH), dim3(256), 0,
+                           stream, qa, ka, nb, sta, sqrt_d, cut, kv_nb, kv_inds, nullptr, 0, 0,
+                           NatGrid{}, sbuf);
+        return hipGetLastError();
+    } else {
+        return launch_rows_t<D, CPT, 1, false, 2>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb,
+                                                  kv_inds, stream, QSource{}, sbuf);
+    }
 }
 
 // top-k variant: rows of up to 2048 blocks (the caller checks)
@@ -982,10 +1059,14 @@ static bool select_pools_q(int D, int nb) {
 template <int D>
 static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int nb,
                                   const uint8_t *sta, float sqrt_d, int64_t cut, int32_t *kv_nb,
-                                  int32_t *kv_inds, hipStream_t stream, QSource qsrc = {}) {
-#define NABLA_ROWS(CPT, RW) \
-    return launch_rows_t<D, CPT, RW>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream, \
-                                     qsrc)
+                                  int32_t *kv_inds, hipStream_t stream, QSource qsrc,
+                                  float *sbuf) {
+#define NABLA_ROWS(CPT, RW)                                                                   \
+    return sbuf != nullptr                                                                    \
+               ? launch_rows_split_t<D, CPT, RW>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb,     \
+                                                 kv_inds, stream, qsrc, sbuf)                 \
+               : launch_rows_t<D, CPT, RW>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, \
+                                           stream, qsrc)
     if (nb <= 64) NABLA_ROWS(1, 8);
     if (nb <= 128) NABLA_ROWS(2, 8);
     if (nb <= 256) NABLA_ROWS(4, 8);
@@ -1031,7 +1112,7 @@ hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, in
 hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, int S,
                              int heads, int D, int H, int W, bool natural, const uint8_t *sta,
                              int64_t cut_fixed, float sqrt_d, int32_t *kv_nb, int32_t *kv_inds,
-                             float *qa, float *ka, hipStream_t stream) {
+                             float *qa, float *ka, float *sbuf, hipStream_t stream) {
     const int nb = S / kBlock;
     dim3 pgrid(nb, B);
     // bf16 whole blocks: the selection kernel pools q itself, the pooling pass only k
@@ -1051,11 +1132,12 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
     const int BH = B * heads;
     QSource qsrc = {};
     if (qfused) qsrc = QSource{(const bf16 *)q, S, heads, ng};
+    if (!mask_scores_split(nb)) sbuf = nullptr;
     if (D == 64)
         return launch_select_d<64>(qa, ka, BH, nb, sta, sqrt_d, cut_fixed, kv_nb, kv_inds, stream,
-                                   qsrc);
+                                   qsrc, sbuf);
     return launch_select_d<128>(qa, ka, BH, nb, sta, sqrt_d, cut_fixed, kv_nb, kv_inds, stream,
-                                qsrc);
+                                qsrc, sbuf);
 }
 
 }  // namespace nabla

@@ -84,7 +84,11 @@ nabla_status nabla_sta_mask(uint8_t *sta, int Tt, int Ht, int Wt, int win_t, int
 
 size_t nabla_block_mask_workspace(int B, int S, int heads, int head_dim) {
     if (!sizes_ok(B, S, heads, head_dim) || S % kBlock) return 0;
-    return 2ull * (size_t)B * heads * (size_t)(S / kBlock) * head_dim * sizeof(float);
+    const size_t nb = (size_t)(S / kBlock);
+    const size_t pooled = 2ull * (size_t)B * heads * nb * head_dim * sizeof(float);
+    const size_t scores =
+        nabla::mask_scores_split((int)nb) ? (size_t)B * heads * nb * nb * sizeof(float) : 0;
+    return pooled + scores;
 }
 
 }  // extern "C"
@@ -126,10 +130,10 @@ nabla_status estimate(const void *q, const void *k, nabla_dtype dtype, int B, in
     const float cut32 = (float)(1.0 - thr);
     const int64_t cut_fixed = (int64_t)ceil(ldexp((double)cut32, 48));
     const float sqrt_d = (float)sqrt((double)head_dim);
+    float *sbuf = ka + (size_t)B * heads * nb * head_dim;  // the score buffer, if any
     return from_hip(nabla::launch_block_mask(q, k, dtype == NABLA_BF16, B, S, heads, head_dim,
                                              H, W, natural, sta, cut_fixed, sqrt_d, kv_nb,
-                                             kv_inds, qa,
-                                             ka, as_stream(stream)));
+                                             kv_inds, qa, ka, sbuf, as_stream(stream)));
 }
 
 // S of the padded fractal layout of a T x H x W grid, or -1 when the sizes are invalid.

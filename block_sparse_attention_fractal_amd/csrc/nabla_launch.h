@@ -24,7 +24,10 @@ hipError_t launch_sta_mask(uint8_t *sta, int Tt, int Ht, int Wt, int win_t, int 
 hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, int S,
                              int heads, int D, int H, int W, bool natural, const uint8_t *sta,
                              int64_t cut_fixed, float sqrt_d, int32_t *kv_nb, int32_t *kv_inds,
-                             float *qa, float *ka, hipStream_t stream);
+                             float *qa, float *ka, float *sbuf, hipStream_t stream);
+// Rows whose selection runs from a score buffer of B * heads * nb * nb floats in the
+// workspace (scores and selection in two launches): 513 to 2048 blocks.
+inline bool mask_scores_split(int nb) { return nb > 512 && nb <= 2048; }
 
 // The top-k variant: pooled blocks, smooth-k, the topk largest scores per row (k <= nb,
 // nb <= 2048), STA union.  H, W as for launch_block_mask.

@@ -94,8 +94,10 @@ nabla_status nabla_fractal_permute(const void *x, void *y, nabla_dtype dtype, in
 nabla_status nabla_sta_mask(uint8_t *sta, int Tt, int Ht, int Wt, int win_t, int win_h,
                             int win_w, void *stream);
 
-/* Bytes of workspace nabla_block_mask needs (pooled Q and K in fp32):
- * 2 * B * heads * (S/64) * head_dim * 4.  0 if the sizes are invalid. */
+/* Bytes of workspace nabla_block_mask needs: pooled Q and K in fp32,
+ * 2 * B * heads * (S/64) * head_dim * 4, and for rows of 513 to 2048 blocks the block scores
+ * (B * heads * (S/64)^2 * 4; the selection then runs as a second launch).  0 if the sizes are
+ * invalid. */
 size_t nabla_block_mask_workspace(int B, int S, int heads, int head_dim);
 
 /*

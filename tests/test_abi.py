@@ -61,7 +61,10 @@ def test_version_and_status_strings(L):
 
 
 def test_workspace_size(L):
-    assert L.nabla_block_mask_workspace(1, 61440, 16, 128) == 2 * 16 * 960 * 128 * 4
+    # pooled q and k; rows of 513-2048 blocks add the block scores
+    assert L.nabla_block_mask_workspace(1, 61440, 16, 128) == 2 * 16 * 960 * 128 * 4 + 16 * 960 * 960 * 4
+    assert L.nabla_block_mask_workspace(1, 8192, 8, 128) == 2 * 8 * 128 * 128 * 4
+    assert L.nabla_block_mask_workspace(2, 2049 * 64, 1, 64) == 2 * 2 * 2049 * 64 * 4
     assert L.nabla_block_mask_workspace(1, 100, 16, 128) == 0
     assert L.nabla_block_mask_workspace(0, 64, 1, 64) == 0
 
