@@ -310,19 +310,19 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
                                                  const bf16 *__restrict__ q, int S, int heads,
                                                  NatGrid ng, float *__restrict__ sbuf) {
     constexpr int NWV = 4;
+    static_assert(PH == 0 || PH == 2, "fused (0) or selection from the score buffer (2)");
     constexpr bool SC = PH != 2;  // this launch computes the scores
-    constexpr bool SL = PH != 1;  // this launch selects
     constexpr bool KST = SC && CPT >= 4;
     constexpr int KCOL = KST ? 64 * CPT : 1;  // float4s of one staged column (>= 256)
     constexpr int KRND = (KCOL + 255) / 256;   // staging rounds of 256 float4s (KCOL rounded up)
     __shared__ __attribute__((aligned(16))) float qs[NWV][SC ? RW : 1][SC ? D : 4];
-    __shared__ SelectWaveScratch scr[SL ? NWV : 1];
+    __shared__ SelectWaveScratch scr[NWV];
     __shared__ __attribute__((aligned(1024))) float4 kst[2][KST ? KRND * 256 : 1];
     const int bh = blockIdx.y, lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int row0 = (blockIdx.x * NWV + wv) * RW;
     // with KST every wave takes part in the staging (loads and barriers) of the scores
     if (!KST && row0 >= nb) return;
-    SelectWaveScratch &W = scr[SL ? wv : 0];
+    SelectWaveScratch &W = scr[wv];
     const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 
     constexpr int LPB = 64 / RW, DPL = D / LPB;  // lanes per query block, dims per lane
@@ -471,30 +471,6 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
         }
     }
     }  // SC
-    if constexpr (PH == 1) {
-        // scores launch: the rows' scores (divided by sqrt(D), -0 as +0) to sbuf [bh][nb][nb]
-        if (row0 >= nb) return;
-#pragma unroll 1
-        for (int r = 0; r < RW; ++r) {
-            const int i = row0 + r;
-            if (i >= nb) break;  // wave-uniform
-            float *srow = sbuf + ((int64_t)bh * nb + i) * nb;
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) {
-                float a = 0.0f;
-#pragma unroll
-                for (int rr = 0; rr < RW; ++rr)
-                    if (rr == r) {
-                        if constexpr (MF)
-                            a = acc[rr >> 2][c][rr & 3];
-                        else
-                            a = vacc[rr][c];
-                    }
-                if (64 * c + lane < nb) srow[64 * c + lane] = (TOPK ? a : a / sqrt_d) + 0.0f;
-            }
-        }
-        return;
-    }
     if (KST && row0 >= nb) return;  // no barrier below: waves are independent
 
     // ---- per row: softmax on the 2^-48 grid, cut key, STA union, compaction
@@ -738,6 +714,86 @@ __global__ __launch_bounds__(256, 4) void select_rows_w4_kernel(NABLA_SELECT_ARG
 }
 #undef NABLA_SELECT_ARGS
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ---- block scores as a tiled product (the two-launch path, rows of 513-2048 blocks).
+// S[bh][i][j] = fl32(dot(qa_i, ka_j)) / fl32(sqrt D), -0 stored as +0, for one 64 x 64 block of
+// one (b, head) per workgroup.  d runs in chunks of 32: a chunk of the block's 64 q means and
+// 64 k means is staged in LDS, d-major (row pitch 65 floats, conflict-free operand reads), while
+// the next chunk's global loads are already in flight in registers; each of the four waves
+// computes a 32 x 32 tile with v_mfma_f32_32x32x2_f32, two dimensions per step, d ascending.
+// Lane l supplies A = qa[row l % 32][d + l / 32] and B = ka[block l % 32][d + l / 32];
+// register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.  A chain of
+// these steps gives bits identical to fmaf chained in d order (measured on gfx950,
+// subnormals included), so each score is the readings' fp32 fma chain over d.  The small LDS
+// footprint (16.6 KiB) leaves room for eight workgroups per CU to cover each other's loads.
+template <int D>
+__global__ __launch_bounds__(256) void scores_kernel(const float *__restrict__ qa,
+                                                     const float *__restrict__ ka, int nb,
+                                                     float sqrt_d, float *__restrict__ sbuf) {
+    constexpr int P = 65, KC = 32, NCK = D / KC;  // pitch; dimensions per chunk; chunks
+    constexpr int C4 = KC / 4;                    // float4s per row and chunk
+    constexpr int NL = 64 * C4 / 256;             // float4 loads per lane, operand and chunk
+    __shared__ float As[KC][P], Bs[KC][P];
+    const int bh = blockIdx.z, i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const float *qb = qa + (int64_t)bh * nb * D;                                     // [nb][D]
+    const float4 *kb = reinterpret_cast<const float4 *>(ka) + (int64_t)bh * (D / 4) * nb;  // [D/4][nb]
+    // chunk loads: 64 rows x C4 float4s of each operand, NL per lane each.  A: rows of q means
+    // (d fastest, coalesced); B: the k-mean float4 layout (blocks fastest, coalesced).
+    float4 xa[NL], xb[NL];
+    auto load = [&](int ck) {
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int e = u * 256 + tid;
+            const int ra = e / C4, da = e % C4, rb = e & 63, db = e >> 6;
+            xa[u] = i0 + ra < nb
+                        ? *reinterpret_cast<const float4 *>(qb + (int64_t)(i0 + ra) * D + ck * KC + 4 * da)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+            xb[u] = j0 + rb < nb ? kb[(int64_t)(ck * C4 + db) * nb + j0 + rb]
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto store = [&]() {
+#pragma unroll
+        for (int u = 0; u < NL; ++u) {
+            const int e = u * 256 + tid;
+            const int ra = e / C4, da = e % C4, rb = e & 63, db = e >> 6;
+            As[4 * da + 0][ra] = xa[u].x;
+            As[4 * da + 1][ra] = xa[u].y;
+            As[4 * da + 2][ra] = xa[u].z;
+            As[4 * da + 3][ra] = xa[u].w;
+            Bs[4 * db + 0][rb] = xb[u].x;
+            Bs[4 * db + 1][rb] = xb[u].y;
+            Bs[4 * db + 2][rb] = xb[u].z;
+            Bs[4 * db + 3][rb] = xb[u].w;
+        }
+    };
+    const int wi = (w >> 1) * 32, wj = (w & 1) * 32, hi = lane >> 5, l32 = lane & 31;
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    load(0);
+#pragma unroll 1
+    for (int ck = 0; ck < NCK; ++ck) {
+        store();
+        __syncthreads();                  // chunk ck staged
+        if (ck + 1 < NCK) load(ck + 1);   // in flight under this chunk's MFMAs
+#pragma unroll
+        for (int d = 0; d < KC; d += 2)
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[d + hi][wi + l32], Bs[d + hi][wj + l32],
+                                                        acc, 0, 0, 0);
+        __syncthreads();                  // every wave is done with chunk ck
+    }
+    float *sb = sbuf + (int64_t)bh * nb * nb;
+    const int j = j0 + wj + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int i = i0 + wi + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (i < nb && j < nb) sb[(int64_t)i * nb + j] = acc[r] / sqrt_d + 0.0f;
+    }
+}
+
 // ---------------------------------------------------------------- select (long rows)
 // Rows of more than 2048 blocks.  grid (ceil(nb / R), B*heads); 512 lanes; lane t owns
 // columns j = c*512 + t, c < CPT; the whole workgroup works on one row at a time.
@@ -973,17 +1029,19 @@ static hipError_t launch_rows_t(const float *qa, const float *ka, int BH, int nb
 }
 
 // Rows of 513-2048 blocks in two launches through the score buffer sbuf [BH][nb][nb]: the
-// scores launch (q means, staged k means, matrix-core scores) holds the score accumulators
-// and the staged columns, which leave room for two waves per SIMD; the selection launch
-// reads one row per wave and, without them, keeps four waves per SIMD resident to hide the
-// latency of its reductions, LDS histograms and ballots.
-template <int D, int CPT, int RW>
+// scores as a tiled matrix-core product of the pooled q and k (scores_kernel), then the
+// selection, one row per wave.  Without the score accumulators and staged k columns of the
+// fused kernel, the selection keeps four waves per SIMD resident (rows of up to 16 column
+// groups) to hide the latency of its reductions, LDS histograms and ballots.
+template <int D, int CPT>
 static hipError_t launch_rows_split_t(const float *qa, const float *ka, int BH, int nb,
                                       const uint8_t *sta, float sqrt_d, int64_t cut,
                                       int32_t *kv_nb, int32_t *kv_inds, hipStream_t stream,
-                                      QSource qsrc, float *sbuf) {
-    hipError_t e = launch_rows_t<D, CPT, RW, false, 1>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb,
-                                                      kv_inds, stream, qsrc, sbuf);
+                                      float *sbuf) {
+    const int nt = (nb + 63) / 64;
+    hipLaunchKernelGGL((scores_kernel<D>), dim3(nt, nt, BH), dim3(256), 0, stream, qa, ka, nb,
+                       sqrt_d, sbuf);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (CPT <= 16) {
         hipLaunchKernelGGL((select_rows_w4_kernel<D, CPT>), dim3((nb + 3) / 4, BH), dim3(256), 0,
@@ -1063,8 +1121,8 @@ static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int 
                                   float *sbuf) {
 #define NABLA_ROWS(CPT, RW)                                                                   \
     return sbuf != nullptr                                                                    \
-               ? launch_rows_split_t<D, CPT, RW>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb,     \
-                                                 kv_inds, stream, qsrc, sbuf)                 \
+               ? launch_rows_split_t<D, CPT>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, \
+                                             stream, sbuf)                                    \
                : launch_rows_t<D, CPT, RW>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, \
                                            stream, qsrc)
     if (nb <= 64) NABLA_ROWS(1, 8);
@@ -1117,7 +1175,10 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
     dim3 pgrid(nb, B);
     // bf16 whole blocks: the selection kernel pools q itself, the pooling pass only k
     const bool padded = !natural && H > 0;
-    const bool qfused = bf16_in && !padded && select_pools_q(D, nb);
+    // rows of 513-2048 blocks with a score buffer: the scores are a tiled product of the pooled
+    // q and k (both pooled here); other rows pool q inside the selection kernel where it can
+    const bool split = sbuf != nullptr && mask_scores_split(nb);
+    const bool qfused = !split && bf16_in && !padded && select_pools_q(D, nb);
     const NatGrid ng = nat_grid(natural ? W : 0);
     if (bf16_in)
         hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
@@ -1132,7 +1193,7 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
     const int BH = B * heads;
     QSource qsrc = {};
     if (qfused) qsrc = QSource{(const bf16 *)q, S, heads, ng};
-    if (!mask_scores_split(nb)) sbuf = nullptr;
+    if (!split) sbuf = nullptr;
     if (D == 64)
         return launch_select_d<64>(qa, ka, BH, nb, sta, sqrt_d, cut_fixed, kv_nb, kv_inds, stream,
                                    qsrc, sbuf);
