@@ -22,16 +22,24 @@
 //          so the first kept position does not depend on summation order.
 // The row's arg-max block is always kept.
 //
+// The score chain runs on the fp32 matrix cores (v_mfma_f32_4x4x1_16b_f32 in the fused
+// selection kernel, v_mfma_f32_32x32x2_f32 in scores_kernel): each MFMA step is one
+// correctly rounded fma, applied in step order (measured on gfx950 against fmaf chains,
+// subnormals included), so the chain over d ascending is exactly the one above.
+//
 // Kernels
-//   pool_kernel    HBM-bound: each workgroup reads the 64 token rows of one
-//                  block of q or k once (16-byte coalesced loads) and writes
-//                  heads*D fp32 means.
-//   select_kernel  one workgroup (512 lanes) per (b, head, R query blocks):
-//                  R x nb scores on the fp32 VALU (bit-exact order; MFMA would
-//                  not fix the order), then per row: max, exp, Z, a
-//                  histogram-refined search for the cut key over the 64-bit
-//                  keys (orderable(s) << 12 | j) with exact integer masses, the
-//                  STA union, and a ballot compaction of the kept indices.
+//   pool_kernel         HBM-bound: each workgroup reads the 64 token rows of one block of
+//                       q and k (16-byte coalesced loads) and writes heads*D fp32 means.
+//   select_rows_kernel  rows of up to 512 blocks (and the top-k variant): one wave owns
+//                       whole rows; q pooled here where it can be, k means staged in LDS
+//                       per 4 dimensions, scores on the matrix cores, then per row: max,
+//                       exp, Z, a histogram-refined search for the cut key over the 64-bit
+//                       keys (orderable(s) << 12 | j) with exact integer masses, the STA
+//                       union and a ballot compaction of the kept indices.
+//   scores_kernel +     rows of 513-2048 blocks: the scores as a tiled product into a
+//   select_rows_w4      workspace buffer, then the same selection one row per wave, four
+//                       waves per SIMD.
+//   select_kernel       rows of more than 2048 blocks: one workgroup per row group.
 #include "nabla_device.h"
 #include "nabla_launch.h"
 
@@ -46,7 +54,7 @@ namespace nabla {
 // count min(8, H - 8 ht) * min(8, W - 8 wt).  H = W = 0: whole 64-token blocks.
 // ng.W > 0: q and k are in natural order (whole patches, rows of ng.W tokens); block i's
 // rows are read where the fractal permute would have taken them from, in the same order.
-// first = 1: k only (the selection kernel pools q itself).
+// first = 1: k only (the fused selection kernel pools q itself).
 template <typename Tin>
 __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
                                                    const Tin *__restrict__ k,
@@ -290,10 +298,12 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
 // TOPK: the top-k variant ("sla" page, get_block_map): scores without the 1/sqrt(D)
 // scale, every block weighs one unit instead of its softmax weight, and `cut` is
 // nb - k + 1, so the cut keeps exactly the k largest keys (none when k = 0).
-// KST (rows of 129 .. 1024 blocks): the k means of one float4 column (4 dims of every
-// block) are staged in LDS once per workgroup, double-buffered and loaded straight from
-// memory into LDS, and the four waves read them from there; other rows read them from
-// global memory through L1 (measured at 2048 blocks: single-buffered staging is no faster).
+// KST (rows of 193 blocks or more, 4+ column groups): the k means of one float4 column
+// (4 dims of every block) are staged in LDS once per workgroup, double-buffered and loaded
+// straight from memory into LDS, and the four waves read them from there; shorter rows read
+// them from global memory through L1.
+// PH: 0 = scores and selection in this kernel; 2 = selection only, the scores read from the
+// score buffer sbuf [bh][nb][nb] that scores_kernel wrote (no q means, k means or staging).
 //
 // q != null (bf16, whole blocks; configurations whose lanes cover a row in 16-byte chunks):
 // each wave pools its own RW query blocks from q (in place of reading qa), with the same
