@@ -298,7 +298,7 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
 // TOPK: the top-k variant ("sla" page, get_block_map): scores without the 1/sqrt(D)
 // scale, every block weighs one unit instead of its softmax weight, and `cut` is
 // nb - k + 1, so the cut keeps exactly the k largest keys (none when k = 0).
-// KST (rows of 193 blocks or more, 4+ column groups): the k means of one float4 column
+// KST (rows of 129 blocks or more, 4+ column groups): the k means of one float4 column
 // (4 dims of every block) are staged in LDS once per workgroup, double-buffered and loaded
 // straight from memory into LDS, and the four waves read them from there; shorter rows read
 // them from global memory through L1.
