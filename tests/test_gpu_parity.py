@@ -190,10 +190,12 @@ def test_block_mask_uniform_ties(orc, dev):
     (1, 128, "bf16", 1),      # one column group, one block
     (65, 128, "bf16", 2),     # 2 groups, the second holds one block; batch offset
     (300, 128, "bf16", 1),    # 8 groups, eight rows per wave (two row quads on the matrix cores)
+    (513, 128, "bf16", 1),    # the shortest rows of the two-launch path: score tiles of one row / block
     (897, 128, "bf16", 1),    # 15 groups, the last holds one block
     (1000, 64, "bf16", 1),    # 16 groups, D = 64 (q pooled by the pooling pass)
     (1857, 128, "bf16", 1),   # 30 groups, two rows per wave (vector scores)
     (1921, 128, "fp32", 1),   # 32 groups, fp32 inputs
+    (2048, 64, "bf16", 1),    # the longest rows of the two-launch path, D = 64
 ])
 def test_block_mask_row_lengths(orc, dev, nb, D, dtype, B):
     """Rows of every column-group count of the selection kernel, each with a partial last
