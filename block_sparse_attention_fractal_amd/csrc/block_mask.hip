@@ -47,15 +47,19 @@ namespace nabla {
 
 // ---------------------------------------------------------------- pool
 // grid (nb, B): block i of q is pooled into qa [B*heads][nb][D] and block i of k into
-// ka [B*heads][D/4][nb][4].  One workgroup does both, so that the whole grid is resident
-// at once (no partial second round of workgroups).
+// ka [B*heads][D/4][nb][4] (the layout the selection kernels read), or, KROW, into
+// ka [B*heads][nb][D] like q (for scores_kernel: whole 512-byte rows per head, where the
+// column layout's scattered 16-byte writes cost about a tenth of the kernel's time).  One
+// workgroup does both, so that the whole grid is resident at once (no partial second round
+// of workgroups).
 // H, W > 0: the latent grid of a padded fractal layout (Wt = ceil(W/8) patches per row
 // of patches): a block averages its tokens only, summed in order and divided by their
 // count min(8, H - 8 ht) * min(8, W - 8 wt).  H = W = 0: whole 64-token blocks.
 // ng.W > 0: q and k are in natural order (whole patches, rows of ng.W tokens); block i's
 // rows are read where the fractal permute would have taken them from, in the same order.
 // first = 1: k only (the fused selection kernel pools q itself).
-template <typename Tin>
+// PAD: the instance for padded grids (H > 0); the other one has no per-row checks.
+template <typename Tin, bool PAD, bool KROW>
 __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
                                                    const Tin *__restrict__ k,
                                                    float *__restrict__ qa,
@@ -67,13 +71,13 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
     const int row_elems = heads * D;
     const int nchunks = row_elems / EPC;
     int vrows = kTile, vcols = kTile;
-    if (H > 0) {
+    if (PAD && H > 0) {
         const int Ht = (H + kTile - 1) / kTile, Wt = (W + kTile - 1) / kTile;
         const int th = (i / Wt) % Ht, tw = i % Wt;
         vrows = min(kTile, H - th * kTile);
         vcols = min(kTile, W - tw * kTile);
     }
-    const bool whole = vrows == kTile && vcols == kTile;
+    const bool whole = !PAD || (vrows == kTile && vcols == kTile);
     const int cnt = vrows * vcols;
     for (int item = threadIdx.x + first * nchunks; item < 2 * nchunks; item += 256) {
     const int z = item >= nchunks;  // 0: q, 1: k
@@ -120,10 +124,11 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
         const int64_t bhh = (int64_t)b * heads + h;
 #pragma unroll
         for (int e = 0; e < EPC; e += 4) {
-            // q: row-major [bh][nb][D]; k: [bh][D/4][nb] float4s, so that the score loop
-            // reads the k means of consecutive blocks from consecutive addresses
-            float *out = z ? xa + ((bhh * (D / 4) + (d + e) / 4) * nb + i) * 4
-                           : xa + (bhh * nb + i) * D + d + e;
+            // q (and k with KROW): row-major [bh][nb][D]; k: [bh][D/4][nb] float4s, so that
+            // the selection's score loop reads the k means of consecutive blocks from
+            // consecutive addresses
+            float *out = (z && !KROW) ? xa + ((bhh * (D / 4) + (d + e) / 4) * nb + i) * 4
+                                      : xa + (bhh * nb + i) * D + d + e;
             // mean: * 2^-6 on whole blocks (exact, equal to / 64), else / token count
             float m[4];
 #pragma unroll
@@ -136,8 +141,10 @@ __global__ __launch_bounds__(256) void pool_kernel(const Tin *__restrict__ q,
 }
 
 // ---------------------------------------------------------------- select helpers
-__device__ __forceinline__ float nabla_exp(float x) {
-    if (!(x >= -64.0f)) return 0.0f;
+// Branch-free: the polynomial runs on max(x, -64) and the result is selected, so that a
+// wave evaluates it once with no divergent paths (x >= -64 takes exactly the same steps).
+__device__ __forceinline__ float nabla_exp(float x_in) {
+    const float x = fmaxf(x_in, -64.0f);
     const float log2e = 1.44269504088896341f;
     const float ln2_hi = 0.693145751953125f;
     const float ln2_lo = 1.42860682030941723e-6f;
@@ -153,7 +160,7 @@ __device__ __forceinline__ float nabla_exp(float x) {
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
     const float two_n = __int_as_float(((int)n + 127) << 23);
-    return p * two_n;
+    return x_in >= -64.0f ? p * two_n : 0.0f;
 }
 
 // Monotone map of finite floats to unsigned ints (callers pass no -0).
@@ -165,18 +172,17 @@ __device__ __forceinline__ float f32_from_orderable(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// floor(v * 2^48) for 0 <= v <= 1, exactly: v = m * 2^(u - 23) with the 24-bit
-// significand m and unbiased exponent u <= 0, so v * 2^48 = m * 2^(u + 25), an integer
-// shift of m (right shifts truncate, which is the floor for v >= 0).  Denormals and 0
-// give 0 (below 2^-78).
+// floor(v * 2^48) for 0 <= v <= 1, exactly and without branches: t = v * 2^16 is exact,
+// its integer part h = trunc(t) <= 2^16 and its fraction f = t - h are exact (h is zero or
+// at least t / 2), and f * 2^32 < 2^32 is exact, so floor(v * 2^48) = h * 2^32 +
+// trunc(f * 2^32): h is the high word, trunc(f * 2^32) the low word.  Denormals and 0 give 0.
+// (Equal, for every float in [0, 1], to the shift of the 24-bit significand by its exponent.)
 __device__ __forceinline__ int64_t fix48(float v) {
-    const uint32_t bits = __float_as_uint(v);
-    const int biased = (int)(bits >> 23) & 0xff;
-    if (biased == 0) return 0;
-    const uint64_t m = (uint64_t)((bits & 0x7fffffu) | 0x800000u);
-    const int sh = biased - 127 + 25;
-    if (sh >= 0) return (int64_t)(m << sh);
-    return sh > -64 ? (int64_t)(m >> -sh) : 0;
+    const float t = v * 65536.0f;
+    const uint32_t h = (uint32_t)t;
+    const float f = t - (float)h;
+    const uint32_t l = (uint32_t)(f * 4294967296.0f);
+    return (int64_t)(((uint64_t)h << 32) | l);
 }
 
 template <int NW>
@@ -535,7 +541,7 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
             esum = wave_sum_i64(esum);
             const float Z = (float)(double)esum * 0x1p-48f;
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? fix48(nabla_exp(s[c] - smax) / Z) : 0;
+            for (int c = 0; c < CPT; ++c) P[c] = fix48(valid[c] ? nabla_exp(s[c] - smax) / Z : 0.0f);
         } else {
             float e[CPT];
             int64_t esum = 0;
@@ -547,26 +553,30 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
             esum = wave_sum_i64(esum);
             const float Z = (float)(double)esum * 0x1p-48f;
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? fix48(e[c] / Z) : 0;
+            for (int c = 0; c < CPT; ++c) P[c] = fix48(e[c] / Z);  // e = 0 off the row
         }
 
         // One histogram pass over the members (inr) into kSelBins bins (bin_of); returns
         // the bin holding the cut (-1 if the members' mass stays below it) with the mass
-        // before it and its count (counted with ballots once the bin is known).
-        auto hist_pass = [&](auto inr, auto bin_of, int64_t below, int64_t &bbelow, int &bcnt) {
+        // before it, its count and, bit c of fbits, whether column group c of this lane is
+        // in it (the count taken with ballots of those bits once the bin is known).
+        static_assert(CPT <= 32, "one bit per column group");
+        auto hist_pass = [&](auto inr, auto bin_of, int64_t below, int64_t &bbelow, int &bcnt,
+                             uint32_t &fbits) {
 #pragma unroll
             for (int q = 0; q < kSelBins / 64; ++q) {
                 W.hm[lane * (kSelBins / 64) + q] = 0;
                 if (!LEAN) W.hc[lane * (kSelBins / 64) + q] = 0;
             }
             __builtin_amdgcn_wave_barrier();
+            // every lane adds for every column (non-members add 0 to bin 0): no divergent paths
 #pragma unroll
-            for (int c = 0; c < CPT; ++c)
-                if (inr(c)) {
-                    const int bn = bin_of(c);
-                    atomicAdd((unsigned long long *)&W.hm[bn], (unsigned long long)P[c]);
-                    if (!LEAN) atomicAdd(&W.hc[bn], 1);
-                }
+            for (int c = 0; c < CPT; ++c) {
+                const bool in = inr(c);
+                const int bn = in ? bin_of(c) : 0;
+                atomicAdd((unsigned long long *)&W.hm[bn], (unsigned long long)(in ? P[c] : 0));
+                if (!LEAN) atomicAdd(&W.hc[bn], in ? 1 : 0);
+            }
             __builtin_amdgcn_wave_barrier();
             int64_t m[kSelBins / 64];
             int64_t tot = 0;
@@ -591,10 +601,13 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
             const int src = __builtin_ctzll(bal);
             bbelow = (int64_t)shfl_u64((uint64_t)fb, src);
             const int fbin = __builtin_amdgcn_readlane(found, src);
+            fbits = 0;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) fbits |= (inr(c) && bin_of(c) == fbin ? 1u : 0u) << c;
             if constexpr (LEAN) {
                 int n = 0;
 #pragma unroll
-                for (int c = 0; c < CPT; ++c) n += __popcll(__ballot(inr(c) && bin_of(c) == fbin));
+                for (int c = 0; c < CPT; ++c) n += __popcll(__ballot((fbits >> c) & 1u));
                 bcnt = n;
             } else {
                 bcnt = W.hc[fbin];
@@ -631,13 +644,22 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
         if (cut > 0) {
             const float range = smax - smin;
             const float scale = range > 1e-30f ? (float)kSelBins / range : 0.0f;
-            auto bin_f = [&](int c) {
+            // bins of the score range, computed once and kept as bytes (0 off the row)
+            static_assert(kSelBins <= 256, "bins are kept in bytes");
+            uint32_t bpk[(CPT + 3) / 4];
+#pragma unroll
+            for (int u = 0; u < (CPT + 3) / 4; ++u) bpk[u] = 0;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
                 const int bi = (int)((s[c] - smin) * scale);
-                return bi > kSelBins - 1 ? kSelBins - 1 : bi;
-            };
+                const uint32_t bc = valid[c] ? (uint32_t)(bi > kSelBins - 1 ? kSelBins - 1 : bi) : 0u;
+                bpk[c >> 2] |= bc << (8 * (c & 3));
+            }
+            auto bin_f = [&](int c) { return (int)((bpk[c >> 2] >> (8 * (c & 3))) & 0xffu); };
             int64_t below = 0;
             int cnt = 0;
-            const int b = hist_pass([&](int c) { return valid[c]; }, bin_f, 0, below, cnt);
+            uint32_t inb = 0;  // bit c: column group c of this lane is in the cut bin
+            const int b = hist_pass([&](int c) { return valid[c]; }, bin_f, 0, below, cnt, inb);
             if (b < 0 && TOPK) {  // k = 0: no block is selected
                 T = ~0ull;
             } else if (b < 0) {  // total mass below the cut: only the arg-max (largest key) stays
@@ -647,13 +669,13 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
                     if (valid[c]) km = key_of(c) > km ? key_of(c) : km;
                 T = wave_max_u64(km);
             } else if (cnt <= 64) {
-                T = rank_list([&](int c) { return valid[c] && bin_f(c) == b; }, below);
+                T = rank_list([&](int c) { return ((inb >> c) & 1u) != 0; }, below);
             } else {
                 // many keys share the bin: narrow its key range by histogram passes
                 uint64_t lo = ~0ull, hi = 0;
 #pragma unroll
                 for (int c = 0; c < CPT; ++c)
-                    if (valid[c] && bin_f(c) == b) {
+                    if ((inb >> c) & 1u) {
                         const uint64_t kk = key_of(c);
                         lo = kk < lo ? kk : lo;
                         hi = kk > hi ? kk : hi;
@@ -669,8 +691,9 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
                     };
                     int64_t b2below = 0;
                     int c2 = 0;
+                    uint32_t inb2 = 0;
                     const int b2 = hist_pass(inr, [&](int c) { return (int)((key_of(c) - lo) >> shift); },
-                                             below, b2below, c2);
+                                             below, b2below, c2, inb2);
                     // b2 >= 0: the range holds the cut by construction
                     const uint64_t nlo = lo + ((uint64_t)b2 << shift);
                     const uint64_t nhi0 = nlo + ((1ull << shift) - 1);
@@ -728,8 +751,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---- block scores as a tiled product (the two-launch path, rows of 513-2048 blocks).
 // S[bh][i][j] = fl32(dot(qa_i, ka_j)) / fl32(sqrt D), -0 stored as +0, for one 64 x 64 block of
-// one (b, head) per workgroup.  d runs in chunks of 32: a chunk of the block's 64 q means and
-// 64 k means is staged in LDS, d-major (row pitch 65 floats, conflict-free operand reads), while
+// one (b, head) per workgroup; qa and ka both row-major [bh][nb][D].  d runs in chunks of 32: a
+// chunk of the block's 64 q means and 64 k means is staged in LDS, d-major (row pitch 65 floats,
+// conflict-free operand reads), while
 // the next chunk's global loads are already in flight in registers; each of the four waves
 // computes a 32 x 32 tile with v_mfma_f32_32x32x2_f32, two dimensions per step, d ascending.
 // Lane l supplies A = qa[row l % 32][d + l / 32] and B = ka[block l % 32][d + l / 32];
@@ -737,46 +761,53 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // these steps gives bits identical to fmaf chained in d order (measured on gfx950,
 // subnormals included), so each score is the readings' fp32 fma chain over d.  The small LDS
 // footprint (16.6 KiB) leaves room for eight workgroups per CU to cover each other's loads.
+// grid: nt * nt * BH workgroups in one dimension (nt = ceil(nb / 64)).  Workgroups go to the
+// eight XCDs in turn by id; when the count divides by eight, id n takes tile
+// (n mod 8) * count / 8 + n / 8 in (bh, row tile, column tile) order, so that each XCD works on
+// one eighth of the (b, head) pairs and their pooled q and k stay in its own L2.
 template <int D>
-__global__ __launch_bounds__(256) void scores_kernel(const float *__restrict__ qa,
+__global__ __launch_bounds__(256, 8) void scores_kernel(const float *__restrict__ qa,
                                                      const float *__restrict__ ka, int nb,
                                                      float sqrt_d, float *__restrict__ sbuf) {
     constexpr int P = 65, KC = 32, NCK = D / KC;  // pitch; dimensions per chunk; chunks
     constexpr int C4 = KC / 4;                    // float4s per row and chunk
     constexpr int NL = 64 * C4 / 256;             // float4 loads per lane, operand and chunk
     __shared__ float As[KC][P], Bs[KC][P];
-    const int bh = blockIdx.z, i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+    const int nt = (nb + 63) / 64, count = (int)gridDim.x;
+    int n = (int)blockIdx.x;
+    if (count % 8 == 0) n = (n % 8) * (count / 8) + n / 8;
+    const int bh = n / (nt * nt), tt = n - bh * nt * nt;
+    const int i0 = (tt / nt) * 64, j0 = (tt % nt) * 64;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const float *qb = qa + (int64_t)bh * nb * D;                                     // [nb][D]
-    const float4 *kb = reinterpret_cast<const float4 *>(ka) + (int64_t)bh * (D / 4) * nb;  // [D/4][nb]
-    // chunk loads: 64 rows x C4 float4s of each operand, NL per lane each.  A: rows of q means
-    // (d fastest, coalesced); B: the k-mean float4 layout (blocks fastest, coalesced).
+    const float *qb = qa + (int64_t)bh * nb * D;  // [nb][D]
+    const float *kb = ka + (int64_t)bh * nb * D;  // [nb][D] (the pooling pass's row-major k means)
+    // chunk loads: 64 rows x C4 float4s of each operand, NL per lane each, d fastest (coalesced)
     float4 xa[NL], xb[NL];
     auto load = [&](int ck) {
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const int e = u * 256 + tid;
-            const int ra = e / C4, da = e % C4, rb = e & 63, db = e >> 6;
-            xa[u] = i0 + ra < nb
-                        ? *reinterpret_cast<const float4 *>(qb + (int64_t)(i0 + ra) * D + ck * KC + 4 * da)
-                        : make_float4(0.f, 0.f, 0.f, 0.f);
-            xb[u] = j0 + rb < nb ? kb[(int64_t)(ck * C4 + db) * nb + j0 + rb]
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int r = e / C4, dc = e % C4;
+            const int64_t off = (int64_t)r * D + ck * KC + 4 * dc;
+            xa[u] = i0 + r < nb ? *reinterpret_cast<const float4 *>(qb + (int64_t)i0 * D + off)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            xb[u] = j0 + r < nb ? *reinterpret_cast<const float4 *>(kb + (int64_t)j0 * D + off)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
     auto store = [&]() {
 #pragma unroll
         for (int u = 0; u < NL; ++u) {
             const int e = u * 256 + tid;
-            const int ra = e / C4, da = e % C4, rb = e & 63, db = e >> 6;
-            As[4 * da + 0][ra] = xa[u].x;
-            As[4 * da + 1][ra] = xa[u].y;
-            As[4 * da + 2][ra] = xa[u].z;
-            As[4 * da + 3][ra] = xa[u].w;
-            Bs[4 * db + 0][rb] = xb[u].x;
-            Bs[4 * db + 1][rb] = xb[u].y;
-            Bs[4 * db + 2][rb] = xb[u].z;
-            Bs[4 * db + 3][rb] = xb[u].w;
+            const int r = e / C4, dc = e % C4;
+            As[4 * dc + 0][r] = xa[u].x;
+            As[4 * dc + 1][r] = xa[u].y;
+            As[4 * dc + 2][r] = xa[u].z;
+            As[4 * dc + 3][r] = xa[u].w;
+            Bs[4 * dc + 0][r] = xb[u].x;
+            Bs[4 * dc + 1][r] = xb[u].y;
+            Bs[4 * dc + 2][r] = xb[u].z;
+            Bs[4 * dc + 3][r] = xb[u].w;
         }
     };
     const int wi = (w >> 1) * 32, wj = (w & 1) * 32, hi = lane >> 5, l32 = lane & 31;
@@ -913,7 +944,7 @@ __global__ __launch_bounds__(512) void select_kernel(const float *__restrict__ q
         const float Z = (float)(double)ze * 0x1p-48f;
         int64_t P[CPT];
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) P[c] = valid[c] ? fix48(e[c] / Z) : 0;
+        for (int c = 0; c < CPT; ++c) P[c] = fix48(e[c] / Z);  // e = 0 off the row
 
         // cut key T: the smallest key whose inclusive prefix mass reaches cut
         uint64_t T;
@@ -1049,7 +1080,8 @@ static hipError_t launch_rows_split_t(const float *qa, const float *ka, int BH, 
                                       int32_t *kv_nb, int32_t *kv_inds, hipStream_t stream,
                                       float *sbuf) {
     const int nt = (nb + 63) / 64;
-    hipLaunchKernelGGL((scores_kernel<D>), dim3(nt, nt, BH), dim3(256), 0, stream, qa, ka, nb,
+    if ((int64_t)nt * nt * BH > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((scores_kernel<D>), dim3(nt * nt * BH), dim3(256), 0, stream, qa, ka, nb,
                        sqrt_d, sbuf);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1149,21 +1181,37 @@ static hipError_t launch_select_d(const float *qa, const float *ka, int BH, int 
     return launch_select_t<D, 8, 8>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb, kv_inds, stream);
 }
 
+// The pooling pass (grid (nb, B)); H > 0 selects the instance with per-row padding checks,
+// krow the row-major k means.
+static void launch_pool(const void *q, const void *k, bool bf16_in, int B, int S, int heads,
+                        int D, int H, int W, NatGrid ng, int first, bool krow, float *qa,
+                        float *ka, hipStream_t stream) {
+    const dim3 grid(S / kBlock, B);
+#define NABLA_POOL(T, PAD, KR)                                                                  \
+    hipLaunchKernelGGL((pool_kernel<T, PAD, KR>), grid, dim3(256), 0, stream, (const T *)q,    \
+                       (const T *)k, qa, ka, S, heads, D, H, W, ng, first)
+#define NABLA_POOL_K(T, PAD)             \
+    if (krow) NABLA_POOL(T, PAD, true);  \
+    else NABLA_POOL(T, PAD, false)
+    if (bf16_in) {
+        if (H > 0) { NABLA_POOL_K(bf16, true); }
+        else { NABLA_POOL_K(bf16, false); }
+    } else {
+        if (H > 0) { NABLA_POOL_K(float, true); }
+        else { NABLA_POOL_K(float, false); }
+    }
+#undef NABLA_POOL_K
+#undef NABLA_POOL
+}
+
 hipError_t launch_block_mask_topk(const void *q, const void *k, bool bf16_in, int B, int S,
                                   int heads, int D, int H, int W, bool natural,
                                   const uint8_t *sta, int topk,
                                   int32_t *kv_nb, int32_t *kv_inds, float *qa, float *ka,
                                   hipStream_t stream) {
     const int nb = S / kBlock;
-    dim3 pgrid(nb, B);
-    if (bf16_in)
-        hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, qa, ka, S, heads, D, natural ? 0 : H,
-                           natural ? 0 : W, nat_grid(natural ? W : 0), 0);
-    else
-        hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
-                           (const float *)k, qa, ka, S, heads, D, natural ? 0 : H,
-                           natural ? 0 : W, nat_grid(natural ? W : 0), 0);
+    launch_pool(q, k, bf16_in, B, S, heads, D, natural ? 0 : H, natural ? 0 : W,
+                nat_grid(natural ? W : 0), 0, false, qa, ka, stream);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int BH = B * heads;
@@ -1182,7 +1230,6 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
                              int64_t cut_fixed, float sqrt_d, int32_t *kv_nb, int32_t *kv_inds,
                              float *qa, float *ka, float *sbuf, hipStream_t stream) {
     const int nb = S / kBlock;
-    dim3 pgrid(nb, B);
     // bf16 whole blocks: the selection kernel pools q itself, the pooling pass only k
     const bool padded = !natural && H > 0;
     // rows of 513-2048 blocks with a score buffer: the scores are a tiled product of the pooled
@@ -1190,14 +1237,8 @@ hipError_t launch_block_mask(const void *q, const void *k, bool bf16_in, int B, 
     const bool split = sbuf != nullptr && mask_scores_split(nb);
     const bool qfused = !split && bf16_in && !padded && select_pools_q(D, nb);
     const NatGrid ng = nat_grid(natural ? W : 0);
-    if (bf16_in)
-        hipLaunchKernelGGL(pool_kernel<bf16>, pgrid, dim3(256), 0, stream, (const bf16 *)q,
-                           (const bf16 *)k, qa, ka, S, heads, D, natural ? 0 : H,
-                           natural ? 0 : W, ng, qfused ? 1 : 0);
-    else
-        hipLaunchKernelGGL(pool_kernel<float>, pgrid, dim3(256), 0, stream, (const float *)q,
-                           (const float *)k, qa, ka, S, heads, D, natural ? 0 : H,
-                           natural ? 0 : W, ng, 0);
+    launch_pool(q, k, bf16_in, B, S, heads, D, natural ? 0 : H, natural ? 0 : W, ng,
+                qfused ? 1 : 0, split, qa, ka, stream);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int BH = B * heads;
