@@ -502,7 +502,14 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
         for (int c = 0; c < CPT; ++c) {
             valid[c] = 64 * c + lane < nb;
             if constexpr (PH == 2) {
-                s[c] = valid[c] ? sbuf[row * nb + 64 * c + lane] : 0.0f;
+                if constexpr (CPT > 16) {
+                    // every lane loads (the last column again past the row's end): no
+                    // branches (shorter rows keep the branch: the hoisted loads spill there)
+                    const float v = sbuf[row * nb + (valid[c] ? 64 * c + lane : nb - 1)];
+                    s[c] = valid[c] ? v : 0.0f;
+                } else {
+                    s[c] = valid[c] ? sbuf[row * nb + 64 * c + lane] : 0.0f;
+                }
             } else {
                 float a = 0.0f;
 #pragma unroll
@@ -547,7 +554,7 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
             int64_t esum = 0;
 #pragma unroll
             for (int c = 0; c < CPT; ++c) {
-                e[c] = valid[c] ? nabla_exp(s[c] - smax) : 0.0f;
+                e[c] = nabla_exp(valid[c] ? s[c] - smax : -INFINITY);  // 0 off the row
                 esum += fix48(e[c]);
             }
             esum = wave_sum_i64(esum);
@@ -932,7 +939,7 @@ __global__ __launch_bounds__(512) void select_kernel(const float *__restrict__ q
         int64_t esum = 0;
 #pragma unroll
         for (int c = 0; c < CPT; ++c) {
-            e[c] = valid[c] ? nabla_exp(s[c] - smax) : 0.0f;
+            e[c] = nabla_exp(valid[c] ? s[c] - smax : -INFINITY);  // 0 off the row
             esum += fix48(e[c]);
         }
         esum = wave_sum_i64(esum);
