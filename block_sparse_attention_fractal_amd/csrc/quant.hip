@@ -150,9 +150,9 @@ __global__ __launch_bounds__(256) void quant_kmean_kernel(const float *__restric
     if (tid < CW) km[bh * D + d0 + tid] = acc / (float)ntok;  // ntok: the token count
 }
 
-__device__ __forceinline__ uint32_t int8_code(float x, float scale) {
-    if (scale == 0.0f) return 0u;
-    const float r = fminf(fmaxf(__builtin_rintf(x / scale), -127.0f), 127.0f);
+// the byte of clamp(n, -127, 127) for an integral n (the code of rint(x / scale))
+__device__ __forceinline__ uint32_t int8_of(float n) {
+    const float r = fminf(fmaxf(n, -127.0f), 127.0f);
     return (uint32_t)(uint8_t)(int8_t)(int)r;
 }
 
@@ -227,14 +227,34 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q
     const float scale = amax / 127.0f;
     int8_t *dst = (is_k ? k8 : q8) + item * (kBlock * D);
     if (lane == 0) (is_k ? ks : qs)[item] = scale;
+    // rint(x / scale) through the block's reciprocal: with inv = fl(1 / scale) and
+    // |x| <= amax, |x / scale| <= 127 (1 + 2^-24), and fl(x * inv) differs from the IEEE
+    // quotient fl(x / scale) by at most |x / scale| (1.5 * 2^-23 + 2^-48) < 2^-15.  So where
+    // fl(x * inv) lies farther than 2^-15 from every half-integer, both round to the same
+    // integer; the rare columns closer to one (and blocks whose scale is 0 or subnormal,
+    // where 1 / scale may overflow) take the IEEE quotient itself.
+    const float inv = 1.0f / scale;
+    const bool fast = scale >= 0x1p-126f;  // wave-uniform
 #pragma unroll
     for (int r = 0; r < CPL; ++r) {
         const int e = 64 * r + lane;
+        float n[8];
+        float gap = 1.0f;  // the least distance of a quotient to a half-integer
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float qv = x[r][i] * inv;
+            n[i] = __builtin_rintf(qv);
+            gap = fminf(gap, fabsf(fabsf(qv - n[i]) - 0.5f));
+        }
+        if (!fast || gap <= 0x1p-15f) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) n[i] = scale == 0.0f ? 0.0f : __builtin_rintf(x[r][i] / scale);
+        }
         uint32_t w0 = 0, w1 = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            w0 |= int8_code(x[r][i], scale) << (8 * i);
-            w1 |= int8_code(x[r][4 + i], scale) << (8 * i);
+            w0 |= int8_of(n[i]) << (8 * i);
+            w1 |= int8_of(n[4 + i]) << (8 * i);
         }
         *reinterpret_cast<uint2 *>(dst + 8 * e) = make_uint2(w0, w1);
     }
