@@ -60,40 +60,39 @@ __device__ __forceinline__ void load8_f32(const float *p, float (&x)[8]) {
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-// bs[item][d] = sequential fp32 sum of the block's 64 tokens, item = (b*heads + h)*nb + j.
-// 256 lanes = 16 blocks x D/8 lanes of 8 channels (16-byte loads); each lane adds its 64
-// rows in token order, 16 rows of loads in flight at a time.
+// bs[(b*heads + h)*nb + j][d] = sequential fp32 sum of block j's 64 tokens.  grid (nb, B):
+// one workgroup per block reads its 64 token rows whole (every head, 16-byte loads, each row
+// one contiguous run); lane item c (heads * D/8 of them per row, 256 at a time) adds channels
+// 8c .. 8c+7 of the row over the block's rows in token order, 16 rows of loads in flight.
 template <int D, typename Tin, bool kPad>
 __global__ __launch_bounds__(256) void quant_ksum_kernel(const Tin *__restrict__ k,
                                                          float *__restrict__ bs, int S,
-                                                         int heads, int64_t items, QuantPad g) {
-    constexpr int CG = D / 8;                // lanes per block
-    constexpr int BPW = 256 / CG;            // blocks per workgroup
+                                                         int heads, QuantPad g) {
+    constexpr int CG = D / 8;  // 8-channel chunks per head
     const int nb = S / kBlock;
-    const int64_t item = (int64_t)blockIdx.x * BPW + threadIdx.x / CG;
-    if (item >= items) return;
-    const int cg = threadIdx.x % CG;
-    const int j = (int)(item % nb), bh = (int)(item / nb);
-    const int b = bh / heads, h = bh % heads;
+    const int j = blockIdx.x, b = blockIdx.y;
     const int64_t tok = (int64_t)heads * D;
-    const Tin *src = k + (int64_t)b * S * tok + (int64_t)h * D + 8 * cg;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int vr = kTile, vc = kTile;
     if constexpr (kPad) qpatch(g, j, vr, vc);
-    for (int r0 = 0; r0 < kBlock; r0 += 16) {
-        float x[16][8];
+    for (int c = threadIdx.x; c < heads * CG; c += 256) {
+        const int h = c / CG, cg = c - h * CG;
+        const Tin *src = k + (int64_t)b * S * tok + 8 * c;  // channels h*D + 8cg
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int r0 = 0; r0 < kBlock; r0 += 16) {
+            float x[16][8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) load8_f32(src + block_row_token(j, r0 + r, g.ng) * tok, x[r]);
+            for (int r = 0; r < 16; ++r) load8_f32(src + block_row_token(j, r0 + r, g.ng) * tok, x[r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            if (kPad && !qrow_ok(r0 + r, vr, vc)) continue;  // padding: not a token
+            for (int r = 0; r < 16; ++r) {
+                if (kPad && !qrow_ok(r0 + r, vr, vc)) continue;  // padding: not a token
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += x[r][i];
+                for (int i = 0; i < 8; ++i) acc[i] += x[r][i];
+            }
         }
+        float *dst = bs + (((int64_t)b * heads + h) * nb + j) * D + 8 * cg;
+        *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4 *>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
-    float *dst = bs + item * D + 8 * cg;
-    *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *reinterpret_cast<float4 *>(dst + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 // km[bh][d] = (sequential sum over blocks of bs) / ntok (S unless the layout is padded).  One
@@ -169,8 +168,9 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// One wave per (block, tensor): blockIdx.y = 0 quantizes q, 1 quantizes k - k_mean; the four
-// waves of a workgroup take four consecutive blocks.  Lane l holds the 8-element chunks
+// One wave per (block, head, tensor): blockIdx.y = 0 quantizes q, 1 quantizes k - k_mean; the
+// waves are numbered with the head fastest, so the four waves of a workgroup (and neighbouring
+// workgroups) read neighbouring 2 D-byte runs of the same token rows.  Lane l holds the 8-element chunks
 // e = 64 r + l (row e / (D/8)) in registers, so each load instruction of the wave reads whole
 // rows; the block maximum is a wave reduction, then the codes are written as 8-byte runs in
 // the same row-major order.  No barrier.
@@ -187,11 +187,12 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const Tin *__restrict__ q
     constexpr int CPL = kBlock * CH / 64;      // chunks per lane
     const int nb = S / kBlock;
     const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= items) return;  // wave-uniform; no barrier in this kernel
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // ((b nb + j) heads + h)
+    if (wid >= items) return;  // wave-uniform; no barrier in this kernel
     const bool is_k = blockIdx.y == 1;
-    const int j = (int)(item % nb), bh = (int)(item / nb);
-    const int b = bh / heads, h = bh % heads;
+    const int h = (int)(wid % heads), j = (int)((wid / heads) % nb);
+    const int b = (int)(wid / ((int64_t)heads * nb)), bh = b * heads + h;
+    const int64_t item = (int64_t)bh * nb + j;  // the block's place in the outputs
     const int64_t tok = (int64_t)heads * D;
     const Tin *src = (is_k ? k : q) + (int64_t)b * S * tok + (int64_t)h * D;
     const int c = lane % CH;  // the same channel chunk for every r (64 % CH == 0)
@@ -412,10 +413,8 @@ static hipError_t launch_quant_t(const void *q, const void *k, const void *v, in
                                             round256q((size_t)items * D * 4));
     const Tin *qi = static_cast<const Tin *>(q), *ki = static_cast<const Tin *>(k),
               *vi = static_cast<const Tin *>(v);
-    constexpr int kBlocksPerWg = 256 / (D / 8);
-    hipLaunchKernelGGL((quant_ksum_kernel<D, Tin, kPad>),
-                       dim3((items + kBlocksPerWg - 1) / kBlocksPerWg), dim3(256), 0, st, ki, bs,
-                       S, heads, items, g);
+    hipLaunchKernelGGL((quant_ksum_kernel<D, Tin, kPad>), dim3(nb, B), dim3(256), 0, st, ki, bs,
+                       S, heads, g);
     hipLaunchKernelGGL((quant_kmean_kernel<D>), dim3(B * heads * (D / 8)), dim3(256), 0, st, bs,
                        km, S, ntok);
     hipLaunchKernelGGL((quant_qk_kernel<D, Tin, kPad>), dim3((items + 3) / 4, 2), dim3(256), 0, st,
