@@ -651,18 +651,28 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
         if (cut > 0) {
             const float range = smax - smin;
             const float scale = range > 1e-30f ? (float)kSelBins / range : 0.0f;
-            // bins of the score range, computed once and kept as bytes (0 off the row)
+            // bins of the score range (0 off the row).  One row per wave: computed once and kept
+            // as bytes; several rows per wave (the fused kernel, registers held by the score
+            // accumulators): recomputed where needed
             static_assert(kSelBins <= 256, "bins are kept in bytes");
-            uint32_t bpk[(CPT + 3) / 4];
-#pragma unroll
-            for (int u = 0; u < (CPT + 3) / 4; ++u) bpk[u] = 0;
-#pragma unroll
-            for (int c = 0; c < CPT; ++c) {
+            constexpr bool KEEPB = RW == 1;
+            uint32_t bpk[KEEPB ? (CPT + 3) / 4 : 1];
+            auto bin_of_score = [&](int c) -> uint32_t {
                 const int bi = (int)((s[c] - smin) * scale);
-                const uint32_t bc = valid[c] ? (uint32_t)(bi > kSelBins - 1 ? kSelBins - 1 : bi) : 0u;
-                bpk[c >> 2] |= bc << (8 * (c & 3));
+                return valid[c] ? (uint32_t)(bi > kSelBins - 1 ? kSelBins - 1 : bi) : 0u;
+            };
+            if constexpr (KEEPB) {
+#pragma unroll
+                for (int u = 0; u < (CPT + 3) / 4; ++u) bpk[u] = 0;
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) bpk[c >> 2] |= bin_of_score(c) << (8 * (c & 3));
             }
-            auto bin_f = [&](int c) { return (int)((bpk[c >> 2] >> (8 * (c & 3))) & 0xffu); };
+            auto bin_f = [&](int c) -> int {
+                if constexpr (KEEPB)
+                    return (int)((bpk[c >> 2] >> (8 * (c & 3))) & 0xffu);
+                else
+                    return (int)bin_of_score(c);
+            };
             int64_t below = 0;
             int cnt = 0;
             uint32_t inb = 0;  // bit c: column group c of this lane is in the cut bin

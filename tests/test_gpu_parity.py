@@ -186,21 +186,26 @@ def test_block_mask_uniform_ties(orc, dev):
 
 
 # ------------------------------------------------------------------ attention
-@pytest.mark.parametrize("nb,D,dtype,B", [
-    (1, 128, "bf16", 1),      # one column group, one block
-    (65, 128, "bf16", 2),     # 2 groups, the second holds one block; batch offset
-    (300, 128, "bf16", 1),    # 8 groups, eight rows per wave (two row quads on the matrix cores)
-    (513, 128, "bf16", 1),    # the shortest rows of the two-launch path: score tiles of one row / block
-    (897, 128, "bf16", 1),    # 15 groups, the last holds one block
-    (1000, 64, "bf16", 1),    # 16 groups, D = 64 (q pooled by the pooling pass)
-    (1857, 128, "bf16", 1),   # 30 groups, two rows per wave (vector scores)
-    (1921, 128, "fp32", 1),   # 32 groups, fp32 inputs
-    (2048, 64, "bf16", 1),    # the longest rows of the two-launch path, D = 64
+@pytest.mark.parametrize("nb,D,dtype,B,h", [
+    (1, 128, "bf16", 1, 2),      # one column group, one block
+    (65, 128, "bf16", 2, 2),     # 2 groups, the second holds one block; batch offset
+    (300, 128, "bf16", 1, 2),    # 8 groups, eight rows per wave (two row quads on the matrix cores)
+    (513, 128, "bf16", 1, 2),    # the shortest rows of the two-launch path: score tiles of one row / block
+    (600, 128, "bf16", 1, 3),    # three heads: score tiles and selection rows of several heads
+    (700, 128, "bf16", 2, 4),    # four heads, two batches: (b, head) offsets of the score buffer
+    (897, 128, "bf16", 1, 2),    # 15 groups, the last holds one block
+    (960, 128, "fp32", 1, 2),    # fp32 inputs, 15 groups
+    (1000, 64, "bf16", 1, 2),    # 16 groups, D = 64 (q pooled by the pooling pass)
+    (1024, 64, "bf16", 1, 6),    # six heads, D = 64, 16 full groups
+    (1857, 128, "bf16", 1, 2),   # 30 groups, two rows per wave (vector scores)
+    (1921, 128, "fp32", 1, 2),   # 32 groups, fp32 inputs
+    (2048, 64, "bf16", 1, 2),    # the longest rows of the two-launch path, D = 64
 ])
-def test_block_mask_row_lengths(orc, dev, nb, D, dtype, B):
+def test_block_mask_row_lengths(orc, dev, nb, D, dtype, B, h):
     """Rows of every column-group count of the selection kernel, each with a partial last
-    group, against the oracle estimator on every row (fractal-order call, band STA)."""
-    h, S = 2, nb * 64
+    group, against the oracle estimator on every row (fractal-order call, band STA), with
+    several head counts and batches on the two-launch path."""
+    S = nb * 64
     rng = np.random.default_rng(1000 + nb)
     # a shared direction per head plus noise: scores spread, so the cut moves between rows
     base = rng.standard_normal((1, 1, h, D)).astype(np.float32)
@@ -213,12 +218,12 @@ def test_block_mask_row_lengths(orc, dev, nb, D, dtype, B):
     ii = np.arange(nb)
     sta = (np.abs(ii[:, None] - ii[None, :]) <= 2).astype(np.uint8)
     for thr in (0.9, 0.5):
-        say("[mask-rows] nb", nb, "D", D, dtype, "B", B, "thr", thr)
+        say("[mask-rows] nb", nb, "D", D, dtype, "B", B, "heads", h, "thr", thr)
         kv_nb, kv_inds = nabla.nabla_block_mask(gq, gk, torch.from_numpy(sta).to(dev), thr)
         o = orc.block_mask(q, k, sta, thr)
         band = orc.band_rows(o["diag"], thr)
         compare_lists(kv_nb.cpu().numpy(), kv_inds.cpu().numpy(), o["kv_nb"], o["kv_inds"], band,
-                      "rows nb=%d D=%d %s thr=%g" % (nb, D, dtype, thr))
+                      "rows nb=%d D=%d %s h=%d thr=%g" % (nb, D, dtype, h, thr))
 
 
 def check_attention(got, want, label):
