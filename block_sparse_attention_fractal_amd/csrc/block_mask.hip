@@ -502,14 +502,7 @@ __device__ __forceinline__ void select_rows_body(const float *__restrict__ qa,
         for (int c = 0; c < CPT; ++c) {
             valid[c] = 64 * c + lane < nb;
             if constexpr (PH == 2) {
-                if constexpr (CPT > 16) {
-                    // every lane loads (the last column again past the row's end): no
-                    // branches (shorter rows keep the branch: the hoisted loads spill there)
-                    const float v = sbuf[row * nb + (valid[c] ? 64 * c + lane : nb - 1)];
-                    s[c] = valid[c] ? v : 0.0f;
-                } else {
-                    s[c] = valid[c] ? sbuf[row * nb + 64 * c + lane] : 0.0f;
-                }
+                s[c] = valid[c] ? sbuf[row * nb + 64 * c + lane] : 0.0f;
             } else {
                 float a = 0.0f;
 #pragma unroll
@@ -764,6 +757,303 @@ __global__ __launch_bounds__(256, 4) void select_rows_w4_kernel(NABLA_SELECT_ARG
 }
 #undef NABLA_SELECT_ARGS
 
+// ---- rows of 1025-2048 blocks (30 or 32 column groups) from the score buffer, split over WV
+// waves of one workgroup.  Wave v holds column groups CH v .. CH v + CH - 1; with WV = 2 and
+// CH = 15 or 16 (as select_rows_w4_kernel holds a whole row of up to 1024 blocks) a wave fits
+// in 128 registers and four waves per SIMD are resident, where a wave holding the whole row
+// needs about 236 registers and runs two per SIMD.  The waves meet in LDS around every
+// quantity of the whole row (extremes, Z, the histogram, the cut bin's members, the kept
+// counts), with a workgroup barrier in between; each decision is taken from the same shared
+// values in every wave, so all run the same path and the same barriers.  The arithmetic is
+// select_rows_body's, and so are the lists.
+template <int WV>
+struct SelectPairShared {
+    int64_t hm[kSelBins];  // the row's histogram masses
+    uint64_t lkey[64];     // keys and masses of the cut bin's members
+    int64_t lmass[64];
+    float fmax[WV], fmin[WV];
+    int64_t isum[WV];
+    uint64_t kext[WV][2];  // per wave: lowest and highest member key (or the arg-max key)
+    int cnt[WV];           // per wave: members of the cut bin
+    int kcnt[WV];          // per wave: kept blocks
+};
+
+// values read back from LDS are the same in every lane: readfirstlane makes them scalar, so that
+// every branch on them (and the barriers inside) is a uniform, scalar branch
+__device__ __forceinline__ int uni_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uni_u64(uint64_t v) {
+    return u64_of((uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v),
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ float uni_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+template <int CH, int WV>
+__global__ __launch_bounds__(64 * WV, 4) void select_pair_kernel(int nb,
+                                                             const uint8_t *__restrict__ sta,
+                                                             int64_t cut,
+                                                             int32_t *__restrict__ kv_nb,
+                                                             int32_t *__restrict__ kv_inds,
+                                                             const float *__restrict__ sbuf) {
+    static_assert(CH <= 32 && kSelBins == 256, "bit masks per column group; 4 bins per lane");
+    __shared__ SelectPairShared<WV> sp;
+    // sums over the waves of per-wave values in LDS: all, or those of the waves before this one
+    auto all_of = [&](const int *a) {
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < WV; ++w) t += a[w];
+        return t;
+    };
+    auto before = [&](const int *a, int v) {
+        int t = 0;
+#pragma unroll
+        for (int w = 0; w < WV; ++w) t += w < v ? a[w] : 0;
+        return t;
+    };
+    const int i = blockIdx.x, bh = blockIdx.y;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t row = (int64_t)bh * nb + i;
+    const uint64_t lanes_below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    auto col = [&](int c) { return 64 * (CH * wv + c) + lane; };
+
+    float s[CH];
+    bool valid[CH];
+    float smax = -INFINITY, smin = INFINITY;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        valid[c] = col(c) < nb;
+        s[c] = valid[c] ? sbuf[row * nb + col(c)] : 0.0f;
+        if (valid[c]) {
+            smax = fmaxf(smax, s[c]);
+            smin = fminf(smin, s[c]);
+        }
+    }
+    smax = wave_max_f32(smax);
+    smin = wave_min_f32(smin);
+    if (lane == 0) {
+        sp.fmax[wv] = smax;
+        sp.fmin[wv] = smin;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WV; ++w) {
+        smax = fmaxf(smax, sp.fmax[w]);
+        smin = fminf(smin, sp.fmin[w]);
+    }
+    smax = uni_f32(smax);
+    smin = uni_f32(smin);
+    auto key_of = [&](int c) -> uint64_t {
+        return ((uint64_t)f32_orderable(s[c]) << 12) | (uint64_t)col(c);
+    };
+
+    // weights on the 2^-48 grid: Z from the exact integer sum over both halves
+    int64_t P[CH];
+    {
+        float e[CH];
+        int64_t es = 0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            e[c] = nabla_exp(valid[c] ? s[c] - smax : -INFINITY);  // 0 off the row
+            es += fix48(e[c]);
+        }
+        es = wave_sum_i64(es);
+        if (lane == 0) sp.isum[wv] = es;
+        __syncthreads();
+        es = 0;
+#pragma unroll
+        for (int w = 0; w < WV; ++w) es += sp.isum[w];
+        es = (int64_t)uni_u64((uint64_t)es);
+        const float Z = (float)(double)es * 0x1p-48f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) P[c] = fix48(e[c] / Z);
+    }
+
+    // One histogram pass over the members (inr) of both waves into the shared bins (bin_of):
+    // the bin holding the cut (-1 if the members' mass stays below it), the mass before it, the
+    // members of that bin in both waves, and this wave's member bits.
+    auto hist_pass = [&](auto inr, auto bin_of, int64_t below, int64_t &bbelow, int &bcnt,
+                         uint32_t &fbits) -> int {
+        for (int t = threadIdx.x; t < kSelBins; t += 64 * WV) sp.hm[t] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const bool in = inr(c);
+            const int bn = in ? bin_of(c) : 0;
+            atomicAdd((unsigned long long *)&sp.hm[bn], (unsigned long long)(in ? P[c] : 0));
+        }
+        __syncthreads();
+        // every wave scans all bins (lane l: bins 4l .. 4l + 3) and finds the same bin
+        int64_t m[kSelBins / 64];
+        int64_t tot = 0;
+#pragma unroll
+        for (int q = 0; q < kSelBins / 64; ++q) {
+            m[q] = sp.hm[lane * (kSelBins / 64) + q];
+            tot += m[q];
+        }
+        int64_t run = below + wave_incl_scan_i64(tot, lane) - tot;
+        int found = -1;
+        int64_t fb = 0;
+#pragma unroll
+        for (int q = 0; q < kSelBins / 64; ++q) {
+            if (found < 0 && run < cut && run + m[q] >= cut) {
+                found = lane * (kSelBins / 64) + q;
+                fb = run;
+            }
+            run += m[q];
+        }
+        const uint64_t bal = __ballot(found >= 0);
+        if (bal == 0ull) return -1;  // the same in both waves
+        const int src = __builtin_ctzll(bal);
+        bbelow = (int64_t)shfl_u64((uint64_t)fb, src);
+        const int fbin = __builtin_amdgcn_readlane(found, src);
+        fbits = 0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) fbits |= (inr(c) && bin_of(c) == fbin ? 1u : 0u) << c;
+        int n = 0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) n += __popcll(__ballot((fbits >> c) & 1u));
+        if (lane == 0) sp.cnt[wv] = n;
+        __syncthreads();
+        bcnt = uni_i32(all_of(sp.cnt));
+        return fbin;
+    };
+    // Exact rank of the at most 64 members (bits mb) of the last pass's bin: wave 0's first,
+    // then wave 1's; the smallest key whose prefix reaches the cut.
+    auto rank_list = [&](uint32_t mb, int64_t below) -> uint64_t {
+        int n = uni_i32(before(sp.cnt, wv));
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const bool in = (mb >> c) & 1u;
+            const uint64_t bal = __ballot(in);
+            if (in) {
+                const int pos = n + __popcll(bal & lanes_below);
+                sp.lkey[pos] = key_of(c);
+                sp.lmass[pos] = P[c];
+            }
+            n += __popcll(bal);
+        }
+        __syncthreads();
+        const int total = uni_i32(all_of(sp.cnt));
+        uint64_t best = ~0ull;
+        if (lane < total) {
+            const uint64_t k0 = sp.lkey[lane];
+            int64_t pre = sp.lmass[lane];
+#pragma unroll 8
+            for (int m2 = 0; m2 < total; ++m2) pre += sp.lkey[m2] < k0 ? sp.lmass[m2] : 0;
+            if (below + pre >= cut) best = k0;
+        }
+        return wave_min_u64(best);
+    };
+
+    uint64_t T = 0;  // cut <= 0: every block is kept
+    if (cut > 0) {
+        const float range = smax - smin;
+        const float scale = range > 1e-30f ? (float)kSelBins / range : 0.0f;
+        uint32_t bpk[(CH + 3) / 4];  // the bins, as bytes (0 off the row)
+#pragma unroll
+        for (int u = 0; u < (CH + 3) / 4; ++u) bpk[u] = 0;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int bi = (int)((s[c] - smin) * scale);
+            const uint32_t bc = valid[c] ? (uint32_t)(bi > kSelBins - 1 ? kSelBins - 1 : bi) : 0u;
+            bpk[c >> 2] |= bc << (8 * (c & 3));
+        }
+        auto bin_f = [&](int c) -> int { return (int)((bpk[c >> 2] >> (8 * (c & 3))) & 0xffu); };
+        int64_t below = 0;
+        int cnt = 0;
+        uint32_t inb = 0;
+        const int b = hist_pass([&](int c) { return valid[c]; }, bin_f, 0, below, cnt, inb);
+        if (b < 0) {  // total mass below the cut: only the arg-max (largest key) stays
+            uint64_t km = 0;
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                if (valid[c]) km = key_of(c) > km ? key_of(c) : km;
+            km = wave_max_u64(km);
+            if (lane == 0) sp.kext[wv][1] = km;
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < WV; ++w) T = sp.kext[w][1] > T ? sp.kext[w][1] : T;
+            T = uni_u64(T);
+        } else if (cnt <= 64) {
+            T = rank_list(inb, below);
+        } else {
+            // many keys share the bin: narrow its key range by histogram passes
+            uint64_t lo = ~0ull, hi = 0;
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                if ((inb >> c) & 1u) {
+                    const uint64_t kk = key_of(c);
+                    lo = kk < lo ? kk : lo;
+                    hi = kk > hi ? kk : hi;
+                }
+            lo = wave_min_u64(lo);
+            hi = wave_max_u64(hi);
+            if (lane == 0) {
+                sp.kext[wv][0] = lo;
+                sp.kext[wv][1] = hi;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int w = 0; w < WV; ++w) {
+                lo = sp.kext[w][0] < lo ? sp.kext[w][0] : lo;
+                hi = sp.kext[w][1] > hi ? sp.kext[w][1] : hi;
+            }
+            lo = uni_u64(lo);
+            hi = uni_u64(hi);
+            for (;;) {
+                const uint64_t span = hi - lo;
+                const int shift = span < (uint64_t)kSelBins ? 0 : 64 - __clzll((long long)span) - 8;
+                int64_t b2below = 0;
+                int c2 = 0;
+                uint32_t inb2 = 0;
+                const int b2 = hist_pass(
+                    [&](int c) {
+                        const uint64_t kk = key_of(c);
+                        return valid[c] && kk >= lo && kk <= hi;
+                    },
+                    [&](int c) { return (int)((key_of(c) - lo) >> shift); }, below, b2below, c2,
+                    inb2);
+                if (b2 < 0) {  // not reached: the range holds the cut by construction
+                    T = lo;
+                    break;
+                }
+                if (c2 <= 64 || shift == 0) {
+                    T = rank_list(inb2, b2below);
+                    break;
+                }
+                const uint64_t nlo = lo + ((uint64_t)b2 << shift);
+                const uint64_t nhi0 = nlo + ((1ull << shift) - 1);
+                lo = nlo;
+                hi = nhi0 < hi ? nhi0 : hi;
+                below = b2below;
+            }
+        }
+    }
+
+    // kept = key >= T, or the STA window; kv_inds ascending: wave 0's columns, then wave 1's
+    uint32_t kbits = 0;
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const bool kept =
+            valid[c] && (key_of(c) >= T || (sta != nullptr && sta[(int64_t)i * nb + col(c)] != 0));
+        kbits |= (kept ? 1u : 0u) << c;
+        n += __popcll(__ballot(kept));
+    }
+    if (lane == 0) sp.kcnt[wv] = n;
+    __syncthreads();
+    int base = uni_i32(before(sp.kcnt, wv));
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        const bool kept = (kbits >> c) & 1u;
+        const uint64_t bal = __ballot(kept);
+        if (kept) kv_inds[row * nb + base + __popcll(bal & lanes_below)] = col(c);
+        base += __popcll(bal);
+    }
+    if (threadIdx.x == 0) kv_nb[row] = all_of(sp.kcnt);
+}
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---- block scores as a tiled product (the two-launch path, rows of 513-2048 blocks).
@@ -942,6 +1232,8 @@ __global__ __launch_bounds__(512) void select_kernel(const float *__restrict__ q
             kmin = sh.red_min[w] < kmin ? sh.red_min[w] : kmin;
             kmax = sh.red_max[w] > kmax ? sh.red_max[w] : kmax;
         }
+        kmin = uni_u64(kmin);
+        kmax = uni_u64(kmax);
         const float smax = f32_from_orderable((uint32_t)(kmax >> 12));
 
         // softmax weights on the 2^-48 grid
@@ -958,6 +1250,7 @@ __global__ __launch_bounds__(512) void select_kernel(const float *__restrict__ q
         int64_t ze = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) ze += sh.red_sum[w];
+        ze = (int64_t)uni_u64((uint64_t)ze);
         const float Z = (float)(double)ze * 0x1p-48f;
         int64_t P[CPT];
 #pragma unroll
@@ -1012,16 +1305,16 @@ __global__ __launch_bounds__(512) void select_kernel(const float *__restrict__ q
                     sh.sel_key = sh.hkey[found];
                 }
                 __syncthreads();
-                const int bsel = sh.sel_bin;
+                const int bsel = uni_i32(sh.sel_bin);
                 if (bsel < 0) {  // total mass below the cut: keep only the arg-max
                     T = kmax;
                     break;
                 }
-                if (sh.sel_cnt == 1 || shift == 0) {
-                    T = sh.sel_key;
+                if (uni_i32(sh.sel_cnt) == 1 || shift == 0) {
+                    T = uni_u64(sh.sel_key);
                     break;
                 }
-                below = sh.sel_below;
+                below = (int64_t)uni_u64((uint64_t)sh.sel_below);
                 const uint64_t nlo = lo + ((uint64_t)bsel << shift);
                 const uint64_t nhi = nlo + ((1ull << shift) - 1);
                 lo = nlo;
@@ -1088,9 +1381,10 @@ static hipError_t launch_rows_t(const float *qa, const float *ka, int BH, int nb
 
 // Rows of 513-2048 blocks in two launches through the score buffer sbuf [BH][nb][nb]: the
 // scores as a tiled matrix-core product of the pooled q and k (scores_kernel), then the
-// selection, one row per wave.  Without the score accumulators and staged k columns of the
-// fused kernel, the selection keeps four waves per SIMD resident (rows of up to 16 column
-// groups) to hide the latency of its reductions, LDS histograms and ballots.
+// selection, one row per wave up to 16 column groups and one row per pair of waves beyond.
+// Without the score accumulators and staged k columns of the fused kernel, the selection
+// keeps four waves per SIMD resident to hide the latency of its reductions, LDS histograms
+// and ballots.
 template <int D, int CPT>
 static hipError_t launch_rows_split_t(const float *qa, const float *ka, int BH, int nb,
                                       const uint8_t *sta, float sqrt_d, int64_t cut,
@@ -1108,8 +1402,10 @@ static hipError_t launch_rows_split_t(const float *qa, const float *ka, int BH, 
                            NatGrid{}, sbuf);
         return hipGetLastError();
     } else {
-        return launch_rows_t<D, CPT, 1, false, 2>(qa, ka, BH, nb, sta, sqrt_d, cut, kv_nb,
-                                                  kv_inds, stream, QSource{}, sbuf);
+        // two waves per row, CPT / 2 column groups each
+        hipLaunchKernelGGL((select_pair_kernel<CPT / 2, 2>), dim3(nb, BH), dim3(128), 0, stream,
+                           nb, sta, cut, kv_nb, kv_inds, sbuf);
+        return hipGetLastError();
     }
 }
 

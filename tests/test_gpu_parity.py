@@ -185,6 +185,33 @@ def test_block_mask_uniform_ties(orc, dev):
         assert np.all(kv_nb.cpu().numpy() == want)
 
 
+@pytest.mark.parametrize("nb", [960, 1100, 1880])
+def test_block_mask_long_row_degenerate(orc, dev, nb):
+    """The degenerate selections on rows of one wave (960 blocks) and of a pair of waves (1100
+    and 1880 blocks): Q = 0 (every score 0: one histogram bin, the order decided by the index
+    tie-break through the refinement passes), thr = 0 (only the arg-max and the band) and
+    thr = 1 (every block), against the oracle on every row."""
+    B, h, D = 1, 2, 128
+    S = nb * 64
+    rng = np.random.default_rng(40 + nb)
+    k = synth.round_bf16(rng.standard_normal((B, S, h, D)).astype(np.float32))
+    q = synth.round_bf16(rng.standard_normal((B, S, h, D)).astype(np.float32))
+    ii = np.arange(nb)
+    sta = (np.abs(ii[:, None] - ii[None, :]) <= 1).astype(np.uint8)
+    gk = torch.from_numpy(k).to(torch.bfloat16).to(dev)
+    gsta = torch.from_numpy(sta).to(dev)
+    for label, qq, thr, st in (("ties", np.zeros_like(q), 0.9, None), ("thr0", q, 0.0, sta),
+                               ("thr1", q, 1.0, None)):
+        say("[mask-degenerate] nb", nb, label)
+        gq = torch.from_numpy(qq).to(torch.bfloat16).to(dev)
+        kv_nb, kv_inds = nabla.nabla_block_mask(gq, gk, None if st is None else gsta, thr)
+        o = orc.block_mask(qq, k, st, thr)
+        compare_lists(kv_nb.cpu().numpy(), kv_inds.cpu().numpy(), o["kv_nb"], o["kv_inds"],
+                      orc.band_rows(o["diag"], thr), "degenerate nb=%d %s" % (nb, label))
+        if label == "thr1":
+            assert np.all(kv_nb.cpu().numpy() == nb)
+
+
 # ------------------------------------------------------------------ attention
 @pytest.mark.parametrize("nb,D,dtype,B,h", [
     (1, 128, "bf16", 1, 2),      # one column group, one block
@@ -197,9 +224,12 @@ def test_block_mask_uniform_ties(orc, dev):
     (960, 128, "fp32", 1, 2),    # fp32 inputs, 15 groups
     (1000, 64, "bf16", 1, 2),    # 16 groups, D = 64 (q pooled by the pooling pass)
     (1024, 64, "bf16", 1, 6),    # six heads, D = 64, 16 full groups
-    (1857, 128, "bf16", 1, 2),   # 30 groups, two rows per wave (vector scores)
+    (1025, 128, "bf16", 1, 2),   # 32 groups over a pair of waves: the second wave holds one block
+    (1857, 128, "bf16", 1, 2),   # 30 groups, 15 per wave of the pair
     (1921, 128, "fp32", 1, 2),   # 32 groups, fp32 inputs
-    (2048, 64, "bf16", 1, 2),    # the longest rows of the two-launch path, D = 64
+    (2048, 64, "bf16", 2, 3),    # the longest rows of the two-launch path, D = 64, (b, head) offsets
+    (2049, 128, "bf16", 1, 2),   # rows of more than 2048 blocks: one workgroup of eight waves per row
+    (4096, 64, "fp32", 1, 1),    # the longest rows the estimator takes
 ])
 def test_block_mask_row_lengths(orc, dev, nb, D, dtype, B, h):
     """Rows of every column-group count of the selection kernel, each with a partial last
