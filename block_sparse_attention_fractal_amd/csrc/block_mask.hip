@@ -37,9 +37,10 @@
 //                       keys (orderable(s) << 12 | j) with exact integer masses, the STA
 //                       union and a ballot compaction of the kept indices.
 //   scores_kernel +     rows of 513-2048 blocks: the scores as a tiled product into a
-//   select_rows_w4      workspace buffer, then the same selection one row per wave, four
-//                       waves per SIMD.
-//   select_kernel       rows of more than 2048 blocks: one workgroup per row group.
+//   select_rows_w4 /    workspace buffer, then the same selection, four waves per SIMD:
+//   select_pair         one row per wave up to 1024 blocks, one row per pair of waves
+//                       beyond (the waves meet in LDS around each row-wide quantity).
+//   select_kernel       rows of more than 2048 blocks: a workgroup of eight waves per row.
 #include "nabla_device.h"
 #include "nabla_launch.h"
 
