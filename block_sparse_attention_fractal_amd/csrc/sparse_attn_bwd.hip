@@ -42,8 +42,26 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// 16-byte chunk swizzle of the tiles in LDS.  Each tile is read two ways: as rows (16 bytes
+// per lane, rfrag: the 16 lanes of a cycle take 16 rows with distinct row % 16) and
+// transposed (8 bytes per lane, tfrag: the 32 lanes of a cycle take 4 rows R .. R + 3,
+// R % 4 = 0, times chunks 4 t .. 4 t + 3, in two half chunks).  On the 64 four-byte banks
+// both are free of conflicts when the swizzle is a bijection on row % 16 (rows) and sends
+// the row bits that vary inside a transposed read to the chunk bits that do not:
+//   CH = 16 (256-byte rows): bits 0-1 of the row to bits 2-3 of the chunk, bits 2-3 to 0-1;
+//   CH = 8 (128-byte rows, two per bank line): row bit 1 to chunk bit 2, bits 2-3 to 0-1.
+// (The forward's row swizzle, row % CH, makes the transposed reads 4-way conflicted.)
+template <int CH>
+__device__ __forceinline__ int bswz(int row) {
+    static_assert(CH == 16 || CH == 8, "D = 128 or 64");
+    if constexpr (CH == 16)
+        return ((row & 3) << 2) | ((row >> 2) & 3);
+    else
+        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
 // Transposing read of a bf16 tile in LDS (rows of ROWB bytes, 16-byte chunks XOR-swizzled
-// by kswz): the A operand [32 (d) x 16 (rows)] of k-step kk = 2 mt + p, output d tile dt,
+// by bswz): the A operand [32 (d) x 16 (rows)] of k-step kk = 2 mt + p, output d tile dt,
 // i.e. lane l gets tile[32 mt + 16 p + 8 (l / 32) + 0..7][32 dt + l % 32].
 template <int D>
 __device__ __forceinline__ bf16x8 tfrag(const char *tb, int lane, int dt, int kk) {
@@ -54,7 +72,7 @@ __device__ __forceinline__ bf16x8 tfrag(const char *tb, int lane, int dt, int kk
     for (int r = 0; r < 2; ++r) {
         const int row = 32 * mt + 16 * p + 8 * (g16 >> 1) + 4 * r + (sl >> 2);
         const int d = 32 * dt + 16 * (g16 & 1) + 4 * (sl & 3);
-        const int c = (d >> 3) ^ kswz<CH>(row);
+        const int c = (d >> 3) ^ bswz<CH>(row);
         const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
             (NABLA_LDS bf16x4 *)(tb + row * ROWB + (c << 4) + (d & 7) * 2));
         a[4 * r + 0] = x[0];
@@ -71,12 +89,12 @@ template <int D>
 __device__ __forceinline__ bf16x8 rfrag(const char *tb, int row, int hi, int ks) {
     constexpr int CH = D / 8, ROWB = 2 * D;
     const int c = 2 * ks + hi;
-    return *reinterpret_cast<const bf16x8 *>(tb + row * ROWB + ((c ^ kswz<CH>(row)) << 4));
+    return *reinterpret_cast<const bf16x8 *>(tb + row * ROWB + ((c ^ bswz<CH>(row)) << 4));
 }
 
 // Per-lane byte offsets (global side) of the 16-byte chunks this thread moves for one
 // 64-row tile: chunk e = r * 128 + tid lands at byte 16 e of the LDS tile, i.e. row e / CH,
-// position e % CH, so the lane fetches global chunk (e % CH) ^ kswz(row).
+// position e % CH, so the lane fetches global chunk (e % CH) ^ bswz(row).
 template <int D>
 __device__ __forceinline__ void tile_offsets(int tid, int64_t tok, uint32_t (&off)[kBlock * D / 8 / kBwdThreads]) {
     constexpr int CH = D / 8;
@@ -84,7 +102,7 @@ __device__ __forceinline__ void tile_offsets(int tid, int64_t tok, uint32_t (&of
     for (int r = 0; r < kBlock * CH / kBwdThreads; ++r) {
         const int e = r * kBwdThreads + tid;
         const int row = e / CH, cpos = e % CH;
-        off[r] = (uint32_t)((row * tok + 8 * (cpos ^ kswz<CH>(row))) * 2);
+        off[r] = (uint32_t)((row * tok + 8 * (cpos ^ bswz<CH>(row))) * 2);
     }
 }
 
