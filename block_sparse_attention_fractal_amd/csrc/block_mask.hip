@@ -779,8 +779,9 @@ struct SelectPairShared {
     int kcnt[WV];          // per wave: kept blocks
 };
 
-// values read back from LDS are the same in every lane: readfirstlane makes them scalar, so that
-// every branch on them (and the barriers inside) is a uniform, scalar branch
+// Values the waves read back from LDS (or combine from it) are the same in every lane of a wave:
+// readfirstlane makes them scalar, so that every branch on them, and the barriers inside such
+// branches, is a uniform scalar branch.
 __device__ __forceinline__ int uni_i32(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ uint64_t uni_u64(uint64_t v) {
     return u64_of((uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v),
@@ -791,12 +792,9 @@ __device__ __forceinline__ float uni_f32(float v) {
 }
 
 template <int CH, int WV>
-__global__ __launch_bounds__(64 * WV, 4) void select_pair_kernel(int nb,
-                                                             const uint8_t *__restrict__ sta,
-                                                             int64_t cut,
-                                                             int32_t *__restrict__ kv_nb,
-                                                             int32_t *__restrict__ kv_inds,
-                                                             const float *__restrict__ sbuf) {
+__global__ __launch_bounds__(64 * WV, 4) void select_pair_kernel(
+    int nb, const uint8_t *__restrict__ sta, int64_t cut, int32_t *__restrict__ kv_nb,
+    int32_t *__restrict__ kv_inds, const float *__restrict__ sbuf) {
     static_assert(CH <= 32 && kSelBins == 256, "bit masks per column group; 4 bins per lane");
     __shared__ SelectPairShared<WV> sp;
     // sums over the waves of per-wave values in LDS: all, or those of the waves before this one
