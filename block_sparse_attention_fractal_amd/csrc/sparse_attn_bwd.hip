@@ -580,6 +580,270 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dkdv_kernel(
     store_rowT<D>(dv + head0 + (int64_t)ktok * tok, dva, hi, vmul);
 }
 
+// ---- dk, dv at D = 128 with 16 keys per wave.  One workgroup of 4 waves per kv block j of
+// (b, h); wave w owns keys 16 w .. 16 w + 15, lane (jl, g) = (l % 16, l / 16) key 16 w + jl.
+// The products run on v_mfma_f32_16x16x32_bf16, whose lane layout (checked on the GPU against
+// a CPU product) is: A [16 x 32]: lane i + 16 g holds row i, k = 8 g .. 8 g + 7; B [32 x 16]:
+// lane n + 16 g holds k = 8 g .. 8 g + 7 of column n; D [16 x 16]: lane n + 16 g holds rows
+// 4 g .. 4 g + 3 of column n.  A wave then needs about 200 registers (dK^T and dV^T for 16
+// keys, K and V as B operands), so two workgroups, 8 waves, two per SIMD, are resident on a
+// CU where the 32-key kernel runs one wave per SIMD and leaves the SIMD idle whenever that
+// wave waits.  The arithmetic per (query, key) is the 32-key kernel's.
+constexpr int kDkdv16Threads = 256;
+
+// Query of A-operand row m (0..63) of the S and dP products.  Output register r of lane
+// (n, g) in query m-tile mt is then query 32 (mt / 2) + 8 g + 4 (mt % 2) + r: m-tiles 2 kq and
+// 2 kq + 1 give each lane the 8 consecutive queries 32 kq + 8 g + 0..7 that the B operand of
+// the products over queries needs, with no data movement.
+__device__ __forceinline__ int pi16(int m) {
+    const int mt = m >> 4, g = (m >> 2) & 3, r = m & 3;
+    return 32 * (mt >> 1) + 8 * g + 4 * (mt & 1) + r;
+}
+// 16-byte chunk swizzle of this kernel's Q and dO tiles (256-byte rows).  Its row reads take
+// the 16 rows pi16(16 mt + 0..15), which differ in row bits 0, 1, 3 and 4; its transposed
+// reads take rows R + 8 g + 0..3 (bits 0, 1 within a lane group g, bits 3, 4 across groups)
+// times two chunks 2c, 2c + 1.  Row bit 0 goes to chunk bits 0 and 1, bit 1 to bit 2, bit 3
+// to bit 3 and bit 4 to bits 0 and 3.  Both patterns then cover the 64 four-byte banks once
+// per cycle whether a cycle serves consecutive lanes (16 for 16-byte reads, 32 for 8-byte
+// reads) or lanes l and l + 32 together (a CPU model checks all four cases).  The swizzle
+// does not depend on row bits 2 and 5, so a lane's addresses for m-tiles (row reads) and for
+// k-steps and halves (transposed reads) differ by constants.
+__device__ __forceinline__ int sw16(int row) {
+    return ((row & 1) ? 3 : 0) ^ (((row >> 1) & 1) << 2) ^ (((row >> 3) & 1) << 3) ^
+           (((row >> 4) & 1) ? 9 : 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool kPad>
+__global__ __launch_bounds__(kDkdv16Threads, 2) void bwd_dkdv16_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
+    bf16 *__restrict__ dk, bf16 *__restrict__ dv, int S, int heads,
+    const int32_t *__restrict__ q_nb, const int32_t *__restrict__ q_inds,
+    const int32_t *__restrict__ order, float scale, float scale_log2, int Ht, int Wt, int Hv,
+    int Wv) {
+    constexpr int D = 128, CH = D / 8, KS = D / 32, MD = D / 16;
+    constexpr int CPT = kBlock * CH / kDkdv16Threads;  // 16-byte chunks per thread and tile
+    constexpr int ROWB = 2 * D;
+    __shared__ __attribute__((aligned(1024))) bf16 qsh[2][kBlock * D];
+    __shared__ __attribute__((aligned(1024))) bf16 dsh[2][kBlock * D];
+    __shared__ __attribute__((aligned(16))) float lsh[2][kBlock];  // -lse (log2 units)
+    __shared__ __attribute__((aligned(16))) float esh[2][kBlock];  // -Delta
+
+    const int nb = S / kBlock;
+    const int64_t row = order[blockIdx.x];  // longest lists first, within phases of heads
+    const int bh = (int)(row / nb), j = (int)(row % nb);
+    const int b = bh / heads, h = bh % heads;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, jl = lane & 15, g = lane >> 4;
+    const int64_t tok = (int64_t)heads * D;
+    const int64_t head0 = (int64_t)b * S * tok + (int64_t)h * D;
+    const int ktok = j * kBlock + 16 * w + jl;
+    const int n = clamp_count(q_nb[row], nb);
+    const int32_t *list = q_inds + row * nb;
+
+    // K (times scale * log2 e) and V as B operands: lane (jl, g) holds d = 32 ks + 8 g + 0..7
+    bf16x8 kf[KS], vf[KS];
+    {
+        const bf16 *kr = k + head0 + (int64_t)ktok * tok + 8 * g;
+        const bf16 *vr = v + head0 + (int64_t)ktok * tok + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 x = load8_bf16(kr + 32 * ks);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kf[ks][e] = (bf16)((float)x[e] * scale_log2);
+            vf[ks] = load8_bf16(vr + 32 * ks);
+        }
+    }
+
+    // chunk e = r * 256 + tid of a tile lands at LDS byte 16 e (row e / CH, position e % CH)
+    // and holds global chunk (e % CH) ^ sw16(row)
+    uint32_t off[CPT];
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+        const int e = r * kDkdv16Threads + tid;
+        const int rr = e / CH, cpos = e % CH;
+        off[r] = (uint32_t)((rr * tok + 8 * (cpos ^ sw16(rr))) * 2);
+    }
+    const uint32_t ldq = __builtin_amdgcn_readfirstlane(lds_offset(qsh[0]) + w * 64 * 16);
+    const uint32_t ldd = __builtin_amdgcn_readfirstlane(lds_offset(dsh[0]) + w * 64 * 16);
+    float stash = 0.0f;  // thread t < 64: -lse of row t of the next tile; 64 <= t < 128: -Delta
+    auto issue = [&](int ii, int stage) {
+        const int i = __builtin_amdgcn_readfirstlane(clamp_block(ii, nb));
+        const bf16 *qb = q + head0 + (int64_t)i * kBlock * tok;
+        const bf16 *db = dout + head0 + (int64_t)i * kBlock * tok;
+#pragma unroll
+        for (int r = 0; r < CPT; ++r) {
+            const uint32_t sb = stage * (kBlock * D * 2) + r * kDkdv16Threads * 16;
+            lds_direct16_sv(qb, off[r], ldq + sb);
+            lds_direct16_sv(db, off[r], ldd + sb);
+        }
+        if (tid < 128) {
+            const int64_t rr = (int64_t)bh * S + (int64_t)i * kBlock + (tid & 63);
+            stash = -(tid < 64 ? lse[rr] * kLog2e : delta[rr]);
+        }
+    };
+    auto land = [&](int stage) {  // after vm_wait: the row statistics into LDS
+        if (tid < 64)
+            lsh[stage][tid] = stash;
+        else if (tid < 128)
+            esh[stage][tid - 64] = stash;
+    };
+
+    f32x4 dka[MD], dva[MD];
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+        dka[md] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        dva[md] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // This lane's LDS byte offsets within a tile.  Row reads: row pi16(16 mt + jl) =
+    // rr0 + 32 (mt / 2) + 4 (mt % 2), chunk (4 ks + g) ^ sw16(rr0).  Transposed reads: row
+    // rt0 + 32 kq + 4 hh, chunk (2 md + (jl % 4) / 2) ^ sw16(rt0), byte 8 (jl % 2) in it.
+    const int rr0 = pi16(jl), rt0 = 8 * g + (jl >> 2);
+    uint32_t offr[KS], offt[MD];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        offr[ks] = (uint32_t)(rr0 * ROWB + (((4 * ks + g) ^ sw16(rr0)) << 4));
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+        offt[md] = (uint32_t)(rt0 * ROWB + (((2 * md + ((jl & 3) >> 1)) ^ sw16(rt0)) << 4) +
+                              8 * (jl & 1));
+    const int q0l = 8 * g;  // queries 32 (mt / 2) + 8 g + 4 (mt % 2) + 0..3 of S's registers
+
+    // one tile in LDS stage ST (a constant, so that every LDS address is a lane offset plus
+    // an immediate)
+    auto tile = [&](auto stc, int u) {
+        constexpr int ST = decltype(stc)::value;
+        if (u + 1 < n) issue(list[u + 1], ST ^ 1);
+        const char *qb = reinterpret_cast<const char *>(qsh[ST]);
+        const char *db = reinterpret_cast<const char *>(dsh[ST]);
+        // S - lse (log2 units) and dP - Delta for this wave's keys: the accumulators start at
+        // minus the statistics of their queries
+        f32x4 sacc[4], pacc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int q0 = q0l + 32 * (mt >> 1) + 4 * (mt & 1);
+            const float4 l4 = *reinterpret_cast<const float4 *>(&lsh[ST][q0]);
+            const float4 e4 = *reinterpret_cast<const float4 *>(&esh[ST][q0]);
+            sacc[mt] = f32x4{l4.x, l4.y, l4.z, l4.w};
+            pacc[mt] = f32x4{e4.x, e4.y, e4.z, e4.w};
+        }
+        // the row fragments of k-step ks + 1 are read under the MFMAs of k-step ks
+        bf16x8 fq[2][4], fd[2][4];
+        auto rread = [&](int ks) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int ro = (32 * (mt >> 1) + 4 * (mt & 1)) * ROWB;
+                fq[ks & 1][mt] = *reinterpret_cast<const bf16x8 *>(qb + ro + offr[ks]);
+                fd[ks & 1][mt] = *reinterpret_cast<const bf16x8 *>(db + ro + offr[ks]);
+            }
+        };
+        rread(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) rread(ks + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                sacc[mt] = mfma16(fq[ks & 1][mt], kf[ks], sacc[mt]);
+                pacc[mt] = mfma16(fd[ks & 1][mt], vf[ks], pacc[mt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // P and dS = P (dP - Delta), packed as the B operands of the two k-steps over the
+        // tile's queries (k-step kq: queries 32 kq + 8 g + 0..7 = m-tiles 2 kq, 2 kq + 1)
+        bf16x8 pp[2], dd[2];
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+            for (int hm = 0; hm < 2; ++hm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float pr = __builtin_amdgcn_exp2f(sacc[2 * kq + hm][r]);
+                    pp[kq][4 * hm + r] = (bf16)pr;
+                    dd[kq][4 * hm + r] = (bf16)(pr * pacc[2 * kq + hm][r]);
+                }
+        // dV^T += dO^T P and dK^T += Q^T dS: the A operands are transposing reads, lane
+        // (jl, g) getting column d = 16 md + jl of rows 32 kq + 8 g + 0..7
+        // the transposed fragments of d tile md + 1 are read under the MFMAs of d tile md
+        bf16x8 at_d[2][2], at_q[2][2];
+        auto tread = [&](int md) {
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int ro = (32 * kq + 4 * hh) * ROWB;
+                    const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (NABLA_LDS bf16x4 *)(db + ro + offt[md]));
+                    const bf16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (NABLA_LDS bf16x4 *)(qb + ro + offt[md]));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        at_d[md & 1][kq][4 * hh + e] = x[e];
+                        at_q[md & 1][kq][4 * hh + e] = y[e];
+                    }
+                }
+        };
+        tread(0);
+#pragma unroll
+        for (int md = 0; md < MD; ++md) {
+            if (md + 1 < MD) tread(md + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kq = 0; kq < 2; ++kq) {
+                dva[md] = mfma16(at_d[md & 1][kq], pp[kq], dva[md]);
+                dka[md] = mfma16(at_q[md & 1][kq], dd[kq], dka[md]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        vm_wait<0>();
+        if (u + 1 < n) land(ST ^ 1);
+        __syncthreads();  // tile u + 1 has landed; everyone is done with tile u's stage
+    };
+
+    if (n > 0) {
+        issue(list[0], 0);
+        vm_wait<0>();
+        land(0);
+    }
+    __syncthreads();
+    for (int u = 0; u < n; u += 2) {
+        tile(std::integral_constant<int, 0>{}, u);
+        if (u + 1 < n) tile(std::integral_constant<int, 1>{}, u + 1);
+    }
+    float kmul = scale, vmul = 1.0f;
+    if constexpr (kPad) {
+        // this lane's key (16 w + jl of block j) at a padding position: dk = dv = 0
+        int vr, vc;
+        patch_extent(j, Ht, Wt, Hv, Wv, vr, vc);
+        const int key = 16 * w + jl;
+        if (!((key >> 3) < vr && (key & 7) < vc)) {
+#pragma unroll
+            for (int md = 0; md < MD; ++md) {
+                dka[md] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                dva[md] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            kmul = 0.0f;
+            vmul = 0.0f;
+        }
+    }
+    // lane (jl, g) holds d = 16 md + 4 g + 0..3 of its key: 8-byte runs of the key's row
+    bf16 *dkr = dk + head0 + (int64_t)ktok * tok + 4 * g;
+    bf16 *dvr = dv + head0 + (int64_t)ktok * tok + 4 * g;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+        bf16x4 xk, xv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            xk[r] = (bf16)(dka[md][r] * kmul);
+            xv[r] = (bf16)(dva[md][r] * vmul);
+        }
+        *reinterpret_cast<bf16x4 *>(dkr + 16 * md) = xk;
+        *reinterpret_cast<bf16x4 *>(dvr + 16 * md) = xv;
+    }
+}
+
 // ---- host side
 
 // Workspace: [Delta: B*heads*S fp32 | q_nb: B*heads*nb | q_inds: B*heads*nb*nb int32 |
@@ -641,9 +905,14 @@ static hipError_t launch_bwd_t(const bf16 *q, const bf16 *k, const bf16 *v, cons
     hipLaunchKernelGGL((bwd_dq_kernel<D, kPad>), dim3(rows), dim3(kBwdThreads), 0, stream, q, k,
                        v, dout, lse, delta, dq, S, heads, kv_nb, kv_inds, order_q, scale,
                        scale_log2, Ht, Wt, Hv, Wv);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kPad>), dim3(rows), dim3(kBwdThreads), 0, stream, q, k,
-                       v, dout, lse, delta, dk, dv, S, heads, q_nb, q_inds, order_k, scale,
-                       scale_log2, Ht, Wt, Hv, Wv);
+    if constexpr (D == 128)
+        hipLaunchKernelGGL((bwd_dkdv16_kernel<kPad>), dim3(rows), dim3(kDkdv16Threads), 0, stream,
+                           q, k, v, dout, lse, delta, dk, dv, S, heads, q_nb, q_inds, order_k,
+                           scale, scale_log2, Ht, Wt, Hv, Wv);
+    else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, kPad>), dim3(rows), dim3(kBwdThreads), 0, stream, q,
+                           k, v, dout, lse, delta, dk, dv, S, heads, q_nb, q_inds, order_k, scale,
+                           scale_log2, Ht, Wt, Hv, Wv);
     return hipGetLastError();
 }
 
