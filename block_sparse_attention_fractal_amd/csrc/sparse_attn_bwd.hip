@@ -9,14 +9,17 @@
 //   P  = exp(scale q k^T - lse),   dP = dO V^T,   Delta = rowsum(dO * O)
 //   dS = P (dP - Delta),   dq = scale dS K,   dk = scale dS^T Q,   dv = P^T dO.
 //
-// Kernels (bf16 tensors, fp32 accumulation, v_mfma_f32_32x32x16_bf16):
+// Kernels (bf16 tensors, fp32 accumulation):
 //   bwd_delta_kernel          Delta per (b, h, token) from the stored O and dO.
 //   bwd_tlist_*               transposed lists: for kv block j of (b, h), the query
 //                             blocks whose lists hold j, ascending.
 //   bwd_dq_kernel             one workgroup per query block walks its kv list:
-//                             S^T = K Q^T, dP^T = V dO^T, dS^T, dq^T += K^T dS^T.
-//   bwd_dkdv_kernel           one workgroup per kv block walks its query list:
-//                             S = Q K^T, dP = dO V^T, dS, dv^T += dO^T P, dk^T += Q^T dS.
+//                             S^T = K Q^T, dP^T = V dO^T, dS^T, dq^T += K^T dS^T
+//                             (v_mfma_f32_32x32x16_bf16, 32 rows per wave).
+//   bwd_dkdv16_kernel         D = 128: one workgroup per kv block walks its query list:
+//                             S = Q K^T, dP = dO V^T, dS, dv^T += dO^T P, dk^T += Q^T dS
+//                             (v_mfma_f32_16x16x32_bf16, 16 keys per wave, 2 waves per SIMD).
+//   bwd_dkdv_kernel           the same at D = 64 (32x32x16, 32 keys per wave).
 // Both gradient kernels recompute S and dP, so every output row is written once by one
 // workgroup in a fixed order: no atomics, and the results are deterministic.
 //
