@@ -236,7 +236,8 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
     for (;;) {
     if (tid == 0) sh.slot = atomicAdd(counter, 1);
     __syncthreads();
-    const int pos = sh.slot;
+    // the same in every lane: read as a scalar, so that the exit test is a scalar branch
+    const int pos = __builtin_amdgcn_readfirstlane(sh.slot);
     if (pos >= ngroups) break;
     const int grp = order[pos];
     const int bh = grp / groups_per_bh;
