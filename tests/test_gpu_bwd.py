@@ -98,13 +98,16 @@ def lse_check(got, want, label):
     assert np.all(got[~fin] == -np.inf), label
 
 
-@pytest.mark.parametrize("D,S,h,seed", [(128, 1024, 2, 31), (64, 1344, 3, 32), (128, 256, 1, 33)])
-def test_bwd_full_parity_random_lists(orc, dev, D, S, h, seed):
+@pytest.mark.parametrize("D,S,h,seed,B", [(128, 1024, 2, 31, 1), (64, 1344, 3, 32, 1),
+                                           (128, 256, 1, 33, 1), (128, 512, 3, 34, 2),
+                                           (64, 384, 2, 35, 2)])
+def test_bwd_full_parity_random_lists(orc, dev, D, S, h, seed, B):
     """Every lse, dq, dk, dv element against the oracle on random lists: ragged counts, any
-    order, one empty row, one row that lists every block."""
+    order, one empty row, one row that lists every block; batches of two give the (b, head)
+    offsets of every kernel."""
     rng = np.random.default_rng(seed)
-    B, nb = 1, S // 64
-    say("[bwd full] D=%d S=%d heads=%d seed=%d" % (D, S, h, seed))
+    nb = S // 64
+    say("[bwd full] B=%d D=%d S=%d heads=%d seed=%d" % (B, D, S, h, seed))
     arrs = [bf16_round(rng.standard_normal((B, S, h, D)).astype(np.float32)) for _ in range(4)]
     (q, tq), (k, tk), (v, tv), (do, tdo) = arrs
     kv_nb, kv_inds = random_lists(rng, B, h, nb, empty={(0, h - 1, nb // 2)}, full={(0, 0, 1)})
