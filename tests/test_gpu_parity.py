@@ -212,6 +212,33 @@ def test_block_mask_long_row_degenerate(orc, dev, nb):
             assert np.all(kv_nb.cpu().numpy() == nb)
 
 
+def test_block_mask_long_rows_repeatable(orc, dev):
+    """Rows of a pair of waves (1880 blocks) whose cut bins need refinement passes, five calls
+    in a row: the lists are the same on every call (the waves' decisions come from shared LDS
+    values around barriers).  Every kv block's tokens equal one of 8 vectors, so a row's
+    scores take 8 values and each of them is held by about 235 blocks (ties broken by index)."""
+    B, h, D, nb = 1, 4, 128, 1880
+    S = nb * 64
+    rng = np.random.default_rng(77)
+    kvec = synth.round_bf16(rng.standard_normal((8, h, D)).astype(np.float32))
+    k = np.ascontiguousarray(kvec[(np.arange(S) // 64) % 8][None])  # [1, S, h, D]
+    q = synth.round_bf16(rng.standard_normal((B, S, h, D)).astype(np.float32))
+    gq, gk = (torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in (q, k))
+    first = None
+    for rep in range(5):
+        kv_nb, kv_inds = nabla.nabla_block_mask(gq, gk, None, 0.9)
+        g_nb, g_inds = kv_nb.cpu().numpy(), kv_inds.cpu().numpy()
+        if first is None:
+            first = (g_nb, g_inds)
+            o = orc.block_mask(q, k, None, 0.9)
+            compare_lists(g_nb, g_inds, o["kv_nb"], o["kv_inds"], orc.band_rows(o["diag"], 0.9),
+                          "tied kv blocks nb=%d" % nb)
+            continue
+        same = rows_equal(g_nb, g_inds, *first)
+        say("[mask-repeat] call", rep, "differing rows", int((~same).sum()))
+        assert same.all(), "call %d: rows %s differ" % (rep, np.flatnonzero(~same)[:16].tolist())
+
+
 # ------------------------------------------------------------------ attention
 @pytest.mark.parametrize("nb,D,dtype,B,h", [
     (1, 128, "bf16", 1, 2),      # one column group, one block
