@@ -893,12 +893,13 @@ static hipError_t launch_bwd_t(const bf16 *q, const bf16 *k, const bf16 *v, cons
                        nb, tmat);
     hipLaunchKernelGGL(bwd_tlist_compact_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, tmat,
                        nb, (int64_t)rows, q_nb, q_inds);
-    // Launch orders: longest lists first within phases of a few heads (enough rows for
-    // three rounds of the resident workgroups), so that the long rows do not start last
-    // and the K/V (or Q/dO) tiles read together stay in the caches.
+    // Launch orders: longest lists first within phases of as few heads as give one round of
+    // the resident workgroups (one head at 720p), so that the long rows do not start last
+    // and the K/V (or Q/dO) tiles read together stay in the caches (A/B at 720p: phases of
+    // 1, 2, 3 and 5 heads 24.8, 25.6, 26.7 and 27.5 ms).
     const int resident = resident_workgroups<bwd_dq_kernel<D, kPad>>(kBwdThreads);
     if (resident <= 0) return hipErrorInvalidDevice;
-    int hpp = (3 * resident + nb - 1) / nb;
+    int hpp = (resident + nb - 1) / nb;
     hpp = hpp < 1 ? 1 : (hpp > (int)BH ? (int)BH : hpp);
     hipError_t e = launch_longest_first(kv_nb, (int)rows, hpp * nb, nb, order_q, stream);
     if (e != hipSuccess) return e;
