@@ -387,6 +387,161 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
     store_rowT<D>(dq + head0 + (int64_t)qtok * tok, acc, hi, scale);
 }
 
+// ---- dq at D = 128 with the keys of each tile split over waves.  One workgroup of 4 waves per
+// query block i: wave w takes rows 32 (w % 2) .. + 31 (lane (l32, hi): row 32 (w % 2) + l32) and
+// keys 32 (w / 2) .. + 31 of every listed tile, and accumulates its own part of dQ^T; the two
+// key halves' parts are added through LDS once per block, in a fixed order.  A wave holds half
+// the score accumulators and fragments of the 2-wave kernel: about 230 registers, so two
+// workgroups (two waves per SIMD) are resident on a CU, with the same LDS bytes per MFMA.
+constexpr int kDq4Threads = 256;
+
+template <bool kPad>
+__global__ __launch_bounds__(kDq4Threads, 2) void bwd_dq4_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const bf16 *__restrict__ dout, const float *__restrict__ lse, const float *__restrict__ delta,
+    bf16 *__restrict__ dq, int S, int heads, const int32_t *__restrict__ kv_nb,
+    const int32_t *__restrict__ kv_inds, const int32_t *__restrict__ order, float scale,
+    float scale_log2, int Ht, int Wt, int Hv, int Wv) {
+    constexpr int D = 128, KS = D / 16, DT = D / 32, CH = D / 8;
+    constexpr int CPT = kBlock * CH / kDq4Threads;
+    __shared__ __attribute__((aligned(1024))) bf16 ksh[2][kBlock * D];
+    __shared__ __attribute__((aligned(1024))) bf16 vsh[2][kBlock * D];
+
+    const int nb = S / kBlock;
+    const int64_t row = order[blockIdx.x];  // longest lists first, within phases of heads
+    const int bh = (int)(row / nb), i = (int)(row % nb);
+    const int b = bh / heads, h = bh % heads;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+    const int rh = w & 1, kh = w >> 1;  // row half, key half
+    const int64_t tok = (int64_t)heads * D;
+    const int64_t head0 = (int64_t)b * S * tok + (int64_t)h * D;
+    const int qtok = i * kBlock + 32 * rh + l32;
+    const int n = clamp_count(kv_nb[row], nb);
+    const int32_t *list = kv_inds + row * nb;
+
+    bf16x8 qf[KS], df[KS];
+    {
+        const bf16 *qr = q + head0 + (int64_t)qtok * tok + 8 * hi;
+        const bf16 *dr = dout + head0 + (int64_t)qtok * tok + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 x = load8_bf16(qr + 16 * ks);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)((float)x[e] * scale_log2);
+            df[ks] = load8_bf16(dr + 16 * ks);
+        }
+    }
+    const float lse2 = lse[(int64_t)bh * S + qtok] * kLog2e;
+    const float dl = delta[(int64_t)bh * S + qtok];
+
+    uint32_t off[CPT];
+#pragma unroll
+    for (int r = 0; r < CPT; ++r) {
+        const int e = r * kDq4Threads + tid;
+        const int rr = e / CH, cpos = e % CH;
+        off[r] = (uint32_t)((rr * tok + 8 * (cpos ^ bswz<CH>(rr))) * 2);
+    }
+    const uint32_t ldk = __builtin_amdgcn_readfirstlane(lds_offset(ksh[0]) + w * 64 * 16);
+    const uint32_t ldv = __builtin_amdgcn_readfirstlane(lds_offset(vsh[0]) + w * 64 * 16);
+    auto issue = [&](int jj, int stage) {
+        const int j = __builtin_amdgcn_readfirstlane(clamp_block(jj, nb));
+        const bf16 *kb = k + head0 + (int64_t)j * kBlock * tok;
+        const bf16 *vb = v + head0 + (int64_t)j * kBlock * tok;
+#pragma unroll
+        for (int r = 0; r < CPT; ++r) {
+            const uint32_t sb = stage * (kBlock * D * 2) + r * kDq4Threads * 16;
+            lds_direct16_sv(kb, off[r], ldk + sb);
+            lds_direct16_sv(vb, off[r], ldv + sb);
+        }
+    };
+
+    f32x16 acc[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = splat16(0.0f);
+
+    if (n > 0) issue(list[0], 0);
+    vm_wait<0>();
+    __syncthreads();
+    const int kvr = 32 * kh + sigma32(l32);  // this lane's key row in the S^T product
+    for (int u = 0; u < n; ++u) {
+        const int st = u & 1;
+        if (u + 1 < n) issue(list[u + 1], st ^ 1);
+        const char *kb = reinterpret_cast<const char *>(ksh[st]);
+        const char *vb = reinterpret_cast<const char *>(vsh[st]);
+        // S^T - lse and dP^T for this wave's 32 keys
+        f32x16 sacc = splat16(-lse2), pacc = splat16(-dl);
+        constexpr int KLA = 1;
+        bf16x8 fr[KLA + 1][2];
+        auto fread = [&](int ks) {
+            fr[ks & KLA][0] = rfrag<D>(kb, kvr, hi, ks);
+            fr[ks & KLA][1] = rfrag<D>(vb, kvr, hi, ks);
+        };
+#pragma unroll
+        for (int ks = 0; ks < KLA; ++ks) fread(ks);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + KLA < KS) fread(ks + KLA);
+            __builtin_amdgcn_sched_barrier(0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks & KLA][0], qf[ks], sacc, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[ks & KLA][1], df[ks], pacc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        bf16x8 kt[2][2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) kt[0][p] = tfrag<D>(kb, lane, 0, 2 * kh + p);
+        // dS^T = P^T (dP^T - Delta), packed: registers 8p .. 8p+7 = 16 consecutive keys
+        bf16x8 ds[2];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            ds[j >> 3][j & 7] = (bf16)(__builtin_amdgcn_exp2f(sacc[j]) * pacc[j]);
+        if constexpr (kPad) {
+            // a partial patch: its padding positions are not keys (register j holds key
+            // 32 kh + 16 (j / 8) + 8 hi + j % 8 of the block)
+            int vr, vc;
+            patch_extent(clamp_block(list[u], nb), Ht, Wt, Hv, Wv, vr, vc);
+            if (vr < kTile || vc < kTile) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = 32 * kh + 16 * (j >> 3) + 8 * hi + (j & 7);
+                    if (!((key >> 3) < vr && (key & 7) < vc)) ds[j >> 3][j & 7] = (bf16)0.0f;
+                }
+            }
+        }
+        // dQ^T += K^T dS^T over this wave's keys (k-steps 2 kh, 2 kh + 1)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            if (dt + 1 < DT) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) kt[(dt + 1) & 1][p] = tfrag<D>(kb, lane, dt + 1, 2 * kh + p);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) mfma_acc(acc[dt], kt[dt & 1][p], ds[p]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        vm_wait<0>();
+        __syncthreads();  // tile u + 1 has landed; everyone is done with tile u's stage
+    }
+    acc_settle(acc);
+    // the key half 1 waves hand their parts to the key half 0 waves through LDS (the ring is
+    // free: the walk ended with a barrier and no load is in flight)
+    float *part = reinterpret_cast<float *>(&ksh[0][0]) + (size_t)rh * (DT * 16 * 64);
+    if (kh == 1) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part[(dt * 16 + r) * 64 + lane] = acc[dt][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[dt][r] += part[(dt * 16 + r) * 64 + lane];
+        store_rowT<D>(dq + head0 + (int64_t)qtok * tok, acc, hi, scale);
+    }
+}
+
 // ---- dk, dv.  One workgroup (2 waves) per kv block j of (b, h); wave w owns keys 32 w ..
 // 32 w + 31, lane (l32, hi) key 32 w + l32.  Q and dO tiles of the query blocks that list
 // j go through a 2-stage LDS ring, with their rows' lse (log2 units) and Delta.
@@ -906,9 +1061,14 @@ static hipError_t launch_bwd_t(const bf16 *q, const bf16 *k, const bf16 *v, cons
     e = launch_longest_first(q_nb, (int)rows, hpp * nb, nb, order_k, stream);
     if (e != hipSuccess) return e;
     const float scale_log2 = scale * kLog2e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, kPad>), dim3(rows), dim3(kBwdThreads), 0, stream, q, k,
-                       v, dout, lse, delta, dq, S, heads, kv_nb, kv_inds, order_q, scale,
-                       scale_log2, Ht, Wt, Hv, Wv);
+    if constexpr (D == 128)
+        hipLaunchKernelGGL((bwd_dq4_kernel<kPad>), dim3(rows), dim3(kDq4Threads), 0, stream, q, k,
+                           v, dout, lse, delta, dq, S, heads, kv_nb, kv_inds, order_q, scale,
+                           scale_log2, Ht, Wt, Hv, Wv);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<D, kPad>), dim3(rows), dim3(kBwdThreads), 0, stream, q,
+                           k, v, dout, lse, delta, dq, S, heads, kv_nb, kv_inds, order_q, scale,
+                           scale_log2, Ht, Wt, Hv, Wv);
     if constexpr (D == 128)
         hipLaunchKernelGGL((bwd_dkdv16_kernel<kPad>), dim3(rows), dim3(kDkdv16Threads), 0, stream,
                            q, k, v, dout, lse, delta, dk, dv, S, heads, q_nb, q_inds, order_k,
