@@ -13,9 +13,11 @@
 //   bwd_delta_kernel          Delta per (b, h, token) from the stored O and dO.
 //   bwd_tlist_*               transposed lists: for kv block j of (b, h), the query
 //                             blocks whose lists hold j, ascending.
-//   bwd_dq_kernel             one workgroup per query block walks its kv list:
+//   bwd_dq4_kernel            D = 128: one workgroup per query block walks its kv list:
 //                             S^T = K Q^T, dP^T = V dO^T, dS^T, dq^T += K^T dS^T
-//                             (v_mfma_f32_32x32x16_bf16, 32 rows per wave).
+//                             (v_mfma_f32_32x32x16_bf16, 32 rows and 32 keys per wave,
+//                             2 waves per SIMD; the key halves' parts added at the end).
+//   bwd_dq_kernel             the same at D = 64 (32 rows and all 64 keys per wave).
 //   bwd_dkdv16_kernel         D = 128: one workgroup per kv block walks its query list:
 //                             S = Q K^T, dP = dO V^T, dS, dv^T += dO^T P, dk^T += Q^T dS
 //                             (v_mfma_f32_16x16x32_bf16, 16 keys per wave, 2 waves per SIMD).
