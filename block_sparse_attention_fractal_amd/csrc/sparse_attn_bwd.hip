@@ -394,7 +394,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dq_kernel(
 // keys 32 (w / 2) .. + 31 of every listed tile, and accumulates its own part of dQ^T; the two
 // key halves' parts are added through LDS once per block, in a fixed order.  A wave holds half
 // the score accumulators and fragments of the 2-wave kernel: about 230 registers, so two
-// workgroups (two waves per SIMD) are resident on a CU, with the same LDS bytes per MFMA.
+// workgroups (two waves per SIMD) are resident on a CU, with the same LDS bytes per MFMA.  The
+// dQ accumulators stay in VGPRs (plain MFMA builtins): under 256 registers nothing needs them
+// pinned to AGPRs, and pinned they cost copies between the register classes in every tile.
 constexpr int kDq4Threads = 256;
 
 template <bool kPad>
@@ -518,13 +520,13 @@ __global__ __launch_bounds__(kDq4Threads, 2) void bwd_dq4_kernel(
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int p = 0; p < 2; ++p) mfma_acc(acc[dt], kt[dt & 1][p], ds[p]);
+            for (int p = 0; p < 2; ++p)
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[dt & 1][p], ds[p], acc[dt], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         vm_wait<0>();
         __syncthreads();  // tile u + 1 has landed; everyone is done with tile u's stage
     }
-    acc_settle(acc);
     // the key half 1 waves hand their parts to the key half 0 waves through LDS (the ring is
     // free: the walk ended with a barrier and no load is in flight)
     float *part = reinterpret_cast<float *>(&ksh[0][0]) + (size_t)rh * (DT * 16 * 64);
